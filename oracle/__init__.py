@@ -1,0 +1,203 @@
+"""CPU oracle for the DSA lightning indexer and the ADIndex group token bank.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the CPU-baseline leg of
+the benchmark use it; the GPU library never does.  The arithmetic lives in
+``oracle.c`` (plain C, fp64); this module compiles it with gcc and marshals
+host arrays through ctypes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_SRC = os.path.join(_HERE, "oracle.c")
+
+F32, BF16, E4M3 = 0, 1, 2
+FORCE_BANK = 1
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (OpenMP over queries)."""
+    if force or not os.path.exists(LIB_PATH):
+        tmp = LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-Wall", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True, cwd=_HERE)
+        os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I32, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
+        L.oracle_e4m3_to_double.restype = D
+        L.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
+        L.oracle_bf16_to_double.restype = D
+        L.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+        L.oracle_max_threads.restype = I32
+        L.oracle_prefill.restype = I32
+        L.oracle_prefill.argtypes = [P, P, P, P, P, I32, I64, I64, I32, I32, I64, I32, P, I64, P, P, I32]
+        L.oracle_decode.restype = I32
+        L.oracle_decode.argtypes = [P, P, P, P, P, I32, I64, I32, I32, I32, P, I64, P, P, I32]
+        L.oracle_group_bank.restype = I32
+        L.oracle_group_bank.argtypes = [P, P, P, P, P, I32, I64, I64, I32, I32, I64, P, P, P, I32, I32,
+                                        I32, I32, ctypes.c_uint, P, I64, P, P, P, P, I32]
+        L.oracle_group_bank_pairs.restype = I64
+        L.oracle_group_bank_pairs.argtypes = [I64, I64, I32, I32, ctypes.c_uint]
+        for name in ("oracle_cost_prefill_base",):
+            getattr(L, name).restype = D
+            getattr(L, name).argtypes = [D]
+        L.oracle_cost_prefill_reuse.restype = D
+        L.oracle_cost_prefill_reuse.argtypes = [D, D, D]
+        L.oracle_cost_mtp_base_round.restype = D
+        L.oracle_cost_mtp_base_round.argtypes = [D, I32]
+        L.oracle_cost_mtp_reuse_round.restype = D
+        L.oracle_cost_mtp_reuse_round.argtypes = [D, I32, D, I32]
+        L.oracle_speedup_joint.restype = D
+        L.oracle_speedup_joint.argtypes = [D, I32, D, I32, I32, D]
+        _lib = L
+    return _lib
+
+
+# ------------------------------------------------------------------ marshalling
+
+def _host(x):
+    """A contiguous host numpy array holding exactly the bytes of ``x``."""
+    if x is None:
+        return None
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach()
+            if x.dtype == torch.bfloat16:
+                x = x.view(torch.int16)
+            x = x.cpu().contiguous().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(x)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dtype_code(dtype: str) -> int:
+    return {"f32": F32, "bf16": BF16, "fp8": E4M3}[dtype]
+
+
+def _rows(rows):
+    if rows is None:
+        return None, 0
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    return r, len(r)
+
+
+def prefill(q, k, w, dtype, q_pos0, topk, q_scale=None, k_scale=None, rows=None, nthreads=0):
+    """Dense indexer (Eq. 1-2) for every query row (or ``rows``).
+
+    Returns (idx int32 [n,topk], score float64 [n,topk]).
+    """
+    q, k, w = _host(q), _host(k), _host(w).astype(np.float32)
+    q_scale, k_scale = _host(q_scale), _host(k_scale)
+    Tq, H, d = q.shape
+    Tk = k.shape[0]
+    r, nr = _rows(rows)
+    n = nr if r is not None else Tq
+    idx = np.empty((n, topk), np.int32)
+    sc = np.empty((n, topk), np.float64)
+    rc = lib().oracle_prefill(_ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(w), _dtype_code(dtype),
+                              Tq, Tk, H, d, q_pos0, topk, _ptr(r), nr, _ptr(idx), _ptr(sc), nthreads)
+    if rc != 0:
+        raise ValueError(f"oracle_prefill failed ({rc})")
+    return idx, sc
+
+
+def decode(q, k_cache, k_scale, w, seq_lens, topk, rows=None, nthreads=0):
+    """Decode indexer: one bf16 query per sequence against an E4M3 cache."""
+    q, k_cache, k_scale = _host(q), _host(k_cache), _host(k_scale)
+    w = _host(w).astype(np.float32)
+    seq = _host(seq_lens).astype(np.int32)
+    B, H, d = q.shape
+    Nmax = k_cache.shape[1]
+    r, nr = _rows(rows)
+    n = nr if r is not None else B
+    idx = np.empty((n, topk), np.int32)
+    sc = np.empty((n, topk), np.float64)
+    rc = lib().oracle_decode(_ptr(q), _ptr(k_cache), _ptr(k_scale), _ptr(w), _ptr(seq), B, Nmax, H, d,
+                             topk, _ptr(r), nr, _ptr(idx), _ptr(sc), nthreads)
+    if rc != 0:
+        raise ValueError(f"oracle_decode failed ({rc})")
+    return idx, sc
+
+
+def group_bank(q, k, w, qbar, wbar, dtype, q_pos0, G, P, topk, flags=0, q_scale=None, k_scale=None,
+               qbar_scale=None, rows=None, want_bank=False, nthreads=0):
+    """ADIndex bank sharing (Eq. 8, 13, 14) with fallback to the original indexer.
+
+    Returns (idx [n,topk], score [n,topk], bank [NG,P] or None, pairs).
+    """
+    q, k, w = _host(q), _host(k), _host(w).astype(np.float32)
+    qbar, wbar = _host(qbar), _host(wbar).astype(np.float32)
+    q_scale, k_scale, qbar_scale = _host(q_scale), _host(k_scale), _host(qbar_scale)
+    Tq, H, d = q.shape
+    Tk = k.shape[0]
+    NG, Hs, _ = qbar.shape
+    r, nr = _rows(rows)
+    n = nr if r is not None else Tq
+    idx = np.empty((n, topk), np.int32)
+    sc = np.empty((n, topk), np.float64)
+    bank = np.empty((NG, P), np.int32) if want_bank else None
+    pairs = ctypes.c_int64(0)
+    rc = lib().oracle_group_bank(_ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(w), _dtype_code(dtype),
+                                 Tq, Tk, H, d, q_pos0, _ptr(qbar), _ptr(qbar_scale), _ptr(wbar), Hs, G, P,
+                                 topk, flags, _ptr(r), nr, _ptr(idx), _ptr(sc), _ptr(bank),
+                                 ctypes.cast(ctypes.pointer(pairs), ctypes.c_void_p), nthreads)
+    if rc != 0:
+        raise ValueError(f"oracle_group_bank failed ({rc})")
+    return idx, sc, bank, pairs.value
+
+
+def group_bank_pairs(Tq, q_pos0, G, P, flags=0) -> int:
+    return lib().oracle_group_bank_pairs(Tq, q_pos0, G, P, flags)
+
+
+def e4m3_to_double(code: int) -> float:
+    return lib().oracle_e4m3_to_double(code)
+
+
+def bf16_to_double(bits: int) -> float:
+    return lib().oracle_bf16_to_double(bits & 0xFFFF)
+
+
+def cost_prefill_base(L):
+    return lib().oracle_cost_prefill_base(L)
+
+
+def cost_prefill_reuse(L, G, P):
+    return lib().oracle_cost_prefill_reuse(L, G, P)
+
+
+def cost_mtp_base_round(N, m=16):
+    return lib().oracle_cost_mtp_base_round(N, m)
+
+
+def cost_mtp_reuse_round(N, G, P, m=16):
+    return lib().oracle_cost_mtp_reuse_round(N, G, P, m)
+
+
+def speedup_joint(L, G, P, R=32, m=16, a=8):
+    return lib().oracle_speedup_joint(L, G, P, R, m, a)
+
+
+def max_threads() -> int:
+    return lib().oracle_max_threads()

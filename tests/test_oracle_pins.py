@@ -1,0 +1,372 @@
+"""Pins for the CPU oracle: what the pages and the mathematics fix, independent of
+the oracle's own code.  CPU only.
+
+Each test names the mistake it is there to catch.  References are to
+"ADIndex: Layer-Adaptive Sparse Attention Indexing via Group-Level
+Distillation" (Qi et al.).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.bruteforce import lexsort_topk
+from workloads import make_decode, make_group_bank, make_prefill, to_bf16
+from workloads.gen import e4m3_quantize_rows
+
+GOLDEN = __file__.replace("test_oracle_pins.py", "golden/table5_speedups.txt")
+
+
+def _bf16(x):
+    return to_bf16(torch.as_tensor(np.asarray(x, np.float32)))
+
+
+def _f64(t):
+    return t.float().double().numpy() if isinstance(t, torch.Tensor) else np.asarray(t, np.float64)
+
+
+def _matmul_topk(qv, kv, q_pos0, K):
+    """Library-routine reference for H=1, w=1, q,k >= 0: score = q . k."""
+    S = qv @ kv.T
+    Tq, Tk = S.shape
+    valid = np.arange(Tk)[None, :] <= (q_pos0 + np.arange(Tq))[:, None]
+    return lexsort_topk(S, valid, K), S
+
+
+# ------------------------------------------------------------------ decoders
+
+def test_e4m3_decoder_matches_torch(oracle_lib):
+    """All 256 E4M3 codes against torch's float8_e4m3fn (OCP E4M3) conversion."""
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).double().numpy()
+    got = np.array([oracle.e4m3_to_double(c) for c in range(256)])
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert nan.sum() == 2  # S.1111.111 only
+    assert np.array_equal(ref[~nan], got[~nan])
+    assert oracle.e4m3_to_double(0x7E) == 448.0 and oracle.e4m3_to_double(0x01) == 2.0 ** -9
+
+
+def test_bf16_decoder_matches_torch(oracle_lib):
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 1 << 16, 4000)
+    bits = bits[((bits >> 7) & 0xFF) != 0xFF]  # finite patterns
+    ref = torch.as_tensor(bits.astype(np.int16)).view(torch.bfloat16).double().numpy()
+    got = np.array([oracle.bf16_to_double(int(b)) for b in bits])
+    assert np.array_equal(ref, got)
+
+
+# ----------------------------------------------------------- Eq. (1)-(2) pins
+
+@pytest.mark.parametrize("Tq,Tk,d,K", [(40, 97, 32, 16), (97, 97, 16, 200), (1, 5, 8, 3)])
+def test_single_head_is_a_matmul(oracle_lib, Tq, Tk, d, K):
+    """H=1, w=1, q,k >= 0: Eq. (1) is q . k.  Checked against np.matmul and a
+    full lexsort.  Catches a transposed operand, a wrong ReLU sign, causal or
+    q_pos0 off-by-ones, the tie rule and the padding."""
+    rng = np.random.default_rng(Tq * 131 + Tk)
+    qv = rng.integers(0, 4, (Tq, 1, d)).astype(np.float32)
+    kv = rng.integers(0, 4, (Tk, d)).astype(np.float32)
+    q_pos0 = Tk - Tq
+    idx, sc = oracle.prefill(_bf16(qv), _bf16(kv), np.ones((Tq, 1), np.float32), "bf16", q_pos0, K)
+    (ref_i, ref_s), _ = _matmul_topk(qv[:, 0, :].astype(np.float64), kv.astype(np.float64), q_pos0, K)
+    assert np.array_equal(idx, ref_i)
+    assert np.array_equal(sc, ref_s)
+
+
+def test_relu_acts_per_head(oracle_lib):
+    """Heads q and -q with unit weights: ReLU(x) + ReLU(-x) = |x|.  A dropped
+    ReLU gives 0, a ReLU after the head sum gives 0."""
+    rng = np.random.default_rng(2)
+    Tq = Tk = 64
+    d = 16
+    q0 = rng.integers(-3, 4, (Tq, d)).astype(np.float32)
+    kv = rng.integers(-3, 4, (Tk, d)).astype(np.float32)
+    q = np.stack([q0, -q0], axis=1)
+    idx, sc = oracle.prefill(_bf16(q), _bf16(kv), np.ones((Tq, 2), np.float32), "bf16", 0, 8)
+    S = np.abs(q0.astype(np.float64) @ kv.T.astype(np.float64))
+    ref_i, ref_s = lexsort_topk(S, np.tril(np.ones((Tq, Tk), bool)), 8)
+    assert np.array_equal(idx, ref_i) and np.array_equal(sc, ref_s)
+
+
+def test_gate_weights_scale_their_own_head(oracle_lib):
+    """q_j = c_j q_0 with c_j > 0: the score is (sum_j w_{t,j} c_j) ReLU(q_0 . k),
+    with per-query, per-head w of mixed sign.  Catches a w indexed by the wrong
+    query or head, and a transposed [H,d] layout."""
+    rng = np.random.default_rng(3)
+    Tq, Tk, d, H = 30, 50, 8, 3
+    c = np.array([1.0, 2.0, 0.5])
+    q0 = rng.integers(-3, 4, (Tq, d)).astype(np.float32)
+    q = q0[:, None, :] * c[None, :, None]
+    w = rng.integers(-3, 4, (Tq, H)).astype(np.float32)
+    kv = rng.integers(-3, 4, (Tk, d)).astype(np.float32)
+    q_pos0 = Tk - Tq
+    idx, sc = oracle.prefill(_bf16(q.astype(np.float32)), _bf16(kv), w, "bf16", q_pos0, Tk)
+    coef = (w.astype(np.float64) * c[None, :]).sum(1)
+    S = coef[:, None] * np.maximum(q0.astype(np.float64) @ kv.T.astype(np.float64), 0.0)
+    valid = np.arange(Tk)[None, :] <= (q_pos0 + np.arange(Tq))[:, None]
+    ref_i, ref_s = lexsort_topk(S + 0.0, valid, Tk)
+    assert np.array_equal(idx, ref_i)
+    assert np.array_equal(sc, ref_s)
+
+
+def test_zero_weights_rank_by_index(oracle_lib):
+    """w = 0: every score is 0 (and -0 ranks as +0), so the selection is the
+    first min(K, t+1) positions."""
+    wl = make_prefill(T=70, H=4, d=16, topk=32, dtype="bf16", dist="int", seed=4)
+    w = -np.zeros((70, 4), np.float32)
+    idx, sc = oracle.prefill(wl["q"], wl["k"], w, "bf16", 0, 32)
+    for t in range(70):
+        m = min(32, t + 1)
+        assert list(idx[t, :m]) == list(range(m)) and (idx[t, m:] == -1).all()
+        assert (sc[t, :m] == 0).all() and np.isneginf(sc[t, m:]).all()
+
+
+def test_bruteforce_random_small(oracle_lib):
+    """The full score matrix (numpy einsum) then a full lexsort per row, on
+    integer inputs with many ties; several heads, K above and below the prefix."""
+    for seed, (T, H, d, K) in enumerate([(96, 4, 32, 16), (50, 3, 8, 64), (130, 5, 16, 33)]):
+        wl = make_prefill(T=T, H=H, d=d, topk=K, dtype="bf16", dist="int", seed=seed)
+        q = _f64(wl["q"])
+        k = _f64(wl["k"])
+        w = _f64(wl["w"])
+        S = (w[:, :, None] * np.maximum(np.einsum("thc,sc->ths", q, k), 0)).sum(1)
+        ref_i, ref_s = lexsort_topk(S, np.tril(np.ones((T, T), bool)), K)
+        idx, sc = oracle.prefill(wl["q"], wl["k"], wl["w"], "bf16", 0, K)
+        assert np.array_equal(idx, ref_i) and np.array_equal(sc, ref_s)
+
+
+def test_invariants_and_rows(oracle_lib):
+    """Selected indices are causal, distinct, ascending, exactly min(K, t+1);
+    computing a subset of rows gives the same rows."""
+    wl = make_prefill(T=300, H=4, d=32, topk=40, dtype="bf16", dist="normal", seed=5, Tq=120)
+    q_pos0 = wl.params["q_pos0"]
+    idx, sc = oracle.prefill(wl["q"], wl["k"], wl["w"], "bf16", q_pos0, 40)
+    for i in range(120):
+        t = q_pos0 + i
+        v = idx[i][idx[i] >= 0]
+        assert len(v) == min(40, t + 1) and (np.diff(v) > 0).all() and v.max() <= t
+    rows = [0, 7, 119, 7]
+    i2, s2 = oracle.prefill(wl["q"], wl["k"], wl["w"], "bf16", q_pos0, 40, rows=rows)
+    assert np.array_equal(i2, idx[rows]) and np.array_equal(s2, sc[rows])
+
+
+def test_fp8_scales_multiply_each_token(oracle_lib):
+    """E4M3 inputs with per-token scales, H=1, w=1, non-negative values: the
+    score is the matmul of the torch-dequantised tensors."""
+    rng = np.random.default_rng(6)
+    Tq = Tk = 48
+    d = 32
+    qf = torch.as_tensor(np.abs(rng.standard_normal((Tq, 1, d))).astype(np.float32))
+    kf = torch.as_tensor(np.abs(rng.standard_normal((Tk, d))).astype(np.float32) * 5)
+    qc, qs = e4m3_quantize_rows(qf.reshape(Tq, d))
+    kc, ks = e4m3_quantize_rows(kf)
+    idx, sc = oracle.prefill(qc.reshape(Tq, 1, d), kc, np.ones((Tq, 1), np.float32), "fp8", 0, 10,
+                             q_scale=qs, k_scale=ks)
+    qd = qc.view(torch.float8_e4m3fn).double() * qs.double()[:, None]
+    kd = kc.view(torch.float8_e4m3fn).double() * ks.double()[:, None]
+    S = (qd @ kd.T).numpy()
+    ref_i, ref_s = lexsort_topk(S, np.tril(np.ones((Tq, Tk), bool)), 10)
+    assert np.array_equal(idx, ref_i)
+    np.testing.assert_allclose(sc, ref_s, rtol=1e-14)
+
+
+# ------------------------------------------------------------------- decode
+
+def test_decode_equals_prefill_row(oracle_lib):
+    """decode with seq_len = t+1 is prefill row t (integer values: the E4M3 cache
+    converts exactly to the bf16 keys of the prefill call); ragged lengths."""
+    B, N, H, d, K = 5, 90, 4, 32, 20
+    lens = [90, 1, 37, 64, 20]
+    wl = make_decode(B, N, H, d, K, dist="int", seed=7, seq_lens=lens)
+    idx, sc = oracle.decode(wl["q"], wl["k_cache"], wl["k_scale"], wl["w"], wl["seq_lens"], K)
+    kb = to_bf16(wl["k_cache"].view(torch.float8_e4m3fn).float())
+    for b in range(B):
+        n = lens[b]
+        pi, ps = oracle.prefill(wl["q"][b:b + 1], kb[b, :n], wl["w"][b:b + 1], "bf16", n - 1, K)
+        assert np.array_equal(idx[b], pi[0]) and np.array_equal(sc[b], ps[0])
+
+
+def test_decode_single_head_matmul(oracle_lib):
+    B, N, d, K = 3, 200, 64, 50
+    rng = np.random.default_rng(8)
+    q = np.abs(rng.standard_normal((B, 1, d))).astype(np.float32)
+    kf = torch.as_tensor(np.abs(rng.standard_normal((B * N, d))).astype(np.float32))
+    kc, ks = e4m3_quantize_rows(kf)
+    qb = _bf16(q)
+    idx, sc = oracle.decode(qb, kc.reshape(B, N, d), ks.reshape(B, N), np.ones((B, 1), np.float32),
+                            np.array([200, 150, 3], np.int32), K)
+    kd = (kc.view(torch.float8_e4m3fn).double() * ks.double()[:, None]).numpy().reshape(B, N, d)
+    for b, n in enumerate([200, 150, 3]):
+        S = (qb[b].double().numpy() @ kd[b, :n].T)
+        ri, rs = lexsort_topk(S, np.ones_like(S, bool), K)
+        assert np.array_equal(idx[b], ri[0])
+        np.testing.assert_allclose(sc[b], rs[0], rtol=1e-14)
+
+
+# --------------------------------------------------------- group bank pins
+
+def _gb(T, G, P, K, seed, Hs=None, H=4, d=16, Tq=None, dist="int", **kw):
+    return make_group_bank(T=T, H=H, Hs=Hs or H, d=d, topk=K, G=G, P=P, dtype="bf16", dist=dist,
+                           seed=seed, Tq=Tq, **kw)
+
+
+def test_full_bank_equals_dense(oracle_lib):
+    """Forced bank with P >= every prefix: the bank is the whole prefix, so
+    every query's candidate set is its whole prefix and the result is dense."""
+    wl = _gb(T=80, G=4, P=128, K=24, seed=9, Tq=64)
+    p = wl.params
+    d_i, d_s = oracle.prefill(wl["q"], wl["k"], wl["w"], "bf16", p["q_pos0"], 24)
+    g_i, g_s, bank, _ = oracle.group_bank(wl["q"], wl["k"], wl["w"], wl["qbar"], wl["wbar"], "bf16",
+                                          p["q_pos0"], 4, 128, 24, flags=oracle.FORCE_BANK,
+                                          want_bank=True)
+    assert np.array_equal(d_i, g_i) and np.array_equal(d_s, g_s)
+    for g in range(16):
+        a = p["q_pos0"] + 4 * g
+        assert list(bank[g][bank[g] >= 0]) == list(range(a + 1))
+
+
+def test_anchor_query_as_group_query_recovers_dense(oracle_lib):
+    """With q-bar = the anchor's own q and w-bar = its w, and K <= P, the anchor's
+    top-K lies inside the bank (a top-P of the same score), so the anchor row
+    equals the dense row (the exact-recovery statement of Section 1)."""
+    T, G, P, K = 200, 8, 40, 12
+    wl = _gb(T=T, G=G, P=P, K=K, seed=10, dist="normal")
+    qbar = wl["q"][::G].clone()
+    wbar = wl["w"][::G].clone()
+    d_i, _ = oracle.prefill(wl["q"], wl["k"], wl["w"], "bf16", 0, K)
+    g_i, _, bank, _ = oracle.group_bank(wl["q"], wl["k"], wl["w"], qbar, wbar, "bf16", 0, G, P, K,
+                                        want_bank=True)
+    n_checked = 0
+    for g in range(T // G):
+        a = g * G
+        if a + 1 > P:
+            assert np.array_equal(g_i[a], d_i[a])
+            n_checked += 1
+        else:
+            assert (bank[g] == -1).all()
+    assert n_checked > 10
+
+
+def test_exact_recovery_and_bank_shape(oracle_lib):
+    """Whenever a query's dense top-K lies in its candidate set C_i = bank U
+    {t+1..i}, the bank result equals the dense result; otherwise it is a top-K of
+    C_i.  Banks hold min(P, t+1) ascending prefix positions; the t+1 > P rule is
+    strict; the trailing incomplete group uses the original indexer."""
+    T, G, P, K = 203, 4, 48, 16
+    wl = _gb(T=T, G=G, P=P, K=K, seed=11, H=3, Hs=2, d=8)
+    q, k, w = _f64(wl["q"]), _f64(wl["k"]), _f64(wl["w"])
+    qb, wb = _f64(wl["qbar"]), _f64(wl["wbar"])
+    d_i, _ = oracle.prefill(wl["q"], wl["k"], wl["w"], "bf16", 0, K)
+    g_i, g_s, bank, _ = oracle.group_bank(wl["q"], wl["k"], wl["w"], wl["qbar"], wl["wbar"], "bf16",
+                                          0, G, P, K, want_bank=True)
+    S = (w[:, :, None] * np.maximum(np.einsum("thc,sc->ths", q, k), 0)).sum(1)
+    Sb = (wb[:, :, None] * np.maximum(np.einsum("ghc,sc->ghs", qb, k), 0)).sum(1)
+    full_groups = T // G
+    recovered = 0
+    for i in range(T):
+        g, t = i // G, i
+        a = g * G
+        if g >= full_groups or a + 1 <= P:
+            assert np.array_equal(g_i[i], d_i[i]), i
+            if g < len(bank):
+                assert (bank[g] == -1).all()
+            continue
+        b = bank[g][bank[g] >= 0]
+        assert len(b) == P and (np.diff(b) > 0).all() and b.max() <= a
+        # the bank is a top-P of the group score over s <= a
+        rb, _ = lexsort_topk(Sb[g:g + 1, :a + 1], np.ones((1, a + 1), bool), P)
+        assert np.array_equal(b, rb[0])
+        cand = np.concatenate([b, np.arange(a + 1, t + 1)])
+        ri, rs = lexsort_topk(S[i:i + 1, cand], np.ones((1, len(cand)), bool), K)
+        ref = np.full(K, -1, np.int32)
+        sel = np.sort(cand[ri[0][ri[0] >= 0]])
+        ref[:len(sel)] = sel
+        assert np.array_equal(g_i[i], ref)
+        dense = d_i[i][d_i[i] >= 0]
+        if np.isin(dense, cand).all():
+            assert np.array_equal(g_i[i], d_i[i])
+            recovered += 1
+    # with P = 3K and 3 heads some queries are fully covered
+    assert recovered > 0
+
+
+def test_eligibility_boundary(oracle_lib):
+    """Anchor t with t+1 == P falls back; t+1 == P+1 builds a bank."""
+    G, P = 4, 21
+    wl = _gb(T=40, G=G, P=P, K=8, seed=12)
+    _, _, bank, _ = oracle.group_bank(wl["q"], wl["k"], wl["w"], wl["qbar"], wl["wbar"], "bf16", 0,
+                                      G, P, 8, want_bank=True)
+    # anchors 0,4,...,36: anchor 20 sees exactly P = 21 keys and falls back;
+    # anchor 24 sees 25 > 21 and builds a bank of P
+    assert (bank[5] == -1).all() and (bank[6] >= 0).all()
+    assert oracle.group_bank_pairs(40, 0, G, P) == _pairs_closed_form(40, 0, G, P)
+
+
+def _pairs_closed_form(Tq, q_pos0, G, P):
+    """Scored pairs: fallback queries score t+1 keys; a bank group scores its
+    anchor prefix once, then each member r scores |bank| + r (Appendix A.2,
+    Eq. (17) with |bank| = P)."""
+    total = 0
+    for g in range(-(-Tq // G)):
+        a = q_pos0 + g * G
+        members = min(G, Tq - g * G)
+        if members == G and a + 1 > P:
+            total += (a + 1) + G * P + G * (G - 1) // 2
+        else:
+            total += sum(a + r + 1 for r in range(members))
+    return total
+
+
+@pytest.mark.parametrize("Tq,q_pos0,G,P", [(203, 0, 4, 48), (160, 40, 16, 64), (65536, 0, 16, 8192),
+                                           (131072, 0, 8, 4096)])
+def test_pair_count_closed_form(oracle_lib, Tq, q_pos0, G, P):
+    assert oracle.group_bank_pairs(Tq, q_pos0, G, P) == _pairs_closed_form(Tq, q_pos0, G, P)
+
+
+def test_pair_count_matches_continuous_model(oracle_lib):
+    """The discrete count approaches Eq. (19); config 5's count gives the 3.38 of
+    Table 5(a) at G=16, P=8K, L=64K."""
+    L, G, P = 65536, 16, 8192
+    disc = oracle.group_bank_pairs(L, 0, G, P)
+    base = L * (L + 1) // 2
+    assert disc == 635_846_144 and base == 2_147_516_416
+    assert round(base / disc, 2) == 3.38
+    assert abs(disc / oracle.cost_prefill_reuse(L, G, P) - 1) < 1e-3
+
+
+def test_group_bank_pairs_reported(oracle_lib):
+    wl = _gb(T=120, G=4, P=30, K=8, seed=13)
+    _, _, _, pairs = oracle.group_bank(wl["q"], wl["k"], wl["w"], wl["qbar"], wl["wbar"], "bf16", 0,
+                                       4, 30, 8)
+    assert pairs == _pairs_closed_form(120, 0, 4, 30)
+
+
+# ----------------------------------------------------------- Table 5 pins
+
+def _table5():
+    rows = []
+    for line in open(GOLDEN):
+        if line.startswith("#") or not line.strip():
+            continue
+        panel, G, P, *vals = line.split()
+        rows.append((panel, int(G), int(P[:-1]) * 1024, [float(v) for v in vals]))
+    return rows
+
+
+def test_table5_all_entries(oracle_lib):
+    """All 108 printed speedups of Appendix A, Table 5 (a)-(c) from the cost
+    model of Eq. (15)-(24) and (28)."""
+    n = 0
+    for panel, G, P, vals in _table5():
+        for L, v in zip([16384, 32768, 65536, 131072], vals):
+            if panel == "a":
+                s = oracle.cost_prefill_base(L) / oracle.cost_prefill_reuse(L, G, P)
+            elif panel == "b":
+                s = oracle.cost_mtp_base_round(L) / oracle.cost_mtp_reuse_round(L, G, P)
+            else:
+                s = oracle.speedup_joint(L, G, P)
+            assert math.isclose(round(s, 2), v), (panel, G, P, L, s, v)
+            n += 1
+    assert n == 108
