@@ -1,0 +1,136 @@
+/*
+ * dsa_indexer.h -- C ABI of the MI355X (gfx950) DSA lightning-indexer library
+ * (libdsaidx.so).
+ *
+ * The operations are those of "ADIndex: Layer-Adaptive Sparse Attention
+ * Indexing via Group-Level Distillation" (Qi et al.):
+ *
+ *   Section 3, Eq. (1):  I_{t,s} = sum_{j<H} w_{t,j} * ReLU(q_{t,j} . k_s), s <= t
+ *                        (no further scale factor; per-token fp8 scales are part
+ *                        of the dequantised q and k)
+ *   Section 3, Eq. (2):  T_t = TopK_{s<=t}(I_{t,s}, K)
+ *   Section 4.3, Eq. (13)-(14) with Eq. (8): the group token bank P_t = TopK of
+ *                        the group score over s <= t (size P), built for
+ *                        complete groups whose anchor t sees t+1 > P keys, and
+ *                        T_i = TopK over C_i = P_t U {t+1..i} with the original
+ *                        indexer; other groups use Eq. (2).
+ *
+ * Conventions shared by every entry point
+ *  - Every tensor pointer is DEVICE memory owned by the caller, contiguous,
+ *    row-major (last dimension fastest) and 16-byte aligned.  The library never
+ *    allocates or frees device memory: scratch comes from the caller's
+ *    workspace `ws` of `ws_bytes` bytes (16-byte aligned), sized by the
+ *    matching *_workspace_size() call.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    asynchronously; nothing synchronises the host.
+ *  - Ranking: higher score first, ties to the lower key index; -0 ranks as +0.
+ *    Each output row holds the selected key indices in ascending order, then -1
+ *    up to `topk`; the optional score row holds fp32 scores, -inf at padding.
+ *    Exactly min(topk, number of candidates) entries are valid.  Outputs are
+ *    deterministic run to run.
+ *  - Inputs must be finite; they are not checked on the device.
+ *  - Return value: DSAIDX_OK, or a negative dsaidx_status.  Argument errors are
+ *    detected on the host before anything is enqueued and leave the outputs
+ *    untouched; a failed launch returns DSAIDX_ERR_HIP; device faults surface at
+ *    the caller's next synchronisation.  indexer_last_error() then returns a
+ *    message for the calling thread.  No C++ exception crosses this interface.
+ *  - Supported sizes: 1 <= H <= 64 (heads are padded to 32 or 64 on the
+ *    device); d in {32, 64, 128} for bf16 and {64, 128} for fp8;
+ *    1 <= topk <= 2048; group size G in {4, 8, 16}; topk <= P <= 16384.
+ */
+#ifndef DSA_INDEXER_H
+#define DSA_INDEXER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DSAIDX_OK = 0,
+    DSAIDX_ERR_INVALID_ARG = -1, /* null pointer, bad size, bad alignment */
+    DSAIDX_ERR_UNSUPPORTED = -2, /* valid but outside the supported sizes */
+    DSAIDX_ERR_WORKSPACE = -3,   /* ws_bytes below the *_workspace_size() value */
+    DSAIDX_ERR_HIP = -4          /* a HIP launch or runtime call failed */
+} dsaidx_status;
+
+typedef enum {
+    DSAIDX_BF16 = 1,     /* bfloat16 q and k, no scales */
+    DSAIDX_FP8_E4M3 = 2  /* OCP FP8 E4M3 ("fn") codes, one fp32 scale per token */
+} dsaidx_dtype;
+
+enum { DSAIDX_FORCE_BANK = 1u }; /* group bank: also build banks when t+1 <= P */
+
+/*
+ * Dense causal indexer, Eq. (1)-(2).  Query i of the call sits at position
+ * q_pos0 + i and sees keys 0 .. q_pos0 + i; a chunked prefill passes each
+ * query chunk with its q_pos0 and Tk >= q_pos0 + Tq.
+ *   q        [Tq, H, d]   dtype codes
+ *   q_scale  [Tq] fp32    per-query-token scale (fp8 only, else NULL)
+ *   k        [Tk, d]      dtype codes
+ *   k_scale  [Tk] fp32    per-key-token scale (fp8 only, else NULL)
+ *   w        [Tq, H] fp32 per-query head weights
+ *   out_idx  [Tq, topk] int32;  out_score [Tq, topk] fp32 or NULL
+ * The Tq x Tk score matrix is never stored: each query keeps a streaming
+ * candidate buffer in `ws`.
+ */
+int indexer_prefill(const void *q, const float *q_scale, const void *k, const float *k_scale,
+                    const float *w, int dtype, int64_t Tq, int64_t Tk, int H, int d,
+                    int64_t q_pos0, int topk, int32_t *out_idx, float *out_score, void *ws,
+                    size_t ws_bytes, void *stream);
+size_t indexer_prefill_workspace_size(int64_t Tq, int64_t Tk, int H, int d, int topk, int dtype);
+
+/*
+ * Decode indexer, Eq. (1)-(2) for one new query per sequence, scanning its
+ * whole cache (Section 3: O(L) per decoding query).
+ *   q        [B, H, d] bf16
+ *   k_cache  [B, Nmax, d] E4M3 codes;  k_scale [B, Nmax] fp32
+ *   w        [B, H] fp32
+ *   seq_lens [B] int32 (device): sequence b's query sees keys 0 .. seq_lens[b]-1,
+ *            0 <= seq_lens[b] <= Nmax (checked on the device: out-of-range
+ *            lengths are clamped to [0, Nmax])
+ *   out_idx  [B, topk] int32;  out_score [B, topk] fp32 or NULL
+ */
+int indexer_decode(const void *q, const uint8_t *k_cache, const float *k_scale, const float *w,
+                   const int32_t *seq_lens, int B, int64_t Nmax, int H, int d, int topk,
+                   int32_t *out_idx, float *out_score, void *ws, size_t ws_bytes, void *stream);
+size_t indexer_decode_workspace_size(int B, int64_t Nmax, int H, int d, int topk);
+
+/*
+ * ADIndex group token bank, Section 4.3 Eq. (13)-(14) with the group score of
+ * Eq. (8).  Queries are as in indexer_prefill; the call's queries form
+ * consecutive groups of G starting at query 0 (q_pos0 must be a multiple of
+ * G).  Group g's anchor sits at t = q_pos0 + gG.
+ *   qbar       [ceil(Tq/G), Hs, d] dtype codes: the group indexer's query
+ *   qbar_scale [ceil(Tq/G)] fp32 (fp8 only, else NULL)
+ *   wbar       [ceil(Tq/G), Hs] fp32: the group indexer's head weights
+ *   flags      DSAIDX_FORCE_BANK or 0
+ *   out_idx    [Tq, topk] int32; out_score [Tq, topk] fp32 or NULL
+ *   out_bank   [ceil(Tq/G), P] int32 or NULL: each bank in ascending order
+ *              (min(P, t+1) entries, then -1); rows of groups that use the
+ *              original indexer are all -1
+ */
+int indexer_group_bank(const void *q, const float *q_scale, const void *k, const float *k_scale,
+                       const float *w, int dtype, int64_t Tq, int64_t Tk, int H, int d,
+                       int64_t q_pos0, const void *qbar, const float *qbar_scale,
+                       const float *wbar, int Hs, int G, int P, int topk, unsigned flags,
+                       int32_t *out_idx, int32_t *out_bank, float *out_score, void *ws,
+                       size_t ws_bytes, void *stream);
+size_t indexer_group_bank_workspace_size(int64_t Tq, int64_t Tk, int H, int Hs, int d, int G,
+                                         int P, int topk, int dtype);
+
+/* Number of query-key scores indexer_group_bank evaluates for these sizes
+ * (the unit of the cost model of Appendix A.1): fallback queries score t+1
+ * keys, a bank group scores its anchor prefix once and each member i scores
+ * |P_t| + (i - t) candidates.  Host only; -1 on bad arguments. */
+int64_t indexer_group_bank_pairs(int64_t Tq, int64_t q_pos0, int G, int P, unsigned flags);
+
+/* Message describing the calling thread's last non-OK return ("" if none). */
+const char *indexer_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_INDEXER_H */

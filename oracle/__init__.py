@@ -45,6 +45,8 @@ def lib():
         L.oracle_bf16_to_double.restype = D
         L.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
         L.oracle_max_threads.restype = I32
+        L.oracle_score_pairs.restype = I32
+        L.oracle_score_pairs.argtypes = [P, P, I32, P, P, I32, P, I32, I32, P, P, I64, P, I32]
         L.oracle_prefill.restype = I32
         L.oracle_prefill.argtypes = [P, P, P, P, P, I32, I64, I64, I32, I32, I64, I32, P, I64, P, P, I32]
         L.oracle_decode.restype = I32
@@ -120,6 +122,24 @@ def prefill(q, k, w, dtype, q_pos0, topk, q_scale=None, k_scale=None, rows=None,
     if rc != 0:
         raise ValueError(f"oracle_prefill failed ({rc})")
     return idx, sc
+
+
+def score_pairs(q, k, w, rows, keys, q_dtype, k_dtype, q_scale=None, k_scale=None, nthreads=0):
+    """Eq. (1) for the pairs (q row rows[p], k row keys[p]); q [*,H,d], k [*,d]
+    (a decode cache may be passed flattened to [B*Nmax, d])."""
+    q, k, w = _host(q), _host(k), _host(w).astype(np.float32)
+    q_scale, k_scale = _host(q_scale), _host(k_scale)
+    H, d = q.shape[-2], q.shape[-1]
+    r = np.ascontiguousarray(np.asarray(rows, np.int64).ravel())
+    kk = np.ascontiguousarray(np.asarray(keys, np.int64).ravel())
+    assert r.shape == kk.shape
+    out = np.empty(len(r), np.float64)
+    rc = lib().oracle_score_pairs(_ptr(q), _ptr(q_scale), _dtype_code(q_dtype), _ptr(k), _ptr(k_scale),
+                                  _dtype_code(k_dtype), _ptr(w), H, d, _ptr(r), _ptr(kk), len(r), _ptr(out),
+                                  nthreads)
+    if rc != 0:
+        raise ValueError(f"oracle_score_pairs failed ({rc})")
+    return out
 
 
 def decode(q, k_cache, k_scale, w, seq_lens, topk, rows=None, nthreads=0):

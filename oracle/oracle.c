@@ -176,6 +176,37 @@ static double *load_keys(const void *k, const float *k_scale, int dtype, int64_t
     return K;
 }
 
+/* ------------------------------------------------- single scores, Eq. 1 */
+
+int oracle_score_pairs(const void *q, const float *q_scale, int q_dtype, const void *k,
+                       const float *k_scale, int k_dtype, const float *w, int H, int d,
+                       const int64_t *rows, const int64_t *keys, int64_t n, double *out,
+                       int nthreads)
+{
+    if (H <= 0 || d <= 0 || n < 0)
+        return -1;
+    set_threads(nthreads);
+    int err = 0;
+#pragma omp parallel
+    {
+        double *qrow = malloc(sizeof(double) * (size_t)H * d);
+        double *wrow = malloc(sizeof(double) * (size_t)H);
+        double *krow = malloc(sizeof(double) * (size_t)d);
+        if (!qrow || !wrow || !krow)
+            err = -2;
+#pragma omp for schedule(static)
+        for (int64_t p = 0; p < n; ++p) {
+            if (!qrow || !wrow || !krow) continue;
+            load_row(q, q_scale, q_dtype, rows[p], H * d, qrow);
+            for (int j = 0; j < H; ++j) wrow[j] = (double)w[rows[p] * H + j];
+            load_row(k, k_scale, k_dtype, keys[p], d, krow);
+            out[p] = indexer_score(qrow, wrow, krow, H, d);
+        }
+        free(qrow); free(wrow); free(krow);
+    }
+    return err;
+}
+
 /* ------------------------------------------------------ dense prefill */
 
 int oracle_prefill(const void *q, const float *q_scale, const void *k, const float *k_scale,

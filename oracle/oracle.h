@@ -30,6 +30,13 @@ double oracle_e4m3_to_double(uint8_t c);
 double oracle_bf16_to_double(uint16_t b);
 int oracle_max_threads(void);
 
+/* Eq. (1) for n given (query row, key row) pairs: q rows of [*, H, d] in
+ * q_dtype, k rows of [*, d] in k_dtype, w rows of [*, H]. */
+int oracle_score_pairs(const void *q, const float *q_scale, int q_dtype, const void *k,
+                       const float *k_scale, int k_dtype, const float *w, int H, int d,
+                       const int64_t *rows, const int64_t *keys, int64_t n, double *out,
+                       int nthreads);
+
 int oracle_prefill(const void *q, const float *q_scale, const void *k, const float *k_scale,
                    const float *w, int dtype, int64_t Tq, int64_t Tk, int H, int d, int64_t q_pos0,
                    int topk, const int64_t *rows, int64_t nrows, int32_t *out_idx,

@@ -1,0 +1,148 @@
+"""MI355X (gfx950) DSA lightning indexer: Python binding of libdsaidx.so.
+
+The functions below only marshal arguments: every step of the indexer runs in
+the library's HIP kernels.  torch supplies device memory (inputs, outputs and
+the workspace) and the current HIP stream.  There is no CPU fallback: calling
+without the built library, or with host tensors, raises.
+
+    idx, score = indexer_prefill(q, k, w, q_pos0, topk, q_scale=None, k_scale=None)
+    idx, score = indexer_decode(q, k_cache, k_scale, w, seq_lens, topk)
+    idx, score, bank = indexer_group_bank(q, k, w, qbar, wbar, q_pos0, G, P, topk, ...)
+
+Tensors (contiguous, on the GPU): q [Tq,H,d] bf16 or uint8 E4M3 codes,
+k [Tk,d] the same dtype, w [Tq,H] fp32, per-token fp32 scales for E4M3.
+"""
+from __future__ import annotations
+
+import torch
+
+from ._lib import (DSAIDX_BF16, DSAIDX_FORCE_BANK, DSAIDX_FP8_E4M3, DSAIDX_OK, LIB_PATH,  # noqa: F401
+                   last_error, lib)
+
+__all__ = ["indexer_prefill", "indexer_decode", "indexer_group_bank", "indexer_group_bank_pairs",
+           "workspace_prefill", "workspace_decode", "workspace_group_bank", "FORCE_BANK", "lib",
+           "LIB_PATH"]
+
+FORCE_BANK = DSAIDX_FORCE_BANK
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dev(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("indexer tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("indexer tensors must be contiguous")
+        dev = t.device if dev is None else dev
+    return dev
+
+
+def _dtype(q):
+    if q.dtype == torch.bfloat16:
+        return DSAIDX_BF16
+    if q.dtype == torch.uint8:
+        return DSAIDX_FP8_E4M3
+    raise ValueError(f"q dtype {q.dtype}: expected bfloat16 or uint8 E4M3 codes")
+
+
+def _check(rc, what):
+    if rc != DSAIDX_OK:
+        raise RuntimeError(f"{what} failed ({rc}): {last_error()}")
+
+
+def _stream(dev):
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _ws(nbytes, dev, ws):
+    if nbytes == 0:
+        return None
+    if ws is not None and ws.numel() * ws.element_size() >= nbytes:
+        return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+
+def workspace_prefill(Tq, Tk, H, d, topk, dtype):
+    return lib().indexer_prefill_workspace_size(Tq, Tk, H, d, topk, dtype)
+
+
+def workspace_decode(B, Nmax, H, d, topk):
+    return lib().indexer_decode_workspace_size(B, Nmax, H, d, topk)
+
+
+def workspace_group_bank(Tq, Tk, H, Hs, d, G, P, topk, dtype):
+    return lib().indexer_group_bank_workspace_size(Tq, Tk, H, Hs, d, G, P, topk, dtype)
+
+
+def indexer_group_bank_pairs(Tq, q_pos0, G, P, flags=0):
+    return lib().indexer_group_bank_pairs(Tq, q_pos0, G, P, flags)
+
+
+def indexer_prefill(q, k, w, q_pos0=0, topk=2048, q_scale=None, k_scale=None, want_score=True,
+                    out_idx=None, out_score=None, ws=None):
+    """Dense causal indexer (Eq. (1)-(2)); returns (idx int32 [Tq,topk], score fp32 or None)."""
+    dev = _dev(q, k, w, q_scale, k_scale, out_idx, out_score, ws)
+    Tq, H, d = q.shape
+    Tk = k.shape[0]
+    dt = _dtype(q)
+    if out_idx is None:
+        out_idx = torch.empty((Tq, topk), dtype=torch.int32, device=dev)
+    if want_score and out_score is None:
+        out_score = torch.empty((Tq, topk), dtype=torch.float32, device=dev)
+    ws = _ws(workspace_prefill(Tq, Tk, H, d, topk, dt), dev, ws)
+    rc = lib().indexer_prefill(_ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(w), dt, Tq, Tk, H, d,
+                               q_pos0, topk, _ptr(out_idx), _ptr(out_score), _ptr(ws),
+                               0 if ws is None else ws.numel(), _stream(dev))
+    _check(rc, "indexer_prefill")
+    return out_idx, out_score
+
+
+def indexer_decode(q, k_cache, k_scale, w, seq_lens, topk=2048, want_score=True, out_idx=None,
+                   out_score=None, ws=None):
+    """Decode indexer over an E4M3 cache; returns (idx int32 [B,topk], score fp32 or None)."""
+    dev = _dev(q, k_cache, k_scale, w, seq_lens, out_idx, out_score, ws)
+    B, H, d = q.shape
+    Nmax = k_cache.shape[1]
+    if q.dtype != torch.bfloat16 or k_cache.dtype != torch.uint8 or seq_lens.dtype != torch.int32:
+        raise ValueError("decode takes bf16 q, uint8 E4M3 k_cache and int32 seq_lens")
+    if out_idx is None:
+        out_idx = torch.empty((B, topk), dtype=torch.int32, device=dev)
+    if want_score and out_score is None:
+        out_score = torch.empty((B, topk), dtype=torch.float32, device=dev)
+    ws = _ws(workspace_decode(B, Nmax, H, d, topk), dev, ws)
+    rc = lib().indexer_decode(_ptr(q), _ptr(k_cache), _ptr(k_scale), _ptr(w), _ptr(seq_lens), B, Nmax, H, d,
+                              topk, _ptr(out_idx), _ptr(out_score), _ptr(ws), 0 if ws is None else ws.numel(),
+                              _stream(dev))
+    _check(rc, "indexer_decode")
+    return out_idx, out_score
+
+
+def indexer_group_bank(q, k, w, qbar, wbar, q_pos0, G, P, topk=2048, q_scale=None, k_scale=None,
+                       qbar_scale=None, flags=0, want_score=True, want_bank=False, out_idx=None,
+                       out_score=None, out_bank=None, ws=None):
+    """ADIndex bank sharing (Eq. (8), (13), (14)); returns (idx, score or None, bank or None)."""
+    dev = _dev(q, k, w, qbar, wbar, q_scale, k_scale, qbar_scale, out_idx, out_score, out_bank, ws)
+    Tq, H, d = q.shape
+    Tk = k.shape[0]
+    Hs = qbar.shape[1]
+    dt = _dtype(q)
+    NG = -(-Tq // G)
+    if out_idx is None:
+        out_idx = torch.empty((Tq, topk), dtype=torch.int32, device=dev)
+    if want_score and out_score is None:
+        out_score = torch.empty((Tq, topk), dtype=torch.float32, device=dev)
+    if want_bank and out_bank is None:
+        out_bank = torch.empty((NG, P), dtype=torch.int32, device=dev)
+    ws = _ws(workspace_group_bank(Tq, Tk, H, Hs, d, G, P, topk, dt), dev, ws)
+    rc = lib().indexer_group_bank(_ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(w), dt, Tq, Tk, H, d,
+                                  q_pos0, _ptr(qbar), _ptr(qbar_scale), _ptr(wbar), Hs, G, P, topk, flags,
+                                  _ptr(out_idx), _ptr(out_bank), _ptr(out_score), _ptr(ws),
+                                  0 if ws is None else ws.numel(), _stream(dev))
+    _check(rc, "indexer_group_bank")
+    return out_idx, out_score, out_bank

@@ -1,0 +1,54 @@
+"""ctypes view of libdsaidx.so (the C ABI of include/dsa_indexer.h)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdsaidx.so")
+
+DSAIDX_OK = 0
+DSAIDX_ERR_INVALID_ARG = -1
+DSAIDX_ERR_UNSUPPORTED = -2
+DSAIDX_ERR_WORKSPACE = -3
+DSAIDX_ERR_HIP = -4
+DSAIDX_BF16 = 1
+DSAIDX_FP8_E4M3 = 2
+DSAIDX_FORCE_BANK = 1
+
+# exported symbol -> (restype, argtypes)
+_P, _I, _I64, _U, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint, ctypes.c_size_t
+SIGNATURES = {
+    "indexer_prefill": (_I, [_P, _P, _P, _P, _P, _I, _I64, _I64, _I, _I, _I64, _I, _P, _P, _P, _SZ, _P]),
+    "indexer_prefill_workspace_size": (_SZ, [_I64, _I64, _I, _I, _I, _I]),
+    "indexer_decode": (_I, [_P, _P, _P, _P, _P, _I, _I64, _I, _I, _I, _P, _P, _P, _SZ, _P]),
+    "indexer_decode_workspace_size": (_SZ, [_I, _I64, _I, _I, _I]),
+    "indexer_group_bank": (_I, [_P, _P, _P, _P, _P, _I, _I64, _I64, _I, _I, _I64, _P, _P, _P, _I, _I, _I,
+                                _I, _U, _P, _P, _P, _P, _SZ, _P]),
+    "indexer_group_bank_workspace_size": (_SZ, [_I64, _I64, _I, _I, _I, _I, _I, _I, _I]),
+    "indexer_group_bank_pairs": (_I64, [_I64, _I64, _I, _I, _U]),
+    "indexer_last_error": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the in-tree library; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it first (python -m sparse_attention_indexer_dsa_amd.build "
+                "or __graft_entry__.build()); there is no fallback path")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().indexer_last_error().decode()

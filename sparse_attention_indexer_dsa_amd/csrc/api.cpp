@@ -1,0 +1,395 @@
+// api.cpp -- the C ABI of libdsaidx.so (declared in include/dsa_indexer.h):
+// host-side validation, workspace layout and kernel dispatch.  Every argument
+// error is caught here, before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/dsa_indexer.h"
+#include "launch.h"
+
+using namespace dsaidx;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return DSAIDX_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(DSAIDX_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kMaxTopK = 2048;
+constexpr int kMaxBank = 16384;
+constexpr int kMaxHeads = 64;
+// Rows per launch of the streaming kernel: bounds the candidate workspace.
+constexpr int64_t kRowsPerLaunch = 16384;
+constexpr int64_t kAnchorsPerLaunch = 4096;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Candidate-buffer entries per row: room for K survivors plus 2048+K new
+// arrivals between compactions (a multiple of 64).
+int cap_for(int K) { return (2 * K + 2048 + 63) / 64 * 64; }
+
+size_t cand_bytes(int64_t rows, int K) {
+  return 2 * align_up((size_t)rows * (size_t)cap_for(K) * 4u);
+}
+
+int row_bytes(int dtype, int d) { return dtype == DSAIDX_BF16 ? 2 * d : d; }
+
+int check_shape(int dtype, int H, int d, int topk) {
+  if (dtype != DSAIDX_BF16 && dtype != DSAIDX_FP8_E4M3)
+    return fail(DSAIDX_ERR_INVALID_ARG, "dtype %d is not DSAIDX_BF16 or DSAIDX_FP8_E4M3", dtype);
+  if (H < 1) return fail(DSAIDX_ERR_INVALID_ARG, "H = %d must be positive", H);
+  if (H > kMaxHeads) return fail(DSAIDX_ERR_UNSUPPORTED, "H = %d above %d", H, kMaxHeads);
+  if (d <= 0) return fail(DSAIDX_ERR_INVALID_ARG, "d = %d must be positive", d);
+  const bool d_ok = dtype == DSAIDX_BF16 ? (d == 32 || d == 64 || d == 128) : (d == 64 || d == 128);
+  if (!d_ok) return fail(DSAIDX_ERR_UNSUPPORTED, "d = %d unsupported for this dtype", d);
+  if (topk < 1) return fail(DSAIDX_ERR_INVALID_ARG, "topk = %d must be positive", topk);
+  if (topk > kMaxTopK) return fail(DSAIDX_ERR_UNSUPPORTED, "topk = %d above %d", topk, kMaxTopK);
+  return DSAIDX_OK;
+}
+
+int check_prefill_common(const void* q, const float* q_scale, const void* k, const float* k_scale,
+                         const float* w, int dtype, int64_t Tq, int64_t Tk, int H, int d,
+                         int64_t q_pos0, int topk, const int32_t* out_idx, const float* out_score) {
+  int rc = check_shape(dtype, H, d, topk);
+  if (rc) return rc;
+  if (Tq < 0 || Tk < 0 || q_pos0 < 0)
+    return fail(DSAIDX_ERR_INVALID_ARG, "negative size (Tq=%lld Tk=%lld q_pos0=%lld)",
+                (long long)Tq, (long long)Tk, (long long)q_pos0);
+  if (q_pos0 + Tq > Tk)
+    return fail(DSAIDX_ERR_INVALID_ARG, "q_pos0 + Tq = %lld exceeds Tk = %lld",
+                (long long)(q_pos0 + Tq), (long long)Tk);
+  if (Tk > INT32_MAX) return fail(DSAIDX_ERR_UNSUPPORTED, "Tk above INT32_MAX");
+  if (Tq > 0 && (!q || !k || !w || !out_idx))
+    return fail(DSAIDX_ERR_INVALID_ARG, "null q, k, w or out_idx");
+  const bool fp8 = dtype == DSAIDX_FP8_E4M3;
+  if (Tq > 0 && fp8 && (!q_scale || !k_scale))
+    return fail(DSAIDX_ERR_INVALID_ARG, "fp8 inputs need q_scale and k_scale");
+  if (!fp8 && (q_scale || k_scale))
+    return fail(DSAIDX_ERR_INVALID_ARG, "bf16 inputs take no scales (pass NULL)");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(w) || !aligned16(out_idx) ||
+      !aligned16(out_score))
+    return fail(DSAIDX_ERR_INVALID_ARG, "q, k, w and outputs must be 16-byte aligned");
+  if (((uintptr_t)q_scale & 3u) || ((uintptr_t)k_scale & 3u))
+    return fail(DSAIDX_ERR_INVALID_ARG, "scales must be 4-byte aligned");
+  return DSAIDX_OK;
+}
+
+int check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return DSAIDX_OK;
+  if (!ws) return fail(DSAIDX_ERR_WORKSPACE, "null workspace (%zu bytes needed)", need);
+  if (!aligned16(ws)) return fail(DSAIDX_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (ws_bytes < need)
+    return fail(DSAIDX_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+  return DSAIDX_OK;
+}
+
+// Dense rows [r0, r1) of a prefill-shaped call, sliced into launches.
+hipError_t run_dense(const void* q, const float* q_scale, const void* k, const float* k_scale,
+                     const float* w, int dtype, int H, int d, int64_t q_pos0, int64_t r0,
+                     int64_t r1, int topk, int32_t* out_idx, float* out_score, void* ws,
+                     hipStream_t stream) {
+  const int rb = row_bytes(dtype, d);
+  const int cap = cap_for(topk);
+  for (int64_t s = r0; s < r1; s += kRowsPerLaunch) {
+    const int64_t n = r1 - s < kRowsPerLaunch ? r1 - s : kRowsPerLaunch;
+    ScanArgs a{};
+    a.q = (const uint8_t*)q + s * H * (int64_t)rb;
+    a.q_scale = q_scale ? q_scale + s : nullptr;
+    a.w = w + s * H;
+    a.k = k;
+    a.k_scale = k_scale;
+    a.H = H;
+    a.d = d;
+    a.nq = n;
+    a.pos0 = q_pos0 + s;
+    a.pos_stride = 1;
+    a.bank = nullptr;
+    a.K = topk;
+    a.cap = cap;
+    a.cand_key = (uint32_t*)ws;
+    a.cand_idx = (int32_t*)((uint8_t*)ws + align_up((size_t)n * cap * 4u));
+    a.out_idx = out_idx + s * topk;
+    a.out_score = out_score ? out_score + s * topk : nullptr;
+    a.out_stride = topk;
+    hipError_t e = launch_scan_topk(a, dtype, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+struct GroupPlan {
+  int64_t NG, nfull, g0;  // groups; complete groups; first bank group
+};
+
+GroupPlan plan_groups(int64_t Tq, int64_t q_pos0, int G, int P, unsigned flags) {
+  GroupPlan p;
+  p.NG = (Tq + G - 1) / G;
+  p.nfull = Tq / G;
+  if (flags & DSAIDX_FORCE_BANK) {
+    p.g0 = 0;
+  } else {
+    // smallest g with anchor q_pos0 + gG seeing more than P keys
+    const int64_t need = (int64_t)P - q_pos0;  // gG >= need  <=>  anchor + 1 > P
+    p.g0 = need <= 0 ? 0 : (need + G - 1) / G;
+  }
+  if (p.g0 > p.nfull) p.g0 = p.nfull;
+  return p;
+}
+
+size_t group_ws_bytes(int64_t Tq, int G, int P, int topk, unsigned flags, int64_t q_pos0,
+                      bool bank_in_ws) {
+  const GroupPlan p = plan_groups(Tq, q_pos0, G, P, flags);
+  const int64_t nelig = p.nfull - p.g0;
+  size_t bank = bank_in_ws ? align_up((size_t)(nelig > 0 ? nelig : 0) * P * 4u) : 0;
+  const int64_t anchors = nelig < kAnchorsPerLaunch ? nelig : kAnchorsPerLaunch;
+  const int64_t rows = Tq < kRowsPerLaunch ? Tq : kRowsPerLaunch;
+  size_t scan = anchors > 0 ? cand_bytes(anchors, P) : 0;
+  size_t refine = rows > 0 ? cand_bytes(rows, topk) : 0;
+  return bank + (scan > refine ? scan : refine);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* indexer_last_error(void) { return g_last_error.c_str(); }
+
+size_t indexer_prefill_workspace_size(int64_t Tq, int64_t Tk, int H, int d, int topk, int dtype) {
+  (void)Tk; (void)H; (void)d; (void)dtype;
+  if (Tq <= 0 || topk <= 0) return 0;
+  const int64_t rows = Tq < kRowsPerLaunch ? Tq : kRowsPerLaunch;
+  return cand_bytes(rows, topk);
+}
+
+int indexer_prefill(const void* q, const float* q_scale, const void* k, const float* k_scale,
+                    const float* w, int dtype, int64_t Tq, int64_t Tk, int H, int d,
+                    int64_t q_pos0, int topk, int32_t* out_idx, float* out_score, void* ws,
+                    size_t ws_bytes, void* stream) {
+  int rc = check_prefill_common(q, q_scale, k, k_scale, w, dtype, Tq, Tk, H, d, q_pos0, topk,
+                                out_idx, out_score);
+  if (rc) return rc;
+  rc = check_ws(ws, ws_bytes, indexer_prefill_workspace_size(Tq, Tk, H, d, topk, dtype));
+  if (rc) return rc;
+  if (Tq == 0) return ok();
+  hipError_t e = run_dense(q, q_scale, k, k_scale, w, dtype, H, d, q_pos0, 0, Tq, topk, out_idx,
+                           out_score, ws, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "indexer_prefill launch");
+  return ok();
+}
+
+size_t indexer_decode_workspace_size(int B, int64_t Nmax, int H, int d, int topk) {
+  (void)H; (void)d; (void)topk;
+  if (B <= 0 || Nmax <= 0) return 0;
+  const int64_t ld = (Nmax + 63) / 64 * 64;
+  return align_up((size_t)B * (size_t)ld * 4u);
+}
+
+int indexer_decode(const void* q, const uint8_t* k_cache, const float* k_scale, const float* w,
+                   const int32_t* seq_lens, int B, int64_t Nmax, int H, int d, int topk,
+                   int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_shape(DSAIDX_FP8_E4M3, H, d, topk);
+  if (rc) return rc;
+  if (B < 0 || Nmax < 0)
+    return fail(DSAIDX_ERR_INVALID_ARG, "negative size (B=%d Nmax=%lld)", B, (long long)Nmax);
+  if (Nmax > INT32_MAX) return fail(DSAIDX_ERR_UNSUPPORTED, "Nmax above INT32_MAX");
+  if (B > 0 && (!q || !k_cache || !k_scale || !w || !seq_lens || !out_idx))
+    return fail(DSAIDX_ERR_INVALID_ARG, "null q, k_cache, k_scale, w, seq_lens or out_idx");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(w) || !aligned16(out_idx) ||
+      !aligned16(out_score))
+    return fail(DSAIDX_ERR_INVALID_ARG, "q, k_cache, w and outputs must be 16-byte aligned");
+  if (((uintptr_t)k_scale & 3u) || ((uintptr_t)seq_lens & 3u))
+    return fail(DSAIDX_ERR_INVALID_ARG, "k_scale and seq_lens must be 4-byte aligned");
+  rc = check_ws(ws, ws_bytes, indexer_decode_workspace_size(B, Nmax, H, d, topk));
+  if (rc) return rc;
+  if (B == 0) return ok();
+  DecodeArgs a{};
+  a.q = q;
+  a.kc = k_cache;
+  a.k_scale = k_scale;
+  a.w = w;
+  a.seq_lens = seq_lens;
+  a.B = B;
+  a.H = H;
+  a.d = d;
+  a.Nmax = Nmax;
+  a.K = topk;
+  a.logits = (float*)ws;
+  a.ld = (Nmax + 63) / 64 * 64;
+  a.out_idx = out_idx;
+  a.out_score = out_score;
+  hipError_t e = launch_decode(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "indexer_decode launch");
+  return ok();
+}
+
+int64_t indexer_group_bank_pairs(int64_t Tq, int64_t q_pos0, int G, int P, unsigned flags) {
+  if (Tq < 0 || q_pos0 < 0 || G <= 0 || P <= 0) return -1;
+  const GroupPlan p = plan_groups(Tq, q_pos0, G, P, flags);
+  int64_t pairs = 0;
+  // original indexer rows: [0, g0*G) and [nfull*G, Tq); row i scores q_pos0+i+1 keys
+  auto tri = [&](int64_t r0, int64_t r1) {
+    for (int64_t i = r0; i < r1; ++i) pairs += q_pos0 + i + 1;
+  };
+  tri(0, p.g0 * G);
+  tri(p.nfull * G, Tq);
+  for (int64_t g = p.g0; g < p.nfull; ++g) {
+    const int64_t anchor = q_pos0 + g * G;
+    const int64_t nb = anchor + 1 < P ? anchor + 1 : P;
+    pairs += anchor + 1 + (int64_t)G * nb + (int64_t)G * (G - 1) / 2;
+  }
+  return pairs;
+}
+
+size_t indexer_group_bank_workspace_size(int64_t Tq, int64_t Tk, int H, int Hs, int d, int G,
+                                         int P, int topk, int dtype) {
+  (void)Tk; (void)H; (void)Hs; (void)d; (void)dtype;
+  if (Tq <= 0 || G <= 0 || P <= 0 || topk <= 0) return 0;
+  // sized for the worst case: a bank for every complete group, kept in ws
+  return group_ws_bytes(Tq, G, P, topk, DSAIDX_FORCE_BANK, 0, true);
+}
+
+int indexer_group_bank(const void* q, const float* q_scale, const void* k, const float* k_scale,
+                       const float* w, int dtype, int64_t Tq, int64_t Tk, int H, int d,
+                       int64_t q_pos0, const void* qbar, const float* qbar_scale,
+                       const float* wbar, int Hs, int G, int P, int topk, unsigned flags,
+                       int32_t* out_idx, int32_t* out_bank, float* out_score, void* ws,
+                       size_t ws_bytes, void* stream) {
+  int rc = check_prefill_common(q, q_scale, k, k_scale, w, dtype, Tq, Tk, H, d, q_pos0, topk,
+                                out_idx, out_score);
+  if (rc) return rc;
+  if (G != 4 && G != 8 && G != 16)
+    return fail(DSAIDX_ERR_UNSUPPORTED, "group size G = %d not in {4, 8, 16}", G);
+  if (P < topk) return fail(DSAIDX_ERR_INVALID_ARG, "bank size P = %d below topk = %d", P, topk);
+  if (P > kMaxBank) return fail(DSAIDX_ERR_UNSUPPORTED, "bank size P = %d above %d", P, kMaxBank);
+  if (Hs < 1) return fail(DSAIDX_ERR_INVALID_ARG, "Hs = %d must be positive", Hs);
+  if (Hs > kMaxHeads) return fail(DSAIDX_ERR_UNSUPPORTED, "Hs = %d above %d", Hs, kMaxHeads);
+  if (q_pos0 % G) return fail(DSAIDX_ERR_INVALID_ARG, "q_pos0 must be a multiple of G");
+  if (flags & ~(unsigned)DSAIDX_FORCE_BANK)
+    return fail(DSAIDX_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  const bool fp8 = dtype == DSAIDX_FP8_E4M3;
+  if (Tq > 0 && (!qbar || !wbar)) return fail(DSAIDX_ERR_INVALID_ARG, "null qbar or wbar");
+  if (Tq > 0 && fp8 && !qbar_scale)
+    return fail(DSAIDX_ERR_INVALID_ARG, "fp8 inputs need qbar_scale");
+  if (!fp8 && qbar_scale) return fail(DSAIDX_ERR_INVALID_ARG, "bf16 qbar takes no scale");
+  if (!aligned16(qbar) || !aligned16(wbar) || !aligned16(out_bank))
+    return fail(DSAIDX_ERR_INVALID_ARG, "qbar, wbar and out_bank must be 16-byte aligned");
+  if ((uintptr_t)qbar_scale & 3u) return fail(DSAIDX_ERR_INVALID_ARG, "qbar_scale misaligned");
+  rc = check_ws(ws, ws_bytes, group_ws_bytes(Tq, G, P, topk, flags, q_pos0, out_bank == nullptr));
+  if (rc) return rc;
+  if (Tq == 0) return ok();
+
+  hipStream_t st = (hipStream_t)stream;
+  const GroupPlan p = plan_groups(Tq, q_pos0, G, P, flags);
+  const int64_t nelig = p.nfull - p.g0;
+  const int rb = row_bytes(dtype, d);
+  int32_t* bank;
+  void* cand_ws;
+  if (out_bank) {
+    bank = out_bank + p.g0 * (int64_t)P;
+    cand_ws = ws;
+    hipError_t e = launch_fill_i32(out_bank, p.g0 * (int64_t)P, -1, st);
+    if (e == hipSuccess)
+      e = launch_fill_i32(out_bank + p.nfull * (int64_t)P, (p.NG - p.nfull) * (int64_t)P, -1, st);
+    if (e != hipSuccess) return hip_fail(e, "indexer_group_bank bank fill");
+  } else {
+    bank = (int32_t*)ws;
+    cand_ws = (uint8_t*)ws + align_up((size_t)(nelig > 0 ? nelig : 0) * P * 4u);
+  }
+
+  // 1. original indexer for the rows whose groups build no bank
+  hipError_t e = run_dense(q, q_scale, k, k_scale, w, dtype, H, d, q_pos0, 0, p.g0 * G, topk,
+                           out_idx, out_score, cand_ws, st);
+  if (e == hipSuccess)
+    e = run_dense(q, q_scale, k, k_scale, w, dtype, H, d, q_pos0, p.nfull * G, Tq, topk, out_idx,
+                  out_score, cand_ws, st);
+  if (e != hipSuccess) return hip_fail(e, "indexer_group_bank fallback launch");
+
+  // 2. group scan: each bank group's anchor scores its prefix with the group
+  //    indexer and keeps the top P (Eq. (8), (13))
+  const int capP = cap_for(P);
+  for (int64_t s = 0; s < nelig; s += kAnchorsPerLaunch) {
+    const int64_t n = nelig - s < kAnchorsPerLaunch ? nelig - s : kAnchorsPerLaunch;
+    const int64_t g = p.g0 + s;
+    ScanArgs a{};
+    a.q = (const uint8_t*)qbar + g * Hs * (int64_t)rb;
+    a.q_scale = qbar_scale ? qbar_scale + g : nullptr;
+    a.w = wbar + g * Hs;
+    a.k = k;
+    a.k_scale = k_scale;
+    a.H = Hs;
+    a.d = d;
+    a.nq = n;
+    a.pos0 = q_pos0 + g * G;
+    a.pos_stride = G;
+    a.bank = nullptr;
+    a.K = P;
+    a.cap = capP;
+    a.cand_key = (uint32_t*)cand_ws;
+    a.cand_idx = (int32_t*)((uint8_t*)cand_ws + align_up((size_t)n * capP * 4u));
+    a.out_idx = bank + s * (int64_t)P;
+    a.out_score = nullptr;
+    a.out_stride = P;
+    e = launch_scan_topk(a, dtype, st);
+    if (e != hipSuccess) return hip_fail(e, "indexer_group_bank group scan launch");
+  }
+
+  // 3. refinement: every member of a bank group scores bank U {t+1..i} with the
+  //    original indexer and keeps its top K (Eq. (14))
+  const int cap = cap_for(topk);
+  const int64_t groups_per_launch = kRowsPerLaunch / G;
+  for (int64_t s = 0; s < nelig; s += groups_per_launch) {
+    const int64_t ng = nelig - s < groups_per_launch ? nelig - s : groups_per_launch;
+    const int64_t r0 = (p.g0 + s) * G;  // first row of the launch
+    const int64_t n = ng * G;
+    ScanArgs a{};
+    a.q = (const uint8_t*)q + r0 * H * (int64_t)rb;
+    a.q_scale = q_scale ? q_scale + r0 : nullptr;
+    a.w = w + r0 * H;
+    a.k = k;
+    a.k_scale = k_scale;
+    a.H = H;
+    a.d = d;
+    a.nq = n;
+    a.pos0 = q_pos0 + r0;
+    a.pos_stride = 1;
+    a.bank = bank + s * (int64_t)P;
+    a.bank_stride = P;
+    a.group = G;
+    a.K = topk;
+    a.cap = cap;
+    a.cand_key = (uint32_t*)cand_ws;
+    a.cand_idx = (int32_t*)((uint8_t*)cand_ws + align_up((size_t)n * cap * 4u));
+    a.out_idx = out_idx + r0 * topk;
+    a.out_score = out_score ? out_score + r0 * topk : nullptr;
+    a.out_stride = topk;
+    e = launch_scan_topk(a, dtype, st);
+    if (e != hipSuccess) return hip_fail(e, "indexer_group_bank refine launch");
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// launch.h -- host-side launchers of the indexer kernels (internal to libdsaidx).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsaidx {
+
+// One launch of the streaming score + top-K kernel over `nq` query rows.
+// Row j sits at position pos0 + j * pos_stride.  With bank == nullptr the
+// candidates of row j are keys 0 .. its position; otherwise the launch's rows
+// form consecutive groups of `group` (nq a multiple of 4 and of group) and the
+// candidates of row j are its group's bank (bank + g * bank_stride, the first
+// min(bank_stride, anchor+1) entries, ascending) followed by anchor+1 .. its
+// position, where anchor = pos0 + g * group.
+struct ScanArgs {
+  const void* q;         // [nq, H, d] bf16 or E4M3
+  const float* q_scale;  // [nq] (E4M3) or nullptr
+  const float* w;        // [nq, H]
+  const void* k;         // [Tk, d]
+  const float* k_scale;  // [Tk] (E4M3) or nullptr
+  int H, d;
+  int64_t nq, pos0;
+  int pos_stride;
+  const int32_t* bank;
+  int bank_stride, group;
+  int K, cap;              // top-K; candidate-buffer entries per row (>= K + 64)
+  uint32_t* cand_key;      // [nq, cap] workspace
+  int32_t* cand_idx;       // [nq, cap] workspace
+  int32_t* out_idx;        // [nq, out_stride]
+  float* out_score;        // [nq, out_stride] or nullptr
+  int out_stride;
+};
+
+hipError_t launch_scan_topk(const ScanArgs& a, int dtype, hipStream_t stream);
+
+// Decode: scores of one bf16 query per sequence against its E4M3 cache,
+// written to logits [B, Nmax] (fp32), then a per-row top-K.
+struct DecodeArgs {
+  const void* q;          // [B, H, d] bf16
+  const uint8_t* kc;      // [B, Nmax, d] E4M3
+  const float* k_scale;   // [B, Nmax]
+  const float* w;         // [B, H]
+  const int32_t* seq_lens;  // [B]
+  int B, H, d;
+  int64_t Nmax;
+  int K;
+  float* logits;          // [B, ld] workspace, ld >= Nmax and a multiple of 4
+  int64_t ld;
+  int32_t* out_idx;       // [B, K]
+  float* out_score;       // [B, K] or nullptr
+};
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+// Fill n int32 values with v (a kernel, not a memset node).
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t stream);
+
+}  // namespace dsaidx

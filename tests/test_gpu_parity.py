@@ -1,0 +1,268 @@
+"""GPU parity at sizes the oracle finishes in seconds: several 32-key tiles, ragged
+tails, compaction of the candidate buffer, edge cases.  Every call goes through
+the C ABI of libdsaidx.so (via the ctypes binding)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.parity import compare
+from workloads import make_decode, make_group_bank, make_prefill
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_attention_indexer_dsa_amd as m
+    m.lib()  # raises if the library is not built
+    return m
+
+
+def _np(t):
+    return t.cpu().numpy()
+
+
+def _rows(Tq, n=48, seed=0):
+    """Sampled query rows: the first and last few, plus random ones."""
+    if Tq <= n:
+        return np.arange(Tq)
+    rng = np.random.default_rng(seed)
+    head = np.arange(min(4, Tq))
+    tail = np.arange(Tq - 4, Tq)
+    mid = rng.choice(Tq, n - 8, replace=False)
+    return np.unique(np.concatenate([head, mid, tail]))
+
+
+def _prefill_check(dsa, wl, rows=None, exact=None, topk=None, chunk=None):
+    p = wl.params
+    K = topk or p["topk"]
+    dt = wl.dtype
+    dev = "cuda"
+    t = {k: v.to(dev) for k, v in wl.tensors.items()}
+    q_pos0 = p["q_pos0"]
+    Tq = p["Tq"]
+    if chunk is None:
+        gi, gs = dsa.indexer_prefill(t["q"], t["k"], t["w"], q_pos0, K, t.get("q_scale"), t.get("k_scale"))
+    else:
+        gi = torch.empty((Tq, K), dtype=torch.int32, device=dev)
+        gs = torch.empty((Tq, K), dtype=torch.float32, device=dev)
+        for c0 in range(0, Tq, chunk):
+            c1 = min(Tq, c0 + chunk)
+            Tk = q_pos0 + c1
+            dsa.indexer_prefill(t["q"][c0:c1], t["k"][:Tk], t["w"][c0:c1], q_pos0 + c0, K,
+                                None if "q_scale" not in t else t["q_scale"][c0:c1],
+                                None if "k_scale" not in t else t["k_scale"][:Tk],
+                                out_idx=gi[c0:c1], out_score=gs[c0:c1])
+    torch.cuda.synchronize()
+    rows = np.arange(Tq) if rows is None else np.asarray(rows)
+    ri, rs = oracle.prefill(wl["q"], wl["k"], wl["w"], dt, q_pos0, K, wl.tensors.get("q_scale"),
+                            wl.tensors.get("k_scale"), rows=rows)
+    exact = (p["dist"] == "int") if exact is None else exact
+
+    def score_of(r, keys):
+        return oracle.score_pairs(wl["q"], wl["k"], wl["w"], np.full(len(keys), rows[r]), keys, dt, dt,
+                                  wl.tensors.get("q_scale"), wl.tensors.get("k_scale"))
+    compare(_np(gi)[rows], _np(gs)[rows], ri, rs, exact, score_of)
+    return gi, gs
+
+
+def test_config1_tiny_exact(dsa):
+    """T=1024, H=4, d=32, K=64, integer inputs: every row bit-exact."""
+    wl = make_prefill(T=1024, H=4, d=32, topk=64, dtype="bf16", dist="int", seed=0, w_lo=0, w_hi=3)
+    _prefill_check(dsa, wl)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_h64_integer_exact(dsa, dtype):
+    """64 heads, d=128, signed integer q, k, w: ties everywhere, sums exact."""
+    wl = make_prefill(T=1123, H=64, d=128, topk=100, dtype=dtype, dist="int", seed=1)
+    _prefill_check(dsa, wl, rows=_rows(1123, 40, 1))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_h64_random_tolerance(dsa, dtype):
+    wl = make_prefill(T=1500, H=64, d=128, topk=256, dtype=dtype, dist="normal", seed=2, Tq=700)
+    _prefill_check(dsa, wl, rows=_rows(700, 40, 2))
+
+
+@pytest.mark.parametrize("H,d,K,T", [(1, 32, 1, 5), (5, 64, 7, 333), (33, 32, 64, 97), (64, 64, 2048, 150),
+                                     (17, 128, 33, 1), (2, 32, 64, 2)])
+def test_shapes_exact(dsa, H, d, K, T):
+    wl = make_prefill(T=T, H=H, d=d, topk=K, dtype="bf16", dist="int", seed=H * 7 + d)
+    _prefill_check(dsa, wl, rows=_rows(T, 40, 3))
+
+
+def test_fp8_shapes_exact(dsa):
+    wl = make_prefill(T=260, H=20, d=64, topk=50, dtype="fp8", dist="int", seed=4)
+    _prefill_check(dsa, wl)
+
+
+def test_zero_and_negative_weights(dsa):
+    """w = -0: all scores are zero and rank by index; negative w makes many -0
+    products that must rank as +0."""
+    wl = make_prefill(T=400, H=8, d=32, topk=64, dtype="bf16", dist="int", seed=5)
+    wl.tensors["w"] = -torch.zeros_like(wl["w"])
+    gi, gs = _prefill_check(dsa, wl)
+    assert (_np(gi)[399] == np.arange(64)).all()
+    wl2 = make_prefill(T=400, H=8, d=32, topk=64, dtype="bf16", dist="int", seed=6, w_lo=-3, w_hi=0)
+    _prefill_check(dsa, wl2)
+
+
+def test_compaction_many_rounds(dsa):
+    """Small K over a long prefix: the candidate buffer fills and compacts many
+    times; increasing scores (every key beats the threshold) plus ties."""
+    T, d, K = 6000, 32, 16
+    q = torch.ones((T, 1, d), dtype=torch.float32)
+    s = torch.arange(T)
+    k = torch.zeros((T, d), dtype=torch.float32)
+    k[s, s % d] = (s // 24 + 1).clamp(max=250).float()  # non-decreasing with long tie runs
+    wl = make_prefill(T=T, H=1, d=d, topk=K, dtype="bf16", dist="int", seed=7)
+    wl.tensors.update(q=q.to(torch.bfloat16), k=k.to(torch.bfloat16), w=torch.ones((T, 1)))
+    _prefill_check(dsa, wl, rows=_rows(T, 40, 7), exact=True)
+    # random integer data, K small: several compactions at realistic rates
+    wl2 = make_prefill(T=5000, H=16, d=64, topk=24, dtype="bf16", dist="int", seed=8)
+    _prefill_check(dsa, wl2, rows=_rows(5000, 40, 8))
+
+
+def test_chunked_equals_unchunked(dsa):
+    wl = make_prefill(T=2100, H=64, d=128, topk=128, dtype="bf16", dist="normal", seed=9)
+    gi, gs = _prefill_check(dsa, wl, rows=_rows(2100, 24, 9))
+    ci, cs = _prefill_check(dsa, wl, rows=_rows(2100, 24, 10), chunk=512)
+    assert torch.equal(gi, ci) and torch.equal(gs, cs)
+
+
+def test_deterministic(dsa):
+    wl = make_prefill(T=1800, H=64, d=128, topk=512, dtype="fp8", dist="normal", seed=10)
+    t = {k: v.cuda() for k, v in wl.tensors.items()}
+    a = dsa.indexer_prefill(t["q"], t["k"], t["w"], 0, 512, t["q_scale"], t["k_scale"])
+    b = dsa.indexer_prefill(t["q"], t["k"], t["w"], 0, 512, t["q_scale"], t["k_scale"])
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_empty_query_set(dsa):
+    wl = make_prefill(T=10, H=4, d=32, topk=4, dtype="bf16", dist="int", seed=11)
+    t = {k: v.cuda() for k, v in wl.tensors.items()}
+    gi, gs = dsa.indexer_prefill(t["q"][:0], t["k"], t["w"][:0], 0, 4)
+    assert gi.shape == (0, 4)
+
+
+# ------------------------------------------------------------------- decode
+
+def _decode_check(dsa, wl, rows=None, exact=None):
+    p = wl.params
+    t = {k: v.cuda() for k, v in wl.tensors.items()}
+    gi, gs = dsa.indexer_decode(t["q"], t["k_cache"], t["k_scale"], t["w"], t["seq_lens"], p["topk"])
+    torch.cuda.synchronize()
+    B, N = p["B"], p["N"]
+    rows = np.arange(B) if rows is None else np.asarray(rows)
+    ri, rs = oracle.decode(wl["q"], wl["k_cache"], wl["k_scale"], wl["w"], wl["seq_lens"], p["topk"], rows=rows)
+    exact = (p["dist"] == "int") if exact is None else exact
+    kc = wl["k_cache"].reshape(B * N, -1)
+    ks = wl["k_scale"].reshape(B * N)
+
+    def score_of(r, keys):
+        b = rows[r]
+        return oracle.score_pairs(wl["q"], kc, wl["w"], np.full(len(keys), b), b * N + keys, "bf16", "fp8",
+                                  None, ks)
+    compare(_np(gi)[rows], _np(gs)[rows], ri, rs, exact, score_of)
+    return gi, gs
+
+
+def test_decode_ragged_exact(dsa):
+    lens = [0, 1, 63, 64, 65, 3000, 2999, 1500]
+    wl = make_decode(B=8, N=3000, H=64, d=128, topk=64, dist="int", seed=12, seq_lens=lens)
+    _decode_check(dsa, wl)
+
+
+def test_decode_random_tolerance(dsa):
+    wl = make_decode(B=4, N=20000, H=64, d=128, topk=2048, dist="normal", seed=13,
+                     seq_lens=[20000, 19999, 2048, 2049])
+    _decode_check(dsa, wl)
+
+
+def test_decode_small_heads(dsa):
+    wl = make_decode(B=3, N=777, H=7, d=64, topk=100, dist="int", seed=14, seq_lens=[777, 100, 99])
+    _decode_check(dsa, wl)
+
+
+# --------------------------------------------------------------- group bank
+
+def _group_check(dsa, wl, flags=0, rows=None, exact=None):
+    p = wl.params
+    G, P, K = p["G"], p["P"], p["topk"]
+    t = {k: v.cuda() for k, v in wl.tensors.items()}
+    gi, gs, gb = dsa.indexer_group_bank(t["q"], t["k"], t["w"], t["qbar"], t["wbar"], p["q_pos0"], G, P, K,
+                                        t.get("q_scale"), t.get("k_scale"), t.get("qbar_scale"), flags=flags,
+                                        want_bank=True)
+    torch.cuda.synchronize()
+    Tq = p["Tq"]
+    rows = np.arange(Tq) if rows is None else np.asarray(rows)
+    ri, rs, rb, pairs = oracle.group_bank(wl["q"], wl["k"], wl["w"], wl["qbar"], wl["wbar"], wl.dtype,
+                                          p["q_pos0"], G, P, K, flags, wl.tensors.get("q_scale"),
+                                          wl.tensors.get("k_scale"), wl.tensors.get("qbar_scale"), rows=rows,
+                                          want_bank=True)
+    exact = (p["dist"] == "int") if exact is None else exact
+    assert pairs == dsa.indexer_group_bank_pairs(Tq, p["q_pos0"], G, P, flags)
+    if exact:
+        assert np.array_equal(_np(gb), rb)
+
+    def score_of(r, keys):
+        return oracle.score_pairs(wl["q"], wl["k"], wl["w"], np.full(len(keys), rows[r]), keys, wl.dtype,
+                                  wl.dtype, wl.tensors.get("q_scale"), wl.tensors.get("k_scale"))
+    if exact:
+        compare(_np(gi)[rows], _np(gs)[rows], ri, rs, True)
+    else:
+        # the bank is itself a top-P selection: compare it under the tolerance
+        # rule of the group score (Eq. (8)), then compare the rows whose bank
+        # is the oracle's bank
+        groups = np.unique(rows // G)
+        gbank = _np(gb)[groups]
+        bscore = np.full(rb[groups].shape, -np.inf)
+        for n, g in enumerate(groups):
+            v = rb[g][rb[g] >= 0]
+            if len(v):
+                bscore[n, :len(v)] = oracle.score_pairs(wl["qbar"], wl["k"], wl["wbar"], np.full(len(v), g), v,
+                                                        wl.dtype, wl.dtype, wl.tensors.get("qbar_scale"),
+                                                        wl.tensors.get("k_scale"))
+
+        def bank_score_of(n, keys):
+            return oracle.score_pairs(wl["qbar"], wl["k"], wl["wbar"], np.full(len(keys), groups[n]), keys,
+                                      wl.dtype, wl.dtype, wl.tensors.get("qbar_scale"), wl.tensors.get("k_scale"))
+        compare(gbank, None, rb[groups], bscore, False, bank_score_of, label="bank")
+        same_bank = np.array([np.array_equal(_np(gb)[r // G], rb[r // G]) for r in rows])
+        assert same_bank.mean() > 0.5
+        sel = np.nonzero(same_bank)[0]
+        compare(_np(gi)[rows][sel], _np(gs)[rows][sel], ri[sel], rs[sel], False,
+                lambda r, keys: score_of(sel[r], keys))
+    return gi, gs, gb
+
+
+@pytest.mark.parametrize("flags", [0, 1])
+def test_group_bank_exact(dsa, flags):
+    """Integer inputs, G=4, P=96, K=40, with fallback groups, bank groups and a
+    trailing incomplete group."""
+    wl = make_group_bank(T=700, H=8, Hs=5, d=32, topk=40, G=4, P=96, dtype="bf16", dist="int", seed=15,
+                         Tq=646, q_pos0=52)
+    _group_check(dsa, wl, flags)
+
+
+@pytest.mark.parametrize("G", [8, 16])
+def test_group_bank_h64_exact(dsa, G):
+    wl = make_group_bank(T=1600, H=64, Hs=64, d=128, topk=128, G=G, P=512, dtype="bf16", dist="int",
+                         seed=16 + G)
+    _group_check(dsa, wl, rows=_rows(1600, 48, G))
+
+
+def test_group_bank_fp8_exact(dsa):
+    wl = make_group_bank(T=900, H=64, Hs=16, d=128, topk=64, G=16, P=256, dtype="fp8", dist="int", seed=18)
+    _group_check(dsa, wl, rows=_rows(900, 48, 18))
+
+
+def test_group_bank_random(dsa):
+    wl = make_group_bank(T=2000, H=64, Hs=64, d=128, topk=256, G=16, P=1024, dtype="bf16", dist="normal",
+                         seed=19)
+    _group_check(dsa, wl, rows=_rows(2000, 48, 19))
