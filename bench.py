@@ -1,0 +1,344 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X DSA lightning indexer (one GPU).
+
+One step is one layer's indexer pass over the long-prefill workload:
+T = 131072 causal tokens, H = 64 indexer heads, d = 128, top-2048, q and k in
+OCP FP8 E4M3 with one fp32 scale per token, processed as 32 query chunks of
+4096 (chunk c: queries 4096c .. 4096c+4095 against keys 0 .. 4096(c+1)-1).
+`value` is its throughput in TFLOP/s (algorithmic flops 2*H*d per scored
+query-key pair, 8,590,000,128 pairs per step).  The same line carries the
+decode workload (32 sequences x 262144 cached E4M3 keys, bf16 queries,
+top-2048) as HBM GB/s, each with its roofline, and the CPU oracle timed on a
+bounded sample of the same inputs.
+
+Inputs are generated on the GPU before timing (resident in HBM); outputs,
+workspace and streams are allocated before the timed region.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--adindex]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "indexer TFLOP/s & Gpairs/s, prefill 128K; decode HBM GB/s at 256K"
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense FP8 MFMA
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense BF16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def _pairs_causal(q0, n):
+    """Scored pairs of n queries at positions q0..q0+n-1 (each sees t+1 keys)."""
+    return n * q0 + n * (n + 1) // 2
+
+
+def _traffic(kernel_key, per_launch_alg):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel_key)
+    except (ValueError, OSError):
+        return None
+    if not rec or rec.get("source_sha1") != _source_sha1():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def _source_sha1():
+    h = hashlib.sha1()
+    csrc = os.path.join(ROOT, "sparse_attention_indexer_dsa_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()
+
+
+def _events_ms(pairs):
+    return [s.elapsed_time(e) for s, e in pairs]
+
+
+# ------------------------------------------------------------------ prefill
+
+def bench_prefill(dsa, args, log):
+    from workloads import make_workload
+    T, H, d, K, chunk = 131072, 64, 128, 2048, 4096
+    log(f"generating prefill inputs T={T} fp8 on the GPU")
+    wl = make_workload(3, seed=args.seed, device="cuda")
+    q, k, w, qs, ks = wl["q"], wl["k"], wl["w"], wl["q_scale"], wl["k_scale"]
+    out = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    ws = torch.empty(dsa.workspace_prefill(chunk, T, H, d, K, dsa.DSAIDX_FP8_E4M3), dtype=torch.uint8,
+                     device="cuda")
+    nchunks = T // chunk
+    stream = torch.cuda.current_stream()
+
+    def step(evs=None):
+        for c in range(nchunks):
+            q0, q1 = c * chunk, (c + 1) * chunk
+            if evs is not None:
+                s, e = evs[c]
+                s.record(stream)
+            dsa.indexer_prefill(q[q0:q1], k[:q1], w[q0:q1], q0, K, qs[q0:q1], ks[:q1], want_score=False,
+                                out_idx=out[q0:q1], ws=ws)
+            if evs is not None:
+                e.record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(nchunks)] for _ in range(args.steps)]
+    log(f"timing {args.steps} prefill steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = np.array([_events_ms(e) for e in evs])  # [steps, chunks]
+    pairs = _pairs_causal(0, T)
+    flops = 2 * H * d * pairs
+    ms_step = wall * 1e3 / args.steps
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    # dominant kernel: one streaming score+top-K launch per chunk
+    kern_s = launch_ms.sum() * 1e-3 / args.steps
+    achieved = flops / kern_s / 1e12
+    res = dict(value=tflops, ms_per_step=ms_step, gpairs_per_s=pairs / (ms_step * 1e-3) / 1e9,
+               pairs_per_step=pairs, flops_per_step=flops,
+               roofline=dict(bound="mfma", kernel="scan_topk_kernel<fp8,2,128>", achieved=achieved,
+                             peak=PEAK_FP8_TFLOPS, unit="TFLOP/s", frac=achieved / PEAK_FP8_TFLOPS,
+                             launches_per_step=nchunks,
+                             avg_launch_ms=float(launch_ms.mean()),
+                             flops_per_launch=flops / nchunks,
+                             traffic=_traffic("scan_topk_fp8_prefill128k", None)))
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_prefill(wl, out, args, log)
+    return res, cpu
+
+
+def cpu_prefill(wl, out, args, log):
+    """The oracle on a stratified sample of query rows of the same workload;
+    the sampled GPU rows are checked against it (tolerance rule)."""
+    import oracle
+    from tests.parity import compare
+    T, K = 131072, 2048
+    n = args.cpu_rows
+    rows = np.unique(np.concatenate([np.linspace(0, T - 1, n - 2).astype(np.int64), [T - 2, T - 1]]))
+    log(f"cpu oracle on {len(rows)} sampled prefill rows")
+    qh = wl["q"].cpu()
+    kh, wh = wl["k"].cpu(), wl["w"].cpu()
+    qsh, ksh = wl["q_scale"].cpu(), wl["k_scale"].cpu()
+    t0 = time.perf_counter()
+    ri, rs = oracle.prefill(qh, kh, wh, "fp8", 0, K, qsh, ksh, rows=rows)
+    dt = time.perf_counter() - t0
+    pairs = int((rows + 1).sum())
+    gi = out[torch.as_tensor(rows, device="cuda")].cpu().numpy()
+
+    def score_of(r, keys):
+        return oracle.score_pairs(qh, kh, wh, np.full(len(keys), rows[r]), keys, "fp8", "fp8", qsh, ksh)
+    parity = "ok"
+    try:
+        compare(gi, None, ri, rs, False, score_of)
+    except AssertionError as e:  # reported, not raised: the bench still prints its line
+        parity = "FAILED: " + str(e)[:300]
+    return dict(value=2 * 64 * 128 * pairs / dt / 1e12, unit="TFLOP/s", gpairs_per_s=pairs / dt / 1e9,
+                cores=oracle.max_threads(), kind="oracle", seconds=dt,
+                sample=f"{len(rows)} query rows of the 128K prefill spread over positions 0..{T - 1} "
+                       f"({pairs} scored pairs), fp64 C oracle with OpenMP over rows",
+                parity_of_sampled_gpu_rows=parity)
+
+
+# ------------------------------------------------------------------- decode
+
+def bench_decode(dsa, args, log):
+    from workloads import make_workload
+    B, N, H, d, K = 32, 262144, 64, 128, 2048
+    log(f"generating decode inputs B={B} N={N} on the GPU")
+    wl = make_workload(4, seed=args.seed, device="cuda")
+    t = wl.tensors
+    out = torch.empty((B, K), dtype=torch.int32, device="cuda")
+    ws = torch.empty(dsa.workspace_decode(B, N, H, d, K), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        dsa.indexer_decode(t["q"], t["k_cache"], t["k_scale"], t["w"], t["seq_lens"], K, want_score=False,
+                           out_idx=out, ws=ws)
+
+    for _ in range(max(args.warmup, 1) * 3):
+        step()
+    torch.cuda.synchronize()
+    nsteps = args.steps * 20  # a decode step is ~0.2 ms: time many
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nsteps)]
+    log(f"timing {nsteps} decode steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s, e in evs:
+        s.record(stream)
+        step()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = np.array(_events_ms(evs))
+    alg_bytes = B * N * d + B * N * 4 + B * H * d * 2 + B * H * 4 + B * K * 4
+    ms_step = wall * 1e3 / nsteps
+    gbs = alg_bytes / (ms_step * 1e-3) / 1e9
+    achieved = alg_bytes / (call_ms.mean() * 1e-3) / 1e9
+    res = dict(workload="decode scan: 32 sequences x 262144 cached keys, E4M3 cache + fp32 per-token scale, "
+                        "bf16 query, H=64, d=128, top-2048",
+               value=gbs, unit="GB/s", ms_per_step=ms_step, steps=nsteps,
+               gpairs_per_s=B * N / (ms_step * 1e-3) / 1e9, bytes_per_step=alg_bytes,
+               roofline=dict(bound="hbm", kernel="decode_scan_kernel + decode_select_kernel (one call)",
+                             achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s", frac=achieved / PEAK_HBM_GBS,
+                             avg_launch_ms=float(call_ms.mean()), bytes_per_launch=alg_bytes,
+                             traffic=_traffic("decode_scan_decode256k", None)))
+    if not args.no_cpu:
+        import oracle
+        from tests.parity import compare
+        rows = np.arange(0, B, max(1, B // args.cpu_decode_rows))[:args.cpu_decode_rows]
+        log(f"cpu oracle on {len(rows)} decode rows")
+        h = {k2: v.cpu() for k2, v in t.items()}
+        t0 = time.perf_counter()
+        ri, rs = oracle.decode(h["q"], h["k_cache"], h["k_scale"], h["w"], h["seq_lens"], K, rows=rows)
+        dt = time.perf_counter() - t0
+        kc = h["k_cache"].reshape(B * N, d)
+        ksc = h["k_scale"].reshape(B * N)
+
+        def score_of(r, keys):
+            return oracle.score_pairs(h["q"], kc, h["w"], np.full(len(keys), rows[r]), rows[r] * N + keys,
+                                      "bf16", "fp8", None, ksc)
+        parity = "ok"
+        try:
+            compare(out.cpu().numpy()[rows], None, ri, rs, False, score_of)
+        except AssertionError as e:
+            parity = "FAILED: " + str(e)[:300]
+        per_row = alg_bytes / B
+        res["cpu_baseline"] = dict(value=per_row * len(rows) / dt / 1e9, unit="GB/s",
+                                   gpairs_per_s=len(rows) * N / dt / 1e9, cores=oracle.max_threads(),
+                                   kind="oracle", seconds=dt,
+                                   sample=f"{len(rows)} of the 32 decode rows (full 262144-key scans)",
+                                   parity_of_sampled_gpu_rows=parity)
+    return res
+
+
+# ------------------------------------------------------------------ ADIndex
+
+def bench_adindex(dsa, args, log):
+    from workloads import make_workload
+    T, H, d, K, G, P = 65536, 64, 128, 2048, 16, 8192
+    log("generating ADIndex inputs T=65536 bf16 on the GPU")
+    wl = make_workload(5, seed=args.seed, device="cuda")
+    t = wl.tensors
+    out = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    ws = torch.empty(dsa.workspace_group_bank(T, T, H, H, d, G, P, K, dsa.DSAIDX_BF16), dtype=torch.uint8,
+                     device="cuda")
+    dense_out = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    wsd = torch.empty(dsa.workspace_prefill(T, T, H, d, K, dsa.DSAIDX_BF16), dtype=torch.uint8, device="cuda")
+
+    def step():
+        dsa.indexer_group_bank(t["q"], t["k"], t["w"], t["qbar"], t["wbar"], 0, G, P, K, want_score=False,
+                               out_idx=out, ws=ws)
+
+    def dense():
+        dsa.indexer_prefill(t["q"], t["k"], t["w"], 0, K, want_score=False, out_idx=dense_out, ws=wsd)
+
+    res = {}
+    for name, fn, steps in (("adindex", step, args.steps), ("dense", dense, max(1, args.steps // 2))):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        res[name] = (time.perf_counter() - t0) * 1e3 / steps
+    pairs = dsa.indexer_group_bank_pairs(T, 0, G, P)
+    flops = 2 * H * d * pairs
+    dense_pairs = _pairs_causal(0, T)
+    # recall of the bank result against the dense top-K (coverage of Section 5)
+    sample = torch.arange(8192, T, 997, device="cuda")
+    a, b = out[sample].cpu().numpy(), dense_out[sample].cpu().numpy()
+    rec = float(np.mean([len(np.intersect1d(x, y)) / len(y) for x, y in zip(a, b)]))
+    return dict(workload="ADIndex group token bank: T=65536, G=16, P=8192, H=Hs=64, d=128, top-2048, bf16",
+                ms_per_step=res["adindex"], tflops=flops / (res["adindex"] * 1e-3) / 1e12,
+                gpairs_per_s=pairs / (res["adindex"] * 1e-3) / 1e9, pairs=pairs,
+                dense_ms=res["dense"], dense_tflops=2 * H * d * dense_pairs / (res["dense"] * 1e-3) / 1e12,
+                speedup_vs_dense=res["dense"] / res["adindex"], scoring_count_ratio=dense_pairs / pairs,
+                recall_vs_dense=rec,
+                roofline=dict(bound="mfma", achieved=flops / (res["adindex"] * 1e-3) / 1e12,
+                              peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                              frac=flops / (res["adindex"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--cpu-decode-rows", type=int, default=32)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--adindex", action="store_true", help="also time the ADIndex group-bank workload")
+    ap.add_argument("--quiet", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the indexer path here runs on a single MI355X "
+              "(see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    def log(msg):
+        if not args.quiet:
+            print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import sparse_attention_indexer_dsa_amd as dsa
+    dsa.lib()
+
+    pre, cpu = bench_prefill(dsa, args, log)
+    line = {
+        "metric": METRIC,
+        "value": pre["value"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pre["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": "long prefill, one layer: T=131072, H_I=64, d=128, top-2048, E4M3 q and k "
+                               "with per-token fp32 scales, w fp32, 32 causal query chunks of 4096",
+                   "T": 131072, "H": 64, "d": 128, "topk": 2048, "chunk": 4096, "seed": args.seed},
+        "gpairs_per_s": pre["gpairs_per_s"],
+        "pairs_per_step": pre["pairs_per_step"],
+        "roofline": pre["roofline"],
+        "cpu_baseline": cpu,
+    }
+    if not args.no_decode:
+        line["decode"] = bench_decode(dsa, args, log)
+    if args.adindex:
+        line["adindex"] = bench_adindex(dsa, args, log)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
