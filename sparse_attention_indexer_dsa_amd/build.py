@@ -10,6 +10,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsaidx.so")
 SOURCES = ["api.cpp", "scan_topk.hip", "decode.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 FLAGS = [
     "--offload-arch=gfx950",
@@ -27,7 +28,7 @@ def build(verbose: bool = False) -> str:
     """Compile every HIP source into libdsaidx.so (always recompiles)."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-o", tmp, *srcs]
+    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, cwd=CSRC, capture_output=True, text=True)

@@ -8,7 +8,7 @@
 #include <cstring>
 #include <string>
 
-#include "../../include/dsa_indexer.h"
+#include "dsa_indexer.h"
 #include "launch.h"
 
 using namespace dsaidx;
@@ -48,8 +48,9 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Candidate-buffer entries per row: room for K survivors plus 2048+K new
-// arrivals between compactions (a multiple of 64).
+// Candidate-buffer entries per row: room for K survivors plus 2048 + K new
+// arrivals between compactions (a multiple of 64, below 65536 for the 16-bit
+// selection histograms).
 int cap_for(int K) { return (2 * K + 2048 + 63) / 64 * 64; }
 
 size_t cand_bytes(int64_t rows, int K) {
@@ -205,7 +206,7 @@ size_t indexer_decode_workspace_size(int B, int64_t Nmax, int H, int d, int topk
   (void)H; (void)d; (void)topk;
   if (B <= 0 || Nmax <= 0) return 0;
   const int64_t ld = (Nmax + 63) / 64 * 64;
-  return align_up((size_t)B * (size_t)ld * 4u);
+  return align_up((size_t)B * (size_t)ld * 4u) + align_up((size_t)B * kDecHistBins * 4u);
 }
 
 int indexer_decode(const void* q, const uint8_t* k_cache, const float* k_scale, const float* w,
@@ -239,6 +240,7 @@ int indexer_decode(const void* q, const uint8_t* k_cache, const float* k_scale, 
   a.K = topk;
   a.logits = (float*)ws;
   a.ld = (Nmax + 63) / 64 * 64;
+  a.hist = (uint32_t*)((uint8_t*)ws + align_up((size_t)B * (size_t)a.ld * 4u));
   a.out_idx = out_idx;
   a.out_score = out_score;
   hipError_t e = launch_decode(a, (hipStream_t)stream);

@@ -28,6 +28,25 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
   return __uint_as_float(u);
 }
 
+// ReLU on the fp32 bit pattern: negative floats are negative as int32 (and
+// -0 is INT_MIN), so one v_max_i32 gives max(x, +0) for every finite x.
+__device__ __forceinline__ float relu_bits(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
+// sum_r w[r] * ReLU(acc[r]) over the 16 accumulators of one 32x32 MFMA tile,
+// added to four independent partial sums (short dependency chains).
+__device__ __forceinline__ void gated_relu_sum16(const float* w, const v16f& acc, float& s0,
+                                                 float& s1, float& s2, float& s3) {
+#pragma unroll
+  for (int r = 0; r < 16; r += 4) {
+    s0 = fmaf(w[r], relu_bits(acc[r]), s0);
+    s1 = fmaf(w[r + 1], relu_bits(acc[r + 1]), s1);
+    s2 = fmaf(w[r + 2], relu_bits(acc[r + 2]), s2);
+    s3 = fmaf(w[r + 3], relu_bits(acc[r + 3]), s3);
+  }
+}
+
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 __device__ __forceinline__ int popc(uint64_t m) { return __popcll(m); }
@@ -60,44 +79,60 @@ __device__ __forceinline__ void wave_mem_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-// One radix digit step of the selection: given the entries whose key matches
+// LDS words of one wave's selection histogram: 2048 16-bit counters, two per
+// word (every candidate buffer holds fewer than 65536 entries).
+constexpr int kSelectHistWords = 1024;
+
+// One radix digit step of the selection over a candidate buffer of raw fp32
+// scores (compared through order_key): given the entries whose key matches
 // `prefix` on `pmask`, histogram digit (key >> shift) & (NBINS-1) into `hist`
-// (NBINS counters in LDS owned by this wave) and find the digit holding the
-// krem-th largest matching entry.  Updates prefix/pmask/krem; wave-uniform.
+// (this wave's kSelectHistWords LDS words, NBINS <= 2048 16-bit counters) and
+// find the digit holding the krem-th largest matching entry.  Updates
+// prefix/pmask/krem; wave-uniform.
 template <int NBINS>
 __device__ __forceinline__ void radix_step(const uint32_t* keys, int n, uint32_t* hist, int shift,
                                            uint32_t& prefix, uint32_t& pmask, int& krem) {
-  constexpr int PER = NBINS / 64;
+  constexpr int PERW = NBINS / 2 / 64;  // words per lane
+  constexpr int PER = 2 * PERW;         // bins per lane
   const int l = lane_id();
-  uint32_t* mine = hist + l * PER;
+  uint32_t* mine = hist + l * PERW;
 #pragma unroll
-  for (int b = 0; b < PER; b += 4) *(u32x4*)(mine + b) = u32x4{0u, 0u, 0u, 0u};
+  for (int b = 0; b < PERW; b += 4) *(u32x4*)(mine + b) = u32x4{0u, 0u, 0u, 0u};
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const uint32_t dmask = NBINS - 1;
+  auto count = [&](uint32_t raw) {
+    const uint32_t k = order_key(__uint_as_float(raw));
+    if ((k & pmask) == prefix) {
+      const uint32_t bin = (k >> shift) & dmask;
+      atomicAdd(hist + (bin >> 1), 1u << ((bin & 1u) * 16u));
+    }
+  };
+  // 16 independent loads in flight per lane: the buffer usually sits in HBM
   int e = l;
-  for (; e + 192 < n; e += 256) {
-    uint32_t k0 = keys[e], k1 = keys[e + 64], k2 = keys[e + 128], k3 = keys[e + 192];
-    if ((k0 & pmask) == prefix) atomicAdd(hist + ((k0 >> shift) & dmask), 1u);
-    if ((k1 & pmask) == prefix) atomicAdd(hist + ((k1 >> shift) & dmask), 1u);
-    if ((k2 & pmask) == prefix) atomicAdd(hist + ((k2 >> shift) & dmask), 1u);
-    if ((k3 & pmask) == prefix) atomicAdd(hist + ((k3 >> shift) & dmask), 1u);
+  for (; e + 15 * 64 < n; e += 16 * 64) {
+    uint32_t k[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) k[u] = keys[e + 64 * u];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) count(k[u]);
   }
-  for (; e < n; e += 64) {
-    uint32_t k0 = keys[e];
-    if ((k0 & pmask) == prefix) atomicAdd(hist + ((k0 >> shift) & dmask), 1u);
-  }
+  for (; e < n; e += 64) count(keys[e]);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   uint32_t c[PER];
   int local = 0;
 #pragma unroll
-  for (int b = 0; b < PER; b += 4) {
+  for (int b = 0; b < PERW; b += 4) {
     u32x4 v = *(const u32x4*)(mine + b);
-    c[b] = v[0]; c[b + 1] = v[1]; c[b + 2] = v[2]; c[b + 3] = v[3];
-    local += (int)(v[0] + v[1] + v[2] + v[3]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      c[2 * (b + q)] = v[q] & 0xFFFFu;
+      c[2 * (b + q) + 1] = v[q] >> 16;
+      local += (int)((v[q] & 0xFFFFu) + (v[q] >> 16));
+    }
   }
   // entries in higher lanes' (higher) bins
   const int incl = wave_incl_scan(local);
@@ -121,12 +156,13 @@ __device__ __forceinline__ void radix_step(const uint32_t* keys, int n, uint32_t
   pmask |= dmask << shift;
 }
 
-// Keep the top K (by key descending, then by buffer position, i.e. ascending
-// key index) of the n > K entries of a wave's candidate buffer, compacting them
-// in place in their original order.  Returns the K-th largest key.
-// `hist` holds 2048 LDS counters for this wave.  All 64 lanes must call it.
-__device__ __forceinline__ uint32_t wave_select_topk(uint32_t* keys, int32_t* idx, int n, int K,
-                                                     uint32_t* hist) {
+// Keep the top K (by score descending, then by buffer position, i.e. ascending
+// key index) of the n > K entries of a wave's candidate buffer (raw fp32 score
+// bits + key indices), compacting them in place in their original order.
+// Returns the K-th largest score.
+// `hist` is this wave's kSelectHistWords LDS words.  All 64 lanes must call it.
+__device__ __forceinline__ float wave_select_topk(uint32_t* keys, int32_t* idx, int n, int K,
+                                                  uint32_t* hist) {
   wave_mem_fence();
   uint32_t prefix = 0, pmask = 0;
   int krem = K;
@@ -137,26 +173,39 @@ __device__ __forceinline__ uint32_t wave_select_topk(uint32_t* keys, int32_t* id
   const int keep_eq = krem;  // entries equal to kth to keep, earliest first
   const int l = lane_id();
   int out = 0, eq_seen = 0;
-  for (int base = 0; base < n; base += 64) {
-    const int e = base + l;
-    const bool in = e < n;
-    uint32_t key = in ? keys[e] : 0u;
-    int32_t id = in ? idx[e] : 0;
-    const bool gt = in && key > kth;
-    const bool eq = in && key == kth;
-    const uint64_t eqm = ballot(eq);
-    const bool keep = gt || (eq && eq_seen + rank_below(eqm) < keep_eq);
-    eq_seen += popc(eqm);
-    const uint64_t km = ballot(keep);
-    if (keep) {
-      const int p = out + rank_below(km);
-      keys[p] = key;
-      idx[p] = id;
+  constexpr int kU = 8;  // chunks of 64 loaded together
+  for (int base = 0; base < n; base += 64 * kU) {
+    uint32_t raw[kU];
+    int32_t id[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int e = base + 64 * u + l;
+      raw[u] = e < n ? keys[e] : 0u;
+      id[u] = e < n ? idx[e] : 0;
     }
-    out += popc(km);
+    // every load of the batch lands before the first store below overwrites
+    // an earlier position of the same buffer
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int e = base + 64 * u + l;
+      const bool in = e < n;
+      const uint32_t key = order_key(__uint_as_float(raw[u]));
+      const bool gt = in && key > kth;
+      const bool eq = in && key == kth;
+      const uint64_t eqm = ballot(eq);
+      const bool keep = gt || (eq && eq_seen + rank_below(eqm) < keep_eq);
+      eq_seen += popc(eqm);
+      const uint64_t km = ballot(keep);
+      if (keep) {
+        const int p = out + rank_below(km);
+        keys[p] = raw[u];
+        idx[p] = id[u];
+      }
+      out += popc(km);
+    }
   }
   wave_mem_fence();
-  return kth;
+  return key_to_float(kth);
 }
 
 }  // namespace dsaidx

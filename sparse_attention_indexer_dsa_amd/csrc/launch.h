@@ -24,7 +24,7 @@ struct ScanArgs {
   int pos_stride;
   const int32_t* bank;
   int bank_stride, group;
-  int K, cap;              // top-K; candidate-buffer entries per row (>= K + 64)
+  int K, cap;              // top-K; candidate-buffer entries per row (>= 2K + 64, < 65536)
   uint32_t* cand_key;      // [nq, cap] workspace
   int32_t* cand_idx;       // [nq, cap] workspace
   int32_t* out_idx;        // [nq, out_stride]
@@ -33,6 +33,11 @@ struct ScanArgs {
 };
 
 hipError_t launch_scan_topk(const ScanArgs& a, int dtype, hipStream_t stream);
+
+// Row histogram of the decode scores: bins of the top kDecHistBits bits of the
+// order-preserving key.
+constexpr int kDecHistBits = 12;
+constexpr int kDecHistBins = 1 << kDecHistBits;
 
 // Decode: scores of one bf16 query per sequence against its E4M3 cache,
 // written to logits [B, Nmax] (fp32), then a per-row top-K.
@@ -47,6 +52,7 @@ struct DecodeArgs {
   int K;
   float* logits;          // [B, ld] workspace, ld >= Nmax and a multiple of 4
   int64_t ld;
+  uint32_t* hist;         // [B, kDecHistBins] workspace
   int32_t* out_idx;       // [B, K]
   float* out_score;       // [B, K] or nullptr
 };

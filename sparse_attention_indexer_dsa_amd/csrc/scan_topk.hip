@@ -1,7 +1,7 @@
 // scan_topk.hip -- streaming lightning-indexer score + top-K for gfx950.
 //
 // One wavefront owns one query row and walks that query's candidate keys in
-// ascending key index, 32 keys per step:
+// ascending key index:
 //   * MFMA with the query's heads on M and 32 keys on N (ADIndex (Qi et al.),
 //     Section 3, Eq. (1): the per-head dot products q_{t,j} . k_s), bf16
 //     v_mfma_f32_32x32x16_bf16 or fp8 v_mfma_f32_32x32x64_f8f6f4, fp32
@@ -14,27 +14,32 @@
 //     only if it beats the running threshold (the K-th best so far); keys
 //     arrive in ascending index, so a strict ">" keeps the lower index on ties.
 //     When the buffer fills, a wave radix select keeps the best K in order.
-// The 4 waves of a workgroup own 4 consecutive queries that share most of
-// their candidates: the workgroup stages each 32-key tile once in LDS
-// (double-buffered).  The T x T score matrix is never written anywhere.
+// The WPB waves of a workgroup own WPB consecutive queries that share most of
+// their candidates.  The workgroup streams 64-key tiles of K through a
+// three-stage LDS ring fed from a three-deep register ring: a tile's global
+// loads are issued four tiles before it is scored and land in LDS two tiles
+// before, so HBM/MALL latency hides behind two tiles of MFMA work.  Inside a
+// wave the MFMAs of the next 32-key sub-tile are interleaved with the ReLU and
+// head sums of the current one, so the matrix cores and the VALU work at the
+// same time.  The T x T score matrix is never written anywhere.
 //
 // The same kernel serves three uses, picked by its arguments:
 //   dense prefill     candidates 0..t of query t                    (Eq. (2))
 //   group scan        queries = group anchors (q-bar, w-bar, Eq. (8)),
 //                     top-P of the anchor prefix = the bank         (Eq. (13))
-//   bank refinement   candidates = the group's bank, then t+1..i    (Eq. (14))
+//   bank refinement   candidates = the group's bank, then t+1..i    (Eq. (14));
+//                     the bank is staged once into LDS
 #include "device.h"
 #include "launch.h"
 
 namespace dsaidx {
 
-constexpr int kWavesPerBlock = 4;
-constexpr int kThreads = kWavesPerBlock * 64;
-constexpr int kTileKeys = 32;
-constexpr int kHistBins = 2048;
+constexpr int kTileKeys = 64;   // keys per pipeline stage: two 32-key MFMA sub-tiles
+constexpr int kMaxBankLds = 16384;
 
-template <int DT, int MT, int D>
+template <int DT, int MT, int D, int WPB>
 struct ScanCfg {
+  static constexpr int kThreads = WPB * 64;
   static constexpr int kRowBytes = DT == kBF16 ? 2 * D : D;  // bytes of one key row
   static constexpr int kLdsRow = kRowBytes + 16;             // padded LDS row stride
   static constexpr int kChunksPerRow = kRowBytes / 16;
@@ -60,53 +65,63 @@ __device__ __forceinline__ v16f mfma(const typename AFrag<DT>::type& a,
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-// Candidate c of the workgroup -> key index.  Dense: c.  Bank: bank[c] for
-// c < bank_len, then the post-anchor tokens anchor+1, anchor+2, ...
-__device__ __forceinline__ int64_t cand_token(int64_t c, const int32_t* bank, int bank_len,
-                                              int64_t anchor) {
-  if (!bank) return c;
-  return c < bank_len ? (int64_t)bank[c] : anchor + 1 + (c - bank_len);
-}
+// One 64-key tile held in registers between its global load and its LDS store.
+template <int NL>
+struct TileRegs {
+  u32x4 v[NL];
+  int tok;   // key index of candidate `tid` of the tile (threads < 64)
+  float ks;  // its fp8 scale
+};
 
-template <int DT, int MT, int D>
-__global__ void __launch_bounds__(kThreads, 2) scan_topk_kernel(const ScanArgs args) {
-  using C = ScanCfg<DT, MT, D>;
+template <int DT, int MT, int D, bool BANK, int WPB>
+__global__ void __launch_bounds__(WPB * 64, 2) scan_topk_kernel(const ScanArgs args) {
+  using C = ScanCfg<DT, MT, D, WPB>;
   using Frag = typename AFrag<DT>::type;
-  __shared__ __attribute__((aligned(16))) uint8_t s_tile[2][kTileKeys * C::kLdsRow];
-  __shared__ int32_t s_tok[2][kTileKeys];
-  __shared__ float s_kscale[2][kTileKeys];
-  __shared__ __attribute__((aligned(16))) uint32_t s_hist[kWavesPerBlock][kHistBins];
+  constexpr int kThreads = C::kThreads;
+  __shared__ __attribute__((aligned(16))) uint8_t s_tile[3][kTileKeys * C::kLdsRow];
+  __shared__ int32_t s_tok[3][kTileKeys];
+  __shared__ float s_kscale[3][kTileKeys];
+  __shared__ __attribute__((aligned(16))) uint32_t s_hist[WPB][kSelectHistWords];
+  __shared__ int32_t s_bank[BANK ? kMaxBankLds : 1];
+  __shared__ int s_need[3];  // compaction requests of steps i % 3
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int l = tid & 63;
-  const int h = l >> 5;   // which half of the k range / which 16 of each 32 heads
-  const int col = l & 31;  // MFMA column = key within the tile
+  const int h = l >> 5;    // which half of the k range / which 16 of each 32 heads
+  const int col = l & 31;  // MFMA column = key within a 32-key sub-tile
 
   // queries of this workgroup: the longest candidate lists are launched first
-  const int64_t j_hi = args.nq - (int64_t)blockIdx.x * kWavesPerBlock - 1;  // highest row
-  const int64_t j = j_hi - (kWavesPerBlock - 1) + wave;                      // this wave's row
+  const int j_hi = (int)args.nq - (int)blockIdx.x * WPB - 1;  // highest row
+  const int j = j_hi - (WPB - 1) + wave;                      // this wave's row
   const bool active = j >= 0;
-  const int64_t j_lo = j_hi - (kWavesPerBlock - 1) < 0 ? 0 : j_hi - (kWavesPerBlock - 1);
+  const int j_lo = j_hi - (WPB - 1) < 0 ? 0 : j_hi - (WPB - 1);
+  const int pos0 = (int)args.pos0;
 
   // candidate list of the workgroup
-  const int32_t* bank = nullptr;
   int bank_len = 0;
-  int64_t anchor = 0;
-  const int64_t t_hi = args.pos0 + j_hi * args.pos_stride;
-  int64_t ncand_blk;
-  if (args.bank) {
-    const int64_t grp = j_lo / args.group;  // all 4 rows share one group
-    anchor = args.pos0 + grp * args.group;
-    bank = args.bank + grp * args.bank_stride;
-    bank_len = (int)min((int64_t)args.bank_stride, anchor + 1);
+  int anchor = 0;
+  const int t_hi = pos0 + j_hi * args.pos_stride;
+  int ncand_blk;
+  if constexpr (BANK) {
+    const int grp = j_lo / args.group;  // all WPB rows share one group
+    anchor = pos0 + grp * args.group;
+    bank_len = min(args.bank_stride, anchor + 1);
     ncand_blk = bank_len + (t_hi - anchor);
+    const int32_t* gbank = args.bank + (int64_t)grp * args.bank_stride;
+    for (int i = tid; i < bank_len; i += kThreads) s_bank[i] = gbank[i];
+    __syncthreads();
   } else {
     ncand_blk = t_hi + 1;
   }
-  const int64_t t_me = args.pos0 + (active ? j : j_lo) * args.pos_stride;
-  const int64_t ncand_me = args.bank ? bank_len + (t_me - anchor) : t_me + 1;
-  const int ntiles = (int)((ncand_blk + kTileKeys - 1) / kTileKeys);
+  // candidate c of the workgroup -> key index
+  auto cand_token = [&](int c) __attribute__((always_inline)) -> int {
+    if constexpr (!BANK) return c;
+    return c < bank_len ? s_bank[c] : anchor + 1 + (c - bank_len);
+  };
+  const int t_me = pos0 + (active ? j : j_lo) * args.pos_stride;
+  const int ncand_me = BANK ? bank_len + (t_me - anchor) : t_me + 1;
+  const int ntiles = (ncand_blk + kTileKeys - 1) / kTileKeys;
 
   // ---- this wave's query: A fragments and gate weights in registers
   Frag a[MT][C::kSteps];
@@ -114,12 +129,13 @@ __global__ void __launch_bounds__(kThreads, 2) scan_topk_kernel(const ScanArgs a
   {
     float qs = 1.0f;
     if (DT == kFP8 && active) qs = args.q_scale[j];
+    const int jq = active ? j : 0;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       const int head = 32 * m + col;
       const bool hv = active && head < args.H;
-      const uint8_t* qrow = (const uint8_t*)args.q +
-                            ((active ? j : 0) * (int64_t)args.H + (hv ? head : 0)) * C::kRowBytes;
+      const uint8_t* qrow =
+          (const uint8_t*)args.q + ((int64_t)jq * args.H + (hv ? head : 0)) * C::kRowBytes;
 #pragma unroll
       for (int s = 0; s < C::kSteps; ++s) {
         if constexpr (DT == kBF16) {
@@ -137,121 +153,181 @@ __global__ void __launch_bounds__(kThreads, 2) scan_topk_kernel(const ScanArgs a
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int hr = 32 * m + 8 * (r >> 2) + 4 * h + (r & 3);
-        wv[m][r] = (active && hr < args.H) ? args.w[j * (int64_t)args.H + hr] * qs : 0.0f;
+        wv[m][r] = (active && hr < args.H) ? args.w[(int64_t)jq * args.H + hr] * qs : 0.0f;
       }
     }
   }
 
-  uint32_t* ckey = args.cand_key + (active ? j : 0) * (int64_t)args.cap;
-  int32_t* cidx = args.cand_idx + (active ? j : 0) * (int64_t)args.cap;
+  uint32_t* ckey = args.cand_key + (int64_t)(active ? j : 0) * args.cap;  // raw fp32 scores
+  int32_t* cidx = args.cand_idx + (int64_t)(active ? j : 0) * args.cap;
   uint32_t* hist = s_hist[wave];
-  int cnt = 0;          // entries in the candidate buffer (wave-uniform)
-  uint32_t thr = 0u;    // keys must exceed this to enter (wave-uniform)
+  int cnt = 0;                       // entries in the candidate buffer (wave-uniform)
+  float thr = -__builtin_inff();     // scores must exceed this to enter (wave-uniform)
+  // A wave whose buffer passes `lim` raises the flag of the current step; after
+  // that step's barrier every wave holding more than K entries compacts, so the
+  // workgroup pays for one selection at a time instead of one per wave.  A
+  // step appends at most 64 entries, so the buffer cannot overflow meanwhile.
+  const int lim = args.cap - 192;
+  if (tid < 3) s_need[tid] = 0;
 
-  // ---- cooperative tile loader: global -> registers -> LDS
-  u32x4 stage[C::kLoads];
-  int32_t stage_tok = 0;
-  float stage_ks = 1.0f;
-  auto load_tile = [&](int it) {
-    const int64_t base = (int64_t)it * kTileKeys;
+  // ---- tile pipeline: global -> registers (3 sets) -> LDS (3 stages).  Tile t
+  // is loaded at step t-4, stored to LDS stage t%3 at step t-2 and scored at
+  // step t; its first sub-tile's MFMAs are issued at the end of step t-1.
+  using Regs = TileRegs<C::kLoads>;
+  auto load_tile = [&](Regs& R, int it) __attribute__((always_inline)) {
+    const int base = it * kTileKeys;
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i) {
       const int c = tid + i * kThreads;
-      stage[i] = u32x4{0, 0, 0, 0};
+      R.v[i] = u32x4{0, 0, 0, 0};
       if (c < C::kChunks) {
         const int r = c / C::kChunksPerRow, p = c % C::kChunksPerRow;
-        const int64_t cand = base + r;
+        const int cand = base + r;
         if (cand < ncand_blk) {
-          const int64_t tok = cand_token(cand, bank, bank_len, anchor);
-          stage[i] = *(const u32x4*)((const uint8_t*)args.k + tok * C::kRowBytes + p * 16);
+          const int tok = cand_token(cand);
+          R.v[i] = *(const u32x4*)((const uint8_t*)args.k + (int64_t)tok * C::kRowBytes + p * 16);
         }
       }
     }
     if (tid < kTileKeys) {
-      const int64_t cand = base + tid;
-      stage_tok = cand < ncand_blk ? (int32_t)cand_token(cand, bank, bank_len, anchor) : INT32_MAX;
-      stage_ks = (DT == kFP8 && cand < ncand_blk) ? args.k_scale[stage_tok] : 1.0f;
+      const int cand = base + tid;
+      R.tok = cand < ncand_blk ? cand_token(cand) : INT32_MAX;
+      R.ks = (DT == kFP8 && cand < ncand_blk) ? args.k_scale[R.tok] : 1.0f;
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](const Regs& R, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i) {
       const int c = tid + i * kThreads;
       if (c < C::kChunks) {
         const int r = c / C::kChunksPerRow, p = c % C::kChunksPerRow;
-        *(u32x4*)(&s_tile[buf][r * C::kLdsRow + p * 16]) = stage[i];
+        *(u32x4*)(&s_tile[buf][r * C::kLdsRow + p * 16]) = R.v[i];
       }
     }
     if (tid < kTileKeys) {
-      s_tok[buf][tid] = stage_tok;
-      s_kscale[buf][tid] = stage_ks;
+      s_tok[buf][tid] = R.tok;
+      s_kscale[buf][tid] = R.ks;
     }
   };
 
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < ntiles) load_tile(it + 1);
-
-    const int64_t tbase = (int64_t)it * kTileKeys;
-    if (active && tbase < ncand_me) {
-      v16f acc[MT];
+  // MFMAs of 32-key sub-tile u of the tile in LDS stage `buf`
+  auto mfma_sub = [&](v16f (&acc)[MT], int buf, int u) __attribute__((always_inline)) {
 #pragma unroll
-      for (int m = 0; m < MT; ++m) acc[m] = v16f{};
-      const uint8_t* brow = &s_tile[buf][col * C::kLdsRow + h * C::kHalf];
+    for (int m = 0; m < MT; ++m) acc[m] = v16f{};
+    const uint8_t* brow = &s_tile[buf][(32 * u + col) * C::kLdsRow + h * C::kHalf];
 #pragma unroll
-      for (int s = 0; s < C::kSteps; ++s) {
-        Frag b;
-        if constexpr (DT == kBF16) {
-          b = __builtin_bit_cast(v8bf, *(const u32x4*)(brow + 16 * s));
-        } else {
-          u32x4 v0 = *(const u32x4*)(brow + 32 * s);
-          u32x4 v1 = *(const u32x4*)(brow + 32 * s + 16);
-          b[0] = v0[0]; b[1] = v0[1]; b[2] = v0[2]; b[3] = v0[3];
-          b[4] = v1[0]; b[5] = v1[1]; b[6] = v1[2]; b[7] = v1[3];
-        }
-#pragma unroll
-        for (int m = 0; m < MT; ++m) acc[m] = mfma<DT>(a[m][s], b, acc[m]);
+    for (int s = 0; s < C::kSteps; ++s) {
+      Frag b;
+      if constexpr (DT == kBF16) {
+        b = __builtin_bit_cast(v8bf, *(const u32x4*)(brow + 16 * s));
+      } else {
+        struct { u32x4 lo, hi; } pr = {*(const u32x4*)(brow + 32 * s),
+                                       *(const u32x4*)(brow + 32 * s + 16)};
+        b = __builtin_bit_cast(v8i, pr);
       }
-      // ReLU + gate-weighted head sum (Eq. (1)), this lane's 16*MT heads
-      float sc = 0.0f;
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sc = fmaf(wv[m][r], fmaxf(acc[m][r], 0.0f), sc);
-      // the other 16*MT heads of this key live in lane l ^ 32
-      {
-        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sc), __float_as_uint(sc), false,
-                                                   false);
-        sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-      }
-      if constexpr (DT == kFP8) sc *= s_kscale[buf][col];
-      sc += 0.0f;  // -0 -> +0
-      const int32_t tok = s_tok[buf][col];
-      const uint32_t key = order_key(sc);
-      const bool take = (l < 32) && (tbase + col < ncand_me) && ((int64_t)tok <= t_me) && key > thr;
-      const uint64_t tm = ballot(take);
-      if (tm) {
-        if (take) {
-          const int p = cnt + rank_below(tm);
-          ckey[p] = key;
-          cidx[p] = tok;
-        }
-        cnt += popc(tm);
-        if (cnt > args.cap - kTileKeys) {
-          thr = wave_select_topk(ckey, cidx, cnt, args.K, hist);
-          cnt = args.K;
-        }
-      }
+      for (int m = 0; m < MT; ++m) acc[m] = mfma<DT>(a[m][s], b, acc[m]);
     }
+  };
+  // ReLU + gate-weighted head sum (Eq. (1)) of this lane's 16*MT heads
+  auto head_sum = [&](const v16f (&acc)[MT]) __attribute__((always_inline)) -> float {
+    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) gated_relu_sum16(wv[m], acc[m], s0, s1, s2, s3);
+    return (s0 + s1) + (s2 + s3);
+  };
+  // finish the score of sub-tile u (candidates tbase+32u..) and append it if
+  // it beats the threshold.  The partial sums start at +0 and every ReLU term
+  // is >= +0, so no score is -0.
+  auto finish_sub = [&](float part, int buf, int u, int tbase, int step_i) __attribute__((always_inline)) {
+    // the other 16*MT heads of this key live in lane l ^ 32
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false,
+                                               false);
+    float sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    const int kk = 32 * u + col;  // key within the tile
+    if constexpr (DT == kFP8) sc *= s_kscale[buf][kk];
+    const int c0 = tbase + 32 * u;
+    bool take = (l < 32) && sc > thr;
+    if (c0 + 32 > ncand_me) take = take && (c0 + col < ncand_me);
+    const uint64_t tm = ballot(take);
+    if (tm) {
+      if (take) {
+        const int p = cnt + rank_below(tm);
+        ckey[p] = __float_as_uint(sc);
+        cidx[p] = s_tok[buf][kk];
+      }
+      cnt += popc(tm);
+      if (cnt > lim && l == 0) s_need[step_i % 3] = 1;
+    }
+  };
+  // interleave the next sub-tile's MFMAs with the current head sums
+  constexpr int kNumMfma = MT * C::kSteps;
+  constexpr int kValuPerMfma = (32 * MT + kNumMfma - 1) / kNumMfma;
+  auto interleave = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < kNumMfma; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
+    }
+  };
 
-    if (it + 1 < ntiles) store_tile(buf ^ 1);
+  Regs R0, R1, R2;
+  v16f acc0[MT], acc1[MT];
+  if (ntiles > 0) load_tile(R0, 0);
+  if (ntiles > 1) load_tile(R1, 1);
+  if (ntiles > 0) store_tile(R0, 0);
+  if (ntiles > 1) store_tile(R1, 1);
+  if (ntiles > 2) load_tile(R2, 2);
+  if (ntiles > 3) load_tile(R0, 3);
+  __syncthreads();
+  if (active && ncand_me > 0 && ntiles > 0) mfma_sub(acc0, 0, 0);
+  // step i: store tile i+2 (set (i+2)%3), load tile i+4 (into set (i+1)%3),
+  // score tile i with tile i+1's first MFMAs in flight
+  auto step = [&](Regs& Rs, Regs& Rl, int i) __attribute__((always_inline)) {
+    const int buf = i % 3;
+    // requests raised during step i-1 (seen after its barrier); clear the
+    // flag of step i+1, last read before the previous barrier
+    if (i > 0 && s_need[(i - 1) % 3] && active && cnt > args.K) {
+      thr = wave_select_topk(ckey, cidx, cnt, args.K, hist);
+      cnt = args.K;
+    }
+    if (tid == 0) s_need[(i + 1) % 3] = 0;
+    if (i + 2 < ntiles) store_tile(Rs, (i + 2) % 3);
+    if (i + 4 < ntiles) load_tile(Rl, i + 4);
+    const int tbase = i * kTileKeys;
+    const bool s0 = active && tbase < ncand_me;
+    const bool s1 = active && tbase + 32 < ncand_me;
+    const bool n0 = active && tbase + kTileKeys < ncand_me && i + 1 < ntiles;
+    if (s0) {
+      float part;
+      if (s1) {
+        mfma_sub(acc1, buf, 1);
+        part = head_sum(acc0);
+        interleave();
+      } else {
+        part = head_sum(acc0);
+      }
+      finish_sub(part, buf, 0, tbase, i);
+    }
+    if (s1) {
+      float part;
+      if (n0) {
+        mfma_sub(acc0, (i + 1) % 3, 0);
+        part = head_sum(acc1);
+        interleave();
+      } else {
+        part = head_sum(acc1);
+      }
+      finish_sub(part, buf, 1, tbase, i);
+    } else if (n0) {
+      mfma_sub(acc0, (i + 1) % 3, 0);
+    }
     __syncthreads();
+  };
+  for (int i = 0; i < ntiles; i += 3) {
+    step(R2, R1, i);
+    if (i + 1 < ntiles) step(R0, R2, i + 1);
+    if (i + 2 < ntiles) step(R1, R0, i + 2);
   }
 
   if (!active) return;
@@ -261,22 +337,30 @@ __global__ void __launch_bounds__(kThreads, 2) scan_topk_kernel(const ScanArgs a
   } else {
     wave_mem_fence();
   }
-  int32_t* oidx = args.out_idx + j * (int64_t)args.out_stride;
-  float* osc = args.out_score ? args.out_score + j * (int64_t)args.out_stride : nullptr;
+  int32_t* oidx = args.out_idx + (int64_t)j * args.out_stride;
+  float* osc = args.out_score ? args.out_score + (int64_t)j * args.out_stride : nullptr;
   for (int p = l; p < args.K; p += 64) {
     const bool v = p < cnt;
     oidx[p] = v ? cidx[p] : -1;
-    if (osc) osc[p] = v ? key_to_float(ckey[p]) : -__builtin_inff();
+    if (osc) osc[p] = v ? __uint_as_float(ckey[p]) : -__builtin_inff();
   }
 }
 
+template <int DT, int MT, int D, bool BANK, int WPB>
+static hipError_t launch_bw(const ScanArgs& a, hipStream_t stream) {
+  const int64_t blocks = (a.nq + WPB - 1) / WPB;
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL((scan_topk_kernel<DT, MT, D, BANK, WPB>), dim3((unsigned)blocks),
+                     dim3(WPB * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
+// 8 queries per workgroup; 4 when bank groups of 4 must not straddle a workgroup
 template <int DT, int MT, int D>
 static hipError_t launch_t(const ScanArgs& a, hipStream_t stream) {
-  const int64_t blocks = (a.nq + kWavesPerBlock - 1) / kWavesPerBlock;
-  if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((scan_topk_kernel<DT, MT, D>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                     stream, a);
-  return hipGetLastError();
+  if (!a.bank) return launch_bw<DT, MT, D, false, 8>(a, stream);
+  if (a.group % 8 == 0) return launch_bw<DT, MT, D, true, 8>(a, stream);
+  return launch_bw<DT, MT, D, true, 4>(a, stream);
 }
 
 hipError_t launch_scan_topk(const ScanArgs& a, int dtype, hipStream_t stream) {

@@ -184,6 +184,21 @@ def test_decode_random_tolerance(dsa):
     _decode_check(dsa, wl)
 
 
+def test_decode_select_paths(dsa):
+    """All-equal scores (w = 0: one histogram bin holds the whole row, the exact
+    multi-pass path), integer ties at the K-th score (tie cut by index), and a
+    cache longer than the select's LDS bitmap."""
+    wl = make_decode(B=3, N=20000, H=64, d=128, topk=2048, dist="int", seed=21,
+                     seq_lens=[20000, 9000, 2049])
+    wl.tensors["w"] = torch.zeros_like(wl["w"])
+    gi, gs = _decode_check(dsa, wl)
+    assert (_np(gi)[0] == np.arange(2048)).all()
+    wl2 = make_decode(B=2, N=30000, H=4, d=64, topk=1000, dist="int", seed=22, seq_lens=[30000, 25000])
+    _decode_check(dsa, wl2)
+    wl3 = make_decode(B=1, N=600000, H=16, d=64, topk=2048, dist="int", seed=23)
+    _decode_check(dsa, wl3)
+
+
 def test_decode_small_heads(dsa):
     wl = make_decode(B=3, N=777, H=7, d=64, topk=100, dist="int", seed=14, seq_lens=[777, 100, 99])
     _decode_check(dsa, wl)
