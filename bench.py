@@ -43,19 +43,24 @@ def _pairs_causal(q0, n):
     return n * q0 + n * (n + 1) // 2
 
 
-def _traffic(kernel_key, per_launch_alg):
-    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was
-    taken on the current kernel sources; else None."""
+def _traffic(*kernel_keys):
+    """HBM bytes per launch (summed over the given kernels of one call) from the
+    committed rocprofv3 PMC summary, if it was taken on the current kernel
+    sources; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
-        rec = json.load(open(path)).get(kernel_key)
+        recs = json.load(open(path))
     except (ValueError, OSError):
         return None
-    if not rec or rec.get("source_sha1") != _source_sha1():
-        return None
-    return rec.get("hbm_bytes_per_launch")
+    total = 0.0
+    for key in kernel_keys:
+        rec = recs.get(key)
+        if not rec or rec.get("source_sha1") != _source_sha1():
+            return None
+        total += rec["hbm_bytes_per_launch"]
+    return total
 
 
 def _source_sha1():
@@ -123,7 +128,7 @@ def bench_prefill(dsa, args, log):
                              launches_per_step=nchunks,
                              avg_launch_ms=float(launch_ms.mean()),
                              flops_per_launch=flops / nchunks,
-                             traffic=_traffic("scan_topk_fp8_prefill128k", None)))
+                             traffic=_traffic("scan_topk_fp8_prefill128k")))
     cpu = None
     if not args.no_cpu:
         cpu = cpu_prefill(wl, out, args, log)
@@ -204,7 +209,7 @@ def bench_decode(dsa, args, log):
                roofline=dict(bound="hbm", kernel="decode_scan_kernel + decode_select_kernel (one call)",
                              achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s", frac=achieved / PEAK_HBM_GBS,
                              avg_launch_ms=float(call_ms.mean()), bytes_per_launch=alg_bytes,
-                             traffic=_traffic("decode_scan_decode256k", None)))
+                             traffic=_traffic("decode_scan_decode256k", "decode_select_decode256k")))
     if not args.no_cpu:
         import oracle
         from tests.parity import compare
@@ -294,7 +299,18 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--adindex", action="store_true", help="also time the ADIndex group-bank workload")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only copy BYTES device-to-device 5 times (calibrates HBM byte counters)")
     args = ap.parse_args()
+
+    if args.copy_probe:
+        src = torch.empty(args.copy_probe, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": args.copy_probe, "copies": 5}))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the indexer path here runs on a single MI355X "

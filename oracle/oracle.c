@@ -357,8 +357,8 @@ int oracle_group_bank(const void *q, const float *q_scale, const void *k, const 
     int64_t NG = (Tq + G - 1) / G;
     int64_t n_out = rows ? nrows : Tq;
 
-    /* which groups' banks are needed: those of the requested rows (all groups
-     * when the bank itself is requested) */
+    /* which groups' banks are needed: those of the requested rows (every row
+     * when `rows` is NULL); out_bank rows of other groups are written as -1 */
     char *need = calloc((size_t)(NG > 0 ? NG : 1), 1);
     int64_t **banks = calloc((size_t)(NG > 0 ? NG : 1), sizeof(int64_t *));
     int64_t *nbank = calloc((size_t)(NG > 0 ? NG : 1), sizeof(int64_t));
@@ -368,8 +368,6 @@ int oracle_group_bank(const void *q, const float *q_scale, const void *k, const 
         if (i < 0 || i >= Tq) { free(K); free(need); free(banks); free(nbank); return -1; }
         need[i / G] = 1;
     }
-    if (out_bank)
-        for (int64_t g = 0; g < NG; ++g) need[g] = 1;
 
     int err = 0;
 #pragma omp parallel for schedule(dynamic, 1)

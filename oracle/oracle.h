@@ -50,8 +50,10 @@ int oracle_decode(const void *q, const uint8_t *k_cache, const float *k_scale, c
                   int nthreads);
 
 /* out_bank [ceil(Tq/G), P] (ascending bank positions, -1 padding, all -1 for
- * groups that use the original indexer) or NULL; *pairs receives the number
- * of query-key scores the method evaluates over the whole call. */
+ * groups that use the original indexer) or NULL; with `rows`, only the banks
+ * of the requested rows' groups are computed (other rows all -1).  *pairs
+ * receives the number of query-key scores the method evaluates over the
+ * whole call. */
 int oracle_group_bank(const void *q, const float *q_scale, const void *k, const float *k_scale,
                       const float *w, int dtype, int64_t Tq, int64_t Tk, int H, int d,
                       int64_t q_pos0, const void *qbar, const float *qbar_scale, const float *wbar,

@@ -1,0 +1,131 @@
+"""The C ABI of libdsaidx.so without a GPU: the library loads, exports every
+function the header declares, rejects bad arguments on the host before any
+launch (the pointers below are never dereferenced), sizes workspaces, and
+plans the group-bank pair count exactly as the oracle counts it."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa_indexer.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+BF16, FP8 = 1, 2
+
+
+@pytest.fixture(scope="module")
+def L():
+    from sparse_attention_indexer_dsa_amd import _lib
+    return _lib.lib()
+
+
+def P(v):
+    """A fake device pointer: aligned, non-null, never dereferenced by validation."""
+    return ctypes.c_void_p(v)
+
+
+A = P(1 << 20)  # 16-byte aligned
+
+
+def test_header_symbols_exported(L):
+    names = re.findall(r"^\s*(?:[\w\s\*]+?)\b(indexer_\w+)\s*\(", open(HEADER).read(), re.M)
+    names = sorted(set(names))
+    assert len(names) == 8, names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _prefill(L, **kw):
+    a = dict(q=A, qs=None, k=A, ks=None, w=A, dtype=BF16, Tq=16, Tk=16, H=64, d=128, q_pos0=0, topk=8,
+             out=A, sc=None, ws=A, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return L.indexer_prefill(a["q"], a["qs"], a["k"], a["ks"], a["w"], a["dtype"], a["Tq"], a["Tk"], a["H"],
+                             a["d"], a["q_pos0"], a["topk"], a["out"], a["sc"], a["ws"], a["ws_bytes"],
+                             a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(out=None), INVALID), (dict(w=None), INVALID),
+    (dict(topk=0), INVALID), (dict(topk=4096), UNSUPPORTED), (dict(H=0), INVALID), (dict(H=65), UNSUPPORTED),
+    (dict(d=48), UNSUPPORTED), (dict(d=32, dtype=FP8, qs=A, ks=A), UNSUPPORTED), (dict(dtype=3), INVALID),
+    (dict(q_pos0=1), INVALID), (dict(Tk=15), INVALID), (dict(Tq=-1), INVALID),
+    (dict(q=P((1 << 20) + 4)), INVALID), (dict(out=P((1 << 20) + 8)), INVALID),
+    (dict(dtype=FP8), INVALID), (dict(qs=A), INVALID),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=100), WORKSPACE), (dict(ws=P((1 << 20) + 2)), INVALID),
+    (dict(Tk=1 << 31, Tq=1), UNSUPPORTED),
+])
+def test_prefill_rejects(L, kw, code):
+    assert _prefill(L, **kw) == code
+    assert len(L.indexer_last_error()) > 0
+
+
+def test_empty_prefill_is_a_noop(L):
+    assert _prefill(L, Tq=0, ws=None, ws_bytes=0) == OK
+    assert L.indexer_prefill_workspace_size(0, 16, 64, 128, 8, BF16) == 0
+
+
+def test_workspace_sizes(L):
+    a = L.indexer_prefill_workspace_size(4096, 131072, 64, 128, 2048, FP8)
+    b = L.indexer_prefill_workspace_size(8192, 131072, 64, 128, 2048, FP8)
+    c = L.indexer_prefill_workspace_size(40000, 131072, 64, 128, 2048, FP8)
+    assert 0 < a < b <= c  # capped by the rows of one launch
+    assert L.indexer_decode_workspace_size(32, 262144, 64, 128, 2048) >= 32 * 262144 * 4
+    assert L.indexer_group_bank_workspace_size(65536, 65536, 64, 64, 128, 16, 8192, 2048, BF16) > 0
+
+
+def _decode(L, **kw):
+    a = dict(q=A, kc=A, ks=A, w=A, lens=A, B=4, N=1024, H=64, d=128, topk=64, out=A, sc=None, ws=A,
+             ws_bytes=1 << 40)
+    a.update(kw)
+    return L.indexer_decode(a["q"], a["kc"], a["ks"], a["w"], a["lens"], a["B"], a["N"], a["H"], a["d"],
+                            a["topk"], a["out"], a["sc"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kc=None), INVALID), (dict(lens=None), INVALID), (dict(B=-1), INVALID), (dict(N=-2), INVALID),
+    (dict(d=32), UNSUPPORTED), (dict(topk=5000), UNSUPPORTED), (dict(ks=P((1 << 20) + 2)), INVALID),
+    (dict(ws_bytes=10), WORKSPACE), (dict(H=100), UNSUPPORTED),
+])
+def test_decode_rejects(L, kw, code):
+    assert _decode(L, **kw) == code
+
+
+def _group(L, **kw):
+    a = dict(q=A, qs=None, k=A, ks=None, w=A, dtype=BF16, Tq=64, Tk=64, H=8, d=64, q_pos0=0, qbar=A,
+             qbs=None, wbar=A, Hs=8, G=16, P=32, topk=8, flags=0, out=A, bank=None, sc=None, ws=A,
+             ws_bytes=1 << 40)
+    a.update(kw)
+    return L.indexer_group_bank(a["q"], a["qs"], a["k"], a["ks"], a["w"], a["dtype"], a["Tq"], a["Tk"], a["H"],
+                                a["d"], a["q_pos0"], a["qbar"], a["qbs"], a["wbar"], a["Hs"], a["G"], a["P"],
+                                a["topk"], a["flags"], a["out"], a["bank"], a["sc"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(G=5), UNSUPPORTED), (dict(G=32), UNSUPPORTED), (dict(P=4), INVALID), (dict(P=20000), UNSUPPORTED),
+    (dict(q_pos0=8, Tk=128), INVALID), (dict(flags=2), INVALID), (dict(qbar=None), INVALID),
+    (dict(Hs=0), INVALID), (dict(Hs=80), UNSUPPORTED), (dict(dtype=FP8, qs=A, ks=A), INVALID),
+    (dict(qbs=A), INVALID), (dict(bank=P((1 << 20) + 4)), INVALID), (dict(ws_bytes=1), WORKSPACE),
+])
+def test_group_bank_rejects(L, kw, code):
+    assert _group(L, **kw) == code
+
+
+@pytest.mark.parametrize("Tq,q_pos0,G,P,flags", [
+    (65536, 0, 16, 8192, 0), (131072, 0, 8, 4096, 0), (203, 0, 4, 48, 0), (646, 52, 4, 96, 0),
+    (646, 52, 4, 96, 1), (100, 0, 16, 16384, 0), (0, 0, 4, 64, 0),
+])
+def test_pair_plan_matches_oracle(L, Tq, q_pos0, G, P, flags):
+    """The library's launch plan scores exactly the pairs the oracle scores."""
+    assert L.indexer_group_bank_pairs(Tq, q_pos0, G, P, flags) == oracle.group_bank_pairs(Tq, q_pos0, G, P, flags)
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    import sparse_attention_indexer_dsa_amd as dsa
+    q = torch.zeros((4, 4, 32), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        dsa.indexer_prefill(q, torch.zeros((4, 32), dtype=torch.bfloat16), torch.zeros((4, 4)), 0, 2)
