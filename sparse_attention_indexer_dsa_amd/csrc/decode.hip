@@ -105,10 +105,10 @@ __global__ void __launch_bounds__(kDecThreads, 2) decode_scan_kernel(const Decod
       for (int m = 0; m < MT; ++m)
         acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m][s], bf, acc[m], 0, 0, 0);
     }
-    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+    float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
-    for (int m = 0; m < MT; ++m) gated_relu_sum16(wv[m], acc[m], s0, s1, s2, s3);
-    float sc = (s0 + s1) + (s2 + s3);
+    for (int m = 0; m < MT; ++m) gated_relu_sum16(wv[m], acc[m], s0, s1);
+    float sc = s0 + s1;
     auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sc), __float_as_uint(sc), false,
                                                false);
     sc = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * ks;

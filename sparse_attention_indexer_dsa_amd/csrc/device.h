@@ -35,15 +35,13 @@ __device__ __forceinline__ float relu_bits(float x) {
 }
 
 // sum_r w[r] * ReLU(acc[r]) over the 16 accumulators of one 32x32 MFMA tile,
-// added to four independent partial sums (short dependency chains).
+// added to two interleaved partial sums.
 __device__ __forceinline__ void gated_relu_sum16(const float* w, const v16f& acc, float& s0,
-                                                 float& s1, float& s2, float& s3) {
+                                                 float& s1) {
 #pragma unroll
-  for (int r = 0; r < 16; r += 4) {
+  for (int r = 0; r < 16; r += 2) {
     s0 = fmaf(w[r], relu_bits(acc[r]), s0);
     s1 = fmaf(w[r + 1], relu_bits(acc[r + 1]), s1);
-    s2 = fmaf(w[r + 2], relu_bits(acc[r + 2]), s2);
-    s3 = fmaf(w[r + 3], relu_bits(acc[r + 3]), s3);
   }
 }
 

@@ -35,6 +35,7 @@
 namespace dsaidx {
 
 constexpr int kTileKeys = 64;   // keys per pipeline stage: two 32-key MFMA sub-tiles
+constexpr int kStageEntries = kSelectHistWords / 2;  // LDS append stage per wave
 constexpr int kMaxBankLds = 16384;
 
 template <int DT, int MT, int D, int WPB>
@@ -161,39 +162,51 @@ __global__ void __launch_bounds__(WPB * 64, 2) scan_topk_kernel(const ScanArgs a
   uint32_t* ckey = args.cand_key + (int64_t)(active ? j : 0) * args.cap;  // raw fp32 scores
   int32_t* cidx = args.cand_idx + (int64_t)(active ? j : 0) * args.cap;
   uint32_t* hist = s_hist[wave];
-  int cnt = 0;                       // entries in the candidate buffer (wave-uniform)
+  // Scores that enter are first staged in this wave's LDS (the selection
+  // histogram's words, free outside a selection) and flushed to the global
+  // buffer in order when the stage nears full: the tile loop then issues no
+  // global stores, which would share the in-order load counter with the tile
+  // prefetches and force them to drain.
+  uint32_t* stage_key = hist;
+  int32_t* stage_idx = (int32_t*)(hist + kStageEntries);
+  int cnt = 0;                       // entries in the global buffer (wave-uniform)
+  int nst = 0;                       // entries in the LDS stage (wave-uniform)
   float thr = -__builtin_inff();     // scores must exceed this to enter (wave-uniform)
+  auto flush = [&]() __attribute__((always_inline)) {
+    for (int e = l; e < nst; e += 64) {
+      ckey[cnt + e] = stage_key[e];
+      cidx[cnt + e] = stage_idx[e];
+    }
+    cnt += nst;
+    nst = 0;
+    wave_mem_fence();  // the stores are drained here, not in the tile loop
+  };
   // A wave whose buffer passes `lim` raises the flag of the current step; after
   // that step's barrier every wave holding more than K entries compacts, so the
   // workgroup pays for one selection at a time instead of one per wave.  A
   // step appends at most 64 entries, so the buffer cannot overflow meanwhile.
-  const int lim = args.cap - 192;
+  const int lim = args.cap - 192;  // cnt + nst <= lim + 64 < cap after a step
   if (tid < 3) s_need[tid] = 0;
 
   // ---- tile pipeline: global -> registers (3 sets) -> LDS (3 stages).  Tile t
   // is loaded at step t-4, stored to LDS stage t%3 at step t-2 and scored at
   // step t; its first sub-tile's MFMAs are issued at the end of step t-1.
   using Regs = TileRegs<C::kLoads>;
+  // Loads are unconditional (candidates past the end read the last valid
+  // row; their scores are masked when appended), so no load sits behind a
+  // branch and the register ring's wait counts stay exact.
   auto load_tile = [&](Regs& R, int it) __attribute__((always_inline)) {
     const int base = it * kTileKeys;
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i) {
-      const int c = tid + i * kThreads;
-      R.v[i] = u32x4{0, 0, 0, 0};
-      if (c < C::kChunks) {
-        const int r = c / C::kChunksPerRow, p = c % C::kChunksPerRow;
-        const int cand = base + r;
-        if (cand < ncand_blk) {
-          const int tok = cand_token(cand);
-          R.v[i] = *(const u32x4*)((const uint8_t*)args.k + (int64_t)tok * C::kRowBytes + p * 16);
-        }
-      }
+      const int c = (tid + i * kThreads) % C::kChunks;
+      const int r = c / C::kChunksPerRow, p = c % C::kChunksPerRow;
+      const int tok = cand_token(min(base + r, ncand_blk - 1));
+      R.v[i] = *(const u32x4*)((const uint8_t*)args.k + (int64_t)tok * C::kRowBytes + p * 16);
     }
-    if (tid < kTileKeys) {
-      const int cand = base + tid;
-      R.tok = cand < ncand_blk ? cand_token(cand) : INT32_MAX;
-      R.ks = (DT == kFP8 && cand < ncand_blk) ? args.k_scale[R.tok] : 1.0f;
-    }
+    const int tok = cand_token(min(base + (tid & (kTileKeys - 1)), ncand_blk - 1));
+    R.tok = tok;
+    if constexpr (DT == kFP8) R.ks = args.k_scale[tok];
   };
   auto store_tile = [&](const Regs& R, int buf) __attribute__((always_inline)) {
 #pragma unroll
@@ -206,7 +219,7 @@ __global__ void __launch_bounds__(WPB * 64, 2) scan_topk_kernel(const ScanArgs a
     }
     if (tid < kTileKeys) {
       s_tok[buf][tid] = R.tok;
-      s_kscale[buf][tid] = R.ks;
+      if constexpr (DT == kFP8) s_kscale[buf][tid] = R.ks;
     }
   };
 
@@ -231,33 +244,34 @@ __global__ void __launch_bounds__(WPB * 64, 2) scan_topk_kernel(const ScanArgs a
   };
   // ReLU + gate-weighted head sum (Eq. (1)) of this lane's 16*MT heads
   auto head_sum = [&](const v16f (&acc)[MT]) __attribute__((always_inline)) -> float {
-    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+    float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
-    for (int m = 0; m < MT; ++m) gated_relu_sum16(wv[m], acc[m], s0, s1, s2, s3);
-    return (s0 + s1) + (s2 + s3);
+    for (int m = 0; m < MT; ++m) gated_relu_sum16(wv[m], acc[m], s0, s1);
+    return s0 + s1;
   };
   // finish the score of sub-tile u (candidates tbase+32u..) and append it if
   // it beats the threshold.  The partial sums start at +0 and every ReLU term
   // is >= +0, so no score is -0.
-  auto finish_sub = [&](float part, int buf, int u, int tbase, int step_i) __attribute__((always_inline)) {
+  auto finish_sub = [&](float part, int buf, int u, int tbase, int step_buf) __attribute__((always_inline)) {
     // the other 16*MT heads of this key live in lane l ^ 32
     auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false,
                                                false);
     float sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     const int kk = 32 * u + col;  // key within the tile
     if constexpr (DT == kFP8) sc *= s_kscale[buf][kk];
+    // lanes l and l+32 hold the same key: only the low half appends
     const int c0 = tbase + 32 * u;
-    bool take = (l < 32) && sc > thr;
-    if (c0 + 32 > ncand_me) take = take && (c0 + col < ncand_me);
-    const uint64_t tm = ballot(take);
+    uint64_t tm = ballot(sc > thr) & 0xFFFFFFFFull;
+    if (c0 + 32 > ncand_me) tm &= ballot(c0 + col < ncand_me);  // the query's last sub-tile
+    const bool take = (tm >> l) & 1;
     if (tm) {
       if (take) {
-        const int p = cnt + rank_below(tm);
-        ckey[p] = __float_as_uint(sc);
-        cidx[p] = s_tok[buf][kk];
+        const int p = nst + rank_below(tm);
+        stage_key[p] = __float_as_uint(sc);
+        stage_idx[p] = s_tok[buf][kk];
       }
-      cnt += popc(tm);
-      if (cnt > lim && l == 0) s_need[step_i % 3] = 1;
+      nst += popc(tm);
+      if (cnt + nst > lim && l == 0) s_need[step_buf] = 1;
     }
   };
   // interleave the next sub-tile's MFMAs with the current head sums
@@ -273,27 +287,35 @@ __global__ void __launch_bounds__(WPB * 64, 2) scan_topk_kernel(const ScanArgs a
 
   Regs R0, R1, R2;
   v16f acc0[MT], acc1[MT];
-  if (ntiles > 0) load_tile(R0, 0);
-  if (ntiles > 1) load_tile(R1, 1);
-  if (ntiles > 0) store_tile(R0, 0);
-  if (ntiles > 1) store_tile(R1, 1);
-  if (ntiles > 2) load_tile(R2, 2);
-  if (ntiles > 3) load_tile(R0, 3);
+  if (ntiles > 0) {
+    load_tile(R0, 0);
+    load_tile(R1, min(1, ntiles - 1));
+    store_tile(R0, 0);
+    store_tile(R1, 1);
+    load_tile(R2, min(2, ntiles - 1));
+    load_tile(R0, min(3, ntiles - 1));
+  }
   __syncthreads();
   if (active && ncand_me > 0 && ntiles > 0) mfma_sub(acc0, 0, 0);
   // step i: store tile i+2 (set (i+2)%3), load tile i+4 (into set (i+1)%3),
   // score tile i with tile i+1's first MFMAs in flight
-  auto step = [&](Regs& Rs, Regs& Rl, int i) __attribute__((always_inline)) {
-    const int buf = i % 3;
+  // `buf` = i % 3, passed as a literal so every LDS address is base + constant
+  auto step = [&](Regs& Rs, Regs& Rl, int i, const int buf) __attribute__((always_inline)) {
+    const int buf1 = buf == 2 ? 0 : buf + 1, buf2 = buf == 0 ? 2 : buf - 1;
     // requests raised during step i-1 (seen after its barrier); clear the
     // flag of step i+1, last read before the previous barrier
-    if (i > 0 && s_need[(i - 1) % 3] && active && cnt > args.K) {
+    if (i > 0 && s_need[buf2] && active && cnt + nst > args.K) {
+      flush();
       thr = wave_select_topk(ckey, cidx, cnt, args.K, hist);
       cnt = args.K;
+    } else if (active && nst > kStageEntries - 64) {
+      flush();
     }
-    if (tid == 0) s_need[(i + 1) % 3] = 0;
-    if (i + 2 < ntiles) store_tile(Rs, (i + 2) % 3);
-    if (i + 4 < ntiles) load_tile(Rl, i + 4);
+    if (tid == 0) s_need[buf1] = 0;
+    // the same loads and LDS stores every step (past the last tile they
+    // repeat it and are never read), so the wait counts are exact
+    store_tile(Rs, buf2);
+    load_tile(Rl, min(i + 4, ntiles - 1));
     const int tbase = i * kTileKeys;
     const bool s0 = active && tbase < ncand_me;
     const bool s1 = active && tbase + 32 < ncand_me;
@@ -307,35 +329,34 @@ __global__ void __launch_bounds__(WPB * 64, 2) scan_topk_kernel(const ScanArgs a
       } else {
         part = head_sum(acc0);
       }
-      finish_sub(part, buf, 0, tbase, i);
+      finish_sub(part, buf, 0, tbase, buf);
     }
     if (s1) {
       float part;
       if (n0) {
-        mfma_sub(acc0, (i + 1) % 3, 0);
+        mfma_sub(acc0, buf1, 0);
         part = head_sum(acc1);
         interleave();
       } else {
         part = head_sum(acc1);
       }
-      finish_sub(part, buf, 1, tbase, i);
+      finish_sub(part, buf, 1, tbase, buf);
     } else if (n0) {
-      mfma_sub(acc0, (i + 1) % 3, 0);
+      mfma_sub(acc0, buf1, 0);
     }
     __syncthreads();
   };
   for (int i = 0; i < ntiles; i += 3) {
-    step(R2, R1, i);
-    if (i + 1 < ntiles) step(R0, R2, i + 1);
-    if (i + 2 < ntiles) step(R1, R0, i + 2);
+    step(R2, R1, i, 0);
+    if (i + 1 < ntiles) step(R0, R2, i + 1, 1);
+    if (i + 2 < ntiles) step(R1, R0, i + 2, 2);
   }
 
   if (!active) return;
+  flush();
   if (cnt > args.K) {
     wave_select_topk(ckey, cidx, cnt, args.K, hist);
     cnt = args.K;
-  } else {
-    wave_mem_fence();
   }
   int32_t* oidx = args.out_idx + (int64_t)j * args.out_stride;
   float* osc = args.out_score ? args.out_score + (int64_t)j * args.out_stride : nullptr;

@@ -223,7 +223,8 @@ def _group_check(dsa, wl, flags=0, rows=None, exact=None):
     exact = (p["dist"] == "int") if exact is None else exact
     assert pairs == dsa.indexer_group_bank_pairs(Tq, p["q_pos0"], G, P, flags)
     if exact:
-        assert np.array_equal(_np(gb), rb)
+        groups = np.unique(rows // G)  # the oracle computes the banks of the requested rows' groups
+        assert np.array_equal(_np(gb)[groups], rb[groups])
 
     def score_of(r, keys):
         return oracle.score_pairs(wl["q"], wl["k"], wl["w"], np.full(len(keys), rows[r]), keys, wl.dtype,
