@@ -202,11 +202,39 @@ int indexer_prefill(const void* q, const float* q_scale, const void* k, const fl
   return ok();
 }
 
+// decode workspace: histograms [B, bins] | compact-list counts [B, nblk] |
+// compact lists [B, nblk, kpb] of indices and of scores
+struct DecodeWs {
+  size_t hist, clcnt, clidx, clsc, total;
+};
+
+// keys per scan workgroup: about 512 workgroups per call (two per CU), a
+// multiple of 256 keys and at most what one workgroup's LDS score stage holds
+static int64_t decode_keys_per_block(int B, int64_t Nmax) {
+  const int64_t target = ((int64_t)B * Nmax + 511) / 512;
+  int64_t kpb = (target + 255) / 256 * 256;
+  const int64_t row = (Nmax + 255) / 256 * 256;
+  if (kpb > row) kpb = row;
+  if (kpb > kDecMaxKpb) kpb = kDecMaxKpb;
+  return kpb < 256 ? 256 : kpb;
+}
+
+static DecodeWs decode_ws(int B, int64_t Nmax) {
+  const size_t kpb = (size_t)decode_keys_per_block(B, Nmax);
+  const size_t nblk = ((size_t)Nmax + kpb - 1) / kpb;
+  DecodeWs w{};
+  w.hist = 0;
+  w.clcnt = w.hist + align_up((size_t)B * kDecHistBins * 4u);
+  w.clidx = w.clcnt + align_up((size_t)B * nblk * 4u);
+  w.clsc = w.clidx + align_up((size_t)B * nblk * kpb * 4u);
+  w.total = w.clsc + align_up((size_t)B * nblk * kpb * 4u);
+  return w;
+}
+
 size_t indexer_decode_workspace_size(int B, int64_t Nmax, int H, int d, int topk) {
   (void)H; (void)d; (void)topk;
   if (B <= 0 || Nmax <= 0) return 0;
-  const int64_t ld = (Nmax + 63) / 64 * 64;
-  return align_up((size_t)B * (size_t)ld * 4u) + align_up((size_t)B * kDecHistBins * 4u);
+  return decode_ws(B, Nmax).total;
 }
 
 int indexer_decode(const void* q, const uint8_t* k_cache, const float* k_scale, const float* w,
@@ -238,9 +266,14 @@ int indexer_decode(const void* q, const uint8_t* k_cache, const float* k_scale, 
   a.d = d;
   a.Nmax = Nmax;
   a.K = topk;
-  a.logits = (float*)ws;
-  a.ld = (Nmax + 63) / 64 * 64;
-  a.hist = (uint32_t*)((uint8_t*)ws + align_up((size_t)B * (size_t)a.ld * 4u));
+  const DecodeWs lay = decode_ws(B, Nmax);
+  uint8_t* base = (uint8_t*)ws;
+  a.kpb = decode_keys_per_block(B, Nmax);
+  a.nblk = (int)((Nmax + a.kpb - 1) / a.kpb);
+  a.hist = (uint32_t*)(base + lay.hist);
+  a.cl_cnt = (int32_t*)(base + lay.clcnt);
+  a.cl_idx = (int32_t*)(base + lay.clidx);
+  a.cl_sc = (float*)(base + lay.clsc);
   a.out_idx = out_idx;
   a.out_score = out_score;
   hipError_t e = launch_decode(a, (hipStream_t)stream);

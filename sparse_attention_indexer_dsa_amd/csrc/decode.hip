@@ -2,23 +2,28 @@
 // sequence scores its whole E4M3 key cache (ADIndex (Qi et al.), Section 3:
 // O(L) work per decoding query), then the top-K of each row (Eq. (2)).
 //
-// decode_scan: the cache stream is the cost.  Each wavefront takes 32 keys at
-// a time; lane l loads its key's k-half (d/2 bytes) straight into registers
-// (two 32-key tiles in flight while two others are scored), widens E4M3 to
-// bf16 exactly (every E4M3 value is a bf16 value) with
+// decode_scan: the cache stream is the cost.  A workgroup walks a span of up
+// to 16384 keys of one row, 768 keys per loop trip; each wavefront takes 32
+// keys at a time, lane l loading its key's k-half (d/2 bytes) straight into
+// registers (four 32-key tiles in flight while two others are scored), widens
+// E4M3 to bf16 exactly (every E4M3 value is a bf16 value) with
 // v_cvt_scalef32_pk_bf16_fp8, and runs the bf16 MFMA with the query's heads on
 // M.  ReLU, the gate-weighted head sum and the per-key scale follow in
-// registers; the fp32 score row goes to the workspace and every score also
-// counts into a per-row histogram of the top 12 bits of its order-preserving
-// key (LDS, flushed to the row's global histogram once per workgroup).
+// registers.  Scores stay in LDS together with a histogram of the top 12 bits
+// of their order-preserving keys; the histogram is added to the row's, and
+// only the scores in bins at or above the span's own K-th best (a lower bound
+// of the row's K-th best, to 24 bits) leave the chip, as a compact list.  HBM writes
+// cost far more than their share of the traffic, so the row of scores is never
+// written whole.
 //
-// decode_select: one workgroup per row.  The row histogram gives the bin b*
-// that holds the K-th best score and the count above it.  One pass over the
-// row marks every score above b* in an LDS bitmap of the row and gathers the
-// scores inside b* into LDS; two radix rounds over those candidates find the
-// exact K-th score (ties: lower index first), and a prefix popcount of the
-// bitmap writes the selected indices in ascending order.  Rows whose b* bin
-// is too crowded for LDS take an exact multi-pass path over the row instead.
+// decode_finish: one workgroup per row.  The row's compact lists, in span
+// order, form one list in ascending key order that the workgroup holds in
+// registers.  The row histogram gives the bin b* that holds the row's K-th
+// best score; the list's entries inside b* go to LDS, where two radix rounds
+// find the exact K-th score (ties: lower index first); a prefix sum over the
+// threads then writes the selected entries in ascending index order.  Rows
+// whose b* bin or whose list is too long for that take an exact multi-pass
+// path over the lists in global memory instead.
 #include "device.h"
 #include "launch.h"
 
@@ -26,8 +31,61 @@ namespace dsaidx {
 
 constexpr int kDecThreads = 256;
 constexpr int kDecWaves = kDecThreads / 64;
-constexpr int kDecTilesPerWave = 8;  // a multiple of 4: tiles go in pairs
-constexpr int kDecKeysPerBlock = kDecWaves * kDecTilesPerWave * 32;
+constexpr int kDecTilesPerTrip = 6;  // per wave: three pairs of 32-key tiles
+static_assert(kDecKeysPerPass == kDecWaves * kDecTilesPerTrip * 32, "one loop trip = 6 tiles per wave");
+
+// ------------------------------------------------------------------ select
+
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+
+// Exclusive prefix sum over a workgroup of NW waves (all threads call);
+// `total` gets the sum.
+template <int NW = kSelWaves>
+__device__ __forceinline__ int block_excl_scan(int v, int* s_tmp, int& total) {
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  const int incl = wave_incl_scan(v);
+  if (l == 63) s_tmp[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int t = s_tmp[w];
+    before += w < wave ? t : 0;
+    all += t;
+  }
+  __syncthreads();
+  total = all;
+  return before + incl - v;
+}
+
+// Per-thread runs of `per` consecutive bins (higher thread = higher bins):
+// find the bin holding the krem-th largest entry.  s_res[0] = bin,
+// s_res[1] = rank within the bin, s_res[2] = count of the bin.  All threads call.
+template <int NW = kSelWaves, typename F>
+__device__ __forceinline__ void block_find_digit(int per, F bins, int krem, int* s_tmp,
+                                                 int* s_res) {
+  const int tid = threadIdx.x;
+  int local = 0;
+  for (int i = 0; i < per; ++i) local += bins(tid, i);
+  int total;
+  const int excl = block_excl_scan<NW>(local, s_tmp, total);
+  const int above = total - excl - local;
+  if (above < krem && above + local >= krem) {
+    int acc = above;
+    for (int i = per - 1; i >= 0; --i) {
+      const int c = bins(tid, i);
+      if (acc + c >= krem) {
+        s_res[0] = tid * per + i;
+        s_res[1] = krem - acc;
+        s_res[2] = c;
+        break;
+      }
+      acc += c;
+    }
+  }
+  __syncthreads();
+}
 
 template <int D>
 struct DecTile {
@@ -40,7 +98,10 @@ __global__ void __launch_bounds__(kDecThreads, 2) decode_scan_kernel(const Decod
   constexpr int kSteps = D / 16;  // bf16 k-steps
   constexpr int kHalf = D / 2;    // fp8 bytes of a lane's k-half
   constexpr int kVec = DecTile<D>::kVec;
-  __shared__ uint32_t s_hist[kDecHistBins];
+  __shared__ uint32_t s_hist[kDecHistBins / 2];  // two 16-bit counts per word
+  __shared__ float s_score[kDecMaxKpb];
+  __shared__ int s_tmp[kDecWaves];
+  __shared__ int s_res[4];
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -48,9 +109,12 @@ __global__ void __launch_bounds__(kDecThreads, 2) decode_scan_kernel(const Decod
   const int h = l >> 5, col = l & 31;
   int64_t n = args.seq_lens[b];
   n = n < 0 ? 0 : (n > args.Nmax ? args.Nmax : n);
-  const int64_t blk0 = (int64_t)blockIdx.x * kDecKeysPerBlock;
+  const int64_t blk0 = (int64_t)blockIdx.x * args.kpb;
   if (blk0 >= n) return;
-  for (int i = tid; i < kDecHistBins; i += kDecThreads) s_hist[i] = 0;
+  // loop trips of this workgroup: 768 keys each, none wholly past the row end
+  const int64_t left = n - blk0 < args.kpb ? n - blk0 : args.kpb;
+  const int trips = (int)((left + kDecKeysPerPass - 1) / kDecKeysPerPass);
+  for (int i = tid; i < kDecHistBins / 2; i += kDecThreads) s_hist[i] = 0;
 
   v8bf a[MT][kSteps];
   float wv[MT][16];
@@ -73,22 +137,29 @@ __global__ void __launch_bounds__(kDecThreads, 2) decode_scan_kernel(const Decod
   }
   __syncthreads();
 
-  const uint8_t* kbase = args.kc + (int64_t)b * args.Nmax * D;
-  const float* sbase = args.k_scale + (int64_t)b * args.Nmax;
-  float* lrow = args.logits + (int64_t)b * args.ld;
+  // Buffer resources over this workgroup's span [blk0, blk_end) of the row:
+  // the hardware range check returns zeros for loads past the span, so no
+  // load sits behind a branch and the load-counter waits in the loop stay
+  // exact.  Scores are staged in LDS and written out after the loop, so the
+  // loop issues no global stores at all.
+  const int64_t blk_end = n < blk0 + args.kpb ? n : blk0 + args.kpb;
+  const int span = (int)(blk_end - blk0);
+  const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(args.kc + ((int64_t)b * args.Nmax + blk0) * D), (short)0, span * D, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(args.k_scale + (int64_t)b * args.Nmax + blk0), (short)0, span * 4, kBufferWord3);
 
-  // tile i of this wave covers keys blk0 + (i*kDecWaves + wave)*32 + [0, 32)
-  auto key_of = [&](int i) __attribute__((always_inline)) { return blk0 + ((int64_t)i * kDecWaves + wave) * 32 + col; };
+  // tile i of this wave covers span keys (i*kDecWaves + wave)*32 + [0, 32)
+  auto key_of = [&](int i) __attribute__((always_inline)) { return (i * kDecWaves + wave) * 32 + col; };
   auto load = [&](DecTile<D>& t, float& ks, int i) __attribute__((always_inline)) {
-    const int64_t key = key_of(i);
-    const bool kv = key < n;
+    const int key = key_of(i);
 #pragma unroll
     for (int v = 0; v < kVec; ++v)
-      t.v[v] = kv ? *(const u32x4*)(kbase + key * D + h * kHalf + 16 * v) : u32x4{0, 0, 0, 0};
-    ks = kv ? sbase[key] : 0.0f;
+      t.v[v] = __builtin_amdgcn_raw_buffer_load_b128(kres, key * D + h * kHalf + 16 * v, 0, 0);
+    ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sres, key * 4, 0, 0));
   };
   auto score = [&](const DecTile<D>& t, float ks, int i) __attribute__((always_inline)) {
-    const int64_t key = key_of(i);
+    const int key = key_of(i);
     v16f acc[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = v16f{};
@@ -113,89 +184,99 @@ __global__ void __launch_bounds__(kDecThreads, 2) decode_scan_kernel(const Decod
                                                false);
     sc = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * ks;
     sc += 0.0f;  // -0 -> +0
-    if (l < 32 && key < n) {
-      lrow[key] = sc;
-      atomicAdd(&s_hist[order_key(sc) >> (32 - kDecHistBits)], 1u);
+    // lanes l and l+32 hold the same key: the low half records it
+    if (l < 32 && key < span) {
+      s_score[key] = sc;
+      const uint32_t bin = order_key(sc) >> (32 - kDecHistBits);
+      atomicAdd(&s_hist[bin >> 1], 1u << (16 * (bin & 1)));
     }
   };
 
-  // tiles in pairs: the next pair's loads are in flight while a pair is scored
-  DecTile<D> ta0, ta1, tb0, tb1;
-  float ka0, ka1, kb0, kb1;
+  // Tiles go in pairs through a ring of three pair slots: while one pair is
+  // scored the loads of the next two pairs are in flight (16 KB per wave).
+  // Scheduling barriers keep the loads in program order, so each wait is for
+  // the pair about to be scored and never for the pairs behind it.
+  DecTile<D> ta0, ta1, tb0, tb1, tc0, tc1;
+  float ka0, ka1, kb0, kb1, kc0, kc1;
+  auto fence = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
   load(ta0, ka0, 0);
   load(ta1, ka1, 1);
-#pragma unroll
-  for (int i = 0; i < kDecTilesPerWave; i += 4) {
-    load(tb0, kb0, i + 2);
-    load(tb1, kb1, i + 3);
+  fence();
+  load(tb0, kb0, 2);
+  load(tb1, kb1, 3);
+  fence();
+  for (int i = 0; i < kDecTilesPerTrip * trips; i += kDecTilesPerTrip) {
+    load(tc0, kc0, i + 4);
+    load(tc1, kc1, i + 5);
+    fence();
     score(ta0, ka0, i);
     score(ta1, ka1, i + 1);
-    if (i + 4 < kDecTilesPerWave) {
-      load(ta0, ka0, i + 4);
-      load(ta1, ka1, i + 5);
-    }
+    fence();
+    load(ta0, ka0, i + 6);
+    load(ta1, ka1, i + 7);
+    fence();
     score(tb0, kb0, i + 2);
     score(tb1, kb1, i + 3);
+    fence();
+    load(tb0, kb0, i + 8);
+    load(tb1, kb1, i + 9);
+    fence();
+    score(tc0, kc0, i + 4);
+    score(tc1, kc1, i + 5);
+    fence();
   }
   __syncthreads();
   uint32_t* ghist = args.hist + (int64_t)b * kDecHistBins;
-  for (int i = tid; i < kDecHistBins; i += kDecThreads) {
+  for (int i = tid; i < kDecHistBins / 2; i += kDecThreads) {
     const uint32_t c = s_hist[i];
-    if (c) atomicAdd(ghist + i, c);
+    if (c & 0xFFFFu) atomicAdd(ghist + 2 * i, c & 0xFFFFu);
+    if (c >> 16) atomicAdd(ghist + 2 * i + 1, c >> 16);
   }
-}
-
-// ------------------------------------------------------------------ select
-
-constexpr int kSelThreads = 1024;
-constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kCandCap = 8192;       // LDS candidates of the threshold bin
-constexpr int kBitmapWords = 16384;  // rows up to 524288 keys use the bitmap path
-
-// Exclusive prefix sum over the workgroup (all threads call); `total` gets the sum.
-__device__ __forceinline__ int block_excl_scan(int v, int* s_tmp, int& total) {
-  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
-  const int incl = wave_incl_scan(v);
-  if (l == 63) s_tmp[wave] = incl;
-  __syncthreads();
-  int before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) {
-    const int t = s_tmp[w];
-    before += w < wave ? t : 0;
-    all += t;
-  }
-  __syncthreads();
-  total = all;
-  return before + incl - v;
-}
-
-// Per-thread runs of `per` consecutive bins (higher thread = higher bins):
-// find the bin holding the krem-th largest entry.  s_res[0] = bin,
-// s_res[1] = rank within the bin, s_res[2] = count of the bin.  All threads call.
-template <typename F>
-__device__ __forceinline__ void block_find_digit(int per, F bins, int krem, int* s_tmp,
-                                                 int* s_res) {
-  const int tid = threadIdx.x;
-  int local = 0;
-  for (int i = 0; i < per; ++i) local += bins(tid, i);
-  int total;
-  const int excl = block_excl_scan(local, s_tmp, total);
-  const int above = total - excl - local;
-  if (above < krem && above + local >= krem) {
-    int acc = above;
-    for (int i = per - 1; i >= 0; --i) {
-      const int c = bins(tid, i);
-      if (acc + c >= krem) {
-        s_res[0] = tid * per + i;
-        s_res[1] = krem - acc;
-        s_res[2] = c;
-        break;
+  // The K-th best score of the span is a lower bound of the row's K-th best:
+  // scores below it cannot reach the row's top K and are not kept.  Its top
+  // 12 bits come from the histogram, the next 12 from a second histogram over
+  // the span's scores inside that bin; the list keeps every score whose top
+  // 24 bits reach the result.  A span of at most K keys keeps everything.
+  uint32_t keep_from = 0;  // keep scores with (order key >> 8) >= keep_from
+  if (span > args.K) {
+    constexpr int kPer = kDecHistBins / kDecThreads;
+    auto bins16 = [&](int t, int i) __attribute__((always_inline)) {
+      const int bin = t * kPer + i;
+      return (int)((s_hist[bin >> 1] >> (16 * (bin & 1))) & 0xFFFFu);
+    };
+    block_find_digit<kDecWaves>(kPer, bins16, args.K, s_tmp, s_res);
+    const uint32_t bloc = (uint32_t)s_res[0];
+    const int krem = s_res[1];
+    for (int i = tid; i < kDecHistBins / 2; i += kDecThreads) s_hist[i] = 0;
+    __syncthreads();
+    for (int e = tid; e < span; e += kDecThreads) {
+      const uint32_t key = order_key(s_score[e]);
+      if ((key >> 20) == bloc) {
+        const uint32_t sub = (key >> 8) & 0xFFFu;
+        atomicAdd(&s_hist[sub >> 1], 1u << (16 * (sub & 1)));
       }
-      acc += c;
+    }
+    __syncthreads();
+    block_find_digit<kDecWaves>(kPer, bins16, krem, s_tmp, s_res);
+    keep_from = (bloc << 12) | (uint32_t)s_res[0];
+  }
+  // compact list of the kept scores, in ascending key order
+  const int per = (span + kDecThreads - 1) / kDecThreads;
+  const int e0 = tid * per, e1 = e0 + per < span ? e0 + per : span;
+  int mine = 0;
+  for (int e = e0; e < e1; ++e) mine += (order_key(s_score[e]) >> 8) >= keep_from;
+  int total;
+  int pos = block_excl_scan<kDecWaves>(mine, s_tmp, total);
+  const int64_t lbase = ((int64_t)b * args.nblk + blockIdx.x) * args.kpb;
+  for (int e = e0; e < e1; ++e) {
+    const float v = s_score[e];
+    if ((order_key(v) >> 8) >= keep_from) {
+      args.cl_idx[lbase + pos] = (int32_t)(blk0 + e);
+      args.cl_sc[lbase + pos] = v;
+      ++pos;
     }
   }
-  __syncthreads();
+  if (tid == 0) args.cl_cnt[(int64_t)b * args.nblk + blockIdx.x] = total;
 }
 
 // One radix round over n LDS keys (only those matching prefix on pmask):
@@ -225,11 +306,17 @@ __device__ __forceinline__ int block_radix_lds(const uint32_t* keys, int n, int 
   return cnt;
 }
 
-// Exact multi-pass selection straight over the row in global memory (rows
-// whose threshold bin does not fit in LDS, or longer than the bitmap).
-__device__ void select_row_exact(const float* row, int64_t n, int K, int32_t* oidx, float* osc,
-                                 uint32_t* s_h, int* s_tmp, int* s_res) {
-  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+// Exact multi-pass selection over a row's compact lists in global memory
+// (rows whose threshold bin or whose flat list is too long for the finish pass).
+// The lists hold every score that can reach the top K, in ascending key order.
+__device__ void select_lists_exact(const DecodeArgs& args, int b, int nb, int32_t* oidx, float* osc,
+                                   uint32_t* s_h, int* s_tmp, int* s_res) {
+  const int tid = threadIdx.x;
+  const int K = args.K;
+  auto list = [&](int j, int64_t& lbase, int& c) __attribute__((always_inline)) {
+    lbase = ((int64_t)b * args.nblk + j) * args.kpb;
+    c = args.cl_cnt[(int64_t)b * args.nblk + j];
+  };
   uint32_t prefix = 0, pmask = 0;
   int krem = K;
   for (int round = 0; round < 3; ++round) {
@@ -238,9 +325,14 @@ __device__ void select_row_exact(const float* row, int64_t n, int K, int32_t* oi
     const uint32_t dmask = (uint32_t)nbins - 1;
     for (int i = tid; i < nbins; i += kSelThreads) s_h[i] = 0;
     __syncthreads();
-    for (int64_t e = tid; e < n; e += kSelThreads) {
-      const uint32_t key = order_key(row[e]);
-      if ((key & pmask) == prefix) atomicAdd(&s_h[(key >> shift) & dmask], 1u);
+    for (int j = 0; j < nb; ++j) {
+      int64_t lbase;
+      int c;
+      list(j, lbase, c);
+      for (int i = tid; i < c; i += kSelThreads) {
+        const uint32_t key = order_key(args.cl_sc[lbase + i]);
+        if ((key & pmask) == prefix) atomicAdd(&s_h[(key >> shift) & dmask], 1u);
+      }
     }
     __syncthreads();
     const int per = nbins / kSelThreads;
@@ -251,208 +343,230 @@ __device__ void select_row_exact(const float* row, int64_t n, int K, int32_t* oi
     __syncthreads();
   }
   const uint32_t kth = prefix;
-  const int keep_eq = krem;
-  // ordered emission: each wave owns a contiguous segment of the row
-  const int64_t seg = ((n + kSelWaves - 1) / kSelWaves + 63) / 64 * 64;
-  const int64_t s0 = (int64_t)wave * seg, s1 = s0 + seg < n ? s0 + seg : n;
-  int gt = 0, eq = 0;
-  for (int64_t base = s0; base < s1; base += 64) {
-    const int64_t e = base + l;
-    const bool in = e < s1;
-    const uint32_t key = in ? order_key(row[e]) : 0u;
-    gt += popc(ballot(in && key > kth));
-    eq += popc(ballot(in && key == kth));
-  }
-  if (l == 0) {
-    s_res[4 + wave] = gt;
-    s_res[4 + kSelWaves + wave] = eq;
-  }
-  __syncthreads();
-  int gt_before = 0, eq_before = 0;
-  for (int w2 = 0; w2 < wave; ++w2) {
-    gt_before += s_res[4 + w2];
-    eq_before += s_res[4 + kSelWaves + w2];
-  }
-  int out = gt_before + (eq_before < keep_eq ? eq_before : keep_eq);
-  int eq_seen = eq_before;
-  for (int64_t base = s0; base < s1; base += 64) {
-    const int64_t e = base + l;
-    const bool in = e < s1;
-    const float v = in ? row[e] : 0.0f;
-    const uint32_t key = order_key(v);
-    const bool g = in && key > kth;
-    const bool q = in && key == kth;
-    const uint64_t qm = ballot(q);
-    const bool keep = g || (q && eq_seen + rank_below(qm) < keep_eq);
-    eq_seen += popc(qm);
-    const uint64_t km = ballot(keep);
-    const int p = out + rank_below(km);
-    if (keep && p < K) {
-      oidx[p] = (int32_t)e;
-      if (osc) osc[p] = v;
+  const int keep_eq = krem;  // keys equal to kth: keep the keep_eq lowest indices
+  // ordered emission, 1024 list entries at a time
+  int out = 0, eq_seen = 0;
+  for (int j = 0; j < nb; ++j) {
+    int64_t lbase;
+    int c;
+    list(j, lbase, c);
+    for (int c0 = 0; c0 < c; c0 += kSelThreads) {
+      const int i = c0 + tid;
+      const bool in = i < c;
+      const float v = in ? args.cl_sc[lbase + i] : 0.0f;
+      const uint32_t key = order_key(v);
+      const bool g = in && key > kth;
+      const bool q = in && key == kth;
+      int qtot;
+      const int qbefore = block_excl_scan((int)q, s_tmp, qtot);
+      const bool keep = g || (q && eq_seen + qbefore < keep_eq);
+      int ktot;
+      const int kbefore = block_excl_scan((int)keep, s_tmp, ktot);
+      const int p = out + kbefore;
+      if (keep && p < K) {
+        oidx[p] = args.cl_idx[lbase + i];
+        if (osc) osc[p] = v;
+      }
+      out += ktot;
+      eq_seen += qtot;
     }
-    out += popc(km);
   }
 }
 
-// One row: top-K of logits[0..n) by (score desc, index asc), indices ascending.
-__global__ void __launch_bounds__(kSelThreads) decode_select_kernel(const DecodeArgs args) {
-  __shared__ uint32_t s_bits[kBitmapWords];
-  __shared__ uint32_t s_ckey[kCandCap];
-  __shared__ int32_t s_cidx[kCandCap];
+constexpr int kShift = 32 - kDecHistBits;  // order key -> histogram bin
+
+// Rounds of 1024 flat list entries the finish pass holds in registers:
+// longer flat lists take the exact path.
+constexpr int kFinishRounds = 36;
+
+// One row: top-K of its scores by (score desc, index asc), indices ascending.
+// The row's compact lists, read in span order, are one flat list in ascending
+// key order; flat position p = r*1024 + tid sits in thread tid's register r.
+__global__ void __launch_bounds__(kSelThreads) decode_finish_kernel(const DecodeArgs args) {
+  __shared__ uint32_t s_ckey[kDecCandCap];
+  __shared__ int32_t s_cidx[kDecCandCap];
   __shared__ uint32_t s_h[2048];
   __shared__ int s_tmp[kSelWaves];
   __shared__ int s_res[4 + 2 * kSelWaves];
   __shared__ int s_count;
+  __shared__ int s_pref[kSelThreads + 1];
+  __shared__ int s_wc[kFinishRounds * kSelWaves];
   const int b = blockIdx.x;
-  const int tid = threadIdx.x, l = tid & 63;
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
   int64_t n = args.seq_lens[b];
   n = n < 0 ? 0 : (n > args.Nmax ? args.Nmax : n);
   const int K = args.K;
-  const float* row = args.logits + (int64_t)b * args.ld;
   int32_t* oidx = args.out_idx + (int64_t)b * K;
   float* osc = args.out_score ? args.out_score + (int64_t)b * K : nullptr;
-  if (n <= K) {
-    for (int p = tid; p < K; p += kSelThreads) {
-      oidx[p] = p < n ? p : -1;
-      if (osc) osc[p] = p < n ? row[p] : -__builtin_inff();
+  const int nb = (int)((n + args.kpb - 1) / args.kpb);  // scan spans of the row
+  if (nb > kSelThreads) {
+    select_lists_exact(args, b, nb, oidx, osc, s_h, s_tmp, s_res);
+    return;
+  }
+  // list j covers flat positions [s_pref[j], s_pref[j+1])
+  {
+    const int c = tid < nb ? args.cl_cnt[(int64_t)b * args.nblk + tid] : 0;
+    int total;
+    const int before = block_excl_scan(c, s_tmp, total);
+    if (tid < nb) s_pref[tid] = before;
+    if (tid == 0) {
+      s_pref[nb] = total;
+      s_count = 0;
     }
+  }
+  __syncthreads();
+  const int flat = s_pref[nb];
+
+  // 1. threshold bin b* of the row histogram (4 bins per thread); rows of at
+  // most K keys keep everything
+  uint32_t bstar = 0;
+  int need = 0, inbin = 0;
+  if (n > K) {
+    const uint32_t* ghist = args.hist + (int64_t)b * kDecHistBins;
+    constexpr int kPer = kDecHistBins / kSelThreads;
+    block_find_digit(kPer, [&](int t, int i) { return (int)ghist[t * kPer + i]; }, K, s_tmp, s_res);
+    bstar = (uint32_t)s_res[0];
+    need = s_res[1];   // entries of bin b* that are selected
+    inbin = s_res[2];  // entries in bin b*
+    __syncthreads();
+  }
+  if (inbin > kDecCandCap || flat > kSelThreads * kFinishRounds) {
+    select_lists_exact(args, b, nb, oidx, osc, s_h, s_tmp, s_res);
     return;
   }
 
-  // 1. threshold bin b* from the row histogram (4 bins per thread)
-  const uint32_t* ghist = args.hist + (int64_t)b * kDecHistBins;
-  constexpr int kPer = kDecHistBins / kSelThreads;
-  block_find_digit(kPer, [&](int t, int i) { return (int)ghist[t * kPer + i]; }, K, s_tmp, s_res);
-  const uint32_t bstar = (uint32_t)s_res[0];
-  const int need = s_res[1];   // entries of bin b* that are selected
-  const int inbin = s_res[2];  // entries in bin b*
-  constexpr int kShift = 32 - kDecHistBits;
-  __syncthreads();
-  if (inbin > kCandCap || n > 32 * (int64_t)kBitmapWords) {
-    select_row_exact(row, n, K, oidx, osc, s_h, s_tmp, s_res);
-    return;
-  }
-
-  // 2. one pass: bitmap bits for everything above b*, LDS candidates inside b*
-  const int words = (int)((n + 31) / 32);
-  for (int i = tid; i < words; i += kSelThreads) s_bits[i] = 0;
-  if (tid == 0) s_count = 0;
-  __syncthreads();
-  for (int64_t wbase = (int64_t)(tid - l) * 4; wbase < n; wbase += (int64_t)kSelThreads * 4) {
-    const int64_t e0 = wbase + l * 4;  // whole waves iterate together (ballots below)
-    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (e0 + 3 < n) {
-      const float4 f = *(const float4*)(row + e0);
-      v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
-    } else {
-      for (int u = 0; u < 4; ++u) v[u] = e0 + u < n ? row[e0 + u] : 0.0f;
+  // 2. the flat list into registers: every load issued up front (positions
+  // past the end read entry 0 and are marked invalid); entries of b* to LDS
+  // the list holding the first position of each (round, wave) block of 64
+  for (int i = tid; i < kFinishRounds * kSelWaves; i += kSelThreads) {
+    const int p = (i / kSelWaves) * kSelThreads + (i % kSelWaves) * 64;
+    int lo = 0, hi = nb - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_pref[mid] <= p) lo = mid; else hi = mid - 1;
     }
-    uint32_t mine = 0;
+    s_wc[i] = lo;
+  }
+  __syncthreads();
+  const int64_t row0 = (int64_t)b * args.nblk * args.kpb;
+  uint32_t key[kFinishRounds];
+  int32_t idx[kFinishRounds];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const bool in = e0 + u < n;
-      const uint32_t key = order_key(v[u]);
-      const uint32_t bin = key >> kShift;
-      if (in && bin > bstar) mine |= 1u << ((e0 + u) & 31);
-      const bool cand = in && bin == bstar;
+  for (int r = 0; r < kFinishRounds; ++r) {
+    const int p = r * kSelThreads + tid;
+    int j = s_wc[r * kSelWaves + wave];
+    while (j + 1 < nb && s_pref[j + 1] <= p) ++j;
+    const int64_t at = p < flat ? row0 + (int64_t)j * args.kpb + (p - s_pref[j]) : row0;
+    key[r] = order_key(args.cl_sc[at]);
+    idx[r] = args.cl_idx[at];
+  }
+  __syncthreads();  // s_wc is reused below
+#pragma unroll
+  for (int r = 0; r < kFinishRounds; ++r) {
+    if (r * kSelThreads + tid >= flat) idx[r] = -1;
+    if (n > K && r * kSelThreads < flat) {
+      const bool cand = idx[r] >= 0 && (key[r] >> kShift) == bstar;
       const uint64_t m = ballot(cand);
       if (m) {
         const int fl = first_lane(m);
         int base = 0;
         if (l == fl) base = atomicAdd(&s_count, popc(m));
-        base = shfl(base, fl);
-        if (cand) {
-          const int p = base + rank_below(m);
-          if (p < kCandCap) {
-            s_ckey[p] = key;
-            s_cidx[p] = (int32_t)(e0 + u);
-          }
+        base = shfl(base, fl) + rank_below(m);
+        if (cand && base < kDecCandCap) {
+          s_ckey[base] = key[r];
+          s_cidx[base] = idx[r];
         }
       }
     }
-    if (mine && e0 < n) atomicOr(&s_bits[e0 >> 5], mine);
-  }
-  __syncthreads();
-  const int nc = s_count < kCandCap ? s_count : kCandCap;
-
-  // 3. exact K-th key among the candidates (the low 20 bits, two rounds)
-  uint32_t prefix = bstar << kShift, pmask = ~0u << kShift;
-  int krem = need;
-  block_radix_lds(s_ckey, nc, 10, 1024, prefix, pmask, krem, s_h, s_tmp, s_res);
-  const int n_eq = block_radix_lds(s_ckey, nc, 0, 1024, prefix, pmask, krem, s_h, s_tmp, s_res);
-  const uint32_t kth = prefix;
-  const int keep_eq = krem;  // of the n_eq candidates equal to kth keep the keep_eq lowest indices
-
-  // 4. ties at kth: the keep_eq-th largest ~index among them is the cut
-  uint32_t idx_cut = 0u;  // an equal key is kept when ~index >= idx_cut
-  if (keep_eq < n_eq) {
-    uint32_t tp = 0, tm = 0;
-    int tk = keep_eq;
-    for (int round = 0; round < 3; ++round) {
-      const int shift = round == 0 ? 21 : (round == 1 ? 10 : 0);
-      const int nbins = round == 2 ? 1024 : 2048;
-      const uint32_t dmask = (uint32_t)nbins - 1;
-      for (int i = tid; i < nbins; i += kSelThreads) s_h[i] = 0;
-      __syncthreads();
-      for (int i = tid; i < nc; i += kSelThreads) {
-        if (s_ckey[i] != kth) continue;
-        const uint32_t r = ~(uint32_t)s_cidx[i];
-        if ((r & tm) == tp) atomicAdd(&s_h[(r >> shift) & dmask], 1u);
-      }
-      __syncthreads();
-      const int per = (nbins + kSelThreads - 1) / kSelThreads;
-      block_find_digit(per,
-                       [&](int t, int i) { return t * per + i < nbins ? (int)s_h[t * per + i] : 0; },
-                       tk, s_tmp, s_res);
-      tp |= (uint32_t)s_res[0] << shift;
-      tm |= dmask << shift;
-      tk = s_res[1];
-      __syncthreads();
-    }
-    idx_cut = tp;
-  }
-  for (int i = tid; i < nc; i += kSelThreads) {
-    const uint32_t key = s_ckey[i];
-    const uint32_t e = (uint32_t)s_cidx[i];
-    if (key > kth || (key == kth && ~e >= idx_cut)) atomicOr(&s_bits[e >> 5], 1u << (e & 31));
   }
   __syncthreads();
 
-  // 5. emit in ascending index: prefix popcount over the bitmap
-  const int wpt = (words + kSelThreads - 1) / kSelThreads;
-  const int w0 = tid * wpt, w1 = w0 + wpt < words ? w0 + wpt : words;
-  int cnt = 0;
-  for (int wd = w0; wd < w1; ++wd) cnt += __popc(s_bits[wd]);
-  int total;
-  int pos = block_excl_scan(cnt, s_tmp, total);
-  for (int wd = w0; wd < w1; ++wd) {
-    uint32_t bits = s_bits[wd];
-    while (bits) {
-      const int bit = __ffs(bits) - 1;
-      bits &= bits - 1;
-      const int64_t e = (int64_t)wd * 32 + bit;
-      if (pos < K) {
-        oidx[pos] = (int32_t)e;
-        if (osc) osc[pos] = row[e];
+  // 3. the exact K-th key among the candidates (the low 20 bits, two rounds);
+  // the lists hold every entry of bin b*, so there are exactly `inbin`
+  uint32_t kth = 0u, idx_cut = 0u;  // selected: key > kth, or key == kth and ~index >= idx_cut
+  if (n > K) {
+    const int nc = inbin;
+    uint32_t prefix = bstar << kShift, pmask = ~0u << kShift;
+    int krem = need;
+    block_radix_lds(s_ckey, nc, 10, 1024, prefix, pmask, krem, s_h, s_tmp, s_res);
+    const int n_eq = block_radix_lds(s_ckey, nc, 0, 1024, prefix, pmask, krem, s_h, s_tmp, s_res);
+    kth = prefix;
+    const int keep_eq = krem;  // of the n_eq candidates equal to kth keep the keep_eq lowest indices
+    // 4. ties at kth: the keep_eq-th largest ~index among them is the cut
+    if (keep_eq < n_eq) {
+      uint32_t tp = 0, tm = 0;
+      int tk = keep_eq;
+      for (int round = 0; round < 3; ++round) {
+        const int shift = round == 0 ? 21 : (round == 1 ? 10 : 0);
+        const int nbins = round == 2 ? 1024 : 2048;
+        const uint32_t dmask = (uint32_t)nbins - 1;
+        for (int i = tid; i < nbins; i += kSelThreads) s_h[i] = 0;
+        __syncthreads();
+        for (int i = tid; i < nc; i += kSelThreads) {
+          if (s_ckey[i] != kth) continue;
+          const uint32_t rr = ~(uint32_t)s_cidx[i];
+          if ((rr & tm) == tp) atomicAdd(&s_h[(rr >> shift) & dmask], 1u);
+        }
+        __syncthreads();
+        const int pb = (nbins + kSelThreads - 1) / kSelThreads;
+        block_find_digit(pb,
+                         [&](int t, int i) { return t * pb + i < nbins ? (int)s_h[t * pb + i] : 0; },
+                         tk, s_tmp, s_res);
+        tp |= (uint32_t)s_res[0] << shift;
+        tm |= dmask << shift;
+        tk = s_res[1];
+        __syncthreads();
       }
-      ++pos;
+      idx_cut = tp;
     }
+  }
+
+  // 5. emit in ascending index = flat order: selected counts per (round,
+  // wave), one prefix sum over them, then each lane's rank inside its wave
+  auto selected = [&](int r) __attribute__((always_inline)) {
+    return idx[r] >= 0 && (key[r] > kth || (key[r] == kth && ~(uint32_t)idx[r] >= idx_cut));
+  };
+#pragma unroll
+  for (int r = 0; r < kFinishRounds; ++r) {
+    const int c = popc(ballot(selected(r)));
+    if (l == 0) s_wc[r * kSelWaves + wave] = c;
+  }
+  __syncthreads();
+  {
+    const int v = tid < kFinishRounds * kSelWaves ? s_wc[tid] : 0;
+    int total;
+    const int before = block_excl_scan(v, s_tmp, total);
+    if (tid < kFinishRounds * kSelWaves) s_wc[tid] = before;
+    if (tid == 0) s_count = total;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kFinishRounds; ++r) {
+    const bool sel = selected(r);
+    const int pos = s_wc[r * kSelWaves + wave] + rank_below(ballot(sel));
+    if (sel && pos < K) {
+      oidx[pos] = idx[r];
+      if (osc) osc[pos] = key_to_float(key[r]);
+    }
+  }
+  const int total = s_count;
+  for (int p = (total < K ? total : K) + tid; p < K; p += kSelThreads) {
+    oidx[p] = -1;
+    if (osc) osc[p] = -__builtin_inff();
   }
 }
 
 template <int MT, int D>
 static hipError_t launch_dec(const DecodeArgs& a, hipStream_t stream) {
-  const int64_t bx = (a.Nmax + kDecKeysPerBlock - 1) / kDecKeysPerBlock;
   if (a.B <= 0) return hipSuccess;
   hipError_t e = launch_fill_i32((int32_t*)a.hist, (int64_t)a.B * kDecHistBins, 0, stream);
   if (e != hipSuccess) return e;
-  if (bx > 0)
-    hipLaunchKernelGGL((decode_scan_kernel<MT, D>), dim3((unsigned)bx, (unsigned)a.B),
+  if (a.nblk > 0)
+    hipLaunchKernelGGL((decode_scan_kernel<MT, D>), dim3((unsigned)a.nblk, (unsigned)a.B),
                        dim3(kDecThreads), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_select_kernel, dim3((unsigned)a.B), dim3(kSelThreads), 0, stream, a);
+  hipLaunchKernelGGL(decode_finish_kernel, dim3((unsigned)a.B), dim3(kSelThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -14,6 +14,10 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Word 3 of a raw buffer resource on gfx9 (32-bit data format, no swizzle):
+// loads past num_records return zeros and stores past it are dropped.
+constexpr int kBufferWord3 = 0x00020000;
+
 enum { kBF16 = 1, kFP8 = 2 };
 
 // fp32 -> uint32 such that a > b (as reals, -0 == +0 after canonicalisation)

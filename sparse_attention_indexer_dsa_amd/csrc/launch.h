@@ -39,8 +39,9 @@ hipError_t launch_scan_topk(const ScanArgs& a, int dtype, hipStream_t stream);
 constexpr int kDecHistBits = 12;
 constexpr int kDecHistBins = 1 << kDecHistBits;
 
-// Decode: scores of one bf16 query per sequence against its E4M3 cache,
-// written to logits [B, Nmax] (fp32), then a per-row top-K.
+// Decode: scores of one bf16 query per sequence against its E4M3 cache, then
+// a per-row top-K.  Scan workgroups cover kpb keys of a row each and keep, in
+// a compact list, only the scores that can still reach the row's top K.
 struct DecodeArgs {
   const void* q;          // [B, H, d] bf16
   const uint8_t* kc;      // [B, Nmax, d] E4M3
@@ -50,12 +51,18 @@ struct DecodeArgs {
   int B, H, d;
   int64_t Nmax;
   int K;
-  float* logits;          // [B, ld] workspace, ld >= Nmax and a multiple of 4
-  int64_t ld;
-  uint32_t* hist;         // [B, kDecHistBins] workspace
+  int64_t kpb;            // keys per scan workgroup: a multiple of 256, <= kDecMaxKpb
+  int nblk;               // scan workgroups per row: ceil(Nmax / kpb)
+  uint32_t* hist;         // [B, kDecHistBins] workspace, zeroed per call
+  int32_t* cl_cnt;        // [B, nblk] entries of each workgroup's compact list
+  int32_t* cl_idx;        // [B, nblk, kpb] key indices of the compact lists (ascending)
+  float* cl_sc;           // [B, nblk, kpb] their scores
   int32_t* out_idx;       // [B, K]
   float* out_score;       // [B, K] or nullptr
 };
+constexpr int kDecKeysPerPass = 768;  // keys one scan workgroup scores per loop trip
+constexpr int kDecMaxKpb = 16384;     // keys per scan workgroup at most (its LDS score stage)
+constexpr int kDecCandCap = 8192;     // threshold-bin candidates a row keeps in LDS
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
