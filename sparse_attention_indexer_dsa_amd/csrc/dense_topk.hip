@@ -1,0 +1,408 @@
+// dense_topk.hip -- the dense causal indexer for 33..64 heads at d = 128 on
+// gfx950: score + streaming top-K per query (ADIndex (Qi et al.), Section 3,
+// Eq. (1) and Eq. (2)), the layout the long-context prefill runs in.
+//
+// One wavefront owns one query (at position pos0 + j * pos_stride) and walks
+// its candidate keys 0..t in ascending index; the 8 waves of a workgroup own 8
+// consecutive queries and share one stream of 64-key tiles.
+//
+//   * Tiles go from HBM straight into a five-stage LDS ring with
+//     global_load_lds (no register staging): tile t is requested four steps
+//     before it is scored, into stage t % 5.  Each lane's 16-byte chunk lands
+//     at lane*16 of the wave's 1 KB, so the ring holds every key row with its
+//     16-byte chunks XOR-swizzled by the row index; the MFMA operand reads are
+//     then free of bank conflicts without padding.
+//   * Per-head dot products: fp8 v_mfma_f32_32x32x64_f8f6f4 or bf16
+//     v_mfma_f32_32x32x16_bf16, heads on M (two 32-row tiles), keys on N,
+//     fp32 accumulation; B operands are read from LDS one 32-key sub-tile
+//     ahead of their MFMAs.
+//   * ReLU through the identity w*ReLU(s) = (w/2)*|s| + (w/2)*s: the first
+//     term is one FMA with an |.| source modifier per (head, key), the second
+//     summed over heads is (sum_j (w_j/2) q_j) . k, a single dot product per
+//     (query, key) that the workgroup computes with bf16 16x16x32 MFMAs.  Its
+//     query vector is split into a bf16 high and low part (16 significant
+//     bits; every E4M3 and bf16 key element is exact in bf16), so it keeps
+//     integer-valued inputs exact and otherwise errs by about 2^-17 relative
+//     to the score's magnitude.
+//   * Streaming top-K exactly as the general kernel: scores that beat the
+//     running threshold are staged in LDS, flushed to the query's candidate
+//     buffer, and compacted by a wave radix select when it fills; keys arrive
+//     in ascending index, so strict ">" keeps the lower index on ties.
+#include "device.h"
+#include "launch.h"
+
+namespace dsaidx {
+
+namespace {
+
+constexpr int kTile = 64;       // keys per step
+constexpr int kStages = 5;      // LDS ring stages
+constexpr int kAhead = 4;       // a tile is requested this many steps before it is scored
+constexpr int kWaves = 8;       // queries per workgroup
+constexpr int kThreads = kWaves * 64;
+constexpr int kStage = kSelectHistWords / 2;  // LDS append stage entries per wave
+constexpr int kD = 128;
+
+template <int DT>
+struct Cfg {
+  static constexpr int kRowBytes = DT == kBF16 ? 2 * kD : kD;
+  static constexpr int kTileBytes = kTile * kRowBytes;
+  static constexpr int kChunksPerRow = kRowBytes / 16;
+  static constexpr int kDma = kTileBytes / (kThreads * 16);  // 16-byte DMAs per lane per tile
+  static constexpr int kSteps = DT == kBF16 ? kD / 16 : kD / 64;  // main MFMA k-steps
+  // vm operations a wave issues per step: the tile chunks and the key scales
+  static constexpr int kVmPerStep = kDma + 1;
+};
+
+template <int DT>
+struct AFrag;
+template <>
+struct AFrag<kBF16> { typedef v8bf type; };
+template <>
+struct AFrag<kFP8> { typedef v8i type; };
+
+template <int DT>
+__device__ __forceinline__ v16f mfma(const typename AFrag<DT>::type& a,
+                                     const typename AFrag<DT>::type& b, v16f c) {
+  if constexpr (DT == kBF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ uint16_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+template <int DT>
+__global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs args) {
+  using C = Cfg<DT>;
+  using Frag = typename AFrag<DT>::type;
+  __shared__ __attribute__((aligned(16))) uint8_t s_tile[kStages][C::kTileBytes];
+  __shared__ float s_ks[kStages][kTile];
+  __shared__ __attribute__((aligned(16))) uint32_t s_hist[kWaves][kSelectHistWords];
+  __shared__ float s_lin[2][2][kWaves][kTile];                    // [parity][d half][query][key]
+  __shared__ __attribute__((aligned(16))) uint16_t s_qt[kWaves][2][kD];  // bf16 hi / lo of q-tilde
+  __shared__ int s_need[3];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63;
+  const int h = l >> 5;    // which half of the k range / which 16 of each 32 heads
+  const int col = l & 31;  // MFMA column = key within a 32-key sub-tile
+
+  // queries of this workgroup: the longest candidate lists are launched first
+  const int j_hi = (int)args.nq - (int)blockIdx.x * kWaves - 1;
+  const int j = j_hi - (kWaves - 1) + wave;
+  const bool active = j >= 0;
+  const int jq = active ? j : 0;
+  const int pos0 = (int)args.pos0;
+  const int ncand_blk = pos0 + j_hi * args.pos_stride + 1;           // keys 0 .. t_hi
+  const int ncand_me = active ? pos0 + j * args.pos_stride + 1 : 0;  // keys 0 .. t
+  const int ntiles = (ncand_blk + kTile - 1) / kTile;
+
+  // ---- this wave's query: A fragments, gate weights (w/2, with the fp8 query
+  // scale folded in), and q-tilde = sum_j (w_j/2) q_j split into bf16 hi + lo
+  Frag a[2][C::kSteps];
+  float wv[2][16];
+  {
+    const float qs = (DT == kFP8 && active) ? args.q_scale[jq] : 1.0f;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int head = 32 * m + col;
+      const bool hv = active && head < args.H;
+      const uint8_t* qrow =
+          (const uint8_t*)args.q + ((int64_t)jq * args.H + (hv ? head : 0)) * C::kRowBytes;
+#pragma unroll
+      for (int s = 0; s < C::kSteps; ++s) {
+        if constexpr (DT == kBF16) {
+          u32x4 v = hv ? *(const u32x4*)(qrow + h * kD + 16 * s) : u32x4{0, 0, 0, 0};
+          a[m][s] = __builtin_bit_cast(v8bf, v);
+        } else {
+          u32x4 v0 = hv ? *(const u32x4*)(qrow + h * 64 + 32 * s) : u32x4{0, 0, 0, 0};
+          u32x4 v1 = hv ? *(const u32x4*)(qrow + h * 64 + 32 * s + 16) : u32x4{0, 0, 0, 0};
+          struct { u32x4 lo, hi; } pr = {v0, v1};
+          a[m][s] = __builtin_bit_cast(v8i, pr);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int hr = 32 * m + 8 * (r >> 2) + 4 * h + (r & 3);
+        wv[m][r] = (active && hr < args.H) ? 0.5f * args.w[(int64_t)jq * args.H + hr] * qs : 0.0f;
+      }
+    }
+    // q-tilde: lane l owns elements 2l and 2l+1
+    float t0 = 0.0f, t1 = 0.0f;
+    if (active) {
+      const uint8_t* qb = (const uint8_t*)args.q + (int64_t)jq * args.H * C::kRowBytes;
+      for (int hd = 0; hd < args.H; ++hd) {
+        const float wh = 0.5f * args.w[(int64_t)jq * args.H + hd] * qs;
+        float x0, x1;
+        if constexpr (DT == kBF16) {
+          const uint32_t v = *(const uint32_t*)(qb + (int64_t)hd * C::kRowBytes + 4 * l);
+          x0 = __uint_as_float(v << 16);
+          x1 = __uint_as_float(v & 0xFFFF0000u);
+        } else {
+          const uint32_t v = *(const uint16_t*)(qb + (int64_t)hd * C::kRowBytes + 2 * l);
+          const v2bf p = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, false);
+          x0 = (float)p[0];
+          x1 = (float)p[1];
+        }
+        t0 = fmaf(wh, x0, t0);
+        t1 = fmaf(wh, x1, t1);
+      }
+    }
+    const uint16_t h0 = bf16_rne(t0), h1 = bf16_rne(t1);
+    s_qt[wave][0][2 * l] = h0;
+    s_qt[wave][0][2 * l + 1] = h1;
+    s_qt[wave][1][2 * l] = bf16_rne(t0 - __uint_as_float((uint32_t)h0 << 16));
+    s_qt[wave][1][2 * l + 1] = bf16_rne(t1 - __uint_as_float((uint32_t)h1 << 16));
+  }
+
+  // ---- the linear-term MFMA of this wave: keys 16*nb .. +15 of a tile, the
+  // d half kh (k-steps 2kh, 2kh+1 of 32), all 8 queries x {hi, lo} on M
+  const int nb = wave & 3, kh = wave >> 2;
+  v8bf la[2];
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int m = l & 15;
+    la[s] = __builtin_bit_cast(v8bf, *(const u32x4*)&s_qt[m >> 1][m & 1][32 * (2 * kh + s) + 8 * (l >> 4)]);
+  }
+
+  uint32_t* ckey = args.cand_key + (int64_t)jq * args.cap;  // raw fp32 scores
+  int32_t* cidx = args.cand_idx + (int64_t)jq * args.cap;
+  uint32_t* hist = s_hist[wave];
+  // Scores that enter are staged in this wave's LDS (the selection histogram's
+  // words, free outside a selection) and flushed to the candidate buffer when
+  // the stage nears full.  A flush does not wait for its stores: the wait is
+  // where the buffer is read back.
+  uint32_t* stage_key = hist;
+  int32_t* stage_idx = (int32_t*)(hist + kStage);
+  int cnt = 0;                                        // entries in the buffer
+  int nst = 0;                                        // entries in the LDS stage
+  float thr = active ? -__builtin_inff() : __builtin_inff();  // scores must exceed it
+  auto flush = [&]() __attribute__((always_inline)) {
+    for (int e = l; e < nst; e += 64) {
+      ckey[cnt + e] = stage_key[e];
+      cidx[cnt + e] = stage_idx[e];
+    }
+    cnt += nst;
+    nst = 0;
+  };
+  // A wave whose buffer passes `lim` raises the flag of the current step; after
+  // the step's barrier every wave holding more than K entries compacts.  A
+  // step appends at most 64 entries, so the buffer cannot overflow meanwhile.
+  const int lim = args.cap - 192;
+  if (tid < 3) s_need[tid] = 0;
+
+  // ---- tile requests: this lane's chunks of tile t into LDS stage `st`
+  auto request = [&](int t, int st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int n = 0; n < C::kDma; ++n) {
+      const int ci = n * kThreads + wave * 64 + l;  // chunk position in the stage
+      const int r = ci / C::kChunksPerRow, cs = ci % C::kChunksPerRow;
+      const int tok = min(t * kTile + r, ncand_blk - 1);
+      const uint8_t* g = (const uint8_t*)args.k + (int64_t)tok * C::kRowBytes + 16 * (cs ^ (r & 7));
+      __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)&s_tile[st][(n * kThreads + wave * 64) * 16],
+                                       16, 0, 0);
+    }
+    // every wave writes the same 64 scales (fp8), or a placeholder word (bf16),
+    // so all waves issue the same number of requests per step
+    const int tok = min(t * kTile + l, ncand_blk - 1);
+    const float* g = DT == kFP8 ? args.k_scale + tok : args.w;
+    __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)&s_ks[st][0], 4, 0, 0);
+  };
+
+  // B operands of sub-tile u of the tile in stage st (row = 32u + col, and
+  // row & 7 == col & 7 undoes the swizzle)
+  auto load_b = [&](Frag (&bf)[C::kSteps], int st, int u) __attribute__((always_inline)) {
+    const uint8_t* row = &s_tile[st][(32 * u + col) * C::kRowBytes];
+    const int x = col & 7;
+#pragma unroll
+    for (int s = 0; s < C::kSteps; ++s) {
+      if constexpr (DT == kBF16) {
+        bf[s] = __builtin_bit_cast(v8bf, *(const u32x4*)(row + 16 * ((8 * h + s) ^ x)));
+      } else {
+        const int c0 = 4 * h + 2 * s;
+        struct { u32x4 lo, hi; } pr = {*(const u32x4*)(row + 16 * (c0 ^ x)),
+                                       *(const u32x4*)(row + 16 * ((c0 + 1) ^ x))};
+        bf[s] = __builtin_bit_cast(v8i, pr);
+      }
+    }
+  };
+  auto mfma_sub = [&](v16f (&acc)[2], const Frag (&bf)[C::kSteps]) __attribute__((always_inline)) {
+    acc[0] = v16f{};
+    acc[1] = v16f{};
+#pragma unroll
+    for (int s = 0; s < C::kSteps; ++s) {
+      acc[0] = mfma<DT>(a[0][s], bf[s], acc[0]);
+      acc[1] = mfma<DT>(a[1][s], bf[s], acc[1]);
+    }
+  };
+  // sum over this lane's 32 heads of (w/2)*|s|
+  auto abs_sum = [&](const v16f (&acc)[2]) __attribute__((always_inline)) -> float {
+    float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        s0 = fmaf(wv[m][r], __builtin_fabsf(acc[m][r]), s0);
+        s1 = fmaf(wv[m][r + 1], __builtin_fabsf(acc[m][r + 1]), s1);
+      }
+    }
+    return s0 + s1;
+  };
+  // the linear term of tile t (stage st) for all 8 queries: this wave's 16
+  // keys and d half, written to s_lin[t & 1][kh]
+  auto linear = [&](int t, int st) __attribute__((always_inline)) {
+    v4f c = {0.0f, 0.0f, 0.0f, 0.0f};
+    const int r = 16 * nb + (l & 15);
+    const uint8_t* row = &s_tile[st][r * C::kRowBytes];
+    const int x = r & 7;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int ks = 2 * kh + s;  // d elements 32ks + 8(l>>4) .. +7
+      v8bf kb;
+      if constexpr (DT == kBF16) {
+        kb = __builtin_bit_cast(v8bf, *(const u32x4*)(row + 16 * ((4 * ks + (l >> 4)) ^ x)));
+      } else {
+        const int d0 = 32 * ks + 8 * (l >> 4);
+        const uint2 v = *(const uint2*)(row + 16 * ((d0 >> 4) ^ x) + (d0 & 15));
+        const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, false);
+        const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, true);
+        const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, false);
+        const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, true);
+        kb = v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+      }
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(la[s], kb, c, 0, 0, 0);
+    }
+    // rows 4(l>>4)+i = (query 2(l>>4) + i/2, part i%2)
+    const int q0 = 2 * (l >> 4);
+    s_lin[t & 1][kh][q0][r] = c[0] + c[1];
+    s_lin[t & 1][kh][q0 + 1][r] = c[2] + c[3];
+  };
+  // the full score of sub-tile u's key in this lane's column (both lane halves
+  // hold it after the swap): (sum over heads of (w/2)|s| + linear term) * scale
+  auto sub_score = [&](float part, int t, int st, int u) __attribute__((always_inline)) -> float {
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false,
+                                               false);
+    const int kk = 32 * u + col;
+    float sc = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) +
+               (s_lin[t & 1][0][wave][kk] + s_lin[t & 1][1][wave][kk]);
+    if constexpr (DT == kFP8) sc *= s_ks[st][kk];
+    return sc;
+  };
+  // append the step's scores that beat the threshold: lane l holds candidate
+  // tbase + l, so lane order is candidate order and one ballot serves 64
+  auto append = [&](float sc, int tbase, int flag) __attribute__((always_inline)) {
+    uint64_t tm = ballot(sc > thr);
+    if (tbase + kTile > ncand_me) tm &= ballot(tbase + l < ncand_me);  // the query's last tile
+    if (tm) {
+      if ((tm >> l) & 1) {
+        const int p = nst + rank_below(tm);
+        stage_key[p] = __float_as_uint(sc);
+        stage_idx[p] = tbase + l;
+      }
+      nst += popc(tm);
+      if (cnt + nst > lim && l == 0) s_need[flag] = 1;
+    }
+  };
+  constexpr int kValuPerMfma = 8;
+  auto interleave = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 2 * C::kSteps; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
+    }
+  };
+
+  // ---- prologue: tiles 0..3 requested, tile 0's linear term, first MFMAs
+  for (int t = 0; t < kAhead; ++t) request(min(t, ntiles - 1), t);
+  __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): tiles 0..3 in LDS
+  __syncthreads();
+  linear(0, 0);
+  v16f acc0[2], acc1[2];
+  Frag bA[C::kSteps], bB[C::kSteps];
+  load_b(bA, 0, 0);
+  mfma_sub(acc0, bA);
+  load_b(bB, 0, 1);
+  __syncthreads();  // s_lin of tile 0
+
+  // step i scores tile i (stage i % 5) while tile i+1 (stage (i+1) % 5) feeds
+  // the next MFMAs and its linear term, and tile i+4 is requested into stage
+  // (i+4) % 5, the one tile i-1 left.  On entry bB holds tile i's second
+  // sub-tile's B operands and acc0 its first sub-tile's products.
+  for (int i = 0; i < ntiles; ++i) {
+    const int st = i % kStages, st1 = (i + 1) % kStages, st4 = (i + kAhead) % kStages;
+    const int flag = i % 3, flag_prev = (i + 2) % 3, flag_next = (i + 1) % 3;
+    // compaction requests raised during step i-1 (seen after its barrier)
+    if (i > 0 && s_need[flag_prev] && active && cnt + nst > args.K) {
+      flush();
+      thr = wave_select_topk(ckey, cidx, cnt, args.K, hist);
+      cnt = args.K;
+    } else if (nst > kStage - 64) {
+      flush();
+    }
+    if (tid == 0) s_need[flag_next] = 0;
+    request(min(i + kAhead, ntiles - 1), st4);
+    const int tbase = i * kTile;
+    // the same work every step: past the last tile the MFMAs rerun tile
+    // ntiles-1 and the append masks them out
+    load_b(bA, st1, 0);
+    mfma_sub(acc1, bB);
+    const float p0 = abs_sum(acc0);
+    interleave();
+    load_b(bB, st1, 1);
+    mfma_sub(acc0, bA);
+    const float p1 = abs_sum(acc1);
+    interleave();
+    linear(i + 1, st1);
+    const float sc0 = sub_score(p0, i, st, 0);
+    const float sc1 = sub_score(p1, i, st, 1);
+    append(l < 32 ? sc0 : sc1, tbase, flag);
+    // tile i+2 must have landed before the barrier publishes it: after its
+    // requests this wave issued those of tiles i+3 and i+4 (and maybe a
+    // flush's stores, which only makes the count conservative)
+    if constexpr (C::kVmPerStep == 2) __builtin_amdgcn_s_waitcnt(0x3F70 | 4);
+    else __builtin_amdgcn_s_waitcnt(0x3F70 | 6);
+    __syncthreads();
+  }
+
+  if (!active) return;
+  flush();
+  wave_mem_fence();
+  if (cnt > args.K) {
+    wave_select_topk(ckey, cidx, cnt, args.K, hist);
+    cnt = args.K;
+  }
+  int32_t* oidx = args.out_idx + (int64_t)j * args.out_stride;
+  float* osc = args.out_score ? args.out_score + (int64_t)j * args.out_stride : nullptr;
+  for (int p = l; p < args.K; p += 64) {
+    const bool v = p < cnt;
+    oidx[p] = v ? cidx[p] : -1;
+    if (osc) osc[p] = v ? __uint_as_float(ckey[p]) : -__builtin_inff();
+  }
+}
+
+}  // namespace
+
+bool dense_topk_supported(const ScanArgs& a) {
+  return a.bank == nullptr && a.H > 32 && a.H <= 64 && a.d == kD;
+}
+
+hipError_t launch_dense_topk(const ScanArgs& a, int dtype, hipStream_t stream) {
+  const int64_t blocks = (a.nq + kWaves - 1) / kWaves;
+  if (blocks <= 0) return hipSuccess;
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(dense_topk_kernel<kBF16>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(dense_topk_kernel<kFP8>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace dsaidx

@@ -87,7 +87,9 @@ __global__ void __launch_bounds__(WPB * 64, 2) scan_topk_kernel(const ScanArgs a
   __shared__ int s_need[3];  // compaction requests of steps i % 3
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // wave-uniform by construction; readfirstlane lets the compiler see it, so
+  // every per-query condition below is a scalar branch, not an exec-mask dance
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63;
   const int h = l >> 5;    // which half of the k range / which 16 of each 32 heads
   const int col = l & 31;  // MFMA column = key within a 32-key sub-tile
@@ -164,9 +166,10 @@ __global__ void __launch_bounds__(WPB * 64, 2) scan_topk_kernel(const ScanArgs a
   uint32_t* hist = s_hist[wave];
   // Scores that enter are first staged in this wave's LDS (the selection
   // histogram's words, free outside a selection) and flushed to the global
-  // buffer in order when the stage nears full: the tile loop then issues no
-  // global stores, which would share the in-order load counter with the tile
-  // prefetches and force them to drain.
+  // buffer in order when the stage nears full: the tile loop then issues few
+  // global stores.  A flush does not wait for its stores (a wait would drain
+  // the tile prefetches queued before them on the same in-order counter);
+  // they are waited for only where the buffer is read back.
   uint32_t* stage_key = hist;
   int32_t* stage_idx = (int32_t*)(hist + kStageEntries);
   int cnt = 0;                       // entries in the global buffer (wave-uniform)
@@ -179,7 +182,6 @@ __global__ void __launch_bounds__(WPB * 64, 2) scan_topk_kernel(const ScanArgs a
     }
     cnt += nst;
     nst = 0;
-    wave_mem_fence();  // the stores are drained here, not in the tile loop
   };
   // A wave whose buffer passes `lim` raises the flag of the current step; after
   // that step's barrier every wave holding more than K entries compacts, so the
@@ -249,26 +251,28 @@ __global__ void __launch_bounds__(WPB * 64, 2) scan_topk_kernel(const ScanArgs a
     for (int m = 0; m < MT; ++m) gated_relu_sum16(wv[m], acc[m], s0, s1);
     return s0 + s1;
   };
-  // finish the score of sub-tile u (candidates tbase+32u..) and append it if
-  // it beats the threshold.  The partial sums start at +0 and every ReLU term
-  // is >= +0, so no score is -0.
-  auto finish_sub = [&](float part, int buf, int u, int tbase, int step_buf) __attribute__((always_inline)) {
-    // the other 16*MT heads of this key live in lane l ^ 32
+  // the full score of sub-tile u's key in this lane's column; the other
+  // 16*MT heads of that key live in lane l ^ 32, so after the swap both lane
+  // halves hold the sum.  The partial sums start at +0 and every ReLU term is
+  // >= +0, so no score is -0.
+  auto sub_score = [&](float part, int buf, int u) __attribute__((always_inline)) -> float {
     auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false,
                                                false);
     float sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    const int kk = 32 * u + col;  // key within the tile
-    if constexpr (DT == kFP8) sc *= s_kscale[buf][kk];
-    // lanes l and l+32 hold the same key: only the low half appends
-    const int c0 = tbase + 32 * u;
-    uint64_t tm = ballot(sc > thr) & 0xFFFFFFFFull;
-    if (c0 + 32 > ncand_me) tm &= ballot(c0 + col < ncand_me);  // the query's last sub-tile
-    const bool take = (tm >> l) & 1;
+    if constexpr (DT == kFP8) sc *= s_kscale[buf][32 * u + col];
+    return sc;
+  };
+  // append the step's scores that beat the threshold: lane l holds candidate
+  // tbase + l (sub-tile 0 in the low lane half, sub-tile 1 in the high half),
+  // so lane order is candidate order and one ballot serves 64 candidates
+  auto append = [&](float sc, int buf, int tbase, int step_buf) __attribute__((always_inline)) {
+    uint64_t tm = ballot(sc > thr);
+    if (tbase + kTileKeys > ncand_me) tm &= ballot(tbase + l < ncand_me);  // the query's last tile
     if (tm) {
-      if (take) {
+      if ((tm >> l) & 1) {
         const int p = nst + rank_below(tm);
         stage_key[p] = __float_as_uint(sc);
-        stage_idx[p] = s_tok[buf][kk];
+        stage_idx[p] = BANK ? s_tok[buf][l] : tbase + l;
       }
       nst += popc(tm);
       if (cnt + nst > lim && l == 0) s_need[step_buf] = 1;
@@ -306,6 +310,7 @@ __global__ void __launch_bounds__(WPB * 64, 2) scan_topk_kernel(const ScanArgs a
     // flag of step i+1, last read before the previous barrier
     if (i > 0 && s_need[buf2] && active && cnt + nst > args.K) {
       flush();
+      wave_mem_fence();  // the buffer's stores land before the selection reads it
       thr = wave_select_topk(ckey, cidx, cnt, args.K, hist);
       cnt = args.K;
     } else if (active && nst > kStageEntries - 64) {
@@ -320,6 +325,7 @@ __global__ void __launch_bounds__(WPB * 64, 2) scan_topk_kernel(const ScanArgs a
     const bool s0 = active && tbase < ncand_me;
     const bool s1 = active && tbase + 32 < ncand_me;
     const bool n0 = active && tbase + kTileKeys < ncand_me && i + 1 < ntiles;
+    float sc0 = 0.0f, sc1 = 0.0f;
     if (s0) {
       float part;
       if (s1) {
@@ -329,7 +335,7 @@ __global__ void __launch_bounds__(WPB * 64, 2) scan_topk_kernel(const ScanArgs a
       } else {
         part = head_sum(acc0);
       }
-      finish_sub(part, buf, 0, tbase, buf);
+      sc0 = sub_score(part, buf, 0);
     }
     if (s1) {
       float part;
@@ -340,10 +346,11 @@ __global__ void __launch_bounds__(WPB * 64, 2) scan_topk_kernel(const ScanArgs a
       } else {
         part = head_sum(acc1);
       }
-      finish_sub(part, buf, 1, tbase, buf);
+      sc1 = sub_score(part, buf, 1);
     } else if (n0) {
       mfma_sub(acc0, buf1, 0);
     }
+    if (s0) append(l < 32 ? sc0 : sc1, buf, tbase, buf);
     __syncthreads();
   };
   for (int i = 0; i < ntiles; i += 3) {
@@ -354,6 +361,7 @@ __global__ void __launch_bounds__(WPB * 64, 2) scan_topk_kernel(const ScanArgs a
 
   if (!active) return;
   flush();
+  wave_mem_fence();
   if (cnt > args.K) {
     wave_select_topk(ckey, cidx, cnt, args.K, hist);
     cnt = args.K;
@@ -385,6 +393,7 @@ static hipError_t launch_t(const ScanArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_scan_topk(const ScanArgs& a, int dtype, hipStream_t stream) {
+  if (dense_topk_supported(a)) return launch_dense_topk(a, dtype, stream);
   const int MT = a.H <= 32 ? 1 : 2;
   if (dtype == kBF16) {
     if (MT == 1) {
