@@ -9,9 +9,9 @@
 //   * Tiles go from HBM straight into a five-stage LDS ring with
 //     global_load_lds (no register staging): tile t is requested four steps
 //     before it is scored, into stage t % 5.  Each lane's 16-byte chunk lands
-//     at lane*16 of the wave's 1 KB, so the ring holds every key row with its
-//     16-byte chunks XOR-swizzled by the row index; the MFMA operand reads are
-//     then free of bank conflicts without padding.
+//     at lane*16 of the wave's 1 KB; lanes fetch the chunks of each key row in
+//     an order XOR-swizzled by the row index, so the MFMA operand reads are
+//     free of bank conflicts without padding.
 //   * Per-head dot products: fp8 v_mfma_f32_32x32x64_f8f6f4 or bf16
 //     v_mfma_f32_32x32x16_bf16, heads on M (two 32-row tiles), keys on N,
 //     fp32 accumulation; B operands are read from LDS one 32-key sub-tile
@@ -52,6 +52,9 @@ struct Cfg {
   static constexpr int kSteps = DT == kBF16 ? kD / 16 : kD / 64;  // main MFMA k-steps
   // vm operations a wave issues per step: the tile chunks and the key scales
   static constexpr int kVmPerStep = kDma + 1;
+  // chunk c of row r sits at slot c ^ swz(r): any 16 consecutive rows then put
+  // a given chunk in 16 distinct 16-byte bank groups (a 16-lane LDS pass)
+  static __device__ __forceinline__ int swz(int r) { return DT == kBF16 ? (r & 15) : ((r >> 1) & 7); }
 };
 
 template <int DT>
@@ -87,7 +90,7 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   __shared__ __attribute__((aligned(16))) uint32_t s_hist[kWaves][kSelectHistWords];
   __shared__ float s_lin[2][2][kWaves][kTile];                    // [parity][d half][query][key]
   __shared__ __attribute__((aligned(16))) uint16_t s_qt[kWaves][2][kD];  // bf16 hi / lo of q-tilde
-  __shared__ int s_need[3];
+  __shared__ int s_need[2];  // s_need[i & 1] == i: a wave asked for compaction in step i
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -194,35 +197,46 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
     cnt += nst;
     nst = 0;
   };
-  // A wave whose buffer passes `lim` raises the flag of the current step; after
-  // the step's barrier every wave holding more than K entries compacts.  A
-  // step appends at most 64 entries, so the buffer cannot overflow meanwhile.
+  // A wave whose buffer passes `lim` records the step in s_need; after the
+  // step's barrier every wave holding more than K entries compacts.  A step
+  // appends at most 64 entries, so the buffer cannot overflow meanwhile.
   const int lim = args.cap - 192;
-  if (tid < 3) s_need[tid] = 0;
+  if (tid < 2) s_need[tid] = -1;
 
-  // ---- tile requests: this lane's chunks of tile t into LDS stage `st`
+  // ---- tile requests: this lane's chunks of tile t into LDS stage `st`.
+  // Buffer resources end at the workgroup's last candidate key, so rows past
+  // it (the last tile's tail, and the tiles requested past the end) read as
+  // zeros and are masked when appended; no request needs a clamp or branch.
+  const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)args.k, (short)0, ncand_blk * C::kRowBytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t sres = DT == kFP8
+      ? __builtin_amdgcn_make_buffer_rsrc((void*)args.k_scale, (short)0, ncand_blk * 4, kBufferWord3)
+      : __builtin_amdgcn_make_buffer_rsrc((void*)args.w, (short)0, 256, kBufferWord3);
+  int lane_off[C::kDma];  // byte offset of this lane's chunk inside a tile
+#pragma unroll
+  for (int n = 0; n < C::kDma; ++n) {
+    const int ci = n * kThreads + wave * 64 + l;  // chunk position in the stage
+    const int r = ci / C::kChunksPerRow, cs = ci % C::kChunksPerRow;
+    lane_off[n] = r * C::kRowBytes + 16 * (cs ^ C::swz(r));
+  }
   auto request = [&](int t, int st) __attribute__((always_inline)) {
 #pragma unroll
     for (int n = 0; n < C::kDma; ++n) {
-      const int ci = n * kThreads + wave * 64 + l;  // chunk position in the stage
-      const int r = ci / C::kChunksPerRow, cs = ci % C::kChunksPerRow;
-      const int tok = min(t * kTile + r, ncand_blk - 1);
-      const uint8_t* g = (const uint8_t*)args.k + (int64_t)tok * C::kRowBytes + 16 * (cs ^ (r & 7));
-      __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)&s_tile[st][(n * kThreads + wave * 64) * 16],
-                                       16, 0, 0);
+      uint8_t* dst = &s_tile[st][(n * kThreads + wave * 64) * 16];
+      const int off = lane_off[n] + t * C::kTileBytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kres, (lds_void*)dst, 16, off, 0, 0, 0);
     }
-    // every wave writes the same 64 scales (fp8), or a placeholder word (bf16),
+    // every wave writes the same 64 scales (fp8; bf16 loads placeholder words),
     // so all waves issue the same number of requests per step
-    const int tok = min(t * kTile + l, ncand_blk - 1);
-    const float* g = DT == kFP8 ? args.k_scale + tok : args.w;
-    __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)&s_ks[st][0], 4, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(sres, (lds_void*)&s_ks[st][0], 4,
+                                             DT == kFP8 ? 4 * (t * kTile + l) : 4 * l, 0, 0, 0);
   };
 
-  // B operands of sub-tile u of the tile in stage st (row = 32u + col, and
-  // row & 7 == col & 7 undoes the swizzle)
+  // B operands of sub-tile u of the tile in stage st (row 32u + col has the
+  // swizzle of row col)
   auto load_b = [&](Frag (&bf)[C::kSteps], int st, int u) __attribute__((always_inline)) {
     const uint8_t* row = &s_tile[st][(32 * u + col) * C::kRowBytes];
-    const int x = col & 7;
+    const int x = C::swz(col);
 #pragma unroll
     for (int s = 0; s < C::kSteps; ++s) {
       if constexpr (DT == kBF16) {
@@ -263,7 +277,7 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
     v4f c = {0.0f, 0.0f, 0.0f, 0.0f};
     const int r = 16 * nb + (l & 15);
     const uint8_t* row = &s_tile[st][r * C::kRowBytes];
-    const int x = r & 7;
+    const int x = C::swz(r);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int ks = 2 * kh + s;  // d elements 32ks + 8(l>>4) .. +7
@@ -299,7 +313,7 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   };
   // append the step's scores that beat the threshold: lane l holds candidate
   // tbase + l, so lane order is candidate order and one ballot serves 64
-  auto append = [&](float sc, int tbase, int flag) __attribute__((always_inline)) {
+  auto append = [&](float sc, int tbase, int i) __attribute__((always_inline)) {
     uint64_t tm = ballot(sc > thr);
     if (tbase + kTile > ncand_me) tm &= ballot(tbase + l < ncand_me);  // the query's last tile
     if (tm) {
@@ -309,7 +323,7 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
         stage_idx[p] = tbase + l;
       }
       nst += popc(tm);
-      if (cnt + nst > lim && l == 0) s_need[flag] = 1;
+      if (cnt + nst > lim && l == 0) s_need[i & 1] = i;
     }
   };
   constexpr int kValuPerMfma = 8;
@@ -322,7 +336,7 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   };
 
   // ---- prologue: tiles 0..3 requested, tile 0's linear term, first MFMAs
-  for (int t = 0; t < kAhead; ++t) request(min(t, ntiles - 1), t);
+  for (int t = 0; t < kAhead; ++t) request(t, t);
   __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): tiles 0..3 in LDS
   __syncthreads();
   linear(0, 0);
@@ -333,26 +347,24 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   load_b(bB, 0, 1);
   __syncthreads();  // s_lin of tile 0
 
-  // step i scores tile i (stage i % 5) while tile i+1 (stage (i+1) % 5) feeds
-  // the next MFMAs and its linear term, and tile i+4 is requested into stage
+  // step i scores tile i (stage st) while tile i+1 (stage st1) feeds the next
+  // MFMAs and its linear term, and tile i+4 is requested into stage st4 =
   // (i+4) % 5, the one tile i-1 left.  On entry bB holds tile i's second
   // sub-tile's B operands and acc0 its first sub-tile's products.
+  int st = 0, st1 = 1, st4 = kAhead;
   for (int i = 0; i < ntiles; ++i) {
-    const int st = i % kStages, st1 = (i + 1) % kStages, st4 = (i + kAhead) % kStages;
-    const int flag = i % 3, flag_prev = (i + 2) % 3, flag_next = (i + 1) % 3;
     // compaction requests raised during step i-1 (seen after its barrier)
-    if (i > 0 && s_need[flag_prev] && active && cnt + nst > args.K) {
+    if (i > 0 && s_need[(i - 1) & 1] == i - 1 && active && cnt + nst > args.K) {
       flush();
       thr = wave_select_topk(ckey, cidx, cnt, args.K, hist);
       cnt = args.K;
     } else if (nst > kStage - 64) {
       flush();
     }
-    if (tid == 0) s_need[flag_next] = 0;
-    request(min(i + kAhead, ntiles - 1), st4);
+    request(i + kAhead, st4);
     const int tbase = i * kTile;
-    // the same work every step: past the last tile the MFMAs rerun tile
-    // ntiles-1 and the append masks them out
+    // the same work every step: past the last tile the MFMAs run on zeros
+    // and the append masks them out
     load_b(bA, st1, 0);
     mfma_sub(acc1, bB);
     const float p0 = abs_sum(acc0);
@@ -364,13 +376,16 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
     linear(i + 1, st1);
     const float sc0 = sub_score(p0, i, st, 0);
     const float sc1 = sub_score(p1, i, st, 1);
-    append(l < 32 ? sc0 : sc1, tbase, flag);
+    append(l < 32 ? sc0 : sc1, tbase, i);
     // tile i+2 must have landed before the barrier publishes it: after its
     // requests this wave issued those of tiles i+3 and i+4 (and maybe a
     // flush's stores, which only makes the count conservative)
     if constexpr (C::kVmPerStep == 2) __builtin_amdgcn_s_waitcnt(0x3F70 | 4);
     else __builtin_amdgcn_s_waitcnt(0x3F70 | 6);
     __syncthreads();
+    st4 = st;
+    st = st1;
+    st1 = st1 == kStages - 1 ? 0 : st1 + 1;
   }
 
   if (!active) return;
@@ -392,7 +407,10 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
 }  // namespace
 
 bool dense_topk_supported(const ScanArgs& a) {
-  return a.bank == nullptr && a.H > 32 && a.H <= 64 && a.d == kD;
+  // buffer offsets are 32-bit: the key rows up to the last query's position
+  // (plus the tiles requested past it) must stay below 2 GiB
+  const int64_t keys = a.pos0 + (a.nq - 1) * a.pos_stride + 1 + kAhead * kTile;
+  return a.bank == nullptr && a.H > 32 && a.H <= 64 && a.d == kD && keys * 2 * kD < (int64_t(1) << 31);
 }
 
 hipError_t launch_dense_topk(const ScanArgs& a, int dtype, hipStream_t stream) {
