@@ -202,10 +202,12 @@ int indexer_prefill(const void* q, const float* q_scale, const void* k, const fl
   return ok();
 }
 
-// decode workspace: histograms [B, bins] | compact-list counts [B, nblk] |
-// compact lists [B, nblk, kpb] of indices and of scores
+// decode workspace: histograms [B, bins] + candidate counts [B] | row
+// emission state [B, 4] | candidate keys and indices [B, cap] each | per-span
+// counts [B, nblk]: list entries, entries above b*, output offsets | compact
+// lists [B, nblk, kpb] of indices and of scores
 struct DecodeWs {
-  size_t hist, clcnt, clidx, clsc, total;
+  size_t hist, rowsel, ckey, cidx, clcnt, above, off, clidx, clsc, total;
 };
 
 // keys per scan workgroup: about 512 workgroups per call (two per CU), a
@@ -224,8 +226,13 @@ static DecodeWs decode_ws(int B, int64_t Nmax) {
   const size_t nblk = ((size_t)Nmax + kpb - 1) / kpb;
   DecodeWs w{};
   w.hist = 0;
-  w.clcnt = w.hist + align_up((size_t)B * kDecHistBins * 4u);
-  w.clidx = w.clcnt + align_up((size_t)B * nblk * 4u);
+  w.rowsel = w.hist + align_up(((size_t)B * kDecHistBins + (size_t)B) * 4u);
+  w.ckey = w.rowsel + align_up((size_t)B * 16u);
+  w.cidx = w.ckey + align_up((size_t)B * kDecCandCap * 4u);
+  w.clcnt = w.cidx + align_up((size_t)B * kDecCandCap * 4u);
+  w.above = w.clcnt + align_up((size_t)B * nblk * 4u);
+  w.off = w.above + align_up((size_t)B * nblk * 4u);
+  w.clidx = w.off + align_up((size_t)B * nblk * 4u);
   w.clsc = w.clidx + align_up((size_t)B * nblk * kpb * 4u);
   w.total = w.clsc + align_up((size_t)B * nblk * kpb * 4u);
   return w;
@@ -271,6 +278,12 @@ int indexer_decode(const void* q, const uint8_t* k_cache, const float* k_scale, 
   a.kpb = decode_keys_per_block(B, Nmax);
   a.nblk = (int)((Nmax + a.kpb - 1) / a.kpb);
   a.hist = (uint32_t*)(base + lay.hist);
+  a.cand_cnt = (int32_t*)(a.hist + (size_t)B * kDecHistBins);
+  a.rowsel = (uint32_t*)(base + lay.rowsel);
+  a.cand_key = (uint32_t*)(base + lay.ckey);
+  a.cand_idx = (int32_t*)(base + lay.cidx);
+  a.span_above = (int32_t*)(base + lay.above);
+  a.span_off = (int32_t*)(base + lay.off);
   a.cl_cnt = (int32_t*)(base + lay.clcnt);
   a.cl_idx = (int32_t*)(base + lay.clidx);
   a.cl_sc = (float*)(base + lay.clsc);

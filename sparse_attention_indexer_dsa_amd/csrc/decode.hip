@@ -16,14 +16,16 @@
 // cost far more than their share of the traffic, so the row of scores is never
 // written whole.
 //
-// decode_finish: one workgroup per row.  The row's compact lists, in span
-// order, form one list in ascending key order that the workgroup holds in
-// registers.  The row histogram gives the bin b* that holds the row's K-th
-// best score; the list's entries inside b* go to LDS, where two radix rounds
-// find the exact K-th score (ties: lower index first); a prefix sum over the
-// threads then writes the selected entries in ascending index order.  Rows
-// whose b* bin or whose list is too long for that take an exact multi-pass
-// path over the lists in global memory instead.
+// Selection, with the row histogram's bin b* that holds the row's K-th best:
+//   decode_classify (one workgroup per span): counts the span's list entries
+//     above b* and gathers those inside b* into the row's candidate array;
+//   decode_select (one workgroup per row): two radix rounds over the
+//     candidates in LDS find the exact K-th score and the tie cut (ties:
+//     lower index first), and a prefix sum gives every span's output offset;
+//   decode_emit (one workgroup per span): writes the span's selected keys in
+//     ascending index at that offset.
+// Rows of at most K keys are written by decode_select from the lists; rows
+// whose b* bin is too crowded take an exact multi-pass path over the lists.
 #include "device.h"
 #include "launch.h"
 
@@ -375,198 +377,297 @@ __device__ void select_lists_exact(const DecodeArgs& args, int b, int nb, int32_
 
 constexpr int kShift = 32 - kDecHistBits;  // order key -> histogram bin
 
-// Rounds of 1024 flat list entries the finish pass holds in registers:
-// longer flat lists take the exact path.
-constexpr int kFinishRounds = 36;
+constexpr int kSpanThreads = 256;
+constexpr int kSpanWaves = kSpanThreads / 64;
 
-// One row: top-K of its scores by (score desc, index asc), indices ascending.
-// The row's compact lists, read in span order, are one flat list in ascending
-// key order; flat position p = r*1024 + tid sits in thread tid's register r.
-__global__ void __launch_bounds__(kSelThreads) decode_finish_kernel(const DecodeArgs args) {
+// Threshold bin b* of row b from its histogram (all threads of the workgroup
+// call): s_res[0] = b*, s_res[1] = entries of b* inside the top K, s_res[2] =
+// entries in b*.  Thread t holds bins [t*per, (t+1)*per), read as 16-byte
+// vectors in one round trip.
+template <int NW>
+__device__ __forceinline__ void row_threshold(const DecodeArgs& args, int b, int* s_tmp, int* s_res) {
+  constexpr int kPer = kDecHistBins / (NW * 64);
+  static_assert(kPer % 4 == 0, "whole 16-byte vectors of bins per thread");
+  const int tid = threadIdx.x;
+  const u32x4* src = (const u32x4*)(args.hist + (int64_t)b * kDecHistBins + tid * kPer);
+  uint32_t c[kPer];
+#pragma unroll
+  for (int q = 0; q < kPer / 4; ++q) {
+    const u32x4 v = src[q];
+    c[4 * q] = v[0];
+    c[4 * q + 1] = v[1];
+    c[4 * q + 2] = v[2];
+    c[4 * q + 3] = v[3];
+  }
+  int local = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) local += (int)c[i];
+  int total;
+  const int excl = block_excl_scan<NW>(local, s_tmp, total);
+  const int above = total - excl - local;  // entries in higher threads' (higher) bins
+  const int krem = args.K;
+  if (above < krem && above + local >= krem) {
+    int acc = above;
+    bool found = false;
+#pragma unroll
+    for (int i = kPer - 1; i >= 0; --i) {
+      if (!found && acc + (int)c[i] >= krem) {
+        s_res[0] = tid * kPer + i;
+        s_res[1] = krem - acc;
+        s_res[2] = (int)c[i];
+        found = true;
+      }
+      acc += (int)c[i];
+    }
+  }
+  __syncthreads();
+}
+
+// List entries a span workgroup loads per thread at once (strided by the
+// workgroup size, so every load is coalesced and all of them are in flight).
+constexpr int kSpanBatch = 8;
+
+// One workgroup per (span, row): counts the span's list entries above b* and
+// gathers those inside b* into the row's candidate array.
+__global__ void __launch_bounds__(kSpanThreads) decode_classify_kernel(const DecodeArgs args) {
+  __shared__ int s_tmp[kSpanWaves];
+  __shared__ int s_res[4];
+  __shared__ int s_base;
+  const int b = blockIdx.y, j = blockIdx.x;
+  const int tid = threadIdx.x;
+  int64_t n = args.seq_lens[b];
+  n = n < 0 ? 0 : (n > args.Nmax ? args.Nmax : n);
+  if (n <= args.K || (int64_t)j * args.kpb >= n) return;
+  const int64_t lbase = ((int64_t)b * args.nblk + j) * args.kpb;
+  const int c = args.cl_cnt[(int64_t)b * args.nblk + j];
+  // the first batch of the list is requested before the threshold search
+  uint32_t key[kSpanBatch];
+  auto load_batch = [&](int base) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kSpanBatch; ++u) {
+      const int e = base + u * kSpanThreads + tid;
+      key[u] = e < c ? order_key(args.cl_sc[lbase + e]) : 0u;  // key 0: below every bin b*
+    }
+  };
+  load_batch(0);
+  row_threshold<kSpanWaves>(args, b, s_tmp, s_res);
+  const uint32_t bstar = (uint32_t)s_res[0];
+  if (s_res[2] > kDecCandCap) return;  // the select pass takes the exact path
+  uint32_t* ck = args.cand_key + (int64_t)b * kDecCandCap;
+  int32_t* ci = args.cand_idx + (int64_t)b * kDecCandCap;
+  int above = 0;
+  for (int base = 0; base < c; base += kSpanBatch * kSpanThreads) {
+    if (base > 0) load_batch(base);
+    int cand = 0;
+#pragma unroll
+    for (int u = 0; u < kSpanBatch; ++u) {
+      above += (key[u] >> kShift) > bstar;
+      cand += (key[u] >> kShift) == bstar && key[u] != 0u;
+    }
+    int tot;
+    const int before = block_excl_scan<kSpanWaves>(cand, s_tmp, tot);
+    if (tot == 0) continue;
+    if (tid == 0) s_base = atomicAdd(args.cand_cnt + b, tot);
+    __syncthreads();
+    int p = s_base + before;
+#pragma unroll
+    for (int u = 0; u < kSpanBatch; ++u) {
+      if ((key[u] >> kShift) == bstar && key[u] != 0u) {
+        if (p < kDecCandCap) {
+          ck[p] = key[u];
+          ci[p] = args.cl_idx[lbase + base + u * kSpanThreads + tid];
+        }
+        ++p;
+      }
+    }
+    __syncthreads();  // s_base is rewritten by the next batch
+  }
+  int tot_above;
+  block_excl_scan<kSpanWaves>(above, s_tmp, tot_above);
+  if (tid == 0) args.span_above[(int64_t)b * args.nblk + j] = tot_above;
+}
+
+// One workgroup per row: the exact K-th key among the candidates of b*, the
+// tie cut, and every span's output offset.  Rows of at most K keys, and rows
+// whose b* bin or span count is too large, are written here completely.
+__global__ void __launch_bounds__(kSelThreads) decode_select_kernel(const DecodeArgs args) {
   __shared__ uint32_t s_ckey[kDecCandCap];
   __shared__ int32_t s_cidx[kDecCandCap];
   __shared__ uint32_t s_h[2048];
   __shared__ int s_tmp[kSelWaves];
   __shared__ int s_res[4 + 2 * kSelWaves];
-  __shared__ int s_count;
-  __shared__ int s_pref[kSelThreads + 1];
-  __shared__ int s_wc[kFinishRounds * kSelWaves];
+  __shared__ int s_chosen[kSelThreads];  // chosen candidates per span
   const int b = blockIdx.x;
-  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  const int tid = threadIdx.x;
   int64_t n = args.seq_lens[b];
   n = n < 0 ? 0 : (n > args.Nmax ? args.Nmax : n);
   const int K = args.K;
   int32_t* oidx = args.out_idx + (int64_t)b * K;
   float* osc = args.out_score ? args.out_score + (int64_t)b * K : nullptr;
   const int nb = (int)((n + args.kpb - 1) / args.kpb);  // scan spans of the row
-  if (nb > kSelThreads) {
+  if (tid == 0) args.rowsel[4 * b] = 0;  // written here unless set below
+  if (n <= K) {
+    // every span kept all of its keys: the lists are keys 0 .. n-1 in order
+    int off = 0;
+    for (int j = 0; j < nb; ++j) {
+      const int64_t lbase = ((int64_t)b * args.nblk + j) * args.kpb;
+      const int c = args.cl_cnt[(int64_t)b * args.nblk + j];
+      for (int i = tid; i < c; i += kSelThreads) {
+        oidx[off + i] = args.cl_idx[lbase + i];
+        if (osc) osc[off + i] = args.cl_sc[lbase + i];
+      }
+      off += c;
+    }
+    for (int p = (int)n + tid; p < K; p += kSelThreads) {
+      oidx[p] = -1;
+      if (osc) osc[p] = -__builtin_inff();
+    }
+    return;
+  }
+  row_threshold<kSelWaves>(args, b, s_tmp, s_res);
+  const uint32_t bstar = (uint32_t)s_res[0];
+  const int need = s_res[1];   // entries of bin b* that are selected
+  const int nc = s_res[2];     // entries in bin b* (all of them are candidates)
+  __syncthreads();
+  if (nc > kDecCandCap || nb > kSelThreads) {
     select_lists_exact(args, b, nb, oidx, osc, s_h, s_tmp, s_res);
     return;
   }
-  // list j covers flat positions [s_pref[j], s_pref[j+1])
-  {
-    const int c = tid < nb ? args.cl_cnt[(int64_t)b * args.nblk + tid] : 0;
-    int total;
-    const int before = block_excl_scan(c, s_tmp, total);
-    if (tid < nb) s_pref[tid] = before;
-    if (tid == 0) {
-      s_pref[nb] = total;
-      s_count = 0;
+  for (int i = tid; i < nc; i += kSelThreads) {
+    s_ckey[i] = args.cand_key[(int64_t)b * kDecCandCap + i];
+    s_cidx[i] = args.cand_idx[(int64_t)b * kDecCandCap + i];
+  }
+  s_chosen[tid] = 0;
+  __syncthreads();
+
+  // exact K-th key among the candidates (the low 20 bits, two rounds)
+  uint32_t prefix = bstar << kShift, pmask = ~0u << kShift;
+  int krem = need;
+  block_radix_lds(s_ckey, nc, 10, 1024, prefix, pmask, krem, s_h, s_tmp, s_res);
+  const int n_eq = block_radix_lds(s_ckey, nc, 0, 1024, prefix, pmask, krem, s_h, s_tmp, s_res);
+  const uint32_t kth = prefix;
+  const int keep_eq = krem;  // of the n_eq candidates equal to kth keep the keep_eq lowest indices
+  // ties at kth: the keep_eq-th largest ~index among them is the cut
+  uint32_t idx_cut = 0u;  // selected: key > kth, or key == kth and ~index >= idx_cut
+  if (keep_eq < n_eq) {
+    uint32_t tp = 0, tm = 0;
+    int tk = keep_eq;
+    for (int round = 0; round < 3; ++round) {
+      const int shift = round == 0 ? 21 : (round == 1 ? 10 : 0);
+      const int nbins = round == 2 ? 1024 : 2048;
+      const uint32_t dmask = (uint32_t)nbins - 1;
+      for (int i = tid; i < nbins; i += kSelThreads) s_h[i] = 0;
+      __syncthreads();
+      for (int i = tid; i < nc; i += kSelThreads) {
+        if (s_ckey[i] != kth) continue;
+        const uint32_t r = ~(uint32_t)s_cidx[i];
+        if ((r & tm) == tp) atomicAdd(&s_h[(r >> shift) & dmask], 1u);
+      }
+      __syncthreads();
+      const int pb = (nbins + kSelThreads - 1) / kSelThreads;
+      block_find_digit(pb, [&](int t, int i) { return t * pb + i < nbins ? (int)s_h[t * pb + i] : 0; },
+                       tk, s_tmp, s_res);
+      tp |= (uint32_t)s_res[0] << shift;
+      tm |= dmask << shift;
+      tk = s_res[1];
+      __syncthreads();
     }
+    idx_cut = tp;
+  }
+  // chosen candidates per span, then each span's output offset
+  for (int i = tid; i < nc; i += kSelThreads) {
+    const uint32_t key = s_ckey[i];
+    const uint32_t e = (uint32_t)s_cidx[i];
+    if (key > kth || (key == kth && ~e >= idx_cut)) atomicAdd(&s_chosen[e / (uint32_t)args.kpb], 1);
   }
   __syncthreads();
-  const int flat = s_pref[nb];
+  const int mine = tid < nb ? s_chosen[tid] + args.span_above[(int64_t)b * args.nblk + tid] : 0;
+  int total;
+  const int off = block_excl_scan(mine, s_tmp, total);
+  if (tid < nb) args.span_off[(int64_t)b * args.nblk + tid] = off;
+  if (tid == 0) {
+    args.rowsel[4 * b + 1] = kth;
+    args.rowsel[4 * b + 2] = idx_cut;
+    args.rowsel[4 * b] = 1;
+  }
+}
 
-  // 1. threshold bin b* of the row histogram (4 bins per thread); rows of at
-  // most K keys keep everything
-  uint32_t bstar = 0;
-  int need = 0, inbin = 0;
-  if (n > K) {
-    const uint32_t* ghist = args.hist + (int64_t)b * kDecHistBins;
-    constexpr int kPer = kDecHistBins / kSelThreads;
-    block_find_digit(kPer, [&](int t, int i) { return (int)ghist[t * kPer + i]; }, K, s_tmp, s_res);
-    bstar = (uint32_t)s_res[0];
-    need = s_res[1];   // entries of bin b* that are selected
-    inbin = s_res[2];  // entries in bin b*
+// One workgroup per (span, row): writes the span's selected keys, in
+// ascending index, at the span's output offset.  Entry base + u*256 + tid sits
+// in thread tid's register u; a prefix over the (u, wave) ballot counts orders
+// the writes.
+__global__ void __launch_bounds__(kSpanThreads) decode_emit_kernel(const DecodeArgs args) {
+  __shared__ int s_tmp[kSpanWaves];
+  __shared__ int s_wc[kSpanBatch * kSpanWaves];
+  const int b = blockIdx.y, j = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  int64_t n = args.seq_lens[b];
+  n = n < 0 ? 0 : (n > args.Nmax ? args.Nmax : n);
+  if ((int64_t)j * args.kpb >= n || args.rowsel[4 * b] != 1) return;
+  const uint32_t kth = args.rowsel[4 * b + 1], idx_cut = args.rowsel[4 * b + 2];
+  const int64_t lbase = ((int64_t)b * args.nblk + j) * args.kpb;
+  const int c = args.cl_cnt[(int64_t)b * args.nblk + j];
+  int32_t* oidx = args.out_idx + (int64_t)b * args.K;
+  float* osc = args.out_score ? args.out_score + (int64_t)b * args.K : nullptr;
+  int out = args.span_off[(int64_t)b * args.nblk + j];
+  for (int base = 0; base < c; base += kSpanBatch * kSpanThreads) {
+    float v[kSpanBatch];
+    int32_t idx[kSpanBatch];
+#pragma unroll
+    for (int u = 0; u < kSpanBatch; ++u) {
+      const int e = base + u * kSpanThreads + tid;
+      v[u] = e < c ? args.cl_sc[lbase + e] : 0.0f;
+      idx[u] = e < c ? args.cl_idx[lbase + e] : -1;
+    }
+    bool sel[kSpanBatch];
+#pragma unroll
+    for (int u = 0; u < kSpanBatch; ++u) {
+      const uint32_t key = order_key(v[u]);
+      sel[u] = idx[u] >= 0 && (key > kth || (key == kth && ~(uint32_t)idx[u] >= idx_cut));
+      const int cnt = popc(ballot(sel[u]));
+      if (l == 0) s_wc[u * kSpanWaves + wave] = cnt;
+    }
     __syncthreads();
-  }
-  if (inbin > kDecCandCap || flat > kSelThreads * kFinishRounds) {
-    select_lists_exact(args, b, nb, oidx, osc, s_h, s_tmp, s_res);
-    return;
-  }
-
-  // 2. the flat list into registers: every load issued up front (positions
-  // past the end read entry 0 and are marked invalid); entries of b* to LDS
-  // the list holding the first position of each (round, wave) block of 64
-  for (int i = tid; i < kFinishRounds * kSelWaves; i += kSelThreads) {
-    const int p = (i / kSelWaves) * kSelThreads + (i % kSelWaves) * 64;
-    int lo = 0, hi = nb - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_pref[mid] <= p) lo = mid; else hi = mid - 1;
-    }
-    s_wc[i] = lo;
-  }
-  __syncthreads();
-  const int64_t row0 = (int64_t)b * args.nblk * args.kpb;
-  uint32_t key[kFinishRounds];
-  int32_t idx[kFinishRounds];
-#pragma unroll
-  for (int r = 0; r < kFinishRounds; ++r) {
-    const int p = r * kSelThreads + tid;
-    int j = s_wc[r * kSelWaves + wave];
-    while (j + 1 < nb && s_pref[j + 1] <= p) ++j;
-    const int64_t at = p < flat ? row0 + (int64_t)j * args.kpb + (p - s_pref[j]) : row0;
-    key[r] = order_key(args.cl_sc[at]);
-    idx[r] = args.cl_idx[at];
-  }
-  __syncthreads();  // s_wc is reused below
-#pragma unroll
-  for (int r = 0; r < kFinishRounds; ++r) {
-    if (r * kSelThreads + tid >= flat) idx[r] = -1;
-    if (n > K && r * kSelThreads < flat) {
-      const bool cand = idx[r] >= 0 && (key[r] >> kShift) == bstar;
-      const uint64_t m = ballot(cand);
-      if (m) {
-        const int fl = first_lane(m);
-        int base = 0;
-        if (l == fl) base = atomicAdd(&s_count, popc(m));
-        base = shfl(base, fl) + rank_below(m);
-        if (cand && base < kDecCandCap) {
-          s_ckey[base] = key[r];
-          s_cidx[base] = idx[r];
-        }
-      }
-    }
-  }
-  __syncthreads();
-
-  // 3. the exact K-th key among the candidates (the low 20 bits, two rounds);
-  // the lists hold every entry of bin b*, so there are exactly `inbin`
-  uint32_t kth = 0u, idx_cut = 0u;  // selected: key > kth, or key == kth and ~index >= idx_cut
-  if (n > K) {
-    const int nc = inbin;
-    uint32_t prefix = bstar << kShift, pmask = ~0u << kShift;
-    int krem = need;
-    block_radix_lds(s_ckey, nc, 10, 1024, prefix, pmask, krem, s_h, s_tmp, s_res);
-    const int n_eq = block_radix_lds(s_ckey, nc, 0, 1024, prefix, pmask, krem, s_h, s_tmp, s_res);
-    kth = prefix;
-    const int keep_eq = krem;  // of the n_eq candidates equal to kth keep the keep_eq lowest indices
-    // 4. ties at kth: the keep_eq-th largest ~index among them is the cut
-    if (keep_eq < n_eq) {
-      uint32_t tp = 0, tm = 0;
-      int tk = keep_eq;
-      for (int round = 0; round < 3; ++round) {
-        const int shift = round == 0 ? 21 : (round == 1 ? 10 : 0);
-        const int nbins = round == 2 ? 1024 : 2048;
-        const uint32_t dmask = (uint32_t)nbins - 1;
-        for (int i = tid; i < nbins; i += kSelThreads) s_h[i] = 0;
-        __syncthreads();
-        for (int i = tid; i < nc; i += kSelThreads) {
-          if (s_ckey[i] != kth) continue;
-          const uint32_t rr = ~(uint32_t)s_cidx[i];
-          if ((rr & tm) == tp) atomicAdd(&s_h[(rr >> shift) & dmask], 1u);
-        }
-        __syncthreads();
-        const int pb = (nbins + kSelThreads - 1) / kSelThreads;
-        block_find_digit(pb,
-                         [&](int t, int i) { return t * pb + i < nbins ? (int)s_h[t * pb + i] : 0; },
-                         tk, s_tmp, s_res);
-        tp |= (uint32_t)s_res[0] << shift;
-        tm |= dmask << shift;
-        tk = s_res[1];
-        __syncthreads();
-      }
-      idx_cut = tp;
-    }
-  }
-
-  // 5. emit in ascending index = flat order: selected counts per (round,
-  // wave), one prefix sum over them, then each lane's rank inside its wave
-  auto selected = [&](int r) __attribute__((always_inline)) {
-    return idx[r] >= 0 && (key[r] > kth || (key[r] == kth && ~(uint32_t)idx[r] >= idx_cut));
-  };
-#pragma unroll
-  for (int r = 0; r < kFinishRounds; ++r) {
-    const int c = popc(ballot(selected(r)));
-    if (l == 0) s_wc[r * kSelWaves + wave] = c;
-  }
-  __syncthreads();
-  {
-    const int v = tid < kFinishRounds * kSelWaves ? s_wc[tid] : 0;
     int total;
-    const int before = block_excl_scan(v, s_tmp, total);
-    if (tid < kFinishRounds * kSelWaves) s_wc[tid] = before;
-    if (tid == 0) s_count = total;
-  }
-  __syncthreads();
+    const int vwc = tid < kSpanBatch * kSpanWaves ? s_wc[tid] : 0;
+    const int before = block_excl_scan<kSpanWaves>(vwc, s_tmp, total);
+    if (tid < kSpanBatch * kSpanWaves) s_wc[tid] = before;
+    __syncthreads();
 #pragma unroll
-  for (int r = 0; r < kFinishRounds; ++r) {
-    const bool sel = selected(r);
-    const int pos = s_wc[r * kSelWaves + wave] + rank_below(ballot(sel));
-    if (sel && pos < K) {
-      oidx[pos] = idx[r];
-      if (osc) osc[pos] = key_to_float(key[r]);
+    for (int u = 0; u < kSpanBatch; ++u) {
+      const int pos = out + s_wc[u * kSpanWaves + wave] + rank_below(ballot(sel[u]));
+      if (sel[u] && pos < args.K) {
+        oidx[pos] = idx[u];
+        if (osc) osc[pos] = v[u];
+      }
     }
-  }
-  const int total = s_count;
-  for (int p = (total < K ? total : K) + tid; p < K; p += kSelThreads) {
-    oidx[p] = -1;
-    if (osc) osc[p] = -__builtin_inff();
+    out += total;
+    __syncthreads();  // s_wc is rewritten by the next batch
   }
 }
 
 template <int MT, int D>
 static hipError_t launch_dec(const DecodeArgs& a, hipStream_t stream) {
   if (a.B <= 0) return hipSuccess;
-  hipError_t e = launch_fill_i32((int32_t*)a.hist, (int64_t)a.B * kDecHistBins, 0, stream);
+  // histograms and candidate counters are contiguous: one fill clears both
+  hipError_t e = launch_fill_i32((int32_t*)a.hist, (int64_t)a.B * kDecHistBins + a.B, 0, stream);
   if (e != hipSuccess) return e;
   if (a.nblk > 0)
     hipLaunchKernelGGL((decode_scan_kernel<MT, D>), dim3((unsigned)a.nblk, (unsigned)a.B),
                        dim3(kDecThreads), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_finish_kernel, dim3((unsigned)a.B), dim3(kSelThreads), 0, stream, a);
+  if (a.nblk > 0)
+    hipLaunchKernelGGL(decode_classify_kernel, dim3((unsigned)a.nblk, (unsigned)a.B), dim3(kSpanThreads), 0,
+                       stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_select_kernel, dim3((unsigned)a.B), dim3(kSelThreads), 0, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.nblk > 0)
+    hipLaunchKernelGGL(decode_emit_kernel, dim3((unsigned)a.nblk, (unsigned)a.B), dim3(kSpanThreads), 0, stream,
+                       a);
   return hipGetLastError();
 }
 

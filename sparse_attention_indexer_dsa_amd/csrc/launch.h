@@ -62,6 +62,12 @@ struct DecodeArgs {
   int32_t* cl_cnt;        // [B, nblk] entries of each workgroup's compact list
   int32_t* cl_idx;        // [B, nblk, kpb] key indices of the compact lists (ascending)
   float* cl_sc;           // [B, nblk, kpb] their scores
+  int32_t* cand_cnt;      // [B] threshold-bin candidates gathered, zeroed per call
+  uint32_t* cand_key;     // [B, kDecCandCap] their order keys
+  int32_t* cand_idx;      // [B, kDecCandCap] their key indices
+  int32_t* span_above;    // [B, nblk] list entries above the threshold bin
+  int32_t* span_off;      // [B, nblk] output offset of each span's selected keys
+  uint32_t* rowsel;       // [B, 4] emission: mode (1 = by span), K-th key, tie cut
   int32_t* out_idx;       // [B, K]
   float* out_score;       // [B, K] or nullptr
 };
