@@ -123,12 +123,12 @@ def bench_prefill(dsa, args, log):
     achieved = flops / kern_s / 1e12
     res = dict(value=tflops, ms_per_step=ms_step, gpairs_per_s=pairs / (ms_step * 1e-3) / 1e9,
                pairs_per_step=pairs, flops_per_step=flops,
-               roofline=dict(bound="mfma", kernel="scan_topk_kernel<fp8,2,128>", achieved=achieved,
+               roofline=dict(bound="mfma", kernel="dense_topk_kernel<fp8>", achieved=achieved,
                              peak=PEAK_FP8_TFLOPS, unit="TFLOP/s", frac=achieved / PEAK_FP8_TFLOPS,
                              launches_per_step=nchunks,
                              avg_launch_ms=float(launch_ms.mean()),
                              flops_per_launch=flops / nchunks,
-                             traffic=_traffic("scan_topk_fp8_prefill128k")))
+                             traffic=_traffic("dense_topk_fp8_prefill128k")))
     cpu = None
     if not args.no_cpu:
         cpu = cpu_prefill(wl, out, args, log)
@@ -206,10 +206,10 @@ def bench_decode(dsa, args, log):
                         "bf16 query, H=64, d=128, top-2048",
                value=gbs, unit="GB/s", ms_per_step=ms_step, steps=nsteps,
                gpairs_per_s=B * N / (ms_step * 1e-3) / 1e9, bytes_per_step=alg_bytes,
-               roofline=dict(bound="hbm", kernel="decode_scan_kernel + decode_select_kernel (one call)",
+               roofline=dict(bound="hbm", kernel="fill + decode_scan + decode_classify + decode_select + decode_emit (one call)",
                              achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s", frac=achieved / PEAK_HBM_GBS,
                              avg_launch_ms=float(call_ms.mean()), bytes_per_launch=alg_bytes,
-                             traffic=_traffic("decode_scan_decode256k", "decode_select_decode256k")))
+                             traffic=_traffic("decode_call_decode256k")))
     if not args.no_cpu:
         import oracle
         from tests.parity import compare
