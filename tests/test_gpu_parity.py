@@ -143,6 +143,59 @@ def test_deterministic(dsa):
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
+# --- the dense kernel (33..64 heads, d = 128): head padding, the ReLU identity
+# with zero and negative weights, compaction, partial workgroups, K > prefix
+
+@pytest.mark.parametrize("H,dtype", [(33, "bf16"), (40, "fp8"), (63, "bf16"), (48, "fp8")])
+def test_dense_kernel_head_counts(dsa, H, dtype):
+    wl = make_prefill(T=900, H=H, d=128, topk=96, dtype=dtype, dist="int", seed=H)
+    _prefill_check(dsa, wl, rows=_rows(900, 32, H))
+    wl2 = make_prefill(T=700, H=H, d=128, topk=64, dtype=dtype, dist="normal", seed=H + 1)
+    _prefill_check(dsa, wl2, rows=_rows(700, 32, H + 1))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_dense_kernel_signed_weights(dsa, dtype):
+    """Negative and zero weights: (w/2)|s| + (w/2)s must equal w ReLU(s) exactly
+    on integer data, including scores that are exactly zero and rank by index."""
+    wl = make_prefill(T=600, H=64, d=128, topk=80, dtype=dtype, dist="int", seed=11, w_lo=-3, w_hi=0)
+    _prefill_check(dsa, wl, rows=_rows(600, 32, 11))
+    wl2 = make_prefill(T=600, H=64, d=128, topk=80, dtype=dtype, dist="int", seed=12)
+    wl2.tensors["w"][:, ::2] = 0.0
+    _prefill_check(dsa, wl2, rows=_rows(600, 32, 12))
+    wl3 = make_prefill(T=500, H=64, d=128, topk=64, dtype=dtype, dist="int", seed=13)
+    wl3.tensors["w"] = torch.zeros_like(wl3["w"])  # every score is +0: the lowest indices win
+    gi, _ = _prefill_check(dsa, wl3, rows=_rows(500, 16, 13))
+    assert (_np(gi)[499] == np.arange(64)).all()
+
+
+def test_dense_kernel_compaction(dsa):
+    """64 heads at d = 128 with K = 16 over 5000 keys: many compactions, with
+    non-decreasing scores (every key beats the threshold) and long tie runs."""
+    T, H, d, K = 5000, 64, 128, 16
+    q = torch.zeros((T, H, d), dtype=torch.float32)
+    q[:, 0, 0] = 1.0
+    s = torch.arange(T)
+    k = torch.zeros((T, d), dtype=torch.float32)
+    k[:, 0] = (s // 24 + 1).clamp(max=250).float()
+    wl = make_prefill(T=T, H=H, d=d, topk=K, dtype="bf16", dist="int", seed=14)
+    w = torch.zeros((T, H))
+    w[:, 0] = 1.0
+    wl.tensors.update(q=q.to(torch.bfloat16), k=k.to(torch.bfloat16), w=w)
+    _prefill_check(dsa, wl, rows=_rows(T, 32, 14), exact=True)
+    wl2 = make_prefill(T=4000, H=64, d=128, topk=24, dtype="fp8", dist="int", seed=15)
+    _prefill_check(dsa, wl2, rows=_rows(4000, 32, 15))
+
+
+@pytest.mark.parametrize("Tq,q_pos0,K", [(5, 100, 32), (13, 0, 200), (1, 2047, 2048), (9, 60, 2048)])
+def test_dense_kernel_partial_workgroups(dsa, Tq, q_pos0, K):
+    """Query counts that leave waves of the first workgroup idle, chunks that
+    start mid-sequence, and K at or above the prefix (padding with -1)."""
+    wl = make_prefill(T=q_pos0 + Tq, H=64, d=128, topk=K, dtype="fp8", dist="int", seed=Tq + q_pos0,
+                      Tq=Tq, q_pos0=q_pos0)
+    _prefill_check(dsa, wl)
+
+
 def test_empty_query_set(dsa):
     wl = make_prefill(T=10, H=4, d=32, topk=4, dtype="bf16", dist="int", seed=11)
     t = {k: v.cuda() for k, v in wl.tensors.items()}
