@@ -326,15 +326,6 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
       if (cnt + nst > lim && l == 0) s_need[i & 1] = i;
     }
   };
-  constexpr int kValuPerMfma = 8;
-  auto interleave = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int q = 0; q < 2 * C::kSteps; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
-    }
-  };
-
   // ---- prologue: tiles 0..3 requested, tile 0's linear term, first MFMAs
   for (int t = 0; t < kAhead; ++t) request(t, t);
   __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): tiles 0..3 in LDS
@@ -368,11 +359,9 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
     load_b(bA, st1, 0);
     mfma_sub(acc1, bB);
     const float p0 = abs_sum(acc0);
-    interleave();
     load_b(bB, st1, 1);
     mfma_sub(acc0, bA);
     const float p1 = abs_sum(acc1);
-    interleave();
     linear(i + 1, st1);
     const float sc0 = sub_score(p0, i, st, 0);
     const float sc1 = sub_score(p1, i, st, 1);
