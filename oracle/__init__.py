@@ -54,6 +54,8 @@ def lib():
         L.oracle_group_bank.restype = I32
         L.oracle_group_bank.argtypes = [P, P, P, P, P, I32, I64, I64, I32, I32, I64, P, P, P, I32, I32,
                                         I32, I32, ctypes.c_uint, P, I64, P, P, P, P, I32]
+        L.oracle_pool_mean_bf16.restype = I32
+        L.oracle_pool_mean_bf16.argtypes = [P, P, I64, I32, I32, I32, P, P]
         L.oracle_group_bank_pairs.restype = I64
         L.oracle_group_bank_pairs.argtypes = [I64, I64, I32, I32, ctypes.c_uint]
         for name in ("oracle_cost_prefill_base",):
@@ -160,12 +162,38 @@ def decode(q, k_cache, k_scale, w, seq_lens, topk, rows=None, nthreads=0):
     return idx, sc
 
 
+POOL_MEAN = 2  # group_bank flag: the training-free group query (mean pooling)
+
+
+def pool_mean_bf16(q, w, G):
+    """Mean-pooled group query of the training-free variant (Section 5 Abl. 2;
+    Appendix B.3, B.4): (qbar uint16 bf16 bits [ceil(Tq/G), H, d], wbar float32
+    [ceil(Tq/G), H]).  q is bf16 (a torch bfloat16 tensor or uint16 bits)."""
+    q, w = _host(q), _host(w).astype(np.float32)
+    q = np.ascontiguousarray(q.view(np.uint16))
+    Tq, H, d = q.shape
+    NG = -(-Tq // G)
+    qbar = np.empty((NG, H, d), np.uint16)
+    wbar = np.empty((NG, H), np.float32)
+    rc = lib().oracle_pool_mean_bf16(_ptr(q), _ptr(w), Tq, H, d, G, _ptr(qbar), _ptr(wbar))
+    if rc != 0:
+        raise ValueError(f"oracle_pool_mean_bf16 failed ({rc})")
+    return qbar, wbar
+
+
 def group_bank(q, k, w, qbar, wbar, dtype, q_pos0, G, P, topk, flags=0, q_scale=None, k_scale=None,
                qbar_scale=None, rows=None, want_bank=False, nthreads=0):
     """ADIndex bank sharing (Eq. 8, 13, 14) with fallback to the original indexer.
 
+    With ``flags & POOL_MEAN`` the group query is the mean-pooled one of the
+    training-free variant (qbar and wbar are ignored; bf16 only).
     Returns (idx [n,topk], score [n,topk], bank [NG,P] or None, pairs).
     """
+    if flags & POOL_MEAN:
+        if dtype != "bf16":
+            raise ValueError("mean pooling takes bf16 queries")
+        qbar, wbar = pool_mean_bf16(q, w, G)
+        flags &= ~POOL_MEAN
     q, k, w = _host(q), _host(k), _host(w).astype(np.float32)
     qbar, wbar = _host(qbar), _host(wbar).astype(np.float32)
     q_scale, k_scale, qbar_scale = _host(q_scale), _host(k_scale), _host(qbar_scale)

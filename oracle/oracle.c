@@ -416,6 +416,56 @@ int oracle_group_bank(const void *q, const float *q_scale, const void *k, const 
     return err;
 }
 
+/* ------------------------------------------- training-free group query
+ * The "w/o training" variant of Section 5 (Abl. 2, Table 3) and the mean
+ * pooling of Appendix B.3 (Table 8) and B.4: the frozen DSA indexer builds the
+ * bank with a group query that is the mean of the group's own indexer
+ * queries, head by head, and head weights that are the mean of theirs.
+ * The pooled query is a bf16 value that then decides the bank (an integer
+ * result), so it is formed in the precision the library forms it in: an fp32
+ * sum over the group's queries in query order, times 1/G (exact: G is a
+ * power of two), rounded to the nearest bf16 (ties to even); the weights the
+ * same way, kept in fp32.  Complete groups only; the rows of an incomplete
+ * last group (which never builds a bank) are zero.  bf16 queries only. */
+static uint16_t f32_to_bf16_rne(float x)
+{
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    const uint32_t lsb = (u >> 16) & 1u;
+    return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+}
+
+static float bf16_bits_to_f32(uint16_t b)
+{
+    const uint32_t u = (uint32_t)b << 16;
+    float x;
+    memcpy(&x, &u, 4);
+    return x;
+}
+
+int oracle_pool_mean_bf16(const uint16_t *q, const float *w, int64_t Tq, int H, int d, int G,
+                          uint16_t *qbar, float *wbar)
+{
+    if (Tq < 0 || H <= 0 || d <= 0 || (G != 4 && G != 8 && G != 16)) return -1;
+    const int64_t NG = (Tq + G - 1) / G, nfull = Tq / G;
+    const float inv = 1.0f / (float)G;
+    for (int64_t g = 0; g < NG; ++g) {
+        for (int64_t e = 0; e < (int64_t)H * d; ++e) {
+            float s = 0.0f;
+            if (g < nfull)
+                for (int i = 0; i < G; ++i) s += bf16_bits_to_f32(q[(g * G + i) * (int64_t)H * d + e]);
+            qbar[g * (int64_t)H * d + e] = f32_to_bf16_rne(s * inv);
+        }
+        for (int j = 0; j < H; ++j) {
+            float s = 0.0f;
+            if (g < nfull)
+                for (int i = 0; i < G; ++i) s += w[(g * G + i) * (int64_t)H + j];
+            wbar[g * (int64_t)H + j] = s * inv;
+        }
+    }
+    return 0;
+}
+
 /* --------------------------------------------- scoring-count cost model
  * Appendix A of the same paper: one query-key score is one unit of cost. */
 

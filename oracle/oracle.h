@@ -49,6 +49,12 @@ int oracle_decode(const void *q, const uint8_t *k_cache, const float *k_scale, c
                   const int64_t *rows, int64_t nrows, int32_t *out_idx, double *out_score,
                   int nthreads);
 
+/* The training-free group query: qbar [ceil(Tq/G), H, d] bf16 bits and wbar
+ * [ceil(Tq/G), H] are the means of each complete group's q [Tq, H, d] bf16 and
+ * w [Tq, H] (fp32 sums in query order, times 1/G, q rounded to bf16). */
+int oracle_pool_mean_bf16(const uint16_t *q, const float *w, int64_t Tq, int H, int d, int G,
+                          uint16_t *qbar, float *wbar);
+
 /* out_bank [ceil(Tq/G), P] (ascending bank positions, -1 padding, all -1 for
  * groups that use the original indexer) or NULL; with `rows`, only the banks
  * of the requested rows' groups are computed (other rows all -1).  *pairs

@@ -370,3 +370,101 @@ def test_table5_all_entries(oracle_lib):
             assert math.isclose(round(s, 2), v), (panel, G, P, L, s, v)
             n += 1
     assert n == 108
+
+
+# ------------------------------------------- training-free group query pins
+
+def _bits(t):
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def test_pool_mean_of_identical_rows_is_the_row(oracle_lib):
+    """A group of G copies of one query pools to that query, bit for bit, and
+    its gates to the same gates (catches a wrong 1/G scale or group stride)."""
+    G, NG, H, d = 8, 5, 3, 16
+    g = torch.Generator().manual_seed(21)
+    base = to_bf16(torch.randn(NG, H, d, generator=g))
+    wb = to_bf16(torch.rand(NG, H, generator=g)).float()  # 8-bit values: every sum is exact
+    q = base.repeat_interleave(G, 0)
+    w = wb.repeat_interleave(G, 0)
+    qbar, wbar = oracle.pool_mean_bf16(q, w, G)
+    assert np.array_equal(qbar, _bits(base))
+    np.testing.assert_array_equal(wbar, wb.numpy())
+
+
+@pytest.mark.parametrize("G", [4, 8, 16])
+def test_pool_mean_exact_on_integers(oracle_lib, G):
+    """Small integers: every sum is exact, so the pooled query is the exact mean
+    (a library mean in fp64), which bf16 holds exactly; the trailing incomplete
+    group, which never builds a bank, pools to zero."""
+    wl = _gb(T=G * 7 + 3, G=G, P=16, K=8, seed=22 + G)
+    q, w = wl["q"], wl["w"]
+    qbar, wbar = oracle.pool_mean_bf16(q, w, G)
+    full = (q.shape[0] // G) * G
+    ref_q = _f64(q)[:full].reshape(-1, G, *q.shape[1:]).mean(1)
+    ref_w = _f64(w)[:full].reshape(-1, G, w.shape[1]).mean(1)
+    assert np.array_equal(qbar[:-1], _bits(to_bf16(torch.from_numpy(ref_q).float())))
+    np.testing.assert_array_equal(wbar[:-1], ref_w.astype(np.float32))
+    assert (qbar[-1] == 0).all() and (wbar[-1] == 0).all()
+    assert np.abs(ref_q).max() > 0.2  # the case is not trivially zero
+
+
+def test_pool_mean_within_one_ulp_of_exact(oracle_lib):
+    """Normal inputs: the pooled bf16 value is within one bf16 ulp of the fp64
+    mean rounded to bf16 (the fp32 sum of 16 terms adds far less than one)."""
+    G = 16
+    wl = _gb(T=G * 12, G=G, P=16, K=8, seed=25, dist="normal", H=4, d=32)
+    q, w = wl["q"], wl["w"]
+    qbar, wbar = oracle.pool_mean_bf16(q, w, G)
+    ref_q = _f64(q).reshape(-1, G, *q.shape[1:]).mean(1)
+    ref_b = _bits(to_bf16(torch.from_numpy(ref_q).float())).astype(np.int32)
+    mine = qbar.astype(np.int32)
+    # same sign, at most one step apart in the ordered bf16 code space
+    sign = (mine >> 15) == (ref_b >> 15)
+    near = np.abs((mine & 0x7FFF) - (ref_b & 0x7FFF)) <= 1
+    zero = (ref_b & 0x7FFF) <= 1
+    assert (near & (sign | zero)).all()
+    assert (mine == ref_b).mean() > 0.95
+    # fp32 sum of G signed gates: error below G * 2^-24 of the largest term
+    wg = _f64(w).reshape(-1, G, w.shape[1])
+    bound = G * 2.0 ** -24 * np.abs(wg).max(1) + 1e-30
+    assert (np.abs(wbar - wg.mean(1)) <= bound).all()
+
+
+def test_pooled_bank_is_the_bank_of_the_mean(oracle_lib):
+    """The pooling flag uses the pooled query as the group query with all H heads:
+    on integer inputs (where a library mean is exact) it equals the bank built
+    from the library-mean group query and gates."""
+    T, G, P, K = 200, 8, 40, 12
+    wl = _gb(T=T, G=G, P=P, K=K, seed=26)
+    q, w = wl["q"], wl["w"]
+    qb = torch.from_numpy(_f64(q).reshape(-1, G, *q.shape[1:]).mean(1)).float()
+    wb = torch.from_numpy(_f64(w).reshape(-1, G, w.shape[1]).mean(1)).float()
+    e_i, e_s, e_bank, e_pairs = oracle.group_bank(q, wl["k"], w, to_bf16(qb), wb, "bf16", 0, G, P, K,
+                                                  want_bank=True)
+    p_i, p_s, p_bank, p_pairs = oracle.group_bank(q, wl["k"], w, wl["qbar"], wl["wbar"], "bf16", 0,
+                                                  G, P, K, flags=oracle.POOL_MEAN, want_bank=True)
+    assert np.array_equal(e_i, p_i) and np.array_equal(e_s, p_s)
+    assert np.array_equal(e_bank, p_bank) and e_pairs == p_pairs
+    # and it is not the bank of the trained-query stand-in
+    _, _, t_bank, _ = oracle.group_bank(q, wl["k"], w, wl["qbar"], wl["wbar"], "bf16", 0, G, P, K,
+                                        want_bank=True)
+    assert not np.array_equal(t_bank, p_bank)
+
+
+def test_pooled_identical_group_recovers_dense(oracle_lib):
+    """When every query of a group is the same, the pooled query is that query,
+    so with K <= P every query's dense top-K lies in the bank (the exact
+    recovery of Section 1) and the pooled result equals the dense one."""
+    T, G, P, K = 160, 4, 32, 10
+    wl = _gb(T=T, G=G, P=P, K=K, seed=27, dist="normal")
+    q = wl["q"][::G].repeat_interleave(G, 0).contiguous()
+    w = wl["w"][::G].repeat_interleave(G, 0).contiguous()
+    d_i, d_s = oracle.prefill(q, wl["k"], w, "bf16", 0, K)
+    p_i, p_s, bank, _ = oracle.group_bank(q, wl["k"], w, wl["qbar"], wl["wbar"], "bf16", 0, G, P, K,
+                                          flags=oracle.POOL_MEAN, want_bank=True)
+    assert (bank >= 0).any()
+    # members r > 0 score the same as their anchor on the bank, plus the keys
+    # after it; the dense top-K of the anchor's query over s <= t is inside
+    # bank U (t_anchor, t] because a top-P over s <= t_anchor holds its top-K
+    assert np.array_equal(d_i, p_i) and np.array_equal(d_s, p_s)
