@@ -61,7 +61,10 @@ typedef enum {
     DSAIDX_FP8_E4M3 = 2  /* OCP FP8 E4M3 ("fn") codes, one fp32 scale per token */
 } dsaidx_dtype;
 
-enum { DSAIDX_FORCE_BANK = 1u }; /* group bank: also build banks when t+1 <= P */
+enum {
+    DSAIDX_FORCE_BANK = 1u, /* group bank: also build banks when t+1 <= P */
+    DSAIDX_POOL_MEAN = 2u   /* group bank: training-free group query (mean pooling) */
+};
 
 /*
  * Dense causal indexer, Eq. (1)-(2).  Query i of the call sits at position
@@ -106,11 +109,17 @@ size_t indexer_decode_workspace_size(int B, int64_t Nmax, int H, int d, int topk
  *   qbar       [ceil(Tq/G), Hs, d] dtype codes: the group indexer's query
  *   qbar_scale [ceil(Tq/G)] fp32 (fp8 only, else NULL)
  *   wbar       [ceil(Tq/G), Hs] fp32: the group indexer's head weights
- *   flags      DSAIDX_FORCE_BANK or 0
+ *   flags      DSAIDX_FORCE_BANK and/or DSAIDX_POOL_MEAN, or 0
  *   out_idx    [Tq, topk] int32; out_score [Tq, topk] fp32 or NULL
  *   out_bank   [ceil(Tq/G), P] int32 or NULL: each bank in ascending order
  *              (min(P, t+1) entries, then -1); rows of groups that use the
  *              original indexer are all -1
+ * DSAIDX_POOL_MEAN is the training-free variant of Section 5 (ablation 2,
+ * Table 3) and Appendix B.3-B.4: no group indexer; each bank group's query
+ * and gates are the mean of its G members' q and w (fp32 sums in query
+ * order, times 1/G, the query rounded to the nearest bf16), over all H heads.
+ * It takes bf16 inputs, qbar = wbar = qbar_scale = NULL and Hs == H; the
+ * pooled values live in `ws` (no extra allocation).
  */
 int indexer_group_bank(const void *q, const float *q_scale, const void *k, const float *k_scale,
                        const float *w, int dtype, int64_t Tq, int64_t Tk, int H, int d,
@@ -118,8 +127,10 @@ int indexer_group_bank(const void *q, const float *q_scale, const void *k, const
                        const float *wbar, int Hs, int G, int P, int topk, unsigned flags,
                        int32_t *out_idx, int32_t *out_bank, float *out_score, void *ws,
                        size_t ws_bytes, void *stream);
+/* Workspace bytes for any q_pos0 and bank layout; `flags` as in the call (only
+ * DSAIDX_POOL_MEAN changes the size: it adds the pooled queries and gates). */
 size_t indexer_group_bank_workspace_size(int64_t Tq, int64_t Tk, int H, int Hs, int d, int G,
-                                         int P, int topk, int dtype);
+                                         int P, int topk, int dtype, unsigned flags);
 
 /* Number of query-key scores indexer_group_bank evaluates for these sizes
  * (the unit of the cost model of Appendix A.1): fallback queries score t+1

@@ -8,6 +8,8 @@ without the built library, or with host tensors, raises.
     idx, score = indexer_prefill(q, k, w, q_pos0, topk, q_scale=None, k_scale=None)
     idx, score = indexer_decode(q, k_cache, k_scale, w, seq_lens, topk)
     idx, score, bank = indexer_group_bank(q, k, w, qbar, wbar, q_pos0, G, P, topk, ...)
+    idx, score, bank = indexer_group_bank(q, k, w, None, None, q_pos0, G, P, topk,
+                                          flags=POOL_MEAN)   # training-free group query
 
 Tensors (contiguous, on the GPU): q [Tq,H,d] bf16 or uint8 E4M3 codes,
 k [Tk,d] the same dtype, w [Tq,H] fp32, per-token fp32 scales for E4M3.
@@ -16,14 +18,15 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import (DSAIDX_BF16, DSAIDX_FORCE_BANK, DSAIDX_FP8_E4M3, DSAIDX_OK, LIB_PATH,  # noqa: F401
-                   last_error, lib)
+from ._lib import (DSAIDX_BF16, DSAIDX_FORCE_BANK, DSAIDX_FP8_E4M3, DSAIDX_OK,  # noqa: F401
+                   DSAIDX_POOL_MEAN, LIB_PATH, last_error, lib)
 
 __all__ = ["indexer_prefill", "indexer_decode", "indexer_group_bank", "indexer_group_bank_pairs",
-           "workspace_prefill", "workspace_decode", "workspace_group_bank", "FORCE_BANK", "lib",
+           "workspace_prefill", "workspace_decode", "workspace_group_bank", "FORCE_BANK", "POOL_MEAN", "lib",
            "LIB_PATH"]
 
 FORCE_BANK = DSAIDX_FORCE_BANK
+POOL_MEAN = DSAIDX_POOL_MEAN
 
 
 def _ptr(t):
@@ -76,8 +79,8 @@ def workspace_decode(B, Nmax, H, d, topk):
     return lib().indexer_decode_workspace_size(B, Nmax, H, d, topk)
 
 
-def workspace_group_bank(Tq, Tk, H, Hs, d, G, P, topk, dtype):
-    return lib().indexer_group_bank_workspace_size(Tq, Tk, H, Hs, d, G, P, topk, dtype)
+def workspace_group_bank(Tq, Tk, H, Hs, d, G, P, topk, dtype, flags=0):
+    return lib().indexer_group_bank_workspace_size(Tq, Tk, H, Hs, d, G, P, topk, dtype, flags)
 
 
 def indexer_group_bank_pairs(Tq, q_pos0, G, P, flags=0):
@@ -126,11 +129,14 @@ def indexer_decode(q, k_cache, k_scale, w, seq_lens, topk=2048, want_score=True,
 def indexer_group_bank(q, k, w, qbar, wbar, q_pos0, G, P, topk=2048, q_scale=None, k_scale=None,
                        qbar_scale=None, flags=0, want_score=True, want_bank=False, out_idx=None,
                        out_score=None, out_bank=None, ws=None):
-    """ADIndex bank sharing (Eq. (8), (13), (14)); returns (idx, score or None, bank or None)."""
+    """ADIndex bank sharing (Eq. (8), (13), (14)); returns (idx, score or None, bank or None).
+
+    With ``flags & POOL_MEAN`` pass qbar = wbar = None: the group query is the
+    mean of each group's own queries and gates (the training-free variant)."""
     dev = _dev(q, k, w, qbar, wbar, q_scale, k_scale, qbar_scale, out_idx, out_score, out_bank, ws)
     Tq, H, d = q.shape
     Tk = k.shape[0]
-    Hs = qbar.shape[1]
+    Hs = H if qbar is None else qbar.shape[1]
     dt = _dtype(q)
     NG = -(-Tq // G)
     if out_idx is None:
@@ -139,7 +145,7 @@ def indexer_group_bank(q, k, w, qbar, wbar, q_pos0, G, P, topk=2048, q_scale=Non
         out_score = torch.empty((Tq, topk), dtype=torch.float32, device=dev)
     if want_bank and out_bank is None:
         out_bank = torch.empty((NG, P), dtype=torch.int32, device=dev)
-    ws = _ws(workspace_group_bank(Tq, Tk, H, Hs, d, G, P, topk, dt), dev, ws)
+    ws = _ws(workspace_group_bank(Tq, Tk, H, Hs, d, G, P, topk, dt, flags), dev, ws)
     rc = lib().indexer_group_bank(_ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(w), dt, Tq, Tk, H, d,
                                   q_pos0, _ptr(qbar), _ptr(qbar_scale), _ptr(wbar), Hs, G, P, topk, flags,
                                   _ptr(out_idx), _ptr(out_bank), _ptr(out_score), _ptr(ws),

@@ -15,6 +15,7 @@ DSAIDX_ERR_HIP = -4
 DSAIDX_BF16 = 1
 DSAIDX_FP8_E4M3 = 2
 DSAIDX_FORCE_BANK = 1
+DSAIDX_POOL_MEAN = 2
 
 # exported symbol -> (restype, argtypes)
 _P, _I, _I64, _U, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint, ctypes.c_size_t
@@ -25,7 +26,7 @@ SIGNATURES = {
     "indexer_decode_workspace_size": (_SZ, [_I, _I64, _I, _I, _I]),
     "indexer_group_bank": (_I, [_P, _P, _P, _P, _P, _I, _I64, _I64, _I, _I, _I64, _P, _P, _P, _I, _I, _I,
                                 _I, _U, _P, _P, _P, _P, _SZ, _P]),
-    "indexer_group_bank_workspace_size": (_SZ, [_I64, _I64, _I, _I, _I, _I, _I, _I, _I]),
+    "indexer_group_bank_workspace_size": (_SZ, [_I64, _I64, _I, _I, _I, _I, _I, _I, _I, _U]),
     "indexer_group_bank_pairs": (_I64, [_I64, _I64, _I, _I, _U]),
     "indexer_last_error": (ctypes.c_char_p, []),
 }

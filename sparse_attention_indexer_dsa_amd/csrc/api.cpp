@@ -161,11 +161,22 @@ GroupPlan plan_groups(int64_t Tq, int64_t q_pos0, int G, int P, unsigned flags) 
   return p;
 }
 
-size_t group_ws_bytes(int64_t Tq, int G, int P, int topk, unsigned flags, int64_t q_pos0,
-                      bool bank_in_ws) {
+// The pooled group query and gates of the bank groups (DSAIDX_POOL_MEAN).
+size_t pool_q_bytes(int64_t nelig, int H, int d) {
+  return align_up((size_t)(nelig > 0 ? nelig : 0) * H * d * 2u);
+}
+size_t pool_w_bytes(int64_t nelig, int H) {
+  return align_up((size_t)(nelig > 0 ? nelig : 0) * H * 4u);
+}
+
+// workspace: [bank groups' banks, when out_bank is NULL] [pooled group query
+// and gates, with DSAIDX_POOL_MEAN] [candidate buffers of one launch]
+size_t group_ws_bytes(int64_t Tq, int H, int d, int G, int P, int topk, unsigned flags,
+                      int64_t q_pos0, bool bank_in_ws) {
   const GroupPlan p = plan_groups(Tq, q_pos0, G, P, flags);
   const int64_t nelig = p.nfull - p.g0;
   size_t bank = bank_in_ws ? align_up((size_t)(nelig > 0 ? nelig : 0) * P * 4u) : 0;
+  if (flags & DSAIDX_POOL_MEAN) bank += pool_q_bytes(nelig, H, d) + pool_w_bytes(nelig, H);
   const int64_t anchors = nelig < kAnchorsPerLaunch ? nelig : kAnchorsPerLaunch;
   const int64_t rows = Tq < kRowsPerLaunch ? Tq : kRowsPerLaunch;
   size_t scan = anchors > 0 ? cand_bytes(anchors, P) : 0;
@@ -313,11 +324,12 @@ int64_t indexer_group_bank_pairs(int64_t Tq, int64_t q_pos0, int G, int P, unsig
 }
 
 size_t indexer_group_bank_workspace_size(int64_t Tq, int64_t Tk, int H, int Hs, int d, int G,
-                                         int P, int topk, int dtype) {
-  (void)Tk; (void)H; (void)Hs; (void)d; (void)dtype;
-  if (Tq <= 0 || G <= 0 || P <= 0 || topk <= 0) return 0;
+                                         int P, int topk, int dtype, unsigned flags) {
+  (void)Tk; (void)Hs; (void)dtype;
+  if (Tq <= 0 || G <= 0 || P <= 0 || topk <= 0 || H <= 0 || d <= 0) return 0;
   // sized for the worst case: a bank for every complete group, kept in ws
-  return group_ws_bytes(Tq, G, P, topk, DSAIDX_FORCE_BANK, 0, true);
+  return group_ws_bytes(Tq, H, d, G, P, topk, DSAIDX_FORCE_BANK | (flags & DSAIDX_POOL_MEAN), 0,
+                        true);
 }
 
 int indexer_group_bank(const void* q, const float* q_scale, const void* k, const float* k_scale,
@@ -336,17 +348,25 @@ int indexer_group_bank(const void* q, const float* q_scale, const void* k, const
   if (Hs < 1) return fail(DSAIDX_ERR_INVALID_ARG, "Hs = %d must be positive", Hs);
   if (Hs > kMaxHeads) return fail(DSAIDX_ERR_UNSUPPORTED, "Hs = %d above %d", Hs, kMaxHeads);
   if (q_pos0 % G) return fail(DSAIDX_ERR_INVALID_ARG, "q_pos0 must be a multiple of G");
-  if (flags & ~(unsigned)DSAIDX_FORCE_BANK)
+  if (flags & ~(unsigned)(DSAIDX_FORCE_BANK | DSAIDX_POOL_MEAN))
     return fail(DSAIDX_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
   const bool fp8 = dtype == DSAIDX_FP8_E4M3;
-  if (Tq > 0 && (!qbar || !wbar)) return fail(DSAIDX_ERR_INVALID_ARG, "null qbar or wbar");
+  const bool pool = (flags & DSAIDX_POOL_MEAN) != 0;
+  if (pool) {
+    if (fp8) return fail(DSAIDX_ERR_UNSUPPORTED, "DSAIDX_POOL_MEAN takes bf16 queries");
+    if (qbar || wbar || qbar_scale)
+      return fail(DSAIDX_ERR_INVALID_ARG, "DSAIDX_POOL_MEAN takes NULL qbar, wbar and qbar_scale");
+    if (Hs != H) return fail(DSAIDX_ERR_INVALID_ARG, "DSAIDX_POOL_MEAN needs Hs == H");
+  }
+  if (Tq > 0 && !pool && (!qbar || !wbar)) return fail(DSAIDX_ERR_INVALID_ARG, "null qbar or wbar");
   if (Tq > 0 && fp8 && !qbar_scale)
     return fail(DSAIDX_ERR_INVALID_ARG, "fp8 inputs need qbar_scale");
   if (!fp8 && qbar_scale) return fail(DSAIDX_ERR_INVALID_ARG, "bf16 qbar takes no scale");
   if (!aligned16(qbar) || !aligned16(wbar) || !aligned16(out_bank))
     return fail(DSAIDX_ERR_INVALID_ARG, "qbar, wbar and out_bank must be 16-byte aligned");
   if ((uintptr_t)qbar_scale & 3u) return fail(DSAIDX_ERR_INVALID_ARG, "qbar_scale misaligned");
-  rc = check_ws(ws, ws_bytes, group_ws_bytes(Tq, G, P, topk, flags, q_pos0, out_bank == nullptr));
+  rc = check_ws(ws, ws_bytes,
+                group_ws_bytes(Tq, H, d, G, P, topk, flags, q_pos0, out_bank == nullptr));
   if (rc) return rc;
   if (Tq == 0) return ok();
 
@@ -367,6 +387,29 @@ int indexer_group_bank(const void* q, const float* q_scale, const void* k, const
     bank = (int32_t*)ws;
     cand_ws = (uint8_t*)ws + align_up((size_t)(nelig > 0 ? nelig : 0) * P * 4u);
   }
+  // the bank groups' group query: the caller's, or the mean of each group's
+  // own queries and gates (pooled groups g0 .. nfull-1, rows from 0)
+  const void* gq = qbar;
+  const float* gw = wbar;
+  int64_t gq_row0 = 0;  // row of qbar / wbar holding group g0
+  if (pool) {
+    PoolArgs pa{};
+    pa.q = q;
+    pa.w = w;
+    pa.H = H;
+    pa.d = d;
+    pa.G = G;
+    pa.g0 = p.g0;
+    pa.ngroups = nelig > 0 ? nelig : 0;
+    pa.qbar = cand_ws;
+    pa.wbar = (float*)((uint8_t*)cand_ws + pool_q_bytes(nelig, H, d));
+    gq = pa.qbar;
+    gw = pa.wbar;
+    gq_row0 = -p.g0;
+    cand_ws = (uint8_t*)cand_ws + pool_q_bytes(nelig, H, d) + pool_w_bytes(nelig, H);
+    hipError_t e = launch_pool_mean(pa, st);
+    if (e != hipSuccess) return hip_fail(e, "indexer_group_bank pooling launch");
+  }
 
   // 1. original indexer for the rows whose groups build no bank
   hipError_t e = run_dense(q, q_scale, k, k_scale, w, dtype, H, d, q_pos0, 0, p.g0 * G, topk,
@@ -383,9 +426,9 @@ int indexer_group_bank(const void* q, const float* q_scale, const void* k, const
     const int64_t n = nelig - s < kAnchorsPerLaunch ? nelig - s : kAnchorsPerLaunch;
     const int64_t g = p.g0 + s;
     ScanArgs a{};
-    a.q = (const uint8_t*)qbar + g * Hs * (int64_t)rb;
+    a.q = (const uint8_t*)gq + (g + gq_row0) * Hs * (int64_t)rb;
     a.q_scale = qbar_scale ? qbar_scale + g : nullptr;
-    a.w = wbar + g * Hs;
+    a.w = gw + (g + gq_row0) * Hs;
     a.k = k;
     a.k_scale = k_scale;
     a.H = Hs;

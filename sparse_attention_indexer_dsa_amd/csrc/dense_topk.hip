@@ -75,12 +75,6 @@ __device__ __forceinline__ v16f mfma(const typename AFrag<DT>::type& a,
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs)
-__device__ __forceinline__ uint16_t bf16_rne(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-}
-
 template <int DT>
 __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs args) {
   using C = Cfg<DT>;

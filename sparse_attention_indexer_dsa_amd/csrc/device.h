@@ -50,6 +50,12 @@ __device__ __forceinline__ void gated_relu_sum16(const float* w, const v16f& acc
   }
 }
 
+// fp32 -> bf16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ uint16_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 __device__ __forceinline__ int popc(uint64_t m) { return __popcll(m); }

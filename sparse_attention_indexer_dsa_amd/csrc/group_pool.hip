@@ -1,0 +1,87 @@
+// group_pool.hip -- the training-free group query of ADIndex (Qi et al.),
+// Section 5 ablation 2 and Appendix B.3-B.4: a frozen DSA indexer builds a
+// group's token bank from the mean of the group's own indexer queries (head by
+// head) and of their gate weights, in place of a trained group indexer.
+//
+// Memory-bound and tiny beside the scans it feeds: one workgroup row per group,
+// each thread summing one 16-byte chunk (8 bf16) of the H*d query over the G
+// member queries, in query order in fp32, then scaling by 1/G (exact, G a power
+// of two) and rounding to the nearest bf16.  The gates are summed the same way
+// and kept in fp32.  The pooled query is an input of integer decisions (which
+// keys enter the bank), so this order is part of the contract.
+#include "device.h"
+#include "launch.h"
+
+namespace dsaidx {
+
+namespace {
+
+constexpr int kPoolThreads = 256;
+
+__device__ __forceinline__ float lo_bf16(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+template <int G>
+__global__ void __launch_bounds__(kPoolThreads) pool_mean_kernel(const PoolArgs a) {
+  const int64_t grp = a.g0 + blockIdx.y;
+  const int nchunk = a.H * a.d / 8;  // 16-byte chunks of one query row
+  const int c = blockIdx.x * kPoolThreads + threadIdx.x;
+  const float inv = 1.0f / (float)G;
+  if (c < nchunk) {
+    const uint4* src = reinterpret_cast<const uint4*>(a.q) + grp * G * nchunk + c;
+    uint4 v[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) v[i] = src[(int64_t)i * nchunk];
+    float s[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s[j] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      s[0] += lo_bf16(v[i].x); s[1] += hi_bf16(v[i].x);
+      s[2] += lo_bf16(v[i].y); s[3] += hi_bf16(v[i].y);
+      s[4] += lo_bf16(v[i].z); s[5] += hi_bf16(v[i].z);
+      s[6] += lo_bf16(v[i].w); s[7] += hi_bf16(v[i].w);
+    }
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      o[j] = (uint32_t)bf16_rne(s[2 * j] * inv) | ((uint32_t)bf16_rne(s[2 * j + 1] * inv) << 16);
+    reinterpret_cast<uint4*>(a.qbar)[(int64_t)blockIdx.y * nchunk + c] =
+        make_uint4(o[0], o[1], o[2], o[3]);
+  }
+  if (blockIdx.x == 0 && threadIdx.x < a.H) {
+    const float* src = a.w + grp * G * a.H + threadIdx.x;
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < G; ++i) s += src[(int64_t)i * a.H];
+    a.wbar[(int64_t)blockIdx.y * a.H + threadIdx.x] = s * inv;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pool_mean(const PoolArgs& args, hipStream_t stream) {
+  if ((args.H * args.d) % 8 || args.H > kPoolThreads) return hipErrorInvalidValue;
+  const int nchunk = args.H * args.d / 8;
+  const int bx = (nchunk + kPoolThreads - 1) / kPoolThreads;
+  constexpr int64_t kGroupsPerLaunch = 32768;  // grid y limit
+  for (int64_t s = 0; s < args.ngroups; s += kGroupsPerLaunch) {
+    PoolArgs a = args;
+    a.g0 = args.g0 + s;
+    a.ngroups = args.ngroups - s < kGroupsPerLaunch ? args.ngroups - s : kGroupsPerLaunch;
+    a.qbar = (uint8_t*)args.qbar + s * args.H * args.d * 2;
+    a.wbar = args.wbar + s * args.H;
+    const dim3 grid((unsigned)bx, (unsigned)a.ngroups);
+    switch (a.G) {
+      case 4: hipLaunchKernelGGL(pool_mean_kernel<4>, grid, dim3(kPoolThreads), 0, stream, a); break;
+      case 8: hipLaunchKernelGGL(pool_mean_kernel<8>, grid, dim3(kPoolThreads), 0, stream, a); break;
+      case 16: hipLaunchKernelGGL(pool_mean_kernel<16>, grid, dim3(kPoolThreads), 0, stream, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace dsaidx

@@ -77,6 +77,20 @@ constexpr int kDecCandCap = 8192;     // threshold-bin candidates a row keeps in
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
+// Mean-pooled group query: for groups g0 .. g0+ngroups-1 of G consecutive
+// queries of q [*, H, d] bf16 and w [*, H], writes qbar [ngroups, H, d] bf16
+// and wbar [ngroups, H] fp32 (fp32 sums in query order, times 1/G, q rounded
+// to the nearest bf16).  H*d a multiple of 8, q 16-byte aligned; H <= 256.
+struct PoolArgs {
+  const void* q;
+  const float* w;
+  int H, d, G;
+  int64_t g0, ngroups;
+  void* qbar;
+  float* wbar;
+};
+hipError_t launch_pool_mean(const PoolArgs& a, hipStream_t stream);
+
 // Fill n int32 values with v (a kernel, not a memset node).
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t stream);
 

@@ -74,7 +74,11 @@ def test_workspace_sizes(L):
     c = L.indexer_prefill_workspace_size(40000, 131072, 64, 128, 2048, FP8)
     assert 0 < a < b <= c  # capped by the rows of one launch
     assert L.indexer_decode_workspace_size(32, 262144, 64, 128, 2048) >= 32 * 262144 * 4
-    assert L.indexer_group_bank_workspace_size(65536, 65536, 64, 64, 128, 16, 8192, 2048, BF16) > 0
+    g = L.indexer_group_bank_workspace_size(65536, 65536, 64, 64, 128, 16, 8192, 2048, BF16, 0)
+    assert g > 0
+    # mean pooling adds the pooled bf16 queries and fp32 gates of every complete group
+    gp = L.indexer_group_bank_workspace_size(65536, 65536, 64, 64, 128, 16, 8192, 2048, BF16, 2)
+    assert gp - g == 4096 * 64 * 128 * 2 + 4096 * 64 * 4
 
 
 def _decode(L, **kw):
@@ -106,7 +110,10 @@ def _group(L, **kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(G=5), UNSUPPORTED), (dict(G=32), UNSUPPORTED), (dict(P=4), INVALID), (dict(P=20000), UNSUPPORTED),
-    (dict(q_pos0=8, Tk=128), INVALID), (dict(flags=2), INVALID), (dict(qbar=None), INVALID),
+    (dict(q_pos0=8, Tk=128), INVALID), (dict(flags=4), INVALID), (dict(qbar=None), INVALID),
+    (dict(flags=2), INVALID), (dict(flags=2, qbar=None), INVALID),
+    (dict(flags=2, qbar=None, wbar=None, Hs=4), INVALID),
+    (dict(flags=2, qbar=None, wbar=None, dtype=FP8, qs=A, ks=A), UNSUPPORTED),
     (dict(Hs=0), INVALID), (dict(Hs=80), UNSUPPORTED), (dict(dtype=FP8, qs=A, ks=A), INVALID),
     (dict(qbs=A), INVALID), (dict(bank=P((1 << 20) + 4)), INVALID), (dict(ws_bytes=1), WORKSPACE),
 ])

@@ -100,20 +100,27 @@ def test_decode_256k(dsa, dist):
     compare(gi.cpu().numpy()[rows], gs.cpu().numpy()[rows], ri, rs, dist == "int", score_of)
 
 
+@pytest.mark.parametrize("pool", [False, True])
 @pytest.mark.parametrize("dist", ["normal", "int"])
-def test_adindex_64k_bank(dsa, dist):
-    """T=65536, G=16, P=8192, 64-head group indexer; sampled rows in the
-    fallback groups (anchor+1 <= P) and in bank groups, with their banks."""
+def test_adindex_64k_bank(dsa, dist, pool):
+    """T=65536, G=16, P=8192, 64-head group indexer (or, with pooling, the
+    training-free mean-pooled group query); sampled rows in the fallback groups
+    (anchor+1 <= P) and in bank groups, with their banks."""
     T, G, P, K = 65536, 16, 8192, 2048
+    flags = dsa.POOL_MEAN if pool else 0
     wl = make_workload(5, seed=6, device="cuda", dist=dist)
     t = wl.tensors
-    gi, gs, gb = dsa.indexer_group_bank(t["q"], t["k"], t["w"], t["qbar"], t["wbar"], 0, G, P, K,
-                                        want_bank=True)
+    gi, gs, gb = dsa.indexer_group_bank(t["q"], t["k"], t["w"], None if pool else t["qbar"],
+                                        None if pool else t["wbar"], 0, G, P, K, flags=flags, want_bank=True)
     torch.cuda.synchronize()
     rows = np.unique(np.array([5, 8191, 8192, 8193, 8207, 20000, 33333, 50001, 65520, 65535]))
     h = _host(t)
     ri, rs, rb, pairs = oracle.group_bank(h["q"], h["k"], h["w"], h["qbar"], h["wbar"], "bf16", 0, G, P, K,
-                                          rows=rows, want_bank=True)
+                                          flags=flags, rows=rows, want_bank=True)
+    if pool:  # score the banks with the oracle's pooled query
+        pq, pw = oracle.pool_mean_bf16(h["q"], h["w"], G)
+        h["qbar"] = torch.from_numpy(pq.view(np.int16)).view(torch.bfloat16)
+        h["wbar"] = torch.from_numpy(pw)
     assert pairs == dsa.indexer_group_bank_pairs(T, 0, G, P) == 635_846_144
     gbank = gb.cpu().numpy()
     groups = np.unique(rows // G)

@@ -263,7 +263,9 @@ def _group_check(dsa, wl, flags=0, rows=None, exact=None):
     p = wl.params
     G, P, K = p["G"], p["P"], p["topk"]
     t = {k: v.cuda() for k, v in wl.tensors.items()}
-    gi, gs, gb = dsa.indexer_group_bank(t["q"], t["k"], t["w"], t["qbar"], t["wbar"], p["q_pos0"], G, P, K,
+    pool = bool(flags & dsa.POOL_MEAN)
+    gqbar, gwbar = (None, None) if pool else (t["qbar"], t["wbar"])
+    gi, gs, gb = dsa.indexer_group_bank(t["q"], t["k"], t["w"], gqbar, gwbar, p["q_pos0"], G, P, K,
                                         t.get("q_scale"), t.get("k_scale"), t.get("qbar_scale"), flags=flags,
                                         want_bank=True)
     torch.cuda.synchronize()
@@ -290,16 +292,21 @@ def _group_check(dsa, wl, flags=0, rows=None, exact=None):
         # is the oracle's bank
         groups = np.unique(rows // G)
         gbank = _np(gb)[groups]
+        qbar, wbar = wl["qbar"], wl["wbar"]
+        if pool:  # the group score of the pooled query (the oracle's pooling)
+            pq, pw = oracle.pool_mean_bf16(wl["q"], wl["w"], G)
+            qbar = torch.from_numpy(pq.view(np.int16)).view(torch.bfloat16)
+            wbar = torch.from_numpy(pw)
         bscore = np.full(rb[groups].shape, -np.inf)
         for n, g in enumerate(groups):
             v = rb[g][rb[g] >= 0]
             if len(v):
-                bscore[n, :len(v)] = oracle.score_pairs(wl["qbar"], wl["k"], wl["wbar"], np.full(len(v), g), v,
+                bscore[n, :len(v)] = oracle.score_pairs(qbar, wl["k"], wbar, np.full(len(v), g), v,
                                                         wl.dtype, wl.dtype, wl.tensors.get("qbar_scale"),
                                                         wl.tensors.get("k_scale"))
 
         def bank_score_of(n, keys):
-            return oracle.score_pairs(wl["qbar"], wl["k"], wl["wbar"], np.full(len(keys), groups[n]), keys,
+            return oracle.score_pairs(qbar, wl["k"], wbar, np.full(len(keys), groups[n]), keys,
                                       wl.dtype, wl.dtype, wl.tensors.get("qbar_scale"), wl.tensors.get("k_scale"))
         compare(gbank, None, rb[groups], bscore, False, bank_score_of, label="bank")
         same_bank = np.array([np.array_equal(_np(gb)[r // G], rb[r // G]) for r in rows])
@@ -329,6 +336,31 @@ def test_group_bank_h64_exact(dsa, G):
 def test_group_bank_fp8_exact(dsa):
     wl = make_group_bank(T=900, H=64, Hs=16, d=128, topk=64, G=16, P=256, dtype="fp8", dist="int", seed=18)
     _group_check(dsa, wl, rows=_rows(900, 48, 18))
+
+
+@pytest.mark.parametrize("G", [4, 8, 16])
+def test_group_bank_pooled_exact(dsa, G):
+    """Training-free group query (mean pooling) at H = 64, d = 128 on integer
+    inputs: the pooled query, the bank and every refined row match exactly."""
+    wl = make_group_bank(T=1600, H=64, Hs=64, d=128, topk=128, G=G, P=512, dtype="bf16", dist="int",
+                         seed=40 + G)
+    _group_check(dsa, wl, flags=dsa.POOL_MEAN, rows=_rows(1600, 48, 40 + G))
+
+
+@pytest.mark.parametrize("flags", [2, 3])
+def test_group_bank_pooled_small_heads(dsa, flags):
+    """Pooling with the general kernel (8 heads, d = 32), fallback and bank
+    groups, a trailing incomplete group and q_pos0 > 0; with and without
+    forced banks."""
+    wl = make_group_bank(T=700, H=8, Hs=8, d=32, topk=40, G=4, P=96, dtype="bf16", dist="int", seed=44,
+                         Tq=646, q_pos0=52)
+    _group_check(dsa, wl, flags)
+
+
+def test_group_bank_pooled_random(dsa):
+    wl = make_group_bank(T=2000, H=64, Hs=64, d=128, topk=256, G=16, P=1024, dtype="bf16", dist="normal",
+                         seed=45)
+    _group_check(dsa, wl, flags=dsa.POOL_MEAN, rows=_rows(2000, 48, 45))
 
 
 def test_group_bank_random(dsa):
