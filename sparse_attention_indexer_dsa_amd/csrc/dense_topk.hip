@@ -74,6 +74,44 @@ __device__ __forceinline__ v16f mfma(const typename AFrag<DT>::type& a,
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Descriptor words of a raw buffer of `bytes` bytes at p (no stride; reads
+// past the end return zero), held in SGPRs.
+__device__ __forceinline__ v4i raw_buffer_words(const void* p, uint32_t bytes) {
+  const uint64_t a = (uint64_t)p;
+  v4i r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
+  r.z = __builtin_amdgcn_readfirstlane((int)bytes);
+  r.w = (int)kBufferWord3;
+  return r;
+}
+
+// LDS byte address of a pointer into a __shared__ array (wave-uniform here).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void*)p);
+}
+
+// Tile loads straight into LDS (buffer_load ... lds): lane i's bytes land at
+// LDS address m0 + size * i.  They are written as asm, not with the builtin,
+// because the compiler cannot tell the LDS stage a builtin load writes from
+// the stages the same step reads (the stage index is a run-time value), and so
+// it waits for every load in flight, this step's too, before each LDS read: the
+// ring's prefetch distance collapses to zero.  The kernel orders the ring
+// itself: a wave waits for its own loads of a tile with s_waitcnt vmcnt and the
+// barrier that follows publishes the tile to the workgroup.  These loads have
+// no register results, so nothing is left in flight that the compiler could
+// reuse; m0 is declared clobbered, and one wait state separates its write
+// from the load (the SALU-to-LDS-DMA m0 hazard).
+__device__ __forceinline__ void dma_b128(const v4i& rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_b32(const v4i& rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
 
 template <int DT>
 __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs args) {
@@ -201,11 +239,9 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   // Buffer resources end at the workgroup's last candidate key, so rows past
   // it (the last tile's tail, and the tiles requested past the end) read as
   // zeros and are masked when appended; no request needs a clamp or branch.
-  const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)args.k, (short)0, ncand_blk * C::kRowBytes, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t sres = DT == kFP8
-      ? __builtin_amdgcn_make_buffer_rsrc((void*)args.k_scale, (short)0, ncand_blk * 4, kBufferWord3)
-      : __builtin_amdgcn_make_buffer_rsrc((void*)args.w, (short)0, 256, kBufferWord3);
+  const v4i kres = raw_buffer_words(args.k, ncand_blk * C::kRowBytes);
+  const v4i sres = DT == kFP8 ? raw_buffer_words(args.k_scale, ncand_blk * 4)
+                              : raw_buffer_words(args.w, 256);
   int lane_off[C::kDma];  // byte offset of this lane's chunk inside a tile
 #pragma unroll
   for (int n = 0; n < C::kDma; ++n) {
@@ -215,15 +251,12 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   }
   auto request = [&](int t, int st) __attribute__((always_inline)) {
 #pragma unroll
-    for (int n = 0; n < C::kDma; ++n) {
-      uint8_t* dst = &s_tile[st][(n * kThreads + wave * 64) * 16];
-      const int off = lane_off[n] + t * C::kTileBytes;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kres, (lds_void*)dst, 16, off, 0, 0, 0);
-    }
+    for (int n = 0; n < C::kDma; ++n)
+      dma_b128(kres, lds_addr(&s_tile[st][(n * kThreads + wave * 64) * 16]),
+               lane_off[n] + t * C::kTileBytes);
     // every wave writes the same 64 scales (fp8; bf16 loads placeholder words),
     // so all waves issue the same number of requests per step
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(sres, (lds_void*)&s_ks[st][0], 4,
-                                             DT == kFP8 ? 4 * (t * kTile + l) : 4 * l, 0, 0, 0);
+    dma_b32(sres, lds_addr(&s_ks[st][0]), DT == kFP8 ? 4 * (t * kTile + l) : 4 * l);
   };
 
   // B operands of sub-tile u of the tile in stage st (row 32u + col has the
@@ -371,6 +404,9 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
     st1 = st1 == kStages - 1 ? 0 : st1 + 1;
   }
 
+  // the requests issued past the last tile: none may still be writing LDS
+  // when the wave ends
+  __builtin_amdgcn_s_waitcnt(0x3F70);
   if (!active) return;
   flush();
   wave_mem_fence();
