@@ -19,6 +19,7 @@ _SRC = os.path.join(_HERE, "oracle.c")
 
 F32, BF16, E4M3 = 0, 1, 2
 FORCE_BANK = 1
+WINDOW = 4  # group_bank flag: MTP window, eligibility decided on the first query
 
 _lib = None
 
@@ -56,6 +57,11 @@ def lib():
                                         I32, I32, ctypes.c_uint, P, I64, P, P, P, P, I32]
         L.oracle_pool_mean_bf16.restype = I32
         L.oracle_pool_mean_bf16.argtypes = [P, P, I64, I32, I32, I32, P, P]
+        L.oracle_mtp.restype = I32
+        L.oracle_mtp.argtypes = [P, P, P, P, P, P, P, I32, I64, I32, I32, I32, I32, I32, I32, I32, P, I64,
+                                 P, P, P, P, I32]
+        L.oracle_mtp_pairs.restype = I64
+        L.oracle_mtp_pairs.argtypes = [P, I32, I32, I32, I32]
         L.oracle_group_bank_pairs.restype = I64
         L.oracle_group_bank_pairs.argtypes = [I64, I64, I32, I32, ctypes.c_uint]
         for name in ("oracle_cost_prefill_base",):
@@ -213,6 +219,50 @@ def group_bank(q, k, w, qbar, wbar, dtype, q_pos0, G, P, topk, flags=0, q_scale=
     if rc != 0:
         raise ValueError(f"oracle_group_bank failed ({rc})")
     return idx, sc, bank, pairs.value
+
+
+def mtp(q, k_cache, k_scale, w, qbar, wbar, prefix_lens, G, P, topk, flags=0, rows=None, want_bank=False,
+        nthreads=0):
+    """MTP target verification (Section 4.3; Appendix A.2): windows of m bf16
+    queries [B,m,H,d] over E4M3 caches [B,Nmax,d]; N_b = prefix_lens[b] keys
+    visible to each window's first query.  ``flags & POOL_MEAN`` pools each
+    group's own queries and gates (qbar, wbar ignored).  Rows index [B*m].
+    Returns (idx [n,topk], score [n,topk], bank [B,m/G,P] or None, pairs)."""
+    q, k_cache, k_scale = _host(q), _host(k_cache), _host(k_scale)
+    w = _host(w).astype(np.float32)
+    B, m, H, d = q.shape
+    Nmax = k_cache.shape[1]
+    if flags & POOL_MEAN:
+        pooled = [pool_mean_bf16(q[b], w[b], G) for b in range(B)]
+        qbar = np.stack([p[0] for p in pooled])
+        wbar = np.stack([p[1] for p in pooled])
+    else:
+        qbar, wbar = _host(qbar), _host(wbar).astype(np.float32)
+    qbar = np.ascontiguousarray(np.asarray(qbar).view(np.uint16))
+    Hs = qbar.shape[2]
+    lens = np.ascontiguousarray(_host(prefix_lens).astype(np.int32))
+    r, nr = _rows(None if rows is None else np.unique(rows))
+    if rows is not None and len(np.unique(rows)) != len(rows):
+        raise ValueError("rows must be distinct")
+    order = None if rows is None else np.argsort(np.argsort(np.asarray(rows)))
+    n = nr if r is not None else B * m
+    idx = np.empty((n, topk), np.int32)
+    sc = np.empty((n, topk), np.float64)
+    bank = np.empty((B, m // G, P), np.int32) if want_bank else None
+    pairs = ctypes.c_int64(0)
+    rc = lib().oracle_mtp(_ptr(q), _ptr(k_cache), _ptr(k_scale), _ptr(w), _ptr(qbar), _ptr(wbar), _ptr(lens), B,
+                          Nmax, m, H, Hs, d, G, P, topk, _ptr(r), nr, _ptr(idx), _ptr(sc), _ptr(bank),
+                          ctypes.cast(ctypes.pointer(pairs), ctypes.c_void_p), nthreads)
+    if rc != 0:
+        raise ValueError(f"oracle_mtp failed ({rc})")
+    if order is not None:  # back to the caller's row order
+        idx, sc = idx[order], sc[order]
+    return idx, sc, bank, pairs.value
+
+
+def mtp_pairs(prefix_lens, m, G, P) -> int:
+    lens = np.ascontiguousarray(np.asarray(prefix_lens, np.int32))
+    return lib().oracle_mtp_pairs(_ptr(lens), len(lens), m, G, P)
 
 
 def group_bank_pairs(Tq, q_pos0, G, P, flags=0) -> int:

@@ -296,6 +296,8 @@ static int group_uses_bank(int64_t g, int64_t Tq, int64_t q_pos0, int G, int P, 
     int64_t anchor = q_pos0 + g * G;
     if (flags & ORACLE_FORCE_BANK)
         return 1;
+    if (flags & ORACLE_WINDOW)
+        anchor = q_pos0; /* MTP: decided once, on the window's first query */
     return anchor + 1 > P;
 }
 
@@ -341,19 +343,14 @@ static int64_t build_bank(const double *K, const void *qbar, const float *qbar_s
     return nb;
 }
 
-int oracle_group_bank(const void *q, const float *q_scale, const void *k, const float *k_scale,
-                      const float *w, int dtype, int64_t Tq, int64_t Tk, int H, int d,
-                      int64_t q_pos0, const void *qbar, const float *qbar_scale, const float *wbar,
-                      int Hs, int G, int P, int topk, unsigned flags, const int64_t *rows,
-                      int64_t nrows, int32_t *out_idx, double *out_score, int32_t *out_bank,
-                      int64_t *pairs, int nthreads)
+/* Eq. (13)-(14) over keys already widened to fp64 (K [>= q_pos0+Tq, d]);
+ * q, qbar in `dtype` codes.  Rows and outputs as in oracle_group_bank. */
+static int group_bank_core(const double *K, const void *q, const float *q_scale, const float *w,
+                           int dtype, int64_t Tq, int H, int d, int64_t q_pos0, const void *qbar,
+                           const float *qbar_scale, const float *wbar, int Hs, int G, int P,
+                           int topk, unsigned flags, const int64_t *rows, int64_t nrows,
+                           int32_t *out_idx, double *out_score, int32_t *out_bank)
 {
-    if (q_pos0 < 0 || q_pos0 + Tq > Tk || topk <= 0 || H <= 0 || Hs <= 0 || d <= 0 || G <= 0 ||
-        P <= 0)
-        return -1;
-    set_threads(nthreads);
-    double *K = load_keys(k, k_scale, dtype, Tk, d);
-    if (!K) return -2;
     int64_t NG = (Tq + G - 1) / G;
     int64_t n_out = rows ? nrows : Tq;
 
@@ -362,10 +359,10 @@ int oracle_group_bank(const void *q, const float *q_scale, const void *k, const 
     char *need = calloc((size_t)(NG > 0 ? NG : 1), 1);
     int64_t **banks = calloc((size_t)(NG > 0 ? NG : 1), sizeof(int64_t *));
     int64_t *nbank = calloc((size_t)(NG > 0 ? NG : 1), sizeof(int64_t));
-    if (!need || !banks || !nbank) { free(K); free(need); free(banks); free(nbank); return -2; }
+    if (!need || !banks || !nbank) { free(need); free(banks); free(nbank); return -2; }
     for (int64_t r = 0; r < n_out; ++r) {
         int64_t i = rows ? rows[r] : r;
-        if (i < 0 || i >= Tq) { free(K); free(need); free(banks); free(nbank); return -1; }
+        if (i < 0 || i >= Tq) { free(need); free(banks); free(nbank); return -1; }
         need[i / G] = 1;
     }
 
@@ -409,10 +406,97 @@ int oracle_group_bank(const void *q, const float *q_scale, const void *k, const 
                     out_score ? out_score + r * topk : NULL);
         free(qrow); free(wrow); free(c);
     }
+    for (int64_t g = 0; g < NG; ++g) free(banks[g]);
+    free(banks); free(nbank); free(need);
+    return err;
+}
+
+int oracle_group_bank(const void *q, const float *q_scale, const void *k, const float *k_scale,
+                      const float *w, int dtype, int64_t Tq, int64_t Tk, int H, int d,
+                      int64_t q_pos0, const void *qbar, const float *qbar_scale, const float *wbar,
+                      int Hs, int G, int P, int topk, unsigned flags, const int64_t *rows,
+                      int64_t nrows, int32_t *out_idx, double *out_score, int32_t *out_bank,
+                      int64_t *pairs, int nthreads)
+{
+    if (q_pos0 < 0 || q_pos0 + Tq > Tk || topk <= 0 || H <= 0 || Hs <= 0 || d <= 0 || G <= 0 ||
+        P <= 0)
+        return -1;
+    set_threads(nthreads);
+    double *K = load_keys(k, k_scale, dtype, Tk, d);
+    if (!K) return -2;
+    int err = group_bank_core(K, q, q_scale, w, dtype, Tq, H, d, q_pos0, qbar, qbar_scale, wbar, Hs,
+                              G, P, topk, flags, rows, nrows, out_idx, out_score, out_bank);
     if (pairs)
         *pairs = oracle_group_bank_pairs(Tq, q_pos0, G, P, flags);
-    for (int64_t g = 0; g < NG; ++g) free(banks[g]);
-    free(banks); free(nbank); free(need); free(K);
+    free(K);
+    return err;
+}
+
+/* ------------------------------------------------ MTP target verification
+ * Section 4.3 (application to MTP) and Appendix A.2, Eq. (20)-(22).  Each of
+ * B sequences verifies a window of m query tokens: query r of sequence b sits
+ * at position N_b - 1 + r, so it sees N_b + r keys of that sequence's cache.
+ * Whether the window reuses banks is decided once, on N_b: N_b <= P sends all
+ * m queries to the original indexer; otherwise the window splits into m/G
+ * groups, the anchor of group g (query gG) builds a bank of the P best of its
+ * N_b + gG visible keys with the group query, and every member refines over
+ * the bank plus the keys after the anchor (Eq. 14).  Queries are bf16; the
+ * cache is E4M3 codes with one fp32 scale per token, as in decode. */
+int64_t oracle_mtp_pairs(const int32_t *prefix_lens, int B, int m, int G, int P)
+{
+    int64_t pairs = 0;
+    for (int b = 0; b < B; ++b)
+        pairs += oracle_group_bank_pairs(m, (int64_t)prefix_lens[b] - 1, G, P, ORACLE_WINDOW);
+    return pairs;
+}
+
+int oracle_mtp(const void *q, const uint8_t *k_cache, const float *k_scale, const float *w,
+               const void *qbar, const float *wbar, const int32_t *prefix_lens, int B,
+               int64_t Nmax, int m, int H, int Hs, int d, int G, int P, int topk,
+               const int64_t *rows, int64_t nrows, int32_t *out_idx, double *out_score,
+               int32_t *out_bank, int64_t *pairs, int nthreads)
+{
+    if (B < 0 || m <= 0 || G <= 0 || m % G || topk <= 0 || H <= 0 || Hs <= 0 || d <= 0 || P <= 0)
+        return -1;
+    for (int b = 0; b < B; ++b)
+        if (prefix_lens[b] < 1 || prefix_lens[b] + m - 1 > Nmax) return -1;
+    for (int64_t r = 1; rows && r < nrows; ++r)
+        if (rows[r] <= rows[r - 1]) return -1; /* rows ascending */
+    set_threads(nthreads);
+    const int NGs = m / G;
+    int err = 0;
+    int64_t r0 = 0; /* first entry of `rows` in sequence b */
+    for (int b = 0; b < B && !err; ++b) {
+        int64_t r1 = r0;
+        if (rows)
+            while (r1 < nrows && rows[r1] < (int64_t)(b + 1) * m) ++r1;
+        if (rows && r1 == r0 && !out_bank) continue; /* nothing requested here */
+        int64_t *lrows = NULL;
+        if (rows) {
+            lrows = malloc(sizeof(int64_t) * (size_t)(r1 > r0 ? r1 - r0 : 1));
+            if (!lrows) return -2;
+            for (int64_t r = r0; r < r1; ++r) lrows[r - r0] = rows[r] - (int64_t)b * m;
+        }
+        const int64_t Tk = prefix_lens[b] + m - 1; /* keys the window's last query sees */
+        double *K = malloc(sizeof(double) * (size_t)Tk * (size_t)d);
+        if (!K) { free(lrows); return -2; }
+        for (int64_t s = 0; s < Tk; ++s)
+            load_row(k_cache, k_scale, ORACLE_E4M3, (int64_t)b * Nmax + s, d, K + s * d);
+        const int64_t o = rows ? r0 : (int64_t)b * m; /* output row of this call's first row */
+        err = group_bank_core(K, (const uint16_t *)q + (size_t)b * m * H * d, NULL,
+                              w + (size_t)b * m * H, ORACLE_BF16, m, H, d,
+                              (int64_t)prefix_lens[b] - 1,
+                              qbar ? (const uint16_t *)qbar + (size_t)b * NGs * Hs * d : NULL,
+                              NULL, wbar ? wbar + (size_t)b * NGs * Hs : NULL, Hs, G, P, topk,
+                              ORACLE_WINDOW, lrows, rows ? r1 - r0 : 0,
+                              out_idx ? out_idx + o * topk : NULL,
+                              out_score ? out_score + o * topk : NULL,
+                              out_bank ? out_bank + (size_t)b * NGs * P : NULL);
+        free(K); free(lrows);
+        r0 = r1;
+    }
+    if (pairs)
+        *pairs = oracle_mtp_pairs(prefix_lens, B, m, G, P);
     return err;
 }
 

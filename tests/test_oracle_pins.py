@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from tests.bruteforce import lexsort_topk
-from workloads import make_decode, make_group_bank, make_prefill, to_bf16
+from workloads import make_decode, make_group_bank, make_mtp, make_prefill, to_bf16
 from workloads.gen import e4m3_quantize_rows
 
 GOLDEN = __file__.replace("test_oracle_pins.py", "golden/table5_speedups.txt")
@@ -468,3 +468,117 @@ def test_pooled_identical_group_recovers_dense(oracle_lib):
     # after it; the dense top-K of the anchor's query over s <= t is inside
     # bank U (t_anchor, t] because a top-P over s <= t_anchor holds its top-K
     assert np.array_equal(d_i, p_i) and np.array_equal(d_s, p_s)
+
+
+# ------------------------------------------------- MTP verification pins
+
+def _e4m3_values(codes, scale):
+    """E4M3 codes times their per-token scale, decoded by torch (fp64)."""
+    return codes.view(torch.float8_e4m3fn).double() * scale.double()[..., None]
+
+
+def _mtp_dense_ref(q, kv, w, N, m, K):
+    """Original indexer for a window's queries: query r sees keys 0..N-1+r."""
+    S = (w[:, :, None] * np.maximum(np.einsum("rhc,sc->rhs", q, kv), 0)).sum(1)
+    valid = np.arange(kv.shape[0])[None, :] <= (N - 1 + np.arange(m))[:, None]
+    return lexsort_topk(S, valid, K)
+
+
+def test_mtp_pairs_are_eq20_21(oracle_lib):
+    """The discrete count of an MTP round is Eq. (20)-(21): m N + m(m-1)/2 when
+    the window falls back (N <= P), else (m/G) N + m P + (m/2)(m/G + G - 2)."""
+    m, P = 16, 2048
+    for G in (4, 8, 16):
+        for N in (1, 700, P - 1, P, P + 1, 3 * P + 5, 131072):
+            want = m * N + m * (m - 1) // 2 if N <= P else (m // G) * N + m * P + (m // 2) * (m // G + G - 2)
+            assert oracle.mtp_pairs([N], m, G, P) == want, (G, N)
+    assert oracle.mtp_pairs([100, 5000], m, 4, P) == sum(oracle.mtp_pairs([n], m, 4, P) for n in (100, 5000))
+
+
+def test_mtp_eligible_window_is_the_group_bank(oracle_lib):
+    """N > P: every group of the window reuses a bank, exactly as prefill
+    grouping does for groups starting at query N-1 (anchor g sees N + gG keys)."""
+    m, G, P, K, N = 16, 4, 40, 12, 150
+    wl = make_mtp(B=1, N=N + m - 1, m=m, H=3, Hs=2, d=16, topk=K, G=G, P=P, dist="int", seed=30,
+                  prefix_lens=[N])
+    t = wl.tensors
+    mi, ms, mb, pairs = oracle.mtp(t["q"], t["k_cache"], t["k_scale"], t["w"], t["qbar"], t["wbar"],
+                                   t["prefix_lens"], G, P, K, want_bank=True)
+    kv = to_bf16(_e4m3_values(t["k_cache"][0], t["k_scale"][0]).float())  # exact: small integers
+    gi, gs, gb, gp = oracle.group_bank(t["q"][0], kv, t["w"][0], t["qbar"][0], t["wbar"][0], "bf16", N - 1, G, P,
+                                       K, want_bank=True)
+    assert np.array_equal(mi, gi) and np.array_equal(ms, gs)
+    assert np.array_equal(mb[0], gb) and (mb >= 0).all() and pairs == gp
+
+
+def test_mtp_window_falls_back_as_a_whole(oracle_lib):
+    """N <= P: the whole window uses the original indexer even though its later
+    anchors see more than P keys (prefill grouping would build their banks)."""
+    m, G, P, K, N = 16, 4, 40, 12, 33  # anchors see 33, 37, 41, 45 keys
+    wl = make_mtp(B=1, N=N + m - 1, m=m, H=3, Hs=2, d=16, topk=K, G=G, P=P, dist="int", seed=31,
+                  prefix_lens=[N])
+    t = wl.tensors
+    mi, ms, mb, pairs = oracle.mtp(t["q"], t["k_cache"], t["k_scale"], t["w"], t["qbar"], t["wbar"],
+                                   t["prefix_lens"], G, P, K, want_bank=True)
+    assert (mb == -1).all() and pairs == m * N + m * (m - 1) // 2
+    kv = _e4m3_values(t["k_cache"][0], t["k_scale"][0]).numpy()
+    ri, rs = _mtp_dense_ref(_f64(t["q"][0]), kv, _f64(t["w"][0]), N, m, K)
+    assert np.array_equal(mi, ri)
+    np.testing.assert_allclose(ms, rs, rtol=1e-12)
+    kvb = to_bf16(torch.from_numpy(kv).float())
+    _, _, gb, _ = oracle.group_bank(t["q"][0], kvb, t["w"][0], t["qbar"][0], t["wbar"][0], "bf16", N - 1, G, P, K,
+                                    want_bank=True)
+    assert (gb[2:] >= 0).any()  # the per-group rule would differ here
+
+
+def test_mtp_brute_force_batch(oracle_lib):
+    """A batch mixing fallback and bank windows against a direct restatement
+    of the rule in numpy (bank = top-P of the group score over the anchor's
+    visible keys; members rank bank plus post-anchor keys), scales included."""
+    B, m, G, P, K, H, Hs, d = 3, 16, 8, 24, 10, 3, 2, 8
+    lens = [20, 24, 25]
+    wl = make_mtp(B=B, N=60, m=m, H=H, Hs=Hs, d=d, topk=K, G=G, P=P, dist="normal", seed=32,
+                  prefix_lens=lens)
+    t = wl.tensors
+    mi, ms, mb, _ = oracle.mtp(t["q"], t["k_cache"], t["k_scale"], t["w"], t["qbar"], t["wbar"],
+                               t["prefix_lens"], G, P, K, want_bank=True)
+    for b, N in enumerate(lens):
+        kv = _e4m3_values(t["k_cache"][b], t["k_scale"][b]).numpy()
+        q, w = _f64(t["q"][b]), _f64(t["w"][b])
+        S = (w[:, :, None] * np.maximum(np.einsum("rhc,sc->rhs", q, kv), 0)).sum(1)
+        if N <= P:
+            ri, _ = _mtp_dense_ref(q, kv, w, N, m, K)
+            assert np.array_equal(mi[b * m:(b + 1) * m], ri) and (mb[b] == -1).all()
+            continue
+        qb, wb = _f64(t["qbar"][b]), _f64(t["wbar"][b])
+        Sb = (wb[:, :, None] * np.maximum(np.einsum("ghc,sc->ghs", qb, kv), 0)).sum(1)
+        for g in range(m // G):
+            a = N - 1 + g * G
+            bank, _ = lexsort_topk(Sb[g:g + 1, :a + 1], np.ones((1, a + 1), bool), P)
+            assert np.array_equal(mb[b, g], bank[0])
+            for i in range(G):
+                r = g * G + i
+                cand = np.concatenate([bank[0], np.arange(a + 1, a + 1 + i)])
+                ci, _ = lexsort_topk(S[r:r + 1, cand], np.ones((1, len(cand)), bool), K)
+                assert np.array_equal(mi[b * m + r], np.sort(cand[ci[0]])), (b, r)
+
+
+def test_mtp_rows_and_pooling(oracle_lib):
+    """Requested rows (any order) equal the full result's rows; mean pooling
+    equals passing the pooled query explicitly."""
+    B, m, G, P, K = 2, 16, 4, 30, 8
+    wl = make_mtp(B=B, N=90, m=m, H=4, Hs=4, d=16, topk=K, G=G, P=P, dist="int", seed=33, prefix_lens=[70, 31])
+    t = wl.tensors
+    fi, fs, fb, _ = oracle.mtp(t["q"], t["k_cache"], t["k_scale"], t["w"], t["qbar"], t["wbar"],
+                               t["prefix_lens"], G, P, K, want_bank=True)
+    rows = [17, 3, 30, 0, 31]
+    ri, rs, _, _ = oracle.mtp(t["q"], t["k_cache"], t["k_scale"], t["w"], t["qbar"], t["wbar"],
+                              t["prefix_lens"], G, P, K, rows=rows)
+    assert np.array_equal(ri, fi[rows]) and np.array_equal(rs, fs[rows])
+    pq = np.stack([oracle.pool_mean_bf16(t["q"][b], t["w"][b], G)[0] for b in range(B)])
+    pw = np.stack([oracle.pool_mean_bf16(t["q"][b], t["w"][b], G)[1] for b in range(B)])
+    ei, _, eb, _ = oracle.mtp(t["q"], t["k_cache"], t["k_scale"], t["w"], pq, pw, t["prefix_lens"], G, P, K,
+                              want_bank=True)
+    pi, _, pb, _ = oracle.mtp(t["q"], t["k_cache"], t["k_scale"], t["w"], None, None, t["prefix_lens"], G, P, K,
+                              flags=oracle.POOL_MEAN, want_bank=True)
+    assert np.array_equal(ei, pi) and np.array_equal(eb, pb) and not np.array_equal(eb, fb)

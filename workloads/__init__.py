@@ -11,6 +11,7 @@ from .gen import (  # noqa: F401
     e4m3_quantize_rows,
     make_decode,
     make_group_bank,
+    make_mtp,
     make_prefill,
     make_workload,
     to_bf16,

@@ -195,6 +195,34 @@ def make_group_bank(T, H, Hs, d, topk, G, P, dtype="bf16", dist="normal", seed=0
     return wl
 
 
+def make_mtp(B, N, m, H, Hs, d, topk, G, P, dist="normal", seed=0, device="cpu", prefix_lens=None,
+             w_lo=-3, w_hi=3, **_):
+    """MTP verification inputs: the decode cache (E4M3 [B,N,d] + scale [B,N]),
+    m bf16 queries per sequence q [B,m,H,d], w [B,m,H], the group indexer's
+    q-bar [B,m/G,Hs,d] bf16 and w-bar [B,m/G,Hs] (drawn as in the group bank
+    inputs), and prefix_lens [B] int32: the keys the window's first query sees
+    (default N - m + 1, so the last query sees the whole cache)."""
+    wl = make_decode(B * m, 1, H, d, topk, dist, seed, device, w_lo=w_lo, w_hi=w_hi)  # queries and gates
+    kv = make_decode(B, N, 1, d, topk, dist, seed + 1, device)                        # the caches
+    g = _gen(seed + 0x9E3779B1, device)
+    NGs = m // G
+    if dist == "int":
+        qbar = to_bf16(_ints(g, (B, NGs, Hs, d), -3, 3, device)).contiguous()
+        wbar = _ints(g, (B, NGs, Hs), w_lo, w_hi, device)
+    else:
+        qbar = to_bf16(_normal(g, (B, NGs, Hs, d), device)).contiguous()
+        wbar = torch.sigmoid(_normal(g, (B, NGs, Hs), device))
+    if prefix_lens is None:
+        prefix_lens = torch.full((B,), N - m + 1, dtype=torch.int32, device=device)
+    else:
+        prefix_lens = torch.as_tensor(prefix_lens, dtype=torch.int32, device=device)
+    t = dict(q=wl["q"].reshape(B, m, H, d).contiguous(), w=wl["w"].reshape(B, m, H).contiguous(),
+             k_cache=kv["k_cache"], k_scale=kv["k_scale"], qbar=qbar, wbar=wbar.contiguous(),
+             prefix_lens=prefix_lens)
+    return Workload("mtp", "fp8", dict(B=B, N=N, m=m, H=H, Hs=Hs, d=d, topk=topk, G=G, P=P, dist=dist,
+                                       seed=seed), t)
+
+
 def make_workload(config: int, seed: int = 0, device="cpu", dist=None, **override):
     """The workload of one of the five configurations (optionally resized)."""
     p = dict(CONFIGS[config])
