@@ -138,6 +138,45 @@ size_t indexer_group_bank_workspace_size(int64_t Tq, int64_t Tk, int H, int Hs, 
  * |P_t| + (i - t) candidates.  Host only; -1 on bad arguments. */
 int64_t indexer_group_bank_pairs(int64_t Tq, int64_t q_pos0, int G, int P, unsigned flags);
 
+/*
+ * MTP target verification with bank sharing: Section 4.3 ("Application to
+ * Prefill and MTP") and Appendix A.2, Eq. (20)-(22).  Each of B sequences
+ * verifies a window of m draft queries.  Query r of sequence b sits at
+ * position N_b - 1 + r, so it sees keys 0 .. N_b - 1 + r of its cache, where
+ * N_b = prefix_lens[b].  A window reuses banks only when N_b > P (decided once
+ * per window): it splits into m/G groups; group g's anchor (query gG) ranks its
+ * N_b + gG visible keys with the group indexer and keeps the best P (the
+ * bank, Eq. (8), (13)); member i ranks the bank plus the i keys after the
+ * anchor with its own query (Eq. (14)).  A window with N_b <= P uses the
+ * original indexer for all m queries.  The arithmetic is that of
+ * indexer_decode (bf16 queries against the E4M3 cache).
+ *   q           [B, m, H, d] bf16;  w [B, m, H] fp32
+ *   k_cache     [B, Nmax, d] E4M3 codes;  k_scale [B, Nmax] fp32
+ *   qbar, wbar  [B, m/G, Hs, d] bf16 and [B, m/G, Hs] fp32: the group
+ *               indexer's query and gates; NULL with DSAIDX_POOL_MEAN (then
+ *               each group's mean query and gates are used, Hs == H)
+ *   prefix_lens [B] int32, device: N_b, clamped on the device to [1, Nmax-m+1]
+ *               (the cache must hold the window's own keys)
+ *   flags       DSAIDX_POOL_MEAN or 0
+ *   out_idx     [B, m, topk] int32 (ascending token indices, then -1);
+ *   out_score   [B, m, topk] fp32 or NULL
+ *   out_bank    [B, m/G, P] int32 or NULL: the banks (ascending; rows of
+ *               windows that fall back are all -1)
+ * G in {4, 8, 16}, m a multiple of G and at most 64, B*m <= 65535,
+ * topk <= P <= 16384, d in {64, 128}, H and Hs <= 64.
+ */
+int indexer_mtp(const void *q, const uint8_t *k_cache, const float *k_scale, const float *w,
+                const void *qbar, const float *wbar, const int32_t *prefix_lens, int B,
+                int64_t Nmax, int m, int H, int Hs, int d, int G, int P, int topk, unsigned flags,
+                int32_t *out_idx, int32_t *out_bank, float *out_score, void *ws, size_t ws_bytes,
+                void *stream);
+/* Workspace bytes for any prefix lengths (sized for the longest rows). */
+size_t indexer_mtp_workspace_size(int B, int64_t Nmax, int m, int H, int Hs, int d, int G, int P,
+                                  int topk, unsigned flags);
+/* Query-key scores indexer_mtp evaluates for these (host) prefix lengths:
+ * Eq. (21) summed over the windows.  -1 on bad arguments. */
+int64_t indexer_mtp_pairs(const int32_t *prefix_lens, int B, int64_t Nmax, int m, int G, int P);
+
 /* Message describing the calling thread's last non-OK return ("" if none). */
 const char *indexer_last_error(void);
 

@@ -10,6 +10,7 @@ without the built library, or with host tensors, raises.
     idx, score, bank = indexer_group_bank(q, k, w, qbar, wbar, q_pos0, G, P, topk, ...)
     idx, score, bank = indexer_group_bank(q, k, w, None, None, q_pos0, G, P, topk,
                                           flags=POOL_MEAN)   # training-free group query
+    idx, score, bank = indexer_mtp(q, k_cache, k_scale, w, qbar, wbar, prefix_lens, G, P, topk)
 
 Tensors (contiguous, on the GPU): q [Tq,H,d] bf16 or uint8 E4M3 codes,
 k [Tk,d] the same dtype, w [Tq,H] fp32, per-token fp32 scales for E4M3.
@@ -22,7 +23,8 @@ from ._lib import (DSAIDX_BF16, DSAIDX_FORCE_BANK, DSAIDX_FP8_E4M3, DSAIDX_OK,  
                    DSAIDX_POOL_MEAN, LIB_PATH, last_error, lib)
 
 __all__ = ["indexer_prefill", "indexer_decode", "indexer_group_bank", "indexer_group_bank_pairs",
-           "workspace_prefill", "workspace_decode", "workspace_group_bank", "FORCE_BANK", "POOL_MEAN", "lib",
+           "workspace_prefill", "workspace_decode", "workspace_group_bank", "indexer_mtp", "indexer_mtp_pairs",
+           "workspace_mtp", "FORCE_BANK", "POOL_MEAN", "lib",
            "LIB_PATH"]
 
 FORCE_BANK = DSAIDX_FORCE_BANK
@@ -151,4 +153,44 @@ def indexer_group_bank(q, k, w, qbar, wbar, q_pos0, G, P, topk=2048, q_scale=Non
                                   _ptr(out_idx), _ptr(out_bank), _ptr(out_score), _ptr(ws),
                                   0 if ws is None else ws.numel(), _stream(dev))
     _check(rc, "indexer_group_bank")
+    return out_idx, out_score, out_bank
+
+
+def workspace_mtp(B, Nmax, m, H, Hs, d, G, P, topk, flags=0):
+    return lib().indexer_mtp_workspace_size(B, Nmax, m, H, Hs, d, G, P, topk, flags)
+
+
+def indexer_mtp_pairs(prefix_lens, Nmax, m, G, P):
+    """Scores the MTP call evaluates for these prefix lengths (host ints)."""
+    import ctypes
+    import numpy as np
+    lens = np.ascontiguousarray(np.asarray(prefix_lens, dtype=np.int32))
+    return lib().indexer_mtp_pairs(lens.ctypes.data_as(ctypes.c_void_p), len(lens), Nmax, m, G, P)
+
+
+def indexer_mtp(q, k_cache, k_scale, w, qbar, wbar, prefix_lens, G, P, topk=2048, flags=0, want_score=True,
+                want_bank=False, out_idx=None, out_score=None, out_bank=None, ws=None):
+    """MTP target verification with bank sharing (Section 4.3; Appendix A.2).
+
+    q [B,m,H,d] bf16, k_cache [B,Nmax,d] uint8 E4M3, k_scale [B,Nmax] fp32,
+    w [B,m,H], qbar [B,m/G,Hs,d] bf16 and wbar [B,m/G,Hs] (None with
+    POOL_MEAN), prefix_lens [B] int32 on the GPU.  Returns (idx [B,m,topk],
+    score or None, bank [B,m/G,P] or None)."""
+    dev = _dev(q, k_cache, k_scale, w, qbar, wbar, prefix_lens, out_idx, out_score, out_bank, ws)
+    B, m, H, d = q.shape
+    Nmax = k_cache.shape[1]
+    Hs = H if qbar is None else qbar.shape[2]
+    if q.dtype != torch.bfloat16 or k_cache.dtype != torch.uint8 or prefix_lens.dtype != torch.int32:
+        raise ValueError("MTP takes bf16 q, uint8 E4M3 k_cache and int32 prefix_lens")
+    if out_idx is None:
+        out_idx = torch.empty((B, m, topk), dtype=torch.int32, device=dev)
+    if want_score and out_score is None:
+        out_score = torch.empty((B, m, topk), dtype=torch.float32, device=dev)
+    if want_bank and out_bank is None:
+        out_bank = torch.empty((B, m // G, P), dtype=torch.int32, device=dev)
+    ws = _ws(workspace_mtp(B, Nmax, m, H, Hs, d, G, P, topk, flags), dev, ws)
+    rc = lib().indexer_mtp(_ptr(q), _ptr(k_cache), _ptr(k_scale), _ptr(w), _ptr(qbar), _ptr(wbar), _ptr(prefix_lens),
+                           B, Nmax, m, H, Hs, d, G, P, topk, flags, _ptr(out_idx), _ptr(out_bank), _ptr(out_score),
+                           _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
+    _check(rc, "indexer_mtp")
     return out_idx, out_score, out_bank

@@ -28,6 +28,10 @@ SIGNATURES = {
                                 _I, _U, _P, _P, _P, _P, _SZ, _P]),
     "indexer_group_bank_workspace_size": (_SZ, [_I64, _I64, _I, _I, _I, _I, _I, _I, _I, _U]),
     "indexer_group_bank_pairs": (_I64, [_I64, _I64, _I, _I, _U]),
+    "indexer_mtp": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I64, _I, _I, _I, _I, _I, _I, _I, _U, _P, _P, _P, _P,
+                         _SZ, _P]),
+    "indexer_mtp_workspace_size": (_SZ, [_I, _I64, _I, _I, _I, _I, _I, _I, _I, _U]),
+    "indexer_mtp_pairs": (_I64, [_P, _I, _I64, _I, _I, _I]),
     "indexer_last_error": (ctypes.c_char_p, []),
 }
 

@@ -249,6 +249,39 @@ static DecodeWs decode_ws(int B, int64_t Nmax) {
   return w;
 }
 
+// The decode pipeline's arguments over `rows` rows of at most Nmax keys, its
+// workspace at ws (decode_ws(rows, Nmax).total bytes).
+static DecodeArgs decode_args(const void* q, const float* w, const int32_t* lens, int rows,
+                              int64_t Nmax, int H, int d, int K, void* ws, int32_t* out_idx,
+                              float* out_score) {
+  DecodeArgs a{};
+  a.q = q;
+  a.w = w;
+  a.seq_lens = lens;
+  a.B = rows;
+  a.H = H;
+  a.d = d;
+  a.Nmax = Nmax;
+  a.K = K;
+  const DecodeWs lay = decode_ws(rows, Nmax);
+  uint8_t* base = (uint8_t*)ws;
+  a.kpb = decode_keys_per_block(rows, Nmax);
+  a.nblk = (int)((Nmax + a.kpb - 1) / a.kpb);
+  a.hist = (uint32_t*)(base + lay.hist);
+  a.cand_cnt = (int32_t*)(a.hist + (size_t)rows * kDecHistBins);
+  a.rowsel = (uint32_t*)(base + lay.rowsel);
+  a.cand_key = (uint32_t*)(base + lay.ckey);
+  a.cand_idx = (int32_t*)(base + lay.cidx);
+  a.span_above = (int32_t*)(base + lay.above);
+  a.span_off = (int32_t*)(base + lay.off);
+  a.cl_cnt = (int32_t*)(base + lay.clcnt);
+  a.cl_idx = (int32_t*)(base + lay.clidx);
+  a.cl_sc = (float*)(base + lay.clsc);
+  a.out_idx = out_idx;
+  a.out_score = out_score;
+  return a;
+}
+
 size_t indexer_decode_workspace_size(int B, int64_t Nmax, int H, int d, int topk) {
   (void)H; (void)d; (void)topk;
   if (B <= 0 || Nmax <= 0) return 0;
@@ -273,33 +306,9 @@ int indexer_decode(const void* q, const uint8_t* k_cache, const float* k_scale, 
   rc = check_ws(ws, ws_bytes, indexer_decode_workspace_size(B, Nmax, H, d, topk));
   if (rc) return rc;
   if (B == 0) return ok();
-  DecodeArgs a{};
-  a.q = q;
+  DecodeArgs a = decode_args(q, w, seq_lens, B, Nmax, H, d, topk, ws, out_idx, out_score);
   a.kc = k_cache;
   a.k_scale = k_scale;
-  a.w = w;
-  a.seq_lens = seq_lens;
-  a.B = B;
-  a.H = H;
-  a.d = d;
-  a.Nmax = Nmax;
-  a.K = topk;
-  const DecodeWs lay = decode_ws(B, Nmax);
-  uint8_t* base = (uint8_t*)ws;
-  a.kpb = decode_keys_per_block(B, Nmax);
-  a.nblk = (int)((Nmax + a.kpb - 1) / a.kpb);
-  a.hist = (uint32_t*)(base + lay.hist);
-  a.cand_cnt = (int32_t*)(a.hist + (size_t)B * kDecHistBins);
-  a.rowsel = (uint32_t*)(base + lay.rowsel);
-  a.cand_key = (uint32_t*)(base + lay.ckey);
-  a.cand_idx = (int32_t*)(base + lay.cidx);
-  a.span_above = (int32_t*)(base + lay.above);
-  a.span_off = (int32_t*)(base + lay.off);
-  a.cl_cnt = (int32_t*)(base + lay.clcnt);
-  a.cl_idx = (int32_t*)(base + lay.clidx);
-  a.cl_sc = (float*)(base + lay.clsc);
-  a.out_idx = out_idx;
-  a.out_score = out_score;
   hipError_t e = launch_decode(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "indexer_decode launch");
   return ok();
@@ -480,6 +489,179 @@ int indexer_group_bank(const void* q, const float* q_scale, const void* k, const
     e = launch_scan_topk(a, dtype, st);
     if (e != hipSuccess) return hip_fail(e, "indexer_group_bank refine launch");
   }
+  return ok();
+}
+
+// ---------------------------------------------------------------- MTP
+
+// workspace: anchor rows' key sources and lengths | refinement rows' | banks
+// (when out_bank is NULL) | pooled group queries and gates (DSAIDX_POOL_MEAN) |
+// gathered candidate keys and scales | the decode pipeline's workspace (the
+// anchor scan and the refinement run one after the other and share it)
+struct MtpWs {
+  size_t a_kc, a_ks, a_len, r_kc, r_ks, r_len, bank, pq, pw, gk, gs, dec, total;
+};
+
+static MtpWs mtp_ws(int B, int64_t Nmax, int m, int H, int d, int G, int P, unsigned flags,
+                    bool bank_in_ws) {
+  const size_t na = (size_t)B * (m / G), nr = (size_t)B * m, cand = (size_t)P + G - 1;
+  MtpWs w{};
+  w.a_kc = 0;
+  w.a_ks = w.a_kc + align_up(na * 8u);
+  w.a_len = w.a_ks + align_up(na * 8u);
+  w.r_kc = w.a_len + align_up(na * 4u);
+  w.r_ks = w.r_kc + align_up(nr * 8u);
+  w.r_len = w.r_ks + align_up(nr * 8u);
+  w.bank = w.r_len + align_up(nr * 4u);
+  w.pq = w.bank + (bank_in_ws ? align_up(na * P * 4u) : 0);
+  const bool pool = (flags & DSAIDX_POOL_MEAN) != 0;
+  w.pw = w.pq + (pool ? align_up(na * H * d * 2u) : 0);
+  w.gk = w.pw + (pool ? align_up(na * H * 4u) : 0);
+  w.gs = w.gk + align_up(na * cand * d);
+  w.dec = w.gs + align_up(na * cand * 4u);
+  const int64_t nmax_r = Nmax > (int64_t)cand ? Nmax : (int64_t)cand;
+  const size_t da = decode_ws((int)na, Nmax).total, dr = decode_ws((int)nr, nmax_r).total;
+  w.total = w.dec + (da > dr ? da : dr);
+  return w;
+}
+
+size_t indexer_mtp_workspace_size(int B, int64_t Nmax, int m, int H, int Hs, int d, int G, int P,
+                                  int topk, unsigned flags) {
+  (void)Hs; (void)topk;
+  if (B <= 0 || Nmax <= 0 || m <= 0 || G <= 0 || m % G || P <= 0 || H <= 0 || d <= 0) return 0;
+  return mtp_ws(B, Nmax, m, H, d, G, P, flags, true).total;
+}
+
+int64_t indexer_mtp_pairs(const int32_t* prefix_lens, int B, int64_t Nmax, int m, int G, int P) {
+  if (B < 0 || m <= 0 || G <= 0 || m % G || P <= 0 || Nmax < m || (B > 0 && !prefix_lens))
+    return -1;
+  int64_t pairs = 0;
+  for (int b = 0; b < B; ++b) {
+    int64_t N = prefix_lens[b];
+    N = N < 1 ? 1 : (N > Nmax - m + 1 ? Nmax - m + 1 : N);  // as the device clamps it
+    if (N <= P) {
+      pairs += m * N + (int64_t)m * (m - 1) / 2;  // every query: N + r keys
+      continue;
+    }
+    for (int g = 0; g < m / G; ++g)
+      pairs += N + (int64_t)g * G + (int64_t)G * P + (int64_t)G * (G - 1) / 2;
+  }
+  return pairs;
+}
+
+int indexer_mtp(const void* q, const uint8_t* k_cache, const float* k_scale, const float* w,
+                const void* qbar, const float* wbar, const int32_t* prefix_lens, int B,
+                int64_t Nmax, int m, int H, int Hs, int d, int G, int P, int topk, unsigned flags,
+                int32_t* out_idx, int32_t* out_bank, float* out_score, void* ws, size_t ws_bytes,
+                void* stream) {
+  int rc = check_shape(DSAIDX_FP8_E4M3, H, d, topk);
+  if (rc) return rc;
+  if (B < 0 || Nmax < 0 || m < 1)
+    return fail(DSAIDX_ERR_INVALID_ARG, "bad size (B=%d Nmax=%lld m=%d)", B, (long long)Nmax, m);
+  if (G != 4 && G != 8 && G != 16)
+    return fail(DSAIDX_ERR_UNSUPPORTED, "group size G = %d not in {4, 8, 16}", G);
+  if (m % G) return fail(DSAIDX_ERR_INVALID_ARG, "window m = %d is not a multiple of G = %d", m, G);
+  if (m > 64) return fail(DSAIDX_ERR_UNSUPPORTED, "window m = %d above 64", m);
+  if (Nmax < m) return fail(DSAIDX_ERR_INVALID_ARG, "Nmax = %lld below the window m", (long long)Nmax);
+  if (Nmax > INT32_MAX) return fail(DSAIDX_ERR_UNSUPPORTED, "Nmax above INT32_MAX");
+  if ((int64_t)B * m > 65535) return fail(DSAIDX_ERR_UNSUPPORTED, "B * m above 65535");
+  if (P < topk) return fail(DSAIDX_ERR_INVALID_ARG, "bank size P = %d below topk = %d", P, topk);
+  if (P > kMaxBank) return fail(DSAIDX_ERR_UNSUPPORTED, "bank size P = %d above %d", P, kMaxBank);
+  if (flags & ~(unsigned)DSAIDX_POOL_MEAN)
+    return fail(DSAIDX_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  const bool pool = (flags & DSAIDX_POOL_MEAN) != 0;
+  if (pool && (qbar || wbar))
+    return fail(DSAIDX_ERR_INVALID_ARG, "DSAIDX_POOL_MEAN takes NULL qbar and wbar");
+  if (pool && Hs != H) return fail(DSAIDX_ERR_INVALID_ARG, "DSAIDX_POOL_MEAN needs Hs == H");
+  if (Hs < 1) return fail(DSAIDX_ERR_INVALID_ARG, "Hs = %d must be positive", Hs);
+  if (Hs > kMaxHeads) return fail(DSAIDX_ERR_UNSUPPORTED, "Hs = %d above %d", Hs, kMaxHeads);
+  if (B > 0 && (!q || !k_cache || !k_scale || !w || !prefix_lens || !out_idx ||
+                (!pool && (!qbar || !wbar))))
+    return fail(DSAIDX_ERR_INVALID_ARG, "null q, k_cache, k_scale, w, qbar, wbar, prefix_lens or out_idx");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(w) || !aligned16(qbar) || !aligned16(wbar) ||
+      !aligned16(out_idx) || !aligned16(out_score) || !aligned16(out_bank))
+    return fail(DSAIDX_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  if (((uintptr_t)k_scale & 3u) || ((uintptr_t)prefix_lens & 3u))
+    return fail(DSAIDX_ERR_INVALID_ARG, "k_scale and prefix_lens must be 4-byte aligned");
+  const MtpWs lay = mtp_ws(B, Nmax, m, H, d, G, P, flags, out_bank == nullptr);
+  rc = check_ws(ws, ws_bytes, lay.total);
+  if (rc) return rc;
+  if (B == 0) return ok();
+
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* base = (uint8_t*)ws;
+  const int NGs = m / G;
+  const int na = B * NGs, nr = B * m;
+  MtpArgs t{};
+  t.kc = k_cache;
+  t.ks = k_scale;
+  t.prefix = prefix_lens;
+  t.B = B;
+  t.m = m;
+  t.G = G;
+  t.P = P;
+  t.d = d;
+  t.Nmax = Nmax;
+  t.a_kc = (const uint8_t**)(base + lay.a_kc);
+  t.a_ks = (const float**)(base + lay.a_ks);
+  t.a_len = (int32_t*)(base + lay.a_len);
+  t.r_kc = (const uint8_t**)(base + lay.r_kc);
+  t.r_ks = (const float**)(base + lay.r_ks);
+  t.r_len = (int32_t*)(base + lay.r_len);
+  int32_t* bank = out_bank ? out_bank : (int32_t*)(base + lay.bank);
+  t.bank = bank;
+  t.gk = base + lay.gk;
+  t.gs = (float*)(base + lay.gs);
+  t.out_idx = out_idx;
+  t.topk = topk;
+  hipError_t e = launch_mtp_plan(t, st);
+  if (e != hipSuccess) return hip_fail(e, "indexer_mtp plan launch");
+
+  // the group query of every group (windows that fall back never read it)
+  const void* gq = qbar;
+  const float* gw = wbar;
+  if (pool) {
+    PoolArgs pa{};
+    pa.q = q;
+    pa.w = w;
+    pa.H = H;
+    pa.d = d;
+    pa.G = G;
+    pa.g0 = 0;
+    pa.ngroups = na;
+    pa.qbar = base + lay.pq;
+    pa.wbar = (float*)(base + lay.pw);
+    gq = pa.qbar;
+    gw = pa.wbar;
+    e = launch_pool_mean(pa, st);
+    if (e != hipSuccess) return hip_fail(e, "indexer_mtp pooling launch");
+  }
+
+  // 1. anchor scan: row (b, g) ranks its anchor's N + gG visible keys with
+  //    the group indexer and keeps the best P, ascending (Eq. (8), (13));
+  //    rows of windows that fall back have no keys and come out all -1
+  DecodeArgs aa = decode_args(gq, gw, t.a_len, na, Nmax, Hs, d, P, base + lay.dec, bank, nullptr);
+  aa.row_kc = t.a_kc;
+  aa.row_ks = t.a_ks;
+  e = launch_decode(aa, st);
+  if (e != hipSuccess) return hip_fail(e, "indexer_mtp anchor scan launch");
+
+  // 2. each bank group's candidates, bank then post-anchor keys, side by side
+  e = launch_mtp_gather(t, st);
+  if (e != hipSuccess) return hip_fail(e, "indexer_mtp gather launch");
+
+  // 3. refinement (Eq. (14)), or the original indexer for fallback windows
+  const int64_t cand = (int64_t)P + G - 1;
+  const int64_t nmax_r = Nmax > cand ? Nmax : cand;
+  DecodeArgs ar = decode_args(q, w, t.r_len, nr, nmax_r, H, d, topk, base + lay.dec, out_idx, out_score);
+  ar.row_kc = t.r_kc;
+  ar.row_ks = t.r_ks;
+  e = launch_decode(ar, st);
+  if (e != hipSuccess) return hip_fail(e, "indexer_mtp refine launch");
+
+  // 4. bank rows: gathered positions -> token indices
+  e = launch_mtp_map(t, st);
+  if (e != hipSuccess) return hip_fail(e, "indexer_mtp map launch");
   return ok();
 }
 

@@ -146,10 +146,12 @@ __global__ void __launch_bounds__(kDecThreads, 2) decode_scan_kernel(const Decod
   // loop issues no global stores at all.
   const int64_t blk_end = n < blk0 + args.kpb ? n : blk0 + args.kpb;
   const int span = (int)(blk_end - blk0);
+  const uint8_t* kc_row = args.row_kc ? args.row_kc[b] : args.kc + (int64_t)b * args.Nmax * D;
+  const float* ks_row = args.row_ks ? args.row_ks[b] : args.k_scale + (int64_t)b * args.Nmax;
   const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(args.kc + ((int64_t)b * args.Nmax + blk0) * D), (short)0, span * D, kBufferWord3);
+      (void*)(kc_row + blk0 * D), (short)0, span * D, kBufferWord3);
   const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(args.k_scale + (int64_t)b * args.Nmax + blk0), (short)0, span * 4, kBufferWord3);
+      (void*)(ks_row + blk0), (short)0, span * 4, kBufferWord3);
 
   // tile i of this wave covers span keys (i*kDecWaves + wave)*32 + [0, 32)
   auto key_of = [&](int i) __attribute__((always_inline)) { return (i * kDecWaves + wave) * 32 + col; };

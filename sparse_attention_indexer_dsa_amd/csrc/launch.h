@@ -53,6 +53,10 @@ struct DecodeArgs {
   const float* k_scale;   // [B, Nmax]
   const float* w;         // [B, H]
   const int32_t* seq_lens;  // [B]
+  // optional per-row key sources (row b reads row_kc[b] [.., d] and
+  // row_ks[b]); when null, row b reads kc + b*Nmax*d and k_scale + b*Nmax
+  const uint8_t* const* row_kc;
+  const float* const* row_ks;
   int B, H, d;
   int64_t Nmax;
   int K;
@@ -90,6 +94,28 @@ struct PoolArgs {
   float* wbar;
 };
 hipError_t launch_pool_mean(const PoolArgs& a, hipStream_t stream);
+
+// MTP verification windows (B sequences, m queries each, groups of G, bank P):
+// per-row key sources and lengths for the anchor scan (rows b*NGs + g) and the
+// refinement (rows b*m + r), the gathered candidate keys of every bank group,
+// and the map from refinement positions back to token indices.
+struct MtpArgs {
+  const uint8_t* kc;       // [B, Nmax, d] E4M3
+  const float* ks;         // [B, Nmax]
+  const int32_t* prefix;   // [B] keys the window's first query sees (clamped to [1, Nmax-m+1])
+  int B, m, G, P, d;
+  int64_t Nmax;
+  const uint8_t** a_kc;  const float** a_ks;  int32_t* a_len;   // [B*m/G]
+  const uint8_t** r_kc;  const float** r_ks;  int32_t* r_len;   // [B*m]
+  const int32_t* bank;     // [B*m/G, P] ascending (anchor scan output)
+  uint8_t* gk;             // [B*m/G, P+G-1, d] gathered keys
+  float* gs;               // [B*m/G, P+G-1] their scales
+  int32_t* out_idx;        // [B*m, topk] refinement output, mapped in place
+  int topk;
+};
+hipError_t launch_mtp_plan(const MtpArgs& a, hipStream_t stream);
+hipError_t launch_mtp_gather(const MtpArgs& a, hipStream_t stream);
+hipError_t launch_mtp_map(const MtpArgs& a, hipStream_t stream);
 
 // Fill n int32 values with v (a kernel, not a memset node).
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t stream);

@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import oracle
@@ -34,7 +35,7 @@ A = P(1 << 20)  # 16-byte aligned
 def test_header_symbols_exported(L):
     names = re.findall(r"^\s*(?:[\w\s\*]+?)\b(indexer_\w+)\s*\(", open(HEADER).read(), re.M)
     names = sorted(set(names))
-    assert len(names) == 8, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -136,3 +137,34 @@ def test_binding_refuses_host_tensors():
     q = torch.zeros((4, 4, 32), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         dsa.indexer_prefill(q, torch.zeros((4, 32), dtype=torch.bfloat16), torch.zeros((4, 4)), 0, 2)
+
+
+def _mtp(L, **kw):
+    a = dict(q=A, kc=A, ks=A, w=A, qbar=A, wbar=A, lens=A, B=4, N=1024, m=16, H=64, Hs=16, d=128, G=4, P=256,
+             topk=64, flags=0, out=A, bank=None, sc=None, ws=A, ws_bytes=1 << 40)
+    a.update(kw)
+    return L.indexer_mtp(a["q"], a["kc"], a["ks"], a["w"], a["qbar"], a["wbar"], a["lens"], a["B"], a["N"], a["m"],
+                         a["H"], a["Hs"], a["d"], a["G"], a["P"], a["topk"], a["flags"], a["out"], a["bank"], a["sc"],
+                         a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(G=5), UNSUPPORTED), (dict(m=12, G=8), INVALID), (dict(m=128), UNSUPPORTED), (dict(N=8), INVALID),
+    (dict(P=32), INVALID), (dict(P=20000), UNSUPPORTED), (dict(flags=1), INVALID), (dict(flags=2), INVALID),
+    (dict(flags=2, qbar=None, wbar=None), INVALID), (dict(qbar=None), INVALID), (dict(lens=None), INVALID),
+    (dict(d=32), UNSUPPORTED), (dict(Hs=0), INVALID), (dict(Hs=80), UNSUPPORTED), (dict(B=5000), UNSUPPORTED),
+    (dict(ks=P((1 << 20) + 2)), INVALID), (dict(ws_bytes=10), WORKSPACE), (dict(topk=4096), UNSUPPORTED),
+])
+def test_mtp_rejects(L, kw, code):
+    assert _mtp(L, **kw) == code
+
+
+def test_mtp_pairs_match_oracle(L):
+    lens = np.array([1, 100, 2048, 2049, 70000, 131057], np.int32)
+    for G in (4, 8, 16):
+        got = L.indexer_mtp_pairs(lens.ctypes.data_as(ctypes.c_void_p), len(lens), 131072, 16, G, 2048)
+        assert got == oracle.mtp_pairs(lens, 16, G, 2048)
+    # out-of-range prefix lengths count as clamped
+    bad = np.array([0, 200000], np.int32)
+    got = L.indexer_mtp_pairs(bad.ctypes.data_as(ctypes.c_void_p), 2, 131072, 16, 4, 2048)
+    assert got == oracle.mtp_pairs([1, 131057], 16, 4, 2048)

@@ -7,7 +7,7 @@ import torch
 
 import oracle
 from tests.parity import compare
-from workloads import make_decode, make_group_bank, make_prefill
+from workloads import make_decode, make_group_bank, make_mtp, make_prefill
 
 pytestmark = pytest.mark.gpu
 
@@ -367,3 +367,101 @@ def test_group_bank_random(dsa):
     wl = make_group_bank(T=2000, H=64, Hs=64, d=128, topk=256, G=16, P=1024, dtype="bf16", dist="normal",
                          seed=19)
     _group_check(dsa, wl, rows=_rows(2000, 48, 19))
+
+
+# ------------------------------------------------------- MTP verification
+
+def _mtp_check(dsa, wl, flags=0, rows=None, exact=None, lens_dev=None):
+    p = wl.params
+    B, N, m, G, P, K = p["B"], p["N"], p["m"], p["G"], p["P"], p["topk"]
+    t = {k: v.cuda() for k, v in wl.tensors.items()}
+    pool = bool(flags & dsa.POOL_MEAN)
+    lens = t["prefix_lens"] if lens_dev is None else torch.as_tensor(lens_dev, dtype=torch.int32).cuda()
+    gi, gs, gb = dsa.indexer_mtp(t["q"], t["k_cache"], t["k_scale"], t["w"], None if pool else t["qbar"],
+                                 None if pool else t["wbar"], lens, G, P, K, flags=flags, want_bank=True)
+    torch.cuda.synchronize()
+    gi, gs, gb = _np(gi).reshape(B * m, K), _np(gs).reshape(B * m, K), _np(gb)
+    rows = np.arange(B * m) if rows is None else np.asarray(rows)
+    ri, rs, rb, _ = oracle.mtp(wl["q"], wl["k_cache"], wl["k_scale"], wl["w"], wl["qbar"], wl["wbar"],
+                               wl["prefix_lens"], G, P, K, flags=flags, rows=rows, want_bank=True)
+    exact = (p["dist"] == "int") if exact is None else exact
+    qf = wl["q"].reshape(B * m, p["H"], p["d"])
+    wf = wl["w"].reshape(B * m, p["H"])
+    kc = wl["k_cache"].reshape(B * N, -1)
+    ks = wl["k_scale"].reshape(B * N)
+    if pool:
+        pooled = [oracle.pool_mean_bf16(wl["q"][b], wl["w"][b], G) for b in range(B)]
+        qbar = torch.from_numpy(np.stack([x[0] for x in pooled]).view(np.int16)).view(torch.bfloat16)
+        wbar = torch.from_numpy(np.stack([x[1] for x in pooled]))
+    else:
+        qbar, wbar = wl["qbar"], wl["wbar"]
+    NGs = m // G
+    qbf = qbar.reshape(B * NGs, -1, p["d"])
+    wbf = wbar.reshape(B * NGs, -1)
+    if exact:
+        assert np.array_equal(gb, rb), "banks differ"
+        compare(gi[rows], gs[rows], ri, rs, True)
+        return gi, gs, gb
+    # banks under the tolerance rule of the group score, then the rows whose
+    # bank is the oracle's
+    for b in range(B):
+        for g in range(NGs):
+            v = rb[b, g][rb[b, g] >= 0]
+            if len(v) == 0:
+                assert (gb[b, g] == -1).all()
+                continue
+            grp = b * NGs + g
+
+            def bank_score(r, keys, grp=grp, b=b):
+                return oracle.score_pairs(qbf, kc, wbf, np.full(len(keys), grp), b * N + keys, "bf16", "fp8",
+                                          None, ks)
+            compare(gb[b, g][None], None, rb[b, g][None], bank_score(0, v)[None], False, bank_score,
+                    label=f"bank {b},{g}")
+
+    def score_of(r, keys):
+        row = rows[r]
+        b = row // m
+        return oracle.score_pairs(qf, kc, wf, np.full(len(keys), row), b * N + keys, "bf16", "fp8", None, ks)
+    same = np.array([np.array_equal(gb[r // m, (r % m) // G], rb[r // m, (r % m) // G]) for r in rows])
+    assert same.mean() > 0.5
+    sel = np.nonzero(same)[0]
+    compare(gi[rows][sel], gs[rows][sel], ri[sel], rs[sel], False, lambda r, keys: score_of(sel[r], keys))
+    return gi, gs, gb
+
+
+@pytest.mark.parametrize("G", [4, 8, 16])
+def test_mtp_mixed_windows_exact(dsa, G):
+    """Integer inputs, 64-head queries, a 16-head group indexer; windows that
+    fall back (N << P, N == P) and windows that share banks (N == P+1, N at the
+    end of the cache)."""
+    P = 256
+    wl = make_mtp(B=4, N=3000, m=16, H=64, Hs=16, d=128, topk=64, G=G, P=P, dist="int", seed=50 + G,
+                  prefix_lens=[40, P, P + 1, 3000 - 16 + 1])
+    gi, _, gb = _mtp_check(dsa, wl)
+    assert (gb[:2] == -1).all() and (gb[2:] >= 0).all()
+
+
+def test_mtp_pooled_exact(dsa):
+    wl = make_mtp(B=3, N=5000, m=16, H=64, Hs=64, d=128, topk=128, G=8, P=1024, dist="int", seed=54,
+                  prefix_lens=[1500, 4985, 900])
+    _mtp_check(dsa, wl, flags=dsa.POOL_MEAN)
+
+
+def test_mtp_small_heads_d64(dsa):
+    """General shapes: 8 heads at d = 64, a 4-head group indexer, topk == P."""
+    wl = make_mtp(B=5, N=700, m=8, H=8, Hs=4, d=64, topk=48, G=4, P=48, dist="int", seed=55,
+                  prefix_lens=[1, 47, 48, 49, 693])
+    _mtp_check(dsa, wl)
+
+
+def test_mtp_prefix_clamped(dsa):
+    """Prefix lengths outside [1, Nmax-m+1] act as the nearest bound."""
+    wl = make_mtp(B=3, N=600, m=16, H=16, Hs=8, d=128, topk=32, G=4, P=100, dist="int", seed=56,
+                  prefix_lens=[1, 585, 585])
+    _mtp_check(dsa, wl, lens_dev=[-5, 585, 100000])
+
+
+def test_mtp_random_tolerance(dsa):
+    wl = make_mtp(B=4, N=20000, m=16, H=64, Hs=16, d=128, topk=512, G=4, P=2048, dist="normal", seed=57,
+                  prefix_lens=[19985, 12000, 2048, 5000])
+    _mtp_check(dsa, wl, rows=_rows(64, 40, 57))
