@@ -528,13 +528,17 @@ __global__ void __launch_bounds__(kSelThreads) decode_select_kernel(const Decode
   }
   row_threshold<kSelWaves>(args, b, s_tmp, s_res);
   const uint32_t bstar = (uint32_t)s_res[0];
-  const int need = s_res[1];   // entries of bin b* that are selected
-  const int nc = s_res[2];     // entries in bin b* (all of them are candidates)
+  const int need = s_res[1];     // entries of bin b* that are selected
+  const int in_bin = s_res[2];   // keys of the row in bin b* (the histogram's count)
   __syncthreads();
-  if (nc > kDecCandCap || nb > kSelThreads) {
+  if (in_bin > kDecCandCap || nb > kSelThreads) {  // the same test decode_classify made
     select_lists_exact(args, b, nb, oidx, osc, s_h, s_tmp, s_res);
     return;
   }
+  // The candidates are the list entries in b*: a span's list may have dropped
+  // b* keys below its own K-th best (which is at most the row's), so there can
+  // be fewer than in_bin, and none of the dropped ones is selected.
+  const int nc = args.cand_cnt[b];
   for (int i = tid; i < nc; i += kSelThreads) {
     s_ckey[i] = args.cand_key[(int64_t)b * kDecCandCap + i];
     s_cidx[i] = args.cand_idx[(int64_t)b * kDecCandCap + i];

@@ -252,6 +252,23 @@ def test_decode_select_paths(dsa):
     _decode_check(dsa, wl3)
 
 
+def test_decode_reused_workspace(dsa):
+    """Rows whose first span holds nearly every key (its own K-th best falls in
+    the row's threshold bin, so its list drops some of that bin's keys), decoded
+    with a workspace that a previous call on other inputs left full: only the
+    candidates this call gathered may be read."""
+    lens = [257, 300, 513, 260, 511, 258, 400, 290]
+    first = make_decode(B=8, N=600, H=64, d=128, topk=100, dist="int", seed=24, seq_lens=lens)
+    wl = make_decode(B=8, N=600, H=64, d=128, topk=100, dist="int", seed=25, seq_lens=lens)
+    ws = torch.empty(dsa.workspace_decode(8, 600, 64, 128, 100), dtype=torch.uint8, device="cuda")
+    for w in (first, wl):
+        t = {k: v.cuda() for k, v in w.tensors.items()}
+        gi, gs = dsa.indexer_decode(t["q"], t["k_cache"], t["k_scale"], t["w"], t["seq_lens"], 100, ws=ws)
+        torch.cuda.synchronize()
+        ri, rs = oracle.decode(w["q"], w["k_cache"], w["k_scale"], w["w"], w["seq_lens"], 100)
+        compare(_np(gi), _np(gs), ri, rs, True)
+
+
 def test_decode_small_heads(dsa):
     wl = make_decode(B=3, N=777, H=7, d=64, topk=100, dist="int", seed=14, seq_lens=[777, 100, 99])
     _decode_check(dsa, wl)
@@ -465,3 +482,11 @@ def test_mtp_random_tolerance(dsa):
     wl = make_mtp(B=4, N=20000, m=16, H=64, Hs=16, d=128, topk=512, G=4, P=2048, dist="normal", seed=57,
                   prefix_lens=[19985, 12000, 2048, 5000])
     _mtp_check(dsa, wl, rows=_rows(64, 40, 57))
+
+
+def test_mtp_no_bank_is_dense(dsa):
+    """NO_BANK: every window uses the original indexer, eligible or not."""
+    wl = make_mtp(B=3, N=4000, m=16, H=64, Hs=8, d=128, topk=256, G=8, P=512, dist="int", seed=58,
+                  prefix_lens=[3985, 100, 2000])
+    _, _, gb = _mtp_check(dsa, wl, flags=dsa.NO_BANK)
+    assert (gb == -1).all()
