@@ -14,7 +14,7 @@ bounded sample of the same inputs.
 Inputs are generated on the GPU before timing (resident in HBM); outputs,
 workspace and streams are allocated before the timed region.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--adindex]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--adindex] [--mtp]
 """
 from __future__ import annotations
 
@@ -301,6 +301,61 @@ def bench_adindex(dsa, args, log):
                               frac=flops / (res["adindex"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS))
 
 
+# ------------------------------------------------------------------ MTP
+
+def bench_mtp(dsa, args, log):
+    """MTP target verification at 256K (the pages' decode-indexer speedups are
+    quoted at 256K for 16-query windows and (G, P) in {8, 16} x {8K, 16K}).
+    The group indexer has 8 heads (one eighth of the 64 indexer heads)."""
+    from workloads import make_mtp
+    B, N, m, H, Hs, d, K = 8, 262144, 16, 64, 8, 128, 2048
+    out = torch.empty((B, m, K), dtype=torch.int32, device="cuda")
+    dense_out = torch.empty_like(out)
+    res = dict(workload=f"MTP verification: B={B} sequences x {m}-query windows, the last query seeing all "
+                        f"{N} keys of an E4M3 cache, H=64, Hs={Hs}, d=128, top-{K}", configs=[])
+    wl = None
+    for G, P in ((8, 8192), (16, 8192), (8, 16384), (16, 16384)):
+        if wl is None or wl.params["G"] != G:
+            log(f"generating MTP inputs (G={G}) on the GPU")
+            wl = make_mtp(B=B, N=N, m=m, H=H, Hs=Hs, d=d, topk=K, G=G, P=P, dist="normal", seed=args.seed,
+                          device="cuda")
+        t = wl.tensors
+        ws = torch.empty(dsa.workspace_mtp(B, N, m, H, Hs, d, G, P, K), dtype=torch.uint8, device="cuda")
+
+        def step():
+            dsa.indexer_mtp(t["q"], t["k_cache"], t["k_scale"], t["w"], t["qbar"], t["wbar"], t["prefix_lens"], G,
+                            P, K, want_score=False, out_idx=out, ws=ws)
+
+        def dense():
+            dsa.indexer_mtp(t["q"], t["k_cache"], t["k_scale"], t["w"], None, None, t["prefix_lens"], G, P, K,
+                            flags=dsa.NO_BANK, want_score=False, out_idx=dense_out, ws=ws)
+        ms = {}
+        for name, fn in (("mtp", step), ("dense", dense)):
+            fn()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                fn()
+            torch.cuda.synchronize()
+            ms[name] = (time.perf_counter() - t0) * 1e3 / args.steps
+        lens = t["prefix_lens"].cpu().numpy()
+        pairs = dsa.indexer_mtp_pairs(lens, N, m, G, P)
+        dense_pairs = dsa.indexer_mtp_pairs(lens, N, m, G, P, dsa.NO_BANK)
+        a, b = out.reshape(B * m, K).cpu().numpy(), dense_out.reshape(B * m, K).cpu().numpy()
+        rec = float(np.mean([len(np.intersect1d(x, y)) / len(y) for x, y in zip(a, b)]))
+        # one read of every sequence's cache and scales is the least any scan needs
+        cache_bytes = B * N * (d + 4)
+        res["configs"].append(dict(G=G, P=P, ms_per_call=ms["mtp"], dense_ms=ms["dense"],
+                                   speedup_vs_dense=ms["dense"] / ms["mtp"],
+                                   scoring_count_ratio=dense_pairs / pairs, pairs=pairs,
+                                   cache_read_gbs=cache_bytes / (ms["mtp"] * 1e-3) / 1e9,
+                                   dense_cache_read_gbs=cache_bytes / (ms["dense"] * 1e-3) / 1e9,
+                                   recall_vs_dense=rec))
+        log(f"MTP G={G} P={P}: {ms['mtp']:.3f} ms, dense {ms['dense']:.3f} ms")
+    res["recall_note"] = "synthetic i.i.d. queries and a random group query: recall is not a quality figure"
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -312,6 +367,7 @@ def main():
     ap.add_argument("--cpu-decode-rows", type=int, default=32)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--adindex", action="store_true", help="also time the ADIndex group-bank workload")
+    ap.add_argument("--mtp", action="store_true", help="also time MTP verification windows at 256K")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only copy BYTES device-to-device 5 times (calibrates HBM byte counters)")
@@ -367,6 +423,8 @@ def main():
         line["decode"] = bench_decode(dsa, args, log)
     if args.adindex:
         line["adindex"] = bench_adindex(dsa, args, log)
+    if args.mtp:
+        line["mtp"] = bench_mtp(dsa, args, log)
     print(json.dumps(line), flush=True)
 
 

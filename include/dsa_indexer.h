@@ -63,7 +63,8 @@ typedef enum {
 
 enum {
     DSAIDX_FORCE_BANK = 1u, /* group bank: also build banks when t+1 <= P */
-    DSAIDX_POOL_MEAN = 2u   /* group bank: training-free group query (mean pooling) */
+    DSAIDX_POOL_MEAN = 2u,  /* group bank, MTP: training-free group query (mean pooling) */
+    DSAIDX_NO_BANK = 8u     /* MTP: every window uses the original indexer (no reuse) */
 };
 
 /*
@@ -157,7 +158,9 @@ int64_t indexer_group_bank_pairs(int64_t Tq, int64_t q_pos0, int G, int P, unsig
  *               each group's mean query and gates are used, Hs == H)
  *   prefix_lens [B] int32, device: N_b, clamped on the device to [1, Nmax-m+1]
  *               (the cache must hold the window's own keys)
- *   flags       DSAIDX_POOL_MEAN or 0
+ *   flags       DSAIDX_POOL_MEAN, DSAIDX_NO_BANK (the original indexer for
+ *               every window, as for a layer configured without reuse; qbar
+ *               and wbar are then not read) or 0
  *   out_idx     [B, m, topk] int32 (ascending token indices, then -1);
  *   out_score   [B, m, topk] fp32 or NULL
  *   out_bank    [B, m/G, P] int32 or NULL: the banks (ascending; rows of
@@ -173,9 +176,10 @@ int indexer_mtp(const void *q, const uint8_t *k_cache, const float *k_scale, con
 /* Workspace bytes for any prefix lengths (sized for the longest rows). */
 size_t indexer_mtp_workspace_size(int B, int64_t Nmax, int m, int H, int Hs, int d, int G, int P,
                                   int topk, unsigned flags);
-/* Query-key scores indexer_mtp evaluates for these (host) prefix lengths:
- * Eq. (21) summed over the windows.  -1 on bad arguments. */
-int64_t indexer_mtp_pairs(const int32_t *prefix_lens, int B, int64_t Nmax, int m, int G, int P);
+/* Query-key scores indexer_mtp evaluates for these (host) prefix lengths and
+ * flags: Eq. (21) summed over the windows.  -1 on bad arguments. */
+int64_t indexer_mtp_pairs(const int32_t *prefix_lens, int B, int64_t Nmax, int m, int G, int P,
+                          unsigned flags);
 
 /* Message describing the calling thread's last non-OK return ("" if none). */
 const char *indexer_last_error(void);

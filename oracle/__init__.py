@@ -20,6 +20,7 @@ _SRC = os.path.join(_HERE, "oracle.c")
 F32, BF16, E4M3 = 0, 1, 2
 FORCE_BANK = 1
 WINDOW = 4  # group_bank flag: MTP window, eligibility decided on the first query
+NO_BANK = 8  # every group (MTP: every window) uses the original indexer
 
 _lib = None
 
@@ -37,7 +38,9 @@ def build(force: bool = True) -> str:
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
+        stale = not os.path.exists(LIB_PATH) or any(
+            os.path.getmtime(os.path.join(_HERE, f)) > os.path.getmtime(LIB_PATH) for f in ("oracle.c", "oracle.h"))
+        if stale:  # built from older sources: rebuild rather than bind a mismatched library
             build()
         L = ctypes.CDLL(LIB_PATH)
         P, I64, I32, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
@@ -58,10 +61,10 @@ def lib():
         L.oracle_pool_mean_bf16.restype = I32
         L.oracle_pool_mean_bf16.argtypes = [P, P, I64, I32, I32, I32, P, P]
         L.oracle_mtp.restype = I32
-        L.oracle_mtp.argtypes = [P, P, P, P, P, P, P, I32, I64, I32, I32, I32, I32, I32, I32, I32, P, I64,
-                                 P, P, P, P, I32]
+        L.oracle_mtp.argtypes = [P, P, P, P, P, P, P, I32, I64, I32, I32, I32, I32, I32, I32, I32,
+                                 ctypes.c_uint, P, I64, P, P, P, P, I32]
         L.oracle_mtp_pairs.restype = I64
-        L.oracle_mtp_pairs.argtypes = [P, I32, I32, I32, I32]
+        L.oracle_mtp_pairs.argtypes = [P, I32, I32, I32, I32, ctypes.c_uint]
         L.oracle_group_bank_pairs.restype = I64
         L.oracle_group_bank_pairs.argtypes = [I64, I64, I32, I32, ctypes.c_uint]
         for name in ("oracle_cost_prefill_base",):
@@ -226,7 +229,8 @@ def mtp(q, k_cache, k_scale, w, qbar, wbar, prefix_lens, G, P, topk, flags=0, ro
     """MTP target verification (Section 4.3; Appendix A.2): windows of m bf16
     queries [B,m,H,d] over E4M3 caches [B,Nmax,d]; N_b = prefix_lens[b] keys
     visible to each window's first query.  ``flags & POOL_MEAN`` pools each
-    group's own queries and gates (qbar, wbar ignored).  Rows index [B*m].
+    group's own queries and gates (qbar, wbar ignored); ``flags & NO_BANK``
+    sends every window to the original indexer.  Rows index [B*m].
     Returns (idx [n,topk], score [n,topk], bank [B,m/G,P] or None, pairs)."""
     q, k_cache, k_scale = _host(q), _host(k_cache), _host(k_scale)
     w = _host(w).astype(np.float32)
@@ -251,7 +255,8 @@ def mtp(q, k_cache, k_scale, w, qbar, wbar, prefix_lens, G, P, topk, flags=0, ro
     bank = np.empty((B, m // G, P), np.int32) if want_bank else None
     pairs = ctypes.c_int64(0)
     rc = lib().oracle_mtp(_ptr(q), _ptr(k_cache), _ptr(k_scale), _ptr(w), _ptr(qbar), _ptr(wbar), _ptr(lens), B,
-                          Nmax, m, H, Hs, d, G, P, topk, _ptr(r), nr, _ptr(idx), _ptr(sc), _ptr(bank),
+                          Nmax, m, H, Hs, d, G, P, topk, flags & NO_BANK, _ptr(r), nr, _ptr(idx), _ptr(sc),
+                          _ptr(bank),
                           ctypes.cast(ctypes.pointer(pairs), ctypes.c_void_p), nthreads)
     if rc != 0:
         raise ValueError(f"oracle_mtp failed ({rc})")
@@ -260,9 +265,9 @@ def mtp(q, k_cache, k_scale, w, qbar, wbar, prefix_lens, G, P, topk, flags=0, ro
     return idx, sc, bank, pairs.value
 
 
-def mtp_pairs(prefix_lens, m, G, P) -> int:
+def mtp_pairs(prefix_lens, m, G, P, flags=0) -> int:
     lens = np.ascontiguousarray(np.asarray(prefix_lens, np.int32))
-    return lib().oracle_mtp_pairs(_ptr(lens), len(lens), m, G, P)
+    return lib().oracle_mtp_pairs(_ptr(lens), len(lens), m, G, P, flags & NO_BANK)
 
 
 def group_bank_pairs(Tq, q_pos0, G, P, flags=0) -> int:

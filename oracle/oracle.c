@@ -294,6 +294,8 @@ static int group_uses_bank(int64_t g, int64_t Tq, int64_t q_pos0, int G, int P, 
     if ((g + 1) * G > Tq)
         return 0; /* incomplete group: original indexer */
     int64_t anchor = q_pos0 + g * G;
+    if (flags & ORACLE_NO_BANK)
+        return 0;
     if (flags & ORACLE_FORCE_BANK)
         return 1;
     if (flags & ORACLE_WINDOW)
@@ -441,18 +443,20 @@ int oracle_group_bank(const void *q, const float *q_scale, const void *k, const 
  * groups, the anchor of group g (query gG) builds a bank of the P best of its
  * N_b + gG visible keys with the group query, and every member refines over
  * the bank plus the keys after the anchor (Eq. 14).  Queries are bf16; the
- * cache is E4M3 codes with one fp32 scale per token, as in decode. */
-int64_t oracle_mtp_pairs(const int32_t *prefix_lens, int B, int m, int G, int P)
+ * cache is E4M3 codes with one fp32 scale per token, as in decode.  With
+ * ORACLE_NO_BANK every window uses the original indexer (the baseline). */
+int64_t oracle_mtp_pairs(const int32_t *prefix_lens, int B, int m, int G, int P, unsigned flags)
 {
     int64_t pairs = 0;
     for (int b = 0; b < B; ++b)
-        pairs += oracle_group_bank_pairs(m, (int64_t)prefix_lens[b] - 1, G, P, ORACLE_WINDOW);
+        pairs += oracle_group_bank_pairs(m, (int64_t)prefix_lens[b] - 1, G, P,
+                                         ORACLE_WINDOW | (flags & ORACLE_NO_BANK));
     return pairs;
 }
 
 int oracle_mtp(const void *q, const uint8_t *k_cache, const float *k_scale, const float *w,
                const void *qbar, const float *wbar, const int32_t *prefix_lens, int B,
-               int64_t Nmax, int m, int H, int Hs, int d, int G, int P, int topk,
+               int64_t Nmax, int m, int H, int Hs, int d, int G, int P, int topk, unsigned flags,
                const int64_t *rows, int64_t nrows, int32_t *out_idx, double *out_score,
                int32_t *out_bank, int64_t *pairs, int nthreads)
 {
@@ -488,7 +492,7 @@ int oracle_mtp(const void *q, const uint8_t *k_cache, const float *k_scale, cons
                               (int64_t)prefix_lens[b] - 1,
                               qbar ? (const uint16_t *)qbar + (size_t)b * NGs * Hs * d : NULL,
                               NULL, wbar ? wbar + (size_t)b * NGs * Hs : NULL, Hs, G, P, topk,
-                              ORACLE_WINDOW, lrows, rows ? r1 - r0 : 0,
+                              ORACLE_WINDOW | (flags & ORACLE_NO_BANK), lrows, rows ? r1 - r0 : 0,
                               out_idx ? out_idx + o * topk : NULL,
                               out_score ? out_score + o * topk : NULL,
                               out_bank ? out_bank + (size_t)b * NGs * P : NULL);
@@ -496,7 +500,7 @@ int oracle_mtp(const void *q, const uint8_t *k_cache, const float *k_scale, cons
         r0 = r1;
     }
     if (pairs)
-        *pairs = oracle_mtp_pairs(prefix_lens, B, m, G, P);
+        *pairs = oracle_mtp_pairs(prefix_lens, B, m, G, P, flags);
     return err;
 }
 

@@ -24,7 +24,11 @@ extern "C" {
 #endif
 
 enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_E4M3 = 2 };
-enum { ORACLE_FORCE_BANK = 1u, ORACLE_WINDOW = 4u /* MTP: one eligibility test per window */ };
+enum {
+    ORACLE_FORCE_BANK = 1u,
+    ORACLE_WINDOW = 4u,  /* MTP: one eligibility test per window */
+    ORACLE_NO_BANK = 8u  /* every group uses the original indexer */
+};
 
 double oracle_e4m3_to_double(uint8_t c);
 double oracle_bf16_to_double(uint16_t b);
@@ -73,13 +77,14 @@ int64_t oracle_group_bank_pairs(int64_t Tq, int64_t q_pos0, int G, int P, unsign
  * with k_scale [B,Nmax], w [B,m,H]; qbar [B,m/G,Hs,d] bf16 and wbar [B,m/G,Hs]
  * the group indexer's query; prefix_lens [B]: N_b, the keys the window's first
  * query sees (1 <= N_b, N_b + m - 1 <= Nmax).  Rows index [B*m] and must be
- * ascending; out_bank [B,m/G,P] (-1 rows for windows that fall back). */
+ * ascending; out_bank [B,m/G,P] (-1 rows for windows that fall back).
+ * flags: ORACLE_NO_BANK (every window falls back) or 0. */
 int oracle_mtp(const void *q, const uint8_t *k_cache, const float *k_scale, const float *w,
                const void *qbar, const float *wbar, const int32_t *prefix_lens, int B,
-               int64_t Nmax, int m, int H, int Hs, int d, int G, int P, int topk,
+               int64_t Nmax, int m, int H, int Hs, int d, int G, int P, int topk, unsigned flags,
                const int64_t *rows, int64_t nrows, int32_t *out_idx, double *out_score,
                int32_t *out_bank, int64_t *pairs, int nthreads);
-int64_t oracle_mtp_pairs(const int32_t *prefix_lens, int B, int m, int G, int P);
+int64_t oracle_mtp_pairs(const int32_t *prefix_lens, int B, int m, int G, int P, unsigned flags);
 
 double oracle_cost_prefill_base(double L);
 double oracle_cost_prefill_reuse(double L, double G, double P);

@@ -20,15 +20,16 @@ from __future__ import annotations
 import torch
 
 from ._lib import (DSAIDX_BF16, DSAIDX_FORCE_BANK, DSAIDX_FP8_E4M3, DSAIDX_OK,  # noqa: F401
-                   DSAIDX_POOL_MEAN, LIB_PATH, last_error, lib)
+                   DSAIDX_NO_BANK, DSAIDX_POOL_MEAN, LIB_PATH, last_error, lib)
 
 __all__ = ["indexer_prefill", "indexer_decode", "indexer_group_bank", "indexer_group_bank_pairs",
            "workspace_prefill", "workspace_decode", "workspace_group_bank", "indexer_mtp", "indexer_mtp_pairs",
-           "workspace_mtp", "FORCE_BANK", "POOL_MEAN", "lib",
+           "workspace_mtp", "FORCE_BANK", "POOL_MEAN", "NO_BANK", "lib",
            "LIB_PATH"]
 
 FORCE_BANK = DSAIDX_FORCE_BANK
 POOL_MEAN = DSAIDX_POOL_MEAN
+NO_BANK = DSAIDX_NO_BANK
 
 
 def _ptr(t):
@@ -160,12 +161,12 @@ def workspace_mtp(B, Nmax, m, H, Hs, d, G, P, topk, flags=0):
     return lib().indexer_mtp_workspace_size(B, Nmax, m, H, Hs, d, G, P, topk, flags)
 
 
-def indexer_mtp_pairs(prefix_lens, Nmax, m, G, P):
+def indexer_mtp_pairs(prefix_lens, Nmax, m, G, P, flags=0):
     """Scores the MTP call evaluates for these prefix lengths (host ints)."""
     import ctypes
     import numpy as np
     lens = np.ascontiguousarray(np.asarray(prefix_lens, dtype=np.int32))
-    return lib().indexer_mtp_pairs(lens.ctypes.data_as(ctypes.c_void_p), len(lens), Nmax, m, G, P)
+    return lib().indexer_mtp_pairs(lens.ctypes.data_as(ctypes.c_void_p), len(lens), Nmax, m, G, P, flags)
 
 
 def indexer_mtp(q, k_cache, k_scale, w, qbar, wbar, prefix_lens, G, P, topk=2048, flags=0, want_score=True,
@@ -174,7 +175,7 @@ def indexer_mtp(q, k_cache, k_scale, w, qbar, wbar, prefix_lens, G, P, topk=2048
 
     q [B,m,H,d] bf16, k_cache [B,Nmax,d] uint8 E4M3, k_scale [B,Nmax] fp32,
     w [B,m,H], qbar [B,m/G,Hs,d] bf16 and wbar [B,m/G,Hs] (None with
-    POOL_MEAN), prefix_lens [B] int32 on the GPU.  Returns (idx [B,m,topk],
+    POOL_MEAN; not read with NO_BANK), prefix_lens [B] int32 on the GPU.  Returns (idx [B,m,topk],
     score or None, bank [B,m/G,P] or None)."""
     dev = _dev(q, k_cache, k_scale, w, qbar, wbar, prefix_lens, out_idx, out_score, out_bank, ws)
     B, m, H, d = q.shape

@@ -16,6 +16,7 @@ DSAIDX_BF16 = 1
 DSAIDX_FP8_E4M3 = 2
 DSAIDX_FORCE_BANK = 1
 DSAIDX_POOL_MEAN = 2
+DSAIDX_NO_BANK = 8
 
 # exported symbol -> (restype, argtypes)
 _P, _I, _I64, _U, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint, ctypes.c_size_t
@@ -31,7 +32,7 @@ SIGNATURES = {
     "indexer_mtp": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I64, _I, _I, _I, _I, _I, _I, _I, _U, _P, _P, _P, _P,
                          _SZ, _P]),
     "indexer_mtp_workspace_size": (_SZ, [_I, _I64, _I, _I, _I, _I, _I, _I, _I, _U]),
-    "indexer_mtp_pairs": (_I64, [_P, _I, _I64, _I, _I, _I]),
+    "indexer_mtp_pairs": (_I64, [_P, _I, _I64, _I, _I, _I, _U]),
     "indexer_last_error": (ctypes.c_char_p, []),
 }
 

@@ -532,14 +532,15 @@ size_t indexer_mtp_workspace_size(int B, int64_t Nmax, int m, int H, int Hs, int
   return mtp_ws(B, Nmax, m, H, d, G, P, flags, true).total;
 }
 
-int64_t indexer_mtp_pairs(const int32_t* prefix_lens, int B, int64_t Nmax, int m, int G, int P) {
+int64_t indexer_mtp_pairs(const int32_t* prefix_lens, int B, int64_t Nmax, int m, int G, int P,
+                          unsigned flags) {
   if (B < 0 || m <= 0 || G <= 0 || m % G || P <= 0 || Nmax < m || (B > 0 && !prefix_lens))
     return -1;
   int64_t pairs = 0;
   for (int b = 0; b < B; ++b) {
     int64_t N = prefix_lens[b];
     N = N < 1 ? 1 : (N > Nmax - m + 1 ? Nmax - m + 1 : N);  // as the device clamps it
-    if (N <= P) {
+    if (N <= P || (flags & DSAIDX_NO_BANK)) {
       pairs += m * N + (int64_t)m * (m - 1) / 2;  // every query: N + r keys
       continue;
     }
@@ -567,16 +568,19 @@ int indexer_mtp(const void* q, const uint8_t* k_cache, const float* k_scale, con
   if ((int64_t)B * m > 65535) return fail(DSAIDX_ERR_UNSUPPORTED, "B * m above 65535");
   if (P < topk) return fail(DSAIDX_ERR_INVALID_ARG, "bank size P = %d below topk = %d", P, topk);
   if (P > kMaxBank) return fail(DSAIDX_ERR_UNSUPPORTED, "bank size P = %d above %d", P, kMaxBank);
-  if (flags & ~(unsigned)DSAIDX_POOL_MEAN)
+  if (flags & ~(unsigned)(DSAIDX_POOL_MEAN | DSAIDX_NO_BANK))
     return fail(DSAIDX_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
   const bool pool = (flags & DSAIDX_POOL_MEAN) != 0;
+  const bool no_bank = (flags & DSAIDX_NO_BANK) != 0;
+  if (pool && no_bank)
+    return fail(DSAIDX_ERR_INVALID_ARG, "DSAIDX_POOL_MEAN and DSAIDX_NO_BANK exclude each other");
   if (pool && (qbar || wbar))
     return fail(DSAIDX_ERR_INVALID_ARG, "DSAIDX_POOL_MEAN takes NULL qbar and wbar");
   if (pool && Hs != H) return fail(DSAIDX_ERR_INVALID_ARG, "DSAIDX_POOL_MEAN needs Hs == H");
   if (Hs < 1) return fail(DSAIDX_ERR_INVALID_ARG, "Hs = %d must be positive", Hs);
   if (Hs > kMaxHeads) return fail(DSAIDX_ERR_UNSUPPORTED, "Hs = %d above %d", Hs, kMaxHeads);
   if (B > 0 && (!q || !k_cache || !k_scale || !w || !prefix_lens || !out_idx ||
-                (!pool && (!qbar || !wbar))))
+                (!pool && !no_bank && (!qbar || !wbar))))
     return fail(DSAIDX_ERR_INVALID_ARG, "null q, k_cache, k_scale, w, qbar, wbar, prefix_lens or out_idx");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(w) || !aligned16(qbar) || !aligned16(wbar) ||
       !aligned16(out_idx) || !aligned16(out_score) || !aligned16(out_bank))
@@ -614,6 +618,7 @@ int indexer_mtp(const void* q, const uint8_t* k_cache, const float* k_scale, con
   t.gs = (float*)(base + lay.gs);
   t.out_idx = out_idx;
   t.topk = topk;
+  t.no_bank = no_bank;
   hipError_t e = launch_mtp_plan(t, st);
   if (e != hipSuccess) return hip_fail(e, "indexer_mtp plan launch");
 

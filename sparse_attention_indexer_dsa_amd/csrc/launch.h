@@ -112,6 +112,7 @@ struct MtpArgs {
   float* gs;               // [B*m/G, P+G-1] their scales
   int32_t* out_idx;        // [B*m, topk] refinement output, mapped in place
   int topk;
+  int no_bank;             // every window uses the original indexer
 };
 hipError_t launch_mtp_plan(const MtpArgs& a, hipStream_t stream);
 hipError_t launch_mtp_gather(const MtpArgs& a, hipStream_t stream);

@@ -33,6 +33,10 @@ __device__ __forceinline__ int64_t window_start(const MtpArgs& a, int b) {
   return n < 1 ? 1 : (n > hi ? hi : n);
 }
 
+// the window reuses banks: its first query sees more than P keys (and the
+// caller did not ask for the original indexer throughout)
+__device__ __forceinline__ bool uses_bank(const MtpArgs& a, int64_t N) { return !a.no_bank && N > a.P; }
+
 __global__ void __launch_bounds__(kMtpThreads) mtp_plan_kernel(const MtpArgs a) {
   const int64_t idx = (int64_t)blockIdx.x * kMtpThreads + threadIdx.x;
   const int NGs = a.m / a.G;
@@ -42,13 +46,13 @@ __global__ void __launch_bounds__(kMtpThreads) mtp_plan_kernel(const MtpArgs a) 
     const int64_t N = window_start(a, b);
     a.a_kc[idx] = a.kc + (int64_t)b * a.Nmax * a.d;
     a.a_ks[idx] = a.ks + (int64_t)b * a.Nmax;
-    a.a_len[idx] = N > a.P ? (int32_t)(N + (int64_t)g * a.G) : 0;
+    a.a_len[idx] = uses_bank(a, N) ? (int32_t)(N + (int64_t)g * a.G) : 0;
   }
   if (idx < (int64_t)a.B * a.m) {
     const int b = (int)(idx / a.m), r = (int)(idx % a.m);
     const int g = r / a.G, i = r % a.G;
     const int64_t N = window_start(a, b);
-    if (N > a.P) {
+    if (uses_bank(a, N)) {
       const int64_t grp = (int64_t)b * NGs + g;
       a.r_kc[idx] = a.gk + grp * cand * a.d;
       a.r_ks[idx] = a.gs + grp * cand;
@@ -73,7 +77,7 @@ __global__ void __launch_bounds__(kMtpThreads) mtp_gather_kernel(const MtpArgs a
   const int64_t grp = blockIdx.y;
   const int b = (int)(grp / NGs), g = (int)(grp % NGs);
   const int64_t N = window_start(a, b);
-  if (N <= a.P) return;  // this window falls back: nothing to gather
+  if (!uses_bank(a, N)) return;  // this window falls back: nothing to gather
   const int64_t anchor = N - 1 + (int64_t)g * a.G;
   const int cpr = a.d / 16;  // chunks per key row
   const int rows_per_block = kMtpThreads / cpr;
@@ -93,7 +97,7 @@ __global__ void __launch_bounds__(kMtpThreads) mtp_map_kernel(const MtpArgs a) {
   const int64_t row = blockIdx.y;
   const int b = (int)(row / a.m), r = (int)(row % a.m);
   const int64_t N = window_start(a, b);
-  if (N <= a.P) return;  // fallback rows already hold token indices
+  if (!uses_bank(a, N)) return;  // fallback rows already hold token indices
   const int j = blockIdx.x * kMtpThreads + threadIdx.x;
   if (j >= a.topk) return;
   const int g = r / a.G;

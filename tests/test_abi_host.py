@@ -151,6 +151,7 @@ def _mtp(L, **kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(G=5), UNSUPPORTED), (dict(m=12, G=8), INVALID), (dict(m=128), UNSUPPORTED), (dict(N=8), INVALID),
     (dict(P=32), INVALID), (dict(P=20000), UNSUPPORTED), (dict(flags=1), INVALID), (dict(flags=2), INVALID),
+    (dict(flags=10, qbar=None, wbar=None, Hs=64), INVALID), (dict(flags=16), INVALID),
     (dict(flags=2, qbar=None, wbar=None), INVALID), (dict(qbar=None), INVALID), (dict(lens=None), INVALID),
     (dict(d=32), UNSUPPORTED), (dict(Hs=0), INVALID), (dict(Hs=80), UNSUPPORTED), (dict(B=5000), UNSUPPORTED),
     (dict(ks=P((1 << 20) + 2)), INVALID), (dict(ws_bytes=10), WORKSPACE), (dict(topk=4096), UNSUPPORTED),
@@ -162,9 +163,11 @@ def test_mtp_rejects(L, kw, code):
 def test_mtp_pairs_match_oracle(L):
     lens = np.array([1, 100, 2048, 2049, 70000, 131057], np.int32)
     for G in (4, 8, 16):
-        got = L.indexer_mtp_pairs(lens.ctypes.data_as(ctypes.c_void_p), len(lens), 131072, 16, G, 2048)
+        got = L.indexer_mtp_pairs(lens.ctypes.data_as(ctypes.c_void_p), len(lens), 131072, 16, G, 2048, 0)
         assert got == oracle.mtp_pairs(lens, 16, G, 2048)
+        got = L.indexer_mtp_pairs(lens.ctypes.data_as(ctypes.c_void_p), len(lens), 131072, 16, G, 2048, 8)
+        assert got == oracle.mtp_pairs(lens, 16, G, 2048, oracle.NO_BANK)
     # out-of-range prefix lengths count as clamped
     bad = np.array([0, 200000], np.int32)
-    got = L.indexer_mtp_pairs(bad.ctypes.data_as(ctypes.c_void_p), 2, 131072, 16, 4, 2048)
+    got = L.indexer_mtp_pairs(bad.ctypes.data_as(ctypes.c_void_p), 2, 131072, 16, 4, 2048, 0)
     assert got == oracle.mtp_pairs([1, 131057], 16, 4, 2048)

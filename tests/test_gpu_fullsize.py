@@ -145,3 +145,29 @@ def test_adindex_64k_bank(dsa, dist, pool):
         assert len(sel) >= len(rows) // 2
         compare(gi.cpu().numpy()[rows][sel], gs.cpu().numpy()[rows][sel], ri[sel], rs[sel], False,
                 lambda r, keys: _score_of(h, "bf16", rows)(sel[r], keys))
+
+
+@pytest.mark.parametrize("G,P", [(8, 8192), (16, 16384)])
+def test_mtp_256k_windows(dsa, G, P):
+    """MTP verification at 256K: 4 sequences of 262144 E4M3 keys, 16-query
+    windows (one ending at the cache end, one shorter, one at the P boundary),
+    an 8-head group indexer; sampled rows and their banks against the oracle."""
+    from workloads import make_mtp
+    B, N, m, K = 4, 262144, 16, 2048
+    lens = [N - m + 1, 100000, P, P + 1]
+    wl = make_mtp(B=B, N=N, m=m, H=64, Hs=8, d=128, topk=K, G=G, P=P, dist="int", seed=60 + G, device="cuda",
+                  prefix_lens=lens)
+    t = wl.tensors
+    gi, gs, gb = dsa.indexer_mtp(t["q"], t["k_cache"], t["k_scale"], t["w"], t["qbar"], t["wbar"],
+                                 t["prefix_lens"], G, P, K, want_bank=True)
+    torch.cuda.synchronize()
+    rows = np.array([0, 7, 15, 16, 25, 40, 47, 48, 60, 63])
+    h = _host(t)
+    ri, rs, rb, _ = oracle.mtp(h["q"], h["k_cache"], h["k_scale"], h["w"], h["qbar"], h["wbar"], h["prefix_lens"],
+                               G, P, K, rows=rows, want_bank=True)
+    gb = gb.cpu().numpy()
+    for r in rows:  # the banks of the sampled rows' groups (window 2 falls back: all -1)
+        b, g = r // m, (r % m) // G
+        assert np.array_equal(gb[b, g], rb[b, g]), (b, g)
+    assert (gb[2] == -1).all() and (gb[3] >= 0).all()
+    compare(gi.reshape(B * m, K).cpu().numpy()[rows], gs.reshape(B * m, K).cpu().numpy()[rows], ri, rs, True)

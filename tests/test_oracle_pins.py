@@ -582,3 +582,19 @@ def test_mtp_rows_and_pooling(oracle_lib):
     pi, _, pb, _ = oracle.mtp(t["q"], t["k_cache"], t["k_scale"], t["w"], None, None, t["prefix_lens"], G, P, K,
                               flags=oracle.POOL_MEAN, want_bank=True)
     assert np.array_equal(ei, pi) and np.array_equal(eb, pb) and not np.array_equal(eb, fb)
+
+
+def test_mtp_no_bank_is_the_original_indexer(oracle_lib):
+    """NO_BANK: every window, eligible or not, ranks each query's visible keys."""
+    m, G, P, K = 16, 4, 30, 9
+    lens = [50, 10]
+    wl = make_mtp(B=2, N=80, m=m, H=3, Hs=2, d=16, topk=K, G=G, P=P, dist="normal", seed=34, prefix_lens=lens)
+    t = wl.tensors
+    mi, ms, mb, pairs = oracle.mtp(t["q"], t["k_cache"], t["k_scale"], t["w"], t["qbar"], t["wbar"],
+                                   t["prefix_lens"], G, P, K, flags=oracle.NO_BANK, want_bank=True)
+    assert (mb == -1).all() and pairs == sum(m * N + m * (m - 1) // 2 for N in lens)
+    for b, N in enumerate(lens):
+        kv = _e4m3_values(t["k_cache"][b], t["k_scale"][b]).numpy()
+        ri, rs = _mtp_dense_ref(_f64(t["q"][b]), kv, _f64(t["w"][b]), N, m, K)
+        assert np.array_equal(mi[b * m:(b + 1) * m], ri)
+        np.testing.assert_allclose(ms[b * m:(b + 1) * m], rs, rtol=1e-12)
