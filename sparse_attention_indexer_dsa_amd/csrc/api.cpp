@@ -499,7 +499,7 @@ int indexer_group_bank(const void* q, const float* q_scale, const void* k, const
 // gathered candidate keys and scales | the decode pipeline's workspace (the
 // anchor scan and the refinement run one after the other and share it)
 struct MtpWs {
-  size_t a_kc, a_ks, a_len, r_kc, r_ks, r_len, bank, pq, pw, gk, gs, dec, total;
+  size_t a_kc, a_ks, a_len, r_kc, r_ks, r_len, r_len2, bank, pq, pw, gk, gs, dec, total;
 };
 
 static MtpWs mtp_ws(int B, int64_t Nmax, int m, int H, int d, int G, int P, unsigned flags,
@@ -512,16 +512,19 @@ static MtpWs mtp_ws(int B, int64_t Nmax, int m, int H, int d, int G, int P, unsi
   w.r_kc = w.a_len + align_up(na * 4u);
   w.r_ks = w.r_kc + align_up(nr * 8u);
   w.r_len = w.r_ks + align_up(nr * 8u);
-  w.bank = w.r_len + align_up(nr * 4u);
+  w.r_len2 = w.r_len + align_up(nr * 4u);
+  w.bank = w.r_len2 + align_up(nr * 4u);
   w.pq = w.bank + (bank_in_ws ? align_up(na * P * 4u) : 0);
   const bool pool = (flags & DSAIDX_POOL_MEAN) != 0;
   w.pw = w.pq + (pool ? align_up(na * H * d * 2u) : 0);
   w.gk = w.pw + (pool ? align_up(na * H * 4u) : 0);
   w.gs = w.gk + align_up(na * cand * d);
   w.dec = w.gs + align_up(na * cand * 4u);
-  const int64_t nmax_r = Nmax > (int64_t)cand ? Nmax : (int64_t)cand;
-  const size_t da = decode_ws((int)na, Nmax).total, dr = decode_ws((int)nr, nmax_r).total;
-  w.total = w.dec + (da > dr ? da : dr);
+  size_t dw = decode_ws((int)na, Nmax).total;
+  const size_t dr = decode_ws((int)nr, Nmax).total, db = decode_ws((int)nr, (int64_t)cand).total;
+  if (dr > dw) dw = dr;
+  if (db > dw) dw = db;
+  w.total = w.dec + dw;
   return w;
 }
 
@@ -611,7 +614,8 @@ int indexer_mtp(const void* q, const uint8_t* k_cache, const float* k_scale, con
   t.a_len = (int32_t*)(base + lay.a_len);
   t.r_kc = (const uint8_t**)(base + lay.r_kc);
   t.r_ks = (const float**)(base + lay.r_ks);
-  t.r_len = (int32_t*)(base + lay.r_len);
+  t.r_len_bank = (int32_t*)(base + lay.r_len);
+  t.r_len_fb = (int32_t*)(base + lay.r_len2);
   int32_t* bank = out_bank ? out_bank : (int32_t*)(base + lay.bank);
   t.bank = bank;
   t.gk = base + lay.gk;
@@ -655,14 +659,22 @@ int indexer_mtp(const void* q, const uint8_t* k_cache, const float* k_scale, con
   e = launch_mtp_gather(t, st);
   if (e != hipSuccess) return hip_fail(e, "indexer_mtp gather launch");
 
-  // 3. refinement (Eq. (14)), or the original indexer for fallback windows
+  // 3. refinement of bank rows (Eq. (14)) over at most P + G - 1 candidates,
+  //    and the original indexer for the rows of fallback windows; each launch
+  //    leaves the other's rows (length -1) alone
   const int64_t cand = (int64_t)P + G - 1;
-  const int64_t nmax_r = Nmax > cand ? Nmax : cand;
-  DecodeArgs ar = decode_args(q, w, t.r_len, nr, nmax_r, H, d, topk, base + lay.dec, out_idx, out_score);
+  DecodeArgs ar = decode_args(q, w, t.r_len_bank, nr, cand, H, d, topk, base + lay.dec, out_idx, out_score);
   ar.row_kc = t.r_kc;
   ar.row_ks = t.r_ks;
+  ar.skip_negative = 1;
   e = launch_decode(ar, st);
   if (e != hipSuccess) return hip_fail(e, "indexer_mtp refine launch");
+  DecodeArgs af = decode_args(q, w, t.r_len_fb, nr, Nmax, H, d, topk, base + lay.dec, out_idx, out_score);
+  af.row_kc = t.r_kc;
+  af.row_ks = t.r_ks;
+  af.skip_negative = 1;
+  e = launch_decode(af, st);
+  if (e != hipSuccess) return hip_fail(e, "indexer_mtp fallback launch");
 
   // 4. bank rows: gathered positions -> token indices
   e = launch_mtp_map(t, st);

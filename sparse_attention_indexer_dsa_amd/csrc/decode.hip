@@ -310,37 +310,100 @@ __device__ __forceinline__ int block_radix_lds(const uint32_t* keys, int n, int 
   return cnt;
 }
 
+constexpr int kShift = 32 - kDecHistBits;  // order key -> histogram bin
+
+// Exclusive prefix over the workgroup of N counts at once (one round of
+// barriers for all N): before[n] = sum of lower threads' v[n], total[n] = sum.
+template <int N>
+__device__ __forceinline__ void block_excl_scan_n(const int (&v)[N], int (&before)[N], int (&total)[N],
+                                                  int* s_tmp) {
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  int incl[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    incl[n] = wave_incl_scan(v[n]);
+    if (l == 63) s_tmp[n * kSelWaves + wave] = incl[n];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    int b = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) {
+      const int t = s_tmp[n * kSelWaves + w];
+      b += w < wave ? t : 0;
+      all += t;
+    }
+    before[n] = b + incl[n] - v[n];
+    total[n] = all;
+  }
+  __syncthreads();
+}
+
 // Exact multi-pass selection over a row's compact lists in global memory
 // (rows whose threshold bin or whose flat list is too long for the finish pass).
-// The lists hold every score that can reach the top K, in ascending key order.
-__device__ void select_lists_exact(const DecodeArgs& args, int b, int nb, int32_t* oidx, float* osc,
-                                   uint32_t* s_h, int* s_tmp, int* s_res) {
+// The lists hold every score that can reach the top K, in ascending key order,
+// and sit side by side: list j of the row is slots j*kpb .. j*kpb + c_j - 1 of
+// one array, so a pass walks all slots in order, kIter batches at a time, with
+// kIter 16-byte loads in flight per thread.  In batch k, thread t holds slots
+// 4t .. 4t+3 of the batch, so (batch, thread, slot) is key order.
+constexpr int kIter = 4;
+__device__ void select_lists_exact(const DecodeArgs& args, int b, int nb, uint32_t bstar, int need,
+                                   int32_t* oidx, float* osc, uint32_t* s_h, int* s_tmp, int* s_res,
+                                   int* s_tmpn, int* s_cnt) {
   const int tid = threadIdx.x;
   const int K = args.K;
-  auto list = [&](int j, int64_t& lbase, int& c) __attribute__((always_inline)) {
-    lbase = ((int64_t)b * args.nblk + j) * args.kpb;
-    c = args.cl_cnt[(int64_t)b * args.nblk + j];
+  constexpr int kB = 4 * kSelThreads;  // slots per batch
+  const int64_t row0 = (int64_t)b * args.nblk * args.kpb;
+  const int64_t nslots = (int64_t)nb * args.kpb;
+  const int kpb = (int)args.kpb;
+  for (int j = tid; j < nb && j < kSelThreads; j += kSelThreads) s_cnt[j] = args.cl_cnt[(int64_t)b * args.nblk + j];
+  __syncthreads();
+  // list j's entry count (spans past the LDS copy are read from memory)
+  auto count = [&](uint32_t j) __attribute__((always_inline)) {
+    return j < (uint32_t)kSelThreads ? s_cnt[j] : args.cl_cnt[(int64_t)b * args.nblk + j];
   };
-  uint32_t prefix = 0, pmask = 0;
-  int krem = K;
-  for (int round = 0; round < 3; ++round) {
-    const int shift = round == 0 ? 21 : (round == 1 ? 10 : 0);
-    const int nbins = round == 2 ? 1024 : 2048;
+  auto load = [&](int64_t s0, float (&v)[kIter][4], uint32_t (&ok)[kIter]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < kIter; ++k) {
+      const int64_t s = s0 + k * kB + 4 * tid;  // kpb is a multiple of 4: one list
+      const uint32_t su = (uint32_t)s;              // slots of a row fit in 32 bits
+      const int lim = s < nslots ? count(su / (uint32_t)kpb) - (int)(su % (uint32_t)kpb) : 0;
+      ok[k] = lim >= 4 ? 0xFu : (lim > 0 ? (1u << lim) - 1u : 0u);
+      if (s < nslots) {
+        const v4f a = *(const v4f*)(args.cl_sc + row0 + s);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[k][u] = a[u];
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[k][u] = 0.0f;
+      }
+    }
+  };
+  // the row histogram already fixed the top 12 bits of the K-th key (bin b*)
+  // and how many of b*'s keys are selected: two 10-bit rounds finish it
+  uint32_t prefix = bstar << kShift, pmask = ~0u << kShift;
+  int krem = need;
+  for (int round = 0; round < 2; ++round) {
+    const int shift = round == 0 ? 10 : 0;
+    constexpr int nbins = 1024;
     const uint32_t dmask = (uint32_t)nbins - 1;
     for (int i = tid; i < nbins; i += kSelThreads) s_h[i] = 0;
     __syncthreads();
-    for (int j = 0; j < nb; ++j) {
-      int64_t lbase;
-      int c;
-      list(j, lbase, c);
-      for (int i = tid; i < c; i += kSelThreads) {
-        const uint32_t key = order_key(args.cl_sc[lbase + i]);
-        if ((key & pmask) == prefix) atomicAdd(&s_h[(key >> shift) & dmask], 1u);
-      }
+    for (int64_t s0 = 0; s0 < nslots; s0 += kIter * kB) {
+      float v[kIter][4];
+      uint32_t ok[kIter];
+      load(s0, v, ok);
+#pragma unroll
+      for (int k = 0; k < kIter; ++k)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t key = order_key(v[k][u]);
+          if ((ok[k] >> u & 1u) && (key & pmask) == prefix) atomicAdd(&s_h[(key >> shift) & dmask], 1u);
+        }
     }
     __syncthreads();
-    const int per = nbins / kSelThreads;
-    block_find_digit(per, [&](int t, int i) { return (int)s_h[t * per + i]; }, krem, s_tmp, s_res);
+    block_find_digit(1, [&](int t, int i) { return (int)s_h[t + i]; }, krem, s_tmp, s_res);
     prefix |= (uint32_t)s_res[0] << shift;
     pmask |= dmask << shift;
     krem = s_res[1];
@@ -348,36 +411,72 @@ __device__ void select_lists_exact(const DecodeArgs& args, int b, int nb, int32_
   }
   const uint32_t kth = prefix;
   const int keep_eq = krem;  // keys equal to kth: keep the keep_eq lowest indices
-  // ordered emission, 1024 list entries at a time
+  // ordered emission
   int out = 0, eq_seen = 0;
-  for (int j = 0; j < nb; ++j) {
-    int64_t lbase;
-    int c;
-    list(j, lbase, c);
-    for (int c0 = 0; c0 < c; c0 += kSelThreads) {
-      const int i = c0 + tid;
-      const bool in = i < c;
-      const float v = in ? args.cl_sc[lbase + i] : 0.0f;
-      const uint32_t key = order_key(v);
-      const bool g = in && key > kth;
-      const bool q = in && key == kth;
-      int qtot;
-      const int qbefore = block_excl_scan((int)q, s_tmp, qtot);
-      const bool keep = g || (q && eq_seen + qbefore < keep_eq);
-      int ktot;
-      const int kbefore = block_excl_scan((int)keep, s_tmp, ktot);
-      const int p = out + kbefore;
-      if (keep && p < K) {
-        oidx[p] = args.cl_idx[lbase + i];
-        if (osc) osc[p] = v;
+  for (int64_t s0 = 0; s0 < nslots; s0 += kIter * kB) {
+    float v[kIter][4];
+    uint32_t ok[kIter];
+    load(s0, v, ok);
+    int nq[kIter], qb[kIter], qt[kIter];
+    uint32_t eqm[kIter], gtm[kIter];
+#pragma unroll
+    for (int k = 0; k < kIter; ++k) {
+      eqm[k] = gtm[k] = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t key = order_key(v[k][u]);
+        if (ok[k] >> u & 1u) {
+          eqm[k] |= (uint32_t)(key == kth) << u;
+          gtm[k] |= (uint32_t)(key > kth) << u;
+        }
       }
-      out += ktot;
-      eq_seen += qtot;
+      nq[k] = __builtin_popcount(eqm[k]);
     }
+    block_excl_scan_n<kIter>(nq, qb, qt, s_tmpn);
+    int nk[kIter], kb[kIter], kt[kIter];
+    uint32_t keep[kIter];
+    int eq_base = eq_seen;
+#pragma unroll
+    for (int k = 0; k < kIter; ++k) {
+      int eq = eq_base + qb[k];
+      keep[k] = gtm[k];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (eqm[k] >> u & 1u) {
+          if (eq < keep_eq) keep[k] |= 1u << u;
+          ++eq;
+        }
+      }
+      nk[k] = __builtin_popcount(keep[k]);
+      eq_base += qt[k];
+    }
+    block_excl_scan_n<kIter>(nk, kb, kt, s_tmpn);
+    int base = out;
+#pragma unroll
+    for (int k = 0; k < kIter; ++k) {
+      if (keep[k]) {
+        // the key indices of this thread's kept slots: one 16-byte load
+        const int64_t s = s0 + k * kB + 4 * tid;
+        const u32x4 ix = *(const u32x4*)(args.cl_idx + row0 + s);
+        int p = base + kb[k];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (keep[k] >> u & 1u) {
+            if (p < K) {
+              oidx[p] = (int32_t)ix[u];
+              if (osc) osc[p] = v[k][u];
+            }
+            ++p;
+          }
+        }
+      }
+      base += kt[k];
+    }
+    out = base;
+    eq_seen = eq_base;
   }
 }
 
-constexpr int kShift = 32 - kDecHistBits;  // order key -> histogram bin
 
 constexpr int kSpanThreads = 256;
 constexpr int kSpanWaves = kSpanThreads / 64;
@@ -499,9 +598,12 @@ __global__ void __launch_bounds__(kSelThreads) decode_select_kernel(const Decode
   __shared__ int s_tmp[kSelWaves];
   __shared__ int s_res[4 + 2 * kSelWaves];
   __shared__ int s_chosen[kSelThreads];  // chosen candidates per span
+  __shared__ int s_tmpn[kIter * kSelWaves];
+  __shared__ int s_cnt[kSelThreads];  // list entries per span (exact path)
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   int64_t n = args.seq_lens[b];
+  if (args.skip_negative && n < 0) return;  // a row this launch does not own
   n = n < 0 ? 0 : (n > args.Nmax ? args.Nmax : n);
   const int K = args.K;
   int32_t* oidx = args.out_idx + (int64_t)b * K;
@@ -532,7 +634,7 @@ __global__ void __launch_bounds__(kSelThreads) decode_select_kernel(const Decode
   const int in_bin = s_res[2];   // keys of the row in bin b* (the histogram's count)
   __syncthreads();
   if (in_bin > kDecCandCap || nb > kSelThreads) {  // the same test decode_classify made
-    select_lists_exact(args, b, nb, oidx, osc, s_h, s_tmp, s_res);
+    select_lists_exact(args, b, nb, bstar, need, oidx, osc, s_h, s_tmp, s_res, s_tmpn, s_cnt);
     return;
   }
   // The candidates are the list entries in b*: a span's list may have dropped

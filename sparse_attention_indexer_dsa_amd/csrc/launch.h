@@ -57,6 +57,7 @@ struct DecodeArgs {
   // row_ks[b]); when null, row b reads kc + b*Nmax*d and k_scale + b*Nmax
   const uint8_t* const* row_kc;
   const float* const* row_ks;
+  int skip_negative;  // rows with seq_lens < 0 write nothing (else: clamped to 0)
   int B, H, d;
   int64_t Nmax;
   int K;
@@ -106,7 +107,9 @@ struct MtpArgs {
   int B, m, G, P, d;
   int64_t Nmax;
   const uint8_t** a_kc;  const float** a_ks;  int32_t* a_len;   // [B*m/G]
-  const uint8_t** r_kc;  const float** r_ks;  int32_t* r_len;   // [B*m]
+  const uint8_t** r_kc;  const float** r_ks;  // [B*m]
+  int32_t* r_len_bank;     // [B*m] refinement lengths of bank rows, -1 elsewhere
+  int32_t* r_len_fb;       // [B*m] lengths of fallback rows, -1 elsewhere
   const int32_t* bank;     // [B*m/G, P] ascending (anchor scan output)
   uint8_t* gk;             // [B*m/G, P+G-1, d] gathered keys
   float* gs;               // [B*m/G, P+G-1] their scales

@@ -13,7 +13,9 @@
 // sequence, decode.hip) run over "rows": the anchor scan has one row per
 // (sequence, group) over the sequence's cache; the refinement has one row per
 // query, over the gathered candidates of its group (bank rows) or over its
-// sequence's cache (fallback rows).  These kernels set those rows up, gather
+// sequence's cache (fallback rows).  Bank rows and fallback rows are refined
+// by two launches, each sized for its own row length (about P, or up to
+// Nmax); a row owned by the other launch has length -1 and is left alone.  These kernels set those rows up, gather
 // each bank group's candidate keys -- the bank, then the G-1 keys after the
 // anchor, already ascending -- into one contiguous run, and map refinement
 // output positions back to token indices (monotone, so the tie order of equal
@@ -56,11 +58,13 @@ __global__ void __launch_bounds__(kMtpThreads) mtp_plan_kernel(const MtpArgs a) 
       const int64_t grp = (int64_t)b * NGs + g;
       a.r_kc[idx] = a.gk + grp * cand * a.d;
       a.r_ks[idx] = a.gs + grp * cand;
-      a.r_len[idx] = a.P + i;
+      a.r_len_bank[idx] = a.P + i;
+      a.r_len_fb[idx] = -1;
     } else {
       a.r_kc[idx] = a.kc + (int64_t)b * a.Nmax * a.d;
       a.r_ks[idx] = a.ks + (int64_t)b * a.Nmax;
-      a.r_len[idx] = (int32_t)(N + r);
+      a.r_len_bank[idx] = -1;
+      a.r_len_fb[idx] = (int32_t)(N + r);
     }
   }
 }
