@@ -102,15 +102,16 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // itself: a wave waits for its own loads of a tile with s_waitcnt vmcnt and the
 // barrier that follows publishes the tile to the workgroup.  These loads have
 // no register results, so nothing is left in flight that the compiler could
-// reuse; m0 is declared clobbered, and one wait state separates its write
-// from the load (the SALU-to-LDS-DMA m0 hazard).
+// reuse.  The compiler writes m0 (an operand bound to it); the leading wait
+// state covers the SALU-write-of-m0 to LDS-DMA hazard, which the compiler
+// cannot see inside asm.
 __device__ __forceinline__ void dma_b128(const v4i& rsrc, uint32_t lds, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
 }
 __device__ __forceinline__ void dma_b32(const v4i& rsrc, uint32_t lds, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-               :: "s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
+  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
 }
 
 template <int DT>

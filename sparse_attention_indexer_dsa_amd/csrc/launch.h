@@ -78,7 +78,7 @@ struct DecodeArgs {
 };
 constexpr int kDecKeysPerPass = 768;  // keys one scan workgroup scores per loop trip
 constexpr int kDecMaxKpb = 16384;     // keys per scan workgroup at most (its LDS score stage)
-constexpr int kDecCandCap = 8192;     // threshold-bin candidates a row keeps in LDS
+constexpr int kDecCandCap = 16384;    // threshold-bin candidates a row keeps in LDS
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
