@@ -21,13 +21,21 @@
  *                                                          (Section 4.3, Eq. (14))
  *   grouping: consecutive, non-overlapping groups of G; incomplete groups use
  *           the original indexer                          (Section 4.3, prefill)
+ *   MTP:    windows of m queries; the window reuses banks only when its first
+ *           query sees more than P keys, then every group scans its anchor's
+ *           visible prefix (Section 4.3, MTP; Appendix A.2, Eq. (20)-(21))
+ *   pooled: the training-free group query is the mean of the group's own
+ *           queries and gates (Section 5 Abl. 2; Appendix B.3, B.4)
  *
  * Readings where the pages are silent (each one also listed in the design
  * notes): no extra scale factor in Eq. (1); s = t is visible; ties rank the
  * lower index first; -0 is ranked as +0; a row's selected indices are written
  * in ascending order and padded with -1 (scores with -inf); the bank is the
  * whole prefix when it is built for a prefix not longer than P (forced mode);
- * query i = t sees only the bank (the literal candidate set of Eq. (14)).
+ * query i = t sees only the bank (the literal candidate set of Eq. (14));
+ * the mean pooling averages the final indexer queries and gates head by head
+ * (fp32 sums in member order, times 1/G, the query rounded to bf16); query r
+ * of an MTP window whose first query sees N keys sits at position N - 1 + r.
  *
  * Precision: inputs are widened to double (bf16 and E4M3 widen exactly; an
  * E4M3 value times its fp32 scale is exact in double), every sum is a double
