@@ -598,3 +598,94 @@ def test_mtp_no_bank_is_the_original_indexer(oracle_lib):
         ri, rs = _mtp_dense_ref(_f64(t["q"][b]), kv, _f64(t["w"][b]), N, m, K)
         assert np.array_equal(mi[b * m:(b + 1) * m], ri)
         np.testing.assert_allclose(ms[b * m:(b + 1) * m], rs, rtol=1e-12)
+
+
+# ------------------------------------------------- calibration pins
+
+LAYERS = __file__.replace("test_oracle_pins.py", "golden/layer_configs.txt")
+
+
+def _table5c_128k():
+    """Printed joint speedups at 128K, Table 5(c): {(G, P): value}."""
+    return {(G, P): v[3] for panel, G, P, v in _table5() if panel == "c"}
+
+
+def _layer_tables():
+    tabs = {}
+    for line in open(LAYERS):
+        if line.startswith("#") or not line.strip():
+            continue
+        t, model, stat, G, P, cnt, layers = line.split()
+        ls = []
+        for part in layers.split(","):
+            lo, _, hi = part.partition("-")
+            ls += list(range(int(lo), int(hi or lo) + 1))
+        assert len(ls) == int(cnt), (t, G, P)
+        tabs.setdefault((int(t), model, stat), {}).update({layer: (int(G), int(P[:-1]) * 1024) for layer in ls})
+    return tabs
+
+
+def test_union_sizes_closed_forms(oracle_lib):
+    """Identical rows unite to K, disjoint rows to G*K, empty slots count for
+    nothing, a trailing incomplete group has no anchor; random rows against
+    Python set unions."""
+    import oracle.calib as calib
+    K, G = 6, 4
+    same = np.tile(np.arange(10, 10 + K), (G, 1))
+    disjoint = np.arange(G * K).reshape(G, K)
+    padded = np.array([[1, 2, 3, -1, -1, -1], [2, 3, 4, 5, -1, -1], [-1] * 6, [9, -1, -1, -1, -1, -1]])
+    idx = np.concatenate([same, disjoint, padded, same[:2]])
+    assert list(calib.union_sizes(idx, G)) == [K, G * K, 6]
+    rng = np.random.default_rng(3)
+    r = np.sort(rng.choice(50, size=(16, 8), replace=True), axis=1)
+    want = [len(set(r[g * 8:(g + 1) * 8].ravel().tolist())) for g in range(2)]
+    assert list(calib.union_sizes(r, 8)) == want
+
+
+def test_union_stats_and_overlap(oracle_lib):
+    import oracle.calib as calib
+    assert calib.union_stat(range(1, 11), "p90") == 9
+    assert calib.union_stat(range(1, 21), "p90") == 18
+    assert calib.union_stat([7], "p90") == 7
+    assert calib.union_stat([1, 2, 9], "max") == 9 and calib.union_stat([1, 2, 9], "mean") == 4
+    a = np.array([[1, 4, 7, -1], [0, 1, 2, 3]])
+    b = np.array([[4, 5, 7, 9], [-1, -1, -1, -1]])
+    assert list(calib.overlap_counts(a, b)) == [2, 0]
+
+
+def test_setting_selection_follows_table5(oracle_lib):
+    """Eq. (5) picks the largest printed 128K joint speedup of Table 5(c) among
+    the settings whose P covers the union statistic of their G."""
+    import oracle.calib as calib
+    s = _table5c_128k()
+    for stats in ({4: 100, 8: 100, 16: 100}, {4: 5000, 8: 9000, 16: 20000}, {4: 4096, 8: 8193, 16: 16385},
+                  {4: 30000, 8: 30000, 16: 30000}):
+        feasible = {k: v for k, v in s.items() if stats[k[0]] <= k[1]}
+        got = calib.select_setting(stats)
+        if not feasible:
+            assert got is None
+            continue
+        best = max(feasible.values())
+        assert s[got] == best, (stats, got, best)
+
+
+def test_layerwise_speedup_eq27(oracle_lib):
+    """A uniform assignment gives that setting's Table 5(c) value; a mixed one
+    sums scoring counts over layers (Eq. (27)), so it lies between its settings'
+    values and equals |layers| over the sum of reciprocal speedups; the printed
+    layer tables partition the 61 (DeepSeek-V3.2) and 78 (GLM-5.1) layers."""
+    import oracle.calib as calib
+    s = _table5c_128k()
+    for (G, P), v in s.items():
+        assert round(calib.layerwise_speedup([(G, P)] * 5, 131072), 2) == v
+    tabs = _layer_tables()
+    assert {k[1]: len(v) for k, v in tabs.items()} == {"deepseek-v3.2": 61, "glm-5.1": 78}
+    for key, layers in tabs.items():
+        assert sorted(layers) == list(range(len(layers))), key
+        settings = [layers[i] for i in range(len(layers))]
+        sp = calib.layerwise_speedup(settings, 131072)
+        vals = [s[x] for x in settings]
+        assert min(vals) - 0.01 <= sp <= max(vals) + 0.01
+        # counts add: base / speedup is each layer's reuse count (base is shared)
+        harm = len(vals) / sum(1.0 / v for v in vals)
+        assert abs(sp / harm - 1) < 0.01, (key, sp, harm)
