@@ -181,6 +181,41 @@ size_t indexer_mtp_workspace_size(int B, int64_t Nmax, int m, int H, int Hs, int
 int64_t indexer_mtp_pairs(const int32_t *prefix_lens, int B, int64_t Nmax, int m, int G, int P,
                           unsigned flags);
 
+/*
+ * Calibration statistics for layer-wise reuse: Section 4.1, Eq. (4)-(5);
+ * Appendix B.2 (capacity statistics), B.4 (coverage); Appendix A, Eq. (15)-(28)
+ * (scoring counts).  Index sets are the indexer's output rows: ascending
+ * token indices, then -1.
+ *
+ * indexer_union_sizes: out_union [T/G] int32 (device) gets, for each complete
+ * group of G consecutive rows of topk_idx [T, K] (device), the size of the
+ * union of their index sets (the inner term of Eq. (4)).  G <= 64, K <= 16384.
+ * indexer_topk_overlap: out_count [n] int32 (device) gets |A_i ∩ B_i| for the
+ * rows of a [n, K] and b [n, K] (device); coverage is out_count / K.
+ */
+int indexer_union_sizes(const int32_t *topk_idx, int64_t T, int K, int G, int32_t *out_union,
+                        void *stream);
+int indexer_topk_overlap(const int32_t *a, const int32_t *b, int64_t n, int K, int32_t *out_count,
+                         void *stream);
+/* Host: the capacity statistic of n union sizes (host memory): stat 0 = max,
+ * 1 = mean, 2 = nearest-rank 90th percentile.  -1 on bad arguments. */
+double indexer_union_stat(const int32_t *sizes, int64_t n, int stat);
+/* Host: the joint scoring speedup of prefill of L tokens plus R verification
+ * rounds of m queries whose first query sees L + (j-1) a keys (Eq. (24),
+ * (28), with Eq. (15)-(16), (19)-(21)).  -1 on bad arguments. */
+double indexer_speedup_joint(double L, int G, int P, int R, int m, double a);
+/* Host: Eq. (5).  stat_by_G [3] holds the union statistic for G = 4, 8, 16;
+ * writes the (G, P), P in {4096, 8192, 16384}, with the largest joint speedup
+ * among those with P >= the statistic of their G (the first such on equal
+ * speedups), or G = P = 0 when none is feasible.  m a multiple of 16. */
+int indexer_select_setting(const double *stat_by_G, double L, int R, int m, double a, int *out_G,
+                           int *out_P);
+/* Host: Eq. (26)-(27), joint: the speedup of a per-layer assignment (G[i],
+ * P[i]; G[i] = 0 is the original indexer), from scoring counts summed over
+ * the layers.  -1 on bad arguments. */
+double indexer_layerwise_speedup(const int *G, const int *P, int nlayers, double L, int R, int m,
+                                 double a);
+
 /* Message describing the calling thread's last non-OK return ("" if none). */
 const char *indexer_last_error(void);
 

@@ -24,7 +24,8 @@ from ._lib import (DSAIDX_BF16, DSAIDX_FORCE_BANK, DSAIDX_FP8_E4M3, DSAIDX_OK,  
 
 __all__ = ["indexer_prefill", "indexer_decode", "indexer_group_bank", "indexer_group_bank_pairs",
            "workspace_prefill", "workspace_decode", "workspace_group_bank", "indexer_mtp", "indexer_mtp_pairs",
-           "workspace_mtp", "FORCE_BANK", "POOL_MEAN", "NO_BANK", "lib",
+           "workspace_mtp", "union_sizes", "topk_overlap", "union_stat", "speedup_joint", "select_setting",
+           "layerwise_speedup", "FORCE_BANK", "POOL_MEAN", "NO_BANK", "lib",
            "LIB_PATH"]
 
 FORCE_BANK = DSAIDX_FORCE_BANK
@@ -195,3 +196,67 @@ def indexer_mtp(q, k_cache, k_scale, w, qbar, wbar, prefix_lens, G, P, topk=2048
                            _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
     _check(rc, "indexer_mtp")
     return out_idx, out_score, out_bank
+
+
+# ------------------------------------------------------------ calibration
+
+def union_sizes(topk_idx, G, out=None):
+    """Eq. (4): union size of the index sets of each complete group of G rows
+    of topk_idx [T, K] int32 (GPU); returns int32 [T // G] on the GPU."""
+    dev = _dev(topk_idx, out)
+    T, K = topk_idx.shape
+    if topk_idx.dtype != torch.int32:
+        raise ValueError("topk_idx must be int32")
+    if out is None:
+        out = torch.empty((T // G,), dtype=torch.int32, device=dev)
+    _check(lib().indexer_union_sizes(_ptr(topk_idx), T, K, G, _ptr(out), _stream(dev)), "indexer_union_sizes")
+    return out
+
+
+def topk_overlap(a, b, out=None):
+    """|A_i ∩ B_i| per row of two int32 [n, K] index-set arrays (GPU)."""
+    dev = _dev(a, b, out)
+    n, K = a.shape
+    if a.shape != b.shape or a.dtype != torch.int32 or b.dtype != torch.int32:
+        raise ValueError("a and b must be int32 of the same shape")
+    if out is None:
+        out = torch.empty((n,), dtype=torch.int32, device=dev)
+    _check(lib().indexer_topk_overlap(_ptr(a), _ptr(b), n, K, _ptr(out), _stream(dev)), "indexer_topk_overlap")
+    return out
+
+
+def union_stat(sizes, stat="max"):
+    """Capacity statistic of union sizes (host ints): 'max', 'mean' or 'p90'."""
+    import ctypes
+    import numpy as np
+    v = np.ascontiguousarray(np.asarray(sizes, dtype=np.int32))
+    r = lib().indexer_union_stat(v.ctypes.data_as(ctypes.c_void_p), len(v), {"max": 0, "mean": 1, "p90": 2}[stat])
+    if r < 0:
+        raise ValueError("indexer_union_stat: bad arguments")
+    return r
+
+
+def speedup_joint(L, G, P, R=32, m=16, a=8):
+    return lib().indexer_speedup_joint(float(L), G, P, R, m, float(a))
+
+
+def select_setting(stat_by_G, L=131072, R=32, m=16, a=8):
+    """Eq. (5): the feasible (G, P) with the largest joint speedup, or None."""
+    import ctypes
+    st = (ctypes.c_double * 3)(*[float(stat_by_G[g]) for g in (4, 8, 16)])
+    G, P = ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib().indexer_select_setting(st, float(L), R, m, float(a), ctypes.byref(G), ctypes.byref(P)),
+           "indexer_select_setting")
+    return None if G.value == 0 else (G.value, P.value)
+
+
+def layerwise_speedup(settings, L, R=32, m=16, a=8):
+    """Eq. (27), joint: settings is a list of (G, P) or None per layer."""
+    import ctypes
+    n = len(settings)
+    Gs = (ctypes.c_int * n)(*[0 if s is None else s[0] for s in settings])
+    Ps = (ctypes.c_int * n)(*[0 if s is None else s[1] for s in settings])
+    r = lib().indexer_layerwise_speedup(Gs, Ps, n, float(L), R, m, float(a))
+    if r < 0:
+        raise ValueError("indexer_layerwise_speedup: bad arguments")
+    return r

@@ -20,6 +20,7 @@ DSAIDX_NO_BANK = 8
 
 # exported symbol -> (restype, argtypes)
 _P, _I, _I64, _U, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint, ctypes.c_size_t
+_D = ctypes.c_double
 SIGNATURES = {
     "indexer_prefill": (_I, [_P, _P, _P, _P, _P, _I, _I64, _I64, _I, _I, _I64, _I, _P, _P, _P, _SZ, _P]),
     "indexer_prefill_workspace_size": (_SZ, [_I64, _I64, _I, _I, _I, _I]),
@@ -33,6 +34,12 @@ SIGNATURES = {
                          _SZ, _P]),
     "indexer_mtp_workspace_size": (_SZ, [_I, _I64, _I, _I, _I, _I, _I, _I, _I, _U]),
     "indexer_mtp_pairs": (_I64, [_P, _I, _I64, _I, _I, _I, _U]),
+    "indexer_union_sizes": (_I, [_P, _I64, _I, _I, _P, _P]),
+    "indexer_topk_overlap": (_I, [_P, _P, _I64, _I, _P, _P]),
+    "indexer_union_stat": (_D, [_P, _I64, _I]),
+    "indexer_speedup_joint": (_D, [_D, _I, _I, _I, _I, _D]),
+    "indexer_select_setting": (_I, [_P, _D, _I, _I, _D, _P, _P]),
+    "indexer_layerwise_speedup": (_D, [_P, _P, _I, _D, _I, _I, _D]),
     "indexer_last_error": (ctypes.c_char_p, []),
 }
 

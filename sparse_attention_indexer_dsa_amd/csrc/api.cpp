@@ -7,6 +7,9 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
+#include <algorithm>
+#include <cmath>
 
 #include "dsa_indexer.h"
 #include "launch.h"
@@ -680,6 +683,120 @@ int indexer_mtp(const void* q, const uint8_t* k_cache, const float* k_scale, con
   e = launch_mtp_map(t, st);
   if (e != hipSuccess) return hip_fail(e, "indexer_mtp map launch");
   return ok();
+}
+
+// --------------------------------------------------------- calibration
+
+int indexer_union_sizes(const int32_t* topk_idx, int64_t T, int K, int G, int32_t* out_union,
+                        void* stream) {
+  if (T < 0 || K < 1 || G < 1)
+    return fail(DSAIDX_ERR_INVALID_ARG, "bad size (T=%lld K=%d G=%d)", (long long)T, K, G);
+  if (G > 64) return fail(DSAIDX_ERR_UNSUPPORTED, "group size G = %d above 64", G);
+  if (K > kMaxBank) return fail(DSAIDX_ERR_UNSUPPORTED, "K = %d above %d", K, kMaxBank);
+  const int64_t groups = T / G;
+  if (groups > INT32_MAX) return fail(DSAIDX_ERR_UNSUPPORTED, "too many groups");
+  if (groups > 0 && (!topk_idx || !out_union))
+    return fail(DSAIDX_ERR_INVALID_ARG, "null topk_idx or out_union");
+  if (((uintptr_t)topk_idx & 3u) || ((uintptr_t)out_union & 3u))
+    return fail(DSAIDX_ERR_INVALID_ARG, "index arrays must be 4-byte aligned");
+  const hipError_t e = launch_union_sizes(topk_idx, groups, K, G, out_union, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "indexer_union_sizes launch");
+  return ok();
+}
+
+int indexer_topk_overlap(const int32_t* a, const int32_t* b, int64_t n, int K, int32_t* out_count,
+                         void* stream) {
+  if (n < 0 || K < 1) return fail(DSAIDX_ERR_INVALID_ARG, "bad size (n=%lld K=%d)", (long long)n, K);
+  if (K > kMaxBank) return fail(DSAIDX_ERR_UNSUPPORTED, "K = %d above %d", K, kMaxBank);
+  if (n > INT32_MAX) return fail(DSAIDX_ERR_UNSUPPORTED, "too many rows");
+  if (n > 0 && (!a || !b || !out_count)) return fail(DSAIDX_ERR_INVALID_ARG, "null a, b or out_count");
+  if (((uintptr_t)a & 3u) || ((uintptr_t)b & 3u) || ((uintptr_t)out_count & 3u))
+    return fail(DSAIDX_ERR_INVALID_ARG, "index arrays must be 4-byte aligned");
+  const hipError_t e = launch_topk_overlap(a, b, n, K, out_count, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "indexer_topk_overlap launch");
+  return ok();
+}
+
+double indexer_union_stat(const int32_t* sizes, int64_t n, int stat) {
+  if (n <= 0 || !sizes || stat < 0 || stat > 2) return -1.0;
+  if (stat == 1) {
+    double sum = 0.0;
+    for (int64_t i = 0; i < n; ++i) sum += sizes[i];
+    return sum / (double)n;
+  }
+  std::vector<int32_t> v(sizes, sizes + n);
+  // max, or the nearest-rank 90th percentile: the ceil(0.9 n)-th smallest
+  const int64_t k = stat == 0 ? n - 1 : (int64_t)std::ceil(0.9 * (double)n) - 1;
+  std::nth_element(v.begin(), v.begin() + k, v.end());
+  return (double)v[k];
+}
+
+// Scoring counts of Appendix A (one score = one unit, whatever the head count)
+static double cost_pre_base(double L) { return 0.5 * L * L; }  // Eq. (15)
+static double cost_pre_reuse(double L, int G, int P) {           // Eq. (19)
+  if (L <= P) return cost_pre_base(L);
+  return 0.5 * (double)P * P + (L * L - (double)P * P) / (2.0 * G) + (P + 0.5 * (G - 1)) * (L - P);
+}
+static double cost_mtp_base(double N, int m) { return m * N + 0.5 * m * (m - 1); }  // Eq. (16)
+static double cost_mtp_reuse(double N, int G, int P, int m) {                       // Eq. (20)-(21)
+  if (N <= P) return cost_mtp_base(N, m);
+  double c = 0.0;
+  for (int b = 0; b < m / G; ++b) c += N + (double)b * G + (double)G * P + 0.5 * G * (G - 1);
+  return c;
+}
+// prefill of L tokens plus R verification rounds whose first query sees
+// L + (j-1) a keys (Eq. (28)); G == 0 is the original indexer
+static void cost_joint(double L, int G, int P, int R, int m, double a, double& base, double& reuse) {
+  base = cost_pre_base(L);
+  reuse = G ? cost_pre_reuse(L, G, P) : cost_pre_base(L);
+  for (int j = 0; j < R; ++j) {
+    const double N = L + j * a;
+    base += cost_mtp_base(N, m);
+    reuse += G ? cost_mtp_reuse(N, G, P, m) : cost_mtp_base(N, m);
+  }
+}
+
+double indexer_speedup_joint(double L, int G, int P, int R, int m, double a) {
+  if (L <= 0 || G < 1 || P < 1 || R < 0 || m < 1 || m % G || a < 0) return -1.0;
+  double base, reuse;
+  cost_joint(L, G, P, R, m, a, base, reuse);
+  return base / reuse;
+}
+
+int indexer_select_setting(const double* stat_by_G, double L, int R, int m, double a, int* out_G,
+                           int* out_P) {
+  if (!stat_by_G || !out_G || !out_P) return fail(DSAIDX_ERR_INVALID_ARG, "null argument");
+  if (L <= 0 || R < 0 || m < 16 || m % 16 || a < 0)
+    return fail(DSAIDX_ERR_INVALID_ARG, "bad workload (L, R, m, a)");
+  static const int kG[3] = {4, 8, 16}, kP[3] = {4096, 8192, 16384};
+  double best = -1.0;
+  *out_G = 0;
+  *out_P = 0;
+  for (int gi = 0; gi < 3; ++gi)
+    for (int pi = 0; pi < 3; ++pi) {
+      if (stat_by_G[gi] > kP[pi]) continue;  // Eq. (5): the bank must hold the statistic
+      const double sp = indexer_speedup_joint(L, kG[gi], kP[pi], R, m, a);
+      if (sp > best) {
+        best = sp;
+        *out_G = kG[gi];
+        *out_P = kP[pi];
+      }
+    }
+  return ok();
+}
+
+double indexer_layerwise_speedup(const int* G, const int* P, int nlayers, double L, int R, int m,
+                                 double a) {
+  if (nlayers <= 0 || !G || !P || L <= 0 || R < 0 || m < 1 || a < 0) return -1.0;
+  double tb = 0.0, tr = 0.0;  // Eq. (27): counts summed over layers
+  for (int i = 0; i < nlayers; ++i) {
+    if (G[i] < 0 || (G[i] > 0 && (P[i] < 1 || m % G[i]))) return -1.0;
+    double base, reuse;
+    cost_joint(L, G[i], P[i], R, m, a, base, reuse);
+    tb += base;
+    tr += reuse;
+  }
+  return tb / tr;
 }
 
 }  // extern "C"

@@ -121,6 +121,13 @@ hipError_t launch_mtp_plan(const MtpArgs& a, hipStream_t stream);
 hipError_t launch_mtp_gather(const MtpArgs& a, hipStream_t stream);
 hipError_t launch_mtp_map(const MtpArgs& a, hipStream_t stream);
 
+// Calibration statistics over top-K index sets [rows, K] (ascending, -1 padded):
+// the union size of each complete group of G rows, and per-row overlaps.
+hipError_t launch_union_sizes(const int32_t* idx, int64_t groups, int K, int G, int32_t* out,
+                              hipStream_t stream);
+hipError_t launch_topk_overlap(const int32_t* a, const int32_t* b, int64_t n, int K, int32_t* out,
+                               hipStream_t stream);
+
 // Fill n int32 values with v (a kernel, not a memset node).
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t stream);
 

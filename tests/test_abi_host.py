@@ -35,7 +35,7 @@ A = P(1 << 20)  # 16-byte aligned
 def test_header_symbols_exported(L):
     names = re.findall(r"^\s*(?:[\w\s\*]+?)\b(indexer_\w+)\s*\(", open(HEADER).read(), re.M)
     names = sorted(set(names))
-    assert len(names) == 11, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -171,3 +171,29 @@ def test_mtp_pairs_match_oracle(L):
     bad = np.array([0, 200000], np.int32)
     got = L.indexer_mtp_pairs(bad.ctypes.data_as(ctypes.c_void_p), 2, 131072, 16, 4, 2048, 0)
     assert got == oracle.mtp_pairs([1, 131057], 16, 4, 2048)
+
+
+
+def test_calibration_host_functions_match_oracle(L):
+    """The library's scoring-count model, capacity statistics, Eq. (5)
+    selection and Eq. (27) aggregation against the oracle's and the printed
+    Table 5(c)."""
+    import oracle.calib as calib
+    import sparse_attention_indexer_dsa_amd as dsa
+    golden = os.path.join(ROOT, "tests", "golden", "table5_speedups.txt")
+    for line in open(golden):
+        if line.startswith("#") or not line.strip() or not line.startswith("c"):
+            continue
+        _, G, P, *vals = line.split()
+        for Lk, v in zip((16384, 32768, 65536, 131072), vals):
+            got = dsa.speedup_joint(Lk, int(G), int(P[:-1]) * 1024)
+            assert round(got, 2) == float(v), (G, P, Lk, got, v)
+    rng = np.random.default_rng(5)
+    for _ in range(20):
+        stats = {g: float(rng.integers(1000, 40000)) for g in (4, 8, 16)}
+        assert dsa.select_setting(stats) == calib.select_setting(stats), stats
+        settings = [calib.SETTINGS[i] if i < 9 else None for i in rng.integers(0, 10, size=7)]
+        assert abs(dsa.layerwise_speedup(settings, 65536) / calib.layerwise_speedup(settings, 65536) - 1) < 1e-12
+    sizes = rng.integers(0, 30000, size=101)
+    for st in ("max", "mean", "p90"):
+        assert dsa.union_stat(sizes, st) == calib.union_stat(sizes, st)

@@ -490,3 +490,38 @@ def test_mtp_no_bank_is_dense(dsa):
                   prefix_lens=[3985, 100, 2000])
     _, _, gb = _mtp_check(dsa, wl, flags=dsa.NO_BANK)
     assert (gb == -1).all()
+
+
+
+# ------------------------------------------------------- calibration kernels
+
+def test_union_sizes_and_overlap(dsa):
+    """Union sizes of groups of G rows and per-row overlaps against the
+    oracle, on random sorted index sets with -1 padding, on sets past the
+    first 2^18 tokens (a second bitmap pass), and on real indexer output
+    (dense top-K vs the group-bank top-K of the same queries)."""
+    import oracle.calib as calib
+    rng = np.random.default_rng(7)
+    T, K = 96, 300
+    idx = np.full((T, K), -1, np.int32)
+    for r in range(T):
+        n = rng.integers(0, K + 1)
+        hi = 600000 if r % 3 == 0 else 5000
+        idx[r, :n] = np.sort(rng.choice(hi, size=n, replace=False))
+    gi = torch.from_numpy(idx).cuda()
+    for G in (4, 8, 16):
+        got = dsa.union_sizes(gi, G).cpu().numpy()
+        assert np.array_equal(got, calib.union_sizes(idx, G)), G
+    other = np.roll(idx, 1, axis=0)
+    got = dsa.topk_overlap(gi, torch.from_numpy(other).cuda()).cpu().numpy()
+    assert np.array_equal(got, calib.overlap_counts(idx, other))
+    wl = make_group_bank(T=2000, H=16, Hs=8, d=64, topk=64, G=8, P=256, dtype="bf16", dist="normal", seed=70)
+    t = {k: v.cuda() for k, v in wl.tensors.items()}
+    di, _ = dsa.indexer_prefill(t["q"], t["k"], t["w"], 0, 64)
+    bi, _, _ = dsa.indexer_group_bank(t["q"], t["k"], t["w"], t["qbar"], t["wbar"], 0, 8, 256, 64)
+    u = dsa.union_sizes(di, 8).cpu().numpy()
+    assert np.array_equal(u, calib.union_sizes(di.cpu().numpy(), 8))
+    cov = dsa.topk_overlap(di, bi).cpu().numpy()
+    assert np.array_equal(cov, calib.overlap_counts(di.cpu().numpy(), bi.cpu().numpy()))
+    # rows before the first bank group use the original indexer: full coverage
+    assert np.array_equal(cov[:256], (di[:256] >= 0).sum(1).cpu().numpy())
