@@ -14,7 +14,7 @@ bounded sample of the same inputs.
 Inputs are generated on the GPU before timing (resident in HBM); outputs,
 workspace and streams are allocated before the timed region.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--adindex] [--mtp]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--adindex] [--mtp] [--calib]
 """
 from __future__ import annotations
 
@@ -356,6 +356,36 @@ def bench_mtp(dsa, args, log):
     return res
 
 
+# ------------------------------------------------------------ calibration
+
+def bench_calib(dsa, args, log):
+    """Calibration statistics over a 128K-token layer's reference top-2048 sets:
+    Eq. (4) union sizes for G = 4, 8, 16 and per-row overlaps.  HBM-bound: one
+    read of the [T, K] int32 index sets (two for the overlap)."""
+    T, K = 131072, 2048
+    log("generating sorted index sets [131072, 2048] on the GPU")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(args.seed)
+    idx = torch.randint(0, T, (T, K), generator=g, device="cuda", dtype=torch.int32).sort(dim=1).values
+    other = idx.roll(1, 0).contiguous()
+    res = dict(workload=f"calibration statistics: index sets [{T}, {K}] int32", runs=[])
+    bytes_once = T * K * 4
+    for name, fn, nbytes in ([(f"union_sizes G={G}", (lambda G=G: dsa.union_sizes(idx, G)), bytes_once)
+                              for G in (4, 8, 16)] + [("topk_overlap", lambda: dsa.topk_overlap(idx, other),
+                                                       2 * bytes_once)]):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        res["runs"].append(dict(name=name, ms=ms, gbs=nbytes / (ms * 1e-3) / 1e9,
+                                frac_of_hbm=nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS))
+        log(f"{name}: {ms:.3f} ms")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -368,6 +398,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--adindex", action="store_true", help="also time the ADIndex group-bank workload")
     ap.add_argument("--mtp", action="store_true", help="also time MTP verification windows at 256K")
+    ap.add_argument("--calib", action="store_true", help="also time the calibration statistics kernels")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only copy BYTES device-to-device 5 times (calibrates HBM byte counters)")
@@ -425,6 +456,8 @@ def main():
         line["adindex"] = bench_adindex(dsa, args, log)
     if args.mtp:
         line["mtp"] = bench_mtp(dsa, args, log)
+    if args.calib:
+        line["calib"] = bench_calib(dsa, args, log)
     print(json.dumps(line), flush=True)
 
 

@@ -189,9 +189,11 @@ int64_t indexer_mtp_pairs(const int32_t *prefix_lens, int B, int64_t Nmax, int m
  *
  * indexer_union_sizes: out_union [T/G] int32 (device) gets, for each complete
  * group of G consecutive rows of topk_idx [T, K] (device), the size of the
- * union of their index sets (the inner term of Eq. (4)).  G <= 64, K <= 16384.
+ * union of their index sets (the inner term of Eq. (4)).  G <= 64, K <= 16384
+ * and a multiple of 4, topk_idx 16-byte aligned.
  * indexer_topk_overlap: out_count [n] int32 (device) gets |A_i ∩ B_i| for the
- * rows of a [n, K] and b [n, K] (device); coverage is out_count / K.
+ * rows of a [n, K] and b [n, K] (device); coverage is out_count / K.  K a
+ * multiple of 4 and at most 16384; a 16-byte aligned.
  */
 int indexer_union_sizes(const int32_t *topk_idx, int64_t T, int K, int G, int32_t *out_union,
                         void *stream);

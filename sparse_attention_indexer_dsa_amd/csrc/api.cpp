@@ -697,8 +697,9 @@ int indexer_union_sizes(const int32_t* topk_idx, int64_t T, int K, int G, int32_
   if (groups > INT32_MAX) return fail(DSAIDX_ERR_UNSUPPORTED, "too many groups");
   if (groups > 0 && (!topk_idx || !out_union))
     return fail(DSAIDX_ERR_INVALID_ARG, "null topk_idx or out_union");
-  if (((uintptr_t)topk_idx & 3u) || ((uintptr_t)out_union & 3u))
-    return fail(DSAIDX_ERR_INVALID_ARG, "index arrays must be 4-byte aligned");
+  if (((uintptr_t)topk_idx & 15u) || ((uintptr_t)out_union & 3u))
+    return fail(DSAIDX_ERR_INVALID_ARG, "topk_idx must be 16-byte aligned, out_union 4-byte");
+  if (K % 4) return fail(DSAIDX_ERR_UNSUPPORTED, "K = %d is not a multiple of 4", K);
   const hipError_t e = launch_union_sizes(topk_idx, groups, K, G, out_union, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "indexer_union_sizes launch");
   return ok();
@@ -710,8 +711,9 @@ int indexer_topk_overlap(const int32_t* a, const int32_t* b, int64_t n, int K, i
   if (K > kMaxBank) return fail(DSAIDX_ERR_UNSUPPORTED, "K = %d above %d", K, kMaxBank);
   if (n > INT32_MAX) return fail(DSAIDX_ERR_UNSUPPORTED, "too many rows");
   if (n > 0 && (!a || !b || !out_count)) return fail(DSAIDX_ERR_INVALID_ARG, "null a, b or out_count");
-  if (((uintptr_t)a & 3u) || ((uintptr_t)b & 3u) || ((uintptr_t)out_count & 3u))
-    return fail(DSAIDX_ERR_INVALID_ARG, "index arrays must be 4-byte aligned");
+  if (((uintptr_t)a & 15u) || ((uintptr_t)b & 3u) || ((uintptr_t)out_count & 3u))
+    return fail(DSAIDX_ERR_INVALID_ARG, "a must be 16-byte aligned, b and out_count 4-byte");
+  if (K % 4) return fail(DSAIDX_ERR_UNSUPPORTED, "K = %d is not a multiple of 4", K);
   const hipError_t e = launch_topk_overlap(a, b, n, K, out_count, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "indexer_topk_overlap launch");
   return ok();

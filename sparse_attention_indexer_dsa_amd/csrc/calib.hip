@@ -41,7 +41,10 @@ __global__ void __launch_bounds__(kCalThreads) union_kernel(const int32_t* idx, 
   const int32_t* rows = idx + g * G * (int64_t)K;
   const int n = G * K;
   int hi = -1;  // the largest index of the group: passes needed
-  for (int e = tid; e < n; e += kCalThreads) hi = max(hi, rows[e]);
+  for (int e = 4 * tid; e < n; e += 4 * kCalThreads) {
+    const int4 q = *reinterpret_cast<const int4*>(rows + e);
+    hi = max(max(hi, max(q.x, q.y)), max(q.z, q.w));
+  }
   __shared__ int s_hi;
   if (tid == 0) s_hi = -1;
   __syncthreads();
@@ -50,14 +53,19 @@ __global__ void __launch_bounds__(kCalThreads) union_kernel(const int32_t* idx, 
   hi = s_hi;
   int count = 0;
   for (int base = 0; base <= hi; base += kBitmapTokens) {
-    for (int w = tid; w < kBitmapWords; w += kCalThreads) s_bits[w] = 0u;
+    // only the words up to the group's largest index are touched
+    const int words = min(kBitmapWords, (hi - base) / 32 + 1);
+    for (int w = tid; w < words; w += kCalThreads) s_bits[w] = 0u;
     __syncthreads();
-    for (int e = tid; e < n; e += kCalThreads) {
-      const int v = rows[e] - base;
-      if (v >= 0 && v < kBitmapTokens) atomicOr(&s_bits[v >> 5], 1u << (v & 31));
+    for (int e = 4 * tid; e < n; e += 4 * kCalThreads) {  // K*G is a multiple of 4
+      const int4 q = *reinterpret_cast<const int4*>(rows + e);
+      const int v[4] = {q.x - base, q.y - base, q.z - base, q.w - base};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (v[u] >= 0 && v[u] < kBitmapTokens) atomicOr(&s_bits[v[u] >> 5], 1u << (v[u] & 31));
     }
     __syncthreads();
-    for (int w = tid; w < kBitmapWords; w += kCalThreads) count += __popc(s_bits[w]);
+    for (int w = tid; w < words; w += kCalThreads) count += __popc(s_bits[w]);
     __syncthreads();
   }
   const int total = block_sum(count, s_tmp);
@@ -79,17 +87,25 @@ __global__ void __launch_bounds__(kCalThreads) overlap_kernel(const int32_t* a, 
     nb += v >= 0;
   }
   nb = block_sum(nb, s_tmp);  // also orders the LDS writes before the reads
+  // each thread merges a run of 4 consecutive entries of a (ascending) with
+  // b: one binary search for the run's first entry, then a linear walk
   int hits = 0;
-  for (int e = tid; e < K; e += kCalThreads) {
-    const int32_t v = ar[e];
-    if (v < 0) continue;
+  for (int e = 4 * tid; e < K; e += 4 * kCalThreads) {
+    const int4 q = *reinterpret_cast<const int4*>(ar + e);
+    const int32_t v[4] = {q.x, q.y, q.z, q.w};
+    if (v[0] < 0) continue;
     int lo = 0, hi = nb;  // valid entries of b are s_b[0, nb), ascending
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
-      if (s_b[mid] < v) lo = mid + 1;
+      if (s_b[mid] < v[0]) lo = mid + 1;
       else hi = mid;
     }
-    hits += lo < nb && s_b[lo] == v;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (v[u] < 0) break;
+      while (lo < nb && s_b[lo] < v[u]) ++lo;
+      hits += lo < nb && s_b[lo] == v[u];
+    }
   }
   const int total = block_sum(hits, s_tmp);
   if (tid == 0) out[r] = total;
