@@ -689,3 +689,74 @@ def test_layerwise_speedup_eq27(oracle_lib):
         # counts add: base / speedup is each layer's reuse count (base is shared)
         harm = len(vals) / sum(1.0 / v for v in vals)
         assert abs(sp / harm - 1) < 0.01, (key, sp, harm)
+
+
+# ------------------------------------------- group query construction pins
+
+def _gq_inputs(Tq=48, dc=32, dh=40, Hs=4, d=16, seed=40):
+    g = torch.Generator().manual_seed(seed)
+    c = torch.randn(Tq, dc, generator=g).to(torch.bfloat16)
+    h = torch.randn(Tq, dh, generator=g).to(torch.bfloat16)
+    wq = (torch.randn(Hs * d, dc, generator=g) / dc ** 0.5).to(torch.bfloat16)
+    wg = (torch.randn(Hs, dh, generator=g) / dh ** 0.5).to(torch.bfloat16)
+    return c, h, wq, wg
+
+
+def test_group_query_mean_pooling_init(oracle_lib):
+    """W_pool = [0, 0, I] (the initialisation of Appendix C.3) makes cbar the
+    group mean; with no rotary part, qbar is W_Q times that mean and the gates
+    are the sigmoid of W_G times the mean hidden state."""
+    from oracle import group_query as gq
+    c, h, wq, wg = _gq_inputs()
+    dc, G, Hs, d = 32, 8, 4, 16
+    wp = np.concatenate([np.zeros((dc, 2 * dc)), np.eye(dc)], 1)
+    q, w = gq.group_query(c, h, wp, wq, wg, G, Hs, d, rope_dim=0)
+    cm = _bf16(c.double().reshape(6, G, dc).mean(1)).double().numpy()          # bf16 operand, twice
+    want = (cm @ wq.double().numpy().T).reshape(6, Hs, d)
+    np.testing.assert_allclose(q, _bf16(want).double().numpy(), rtol=0, atol=0)
+    hm = _bf16(h.double().reshape(6, G, -1).mean(1)).double().numpy()
+    np.testing.assert_allclose(w, 1 / (1 + np.exp(-(hm @ wg.double().numpy().T))), rtol=1e-12)
+
+
+def test_group_query_pool_order_and_single_row(oracle_lib):
+    """The three pooled blocks are max, min, mean in that order; a group of one
+    row pools to the row three times."""
+    from oracle import group_query as gq
+    c = torch.tensor([[1.0, -2.0], [3.0, 5.0], [-1.0, 0.5], [0.0, 0.0]])
+    pc, ph = gq.pool(c, c, 2)
+    assert np.array_equal(pc, [[3, 5, 1, -2, 2, 1.5], [0, 0.5, -1, 0, -0.5, 0.25]])
+    pc1, _ = gq.pool(c, c, 1)
+    assert np.array_equal(pc1[:, :2], pc1[:, 2:4]) and np.array_equal(pc1[:, 2:4], pc1[:, 4:])
+
+
+def test_group_query_rope(oracle_lib):
+    """Rotary embedding: identity at position 0 and past rope_dim; each pair
+    keeps its length; the pair (0, rope_dim/2) turns by the anchor position
+    itself (frequency 1) and the two heads of a group turn alike."""
+    from oracle import group_query as gq
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((3, 2, 16))
+    pos = np.array([0, 5, 40])
+    y = gq.rope(x, pos, 8, 10000.0)
+    assert np.array_equal(y[0], x[0]) and np.array_equal(y[:, :, 8:], x[:, :, 8:])
+    for i in range(4):
+        np.testing.assert_allclose(np.hypot(y[..., i], y[..., i + 4]), np.hypot(x[..., i], x[..., i + 4]))
+    a, b = x[2, 1, 0], x[2, 1, 4]
+    np.testing.assert_allclose([y[2, 1, 0], y[2, 1, 4]], [a * math.cos(40) - b * math.sin(40),
+                                                          b * math.cos(40) + a * math.sin(40)])
+
+
+def test_group_query_anchor_positions_and_tail(oracle_lib):
+    """Group g's query is rotated at q_pos0 + gG (shifting q_pos0 by G shifts
+    the result by one group); an incomplete last group gets zeros."""
+    from oracle import group_query as gq
+    c, h, wq, wg = _gq_inputs(Tq=52)
+    rng = np.random.default_rng(4)
+    wp = rng.standard_normal((32, 96)) / 10
+    q0, w0 = gq.group_query(c, h, wp, wq, wg, 8, 4, 16, q_pos0=16, rope_dim=8)
+    q1, _ = gq.group_query(c[8:], h[8:], wp, wq, wg, 8, 4, 16, q_pos0=24, rope_dim=8)
+    np.testing.assert_allclose(q0[1:6], q1[:5])
+    assert q0.shape == (7, 4, 16) and (q0[6] == 0).all() and (w0[6] == 0).all()
+    # a different anchor position changes the rotated part only
+    q2, _ = gq.group_query(c, h, wp, wq, wg, 8, 4, 16, q_pos0=17, rope_dim=8)
+    assert np.array_equal(q0[:6, :, 8:], q2[:6, :, 8:]) and not np.array_equal(q0[:6, :, :8], q2[:6, :, :8])
