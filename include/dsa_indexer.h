@@ -182,6 +182,29 @@ int64_t indexer_mtp_pairs(const int32_t *prefix_lens, int B, int64_t Nmax, int m
                           unsigned flags);
 
 /*
+ * The group indexer's query and gates: Section 4.2, Eq. (6)-(7) and Appendix
+ * C.3.  For each complete group of G consecutive query rows (anchor position
+ * t = q_pos0 + gG):
+ *   cbar = W_pool [max c; min c; mean c] (element-wise over the group's rows),
+ *   hbar = mean h,  qbar_j = RoPE_t([W_Q cbar]_j),  wbar_j = sigmoid([W_G hbar]_j).
+ *   c       [Tq, dc] bf16: the (normalized) query latents
+ *   h       [Tq, dh] bf16: the (normalized) hidden states
+ *   w_pool  [dc, 3*dc] bf16;  w_q [Hs*d, dc] bf16;  w_g [Hs, dh] bf16
+ *   qbar    [ceil(Tq/G), Hs, d] bf16 out;  wbar [ceil(Tq/G), Hs] fp32 out
+ *           (the row of an incomplete last group is zero)
+ * The rotary embedding turns the pairs (i, i + rope_dim/2), i < rope_dim/2, of
+ * each head by t * rope_base^(-2i/rope_dim) (rope_dim even, <= d; 0: none).
+ * Pooled values and cbar are bf16 (the products' operands; fp32 sums and
+ * accumulation).  G in {4, 8, 16}; dc, dh, d multiples of 16; Hs <= 64.
+ * These feed indexer_group_bank / indexer_mtp as qbar, wbar.
+ */
+int indexer_group_query(const void *c, const void *h, const void *w_pool, const void *w_q,
+                        const void *w_g, int64_t Tq, int dc, int dh, int Hs, int d, int G,
+                        int64_t q_pos0, int rope_dim, float rope_base, void *qbar, float *wbar,
+                        void *ws, size_t ws_bytes, void *stream);
+size_t indexer_group_query_workspace_size(int64_t Tq, int dc, int dh, int Hs, int d, int G);
+
+/*
  * Calibration statistics for layer-wise reuse: Section 4.1, Eq. (4)-(5);
  * Appendix B.2 (capacity statistics), B.4 (coverage); Appendix A, Eq. (15)-(28)
  * (scoring counts).  Index sets are the indexer's output rows: ascending

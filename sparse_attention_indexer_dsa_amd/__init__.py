@@ -24,7 +24,7 @@ from ._lib import (DSAIDX_BF16, DSAIDX_FORCE_BANK, DSAIDX_FP8_E4M3, DSAIDX_OK,  
 
 __all__ = ["indexer_prefill", "indexer_decode", "indexer_group_bank", "indexer_group_bank_pairs",
            "workspace_prefill", "workspace_decode", "workspace_group_bank", "indexer_mtp", "indexer_mtp_pairs",
-           "workspace_mtp", "union_sizes", "topk_overlap", "union_stat", "speedup_joint", "select_setting",
+           "workspace_mtp", "indexer_group_query", "union_sizes", "topk_overlap", "union_stat", "speedup_joint", "select_setting",
            "layerwise_speedup", "FORCE_BANK", "POOL_MEAN", "NO_BANK", "lib",
            "LIB_PATH"]
 
@@ -260,3 +260,29 @@ def layerwise_speedup(settings, L, R=32, m=16, a=8):
     if r < 0:
         raise ValueError("indexer_layerwise_speedup: bad arguments")
     return r
+
+
+# ------------------------------------------------- group query (Eq. (6)-(7))
+
+def indexer_group_query(c, h, w_pool, w_q, w_g, G, Hs, d, q_pos0=0, rope_dim=64, rope_base=10000.0,
+                        qbar=None, wbar=None, ws=None):
+    """The group indexer's query and gates from the query latents c [Tq, dc]
+    and hidden states h [Tq, dh] (bf16, GPU): returns (qbar bf16
+    [ceil(Tq/G), Hs, d], wbar fp32 [ceil(Tq/G), Hs])."""
+    dev = _dev(c, h, w_pool, w_q, w_g, qbar, wbar, ws)
+    Tq, dc = c.shape
+    dh = h.shape[1]
+    for t in (c, h, w_pool, w_q, w_g):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("group query inputs and weights are bf16")
+    NG = -(-Tq // G)
+    if qbar is None:
+        qbar = torch.empty((NG, Hs, d), dtype=torch.bfloat16, device=dev)
+    if wbar is None:
+        wbar = torch.empty((NG, Hs), dtype=torch.float32, device=dev)
+    ws = _ws(lib().indexer_group_query_workspace_size(Tq, dc, dh, Hs, d, G), dev, ws)
+    rc = lib().indexer_group_query(_ptr(c), _ptr(h), _ptr(w_pool), _ptr(w_q), _ptr(w_g), Tq, dc, dh, Hs, d, G, q_pos0,
+                                   rope_dim, float(rope_base), _ptr(qbar), _ptr(wbar), _ptr(ws),
+                                   0 if ws is None else ws.numel(), _stream(dev))
+    _check(rc, "indexer_group_query")
+    return qbar, wbar

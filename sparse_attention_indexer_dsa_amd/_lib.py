@@ -34,6 +34,9 @@ SIGNATURES = {
                          _SZ, _P]),
     "indexer_mtp_workspace_size": (_SZ, [_I, _I64, _I, _I, _I, _I, _I, _I, _I, _U]),
     "indexer_mtp_pairs": (_I64, [_P, _I, _I64, _I, _I, _I, _U]),
+    "indexer_group_query": (_I, [_P, _P, _P, _P, _P, _I64, _I, _I, _I, _I, _I, _I64, _I, ctypes.c_float, _P, _P,
+                                 _P, _SZ, _P]),
+    "indexer_group_query_workspace_size": (_SZ, [_I64, _I, _I, _I, _I, _I]),
     "indexer_union_sizes": (_I, [_P, _I64, _I, _I, _P, _P]),
     "indexer_topk_overlap": (_I, [_P, _P, _I64, _I, _P, _P]),
     "indexer_union_stat": (_D, [_P, _I64, _I]),

@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsaidx.so")
-SOURCES = ["api.cpp", "scan_topk.hip", "dense_topk.hip", "decode.hip", "group_pool.hip", "mtp.hip", "calib.hip"]
+SOURCES = ["api.cpp", "scan_topk.hip", "dense_topk.hip", "decode.hip", "group_pool.hip", "mtp.hip", "calib.hip", "group_query.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 

@@ -685,6 +685,87 @@ int indexer_mtp(const void* q, const uint8_t* k_cache, const float* k_scale, con
   return ok();
 }
 
+// ---------------------------------------------------- group query (Eq. 6-7)
+
+struct GroupQueryWs {
+  size_t pc, ph, cbar, qf, total;
+};
+
+static GroupQueryWs group_query_ws(int64_t Tq, int dc, int dh, int Hs, int d, int G) {
+  const size_t n = (size_t)(Tq / G);
+  GroupQueryWs w{};
+  w.pc = 0;
+  w.ph = w.pc + align_up(n * 3 * dc * 2u);
+  w.cbar = w.ph + align_up(n * dh * 2u);
+  w.qf = w.cbar + align_up(n * dc * 2u);
+  w.total = w.qf + align_up(n * (size_t)Hs * d * 4u);
+  return w;
+}
+
+size_t indexer_group_query_workspace_size(int64_t Tq, int dc, int dh, int Hs, int d, int G) {
+  if (Tq <= 0 || dc <= 0 || dh <= 0 || Hs <= 0 || d <= 0 || G <= 0) return 0;
+  return group_query_ws(Tq, dc, dh, Hs, d, G).total;
+}
+
+int indexer_group_query(const void* c, const void* h, const void* w_pool, const void* w_q,
+                        const void* w_g, int64_t Tq, int dc, int dh, int Hs, int d, int G,
+                        int64_t q_pos0, int rope_dim, float rope_base, void* qbar, float* wbar,
+                        void* ws, size_t ws_bytes, void* stream) {
+  if (Tq < 0 || q_pos0 < 0 || dc < 1 || dh < 1 || Hs < 1 || d < 1)
+    return fail(DSAIDX_ERR_INVALID_ARG, "bad size (Tq=%lld dc=%d dh=%d Hs=%d d=%d)", (long long)Tq, dc,
+                dh, Hs, d);
+  if (G != 4 && G != 8 && G != 16)
+    return fail(DSAIDX_ERR_UNSUPPORTED, "group size G = %d not in {4, 8, 16}", G);
+  if (dc % 16 || dh % 16 || d % 16)
+    return fail(DSAIDX_ERR_UNSUPPORTED, "dc, dh and d must be multiples of 16");
+  if (Hs > kMaxHeads || (int64_t)Hs * d > 65536)
+    return fail(DSAIDX_ERR_UNSUPPORTED, "Hs = %d, d = %d too large", Hs, d);
+  if (dc > 65536 || dh > 65536) return fail(DSAIDX_ERR_UNSUPPORTED, "dc or dh above 65536");
+  if (rope_dim < 0 || rope_dim > d || rope_dim % 2)
+    return fail(DSAIDX_ERR_INVALID_ARG, "rope_dim = %d must be even and at most d", rope_dim);
+  if (!(rope_base > 1.0f)) return fail(DSAIDX_ERR_INVALID_ARG, "rope_base must exceed 1");
+  if (Tq / G > 65535) return fail(DSAIDX_ERR_UNSUPPORTED, "more than 65535 groups per call");
+  if (Tq > 0 && (!c || !h || !w_pool || !w_q || !w_g || !qbar || !wbar))
+    return fail(DSAIDX_ERR_INVALID_ARG, "null input or output");
+  if (!aligned16(c) || !aligned16(h) || !aligned16(w_pool) || !aligned16(w_q) || !aligned16(w_g) ||
+      ((uintptr_t)qbar & 1u) || ((uintptr_t)wbar & 3u))
+    return fail(DSAIDX_ERR_INVALID_ARG, "inputs must be 16-byte aligned");
+  const GroupQueryWs lay = group_query_ws(Tq, dc, dh, Hs, d, G);
+  int rc = check_ws(ws, ws_bytes, lay.total);
+  if (rc) return rc;
+  if (Tq == 0) return ok();
+  uint8_t* base = (uint8_t*)ws;
+  GroupQueryArgs a{};
+  a.c = c;
+  a.h = h;
+  a.w_pool = w_pool;
+  a.w_q = w_q;
+  a.w_g = w_g;
+  a.dc = dc;
+  a.dh = dh;
+  a.Hs = Hs;
+  a.d = d;
+  a.G = G;
+  a.rope_dim = rope_dim;
+  a.rope_base = rope_base;
+  a.q_pos0 = q_pos0;
+  a.ngroups = Tq / G;
+  a.tail = Tq % G != 0;
+  a.pc = base + lay.pc;
+  a.ph = base + lay.ph;
+  a.cbar = base + lay.cbar;
+  a.qf = (float*)(base + lay.qf);
+  a.qbar = qbar;
+  a.wbar = wbar;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (a.tail)  // the incomplete last group's gates are zero (its query row is zeroed by the kernel)
+    e = launch_fill_i32((int32_t*)(wbar + a.ngroups * Hs), Hs, 0, st);
+  if (e == hipSuccess) e = launch_group_query(a, st);
+  if (e != hipSuccess) return hip_fail(e, "indexer_group_query launch");
+  return ok();
+}
+
 // --------------------------------------------------------- calibration
 
 int indexer_union_sizes(const int32_t* topk_idx, int64_t T, int K, int G, int32_t* out_union,

@@ -1,0 +1,195 @@
+// group_query.hip -- the group indexer's query and gates of ADIndex (Qi et
+// al.), Section 4.2 Eq. (6)-(7) and Appendix C.3:
+//
+//   cbar = W_pool [max_i c_i ; min_i c_i ; mean_i c_i],  hbar = mean_i h_i
+//   qbar_j = RoPE_anchor([W_Q cbar]_j),  wbar_j = sigmoid([W_G hbar]_j)
+//
+// over each complete group of G consecutive query rows.  Pooling reads the
+// latents and hidden states once (HBM-bound: the hidden states dominate); the
+// three products are plain bf16 matrix products with fp32 accumulation on the
+// 32x32x16 bf16 MFMA, K contiguous in both operands, so every lane's operand
+// fragment is one 16-byte load; the rotary embedding (fp64 angles, the
+// positions reach 10^5 radians) and the bf16 rounding of the query follow in
+// their own small kernel.
+#include "device.h"
+#include "launch.h"
+
+namespace dsaidx {
+
+namespace {
+
+constexpr int kGqThreads = 256;
+
+__device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return (uint32_t)bf16_rne(lo) | ((uint32_t)bf16_rne(hi) << 16);
+}
+
+// One thread per 8 columns of a group: max, min and mean of c's rows (into
+// pc [n, 3dc]) and the mean of h's rows (into ph [n, dh]), fp32 sums in row
+// order times 1/G, rounded to bf16.
+template <int G>
+__global__ void __launch_bounds__(kGqThreads) gq_pool_kernel(const GroupQueryArgs a) {
+  const int64_t g = blockIdx.y;
+  const int cc = a.dc / 8, hc = a.dh / 8;  // 16-byte chunks per row
+  const int x = blockIdx.x * kGqThreads + threadIdx.x;
+  const float inv = 1.0f / (float)G;
+  if (x < cc) {
+    const uint4* src = reinterpret_cast<const uint4*>(a.c) + g * G * cc + x;
+    uint4 v[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) v[i] = src[(int64_t)i * cc];
+    float mx[8], mn[8], s[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) { mx[j] = -__builtin_inff(); mn[j] = __builtin_inff(); s[j] = 0.0f; }
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float e0 = bf_lo(w[q]), e1 = bf_hi(w[q]);
+        mx[2 * q] = fmaxf(mx[2 * q], e0); mx[2 * q + 1] = fmaxf(mx[2 * q + 1], e1);
+        mn[2 * q] = fminf(mn[2 * q], e0); mn[2 * q + 1] = fminf(mn[2 * q + 1], e1);
+        s[2 * q] += e0; s[2 * q + 1] += e1;
+      }
+    }
+    uint4* dst = reinterpret_cast<uint4*>(a.pc) + g * 3 * cc + x;
+    dst[0] = make_uint4(pack_bf16(mx[0], mx[1]), pack_bf16(mx[2], mx[3]), pack_bf16(mx[4], mx[5]),
+                        pack_bf16(mx[6], mx[7]));
+    dst[cc] = make_uint4(pack_bf16(mn[0], mn[1]), pack_bf16(mn[2], mn[3]), pack_bf16(mn[4], mn[5]),
+                         pack_bf16(mn[6], mn[7]));
+    dst[2 * cc] = make_uint4(pack_bf16(s[0] * inv, s[1] * inv), pack_bf16(s[2] * inv, s[3] * inv),
+                             pack_bf16(s[4] * inv, s[5] * inv), pack_bf16(s[6] * inv, s[7] * inv));
+  }
+  if (x < hc) {
+    const uint4* src = reinterpret_cast<const uint4*>(a.h) + g * G * hc + x;
+    uint4 v[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) v[i] = src[(int64_t)i * hc];
+    float s[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s[j] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) { s[2 * q] += bf_lo(w[q]); s[2 * q + 1] += bf_hi(w[q]); }
+    }
+    reinterpret_cast<uint4*>(a.ph)[g * hc + x] =
+        make_uint4(pack_bf16(s[0] * inv, s[1] * inv), pack_bf16(s[2] * inv, s[3] * inv),
+                   pack_bf16(s[4] * inv, s[5] * inv), pack_bf16(s[6] * inv, s[7] * inv));
+  }
+}
+
+// C = A B^T for A [M, K], B [N, K] bf16 (K contiguous, K % 16 == 0).  A
+// workgroup covers 64 x 64 of C, each wave a 32 x 32 tile on the 32x32x16 bf16
+// MFMA: lane l's A fragment is row l%32, k 8(l/32)..+7 of the k-step (16
+// bytes), likewise for B; lane l then holds C[8(r/4) + 4(l/32) + r%4][l%32].
+// MODE 0: C bf16 [M, N]; 1: C fp32 [M, N]; 2: sigmoid(C) fp32 [M, N].
+template <int MODE>
+__global__ void __launch_bounds__(kGqThreads) gemm_nt_kernel(const uint16_t* A, const uint16_t* B, int M,
+                                                             int N, int K, void* C) {
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int m0 = blockIdx.y * 64 + (wave >> 1) * 32, n0 = blockIdx.x * 64 + (wave & 1) * 32;
+  const int ar = min(m0 + (l & 31), M - 1), br = min(n0 + (l & 31), N - 1);  // rows past the end: clamped
+  const uint16_t* ap = A + (int64_t)ar * K + (l >> 5) * 8;
+  const uint16_t* bp = B + (int64_t)br * K + (l >> 5) * 8;
+  v16f acc = {};
+  int k = 0;
+  for (; k + 64 <= K; k += 64) {  // four k-steps' operands in flight
+    u32x4 av[4], bv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      av[u] = *reinterpret_cast<const u32x4*>(ap + k + 16 * u);
+      bv[u] = *reinterpret_cast<const u32x4*>(bp + k + 16 * u);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, av[u]),
+                                                    __builtin_bit_cast(v8bf, bv[u]), acc, 0, 0, 0);
+  }
+  for (; k < K; k += 16) {
+    const u32x4 av = *reinterpret_cast<const u32x4*>(ap + k);
+    const u32x4 bv = *reinterpret_cast<const u32x4*>(bp + k);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, av), __builtin_bit_cast(v8bf, bv),
+                                                  acc, 0, 0, 0);
+  }
+  const int col = n0 + (l & 31);
+  if (col >= N) return;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = m0 + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+    if (row >= M) continue;
+    const int64_t o = (int64_t)row * N + col;
+    if constexpr (MODE == 0) reinterpret_cast<uint16_t*>(C)[o] = bf16_rne(acc[r]);
+    else if constexpr (MODE == 1) reinterpret_cast<float*>(C)[o] = acc[r];
+    else reinterpret_cast<float*>(C)[o] = 1.0f / (1.0f + __expf(-acc[r]));
+  }
+}
+
+// qbar rows: rotate the pairs (i, i + rope_dim/2) of every head at the
+// group's anchor position, round to bf16; the incomplete last group's row
+// is zero.  One thread per (group, head, pair-or-entry).
+__global__ void __launch_bounds__(kGqThreads) gq_rope_kernel(const GroupQueryArgs a) {
+  const int64_t g = blockIdx.y;
+  const int HD = a.Hs * a.d;
+  const int e = blockIdx.x * kGqThreads + threadIdx.x;  // entry of the row
+  if (e >= HD) return;
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.qbar) + g * HD;
+  if (g >= a.ngroups) {  // the incomplete last group
+    out[e] = 0;
+    return;
+  }
+  const float* q = a.qf + g * HD;
+  const int j = e / a.d, i = e % a.d, half = a.rope_dim / 2;
+  float v = q[e];
+  if (i < a.rope_dim) {
+    const int p = i < half ? i : i - half;  // pair index
+    const double pos = (double)(a.q_pos0 + g * a.G);
+    const double ang = pos * pow((double)a.rope_base, -2.0 * p / a.rope_dim);
+    const double cs = cos(ang), sn = sin(ang);
+    const double x0 = q[j * a.d + p], x1 = q[j * a.d + p + half];
+    v = (float)(i < half ? x0 * cs - x1 * sn : x1 * cs + x0 * sn);
+  }
+  out[e] = bf16_rne(v);
+}
+
+}  // namespace
+
+hipError_t launch_group_query(const GroupQueryArgs& a, hipStream_t stream) {
+  const int64_t n = a.ngroups;
+  if (n > 0) {
+    const int chunks = (a.dc > a.dh ? a.dc : a.dh) / 8;
+    const dim3 pg((unsigned)((chunks + kGqThreads - 1) / kGqThreads), (unsigned)n);
+    switch (a.G) {
+      case 4: hipLaunchKernelGGL(gq_pool_kernel<4>, pg, dim3(kGqThreads), 0, stream, a); break;
+      case 8: hipLaunchKernelGGL(gq_pool_kernel<8>, pg, dim3(kGqThreads), 0, stream, a); break;
+      case 16: hipLaunchKernelGGL(gq_pool_kernel<16>, pg, dim3(kGqThreads), 0, stream, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    auto grid = [&](int N) { return dim3((unsigned)((N + 63) / 64), (unsigned)((n + 63) / 64)); };
+    // cbar = W_pool [max; min; mean]        [n, dc]  (bf16: the next product's operand)
+    hipLaunchKernelGGL(gemm_nt_kernel<0>, grid(a.dc), dim3(kGqThreads), 0, stream, (const uint16_t*)a.pc,
+                       (const uint16_t*)a.w_pool, (int)n, a.dc, 3 * a.dc, (void*)a.cbar);
+    // q = W_Q cbar                           [n, Hs*d] fp32
+    hipLaunchKernelGGL(gemm_nt_kernel<1>, grid(a.Hs * a.d), dim3(kGqThreads), 0, stream,
+                       (const uint16_t*)a.cbar, (const uint16_t*)a.w_q, (int)n, a.Hs * a.d, a.dc, (void*)a.qf);
+    // wbar = sigmoid(W_G hbar)              [n, Hs] fp32
+    hipLaunchKernelGGL(gemm_nt_kernel<2>, grid(a.Hs), dim3(kGqThreads), 0, stream, (const uint16_t*)a.ph,
+                       (const uint16_t*)a.w_g, (int)n, a.Hs, a.dh, (void*)a.wbar);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t rows = a.ngroups + (a.tail ? 1 : 0);
+  if (rows > 0) {
+    const int HD = a.Hs * a.d;
+    hipLaunchKernelGGL(gq_rope_kernel, dim3((unsigned)((HD + kGqThreads - 1) / kGqThreads), (unsigned)rows),
+                       dim3(kGqThreads), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dsaidx

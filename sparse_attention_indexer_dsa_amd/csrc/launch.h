@@ -121,6 +121,29 @@ hipError_t launch_mtp_plan(const MtpArgs& a, hipStream_t stream);
 hipError_t launch_mtp_gather(const MtpArgs& a, hipStream_t stream);
 hipError_t launch_mtp_map(const MtpArgs& a, hipStream_t stream);
 
+// The group indexer's query and gates (Eq. (6)-(7)) for `ngroups` complete
+// groups of G rows of c [*, dc] and h [*, dh] (bf16), plus one zero row of
+// qbar when `tail` (an incomplete last group).  Workspace: pc [ngroups, 3dc],
+// ph [ngroups, dh], cbar [ngroups, dc] bf16; qf [ngroups, Hs*d] fp32.
+struct GroupQueryArgs {
+  const void* c;
+  const void* h;
+  const void* w_pool;  // [dc, 3dc]
+  const void* w_q;     // [Hs*d, dc]
+  const void* w_g;     // [Hs, dh]
+  int dc, dh, Hs, d, G, rope_dim;
+  float rope_base;
+  int64_t q_pos0, ngroups;
+  int tail;
+  void* pc;
+  void* ph;
+  void* cbar;
+  float* qf;
+  void* qbar;   // [ngroups + tail, Hs, d] bf16
+  float* wbar;  // [ngroups + tail, Hs]; the tail row is written by the caller
+};
+hipError_t launch_group_query(const GroupQueryArgs& a, hipStream_t stream);
+
 // Calibration statistics over top-K index sets [rows, K] (ascending, -1 padded):
 // the union size of each complete group of G rows, and per-row overlaps.
 hipError_t launch_union_sizes(const int32_t* idx, int64_t groups, int K, int G, int32_t* out,

@@ -525,3 +525,33 @@ def test_union_sizes_and_overlap(dsa):
     assert np.array_equal(cov, calib.overlap_counts(di.cpu().numpy(), bi.cpu().numpy()))
     # rows before the first bank group use the original indexer: full coverage
     assert np.array_equal(cov[:256], (di[:256] >= 0).sum(1).cpu().numpy())
+
+
+
+# --------------------------------------------------- group query (Eq. 6-7)
+
+@pytest.mark.parametrize("G,Tq,q_pos0,rope_dim", [(16, 1024, 0, 64), (8, 1003, 40960, 64), (4, 64, 131000, 128),
+                                                  (16, 40, 7, 0)])
+def test_group_query(dsa, G, Tq, q_pos0, rope_dim):
+    """qbar and wbar of Eq. (6)-(7) against the oracle: a random pooling
+    projection, the rotary part at large anchor positions, an incomplete last
+    group; bf16 queries agree within two bf16 steps (almost all exactly)."""
+    from oracle import group_query as gq
+    dc, dh, Hs, d = 256, 512, 8, 128
+    g = torch.Generator().manual_seed(80 + G)
+    c = torch.randn(Tq, dc, generator=g).to(torch.bfloat16)
+    h = torch.randn(Tq, dh, generator=g).to(torch.bfloat16)
+    wp = (torch.randn(dc, 3 * dc, generator=g) / (3 * dc) ** 0.5).to(torch.bfloat16)
+    wq = (torch.randn(Hs * d, dc, generator=g) / dc ** 0.5).to(torch.bfloat16)
+    wg = (torch.randn(Hs, dh, generator=g) / dh ** 0.5).to(torch.bfloat16)
+    qb, wb = dsa.indexer_group_query(c.cuda(), h.cuda(), wp.cuda(), wq.cuda(), wg.cuda(), G, Hs, d, q_pos0,
+                                     rope_dim)
+    torch.cuda.synchronize()
+    rq, rw = gq.group_query(c, h, wp, wq, wg, G, Hs, d, q_pos0, rope_dim)
+    gqv = qb.double().cpu().numpy()
+    scale = np.abs(rq).max(axis=2, keepdims=True) + 1e-30
+    assert (np.abs(gqv - rq) <= 2 * 2.0 ** -8 * scale).all()
+    assert (gqv == rq).mean() > 0.97
+    np.testing.assert_allclose(wb.cpu().numpy(), rw, rtol=0, atol=2e-5)
+    if Tq % G:
+        assert (qb[-1] == 0).all() and (wb[-1] == 0).all()
