@@ -14,7 +14,7 @@ bounded sample of the same inputs.
 Inputs are generated on the GPU before timing (resident in HBM); outputs,
 workspace and streams are allocated before the timed region.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--adindex] [--mtp] [--calib]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--adindex] [--mtp] [--calib] [--group-query]
 """
 from __future__ import annotations
 
@@ -356,6 +356,43 @@ def bench_mtp(dsa, args, log):
     return res
 
 
+# ------------------------------------------------------------ group query
+
+def bench_group_query(dsa, args, log):
+    """Eq. (6)-(7) for the 64K ADIndex layer: G = 16 (4096 groups), DeepSeek-
+    like latent sizes (dc = 1536 query latent, dh = 7168 hidden), Hs = 8 heads
+    of d = 128.  HBM-bound: the latents and hidden states are read once."""
+    T, dc, dh, Hs, d, G = 65536, 1536, 7168, 8, 128, 16
+    log("generating group-query inputs on the GPU")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(args.seed)
+    c = torch.randn(T, dc, generator=g, device="cuda").to(torch.bfloat16)
+    h = torch.randn(T, dh, generator=g, device="cuda").to(torch.bfloat16)
+    wp = (torch.randn(dc, 3 * dc, generator=g, device="cuda") / (3 * dc) ** 0.5).to(torch.bfloat16)
+    wq = (torch.randn(Hs * d, dc, generator=g, device="cuda") / dc ** 0.5).to(torch.bfloat16)
+    wg = (torch.randn(Hs, dh, generator=g, device="cuda") / dh ** 0.5).to(torch.bfloat16)
+    ws = torch.empty(dsa.lib().indexer_group_query_workspace_size(T, dc, dh, Hs, d, G), dtype=torch.uint8,
+                     device="cuda")
+    qb = torch.empty((T // G, Hs, d), dtype=torch.bfloat16, device="cuda")
+    wb = torch.empty((T // G, Hs), dtype=torch.float32, device="cuda")
+
+    def step():
+        dsa.indexer_group_query(c, h, wp, wq, wg, G, Hs, d, 0, 64, qbar=qb, wbar=wb, ws=ws)
+    step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    nbytes = T * (dc + dh) * 2
+    n = T // G
+    flops = 2 * n * (3 * dc * dc + dc * Hs * d + dh * Hs)
+    return dict(workload=f"group query (Eq. 6-7): T={T}, G={G}, dc={dc}, dh={dh}, Hs={Hs}, d={d}, bf16",
+                ms_per_call=ms, input_read_gbs=nbytes / (ms * 1e-3) / 1e9,
+                frac_of_hbm=nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, gemm_tflops=flops / (ms * 1e-3) / 1e12)
+
+
 # ------------------------------------------------------------ calibration
 
 def bench_calib(dsa, args, log):
@@ -399,6 +436,7 @@ def main():
     ap.add_argument("--adindex", action="store_true", help="also time the ADIndex group-bank workload")
     ap.add_argument("--mtp", action="store_true", help="also time MTP verification windows at 256K")
     ap.add_argument("--calib", action="store_true", help="also time the calibration statistics kernels")
+    ap.add_argument("--group-query", action="store_true", help="also time the group query construction")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only copy BYTES device-to-device 5 times (calibrates HBM byte counters)")
@@ -458,6 +496,8 @@ def main():
         line["mtp"] = bench_mtp(dsa, args, log)
     if args.calib:
         line["calib"] = bench_calib(dsa, args, log)
+    if args.group_query:
+        line["group_query"] = bench_group_query(dsa, args, log)
     print(json.dumps(line), flush=True)
 
 

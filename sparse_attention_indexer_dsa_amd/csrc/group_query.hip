@@ -6,9 +6,10 @@
 //
 // over each complete group of G consecutive query rows.  Pooling reads the
 // latents and hidden states once (HBM-bound: the hidden states dominate); the
-// three products are plain bf16 matrix products with fp32 accumulation on the
-// 32x32x16 bf16 MFMA, K contiguous in both operands, so every lane's operand
-// fragment is one 16-byte load; the rotary embedding (fp64 angles, the
+// two query products are plain bf16 matrix products with fp32 accumulation on
+// the 32x32x16 bf16 MFMA, K contiguous in both operands, so every lane's
+// operand fragment is one 16-byte load; the gate's few heads are dot products;
+// the rotary embedding (fp64 angles, the
 // positions reach 10^5 radians) and the bf16 rounding of the query follow in
 // their own small kernel.
 #include "device.h"
@@ -83,48 +84,95 @@ __global__ void __launch_bounds__(kGqThreads) gq_pool_kernel(const GroupQueryArg
 }
 
 // C = A B^T for A [M, K], B [N, K] bf16 (K contiguous, K % 16 == 0).  A
-// workgroup covers 64 x 64 of C, each wave a 32 x 32 tile on the 32x32x16 bf16
-// MFMA: lane l's A fragment is row l%32, k 8(l/32)..+7 of the k-step (16
-// bytes), likewise for B; lane l then holds C[8(r/4) + 4(l/32) + r%4][l%32].
-// MODE 0: C bf16 [M, N]; 1: C fp32 [M, N]; 2: sigmoid(C) fp32 [M, N].
+// workgroup covers 128 x 128 of C, each wave 64 x 64 as 2 x 2 tiles of the
+// 32x32x16 bf16 MFMA (each operand fragment feeds two MFMAs).  Lane l's A
+// fragment of a tile is row l%32, k 8(l/32)..+7 of the k-step (one 16-byte
+// load), likewise for B; lane l then holds C[8(r/4) + 4(l/32) + r%4][l%32].
+// Rows past M or N are clamped on load and skipped on store.
+// MODE 0: C bf16 [M, N]; 1: C fp32 [M, N].
 template <int MODE>
 __global__ void __launch_bounds__(kGqThreads) gemm_nt_kernel(const uint16_t* A, const uint16_t* B, int M,
                                                              int N, int K, void* C) {
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int m0 = blockIdx.y * 64 + (wave >> 1) * 32, n0 = blockIdx.x * 64 + (wave & 1) * 32;
-  const int ar = min(m0 + (l & 31), M - 1), br = min(n0 + (l & 31), N - 1);  // rows past the end: clamped
-  const uint16_t* ap = A + (int64_t)ar * K + (l >> 5) * 8;
-  const uint16_t* bp = B + (int64_t)br * K + (l >> 5) * 8;
-  v16f acc = {};
-  int k = 0;
-  for (; k + 64 <= K; k += 64) {  // four k-steps' operands in flight
-    u32x4 av[4], bv[4];
+  const int m0 = blockIdx.y * 128 + (wave >> 1) * 64, n0 = blockIdx.x * 128 + (wave & 1) * 64;
+  const uint16_t* ap[2];
+  const uint16_t* bp[2];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      av[u] = *reinterpret_cast<const u32x4*>(ap + k + 16 * u);
-      bv[u] = *reinterpret_cast<const u32x4*>(bp + k + 16 * u);
+  for (int t = 0; t < 2; ++t) {
+    ap[t] = A + (int64_t)min(m0 + 32 * t + (l & 31), M - 1) * K + (l >> 5) * 8;
+    bp[t] = B + (int64_t)min(n0 + 32 * t + (l & 31), N - 1) * K + (l >> 5) * 8;
+  }
+  v16f acc[2][2] = {};
+  for (int k = 0; k < K; k += 32) {  // two k-steps' operands in flight
+    u32x4 av[2][2], bv[2][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bool in = k + 16 * u < K;
+        av[u][t] = in ? *reinterpret_cast<const u32x4*>(ap[t] + k + 16 * u) : u32x4{0, 0, 0, 0};
+        bv[u][t] = in ? *reinterpret_cast<const u32x4*>(bp[t] + k + 16 * u) : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, av[u][i]),
+                                                              __builtin_bit_cast(v8bf, bv[u][j]), acc[i][j], 0, 0,
+                                                              0);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + 32 * j + (l & 31);
+      if (col >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + 32 * i + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+        if (row >= M) continue;
+        const int64_t o = (int64_t)row * N + col;
+        const float v = acc[i][j][r];
+        if constexpr (MODE == 0) reinterpret_cast<uint16_t*>(C)[o] = bf16_rne(v);
+        else reinterpret_cast<float*>(C)[o] = v;
+      }
+    }
+}
+
+// wbar = sigmoid(W_G hbar): one workgroup per group; thread t takes 8-column
+// chunks t, t+256, ... of hbar and of each head's W_G row (fp32 FMA), then a
+// workgroup sum per head.
+__global__ void __launch_bounds__(kGqThreads) gq_gate_kernel(const GroupQueryArgs a) {
+  __shared__ float s_part[kGqThreads / 64];
+  const int64_t g = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  const int hc = a.dh / 8;
+  const uint4* hrow = reinterpret_cast<const uint4*>(a.ph) + g * hc;
+  for (int j = 0; j < a.Hs; ++j) {
+    const uint4* wrow = reinterpret_cast<const uint4*>(a.w_g) + (int64_t)j * hc;
+    float acc = 0.0f;
+    for (int x = tid; x < hc; x += kGqThreads) {
+      const uint4 hv = hrow[x], wv = wrow[x];
+      const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w}, ww[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc = fmaf(bf_lo(hw[q]), bf_lo(ww[q]), acc);
+        acc = fmaf(bf_hi(hw[q]), bf_hi(ww[q]), acc);
+      }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, av[u]),
-                                                    __builtin_bit_cast(v8bf, bv[u]), acc, 0, 0, 0);
-  }
-  for (; k < K; k += 16) {
-    const u32x4 av = *reinterpret_cast<const u32x4*>(ap + k);
-    const u32x4 bv = *reinterpret_cast<const u32x4*>(bp + k);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, av), __builtin_bit_cast(v8bf, bv),
-                                                  acc, 0, 0, 0);
-  }
-  const int col = n0 + (l & 31);
-  if (col >= N) return;
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if (l == 0) s_part[wave] = acc;
+    __syncthreads();
+    if (tid == 0) {
+      float t = 0.0f;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int row = m0 + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
-    if (row >= M) continue;
-    const int64_t o = (int64_t)row * N + col;
-    if constexpr (MODE == 0) reinterpret_cast<uint16_t*>(C)[o] = bf16_rne(acc[r]);
-    else if constexpr (MODE == 1) reinterpret_cast<float*>(C)[o] = acc[r];
-    else reinterpret_cast<float*>(C)[o] = 1.0f / (1.0f + __expf(-acc[r]));
+      for (int w = 0; w < kGqThreads / 64; ++w) t += s_part[w];
+      a.wbar[g * a.Hs + j] = 1.0f / (1.0f + __expf(-t));
+    }
+    __syncthreads();
   }
 }
 
@@ -170,16 +218,15 @@ hipError_t launch_group_query(const GroupQueryArgs& a, hipStream_t stream) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    auto grid = [&](int N) { return dim3((unsigned)((N + 63) / 64), (unsigned)((n + 63) / 64)); };
+    auto grid = [&](int N) { return dim3((unsigned)((N + 127) / 128), (unsigned)((n + 127) / 128)); };
     // cbar = W_pool [max; min; mean]        [n, dc]  (bf16: the next product's operand)
     hipLaunchKernelGGL(gemm_nt_kernel<0>, grid(a.dc), dim3(kGqThreads), 0, stream, (const uint16_t*)a.pc,
                        (const uint16_t*)a.w_pool, (int)n, a.dc, 3 * a.dc, (void*)a.cbar);
     // q = W_Q cbar                           [n, Hs*d] fp32
     hipLaunchKernelGGL(gemm_nt_kernel<1>, grid(a.Hs * a.d), dim3(kGqThreads), 0, stream,
                        (const uint16_t*)a.cbar, (const uint16_t*)a.w_q, (int)n, a.Hs * a.d, a.dc, (void*)a.qf);
-    // wbar = sigmoid(W_G hbar)              [n, Hs] fp32
-    hipLaunchKernelGGL(gemm_nt_kernel<2>, grid(a.Hs), dim3(kGqThreads), 0, stream, (const uint16_t*)a.ph,
-                       (const uint16_t*)a.w_g, (int)n, a.Hs, a.dh, (void*)a.wbar);
+    // wbar = sigmoid(W_G hbar)              [n, Hs] fp32 (Hs is small: a dot-product kernel)
+    hipLaunchKernelGGL(gq_gate_kernel, dim3((unsigned)n), dim3(kGqThreads), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
