@@ -57,16 +57,24 @@ def _traffic(*kernel_keys):
     total = 0.0
     for key in kernel_keys:
         rec = recs.get(key)
-        if not rec or rec.get("source_sha1") != _source_sha1():
+        if not rec or rec.get("source_sha1") != _source_sha1(KERNEL_SOURCES[key]):
             return None
         total += rec["hbm_bytes_per_launch"]
     return total
 
 
-def _source_sha1():
+# the device sources each measured launch is compiled from (a change to any of
+# them makes the committed counters stale)
+KERNEL_SOURCES = {
+    "dense_topk_fp8_prefill128k": ("dense_topk.hip", "device.h", "launch.h"),
+    "decode_call_decode256k": ("decode.hip", "device.h", "launch.h"),
+}
+
+
+def _source_sha1(names):
     h = hashlib.sha1()
     csrc = os.path.join(ROOT, "sparse_attention_indexer_dsa_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(names):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()
