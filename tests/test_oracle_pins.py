@@ -75,6 +75,28 @@ def test_single_head_is_a_matmul(oracle_lib, Tq, Tk, d, K):
     assert np.array_equal(sc, ref_s)
 
 
+def test_one_hot_keys_known_ranking(oracle_lib):
+    """Key s is c_s times the unit vector e_{s mod d} and every query entry is
+    1, so every head's dot product is c_s: the score is c_s * sum_j w_j where
+    c_s > 0 and 0 otherwise (ReLU), whatever the sign of the weights' sum.
+    The ranking follows c_s (ties by index) for a positive weight sum and
+    puts the zero scores first for a negative one."""
+    T, H, d, K = 60, 3, 8, 10
+    rng = np.random.default_rng(11)
+    cs = rng.integers(-3, 4, T).astype(np.float64)
+    k = np.zeros((T, d))
+    k[np.arange(T), np.arange(T) % d] = cs
+    q = np.ones((T, H, d))
+    for wsum_sign in (1, -1):
+        w = np.full((T, H), 0.5 * wsum_sign)
+        idx, sc = oracle.prefill(_bf16(q), _bf16(k), w.astype(np.float32), "bf16", 0, K)
+        want = np.maximum(cs, 0) * w[0].sum()  # the same weights for every query
+        for t in (0, 9, 59):
+            valid = np.arange(T) <= t
+            ri, rs = lexsort_topk(want[None, :], valid[None, :], K)
+            assert np.array_equal(idx[t], ri[0]) and np.array_equal(sc[t], rs[0]), (wsum_sign, t)
+
+
 def test_relu_acts_per_head(oracle_lib):
     """Heads q and -q with unit weights: ReLU(x) + ReLU(-x) = |x|.  A dropped
     ReLU gives 0, a ReLU after the head sum gives 0."""
