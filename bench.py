@@ -14,7 +14,7 @@ bounded sample of the same inputs.
 Inputs are generated on the GPU before timing (resident in HBM); outputs,
 workspace and streams are allocated before the timed region.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--adindex] [--mtp] [--calib] [--group-query]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--adindex] [--dsa16k] [--mtp] [--calib] [--group-query]
 """
 from __future__ import annotations
 
@@ -93,7 +93,6 @@ def bench_prefill(dsa, args, log):
     wl = make_workload(3, seed=args.seed, device="cuda")
     q, k, w, qs, ks = wl["q"], wl["k"], wl["w"], wl["q_scale"], wl["k_scale"]
     out = torch.empty((T, K), dtype=torch.int32, device="cuda")
-    out_pool = torch.empty((T, K), dtype=torch.int32, device="cuda")
     ws = torch.empty(dsa.workspace_prefill(chunk, T, H, d, K, dsa.DSAIDX_FP8_E4M3), dtype=torch.uint8,
                      device="cuda")
     nchunks = T // chunk
@@ -309,6 +308,34 @@ def bench_adindex(dsa, args, log):
                               frac=flops / (res["adindex"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS))
 
 
+# ---------------------------------------------------- DSA-shaped bf16 prefill
+
+def bench_dsa16k(dsa, args, log):
+    """One layer of DSA-shaped bf16 prefill: T=16384, H=64, d=128, top-2048, one
+    call (134,225,920 pairs, 2.199 TFLOP)."""
+    from workloads import make_workload
+    T, H, d, K = 16384, 64, 128, 2048
+    log("generating DSA bf16 prefill inputs T=16384 on the GPU")
+    wl = make_workload(2, seed=args.seed, device="cuda")
+    t = wl.tensors
+    out = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    ws = torch.empty(dsa.workspace_prefill(T, T, H, d, K, dsa.DSAIDX_BF16), dtype=torch.uint8, device="cuda")
+
+    def step():
+        dsa.indexer_prefill(t["q"], t["k"], t["w"], 0, K, want_score=False, out_idx=out, ws=ws)
+    step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    pairs = _pairs_causal(0, T)
+    tf = 2 * H * d * pairs / (ms * 1e-3) / 1e12
+    return dict(workload="DSA prefill, one layer: T=16384, H=64, d=128, top-2048, bf16", ms_per_call=ms,
+                tflops=tf, gpairs_per_s=pairs / (ms * 1e-3) / 1e9, frac_of_bf16_peak=tf / PEAK_BF16_TFLOPS)
+
+
 # ------------------------------------------------------------------ MTP
 
 def bench_mtp(dsa, args, log):
@@ -443,6 +470,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--adindex", action="store_true", help="also time the ADIndex group-bank workload")
     ap.add_argument("--mtp", action="store_true", help="also time MTP verification windows at 256K")
+    ap.add_argument("--dsa16k", action="store_true", help="also time the 16K bf16 DSA prefill layer")
     ap.add_argument("--calib", action="store_true", help="also time the calibration statistics kernels")
     ap.add_argument("--group-query", action="store_true", help="also time the group query construction")
     ap.add_argument("--quiet", action="store_true")
@@ -500,6 +528,8 @@ def main():
         line["decode"] = bench_decode(dsa, args, log)
     if args.adindex:
         line["adindex"] = bench_adindex(dsa, args, log)
+    if args.dsa16k:
+        line["dsa16k"] = bench_dsa16k(dsa, args, log)
     if args.mtp:
         line["mtp"] = bench_mtp(dsa, args, log)
     if args.calib:
