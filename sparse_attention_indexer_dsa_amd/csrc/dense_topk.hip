@@ -28,6 +28,13 @@
 //     running threshold are staged in LDS, flushed to the query's candidate
 //     buffer, and compacted by a wave radix select when it fills; keys arrive
 //     in ascending index, so strict ">" keeps the lower index on ties.
+//   * Gathering (the bank refinement of Eq. (14), groups of a multiple of 8
+//     queries): the workgroup's candidates are its group's bank followed by
+//     the keys after the anchor.  Each tile's 64 bank positions are copied
+//     into an eight-slot LDS ring seven steps ahead; the tile requests read
+//     them and fetch the listed rows (and fp8 scales) with the same LDS DMA,
+//     and the append stores positions instead of list slots.  The list is
+//     ascending in position, so ties still keep the lower index.
 #include "device.h"
 #include "launch.h"
 
@@ -42,6 +49,8 @@ constexpr int kWaves = 8;       // queries per workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kStage = kSelectHistWords / 2;  // LDS append stage entries per wave
 constexpr int kD = 128;
+constexpr int kIdxRing = 8;   // gathering: tiles of bank positions held in LDS
+constexpr int kIdxAhead = 7;  // a tile's positions are requested this many steps before it is scored
 
 template <int DT>
 struct Cfg {
@@ -114,9 +123,12 @@ __device__ __forceinline__ void dma_b32(const v4i& rsrc, uint32_t lds, uint32_t 
                :: "v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
 }
 
-template <int DT>
+template <int DT, bool GATHER>
 __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs args) {
   using C = Cfg<DT>;
+  // vm operations a wave issues per step: the tile chunks, the key scales and,
+  // gathering, the candidate indices of a later tile
+  constexpr int kVm = C::kVmPerStep + (GATHER ? 1 : 0);
   using Frag = typename AFrag<DT>::type;
   __shared__ __attribute__((aligned(16))) uint8_t s_tile[kStages][C::kTileBytes];
   __shared__ float s_ks[kStages][kTile];
@@ -124,6 +136,9 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   __shared__ float s_lin[2][2][kWaves][kTile];                    // [parity][d half][query][key]
   __shared__ __attribute__((aligned(16))) uint16_t s_qt[kWaves][2][kD];  // bf16 hi / lo of q-tilde
   __shared__ int s_need[2];  // s_need[i & 1] == i: a wave asked for compaction in step i
+  // gathering: the bank positions of tiles t .. t+7, slot t & 7 (tile t+7's
+  // are requested in step t, read by tile t+4's request and tile t's append)
+  __shared__ int32_t s_idx[GATHER ? kIdxRing : 1][kTile];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -137,8 +152,21 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   const bool active = j >= 0;
   const int jq = active ? j : 0;
   const int pos0 = (int)args.pos0;
-  const int ncand_blk = pos0 + j_hi * args.pos_stride + 1;           // keys 0 .. t_hi
-  const int ncand_me = active ? pos0 + j * args.pos_stride + 1 : 0;  // keys 0 .. t
+  const int t_hi = pos0 + j_hi * args.pos_stride;  // the workgroup's last query position
+  // Contiguous: the candidates of query t are keys 0 .. t.  Gathering (bank
+  // refinement, Eq. (14)): the workgroup's 8 queries belong to one group whose
+  // candidates are its bank (nbank ascending positions <= anchor) and then the
+  // keys anchor+1 .. t; candidate c is a position either way, ascending.
+  int anchor = 0, nbank = 0;
+  const int32_t* bank = nullptr;
+  if constexpr (GATHER) {
+    const int g = (j_hi - (kWaves - 1)) / args.group;
+    anchor = pos0 + g * args.group;
+    nbank = min(args.bank_stride, anchor + 1);
+    bank = args.bank + (int64_t)g * args.bank_stride;
+  }
+  const int ncand_blk = GATHER ? nbank + (t_hi - anchor) : t_hi + 1;
+  const int ncand_me = !active ? 0 : GATHER ? nbank + (pos0 + j - anchor) : pos0 + j * args.pos_stride + 1;
   const int ntiles = (ncand_blk + kTile - 1) / kTile;
 
   // ---- this wave's query: A fragments, gate weights (w/2, with the fp8 query
@@ -237,27 +265,58 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   if (tid < 2) s_need[tid] = -1;
 
   // ---- tile requests: this lane's chunks of tile t into LDS stage `st`.
-  // Buffer resources end at the workgroup's last candidate key, so rows past
-  // it (the last tile's tail, and the tiles requested past the end) read as
-  // zeros and are masked when appended; no request needs a clamp or branch.
-  const v4i kres = raw_buffer_words(args.k, ncand_blk * C::kRowBytes);
-  const v4i sres = DT == kFP8 ? raw_buffer_words(args.k_scale, ncand_blk * 4)
+  // Buffer resources end after the workgroup's last query position, so rows
+  // past it (the last tile's tail, and the tiles requested past the end) read
+  // as zeros and are masked when appended; no request needs a clamp or branch.
+  const v4i kres = raw_buffer_words(args.k, (t_hi + 1) * C::kRowBytes);
+  const v4i sres = DT == kFP8 ? raw_buffer_words(args.k_scale, (t_hi + 1) * 4)
                               : raw_buffer_words(args.w, 256);
-  int lane_off[C::kDma];  // byte offset of this lane's chunk inside a tile
+  int lane_row[C::kDma];  // the tile row of this lane's chunk
+  int lane_off[C::kDma];  // its byte offset inside the row's position (swizzled chunk)
 #pragma unroll
   for (int n = 0; n < C::kDma; ++n) {
     const int ci = n * kThreads + wave * 64 + l;  // chunk position in the stage
     const int r = ci / C::kChunksPerRow, cs = ci % C::kChunksPerRow;
-    lane_off[n] = r * C::kRowBytes + 16 * (cs ^ C::swz(r));
+    lane_row[n] = r;
+    lane_off[n] = 16 * (cs ^ C::swz(r));
   }
+  // gathering: the position of candidate c of tile t (past the list: none)
+  constexpr uint32_t kNowhere = 0x80000000u;  // an offset past every buffer range (all < 2 GiB)
+  auto position = [&](int t, int c) __attribute__((always_inline)) -> int {
+    return c < nbank ? s_idx[t & (kIdxRing - 1)][c & (kTile - 1)] : anchor + 1 + (c - nbank);
+  };
   auto request = [&](int t, int st) __attribute__((always_inline)) {
 #pragma unroll
-    for (int n = 0; n < C::kDma; ++n)
-      dma_b128(kres, lds_addr(&s_tile[st][(n * kThreads + wave * 64) * 16]),
-               lane_off[n] + t * C::kTileBytes);
+    for (int n = 0; n < C::kDma; ++n) {
+      uint32_t off;
+      if constexpr (GATHER) {
+        // past the list the position exceeds t_hi; so does a bank entry of -1
+        const uint32_t pos = (uint32_t)position(t, t * kTile + lane_row[n]);
+        off = pos <= (uint32_t)t_hi ? pos * C::kRowBytes + lane_off[n] : kNowhere;
+      } else {
+        off = (uint32_t)(t * kTile + lane_row[n]) * C::kRowBytes + lane_off[n];
+      }
+      dma_b128(kres, lds_addr(&s_tile[st][(n * kThreads + wave * 64) * 16]), off);
+    }
     // every wave writes the same 64 scales (fp8; bf16 loads placeholder words),
     // so all waves issue the same number of requests per step
-    dma_b32(sres, lds_addr(&s_ks[st][0]), DT == kFP8 ? 4 * (t * kTile + l) : 4 * l);
+    uint32_t soff = 4 * l;
+    if constexpr (DT == kFP8) {
+      const int c = t * kTile + l;
+      if constexpr (GATHER) {
+        const uint32_t pos = (uint32_t)position(t, c);
+        soff = pos <= (uint32_t)t_hi ? 4 * pos : kNowhere;
+      } else {
+        soff = 4 * c;
+      }
+    }
+    dma_b32(sres, lds_addr(&s_ks[st][0]), soff);
+  };
+  // gathering: tile t's 64 bank positions into the index ring (every wave
+  // writes the same words, so every wave issues the same requests)
+  const v4i bres = GATHER ? raw_buffer_words(bank, nbank * 4) : v4i{0, 0, 0, 0};
+  auto request_idx = [&](int t) __attribute__((always_inline)) {
+    if constexpr (GATHER) dma_b32(bres, lds_addr(&s_idx[t & (kIdxRing - 1)][0]), 4 * (t * kTile + l));
   };
 
   // B operands of sub-tile u of the tile in stage st (row 32u + col has the
@@ -348,13 +407,19 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
       if ((tm >> l) & 1) {
         const int p = nst + rank_below(tm);
         stage_key[p] = __float_as_uint(sc);
-        stage_idx[p] = tbase + l;
+        stage_idx[p] = GATHER ? position(i, tbase + l) : tbase + l;
       }
       nst += popc(tm);
       if (cnt + nst > lim && l == 0) s_need[i & 1] = i;
     }
   };
-  // ---- prologue: tiles 0..3 requested, tile 0's linear term, first MFMAs
+  // ---- prologue: (gathering: the positions of tiles 0..6) tiles 0..3
+  // requested, tile 0's linear term, first MFMAs
+  if constexpr (GATHER) {
+    for (int t = 0; t < kIdxAhead; ++t) request_idx(t);
+    __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): this wave's copy of the positions
+    __syncthreads();
+  }
   for (int t = 0; t < kAhead; ++t) request(t, t);
   __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): tiles 0..3 in LDS
   __syncthreads();
@@ -381,6 +446,7 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
       flush();
     }
     request(i + kAhead, st4);
+    request_idx(i + kIdxAhead);
     const int tbase = i * kTile;
     // the same work every step: past the last tile the MFMAs run on zeros
     // and the append masks them out
@@ -394,11 +460,11 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
     const float sc0 = sub_score(p0, i, st, 0);
     const float sc1 = sub_score(p1, i, st, 1);
     append(l < 32 ? sc0 : sc1, tbase, i);
-    // tile i+2 must have landed before the barrier publishes it: after its
-    // requests this wave issued those of tiles i+3 and i+4 (and maybe a
-    // flush's stores, which only makes the count conservative)
-    if constexpr (C::kVmPerStep == 2) __builtin_amdgcn_s_waitcnt(0x3F70 | 4);
-    else __builtin_amdgcn_s_waitcnt(0x3F70 | 6);
+    // tile i+2 (gathering: and the positions of tile i+5) must have landed
+    // before the barrier publishes them: after their requests this wave issued
+    // those of steps i-1 and i (and maybe a flush's stores, which only makes
+    // the count conservative)
+    __builtin_amdgcn_s_waitcnt(0x3F70 | (2 * kVm));
     __syncthreads();
     st4 = st;
     st = st1;
@@ -430,16 +496,22 @@ bool dense_topk_supported(const ScanArgs& a) {
   // buffer offsets are 32-bit: the key rows up to the last query's position
   // (plus the tiles requested past it) must stay below 2 GiB
   const int64_t keys = a.pos0 + (a.nq - 1) * a.pos_stride + 1 + kAhead * kTile;
-  return a.bank == nullptr && a.H > 32 && a.H <= 64 && a.d == kD && keys * 2 * kD < (int64_t(1) << 31);
+  // bank refinement: every workgroup's 8 queries must sit in one group
+  const bool shape_ok = a.bank == nullptr || (a.group % kWaves == 0 && a.nq % kWaves == 0 && a.pos_stride == 1);
+  return shape_ok && a.H > 32 && a.H <= 64 && a.d == kD && keys * 2 * kD < (int64_t(1) << 31);
 }
 
 hipError_t launch_dense_topk(const ScanArgs& a, int dtype, hipStream_t stream) {
   const int64_t blocks = (a.nq + kWaves - 1) / kWaves;
   if (blocks <= 0) return hipSuccess;
-  if (dtype == kBF16)
-    hipLaunchKernelGGL(dense_topk_kernel<kBF16>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(dense_topk_kernel<kFP8>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  const dim3 grid((unsigned)blocks), block(kThreads);
+  if (a.bank) {
+    if (dtype == kBF16) hipLaunchKernelGGL((dense_topk_kernel<kBF16, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((dense_topk_kernel<kFP8, true>), grid, block, 0, stream, a);
+  } else {
+    if (dtype == kBF16) hipLaunchKernelGGL((dense_topk_kernel<kBF16, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((dense_topk_kernel<kFP8, false>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

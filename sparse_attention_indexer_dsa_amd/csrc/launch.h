@@ -34,8 +34,9 @@ struct ScanArgs {
 
 hipError_t launch_scan_topk(const ScanArgs& a, int dtype, hipStream_t stream);
 
-// The dense kernel for 33..64 heads at d = 128 (no bank); launch_scan_topk
-// routes there when dense_topk_supported().
+// The dense kernel for 33..64 heads at d = 128 (bank groups: a multiple of 8
+// queries, pos_stride 1); launch_scan_topk routes there when
+// dense_topk_supported().
 bool dense_topk_supported(const ScanArgs& a);
 hipError_t launch_dense_topk(const ScanArgs& a, int dtype, hipStream_t stream);
 

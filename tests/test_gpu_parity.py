@@ -355,6 +355,16 @@ def test_group_bank_fp8_exact(dsa):
     _group_check(dsa, wl, rows=_rows(900, 48, 18))
 
 
+@pytest.mark.parametrize("dtype,G,P,K,flags", [("fp8", 8, 200, 96, 1), ("bf16", 16, 77, 40, 1), ("fp8", 8, 130, 96, 0)])
+def test_group_bank_dense_gather_exact(dsa, dtype, G, P, K, flags):
+    """Bank refinement on the dense kernel (48 heads, d = 128, G a multiple of
+    8): banks shorter than a tile and ragged across tiles, forced banks whose
+    anchors see fewer than P keys, q_pos0 > 0 and a trailing incomplete group."""
+    wl = make_group_bank(T=1300, H=48, Hs=24, d=128, topk=K, G=G, P=P, dtype=dtype, dist="int", seed=60 + G,
+                         Tq=1251, q_pos0=48)
+    _group_check(dsa, wl, flags, rows=np.unique(np.r_[np.arange(0, 80), _rows(1251, 40, 60 + G), 1250]))
+
+
 @pytest.mark.parametrize("G", [4, 8, 16])
 def test_group_bank_pooled_exact(dsa, G):
     """Training-free group query (mean pooling) at H = 64, d = 128 on integer
