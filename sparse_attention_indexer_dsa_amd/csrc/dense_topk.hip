@@ -52,6 +52,11 @@ constexpr int kD = 128;
 constexpr int kIdxRing = 8;   // gathering: tiles of bank positions held in LDS
 constexpr int kIdxAhead = 7;  // a tile's positions are requested this many steps before it is scored
 
+template <int S>
+struct StageC {  // a ring stage as a compile-time constant
+  constexpr operator int() const { return S; }
+};
+
 template <int DT>
 struct Cfg {
   static constexpr int kRowBytes = DT == kBF16 ? 2 * kD : kD;
@@ -133,7 +138,7 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   __shared__ __attribute__((aligned(16))) uint8_t s_tile[kStages][C::kTileBytes];
   __shared__ float s_ks[kStages][kTile];
   __shared__ __attribute__((aligned(16))) uint32_t s_hist[kWaves][kSelectHistWords];
-  __shared__ float s_lin[2][2][kWaves][kTile];                    // [parity][d half][query][key]
+  __shared__ float s_lin[kStages][2][kWaves][kTile];  // [tile's stage][d half][query][key]
   __shared__ __attribute__((aligned(16))) uint16_t s_qt[kWaves][2][kD];  // bf16 hi / lo of q-tilde
   __shared__ int s_need[2];  // s_need[i & 1] == i: a wave asked for compaction in step i
   // gathering: the bank positions of tiles t .. t+7, slot t & 7 (tile t+7's
@@ -285,6 +290,9 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   auto position = [&](int t, int c) __attribute__((always_inline)) -> int {
     return c < nbank ? s_idx[t & (kIdxRing - 1)][c & (kTile - 1)] : anchor + 1 + (c - nbank);
   };
+  // LDS addresses (scalar): this wave's part of stage 0, the scales of stage 0
+  const uint32_t lds_tile = lds_addr(&s_tile[0][0]) + wave * 64 * 16;
+  const uint32_t lds_ks = lds_addr(&s_ks[0][0]);
   auto request = [&](int t, int st) __attribute__((always_inline)) {
 #pragma unroll
     for (int n = 0; n < C::kDma; ++n) {
@@ -296,7 +304,7 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
       } else {
         off = (uint32_t)(t * kTile + lane_row[n]) * C::kRowBytes + lane_off[n];
       }
-      dma_b128(kres, lds_addr(&s_tile[st][(n * kThreads + wave * 64) * 16]), off);
+      dma_b128(kres, lds_tile + st * C::kTileBytes + n * kThreads * 16, off);
     }
     // every wave writes the same 64 scales (fp8; bf16 loads placeholder words),
     // so all waves issue the same number of requests per step
@@ -310,13 +318,14 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
         soff = 4 * c;
       }
     }
-    dma_b32(sres, lds_addr(&s_ks[st][0]), soff);
+    dma_b32(sres, lds_ks + st * kTile * 4, soff);
   };
   // gathering: tile t's 64 bank positions into the index ring (every wave
   // writes the same words, so every wave issues the same requests)
   const v4i bres = GATHER ? raw_buffer_words(bank, nbank * 4) : v4i{0, 0, 0, 0};
+  const uint32_t lds_idx = lds_addr(&s_idx[0][0]);
   auto request_idx = [&](int t) __attribute__((always_inline)) {
-    if constexpr (GATHER) dma_b32(bres, lds_addr(&s_idx[t & (kIdxRing - 1)][0]), 4 * (t * kTile + l));
+    if constexpr (GATHER) dma_b32(bres, lds_idx + (t & (kIdxRing - 1)) * kTile * 4, 4 * (t * kTile + l));
   };
 
   // B operands of sub-tile u of the tile in stage st (row 32u + col has the
@@ -358,9 +367,9 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
     }
     return s0 + s1;
   };
-  // the linear term of tile t (stage st) for all 8 queries: this wave's 16
-  // keys and d half, written to s_lin[t & 1][kh]
-  auto linear = [&](int t, int st) __attribute__((always_inline)) {
+  // the linear term of the tile in stage st for all 8 queries: this wave's
+  // 16 keys and d half, written to s_lin[st][kh]
+  auto linear = [&](int st) __attribute__((always_inline)) {
     v4f c = {0.0f, 0.0f, 0.0f, 0.0f};
     const int r = 16 * nb + (l & 15);
     const uint8_t* row = &s_tile[st][r * C::kRowBytes];
@@ -384,18 +393,20 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
     }
     // rows 4(l>>4)+i = (query 2(l>>4) + i/2, part i%2)
     const int q0 = 2 * (l >> 4);
-    s_lin[t & 1][kh][q0][r] = c[0] + c[1];
-    s_lin[t & 1][kh][q0 + 1][r] = c[2] + c[3];
+    s_lin[st][kh][q0][r] = c[0] + c[1];
+    s_lin[st][kh][q0 + 1][r] = c[2] + c[3];
   };
-  // the full score of sub-tile u's key in this lane's column (both lane halves
-  // hold it after the swap): (sum over heads of (w/2)|s| + linear term) * scale
-  auto sub_score = [&](float part, int t, int st, int u) __attribute__((always_inline)) -> float {
-    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false,
-                                               false);
-    const int kk = 32 * u + col;
+  // the full scores of the step's 64 keys, key l in lane l (sub-tile l / 32,
+  // column l % 32).  p0 and p1 hold this lane's half-head sums for its column
+  // of sub-tiles 0 and 1; swapping the upper half of p0 with the lower half of
+  // p1 leaves both halves of key l's sum in lane l, in the same order on both
+  // lane halves (lower-half heads first).  Then the linear term and the fp8
+  // key scale: (sum over heads of (w/2)|s| + linear term) * scale.
+  auto tile_score = [&](float p0, float p1, int st) __attribute__((always_inline)) -> float {
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
     float sc = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) +
-               (s_lin[t & 1][0][wave][kk] + s_lin[t & 1][1][wave][kk]);
-    if constexpr (DT == kFP8) sc *= s_ks[st][kk];
+               (s_lin[st][0][wave][l] + s_lin[st][1][wave][l]);
+    if constexpr (DT == kFP8) sc *= s_ks[st][l];
     return sc;
   };
   // append the step's scores that beat the threshold: lane l holds candidate
@@ -423,7 +434,7 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   for (int t = 0; t < kAhead; ++t) request(t, t);
   __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): tiles 0..3 in LDS
   __syncthreads();
-  linear(0, 0);
+  linear(0);
   v16f acc0[2], acc1[2];
   Frag bA[C::kSteps], bB[C::kSteps];
   load_b(bA, 0, 0);
@@ -431,12 +442,17 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   load_b(bB, 0, 1);
   __syncthreads();  // s_lin of tile 0
 
-  // step i scores tile i (stage st) while tile i+1 (stage st1) feeds the next
-  // MFMAs and its linear term, and tile i+4 is requested into stage st4 =
-  // (i+4) % 5, the one tile i-1 left.  On entry bB holds tile i's second
-  // sub-tile's B operands and acc0 its first sub-tile's products.
-  int st = 0, st1 = 1, st4 = kAhead;
-  for (int i = 0; i < ntiles; ++i) {
+  // step i scores tile i (stage st = i % 5) while tile i+1 (stage st1) feeds
+  // the next MFMAs and its linear term, and tile i+4 is requested into stage
+  // st4 = (i+4) % 5, the one tile i-1 left.  On entry bB holds tile i's second
+  // sub-tile's B operands and acc0 its first sub-tile's products.  For fp8
+  // the loop is unrolled over the ring so that every stage is a constant (LDS
+  // addresses fold into the instructions' offsets); bf16, whose operands take
+  // twice the registers, keeps one copy of the step with run-time stages.
+  auto step = [&](const int i, auto stage) __attribute__((always_inline)) {
+    const int st = stage;
+    const int st1 = st == kStages - 1 ? 0 : st + 1;
+    const int st4 = st == 0 ? kStages - 1 : st - 1;  // (st + kAhead) % kStages
     // compaction requests raised during step i-1 (seen after its barrier)
     if (i > 0 && s_need[(i - 1) & 1] == i - 1 && active && cnt + nst > args.K) {
       flush();
@@ -456,19 +472,30 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
     load_b(bB, st1, 1);
     mfma_sub(acc0, bA);
     const float p1 = abs_sum(acc1);
-    linear(i + 1, st1);
-    const float sc0 = sub_score(p0, i, st, 0);
-    const float sc1 = sub_score(p1, i, st, 1);
-    append(l < 32 ? sc0 : sc1, tbase, i);
+    linear(st1);
+    append(tile_score(p0, p1, st), tbase, i);
     // tile i+2 (gathering: and the positions of tile i+5) must have landed
     // before the barrier publishes them: after their requests this wave issued
     // those of steps i-1 and i (and maybe a flush's stores, which only makes
     // the count conservative)
     __builtin_amdgcn_s_waitcnt(0x3F70 | (2 * kVm));
     __syncthreads();
-    st4 = st;
-    st = st1;
-    st1 = st1 == kStages - 1 ? 0 : st1 + 1;
+  };
+  static_assert(kStages == 5 && kAhead == kStages - 1, "the loops below assume a five-stage ring");
+  if constexpr (DT == kFP8) {
+    for (int i = 0; i < ntiles; i += kStages) {
+      step(i, StageC<0>{});
+      if (i + 1 >= ntiles) break;
+      step(i + 1, StageC<1>{});
+      if (i + 2 >= ntiles) break;
+      step(i + 2, StageC<2>{});
+      if (i + 3 >= ntiles) break;
+      step(i + 3, StageC<3>{});
+      if (i + 4 >= ntiles) break;
+      step(i + 4, StageC<4>{});
+    }
+  } else {
+    for (int i = 0, st = 0; i < ntiles; ++i, st = st == kStages - 1 ? 0 : st + 1) step(i, st);
   }
 
   // the requests issued past the last tile: none may still be writing LDS
