@@ -26,8 +26,10 @@
 //     to the score's magnitude.
 //   * Streaming top-K exactly as the general kernel: scores that beat the
 //     running threshold are staged in LDS, flushed to the query's candidate
-//     buffer, and compacted by a wave radix select when it fills; keys arrive
-//     in ascending index, so strict ">" keeps the lower index on ties.
+//     buffer, and compacted by a wave radix select when it fills (two 11-bit
+//     digits, and the third only when the K-th best's 22-bit key bucket is
+//     crowded); keys arrive in ascending index, so strict ">" keeps the lower
+//     index on ties.
 //   * Gathering (the bank refinement of Eq. (14), groups of a multiple of 8
 //     queries): the workgroup's candidates are its group's bank followed by
 //     the keys after the anchor.  Each tile's 64 bank positions are copied
@@ -246,6 +248,7 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   uint32_t* ckey = args.cand_key + (int64_t)jq * args.cap;  // raw fp32 scores
   int32_t* cidx = args.cand_idx + (int64_t)jq * args.cap;
   uint32_t* hist = s_hist[wave];
+
   // Scores that enter are staged in this wave's LDS (the selection histogram's
   // words, free outside a selection) and flushed to the candidate buffer when
   // the stage nears full.  A flush does not wait for its stores: the wait is
@@ -345,14 +348,21 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
       }
     }
   };
-  auto mfma_sub = [&](v16f (&acc)[2], const Frag (&bf)[C::kSteps]) __attribute__((always_inline)) {
-    acc[0] = v16f{};
-    acc[1] = v16f{};
+  // the k-steps [s0, s1) of a sub-tile's MFMAs (s0 == 0 starts from zero)
+  auto mfma_steps = [&](v16f (&acc)[2], const Frag (&bf)[C::kSteps], int s0, int s1)
+      __attribute__((always_inline)) {
+    if (s0 == 0) {
+      acc[0] = v16f{};
+      acc[1] = v16f{};
+    }
 #pragma unroll
-    for (int s = 0; s < C::kSteps; ++s) {
+    for (int s = s0; s < s1; ++s) {
       acc[0] = mfma<DT>(a[0][s], bf[s], acc[0]);
       acc[1] = mfma<DT>(a[1][s], bf[s], acc[1]);
     }
+  };
+  auto mfma_sub = [&](v16f (&acc)[2], const Frag (&bf)[C::kSteps]) __attribute__((always_inline)) {
+    mfma_steps(acc, bf, 0, C::kSteps);
   };
   // sum over this lane's 32 heads of (w/2)*|s|
   auto abs_sum = [&](const v16f (&acc)[2]) __attribute__((always_inline)) -> float {
@@ -456,8 +466,7 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
     // compaction requests raised during step i-1 (seen after its barrier)
     if (i > 0 && s_need[(i - 1) & 1] == i - 1 && active && cnt + nst > args.K) {
       flush();
-      thr = wave_select_topk(ckey, cidx, cnt, args.K, hist);
-      cnt = args.K;
+      thr = wave_keep_topk(ckey, cidx, cnt, args.K, hist, kCompactSlack);
     } else if (nst > kStage - 64) {
       flush();
     }
@@ -470,9 +479,13 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
     mfma_sub(acc1, bB);
     const float p0 = abs_sum(acc0);
     load_b(bB, st1, 1);
-    mfma_sub(acc0, bA);
+    // fp8: half of the next sub-tile's MFMAs are held back until after the
+    // linear term, so they still run while the wave scores and appends
+    constexpr int kHeld = DT == kFP8 ? C::kSteps / 2 : C::kSteps;
+    mfma_steps(acc0, bA, 0, kHeld);
     const float p1 = abs_sum(acc1);
     linear(st1);
+    if constexpr (kHeld < C::kSteps) mfma_steps(acc0, bA, kHeld, C::kSteps);
     append(tile_score(p0, p1, st), tbase, i);
     // tile i+2 (gathering: and the positions of tile i+5) must have landed
     // before the barrier publishes them: after their requests this wave issued
@@ -504,10 +517,7 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   if (!active) return;
   flush();
   wave_mem_fence();
-  if (cnt > args.K) {
-    wave_select_topk(ckey, cidx, cnt, args.K, hist);
-    cnt = args.K;
-  }
+  if (cnt > args.K) wave_keep_topk(ckey, cidx, cnt, args.K, hist, -1);
   int32_t* oidx = args.out_idx + (int64_t)j * args.out_stride;
   float* osc = args.out_score ? args.out_score + (int64_t)j * args.out_stride : nullptr;
   for (int p = l; p < args.K; p += 64) {

@@ -92,45 +92,42 @@ __device__ __forceinline__ void wave_mem_fence() {
 // word (every candidate buffer holds fewer than 65536 entries).
 constexpr int kSelectHistWords = 1024;
 
-// One radix digit step of the selection over a candidate buffer of raw fp32
-// scores (compared through order_key): given the entries whose key matches
-// `prefix` on `pmask`, histogram digit (key >> shift) & (NBINS-1) into `hist`
-// (this wave's kSelectHistWords LDS words, NBINS <= 2048 16-bit counters) and
-// find the digit holding the krem-th largest matching entry.  Updates
-// prefix/pmask/krem; wave-uniform.
+// Order LDS accesses of the lanes of one wave (a histogram's updates before
+// its reads).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Zero the first NBINS/2 words of a wave's histogram (every lane its share).
 template <int NBINS>
-__device__ __forceinline__ void radix_step(const uint32_t* keys, int n, uint32_t* hist, int shift,
-                                           uint32_t& prefix, uint32_t& pmask, int& krem) {
+__device__ __forceinline__ void hist_zero(uint32_t* hist) {
+  constexpr int PERW = NBINS / 2 / 64;
+  uint32_t* mine = hist + lane_id() * PERW;
+#pragma unroll
+  for (int b = 0; b < PERW; b += 4) *(u32x4*)(mine + b) = u32x4{0u, 0u, 0u, 0u};
+}
+
+// One 16-bit histogram count (two per word) of order key k's digit
+// (k >> shift) & (NBINS - 1).
+template <int NBINS>
+__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t k, int shift) {
+  const uint32_t bin = (k >> shift) & (NBINS - 1);
+  atomicAdd(hist + (bin >> 1), 1u << ((bin & 1u) * 16u));
+}
+
+// Pick step of a radix digit: given a histogram of the digit (key >> shift)
+// & (NBINS-1) over the entries that match `prefix` on `pmask`, find the digit
+// holding the krem-th largest of them.  Updates prefix/pmask/krem and returns
+// the number of entries with the chosen digit; wave-uniform.
+template <int NBINS>
+__device__ __forceinline__ int radix_pick(const uint32_t* hist, int shift, uint32_t& prefix,
+                                          uint32_t& pmask, int& krem) {
   constexpr int PERW = NBINS / 2 / 64;  // words per lane
   constexpr int PER = 2 * PERW;         // bins per lane
   const int l = lane_id();
-  uint32_t* mine = hist + l * PERW;
-#pragma unroll
-  for (int b = 0; b < PERW; b += 4) *(u32x4*)(mine + b) = u32x4{0u, 0u, 0u, 0u};
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const uint32_t dmask = NBINS - 1;
-  auto count = [&](uint32_t raw) {
-    const uint32_t k = order_key(__uint_as_float(raw));
-    if ((k & pmask) == prefix) {
-      const uint32_t bin = (k >> shift) & dmask;
-      atomicAdd(hist + (bin >> 1), 1u << ((bin & 1u) * 16u));
-    }
-  };
-  // 16 independent loads in flight per lane: the buffer usually sits in HBM
-  int e = l;
-  for (; e + 15 * 64 < n; e += 16 * 64) {
-    uint32_t k[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) k[u] = keys[e + 64 * u];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) count(k[u]);
-  }
-  for (; e < n; e += 64) count(keys[e]);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint32_t* mine = hist + l * PERW;
   uint32_t c[PER];
   int local = 0;
 #pragma unroll
@@ -149,37 +146,88 @@ __device__ __forceinline__ void radix_step(const uint32_t* keys, int n, uint32_t
   const int above = total - incl;
   const uint64_t hit = ballot(above < krem && above + local >= krem);
   const int L = first_lane(hit);
-  int digit = 0, newk = 0;
+  int digit = 0, newk = 0, cnt = 0;
   if (l == L) {
     int acc = above;
 #pragma unroll
     for (int b = PER - 1; b >= 0; --b) {
       int cb = (int)c[b];
-      if (acc + cb >= krem && newk == 0) { digit = l * PER + b; newk = krem - acc; }
+      if (acc + cb >= krem && newk == 0) { digit = l * PER + b; newk = krem - acc; cnt = cb; }
       acc += cb;
     }
   }
   digit = shfl(digit, L);
   krem = shfl(newk, L);
   prefix |= (uint32_t)digit << shift;
-  pmask |= dmask << shift;
+  pmask |= (uint32_t)(NBINS - 1) << shift;
+  return shfl(cnt, L);
+}
+
+// Count step of a radix digit over a candidate buffer of raw fp32 scores
+// (compared through order_key): histogram digit (key >> shift) & (NBINS-1) of
+// the entries whose key matches `prefix` on `pmask` into `hist` (this wave's
+// kSelectHistWords LDS words, NBINS <= 2048 16-bit counters).
+template <int NBINS>
+__device__ __forceinline__ void radix_count(const uint32_t* keys, int n, uint32_t* hist, int shift,
+                                            uint32_t prefix, uint32_t pmask) {
+  const int l = lane_id();
+  hist_zero<NBINS>(hist);
+  wave_lds_sync();
+  auto count = [&](uint32_t raw) {
+    const uint32_t k = order_key(__uint_as_float(raw));
+    if ((k & pmask) == prefix) {
+      hist_add<NBINS>(hist, k, shift);
+    }
+  };
+  // 16 independent loads in flight per lane: the buffer usually sits in HBM
+  int e = l;
+  for (; e + 15 * 64 < n; e += 16 * 64) {
+    uint32_t k[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) k[u] = keys[e + 64 * u];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) count(k[u]);
+  }
+  for (; e < n; e += 64) count(keys[e]);
+  wave_lds_sync();
+}
+// One radix digit step: count, then find the digit holding the krem-th
+// largest matching entry.  Updates prefix/pmask/krem; wave-uniform.
+template <int NBINS>
+__device__ __forceinline__ void radix_step(const uint32_t* keys, int n, uint32_t* hist, int shift,
+                                           uint32_t& prefix, uint32_t& pmask, int& krem) {
+  radix_count<NBINS>(keys, n, hist, shift, prefix, pmask);
+  radix_pick<NBINS>(hist, shift, prefix, pmask, krem);
 }
 
 // Keep the top K (by score descending, then by buffer position, i.e. ascending
 // key index) of the n > K entries of a wave's candidate buffer (raw fp32 score
-// bits + key indices), compacting them in place in their original order.
-// Returns the K-th largest score.
+// bits + key indices), compacting them in place in their original order; n
+// becomes the number kept.  Returns a threshold: no score at or below it can
+// still enter the top K.
+//   * slack >= 0 (a compaction during the stream): when the 22-bit key bucket
+//     that holds the K-th best has at most K + slack entries at or above it,
+//     the third digit is skipped and that whole bucket is kept; the threshold
+//     is then the bucket's lowest value instead of the K-th best score.
+//     slack < 0: exactly K are kept and the threshold is the K-th best score.
 // `hist` is this wave's kSelectHistWords LDS words.  All 64 lanes must call it.
-__device__ __forceinline__ float wave_select_topk(uint32_t* keys, int32_t* idx, int n, int K,
-                                                  uint32_t* hist) {
+__device__ __forceinline__ float wave_keep_topk(uint32_t* keys, int32_t* idx, int& n, int K,
+                                                uint32_t* hist, int slack) {
   wave_mem_fence();
   uint32_t prefix = 0, pmask = 0;
   int krem = K;
   radix_step<2048>(keys, n, hist, 21, prefix, pmask, krem);
-  radix_step<2048>(keys, n, hist, 10, prefix, pmask, krem);
-  radix_step<1024>(keys, n, hist, 0, prefix, pmask, krem);
-  const uint32_t kth = prefix;
-  const int keep_eq = krem;  // entries equal to kth to keep, earliest first
+  radix_count<2048>(keys, n, hist, 10, prefix, pmask);
+  const int in_bucket = radix_pick<2048>(hist, 10, prefix, pmask, krem);
+  // entries at or above the bucket: K - krem above it, in_bucket inside
+  bool bucket = slack >= 0 && K - krem + in_bucket <= K + slack;
+  if (bucket) {
+    const float lo = key_to_float(prefix);
+    bucket = lo == lo;  // a bucket whose lowest key is no number keeps the exact path
+  }
+  if (!bucket) radix_step<1024>(keys, n, hist, 0, prefix, pmask, krem);
+  const uint32_t kth = prefix;  // exact: the K-th best key; bucket: its lowest key
+  const int keep_eq = krem;     // exact: entries equal to kth to keep, earliest first
   const int l = lane_id();
   int out = 0, eq_seen = 0;
   constexpr int kU = 8;  // chunks of 64 loaded together
@@ -202,7 +250,7 @@ __device__ __forceinline__ float wave_select_topk(uint32_t* keys, int32_t* idx, 
       const bool gt = in && key > kth;
       const bool eq = in && key == kth;
       const uint64_t eqm = ballot(eq);
-      const bool keep = gt || (eq && eq_seen + rank_below(eqm) < keep_eq);
+      const bool keep = gt || (eq && (bucket || eq_seen + rank_below(eqm) < keep_eq));
       eq_seen += popc(eqm);
       const uint64_t km = ballot(keep);
       if (keep) {
@@ -213,8 +261,22 @@ __device__ __forceinline__ float wave_select_topk(uint32_t* keys, int32_t* idx, 
       out += popc(km);
     }
   }
+  n = out;
   wave_mem_fence();
   return key_to_float(kth);
+}
+
+// A compaction during the stream may keep up to this many entries beyond K
+// (the whole 22-bit key bucket of the K-th best) instead of a third pass; the
+// buffers' headroom (cap - 192 >= 2K + 1856 entries before a compaction is
+// due) leaves room for them.
+constexpr int kCompactSlack = 256;
+
+// The exact selection: keep the top K of n > K entries; returns the K-th
+// largest score.
+__device__ __forceinline__ float wave_select_topk(uint32_t* keys, int32_t* idx, int n, int K,
+                                                  uint32_t* hist) {
+  return wave_keep_topk(keys, idx, n, K, hist, -1);
 }
 
 }  // namespace dsaidx

@@ -24,7 +24,7 @@ struct ScanArgs {
   int pos_stride;
   const int32_t* bank;
   int bank_stride, group;
-  int K, cap;              // top-K; candidate-buffer entries per row (>= 2K + 64, < 65536)
+  int K, cap;              // top-K; candidate-buffer entries per row (>= 2K + 2048, < 65536)
   uint32_t* cand_key;      // [nq, cap] workspace
   int32_t* cand_idx;       // [nq, cap] workspace
   int32_t* out_idx;        // [nq, out_stride]

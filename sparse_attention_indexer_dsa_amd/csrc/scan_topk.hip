@@ -311,8 +311,7 @@ __global__ void __launch_bounds__(WPB * 64, 2) scan_topk_kernel(const ScanArgs a
     if (i > 0 && s_need[buf2] && active && cnt + nst > args.K) {
       flush();
       wave_mem_fence();  // the buffer's stores land before the selection reads it
-      thr = wave_select_topk(ckey, cidx, cnt, args.K, hist);
-      cnt = args.K;
+      thr = wave_keep_topk(ckey, cidx, cnt, args.K, hist, kCompactSlack);
     } else if (active && nst > kStageEntries - 64) {
       flush();
     }

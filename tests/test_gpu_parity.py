@@ -187,6 +187,16 @@ def test_dense_kernel_compaction(dsa):
     _prefill_check(dsa, wl2, rows=_rows(4000, 32, 15))
 
 
+@pytest.mark.parametrize("H,d,dtype,K", [(64, 128, "fp8", 16), (48, 128, "bf16", 40), (8, 32, "bf16", 8),
+                                         (16, 64, "fp8", 24)])
+def test_compaction_buckets(dsa, H, d, dtype, K):
+    """Normal scores, small K over 6000 keys: most compactions stop after two
+    radix digits and keep the K-th best's whole 22-bit key bucket; the final
+    selection must still be the exact top K (dense and general kernels)."""
+    wl = make_prefill(T=6000, H=H, d=d, topk=K, dtype=dtype, dist="normal", seed=70 + H + K)
+    _prefill_check(dsa, wl, rows=_rows(6000, 40, 70 + H))
+
+
 @pytest.mark.parametrize("Tq,q_pos0,K", [(5, 100, 32), (13, 0, 200), (1, 2047, 2048), (9, 60, 2048)])
 def test_dense_kernel_partial_workgroups(dsa, Tq, q_pos0, K):
     """Query counts that leave waves of the first workgroup idle, chunks that
