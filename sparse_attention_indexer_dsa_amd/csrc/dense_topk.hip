@@ -516,15 +516,8 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   __builtin_amdgcn_s_waitcnt(0x3F70);
   if (!active) return;
   flush();
-  wave_mem_fence();
-  if (cnt > args.K) wave_keep_topk(ckey, cidx, cnt, args.K, hist, -1);
-  int32_t* oidx = args.out_idx + (int64_t)j * args.out_stride;
-  float* osc = args.out_score ? args.out_score + (int64_t)j * args.out_stride : nullptr;
-  for (int p = l; p < args.K; p += 64) {
-    const bool v = p < cnt;
-    oidx[p] = v ? cidx[p] : -1;
-    if (osc) osc[p] = v ? __uint_as_float(ckey[p]) : -__builtin_inff();
-  }
+  wave_emit_topk<32>(ckey, cidx, cnt, args.K, hist, args.out_idx + (int64_t)j * args.out_stride,
+                     args.out_score ? args.out_score + (int64_t)j * args.out_stride : nullptr);
 }
 
 }  // namespace

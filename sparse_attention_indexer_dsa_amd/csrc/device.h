@@ -167,7 +167,8 @@ __device__ __forceinline__ int radix_pick(const uint32_t* hist, int shift, uint3
 // (compared through order_key): histogram digit (key >> shift) & (NBINS-1) of
 // the entries whose key matches `prefix` on `pmask` into `hist` (this wave's
 // kSelectHistWords LDS words, NBINS <= 2048 16-bit counters).
-template <int NBINS>
+// B loads per lane are kept in flight (the buffer usually sits in HBM).
+template <int NBINS, int B = 16>
 __device__ __forceinline__ void radix_count(const uint32_t* keys, int n, uint32_t* hist, int shift,
                                             uint32_t prefix, uint32_t pmask) {
   const int l = lane_id();
@@ -179,24 +180,24 @@ __device__ __forceinline__ void radix_count(const uint32_t* keys, int n, uint32_
       hist_add<NBINS>(hist, k, shift);
     }
   };
-  // 16 independent loads in flight per lane: the buffer usually sits in HBM
-  int e = l;
-  for (; e + 15 * 64 < n; e += 16 * 64) {
-    uint32_t k[16];
+  // every batch, the last one too, issues all its loads before the first
+  // use: a buffer costs ceil(n / (64 B)) memory round trips
+  for (int e0 = l; e0 < n; e0 += B * 64) {
+    uint32_t k[B];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) k[u] = keys[e + 64 * u];
+    for (int u = 0; u < B; ++u) k[u] = e0 + 64 * u < n ? keys[e0 + 64 * u] : 0u;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) count(k[u]);
+    for (int u = 0; u < B; ++u)
+      if (e0 + 64 * u < n) count(k[u]);
   }
-  for (; e < n; e += 64) count(keys[e]);
   wave_lds_sync();
 }
 // One radix digit step: count, then find the digit holding the krem-th
 // largest matching entry.  Updates prefix/pmask/krem; wave-uniform.
-template <int NBINS>
+template <int NBINS, int B = 16>
 __device__ __forceinline__ void radix_step(const uint32_t* keys, int n, uint32_t* hist, int shift,
                                            uint32_t& prefix, uint32_t& pmask, int& krem) {
-  radix_count<NBINS>(keys, n, hist, shift, prefix, pmask);
+  radix_count<NBINS, B>(keys, n, hist, shift, prefix, pmask);
   radix_pick<NBINS>(hist, shift, prefix, pmask, krem);
 }
 
@@ -277,6 +278,63 @@ constexpr int kCompactSlack = 256;
 __device__ __forceinline__ float wave_select_topk(uint32_t* keys, int32_t* idx, int n, int K,
                                                   uint32_t* hist) {
   return wave_keep_topk(keys, idx, n, K, hist, -1);
+}
+
+// The final selection, written straight into a query's output row: the top
+// K of the wave's n buffer entries (all of them when n <= K) in buffer order,
+// i.e. ascending key index, then -1 / -inf padding up to K.  The buffer is
+// read B entries per lane at a time (the caller's registers are free by now).
+// osc may be null.  `hist` is this wave's kSelectHistWords LDS words.
+template <int B>
+__device__ __forceinline__ void wave_emit_topk(const uint32_t* keys, const int32_t* idx, int n,
+                                               int K, uint32_t* hist, int32_t* oidx, float* osc) {
+  wave_mem_fence();
+  const bool select = n > K;
+  uint32_t kth = 0;
+  int keep_eq = 0;
+  if (select) {
+    uint32_t prefix = 0, pmask = 0;
+    int krem = K;
+    radix_step<2048, B>(keys, n, hist, 21, prefix, pmask, krem);
+    radix_step<2048, B>(keys, n, hist, 10, prefix, pmask, krem);
+    radix_step<1024, B>(keys, n, hist, 0, prefix, pmask, krem);
+    kth = prefix;
+    keep_eq = krem;
+  }
+  const int l = lane_id();
+  int out = 0, eq_seen = 0;
+  constexpr int kU = B / 2;  // chunks of 64 (score + index) loaded together
+  for (int base = 0; base < n; base += 64 * kU) {
+    uint32_t raw[kU];
+    int32_t id[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int e = base + 64 * u + l;
+      raw[u] = e < n ? keys[e] : 0u;
+      id[u] = e < n ? idx[e] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int e = base + 64 * u + l;
+      const bool in = e < n;
+      const uint32_t key = order_key(__uint_as_float(raw[u]));
+      const bool eq = in && key == kth;
+      const uint64_t eqm = ballot(eq);
+      const bool keep = in && (!select || key > kth || (eq && eq_seen + rank_below(eqm) < keep_eq));
+      eq_seen += popc(eqm);
+      const uint64_t km = ballot(keep);
+      if (keep) {
+        const int p = out + rank_below(km);
+        oidx[p] = id[u];
+        if (osc) osc[p] = __uint_as_float(raw[u]);
+      }
+      out += popc(km);
+    }
+  }
+  for (int p = out + l; p < K; p += 64) {
+    oidx[p] = -1;
+    if (osc) osc[p] = -__builtin_inff();
+  }
 }
 
 }  // namespace dsaidx

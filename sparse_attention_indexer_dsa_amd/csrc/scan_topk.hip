@@ -311,7 +311,8 @@ __global__ void __launch_bounds__(WPB * 64, 2) scan_topk_kernel(const ScanArgs a
     if (i > 0 && s_need[buf2] && active && cnt + nst > args.K) {
       flush();
       wave_mem_fence();  // the buffer's stores land before the selection reads it
-      thr = wave_keep_topk(ckey, cidx, cnt, args.K, hist, kCompactSlack);
+      thr = wave_select_topk(ckey, cidx, cnt, args.K, hist);
+      cnt = args.K;
     } else if (active && nst > kStageEntries - 64) {
       flush();
     }
@@ -360,18 +361,8 @@ __global__ void __launch_bounds__(WPB * 64, 2) scan_topk_kernel(const ScanArgs a
 
   if (!active) return;
   flush();
-  wave_mem_fence();
-  if (cnt > args.K) {
-    wave_select_topk(ckey, cidx, cnt, args.K, hist);
-    cnt = args.K;
-  }
-  int32_t* oidx = args.out_idx + (int64_t)j * args.out_stride;
-  float* osc = args.out_score ? args.out_score + (int64_t)j * args.out_stride : nullptr;
-  for (int p = l; p < args.K; p += 64) {
-    const bool v = p < cnt;
-    oidx[p] = v ? cidx[p] : -1;
-    if (osc) osc[p] = v ? __uint_as_float(ckey[p]) : -__builtin_inff();
-  }
+  wave_emit_topk<16>(ckey, cidx, cnt, args.K, hist, args.out_idx + (int64_t)j * args.out_stride,
+                     args.out_score ? args.out_score + (int64_t)j * args.out_stride : nullptr);
 }
 
 template <int DT, int MT, int D, bool BANK, int WPB>
