@@ -225,18 +225,19 @@ struct DecodeWs {
 };
 
 // keys per scan workgroup: about 512 workgroups per call (two per CU), a
-// multiple of 256 keys and at most what one workgroup's LDS score stage holds
-static int64_t decode_keys_per_block(int B, int64_t Nmax) {
-  const int64_t target = ((int64_t)B * Nmax + 511) / 512;
+// multiple of 256 keys and at most what one workgroup's LDS score stages
+// hold; R rows per scan workgroup (they share its keys)
+static int64_t decode_keys_per_block(int B, int64_t Nmax, int R = 1) {
+  const int64_t target = ((int64_t)(B / R) * Nmax + 511) / 512;
   int64_t kpb = (target + 255) / 256 * 256;
   const int64_t row = (Nmax + 255) / 256 * 256;
   if (kpb > row) kpb = row;
-  if (kpb > kDecMaxKpb) kpb = kDecMaxKpb;
+  if (kpb > dec_max_kpb(R)) kpb = dec_max_kpb(R);
   return kpb < 256 ? 256 : kpb;
 }
 
-static DecodeWs decode_ws(int B, int64_t Nmax) {
-  const size_t kpb = (size_t)decode_keys_per_block(B, Nmax);
+static DecodeWs decode_ws(int B, int64_t Nmax, int R = 1) {
+  const size_t kpb = (size_t)decode_keys_per_block(B, Nmax, R);
   const size_t nblk = ((size_t)Nmax + kpb - 1) / kpb;
   DecodeWs w{};
   w.hist = 0;
@@ -253,10 +254,11 @@ static DecodeWs decode_ws(int B, int64_t Nmax) {
 }
 
 // The decode pipeline's arguments over `rows` rows of at most Nmax keys, its
-// workspace at ws (decode_ws(rows, Nmax).total bytes).
+// workspace at ws (decode_ws(rows, Nmax, R).total bytes), R rows per scan
+// workgroup.
 static DecodeArgs decode_args(const void* q, const float* w, const int32_t* lens, int rows,
                               int64_t Nmax, int H, int d, int K, void* ws, int32_t* out_idx,
-                              float* out_score) {
+                              float* out_score, int R = 1) {
   DecodeArgs a{};
   a.q = q;
   a.w = w;
@@ -266,9 +268,10 @@ static DecodeArgs decode_args(const void* q, const float* w, const int32_t* lens
   a.d = d;
   a.Nmax = Nmax;
   a.K = K;
-  const DecodeWs lay = decode_ws(rows, Nmax);
+  a.scan_rows = R;
+  const DecodeWs lay = decode_ws(rows, Nmax, R);
   uint8_t* base = (uint8_t*)ws;
-  a.kpb = decode_keys_per_block(rows, Nmax);
+  a.kpb = decode_keys_per_block(rows, Nmax, R);
   a.nblk = (int)((Nmax + a.kpb - 1) / a.kpb);
   a.hist = (uint32_t*)(base + lay.hist);
   a.cand_cnt = (int32_t*)(a.hist + (size_t)rows * kDecHistBins);
@@ -505,7 +508,16 @@ struct MtpWs {
   size_t a_kc, a_ks, a_len, r_kc, r_ks, r_len, r_len2, bank, pq, pw, gk, gs, dec, total;
 };
 
-static MtpWs mtp_ws(int B, int64_t Nmax, int m, int H, int d, int G, int P, unsigned flags,
+// anchor rows per scan workgroup: all the anchors of a window (up to 4) read
+// the same cache, so one pass over it serves them when their heads fit
+static int mtp_anchor_rows(int B, int m, int Hs, int G) {
+  const int ngs = m / G;
+  for (int R : {4, 2})
+    if (ngs % R == 0 && dec_scan_rows_ok(R, Hs, B * ngs)) return R;
+  return 1;
+}
+
+static MtpWs mtp_ws(int B, int64_t Nmax, int m, int H, int Hs, int d, int G, int P, unsigned flags,
                     bool bank_in_ws) {
   const size_t na = (size_t)B * (m / G), nr = (size_t)B * m, cand = (size_t)P + G - 1;
   MtpWs w{};
@@ -523,7 +535,7 @@ static MtpWs mtp_ws(int B, int64_t Nmax, int m, int H, int d, int G, int P, unsi
   w.gk = w.pw + (pool ? align_up(na * H * 4u) : 0);
   w.gs = w.gk + align_up(na * cand * d);
   w.dec = w.gs + align_up(na * cand * 4u);
-  size_t dw = decode_ws((int)na, Nmax).total;
+  size_t dw = decode_ws((int)na, Nmax, mtp_anchor_rows(B, m, Hs, G)).total;
   const size_t dr = decode_ws((int)nr, Nmax).total, db = decode_ws((int)nr, (int64_t)cand).total;
   if (dr > dw) dw = dr;
   if (db > dw) dw = db;
@@ -533,9 +545,9 @@ static MtpWs mtp_ws(int B, int64_t Nmax, int m, int H, int d, int G, int P, unsi
 
 size_t indexer_mtp_workspace_size(int B, int64_t Nmax, int m, int H, int Hs, int d, int G, int P,
                                   int topk, unsigned flags) {
-  (void)Hs; (void)topk;
+  (void)topk;
   if (B <= 0 || Nmax <= 0 || m <= 0 || G <= 0 || m % G || P <= 0 || H <= 0 || d <= 0) return 0;
-  return mtp_ws(B, Nmax, m, H, d, G, P, flags, true).total;
+  return mtp_ws(B, Nmax, m, H, Hs, d, G, P, flags, true).total;
 }
 
 int64_t indexer_mtp_pairs(const int32_t* prefix_lens, int B, int64_t Nmax, int m, int G, int P,
@@ -593,7 +605,7 @@ int indexer_mtp(const void* q, const uint8_t* k_cache, const float* k_scale, con
     return fail(DSAIDX_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
   if (((uintptr_t)k_scale & 3u) || ((uintptr_t)prefix_lens & 3u))
     return fail(DSAIDX_ERR_INVALID_ARG, "k_scale and prefix_lens must be 4-byte aligned");
-  const MtpWs lay = mtp_ws(B, Nmax, m, H, d, G, P, flags, out_bank == nullptr);
+  const MtpWs lay = mtp_ws(B, Nmax, m, H, Hs, d, G, P, flags, out_bank == nullptr);
   rc = check_ws(ws, ws_bytes, lay.total);
   if (rc) return rc;
   if (B == 0) return ok();
@@ -652,7 +664,8 @@ int indexer_mtp(const void* q, const uint8_t* k_cache, const float* k_scale, con
   // 1. anchor scan: row (b, g) ranks its anchor's N + gG visible keys with
   //    the group indexer and keeps the best P, ascending (Eq. (8), (13));
   //    rows of windows that fall back have no keys and come out all -1
-  DecodeArgs aa = decode_args(gq, gw, t.a_len, na, Nmax, Hs, d, P, base + lay.dec, bank, nullptr);
+  DecodeArgs aa = decode_args(gq, gw, t.a_len, na, Nmax, Hs, d, P, base + lay.dec, bank, nullptr,
+                              mtp_anchor_rows(B, m, Hs, G));
   aa.row_kc = t.a_kc;
   aa.row_ks = t.a_ks;
   e = launch_decode(aa, st);

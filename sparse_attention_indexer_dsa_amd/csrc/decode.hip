@@ -95,37 +95,53 @@ struct DecTile {
   u32x4 v[kVec];
 };
 
-template <int MT, int D>
+// R rows per workgroup (R > 1: 8 heads each, one shared key source): the R
+// queries' heads fill 8R rows of the same MFMAs, so the keys are read once
+// for all of them; each row keeps its own score stage, histogram and lists.
+template <int MT, int D, int R>
 __global__ void __launch_bounds__(kDecThreads, 2) decode_scan_kernel(const DecodeArgs args) {
+  static_assert(R == 1 || MT == 1, "several rows per workgroup share one 32-row MFMA tile");
   constexpr int kSteps = D / 16;  // bf16 k-steps
   constexpr int kHalf = D / 2;    // fp8 bytes of a lane's k-half
   constexpr int kVec = DecTile<D>::kVec;
-  __shared__ uint32_t s_hist[kDecHistBins / 2];  // two 16-bit counts per word
-  __shared__ float s_score[kDecMaxKpb];
+  constexpr int kStageKeys = dec_max_kpb(R);
+  __shared__ uint32_t s_hist[R][kDecHistBins / 2];  // two 16-bit counts per word
+  __shared__ float s_score[R][kStageKeys];
   __shared__ int s_tmp[kDecWaves];
   __shared__ int s_res[4];
-  const int b = blockIdx.y;
+  const int rg = blockIdx.y;  // rows rg*R .. rg*R + R-1
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int l = tid & 63;
   const int h = l >> 5, col = l & 31;
-  int64_t n = args.seq_lens[b];
-  n = n < 0 ? 0 : (n > args.Nmax ? args.Nmax : n);
   const int64_t blk0 = (int64_t)blockIdx.x * args.kpb;
+  int span_r[R];  // keys of each row inside this workgroup's span
+  int64_t n = 0;  // the longest row
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    int64_t nr = args.seq_lens[rg * R + r];
+    nr = nr < 0 ? 0 : (nr > args.Nmax ? args.Nmax : nr);
+    n = nr > n ? nr : n;
+    const int64_t left_r = nr - blk0;
+    span_r[r] = left_r <= 0 ? 0 : (int)(left_r < args.kpb ? left_r : args.kpb);
+  }
   if (blk0 >= n) return;
   // loop trips of this workgroup: 768 keys each, none wholly past the row end
   const int64_t left = n - blk0 < args.kpb ? n - blk0 : args.kpb;
   const int trips = (int)((left + kDecKeysPerPass - 1) / kDecKeysPerPass);
-  for (int i = tid; i < kDecHistBins / 2; i += kDecThreads) s_hist[i] = 0;
+  for (int i = tid; i < R * kDecHistBins / 2; i += kDecThreads) (&s_hist[0][0])[i] = 0;
 
+  // the R rows' queries are consecutive in q [rows, H, d] and w [rows, H]:
+  // together they are one query of R*H heads
+  const int HR = R * args.H;
   v8bf a[MT][kSteps];
   float wv[MT][16];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     const int head = 32 * m + col;
-    const bool hv = head < args.H;
+    const bool hv = head < HR;
     const uint8_t* qrow =
-        (const uint8_t*)args.q + ((int64_t)b * args.H + (hv ? head : 0)) * (2 * D);
+        (const uint8_t*)args.q + ((int64_t)rg * HR + (hv ? head : 0)) * (2 * D);
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
       u32x4 v = hv ? *(const u32x4*)(qrow + h * D + 16 * s) : u32x4{0, 0, 0, 0};
@@ -134,7 +150,7 @@ __global__ void __launch_bounds__(kDecThreads, 2) decode_scan_kernel(const Decod
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int hr = 32 * m + 8 * (r >> 2) + 4 * h + (r & 3);
-      wv[m][r] = hr < args.H ? args.w[(int64_t)b * args.H + hr] : 0.0f;
+      wv[m][r] = hr < HR ? args.w[(int64_t)rg * HR + hr] : 0.0f;
     }
   }
   __syncthreads();
@@ -146,8 +162,9 @@ __global__ void __launch_bounds__(kDecThreads, 2) decode_scan_kernel(const Decod
   // loop issues no global stores at all.
   const int64_t blk_end = n < blk0 + args.kpb ? n : blk0 + args.kpb;
   const int span = (int)(blk_end - blk0);
-  const uint8_t* kc_row = args.row_kc ? args.row_kc[b] : args.kc + (int64_t)b * args.Nmax * D;
-  const float* ks_row = args.row_ks ? args.row_ks[b] : args.k_scale + (int64_t)b * args.Nmax;
+  const int b0 = rg * R;  // the row whose key source the workgroup reads
+  const uint8_t* kc_row = args.row_kc ? args.row_kc[b0] : args.kc + (int64_t)b0 * args.Nmax * D;
+  const float* ks_row = args.row_ks ? args.row_ks[b0] : args.k_scale + (int64_t)b0 * args.Nmax;
   const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(kc_row + blk0 * D), (short)0, span * D, kBufferWord3);
   const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
@@ -180,19 +197,33 @@ __global__ void __launch_bounds__(kDecThreads, 2) decode_scan_kernel(const Decod
       for (int m = 0; m < MT; ++m)
         acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m][s], bf, acc[m], 0, 0, 0);
     }
-    float s0 = 0.0f, s1 = 0.0f;
+    // row r's heads are MFMA rows 8r .. 8r+7: accumulators 4r .. 4r+3 of
+    // this lane (heads 4h .. 4h+3 of the row); R == 1 sums every head
+    constexpr int kAcc = R == 1 ? 16 : 4;
 #pragma unroll
-    for (int m = 0; m < MT; ++m) gated_relu_sum16(wv[m], acc[m], s0, s1);
-    float sc = s0 + s1;
-    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sc), __float_as_uint(sc), false,
-                                               false);
-    sc = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * ks;
-    sc += 0.0f;  // -0 -> +0
-    // lanes l and l+32 hold the same key: the low half records it
-    if (l < 32 && key < span) {
-      s_score[key] = sc;
-      const uint32_t bin = order_key(sc) >> (32 - kDecHistBits);
-      atomicAdd(&s_hist[bin >> 1], 1u << (16 * (bin & 1)));
+    for (int r = 0; r < R; ++r) {
+      float s0 = 0.0f, s1 = 0.0f;
+      if constexpr (R == 1) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) gated_relu_sum16(wv[m], acc[m], s0, s1);
+      } else {
+#pragma unroll
+        for (int i = kAcc * r; i < kAcc * (r + 1); i += 2) {
+          s0 = fmaf(wv[0][i], relu_bits(acc[0][i]), s0);
+          s1 = fmaf(wv[0][i + 1], relu_bits(acc[0][i + 1]), s1);
+        }
+      }
+      float sc = s0 + s1;
+      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sc), __float_as_uint(sc), false,
+                                                 false);
+      sc = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * ks;
+      sc += 0.0f;  // -0 -> +0
+      // lanes l and l+32 hold the same key: the low half records it
+      if (l < 32 && key < span_r[r]) {
+        s_score[r][key] = sc;
+        const uint32_t bin = order_key(sc) >> (32 - kDecHistBits);
+        atomicAdd(&s_hist[r][bin >> 1], 1u << (16 * (bin & 1)));
+      }
     }
   };
 
@@ -230,57 +261,66 @@ __global__ void __launch_bounds__(kDecThreads, 2) decode_scan_kernel(const Decod
     fence();
   }
   __syncthreads();
-  uint32_t* ghist = args.hist + (int64_t)b * kDecHistBins;
-  for (int i = tid; i < kDecHistBins / 2; i += kDecThreads) {
-    const uint32_t c = s_hist[i];
-    if (c & 0xFFFFu) atomicAdd(ghist + 2 * i, c & 0xFFFFu);
-    if (c >> 16) atomicAdd(ghist + 2 * i + 1, c >> 16);
-  }
-  // The K-th best score of the span is a lower bound of the row's K-th best:
-  // scores below it cannot reach the row's top K and are not kept.  Its top
-  // 12 bits come from the histogram, the next 12 from a second histogram over
-  // the span's scores inside that bin; the list keeps every score whose top
-  // 24 bits reach the result.  A span of at most K keys keeps everything.
-  uint32_t keep_from = 0;  // keep scores with (order key >> 8) >= keep_from
-  if (span > args.K) {
-    constexpr int kPer = kDecHistBins / kDecThreads;
-    auto bins16 = [&](int t, int i) __attribute__((always_inline)) {
-      const int bin = t * kPer + i;
-      return (int)((s_hist[bin >> 1] >> (16 * (bin & 1))) & 0xFFFFu);
-    };
-    block_find_digit<kDecWaves>(kPer, bins16, args.K, s_tmp, s_res);
-    const uint32_t bloc = (uint32_t)s_res[0];
-    const int krem = s_res[1];
-    for (int i = tid; i < kDecHistBins / 2; i += kDecThreads) s_hist[i] = 0;
-    __syncthreads();
-    for (int e = tid; e < span; e += kDecThreads) {
-      const uint32_t key = order_key(s_score[e]);
-      if ((key >> 20) == bloc) {
-        const uint32_t sub = (key >> 8) & 0xFFFu;
-        atomicAdd(&s_hist[sub >> 1], 1u << (16 * (sub & 1)));
+  for (int r = 0; r < R; ++r) {
+    const int b = rg * R + r;
+    const int span_b = span_r[r];
+    if (span_b == 0) continue;  // the row ends before this span
+    uint32_t* hst = s_hist[r];
+    const float* scr = s_score[r];
+    uint32_t* ghist = args.hist + (int64_t)b * kDecHistBins;
+    for (int i = tid; i < kDecHistBins / 2; i += kDecThreads) {
+      const uint32_t c = hst[i];
+      if (c & 0xFFFFu) atomicAdd(ghist + 2 * i, c & 0xFFFFu);
+      if (c >> 16) atomicAdd(ghist + 2 * i + 1, c >> 16);
+    }
+    // The K-th best score of the span is a lower bound of the row's K-th
+    // best: scores below it cannot reach the row's top K and are not kept.
+    // Its top 12 bits come from the histogram, the next 12 from a second
+    // histogram over the span's scores inside that bin; the list keeps every
+    // score whose top 24 bits reach the result.  A span of at most K keys
+    // keeps everything.
+    uint32_t keep_from = 0;  // keep scores with (order key >> 8) >= keep_from
+    if (span_b > args.K) {
+      constexpr int kPer = kDecHistBins / kDecThreads;
+      auto bins16 = [&](int t, int i) __attribute__((always_inline)) {
+        const int bin = t * kPer + i;
+        return (int)((hst[bin >> 1] >> (16 * (bin & 1))) & 0xFFFFu);
+      };
+      block_find_digit<kDecWaves>(kPer, bins16, args.K, s_tmp, s_res);
+      const uint32_t bloc = (uint32_t)s_res[0];
+      const int krem = s_res[1];
+      for (int i = tid; i < kDecHistBins / 2; i += kDecThreads) hst[i] = 0;
+      __syncthreads();
+      for (int e = tid; e < span_b; e += kDecThreads) {
+        const uint32_t key = order_key(scr[e]);
+        if ((key >> 20) == bloc) {
+          const uint32_t sub = (key >> 8) & 0xFFFu;
+          atomicAdd(&hst[sub >> 1], 1u << (16 * (sub & 1)));
+        }
+      }
+      __syncthreads();
+      block_find_digit<kDecWaves>(kPer, bins16, krem, s_tmp, s_res);
+      keep_from = (bloc << 12) | (uint32_t)s_res[0];
+    }
+    // compact list of the kept scores, in ascending key order
+    const int per = (span_b + kDecThreads - 1) / kDecThreads;
+    const int e0 = tid * per, e1 = e0 + per < span_b ? e0 + per : span_b;
+    int mine = 0;
+    for (int e = e0; e < e1; ++e) mine += (order_key(scr[e]) >> 8) >= keep_from;
+    int total;
+    int pos = block_excl_scan<kDecWaves>(mine, s_tmp, total);
+    const int64_t lbase = ((int64_t)b * args.nblk + blockIdx.x) * args.kpb;
+    for (int e = e0; e < e1; ++e) {
+      const float v = scr[e];
+      if ((order_key(v) >> 8) >= keep_from) {
+        args.cl_idx[lbase + pos] = (int32_t)(blk0 + e);
+        args.cl_sc[lbase + pos] = v;
+        ++pos;
       }
     }
-    __syncthreads();
-    block_find_digit<kDecWaves>(kPer, bins16, krem, s_tmp, s_res);
-    keep_from = (bloc << 12) | (uint32_t)s_res[0];
+    if (tid == 0) args.cl_cnt[(int64_t)b * args.nblk + blockIdx.x] = total;
+    if (R > 1) __syncthreads();  // s_tmp and s_res serve the next row
   }
-  // compact list of the kept scores, in ascending key order
-  const int per = (span + kDecThreads - 1) / kDecThreads;
-  const int e0 = tid * per, e1 = e0 + per < span ? e0 + per : span;
-  int mine = 0;
-  for (int e = e0; e < e1; ++e) mine += (order_key(s_score[e]) >> 8) >= keep_from;
-  int total;
-  int pos = block_excl_scan<kDecWaves>(mine, s_tmp, total);
-  const int64_t lbase = ((int64_t)b * args.nblk + blockIdx.x) * args.kpb;
-  for (int e = e0; e < e1; ++e) {
-    const float v = s_score[e];
-    if ((order_key(v) >> 8) >= keep_from) {
-      args.cl_idx[lbase + pos] = (int32_t)(blk0 + e);
-      args.cl_sc[lbase + pos] = v;
-      ++pos;
-    }
-  }
-  if (tid == 0) args.cl_cnt[(int64_t)b * args.nblk + blockIdx.x] = total;
 }
 
 // One radix round over n LDS keys (only those matching prefix on pmask):
@@ -760,9 +800,20 @@ static hipError_t launch_dec(const DecodeArgs& a, hipStream_t stream) {
   // histograms and candidate counters are contiguous: one fill clears both
   hipError_t e = launch_fill_i32((int32_t*)a.hist, (int64_t)a.B * kDecHistBins + a.B, 0, stream);
   if (e != hipSuccess) return e;
-  if (a.nblk > 0)
-    hipLaunchKernelGGL((decode_scan_kernel<MT, D>), dim3((unsigned)a.nblk, (unsigned)a.B),
-                       dim3(kDecThreads), 0, stream, a);
+  const int R = a.scan_rows > 1 ? a.scan_rows : 1;
+  if (a.nblk > 0) {
+    const dim3 grid((unsigned)a.nblk, (unsigned)(a.B / R));
+    if constexpr (MT == 1) {
+      if (R == 2)
+        hipLaunchKernelGGL((decode_scan_kernel<1, D, 2>), grid, dim3(kDecThreads), 0, stream, a);
+      else if (R == 4)
+        hipLaunchKernelGGL((decode_scan_kernel<1, D, 4>), grid, dim3(kDecThreads), 0, stream, a);
+      else
+        hipLaunchKernelGGL((decode_scan_kernel<1, D, 1>), grid, dim3(kDecThreads), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((decode_scan_kernel<MT, D, 1>), grid, dim3(kDecThreads), 0, stream, a);
+    }
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.nblk > 0)
@@ -780,6 +831,9 @@ static hipError_t launch_dec(const DecodeArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  if (a.scan_rows > 1 && (!dec_scan_rows_ok(a.scan_rows, a.H, a.B) || !a.row_kc || !a.row_ks ||
+                          a.kpb > dec_max_kpb(a.scan_rows)))
+    return hipErrorInvalidValue;
   const int MT = a.H <= 32 ? 1 : 2;
   if (MT == 1) {
     if (a.d == 64) return launch_dec<1, 64>(a, stream);

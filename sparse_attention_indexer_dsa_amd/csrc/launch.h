@@ -59,10 +59,13 @@ struct DecodeArgs {
   const uint8_t* const* row_kc;
   const float* const* row_ks;
   int skip_negative;  // rows with seq_lens < 0 write nothing (else: clamped to 0)
+  // rows per scan workgroup (1, 2 or 4; see dec_scan_rows_ok): rows rR .. rR+R-1
+  // share row r*R's key source and are scored in one pass over it
+  int scan_rows;
   int B, H, d;
   int64_t Nmax;
   int K;
-  int64_t kpb;            // keys per scan workgroup: a multiple of 256, <= kDecMaxKpb
+  int64_t kpb;            // keys per scan workgroup: a multiple of 256, <= dec_max_kpb(scan_rows)
   int nblk;               // scan workgroups per row: ceil(Nmax / kpb)
   uint32_t* hist;         // [B, kDecHistBins] workspace, zeroed per call
   int32_t* cl_cnt;        // [B, nblk] entries of each workgroup's compact list
@@ -79,6 +82,11 @@ struct DecodeArgs {
 };
 constexpr int kDecKeysPerPass = 768;  // keys one scan workgroup scores per loop trip
 constexpr int kDecMaxKpb = 16384;     // keys per scan workgroup at most (its LDS score stage)
+// keys per scan workgroup at most when it scores R rows (R LDS score stages)
+constexpr int dec_max_kpb(int R) { return R == 1 ? kDecMaxKpb : kDecMaxKpb / 2 / R; }
+// Several rows per scan workgroup: 8 heads per row (R rows fill 8R MFMA rows),
+// R in {2, 4}, and the rows of a workgroup must share one key source.
+constexpr bool dec_scan_rows_ok(int R, int H, int B) { return (R == 2 || R == 4) && H == 8 && B % R == 0; }
 constexpr int kDecCandCap = 16384;    // threshold-bin candidates a row keeps in LDS
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

@@ -478,6 +478,19 @@ def test_mtp_mixed_windows_exact(dsa, G):
     assert (gb[:2] == -1).all() and (gb[2:] >= 0).all()
 
 
+@pytest.mark.parametrize("G,m,d", [(8, 16, 128), (4, 16, 128), (4, 32, 128), (4, 16, 64)])
+def test_mtp_shared_anchor_scan(dsa, G, m, d):
+    """An 8-head group indexer: the 2 or 4 anchors of a window (or of half a
+    window, m = 32) are scored in one pass over the cache.  Their lengths
+    differ by G keys, windows that fall back have no anchor keys, and the
+    banks and every refined row match exactly on integer inputs."""
+    P = 256
+    wl = make_mtp(B=4, N=3000, m=m, H=64, Hs=8, d=d, topk=64, G=G, P=P, dist="int", seed=80 + G + m + d,
+                  prefix_lens=[40, P + 1, 1700, 3000 - m + 1])
+    gi, _, gb = _mtp_check(dsa, wl)
+    assert (gb[:1] == -1).all() and (gb[1:] >= 0).all()
+
+
 def test_mtp_pooled_exact(dsa):
     wl = make_mtp(B=3, N=5000, m=16, H=64, Hs=64, d=128, topk=128, G=8, P=1024, dist="int", seed=54,
                   prefix_lens=[1500, 4985, 900])
