@@ -291,35 +291,73 @@ __global__ void __launch_bounds__(kDecThreads, 2) decode_scan_kernel(const Decod
       const int krem = s_res[1];
       for (int i = tid; i < kDecHistBins / 2; i += kDecThreads) hst[i] = 0;
       __syncthreads();
-      for (int e = tid; e < span_b; e += kDecThreads) {
-        const uint32_t key = order_key(scr[e]);
-        if ((key >> 20) == bloc) {
-          const uint32_t sub = (key >> 8) & 0xFFFu;
-          atomicAdd(&hst[sub >> 1], 1u << (16 * (sub & 1)));
+      // eight LDS reads in flight per thread, then their updates
+      for (int e0 = tid; e0 < span_b; e0 += 8 * kDecThreads) {
+        uint32_t kk[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int e = e0 + u * kDecThreads;
+          kk[u] = e < span_b ? order_key(scr[e]) : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (e0 + u * kDecThreads < span_b && (kk[u] >> 20) == bloc) {
+            const uint32_t sub = (kk[u] >> 8) & 0xFFFu;
+            atomicAdd(&hst[sub >> 1], 1u << (16 * (sub & 1)));
+          }
         }
       }
       __syncthreads();
       block_find_digit<kDecWaves>(kPer, bins16, krem, s_tmp, s_res);
       keep_from = (bloc << 12) | (uint32_t)s_res[0];
     }
-    // compact list of the kept scores, in ascending key order
-    const int per = (span_b + kDecThreads - 1) / kDecThreads;
-    const int e0 = tid * per, e1 = e0 + per < span_b ? e0 + per : span_b;
-    int mine = 0;
-    for (int e = e0; e < e1; ++e) mine += (order_key(scr[e]) >> 8) >= keep_from;
-    int total;
-    int pos = block_excl_scan<kDecWaves>(mine, s_tmp, total);
+    // compact list of the kept scores, in ascending key order: wave w takes
+    // the w-th quarter of the span, 64 consecutive keys per step (lane l key
+    // base + l: conflict-free LDS reads, coalesced list writes)
+    const int quarter = ((span_b + kDecWaves - 1) / kDecWaves + 63) / 64 * 64;
+    const int c0 = wave * quarter, c1 = c0 + quarter < span_b ? c0 + quarter : span_b;
+    // eight LDS reads in flight per lane, then their ballots
+    auto keys8 = [&](int base, uint32_t (&kk)[8]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = base + 64 * u + l;
+        kk[u] = e < c1 ? order_key(scr[e]) : 0u;
+      }
+    };
+    int mine = 0;  // wave-uniform
+    for (int base = c0; base < c1; base += 8 * 64) {
+      uint32_t kk[8];
+      keys8(base, kk);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) mine += popc(ballot(base + 64 * u + l < c1 && (kk[u] >> 8) >= keep_from));
+    }
+    if (l == 0) s_tmp[wave] = mine;
+    __syncthreads();
+    int pos = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      pos += w < wave ? s_tmp[w] : 0;
+      total += s_tmp[w];
+    }
     const int64_t lbase = ((int64_t)b * args.nblk + blockIdx.x) * args.kpb;
-    for (int e = e0; e < e1; ++e) {
-      const float v = scr[e];
-      if ((order_key(v) >> 8) >= keep_from) {
-        args.cl_idx[lbase + pos] = (int32_t)(blk0 + e);
-        args.cl_sc[lbase + pos] = v;
-        ++pos;
+    for (int base = c0; base < c1; base += 8 * 64) {
+      uint32_t kk[8];
+      keys8(base, kk);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = base + 64 * u + l;
+        const bool keep = e < c1 && (kk[u] >> 8) >= keep_from;
+        const uint64_t km = ballot(keep);
+        if (keep) {
+          const int p = pos + rank_below(km);
+          args.cl_idx[lbase + p] = (int32_t)(blk0 + e);
+          args.cl_sc[lbase + p] = key_to_float(kk[u]);
+        }
+        pos += popc(km);
       }
     }
     if (tid == 0) args.cl_cnt[(int64_t)b * args.nblk + blockIdx.x] = total;
-    if (R > 1) __syncthreads();  // s_tmp and s_res serve the next row
+    if (R > 1) __syncthreads();  // s_tmp, s_res and the histogram serve the next row
   }
 }
 
