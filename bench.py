@@ -14,7 +14,7 @@ bounded sample of the same inputs.
 Inputs are generated on the GPU before timing (resident in HBM); outputs,
 workspace and streams are allocated before the timed region.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--adindex] [--dsa16k] [--mtp] [--calib] [--group-query]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--adindex [--adindex-len T]] [--dsa16k] [--mtp] [--calib] [--group-query]
 """
 from __future__ import annotations
 
@@ -251,9 +251,9 @@ def bench_decode(dsa, args, log):
 
 def bench_adindex(dsa, args, log):
     from workloads import make_workload
-    T, H, d, K, G, P = 65536, 64, 128, 2048, 16, 8192
-    log("generating ADIndex inputs T=65536 bf16 on the GPU")
-    wl = make_workload(5, seed=args.seed, device="cuda")
+    T, H, d, K, G, P = args.adindex_len, 64, 128, 2048, 16, 8192
+    log(f"generating ADIndex inputs T={T} bf16 on the GPU")
+    wl = make_workload(5, seed=args.seed, device="cuda", T=T)
     t = wl.tensors
     out = torch.empty((T, K), dtype=torch.int32, device="cuda")
     out_pool = torch.empty((T, K), dtype=torch.int32, device="cuda")
@@ -293,7 +293,7 @@ def bench_adindex(dsa, args, log):
     def recall(o):
         return float(np.mean([len(np.intersect1d(x, y)) / len(y) for x, y in zip(o[sample].cpu().numpy(), b)]))
     rec, rec_pool = recall(out), recall(out_pool)
-    return dict(workload="ADIndex group token bank: T=65536, G=16, P=8192, H=Hs=64, d=128, top-2048, bf16",
+    return dict(workload=f"ADIndex group token bank: T={T}, G=16, P=8192, H=Hs=64, d=128, top-2048, bf16",
                 ms_per_step=res["adindex"], tflops=flops / (res["adindex"] * 1e-3) / 1e12,
                 gpairs_per_s=pairs / (res["adindex"] * 1e-3) / 1e9, pairs=pairs,
                 dense_ms=res["dense"], dense_tflops=2 * H * d * dense_pairs / (res["dense"] * 1e-3) / 1e12,
@@ -469,6 +469,8 @@ def main():
     ap.add_argument("--cpu-decode-rows", type=int, default=32)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--adindex", action="store_true", help="also time the ADIndex group-bank workload")
+    ap.add_argument("--adindex-len", type=int, default=65536, metavar="T",
+                    help="sequence length of the ADIndex workload (65536; the pages quote 262144)")
     ap.add_argument("--mtp", action="store_true", help="also time MTP verification windows at 256K")
     ap.add_argument("--dsa16k", action="store_true", help="also time the 16K bf16 DSA prefill layer")
     ap.add_argument("--calib", action="store_true", help="also time the calibration statistics kernels")
