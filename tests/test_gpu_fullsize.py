@@ -100,6 +100,26 @@ def test_decode_256k(dsa, dist):
     compare(gi.cpu().numpy()[rows], gs.cpu().numpy()[rows], ri, rs, dist == "int", score_of)
 
 
+def test_adindex_256k_bank(dsa):
+    """The pages' length, T=262144 (G=16, P=8192, 64-head group indexer,
+    integer inputs): the banks and refined rows of sampled groups match the
+    oracle exactly, early, in the middle and at the end of the sequence."""
+    T, G, P, K = 262144, 16, 8192, 2048
+    wl = make_workload(5, seed=7, device="cuda", dist="int", T=T)
+    t = wl.tensors
+    gi, gs, gb = dsa.indexer_group_bank(t["q"], t["k"], t["w"], t["qbar"], t["wbar"], 0, G, P, K, want_bank=True)
+    torch.cuda.synchronize()
+    rows = np.array([8224, 131077, 262143])
+    h = _host(t)
+    ri, rs, rb, pairs = oracle.group_bank(h["q"], h["k"], h["w"], h["qbar"], h["wbar"], "bf16", 0, G, P, K,
+                                          rows=rows, want_bank=True)
+    assert pairs == dsa.indexer_group_bank_pairs(T, 0, G, P)
+    gbank = gb.cpu().numpy()
+    for g in np.unique(rows // G):
+        assert np.array_equal(gbank[g], rb[g])
+    compare(gi.cpu().numpy()[rows], gs.cpu().numpy()[rows], ri, rs, True)
+
+
 @pytest.mark.parametrize("pool", [False, True])
 @pytest.mark.parametrize("dist", ["normal", "int"])
 def test_adindex_64k_bank(dsa, dist, pool):
