@@ -604,7 +604,7 @@ __device__ __forceinline__ void row_threshold(const DecodeArgs& args, int b, int
 
 // List entries a span workgroup loads per thread at once (strided by the
 // workgroup size, so every load is coalesced and all of them are in flight).
-constexpr int kSpanBatch = 8;
+constexpr int kSpanBatch = 16;
 
 // One workgroup per (span, row): counts the span's list entries above b* and
 // gathers those inside b* into the row's candidate array.
