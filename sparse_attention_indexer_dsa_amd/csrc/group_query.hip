@@ -7,8 +7,8 @@
 // over each complete group of G consecutive query rows.  Pooling reads the
 // latents and hidden states once (HBM-bound: the hidden states dominate); the
 // two query products are plain bf16 matrix products with fp32 accumulation on
-// the 32x32x16 bf16 MFMA, K contiguous in both operands, so every lane's
-// operand fragment is one 16-byte load; the gate's few heads are dot products;
+// the 32x32x16 bf16 MFMA, K contiguous in both operands, staged through LDS
+// in chunks of 64 k; the gate's few heads are dot products;
 // the rotary embedding (fp64 angles, the
 // positions reach 10^5 radians) and the bf16 rounding of the query follow in
 // their own small kernel.
@@ -83,55 +83,100 @@ __global__ void __launch_bounds__(kGqThreads) gq_pool_kernel(const GroupQueryArg
   }
 }
 
-// C = A B^T for A [M, K], B [N, K] bf16 (K contiguous, K % 16 == 0).  A
-// workgroup covers 128 x 128 of C, each wave 64 x 64 as 2 x 2 tiles of the
-// 32x32x16 bf16 MFMA (each operand fragment feeds two MFMAs).  Lane l's A
-// fragment of a tile is row l%32, k 8(l/32)..+7 of the k-step (one 16-byte
-// load), likewise for B; lane l then holds C[8(r/4) + 4(l/32) + r%4][l%32].
-// Rows past M or N are clamped on load and skipped on store.
+// C = A B^T for A [M, K], B [N, K] bf16 (K contiguous, K % 16 == 0), fp32
+// accumulation.  A workgroup covers 128 x 128 of C and walks K in chunks of
+// 64: each chunk of both operands (2 x 16 KB) is staged in LDS, double
+// buffered, and the next chunk's global loads (eight 16-byte loads per
+// thread, coalesced along K) are in flight while the current one is
+// multiplied.  Each wave computes 64 x 64 as 2 x 2 tiles of the 32x32x16 bf16
+// MFMA; lane l's A fragment of a tile and k-step is row l%32, k 8(l/32)..+7
+// (one 16-byte LDS read), likewise for B; lane l then holds
+// C[8(r/4) + 4(l/32) + r%4][l%32].  The MFMAs of every output tile run in
+// ascending k.  Rows past M or N are clamped on load and skipped on store; k
+// past K loads zeros.
 // MODE 0: C bf16 [M, N]; 1: C fp32 [M, N].
+constexpr int kGmTile = 128;                        // rows of C per workgroup (and columns)
+constexpr int kGmKc = 64;                           // k per LDS chunk
+constexpr int kGmRowBytes = kGmKc * 2;              // one operand row of a chunk: 8 x 16 B
+constexpr int kGmMatBytes = kGmTile * kGmRowBytes;  // 16 KB per operand and chunk
+// 16-byte chunk c of row r sits at slot c ^ ((r >> 1) & 7): any 16
+// consecutive rows put one chunk in 16 distinct 16-byte bank groups
+__device__ __forceinline__ int gm_slot(int r, int c) { return c ^ ((r >> 1) & 7); }
+
 template <int MODE>
 __global__ void __launch_bounds__(kGqThreads) gemm_nt_kernel(const uint16_t* A, const uint16_t* B, int M,
                                                              int N, int K, void* C) {
-  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int m0 = blockIdx.y * 128 + (wave >> 1) * 64, n0 = blockIdx.x * 128 + (wave & 1) * 64;
-  const uint16_t* ap[2];
-  const uint16_t* bp[2];
+  __shared__ __attribute__((aligned(16))) uint8_t s_op[2][2 * kGmMatBytes];  // [buffer][A rows | B rows]
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  const int mb = blockIdx.y * kGmTile, nb = blockIdx.x * kGmTile;
+  // this thread's eight chunks of a k-chunk: q = tid + 256i, A for q < 1024
+  // (row q/8, chunk q%8), B after
+  constexpr int kLoads = 2 * kGmMatBytes / 16 / kGqThreads;
+  const uint16_t* src[kLoads];
+  int soff[kLoads];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    ap[t] = A + (int64_t)min(m0 + 32 * t + (l & 31), M - 1) * K + (l >> 5) * 8;
-    bp[t] = B + (int64_t)min(n0 + 32 * t + (l & 31), N - 1) * K + (l >> 5) * 8;
+  for (int i = 0; i < kLoads; ++i) {
+    const int q = tid + kGqThreads * i;
+    const int mat = q / (kGmTile * 8), row = (q / 8) % kGmTile, c = q % 8;
+    const int lim = mat ? N : M;
+    const int grow = min((mat ? nb : mb) + row, lim - 1);
+    src[i] = (mat ? B : A) + (int64_t)grow * K + 8 * c;
+    soff[i] = mat * kGmMatBytes + row * kGmRowBytes + 16 * gm_slot(row, c);
   }
-  v16f acc[2][2] = {};
-  for (int k = 0; k < K; k += 32) {  // two k-steps' operands in flight
-    u32x4 av[2][2], bv[2][2];
+  u32x4 st[kLoads];
+  auto gload = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int i = 0; i < kLoads; ++i) {
+      const int c = (tid + kGqThreads * i) % 8;
+      st[i] = k0 + 8 * c < K ? *reinterpret_cast<const u32x4*>(src[i] + k0) : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto lstore = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) *reinterpret_cast<u32x4*>(&s_op[buf][soff[i]]) = st[i];
+  };
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  v16f acc[2][2] = {};
+  auto compute = [&](int buf) __attribute__((always_inline)) {
+    const uint8_t* sa = &s_op[buf][0];
+    const uint8_t* sb = &s_op[buf][kGmMatBytes];
+#pragma unroll
+    for (int s = 0; s < kGmKc / 16; ++s) {
+      const int c = 2 * s + (l >> 5);
+      v8bf af[2], bf[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const bool in = k + 16 * u < K;
-        av[u][t] = in ? *reinterpret_cast<const u32x4*>(ap[t] + k + 16 * u) : u32x4{0, 0, 0, 0};
-        bv[u][t] = in ? *reinterpret_cast<const u32x4*>(bp[t] + k + 16 * u) : u32x4{0, 0, 0, 0};
+        const int ra = wm + 32 * t + (l & 31), rb = wn + 32 * t + (l & 31);
+        af[t] = *reinterpret_cast<const v8bf*>(sa + ra * kGmRowBytes + 16 * gm_slot(ra, c));
+        bf[t] = *reinterpret_cast<const v8bf*>(sb + rb * kGmRowBytes + 16 * gm_slot(rb, c));
       }
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, av[u][i]),
-                                                              __builtin_bit_cast(v8bf, bv[u][j]), acc[i][j], 0, 0,
-                                                              0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  const int nk = (K + kGmKc - 1) / kGmKc;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kc = 0; kc < nk; ++kc) {
+    const bool more = kc + 1 < nk;
+    if (more) gload((kc + 1) * kGmKc);
+    compute(kc & 1);
+    if (more) lstore((kc + 1) & 1);
+    __syncthreads();
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int col = n0 + 32 * j + (l & 31);
+      const int col = nb + wn + 32 * j + (l & 31);
       if (col >= N) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = m0 + 32 * i + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+        const int row = mb + wm + 32 * i + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
         if (row >= M) continue;
         const int64_t o = (int64_t)row * N + col;
         const float v = acc[i][j][r];
@@ -218,7 +263,9 @@ hipError_t launch_group_query(const GroupQueryArgs& a, hipStream_t stream) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    auto grid = [&](int N) { return dim3((unsigned)((N + 127) / 128), (unsigned)((n + 127) / 128)); };
+    auto grid = [&](int N) {
+      return dim3((unsigned)((N + kGmTile - 1) / kGmTile), (unsigned)((n + kGmTile - 1) / kGmTile));
+    };
     // cbar = W_pool [max; min; mean]        [n, dc]  (bf16: the next product's operand)
     hipLaunchKernelGGL(gemm_nt_kernel<0>, grid(a.dc), dim3(kGqThreads), 0, stream, (const uint16_t*)a.pc,
                        (const uint16_t*)a.w_pool, (int)n, a.dc, 3 * a.dc, (void*)a.cbar);
