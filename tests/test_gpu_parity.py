@@ -563,14 +563,19 @@ def test_union_sizes_and_overlap(dsa):
 
 # --------------------------------------------------- group query (Eq. 6-7)
 
-@pytest.mark.parametrize("G,Tq,q_pos0,rope_dim", [(16, 1024, 0, 64), (8, 1003, 40960, 64), (4, 64, 131000, 128),
-                                                  (16, 40, 7, 0)])
-def test_group_query(dsa, G, Tq, q_pos0, rope_dim):
+@pytest.mark.parametrize("G,Tq,q_pos0,rope_dim,dc,dh,Hs", [(16, 1024, 0, 64, 256, 512, 8),
+                                                            (8, 1003, 40960, 64, 256, 512, 8),
+                                                            (4, 64, 131000, 128, 256, 512, 8),
+                                                            (16, 40, 7, 0, 256, 512, 8),
+                                                            (4, 2100, 96, 64, 80, 48, 3)])
+def test_group_query(dsa, G, Tq, q_pos0, rope_dim, dc, dh, Hs):
     """qbar and wbar of Eq. (6)-(7) against the oracle: a random pooling
     projection, the rotary part at large anchor positions, an incomplete last
-    group; bf16 queries agree within two bf16 steps (almost all exactly)."""
+    group; bf16 queries agree within two bf16 steps (almost all exactly).  The
+    last case has partial product tiles in every dimension (525 groups, 80 and
+    384 columns, k of 240 and 80: partial 64-k chunks)."""
     from oracle import group_query as gq
-    dc, dh, Hs, d = 256, 512, 8, 128
+    d = 128
     g = torch.Generator().manual_seed(80 + G)
     c = torch.randn(Tq, dc, generator=g).to(torch.bfloat16)
     h = torch.randn(Tq, dh, generator=g).to(torch.bfloat16)
