@@ -27,16 +27,18 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return (uint32_t)bf16_rne(lo) | ((uint32_t)bf16_rne(hi) << 16);
 }
 
-// One thread per 8 columns of a group: max, min and mean of c's rows (into
-// pc [n, 3dc]) and the mean of h's rows (into ph [n, dh]), fp32 sums in row
-// order times 1/G, rounded to bf16.
+// One thread per 8 columns of a group, of c (the first dc/8 threads) or of h
+// (the next dh/8): max, min and mean of c's rows (into pc [n, 3dc]) or the
+// mean of h's rows (into ph [n, dh]), fp32 sums in row order times 1/G,
+// rounded to bf16.  Every thread has its G loads in flight together.
 template <int G>
 __global__ void __launch_bounds__(kGqThreads) gq_pool_kernel(const GroupQueryArgs a) {
   const int64_t g = blockIdx.y;
   const int cc = a.dc / 8, hc = a.dh / 8;  // 16-byte chunks per row
-  const int x = blockIdx.x * kGqThreads + threadIdx.x;
+  const int xt = blockIdx.x * kGqThreads + threadIdx.x;
   const float inv = 1.0f / (float)G;
-  if (x < cc) {
+  if (xt < cc) {
+    const int x = xt;
     const uint4* src = reinterpret_cast<const uint4*>(a.c) + g * G * cc + x;
     uint4 v[G];
 #pragma unroll
@@ -62,8 +64,8 @@ __global__ void __launch_bounds__(kGqThreads) gq_pool_kernel(const GroupQueryArg
                          pack_bf16(mn[6], mn[7]));
     dst[2 * cc] = make_uint4(pack_bf16(s[0] * inv, s[1] * inv), pack_bf16(s[2] * inv, s[3] * inv),
                              pack_bf16(s[4] * inv, s[5] * inv), pack_bf16(s[6] * inv, s[7] * inv));
-  }
-  if (x < hc) {
+  } else if (xt < cc + hc) {
+    const int x = xt - cc;
     const uint4* src = reinterpret_cast<const uint4*>(a.h) + g * G * hc + x;
     uint4 v[G];
 #pragma unroll
@@ -253,7 +255,7 @@ __global__ void __launch_bounds__(kGqThreads) gq_rope_kernel(const GroupQueryArg
 hipError_t launch_group_query(const GroupQueryArgs& a, hipStream_t stream) {
   const int64_t n = a.ngroups;
   if (n > 0) {
-    const int chunks = (a.dc > a.dh ? a.dc : a.dh) / 8;
+    const int chunks = (a.dc + a.dh) / 8;
     const dim3 pg((unsigned)((chunks + kGqThreads - 1) / kGqThreads), (unsigned)n);
     switch (a.G) {
       case 4: hipLaunchKernelGGL(gq_pool_kernel<4>, pg, dim3(kGqThreads), 0, stream, a); break;
