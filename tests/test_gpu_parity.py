@@ -491,6 +491,16 @@ def test_mtp_shared_anchor_scan(dsa, G, m, d):
     assert (gb[:1] == -1).all() and (gb[1:] >= 0).all()
 
 
+def test_mtp_shared_anchor_block_edges(dsa):
+    """Anchors of one window that end on either side of a 256-key scan span
+    boundary (lengths 256 and 264, 512 and 520, 767 and 775): the workgroup
+    scores a span for one of its rows and not for the other."""
+    wl = make_mtp(B=3, N=1200, m=16, H=64, Hs=8, d=128, topk=64, G=8, P=255, dist="int", seed=91,
+                  prefix_lens=[256, 512, 767])
+    _, _, gb = _mtp_check(dsa, wl)
+    assert (gb >= 0).any(axis=-1).all()
+
+
 def test_mtp_pooled_exact(dsa):
     wl = make_mtp(B=3, N=5000, m=16, H=64, Hs=64, d=128, topk=128, G=8, P=1024, dist="int", seed=54,
                   prefix_lens=[1500, 4985, 900])
