@@ -5,9 +5,10 @@
 //
 // Index sets are the indexer's output rows: ascending token indices, then -1.
 // union: one workgroup per group marks its G*K indices in an LDS bitmap
-// (2^18 tokens per pass, more passes for longer sequences) and counts the
-// set bits.  overlap: one workgroup per row stages the second set in LDS and
-// binary-searches every entry of the first.
+// (2^18 tokens per pass, more passes only for longer sequences) and counts
+// the set bits.  overlap: one workgroup per row stages the second set in LDS;
+// each thread binary-searches the first entry of its run of the first set and
+// walks the rest.
 #include "device.h"
 #include "launch.h"
 
@@ -36,37 +37,44 @@ __global__ void __launch_bounds__(kCalThreads) union_kernel(const int32_t* idx, 
                                                             int32_t* out) {
   __shared__ uint32_t s_bits[kBitmapWords];
   __shared__ int s_tmp[kCalThreads / 64];
+  __shared__ int s_hi;
   const int tid = threadIdx.x;
   const int64_t g = blockIdx.x;
   const int32_t* rows = idx + g * G * (int64_t)K;
-  const int n = G * K;
-  int hi = -1;  // the largest index of the group: passes needed
-  for (int e = 4 * tid; e < n; e += 4 * kCalThreads) {
-    const int4 q = *reinterpret_cast<const int4*>(rows + e);
-    hi = max(max(hi, max(q.x, q.y)), max(q.z, q.w));
-  }
-  __shared__ int s_hi;
-  if (tid == 0) s_hi = -1;
-  __syncthreads();
-  atomicMax(&s_hi, hi);
-  __syncthreads();
-  hi = s_hi;
+  const int n = G * K;  // a multiple of 4
+  constexpr int kU = 4;  // 16-byte loads per thread in flight
   int count = 0;
-  for (int base = 0; base <= hi; base += kBitmapTokens) {
-    // only the words up to the group's largest index are touched
-    const int words = min(kBitmapWords, (hi - base) / 32 + 1);
-    for (int w = tid; w < words; w += kCalThreads) s_bits[w] = 0u;
+  // one pass per 2^18 tokens; the first pass also finds the group's largest
+  // index, so sequences of up to 2^18 tokens read the group once
+  for (int base = 0;; base += kBitmapTokens) {
+    for (int w = tid; w < kBitmapWords; w += kCalThreads) s_bits[w] = 0u;
+    if (tid == 0) s_hi = -1;
     __syncthreads();
-    for (int e = 4 * tid; e < n; e += 4 * kCalThreads) {  // K*G is a multiple of 4
-      const int4 q = *reinterpret_cast<const int4*>(rows + e);
-      const int v[4] = {q.x - base, q.y - base, q.z - base, q.w - base};
+    int hi = -1;
+    for (int e0 = 4 * tid; e0 < n; e0 += 4 * kCalThreads * kU) {
+      int4 q[kU];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (v[u] >= 0 && v[u] < kBitmapTokens) atomicOr(&s_bits[v[u] >> 5], 1u << (v[u] & 31));
+      for (int u = 0; u < kU; ++u) {
+        const int e = e0 + 4 * kCalThreads * u;
+        q[u] = e < n ? *reinterpret_cast<const int4*>(rows + e) : make_int4(-1, -1, -1, -1);
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int v[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          hi = max(hi, v[c]);
+          const int d = v[c] - base;
+          if (v[c] >= 0 && d >= 0 && d < kBitmapTokens) atomicOr(&s_bits[d >> 5], 1u << (d & 31));
+        }
+      }
     }
+    atomicMax(&s_hi, hi);
     __syncthreads();
-    for (int w = tid; w < words; w += kCalThreads) count += __popc(s_bits[w]);
-    __syncthreads();
+    for (int w = tid; w < kBitmapWords; w += kCalThreads) count += __popc(s_bits[w]);
+    const bool done = s_hi < base + kBitmapTokens;
+    __syncthreads();  // s_bits and s_hi are rewritten by the next pass
+    if (done) break;
   }
   const int total = block_sum(count, s_tmp);
   if (tid == 0) out[g] = total;
@@ -80,32 +88,47 @@ __global__ void __launch_bounds__(kCalThreads) overlap_kernel(const int32_t* a, 
   const int64_t r = blockIdx.x;
   const int32_t* ar = a + r * K;
   const int32_t* br = b + r * K;
+  // b into LDS (4-byte loads, a thread's all in flight together), and this
+  // thread's run of a (8 consecutive entries when K = 8 * threads; K % 4 == 0,
+  // a 16-byte aligned) loaded alongside
   int nb = 0;
+#pragma unroll 8
   for (int e = tid; e < K; e += kCalThreads) {
     const int32_t v = br[e];
     s_b[e] = v;
     nb += v >= 0;
   }
+  const int run = ((K + kCalThreads - 1) / kCalThreads + 3) / 4 * 4;  // entries of a per thread
+  const int a0 = tid * run, a1 = min(a0 + run, K);
+  constexpr int kPre = 2;  // 16-byte pieces of the run loaded before the barrier
+  int4 pre[kPre];
+#pragma unroll
+  for (int p = 0; p < kPre; ++p)
+    pre[p] = a0 + 4 * p < a1 ? *reinterpret_cast<const int4*>(ar + a0 + 4 * p) : make_int4(-1, -1, -1, -1);
   nb = block_sum(nb, s_tmp);  // also orders the LDS writes before the reads
-  // each thread merges a run of 4 consecutive entries of a (ascending) with
-  // b: one binary search for the run's first entry, then a linear walk
+  // each thread merges its run of a (ascending) with b: one binary search for
+  // the run's first entry, then a linear walk
   int hits = 0;
-  for (int e = 4 * tid; e < K; e += 4 * kCalThreads) {
-    const int4 q = *reinterpret_cast<const int4*>(ar + e);
-    const int32_t v[4] = {q.x, q.y, q.z, q.w};
-    if (v[0] < 0) continue;
+  if (a0 < a1 && pre[0].x >= 0) {
     int lo = 0, hi = nb;  // valid entries of b are s_b[0, nb), ascending
+    const int32_t first = pre[0].x;
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
-      if (s_b[mid] < v[0]) lo = mid + 1;
+      if (s_b[mid] < first) lo = mid + 1;
       else hi = mid;
     }
+    auto walk = [&](const int4& q) __attribute__((always_inline)) {
+      const int32_t v[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (v[u] < 0) break;
-      while (lo < nb && s_b[lo] < v[u]) ++lo;
-      hits += lo < nb && s_b[lo] == v[u];
-    }
+      for (int u = 0; u < 4; ++u) {
+        if (v[u] < 0) break;
+        while (lo < nb && s_b[lo] < v[u]) ++lo;
+        hits += lo < nb && s_b[lo] == v[u];
+      }
+    };
+#pragma unroll
+    for (int p = 0; p < kPre; ++p) walk(pre[p]);
+    for (int e = a0 + 4 * kPre; e < a1; e += 4) walk(*reinterpret_cast<const int4*>(ar + e));
   }
   const int total = block_sum(hits, s_tmp);
   if (tid == 0) out[r] = total;
