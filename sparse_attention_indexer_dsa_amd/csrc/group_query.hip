@@ -188,36 +188,66 @@ __global__ void __launch_bounds__(kGqThreads) gemm_nt_kernel(const uint16_t* A, 
     }
 }
 
-// wbar = sigmoid(W_G hbar): one workgroup per group; thread t takes 8-column
-// chunks t, t+256, ... of hbar and of each head's W_G row (fp32 FMA), then a
-// workgroup sum per head.
+// wbar = sigmoid(W_G hbar): one workgroup per 8 groups, 8 heads per pass.
+// Thread t takes 8-column chunks t, t+256, ... of the groups' hbar rows and
+// of the heads' W_G rows, each loaded once per pass (fp32 FMA, in chunk
+// order), then a butterfly sum over the wave and a sum over the waves in
+// order per (group, head): every wbar is summed as with one workgroup per
+// group.
+constexpr int kGateGroups = 8;
+constexpr int kGateHeads = 8;
 __global__ void __launch_bounds__(kGqThreads) gq_gate_kernel(const GroupQueryArgs a) {
-  __shared__ float s_part[kGqThreads / 64];
-  const int64_t g = blockIdx.x;
+  __shared__ float s_part[kGateHeads * kGateGroups][kGqThreads / 64];
+  const int64_t g0 = (int64_t)blockIdx.x * kGateGroups;
+  const int ng = a.ngroups - g0 < kGateGroups ? (int)(a.ngroups - g0) : kGateGroups;
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
   const int hc = a.dh / 8;
-  const uint4* hrow = reinterpret_cast<const uint4*>(a.ph) + g * hc;
-  for (int j = 0; j < a.Hs; ++j) {
-    const uint4* wrow = reinterpret_cast<const uint4*>(a.w_g) + (int64_t)j * hc;
-    float acc = 0.0f;
-    for (int x = tid; x < hc; x += kGqThreads) {
-      const uint4 hv = hrow[x], wv = wrow[x];
-      const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w}, ww[4] = {wv.x, wv.y, wv.z, wv.w};
+  const uint4* hrows = reinterpret_cast<const uint4*>(a.ph) + g0 * hc;
+  for (int j0 = 0; j0 < a.Hs; j0 += kGateHeads) {
+    const int nh = a.Hs - j0 < kGateHeads ? a.Hs - j0 : kGateHeads;
+    float acc[kGateHeads][kGateGroups];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc = fmaf(bf_lo(hw[q]), bf_lo(ww[q]), acc);
-        acc = fmaf(bf_hi(hw[q]), bf_hi(ww[q]), acc);
+    for (int jj = 0; jj < kGateHeads; ++jj)
+#pragma unroll
+      for (int gi = 0; gi < kGateGroups; ++gi) acc[jj][gi] = 0.0f;
+    for (int x = tid; x < hc; x += kGqThreads) {
+      uint4 hv[kGateGroups];
+#pragma unroll
+      for (int gi = 0; gi < kGateGroups; ++gi) hv[gi] = gi < ng ? hrows[gi * hc + x] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int jj = 0; jj < kGateHeads; ++jj) {
+        if (jj >= nh) break;
+        const uint4 wv = reinterpret_cast<const uint4*>(a.w_g)[(int64_t)(j0 + jj) * hc + x];
+        const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+        for (int gi = 0; gi < kGateGroups; ++gi) {
+          const uint32_t hw[4] = {hv[gi].x, hv[gi].y, hv[gi].z, hv[gi].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[jj][gi] = fmaf(bf_lo(hw[q]), bf_lo(ww[q]), acc[jj][gi]);
+            acc[jj][gi] = fmaf(bf_hi(hw[q]), bf_hi(ww[q]), acc[jj][gi]);
+          }
+        }
       }
     }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-    if (l == 0) s_part[wave] = acc;
-    __syncthreads();
-    if (tid == 0) {
-      float t = 0.0f;
+    for (int jj = 0; jj < kGateHeads; ++jj)
 #pragma unroll
-      for (int w = 0; w < kGqThreads / 64; ++w) t += s_part[w];
-      a.wbar[g * a.Hs + j] = 1.0f / (1.0f + __expf(-t));
+      for (int gi = 0; gi < kGateGroups; ++gi) {
+        float v = acc[jj][gi];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+        if (l == 0) s_part[jj * kGateGroups + gi][wave] = v;
+      }
+    __syncthreads();
+    if (tid < kGateHeads * kGateGroups) {
+      const int jj = tid / kGateGroups, gi = tid % kGateGroups;
+      if (jj < nh && gi < ng) {
+        float t = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kGqThreads / 64; ++w) t += s_part[tid][w];
+        a.wbar[(g0 + gi) * a.Hs + j0 + jj] = 1.0f / (1.0f + __expf(-t));
+      }
     }
     __syncthreads();
   }
@@ -274,8 +304,9 @@ hipError_t launch_group_query(const GroupQueryArgs& a, hipStream_t stream) {
     // q = W_Q cbar                           [n, Hs*d] fp32
     hipLaunchKernelGGL(gemm_nt_kernel<1>, grid(a.Hs * a.d), dim3(kGqThreads), 0, stream,
                        (const uint16_t*)a.cbar, (const uint16_t*)a.w_q, (int)n, a.Hs * a.d, a.dc, (void*)a.qf);
-    // wbar = sigmoid(W_G hbar)              [n, Hs] fp32 (Hs is small: a dot-product kernel)
-    hipLaunchKernelGGL(gq_gate_kernel, dim3((unsigned)n), dim3(kGqThreads), 0, stream, a);
+    // wbar = sigmoid(W_G hbar)              [n, Hs] fp32 (Hs is small: dot products)
+    hipLaunchKernelGGL(gq_gate_kernel, dim3((unsigned)((n + kGateGroups - 1) / kGateGroups)), dim3(kGqThreads), 0,
+                       stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
