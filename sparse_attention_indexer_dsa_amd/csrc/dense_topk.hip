@@ -182,49 +182,68 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   float wv[2][16];
   {
     const float qs = (DT == kFP8 && active) ? args.q_scale[jq] : 1.0f;
+    const float* wrow = args.w + (int64_t)jq * args.H;
+    // Every load here is unconditional, with the head clamped into the
+    // query's rows and the value zeroed afterwards, and is issued before its
+    // first use: behind a branch each load cost the wave a full memory round
+    // trip, about a hundred of them before the first tile.
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const int head = 32 * m + col;
       const bool hv = active && head < args.H;
       const uint8_t* qrow =
-          (const uint8_t*)args.q + ((int64_t)jq * args.H + (hv ? head : 0)) * C::kRowBytes;
+          (const uint8_t*)args.q + ((int64_t)jq * args.H + min(head, args.H - 1)) * C::kRowBytes;
 #pragma unroll
       for (int s = 0; s < C::kSteps; ++s) {
         if constexpr (DT == kBF16) {
-          u32x4 v = hv ? *(const u32x4*)(qrow + h * kD + 16 * s) : u32x4{0, 0, 0, 0};
-          a[m][s] = __builtin_bit_cast(v8bf, v);
+          const u32x4 v = *(const u32x4*)(qrow + h * kD + 16 * s);
+          a[m][s] = __builtin_bit_cast(v8bf, hv ? v : u32x4{0, 0, 0, 0});
         } else {
-          u32x4 v0 = hv ? *(const u32x4*)(qrow + h * 64 + 32 * s) : u32x4{0, 0, 0, 0};
-          u32x4 v1 = hv ? *(const u32x4*)(qrow + h * 64 + 32 * s + 16) : u32x4{0, 0, 0, 0};
-          struct { u32x4 lo, hi; } pr = {v0, v1};
+          const u32x4 v0 = *(const u32x4*)(qrow + h * 64 + 32 * s);
+          const u32x4 v1 = *(const u32x4*)(qrow + h * 64 + 32 * s + 16);
+          struct { u32x4 lo, hi; } pr = {hv ? v0 : u32x4{0, 0, 0, 0}, hv ? v1 : u32x4{0, 0, 0, 0}};
           a[m][s] = __builtin_bit_cast(v8i, pr);
         }
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int hr = 32 * m + 8 * (r >> 2) + 4 * h + (r & 3);
-        wv[m][r] = (active && hr < args.H) ? 0.5f * args.w[(int64_t)jq * args.H + hr] * qs : 0.0f;
+        const float wl = wrow[min(hr, args.H - 1)];
+        wv[m][r] = (active && hr < args.H) ? 0.5f * wl * qs : 0.0f;
       }
     }
-    // q-tilde: lane l owns elements 2l and 2l+1
+    // q-tilde: lane l owns elements 2l and 2l+1; heads in batches of 16
+    // whose loads are all in flight together, summed in head order
     float t0 = 0.0f, t1 = 0.0f;
     if (active) {
       const uint8_t* qb = (const uint8_t*)args.q + (int64_t)jq * args.H * C::kRowBytes;
-      for (int hd = 0; hd < args.H; ++hd) {
-        const float wh = 0.5f * args.w[(int64_t)jq * args.H + hd] * qs;
-        float x0, x1;
-        if constexpr (DT == kBF16) {
-          const uint32_t v = *(const uint32_t*)(qb + (int64_t)hd * C::kRowBytes + 4 * l);
-          x0 = __uint_as_float(v << 16);
-          x1 = __uint_as_float(v & 0xFFFF0000u);
-        } else {
-          const uint32_t v = *(const uint16_t*)(qb + (int64_t)hd * C::kRowBytes + 2 * l);
-          const v2bf p = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, false);
-          x0 = (float)p[0];
-          x1 = (float)p[1];
+      constexpr int kB = 16;
+      for (int h0 = 0; h0 < args.H; h0 += kB) {
+        uint32_t qv[kB];
+        float wq[kB];
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+          const int hd = min(h0 + u, args.H - 1);
+          if constexpr (DT == kBF16) qv[u] = *(const uint32_t*)(qb + (int64_t)hd * C::kRowBytes + 4 * l);
+          else qv[u] = *(const uint16_t*)(qb + (int64_t)hd * C::kRowBytes + 2 * l);
+          wq[u] = wrow[hd];
         }
-        t0 = fmaf(wh, x0, t0);
-        t1 = fmaf(wh, x1, t1);
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+          if (h0 + u >= args.H) break;
+          const float wh = 0.5f * wq[u] * qs;
+          float x0, x1;
+          if constexpr (DT == kBF16) {
+            x0 = __uint_as_float(qv[u] << 16);
+            x1 = __uint_as_float(qv[u] & 0xFFFF0000u);
+          } else {
+            const v2bf p = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(qv[u], 1.0f, false);
+            x0 = (float)p[0];
+            x1 = (float)p[1];
+          }
+          t0 = fmaf(wh, x0, t0);
+          t1 = fmaf(wh, x1, t1);
+        }
       }
     }
     const uint16_t h0 = bf16_rne(t0), h1 = bf16_rne(t1);
