@@ -56,8 +56,18 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // selection histograms).
 int cap_for(int K) { return (2 * K + 2048 + 63) / 64 * 64; }
 
-size_t cand_bytes(int64_t rows, int K) {
-  return 2 * align_up((size_t)rows * (size_t)cap_for(K) * 4u);
+size_t cand_bytes_cap(int64_t rows, int cap) { return 2 * align_up((size_t)rows * (size_t)cap * 4u); }
+size_t cand_bytes(int64_t rows, int K) { return cand_bytes_cap(rows, cap_for(K)); }
+
+// Rows of at most this many candidates get a buffer that holds all of them:
+// the dense kernel then keeps every score and a histogram instead of
+// streaming the top K through compactions.
+constexpr int64_t kFullRowMax = 16384;
+int full_cap(int K, int64_t ncand) {
+  const int base = cap_for(K);
+  if (ncand > kFullRowMax) return base;
+  const int c = (int)((ncand + 63) / 64 * 64);
+  return c > base ? c : base;
 }
 
 int row_bytes(int dtype, int d) { return dtype == DSAIDX_BF16 ? 2 * d : d; }
@@ -114,10 +124,9 @@ int check_ws(const void* ws, size_t ws_bytes, size_t need) {
 // Dense rows [r0, r1) of a prefill-shaped call, sliced into launches.
 hipError_t run_dense(const void* q, const float* q_scale, const void* k, const float* k_scale,
                      const float* w, int dtype, int H, int d, int64_t q_pos0, int64_t r0,
-                     int64_t r1, int topk, int32_t* out_idx, float* out_score, void* ws,
+                     int64_t r1, int topk, int cap, int32_t* out_idx, float* out_score, void* ws,
                      hipStream_t stream) {
   const int rb = row_bytes(dtype, d);
-  const int cap = cap_for(topk);
   for (int64_t s = r0; s < r1; s += kRowsPerLaunch) {
     const int64_t n = r1 - s < kRowsPerLaunch ? r1 - s : kRowsPerLaunch;
     ScanArgs a{};
@@ -183,7 +192,7 @@ size_t group_ws_bytes(int64_t Tq, int H, int d, int G, int P, int topk, unsigned
   const int64_t anchors = nelig < kAnchorsPerLaunch ? nelig : kAnchorsPerLaunch;
   const int64_t rows = Tq < kRowsPerLaunch ? Tq : kRowsPerLaunch;
   size_t scan = anchors > 0 ? cand_bytes(anchors, P) : 0;
-  size_t refine = rows > 0 ? cand_bytes(rows, topk) : 0;
+  size_t refine = rows > 0 ? cand_bytes_cap(rows, full_cap(topk, (int64_t)P + G - 1)) : 0;
   return bank + (scan > refine ? scan : refine);
 }
 
@@ -194,10 +203,10 @@ extern "C" {
 const char* indexer_last_error(void) { return g_last_error.c_str(); }
 
 size_t indexer_prefill_workspace_size(int64_t Tq, int64_t Tk, int H, int d, int topk, int dtype) {
-  (void)Tk; (void)H; (void)d; (void)dtype;
+  (void)H; (void)d; (void)dtype;
   if (Tq <= 0 || topk <= 0) return 0;
   const int64_t rows = Tq < kRowsPerLaunch ? Tq : kRowsPerLaunch;
-  return cand_bytes(rows, topk);
+  return cand_bytes_cap(rows, full_cap(topk, Tk));
 }
 
 int indexer_prefill(const void* q, const float* q_scale, const void* k, const float* k_scale,
@@ -210,8 +219,8 @@ int indexer_prefill(const void* q, const float* q_scale, const void* k, const fl
   rc = check_ws(ws, ws_bytes, indexer_prefill_workspace_size(Tq, Tk, H, d, topk, dtype));
   if (rc) return rc;
   if (Tq == 0) return ok();
-  hipError_t e = run_dense(q, q_scale, k, k_scale, w, dtype, H, d, q_pos0, 0, Tq, topk, out_idx,
-                           out_score, ws, (hipStream_t)stream);
+  hipError_t e = run_dense(q, q_scale, k, k_scale, w, dtype, H, d, q_pos0, 0, Tq, topk,
+                           full_cap(topk, Tk), out_idx, out_score, ws, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "indexer_prefill launch");
   return ok();
 }
@@ -428,10 +437,10 @@ int indexer_group_bank(const void* q, const float* q_scale, const void* k, const
 
   // 1. original indexer for the rows whose groups build no bank
   hipError_t e = run_dense(q, q_scale, k, k_scale, w, dtype, H, d, q_pos0, 0, p.g0 * G, topk,
-                           out_idx, out_score, cand_ws, st);
+                           cap_for(topk), out_idx, out_score, cand_ws, st);
   if (e == hipSuccess)
-    e = run_dense(q, q_scale, k, k_scale, w, dtype, H, d, q_pos0, p.nfull * G, Tq, topk, out_idx,
-                  out_score, cand_ws, st);
+    e = run_dense(q, q_scale, k, k_scale, w, dtype, H, d, q_pos0, p.nfull * G, Tq, topk, cap_for(topk),
+                  out_idx, out_score, cand_ws, st);
   if (e != hipSuccess) return hip_fail(e, "indexer_group_bank fallback launch");
 
   // 2. group scan: each bank group's anchor scores its prefix with the group
@@ -465,7 +474,7 @@ int indexer_group_bank(const void* q, const float* q_scale, const void* k, const
 
   // 3. refinement: every member of a bank group scores bank U {t+1..i} with the
   //    original indexer and keeps its top K (Eq. (14))
-  const int cap = cap_for(topk);
+  const int cap = full_cap(topk, (int64_t)P + G - 1);  // every refinement row fits its buffer
   const int64_t groups_per_launch = kRowsPerLaunch / G;
   for (int64_t s = 0; s < nelig; s += groups_per_launch) {
     const int64_t ng = nelig - s < groups_per_launch ? nelig - s : groups_per_launch;

@@ -130,7 +130,7 @@ __device__ __forceinline__ void dma_b32(const v4i& rsrc, uint32_t lds, uint32_t 
                :: "v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
 }
 
-template <int DT, bool GATHER>
+template <int DT, bool GATHER, bool FULL>
 __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs args) {
   using C = Cfg<DT>;
   // vm operations a wave issues per step: the tile chunks, the key scales and,
@@ -267,6 +267,18 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   uint32_t* ckey = args.cand_key + (int64_t)jq * args.cap;  // raw fp32 scores
   int32_t* cidx = args.cand_idx + (int64_t)jq * args.cap;
   uint32_t* hist = s_hist[wave];
+  // Full-row mode (every candidate list fits a row buffer, cap >= the
+  // workgroup's candidates): candidate c's score goes to ckey[c] and into the
+  // wave's LDS histogram of the top 11 order-key bits; nothing is appended or
+  // compacted, and the histogram gives the final selection its first digit.
+  // The row's stores go through a buffer range that drops those past the
+  // query's candidates, so every step issues exactly one store.
+  const __amdgpu_buffer_rsrc_t rres =
+      __builtin_amdgcn_make_buffer_rsrc((void*)ckey, (short)0, FULL ? ncand_me * 4 : 0, kBufferWord3);
+  if constexpr (FULL) {
+    hist_zero<2048>(hist);
+    wave_lds_sync();
+  }
 
   // Scores that enter are staged in this wave's LDS (the selection histogram's
   // words, free outside a selection) and flushed to the candidate buffer when
@@ -441,6 +453,11 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   // append the step's scores that beat the threshold: lane l holds candidate
   // tbase + l, so lane order is candidate order and one ballot serves 64
   auto append = [&](float sc, int tbase, int i) __attribute__((always_inline)) {
+    if constexpr (FULL) {
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rres, 4 * (tbase + l), 0, 0);
+      if (tbase + l < ncand_me) hist_add<2048>(hist, order_key(sc), 21);
+      return;
+    }
     uint64_t tm = ballot(sc > thr);
     if (tbase + kTile > ncand_me) tm &= ballot(tbase + l < ncand_me);  // the query's last tile
     if (tm) {
@@ -483,11 +500,13 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
     const int st1 = st == kStages - 1 ? 0 : st + 1;
     const int st4 = st == 0 ? kStages - 1 : st - 1;  // (st + kAhead) % kStages
     // compaction requests raised during step i-1 (seen after its barrier)
-    if (i > 0 && s_need[(i - 1) & 1] == i - 1 && active && cnt + nst > args.K) {
-      flush();
-      thr = wave_keep_topk(ckey, cidx, cnt, args.K, hist, kCompactSlack);
-    } else if (nst > kStage - 64) {
-      flush();
+    if constexpr (!FULL) {
+      if (i > 0 && s_need[(i - 1) & 1] == i - 1 && active && cnt + nst > args.K) {
+        flush();
+        thr = wave_keep_topk(ckey, cidx, cnt, args.K, hist, kCompactSlack);
+      } else if (nst > kStage - 64) {
+        flush();
+      }
     }
     request(i + kAhead, st4);
     request_idx(i + kIdxAhead);
@@ -509,8 +528,9 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
     // tile i+2 (gathering: and the positions of tile i+5) must have landed
     // before the barrier publishes them: after their requests this wave issued
     // those of steps i-1 and i (and maybe a flush's stores, which only makes
-    // the count conservative)
-    __builtin_amdgcn_s_waitcnt(0x3F70 | (2 * kVm));
+    // the count conservative).  In full-row mode each step also ends with
+    // one store, and the two after those requests are allowed to be pending.
+    __builtin_amdgcn_s_waitcnt(0x3F70 | (2 * kVm + (FULL ? 2 : 0)));
     __syncthreads();
   };
   static_assert(kStages == 5 && kAhead == kStages - 1, "the loops below assume a five-stage ring");
@@ -534,9 +554,17 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   // when the wave ends
   __builtin_amdgcn_s_waitcnt(0x3F70);
   if (!active) return;
-  flush();
-  wave_emit_topk<32>(ckey, cidx, cnt, args.K, hist, args.out_idx + (int64_t)j * args.out_stride,
-                     args.out_score ? args.out_score + (int64_t)j * args.out_stride : nullptr);
+  int32_t* const orow = args.out_idx + (int64_t)j * args.out_stride;
+  float* const srow = args.out_score ? args.out_score + (int64_t)j * args.out_stride : nullptr;
+  if constexpr (FULL) {
+    wave_emit_row<32>(ckey, ncand_me, args.K, hist, orow, srow, [&](int c) __attribute__((always_inline)) {
+      if constexpr (GATHER) return c < nbank ? bank[c] : anchor + 1 + (c - nbank);
+      else return c;
+    });
+  } else {
+    flush();
+    wave_emit_topk<32>(ckey, cidx, cnt, args.K, hist, orow, srow);
+  }
 }
 
 }  // namespace
@@ -550,16 +578,29 @@ bool dense_topk_supported(const ScanArgs& a) {
   return shape_ok && a.H > 32 && a.H <= 64 && a.d == kD && keys * 2 * kD < (int64_t(1) << 31);
 }
 
+template <bool GATHER, bool FULL>
+static void launch_dt(const ScanArgs& a, int dtype, dim3 grid, hipStream_t stream) {
+  if (dtype == kBF16)
+    hipLaunchKernelGGL((dense_topk_kernel<kBF16, GATHER, FULL>), grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((dense_topk_kernel<kFP8, GATHER, FULL>), grid, dim3(kThreads), 0, stream, a);
+}
+
 hipError_t launch_dense_topk(const ScanArgs& a, int dtype, hipStream_t stream) {
   const int64_t blocks = (a.nq + kWaves - 1) / kWaves;
   if (blocks <= 0) return hipSuccess;
-  const dim3 grid((unsigned)blocks), block(kThreads);
+  const dim3 grid((unsigned)blocks);
+  // full-row mode when every row's candidates fit its buffer (cap < 65536,
+  // so the 16-bit histogram counters cannot overflow)
+  const int64_t ncand_max =
+      a.bank ? (int64_t)a.bank_stride + a.group - 1 : a.pos0 + (a.nq - 1) * a.pos_stride + 1;
+  const bool full = ncand_max <= a.cap;
   if (a.bank) {
-    if (dtype == kBF16) hipLaunchKernelGGL((dense_topk_kernel<kBF16, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((dense_topk_kernel<kFP8, true>), grid, block, 0, stream, a);
+    if (full) launch_dt<true, true>(a, dtype, grid, stream);
+    else launch_dt<true, false>(a, dtype, grid, stream);
   } else {
-    if (dtype == kBF16) hipLaunchKernelGGL((dense_topk_kernel<kBF16, false>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((dense_topk_kernel<kFP8, false>), grid, block, 0, stream, a);
+    if (full) launch_dt<false, true>(a, dtype, grid, stream);
+    else launch_dt<false, false>(a, dtype, grid, stream);
   }
   return hipGetLastError();
 }

@@ -280,30 +280,16 @@ __device__ __forceinline__ float wave_select_topk(uint32_t* keys, int32_t* idx, 
   return wave_keep_topk(keys, idx, n, K, hist, -1);
 }
 
-// The final selection, written straight into a query's output row: the top
-// K of the wave's n buffer entries (all of them when n <= K) in buffer order,
-// i.e. ascending key index, then -1 / -inf padding up to K.  The buffer is
-// read B entries per lane at a time (the caller's registers are free by now).
-// osc may be null.  `hist` is this wave's kSelectHistWords LDS words.
-template <int B>
-__device__ __forceinline__ void wave_emit_topk(const uint32_t* keys, const int32_t* idx, int n,
-                                               int K, uint32_t* hist, int32_t* oidx, float* osc) {
-  wave_mem_fence();
-  const bool select = n > K;
-  uint32_t kth = 0;
-  int keep_eq = 0;
-  if (select) {
-    uint32_t prefix = 0, pmask = 0;
-    int krem = K;
-    radix_step<2048, B>(keys, n, hist, 21, prefix, pmask, krem);
-    radix_step<2048, B>(keys, n, hist, 10, prefix, pmask, krem);
-    radix_step<1024, B>(keys, n, hist, 0, prefix, pmask, krem);
-    kth = prefix;
-    keep_eq = krem;
-  }
+// The output pass of a final selection: the entries of keys[0, n) above kth,
+// and the first keep_eq equal to it (all of them when !select), written to
+// oidx / osc in buffer order with index id_of(e, u), then -1 / -inf padding
+// up to K.  Loads are batched kU chunks of 64 per lane; load_id(e) is called
+// for every loaded in-range slot before any is used.
+template <int kU, typename LoadId>
+__device__ __forceinline__ void emit_kept(const uint32_t* keys, int n, int K, bool select, uint32_t kth,
+                                          int keep_eq, int32_t* oidx, float* osc, LoadId load_id) {
   const int l = lane_id();
   int out = 0, eq_seen = 0;
-  constexpr int kU = B / 2;  // chunks of 64 (score + index) loaded together
   for (int base = 0; base < n; base += 64 * kU) {
     uint32_t raw[kU];
     int32_t id[kU];
@@ -311,7 +297,7 @@ __device__ __forceinline__ void wave_emit_topk(const uint32_t* keys, const int32
     for (int u = 0; u < kU; ++u) {
       const int e = base + 64 * u + l;
       raw[u] = e < n ? keys[e] : 0u;
-      id[u] = e < n ? idx[e] : 0;
+      id[u] = e < n ? load_id(e) : 0;
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
@@ -335,6 +321,56 @@ __device__ __forceinline__ void wave_emit_topk(const uint32_t* keys, const int32
     oidx[p] = -1;
     if (osc) osc[p] = -__builtin_inff();
   }
+}
+
+// The final selection, written straight into a query's output row: the top
+// K of the wave's n buffer entries (all of them when n <= K) in buffer order,
+// i.e. ascending key index, then -1 / -inf padding up to K.  The buffer is
+// read B entries per lane at a time (the caller's registers are free by now).
+// osc may be null.  `hist` is this wave's kSelectHistWords LDS words.
+template <int B>
+__device__ __forceinline__ void wave_emit_topk(const uint32_t* keys, const int32_t* idx, int n,
+                                               int K, uint32_t* hist, int32_t* oidx, float* osc) {
+  wave_mem_fence();
+  const bool select = n > K;
+  uint32_t kth = 0;
+  int keep_eq = 0;
+  if (select) {
+    uint32_t prefix = 0, pmask = 0;
+    int krem = K;
+    radix_step<2048, B>(keys, n, hist, 21, prefix, pmask, krem);
+    radix_step<2048, B>(keys, n, hist, 10, prefix, pmask, krem);
+    radix_step<1024, B>(keys, n, hist, 0, prefix, pmask, krem);
+    kth = prefix;
+    keep_eq = krem;
+  }
+  emit_kept<B / 2>(keys, n, K, select, kth, keep_eq, oidx, osc, [&](int e) { return idx[e]; });
+}
+
+// The final selection over a wave's full score row: raw fp32 scores
+// keys[0, n) (n < 65536) of candidates 0 .. n-1, whose top 11 order-key bits
+// `hist` (this wave's kSelectHistWords LDS words, 2048 16-bit counters)
+// already counts, so the first digit needs no pass over the row.  Writes the
+// top K in candidate order with index pos(e), then the padding; osc may be
+// null.
+template <int B, typename Pos>
+__device__ __forceinline__ void wave_emit_row(const uint32_t* keys, int n, int K, uint32_t* hist,
+                                              int32_t* oidx, float* osc, Pos pos) {
+  wave_mem_fence();
+  wave_lds_sync();
+  const bool select = n > K;
+  uint32_t kth = 0;
+  int keep_eq = 0;
+  if (select) {
+    uint32_t prefix = 0, pmask = 0;
+    int krem = K;
+    radix_pick<2048>(hist, 21, prefix, pmask, krem);
+    radix_step<2048, B>(keys, n, hist, 10, prefix, pmask, krem);
+    radix_step<1024, B>(keys, n, hist, 0, prefix, pmask, krem);
+    kth = prefix;
+    keep_eq = krem;
+  }
+  emit_kept<B>(keys, n, K, select, kth, keep_eq, oidx, osc, pos);
 }
 
 }  // namespace dsaidx
