@@ -30,6 +30,13 @@
 //     digits, and the third only when the K-th best's 22-bit key bucket is
 //     crowded); keys arrive in ascending index, so strict ">" keeps the lower
 //     index on ties.
+//   * Full-row top-K, for launches whose rows all fit their buffer (cap at
+//     least the largest row's candidate count): each step stores its 64
+//     scores at their candidate slots with one buffer store (the buffer range
+//     drops those past the row) and counts them in the wave's LDS histogram
+//     of the top 11 key bits.  Nothing is appended or compacted; at the end
+//     the histogram gives the first radix digit, two passes over the row give
+//     the other two, and the output pass maps slots to key positions.
 //   * Gathering (the bank refinement of Eq. (14), groups of a multiple of 8
 //     queries): the workgroup's candidates are its group's bank followed by
 //     the keys after the anchor.  Each tile's 64 bank positions are copied
