@@ -35,8 +35,10 @@
 //     scores at their candidate slots with one buffer store (the buffer range
 //     drops those past the row) and counts them in the wave's LDS histogram
 //     of the top 11 key bits.  Nothing is appended or compacted; at the end
-//     the histogram gives the first radix digit, two passes over the row give
-//     the other two, and the output pass maps slots to key positions.
+//     the histogram gives the first radix digit, one pass over the row keeps
+//     the entries at or above that digit's bin (with their key positions)
+//     and counts the second digit, and the third digit and the output pass
+//     run over the kept list.
 //   * Gathering (the bank refinement of Eq. (14), groups of a multiple of 8
 //     queries): the workgroup's candidates are its group's bank followed by
 //     the keys after the anchor.  Each tile's 64 bank positions are copied
@@ -564,7 +566,7 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   int32_t* const orow = args.out_idx + (int64_t)j * args.out_stride;
   float* const srow = args.out_score ? args.out_score + (int64_t)j * args.out_stride : nullptr;
   if constexpr (FULL) {
-    wave_emit_row<32>(ckey, ncand_me, args.K, hist, orow, srow, [&](int c) __attribute__((always_inline)) {
+    wave_emit_row<32>(ckey, cidx, ncand_me, args.K, hist, orow, srow, [&](int c) __attribute__((always_inline)) {
       if constexpr (GATHER) return c < nbank ? bank[c] : anchor + 1 + (c - nbank);
       else return c;
     });

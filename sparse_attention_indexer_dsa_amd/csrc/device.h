@@ -282,12 +282,13 @@ __device__ __forceinline__ float wave_select_topk(uint32_t* keys, int32_t* idx, 
 
 // The output pass of a final selection: the entries of keys[0, n) above kth,
 // and the first keep_eq equal to it (all of them when !select), written to
-// oidx / osc in buffer order with index id_of(e, u), then -1 / -inf padding
-// up to K.  Loads are batched kU chunks of 64 per lane; load_id(e) is called
-// for every loaded in-range slot before any is used.
-template <int kU, typename LoadId>
+// oidx / osc in buffer order with index map(load_id(e)), then -1 / -inf
+// padding up to K.  Loads are batched kU chunks of 64 per lane: load_id(e)
+// is called for every in-range slot of a batch, then map on each result, so
+// the loads of either stage are all in flight together.
+template <int kU, typename LoadId, typename Map>
 __device__ __forceinline__ void emit_kept(const uint32_t* keys, int n, int K, bool select, uint32_t kth,
-                                          int keep_eq, int32_t* oidx, float* osc, LoadId load_id) {
+                                          int keep_eq, int32_t* oidx, float* osc, LoadId load_id, Map map) {
   const int l = lane_id();
   int out = 0, eq_seen = 0;
   for (int base = 0; base < n; base += 64 * kU) {
@@ -298,6 +299,11 @@ __device__ __forceinline__ void emit_kept(const uint32_t* keys, int n, int K, bo
       const int e = base + 64 * u + l;
       raw[u] = e < n ? keys[e] : 0u;
       id[u] = e < n ? load_id(e) : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int e = base + 64 * u + l;
+      id[u] = e < n ? map(id[u]) : 0;
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
@@ -344,33 +350,70 @@ __device__ __forceinline__ void wave_emit_topk(const uint32_t* keys, const int32
     kth = prefix;
     keep_eq = krem;
   }
-  emit_kept<B / 2>(keys, n, K, select, kth, keep_eq, oidx, osc, [&](int e) { return idx[e]; });
+  emit_kept<B / 2>(keys, n, K, select, kth, keep_eq, oidx, osc, [&](int e) { return idx[e]; },
+                   [](int32_t i) { return i; });
 }
 
 // The final selection over a wave's full score row: raw fp32 scores
 // keys[0, n) (n < 65536) of candidates 0 .. n-1, whose top 11 order-key bits
 // `hist` (this wave's kSelectHistWords LDS words, 2048 16-bit counters)
-// already counts, so the first digit needs no pass over the row.  Writes the
-// top K in candidate order with index pos(e), then the padding; osc may be
-// null.
+// already counts, so the first digit needs no pass over the row.  One pass
+// then keeps the entries at or above the first digit's bin (every entry of
+// the top K, and the rest of that bin) in place, in candidate order, with
+// their indices pos(candidate) in ids[], and counts the second digit of the
+// bin's entries; the third digit and the output pass run over that list
+// only.  pos is called for every candidate of a batch together with the
+// score loads, so a lookup it makes adds no round trip.  Writes the top K in
+// candidate order, then the padding; osc may be null.
 template <int B, typename Pos>
-__device__ __forceinline__ void wave_emit_row(const uint32_t* keys, int n, int K, uint32_t* hist,
+__device__ __forceinline__ void wave_emit_row(uint32_t* keys, int32_t* ids, int n, int K, uint32_t* hist,
                                               int32_t* oidx, float* osc, Pos pos) {
   wave_mem_fence();
   wave_lds_sync();
-  const bool select = n > K;
-  uint32_t kth = 0;
-  int keep_eq = 0;
-  if (select) {
-    uint32_t prefix = 0, pmask = 0;
-    int krem = K;
-    radix_pick<2048>(hist, 21, prefix, pmask, krem);
-    radix_step<2048, B>(keys, n, hist, 10, prefix, pmask, krem);
-    radix_step<1024, B>(keys, n, hist, 0, prefix, pmask, krem);
-    kth = prefix;
-    keep_eq = krem;
+  if (n <= K) {
+    emit_kept<B>(keys, n, K, false, 0u, 0, oidx, osc, pos, [](int32_t i) { return i; });
+    return;
   }
-  emit_kept<B>(keys, n, K, select, kth, keep_eq, oidx, osc, pos);
+  uint32_t prefix = 0, pmask = 0;
+  int krem = K;
+  radix_pick<2048>(hist, 21, prefix, pmask, krem);
+  const uint32_t lo = prefix;  // lowest order key of the first digit's bin
+  hist_zero<2048>(hist);
+  wave_lds_sync();
+  const int l = lane_id();
+  int m = 0;
+  for (int e0 = 0; e0 < n; e0 += B * 64) {
+    uint32_t raw[B];
+    int32_t id[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int e = e0 + 64 * u + l;
+      raw[u] = e < n ? keys[e] : 0u;
+      id[u] = e < n ? pos(e) : 0;
+    }
+    // slot m + rank <= e: an entry moves only down, onto a chunk this batch
+    // has already read (or an earlier one)
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int e = e0 + 64 * u + l;
+      const uint32_t k = order_key(__uint_as_float(raw[u]));
+      const bool keep = e < n && k >= lo;
+      if (keep && (k & pmask) == prefix) hist_add<2048>(hist, k, 10);
+      const uint64_t km = ballot(keep);
+      if (keep) {
+        const int p = m + rank_below(km);
+        keys[p] = raw[u];
+        ids[p] = id[u];
+      }
+      m += popc(km);
+    }
+  }
+  wave_mem_fence();
+  wave_lds_sync();
+  radix_pick<2048>(hist, 10, prefix, pmask, krem);
+  radix_step<1024, B>(keys, m, hist, 0, prefix, pmask, krem);
+  emit_kept<B>(keys, m, K, true, prefix, krem, oidx, osc, [&](int e) { return ids[e]; },
+               [](int32_t i) { return i; });
 }
 
 }  // namespace dsaidx
