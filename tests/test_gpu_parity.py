@@ -209,6 +209,23 @@ def test_dense_kernel_streaming_and_full_rows(dsa, dtype, dist):
     _prefill_check(dsa, short, rows=_rows(6000, 40, 91))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_dense_kernel_full_row_edges(dsa, dtype):
+    """Full-row top-K at its edges: rows of K - 1, K and K + 1 candidates
+    (written whole, or one dropped), and a call where every score is +0, so
+    the first digit's bin holds the whole row and the pass that keeps the
+    entries at or above it keeps them all; the lowest K indices win."""
+    K = 2048
+    wl = make_prefill(T=2100, H=64, d=128, topk=K, dtype=dtype, dist="int", seed=95)
+    rows = np.unique(np.concatenate([np.arange(K - 3, K + 3), _rows(2100, 10, 95)]))
+    _prefill_check(dsa, wl, rows=rows)
+    z = make_prefill(T=5000, H=64, d=128, topk=K, dtype=dtype, dist="int", seed=96)
+    z.tensors["w"] = torch.zeros_like(z["w"])
+    gi, _ = _prefill_check(dsa, z, rows=np.array([0, K - 2, K - 1, K, 3000, 4999]))
+    assert (_np(gi)[4999] == np.arange(K)).all()
+    assert (_np(gi)[K - 2][: K - 1] == np.arange(K - 1)).all() and (_np(gi)[K - 2][K - 1:] == -1).all()
+
+
 @pytest.mark.parametrize("Tq,q_pos0,K", [(5, 100, 32), (13, 0, 200), (1, 2047, 2048), (9, 60, 2048)])
 def test_dense_kernel_partial_workgroups(dsa, Tq, q_pos0, K):
     """Query counts that leave waves of the first workgroup idle, chunks that
