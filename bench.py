@@ -63,11 +63,12 @@ def _traffic(*kernel_keys):
     return total
 
 
-# the device sources each measured launch is compiled from (a change to any of
-# them makes the committed counters stale)
+# the sources each measured launch is compiled from, the host code that picks
+# its launch shape and top-K mode included (a change to any of them makes the
+# committed counters stale)
 KERNEL_SOURCES = {
-    "dense_topk_fp8_prefill128k": ("dense_topk.hip", "device.h", "launch.h"),
-    "decode_call_decode256k": ("decode.hip", "device.h", "launch.h"),
+    "dense_topk_fp8_prefill128k": ("dense_topk.hip", "device.h", "launch.h", "api.cpp"),
+    "decode_call_decode256k": ("decode.hip", "device.h", "launch.h", "api.cpp"),
 }
 
 
@@ -93,9 +94,10 @@ def bench_prefill(dsa, args, log):
     wl = make_workload(3, seed=args.seed, device="cuda")
     q, k, w, qs, ks = wl["q"], wl["k"], wl["w"], wl["q_scale"], wl["k_scale"]
     out = torch.empty((T, K), dtype=torch.int32, device="cuda")
-    ws = torch.empty(dsa.workspace_prefill(chunk, T, H, d, K, dsa.DSAIDX_FP8_E4M3), dtype=torch.uint8,
-                     device="cuda")
     nchunks = T // chunk
+    # one workspace for every chunk: chunks whose rows fit a full-row buffer need more than the last
+    ws = torch.empty(max(dsa.workspace_prefill(chunk, (c + 1) * chunk, H, d, K, dsa.DSAIDX_FP8_E4M3)
+                         for c in range(nchunks)), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
     def step(evs=None):

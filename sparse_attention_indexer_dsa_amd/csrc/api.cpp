@@ -61,8 +61,9 @@ size_t cand_bytes(int64_t rows, int K) { return cand_bytes_cap(rows, cap_for(K))
 
 // Rows of at most this many candidates get a buffer that holds all of them:
 // the dense kernel then keeps every score and a histogram instead of
-// streaming the top K through compactions.
-constexpr int64_t kFullRowMax = 16384;
+// streaming the top K through compactions.  The bound keeps a row's count in
+// the 16-bit histogram counters (a multiple of 64 below 65536).
+constexpr int64_t kFullRowMax = 65472;
 int full_cap(int K, int64_t ncand) {
   const int base = cap_for(K);
   if (ncand > kFullRowMax) return base;

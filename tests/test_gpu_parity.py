@@ -190,23 +190,26 @@ def test_dense_kernel_compaction(dsa):
 @pytest.mark.parametrize("H,d,dtype,K", [(64, 128, "fp8", 16), (48, 128, "bf16", 40), (8, 32, "bf16", 8),
                                          (16, 64, "fp8", 24)])
 def test_compaction_buckets(dsa, H, d, dtype, K):
-    """Normal scores, small K over 20000 keys (more than a full-row buffer
+    """Normal scores, small K over 70000 keys (more than a full-row buffer
     holds, so the top K streams): most compactions stop after two radix
     digits and keep the K-th best's whole 22-bit key bucket; the final
     selection must still be the exact top K (dense and general kernels)."""
-    wl = make_prefill(T=20000, H=H, d=d, topk=K, dtype=dtype, dist="normal", seed=70 + H + K)
-    _prefill_check(dsa, wl, rows=_rows(20000, 40, 70 + H))
+    wl = make_prefill(T=70000, H=H, d=d, topk=K, dtype=dtype, dist="normal", seed=70 + H + K, Tq=192)
+    _prefill_check(dsa, wl, rows=_rows(192, 24, 70 + H))
 
 
 @pytest.mark.parametrize("dtype,dist", [("fp8", "int"), ("bf16", "int"), ("fp8", "normal")])
 def test_dense_kernel_streaming_and_full_rows(dsa, dtype, dist):
-    """Both top-K modes of the dense kernel: a 20000-key call streams its rows
-    through compacting buffers of 2K + 2048 candidates, a 6000-key call keeps
-    every score of a row and selects once at the end; both match the oracle."""
-    wl = make_prefill(T=20000, H=64, d=128, topk=100, dtype=dtype, dist=dist, seed=90)
-    _prefill_check(dsa, wl, rows=_rows(20000, 40, 90))
+    """Both top-K modes of the dense kernel: a 70000-key call streams its rows
+    through compacting buffers of 2K + 2048 candidates; 6000- and 40000-key
+    calls keep every score of a row and select once at the end; all match
+    the oracle."""
+    wl = make_prefill(T=70000, H=64, d=128, topk=100, dtype=dtype, dist=dist, seed=90, Tq=192)
+    _prefill_check(dsa, wl, rows=_rows(192, 24, 90))
     short = make_prefill(T=6000, H=64, d=128, topk=100, dtype=dtype, dist=dist, seed=91)
     _prefill_check(dsa, short, rows=_rows(6000, 40, 91))
+    mid = make_prefill(T=40000, H=64, d=128, topk=100, dtype=dtype, dist=dist, seed=92, Tq=192)
+    _prefill_check(dsa, mid, rows=_rows(192, 24, 92))
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
