@@ -436,9 +436,11 @@ int indexer_group_bank(const void* q, const float* q_scale, const void* k, const
     if (e != hipSuccess) return hip_fail(e, "indexer_group_bank pooling launch");
   }
 
-  // 1. original indexer for the rows whose groups build no bank
+  // 1. original indexer for the rows whose groups build no bank; those before
+  // the first bank group see at most P + G - 1 keys, so their rows fit the
+  // full-row buffers the workspace holds for the refinement
   hipError_t e = run_dense(q, q_scale, k, k_scale, w, dtype, H, d, q_pos0, 0, p.g0 * G, topk,
-                           cap_for(topk), out_idx, out_score, cand_ws, st);
+                           full_cap(topk, q_pos0 + p.g0 * G), out_idx, out_score, cand_ws, st);
   if (e == hipSuccess)
     e = run_dense(q, q_scale, k, k_scale, w, dtype, H, d, q_pos0, p.nfull * G, Tq, topk, cap_for(topk),
                   out_idx, out_score, cand_ws, st);
