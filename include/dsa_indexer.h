@@ -77,8 +77,12 @@ enum {
  *   k_scale  [Tk] fp32    per-key-token scale (fp8 only, else NULL)
  *   w        [Tq, H] fp32 per-query head weights
  *   out_idx  [Tq, topk] int32;  out_score [Tq, topk] fp32 or NULL
- * The Tq x Tk score matrix is never stored: each query keeps a streaming
- * candidate buffer in `ws`.
+ * The whole Tq x Tk score matrix is never stored.  With Tk above 65472 each
+ * query keeps a streaming candidate buffer of 2 topk + 2048 entries in `ws`;
+ * with Tk at most 65472 every query's row of Tk scores fits its buffer, so
+ * the row is stored in `ws` and selected once at the end (the workspace then
+ * grows with Tk: 8 bytes per key per query of a launch of at most 16384
+ * queries, about 2 GB for 4096 queries over 61440 keys).
  */
 int indexer_prefill(const void *q, const float *q_scale, const void *k, const float *k_scale,
                     const float *w, int dtype, int64_t Tq, int64_t Tk, int H, int d,
