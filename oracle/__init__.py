@@ -51,6 +51,8 @@ def lib():
         L.oracle_max_threads.restype = I32
         L.oracle_score_pairs.restype = I32
         L.oracle_score_pairs.argtypes = [P, P, I32, P, P, I32, P, I32, I32, P, P, I64, P, I32]
+        L.oracle_score_pairs_cond.restype = I32
+        L.oracle_score_pairs_cond.argtypes = [P, P, I32, P, P, I32, P, I32, I32, P, P, I64, P, I32]
         L.oracle_prefill.restype = I32
         L.oracle_prefill.argtypes = [P, P, P, P, P, I32, I64, I64, I32, I32, I64, I32, P, I64, P, P, I32]
         L.oracle_decode.restype = I32
@@ -150,6 +152,24 @@ def score_pairs(q, k, w, rows, keys, q_dtype, k_dtype, q_scale=None, k_scale=Non
                                   nthreads)
     if rc != 0:
         raise ValueError(f"oracle_score_pairs failed ({rc})")
+    return out
+
+
+def score_pairs_cond(q, k, w, rows, keys, q_dtype, k_dtype, q_scale=None, k_scale=None, nthreads=0):
+    """The absolute condition of Eq. (1) for the same pairs as score_pairs:
+    sum_j |w_j| sum_c |q_jc| |k_c| in fp64 from the dequantised inputs."""
+    q, k, w = _host(q), _host(k), _host(w).astype(np.float32)
+    q_scale, k_scale = _host(q_scale), _host(k_scale)
+    H, d = q.shape[-2], q.shape[-1]
+    r = np.ascontiguousarray(np.asarray(rows, np.int64).ravel())
+    kk = np.ascontiguousarray(np.asarray(keys, np.int64).ravel())
+    assert r.shape == kk.shape
+    out = np.empty(len(r), np.float64)
+    rc = lib().oracle_score_pairs_cond(_ptr(q), _ptr(q_scale), _dtype_code(q_dtype), _ptr(k), _ptr(k_scale),
+                                       _dtype_code(k_dtype), _ptr(w), H, d, _ptr(r), _ptr(kk), len(r), _ptr(out),
+                                       nthreads)
+    if rc != 0:
+        raise ValueError(f"oracle_score_pairs_cond failed ({rc})")
     return out
 
 

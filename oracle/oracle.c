@@ -215,6 +215,52 @@ int oracle_score_pairs(const void *q, const float *q_scale, int q_dtype, const v
     return err;
 }
 
+/* The absolute condition of Eq. (1) for one pair: sum_j |w_j| sum_c |q_jc| |k_c|.
+ * Any evaluation of the score in binary32 arithmetic (a sum of about d + H
+ * rounded products and partial sums) errs by at most a small multiple of the
+ * unit roundoff times this sum of magnitudes: the standard forward error bound
+ * of a floating-point sum, |fl(sum x_i) - sum x_i| <= gamma_n sum |x_i|. */
+static double indexer_cond(const double *qrow, const double *wrow, const double *krow, int H, int d)
+{
+    double total = 0.0;
+    for (int j = 0; j < H; ++j) {
+        double dot = 0.0;
+        for (int c = 0; c < d; ++c)
+            dot += fabs(qrow[(int64_t)j * d + c]) * fabs(krow[c]);
+        total += fabs(wrow[j]) * dot;
+    }
+    return total;
+}
+
+int oracle_score_pairs_cond(const void *q, const float *q_scale, int q_dtype, const void *k,
+                            const float *k_scale, int k_dtype, const float *w, int H, int d,
+                            const int64_t *rows, const int64_t *keys, int64_t n, double *out,
+                            int nthreads)
+{
+    if (H <= 0 || d <= 0 || n < 0)
+        return -1;
+    set_threads(nthreads);
+    int err = 0;
+#pragma omp parallel
+    {
+        double *qrow = malloc(sizeof(double) * (size_t)H * d);
+        double *wrow = malloc(sizeof(double) * (size_t)H);
+        double *krow = malloc(sizeof(double) * (size_t)d);
+        if (!qrow || !wrow || !krow)
+            err = -2;
+#pragma omp for schedule(static)
+        for (int64_t p = 0; p < n; ++p) {
+            if (!qrow || !wrow || !krow) continue;
+            load_row(q, q_scale, q_dtype, rows[p], H * d, qrow);
+            for (int j = 0; j < H; ++j) wrow[j] = (double)w[rows[p] * H + j];
+            load_row(k, k_scale, k_dtype, keys[p], d, krow);
+            out[p] = indexer_cond(qrow, wrow, krow, H, d);
+        }
+        free(qrow); free(wrow); free(krow);
+    }
+    return err;
+}
+
 /* ------------------------------------------------------ dense prefill */
 
 int oracle_prefill(const void *q, const float *q_scale, const void *k, const float *k_scale,

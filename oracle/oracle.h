@@ -41,6 +41,13 @@ int oracle_score_pairs(const void *q, const float *q_scale, int q_dtype, const v
                        const int64_t *rows, const int64_t *keys, int64_t n, double *out,
                        int nthreads);
 
+/* The absolute condition of Eq. (1) for the same pairs: sum_j |w_j| sum_c
+ * |q_jc| |k_c| (dequantised), the scale of any binary32 evaluation's error. */
+int oracle_score_pairs_cond(const void *q, const float *q_scale, int q_dtype, const void *k,
+                            const float *k_scale, int k_dtype, const float *w, int H, int d,
+                            const int64_t *rows, const int64_t *keys, int64_t n, double *out,
+                            int nthreads);
+
 int oracle_prefill(const void *q, const float *q_scale, const void *k, const float *k_scale,
                    const float *w, int dtype, int64_t Tq, int64_t Tk, int H, int d, int64_t q_pos0,
                    int topk, const int64_t *rows, int64_t nrows, int32_t *out_idx,

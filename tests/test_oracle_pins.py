@@ -227,6 +227,156 @@ def test_decode_single_head_matmul(oracle_lib):
         np.testing.assert_allclose(sc[b], rs[0], rtol=1e-14)
 
 
+# ------------------------------------------------- single-pair scores, Eq. (1)
+
+def test_score_pairs_single_head_is_a_matmul(oracle_lib):
+    """H=1, w=1, q,k >= 0: the score of pair (row r, key s) is q_r . k_s.
+    Checked against np.matmul on a query array and a key array of different
+    lengths, at pairs whose row and key differ: catches a w or q row taken
+    from the key index, a key row taken from the query index, and a
+    transposed operand."""
+    rng = np.random.default_rng(40)
+    Tq, Tk, d = 23, 61, 32
+    qv = rng.integers(0, 4, (Tq, 1, d)).astype(np.float32)
+    kv = rng.integers(0, 4, (Tk, d)).astype(np.float32)
+    rows = rng.integers(0, Tq, 300)
+    keys = rng.integers(0, Tk, 300)
+    got = oracle.score_pairs(_bf16(qv), _bf16(kv), np.ones((Tq, 1), np.float32), rows, keys, "bf16", "bf16")
+    S = np.matmul(qv[:, 0, :].astype(np.float64), kv.T.astype(np.float64))
+    assert np.array_equal(got, S[rows, keys])
+
+
+def _pairs_of(idx):
+    r, c = np.nonzero(idx >= 0)
+    return r, idx[r, c], c
+
+
+@pytest.mark.parametrize("dtype,gates", [("bf16", "mixed"), ("bf16", "negative"), ("fp8", "mixed"),
+                                         ("fp8", "negative")])
+def test_score_pairs_equal_prefill_scores(oracle_lib, dtype, gates):
+    """Every selected (row, key) of a dense prefill call, rescored one pair at
+    a time, gives the score the prefill call reported for it (bf16, and E4M3
+    with per-token scales; queries at q_pos0 > 0 so a row is not its position;
+    gates of mixed sign, or all negative as w = -|N(0,1)|/8).  The prefill
+    scores are pinned by the brute-force and closed-form tests above, so a
+    wrong w row, a dropped or misapplied scale, or a swapped dtype code in the
+    pair scorer fails here."""
+    T, Tq, H, d, K = 150, 60, 6, 32, 40
+    wl = make_prefill(T=T, H=H, d=d, topk=K, dtype=dtype, dist="normal", seed=41, Tq=Tq)
+    w = wl["w"].numpy()
+    if gates == "negative":
+        w = -np.abs(np.random.default_rng(42).standard_normal((Tq, H))).astype(np.float32) / 8
+    q_pos0 = wl.params["q_pos0"]
+    qs, ks = wl.tensors.get("q_scale"), wl.tensors.get("k_scale")
+    idx, sc = oracle.prefill(wl["q"], wl["k"], w, dtype, q_pos0, K, qs, ks)
+    r, keys, c = _pairs_of(idx)
+    got = oracle.score_pairs(wl["q"], wl["k"], w, r, keys, dtype, dtype, qs, ks)
+    assert np.array_equal(got, sc[r, c])
+    if gates == "negative":  # every term is w * ReLU(.) <= 0
+        assert (got <= 0).all()
+
+
+def test_score_pairs_decode_layout(oracle_lib):
+    """The decode layout: bf16 queries [B,H,d] against an E4M3 cache passed
+    flattened to [B*N, d] with its scales [B*N]; pair (b, b*N + s) is key s of
+    sequence b.  It must give the decode call's reported scores (pinned by
+    decode == prefill row above): catches swapped q/k dtype codes and a wrong
+    flattened cache index."""
+    B, N, H, d, K = 4, 120, 8, 64, 30
+    lens = [120, 77, 5, 64]
+    wl = make_decode(B, N, H, d, K, dist="normal", seed=43, seq_lens=lens)
+    idx, sc = oracle.decode(wl["q"], wl["k_cache"], wl["k_scale"], wl["w"], wl["seq_lens"], K)
+    b, keys, c = _pairs_of(idx)
+    kc = wl["k_cache"].reshape(B * N, d)
+    ks = wl["k_scale"].reshape(B * N)
+    got = oracle.score_pairs(wl["q"], kc, wl["w"], b, b * N + keys, "bf16", "fp8", None, ks)
+    assert np.array_equal(got, sc[b, c])
+    # the same pairs through torch's E4M3 decoder and a numpy Eq. (1)
+    qd = wl["q"].double().numpy()
+    kd = (kc.view(torch.float8_e4m3fn).double() * ks.double()[:, None]).numpy()
+    dots = np.einsum("phc,pc->ph", qd[b], kd[b * N + keys])
+    ref = (wl["w"].double().numpy()[b] * np.maximum(dots, 0.0)).sum(1)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-300)
+
+
+def test_score_pairs_cond_closed_forms(oracle_lib):
+    """The absolute condition of Eq. (1), C = sum_j |w_j| sum_c |q_jc| |k_c|:
+    with H = 1 and |w| = 1 it is |q| @ |k|^T (np.matmul of the magnitudes,
+    whatever the signs); with non-negative q, k, w every ReLU and |.| is the
+    identity, so C equals the pinned pair score exactly (bf16, and E4M3 with
+    per-token scales); for signed inputs C >= |score|, and w = 0 gives 0."""
+    rng = np.random.default_rng(44)
+    Tq, Tk, d = 17, 40, 32
+    qv = rng.integers(-3, 4, (Tq, 1, d)).astype(np.float32)
+    kv = rng.integers(-3, 4, (Tk, d)).astype(np.float32)
+    w = np.where(rng.random((Tq, 1)) < 0.5, -1.0, 1.0).astype(np.float32)
+    rows, keys = rng.integers(0, Tq, 200), rng.integers(0, Tk, 200)
+    got = oracle.score_pairs_cond(_bf16(qv), _bf16(kv), w, rows, keys, "bf16", "bf16")
+    ref = np.matmul(np.abs(qv[:, 0, :]).astype(np.float64), np.abs(kv).T.astype(np.float64))
+    assert np.array_equal(got, ref[rows, keys])
+    for dtype in ("bf16", "fp8"):
+        wl = make_prefill(T=90, H=5, d=64, topk=8, dtype=dtype, dist="int", seed=45)
+        q, k = wl["q"], wl["k"]
+        if dtype == "bf16":
+            q, k = _bf16(np.abs(_f64(q))), _bf16(np.abs(_f64(k)))
+            qs = ks = None
+        else:
+            qf = torch.as_tensor(np.abs(rng.standard_normal((90, 5 * 64))).astype(np.float32))
+            kf = torch.as_tensor(np.abs(rng.standard_normal((90, 64))).astype(np.float32))
+            q, qs = e4m3_quantize_rows(qf)
+            k, ks = e4m3_quantize_rows(kf)
+            q = q.reshape(90, 5, 64)
+        wn = np.abs(rng.standard_normal((90, 5))).astype(np.float32)
+        r2, k2 = rng.integers(0, 90, 300), rng.integers(0, 90, 300)
+        c = oracle.score_pairs_cond(q, k, wn, r2, k2, dtype, dtype, qs, ks)
+        sc = oracle.score_pairs(q, k, wn, r2, k2, dtype, dtype, qs, ks)
+        assert np.array_equal(c, sc), dtype
+    wl = make_prefill(T=60, H=8, d=32, topk=8, dtype="bf16", dist="normal", seed=46)
+    r3, k3 = rng.integers(0, 60, 300), rng.integers(0, 60, 300)
+    c = oracle.score_pairs_cond(wl["q"], wl["k"], wl["w"], r3, k3, "bf16", "bf16")
+    sc = oracle.score_pairs(wl["q"], wl["k"], wl["w"], r3, k3, "bf16", "bf16")
+    assert (c >= np.abs(sc)).all() and (c > 0).all()
+    assert (oracle.score_pairs_cond(wl["q"], wl["k"], np.zeros((60, 8), np.float32), r3, k3, "bf16", "bf16")
+            == 0).all()
+
+
+def test_tolerance_rule_accepts_rounding_rejects_errors(oracle_lib):
+    """The comparison rule: perturbing the oracle's scores by binary32-level
+    rounding (2^-20 of each key's absolute condition) passes, also on a row
+    whose K-th score is near zero; a 2% error on one clearly selected key, a
+    dropped key well above the K-th score, or a wrong count fails."""
+    from tests.parity import compare, pair_refs
+    T, K = 300, 64
+    wl = make_prefill(T=T, H=16, d=64, topk=K, dtype="bf16", dist="normal", seed=47)
+    rows = np.arange(100, 300, 7)
+    ri, rs = oracle.prefill(wl["q"], wl["k"], wl["w"], "bf16", 0, K, rows=rows)
+    score_of, cond_of = pair_refs(wl["q"], wl["k"], wl["w"], rows, "bf16", "bf16")
+    cond = np.zeros(ri.shape)
+    for n in range(len(rows)):
+        v = ri[n] >= 0
+        cond[n, v] = cond_of(n, ri[n][v])
+    rng = np.random.default_rng(48)
+    noisy = rs + np.where(ri >= 0, rng.uniform(-1, 1, rs.shape) * 2.0 ** -20 * cond, 0.0)
+    compare(ri, noisy, ri, rs, False, score_of, ref_cond_of=cond_of)
+    bad = rs.copy()
+    n = 3
+    top = np.argmax(rs[n])
+    bad[n, top] *= 1.02
+    with pytest.raises(AssertionError):
+        compare(ri, bad, ri, rs, False, score_of, ref_cond_of=cond_of)
+    dropped = ri.copy()
+    keep = np.delete(dropped[n][dropped[n] >= 0], top)
+    dropped[n] = -1
+    others = np.setdiff1d(np.arange(rows[n] + 1), ri[n])
+    dropped[n][:K] = np.sort(np.concatenate([keep, others[:1]]))
+    with pytest.raises(AssertionError):
+        compare(dropped, None, ri, rs, False, score_of, ref_cond_of=cond_of)
+    short = ri.copy()
+    short[n, K - 1] = -1
+    with pytest.raises(AssertionError):
+        compare(short, None, ri, rs, False, score_of, ref_cond_of=cond_of)
+
+
 # --------------------------------------------------------- group bank pins
 
 def _gb(T, G, P, K, seed, Hs=None, H=4, d=16, Tq=None, dist="int", **kw):
