@@ -14,7 +14,15 @@ bounded sample of the same inputs.
 Inputs are generated on the GPU before timing (resident in HBM); outputs,
 workspace and streams are allocated before the timed region.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--adindex [--adindex-len T]] [--dsa16k] [--mtp] [--calib] [--group-query]
+The line also carries, each with its roofline and an oracle baseline on
+sampled rows: the 16K bf16 DSA prefill layer (dsa16k), the 64K ADIndex group
+bank against the dense indexer (adindex), the 61-layer pass with Table 9's
+per-layer (G, P) (layerwise), and the plain HBM read stream (decode.read_ceiling).
+If any sampled GPU rows disagree with the oracle, `value` is null, the line
+says why, and the exit status is 1.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-dsa16k] [--no-adindex]
+                    [--adindex-len T] [--no-layerwise] [--mtp] [--calib] [--group-query]
 """
 from __future__ import annotations
 
@@ -85,6 +93,58 @@ def _events_ms(pairs):
     return [s.elapsed_time(e) for s, e in pairs]
 
 
+def _cpu_model():
+    """The host CPU's model name (first entry of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _cpu_fields(oracle):
+    return dict(cores=oracle.max_threads(), cpu_model=_cpu_model(), host_logical_cpus=os.cpu_count())
+
+
+PARITY = {}  # leg name -> "ok" or the failure message; any failure invalidates the line
+
+
+def _parity(name, fn):
+    """Run a parity check of sampled GPU rows against the oracle; record it."""
+    try:
+        fn()
+        PARITY[name] = "ok"
+    except AssertionError as e:
+        PARITY[name] = "FAILED: " + str(e)[:300]
+    return PARITY[name]
+
+
+def _stratified(T, n, always=()):
+    """n rows spread evenly over 0..T-1, the last 16 rows and `always`."""
+    r = np.concatenate([np.linspace(0, T - 1, n).astype(np.int64), np.arange(T - 16, T),
+                        np.asarray(always, np.int64)])
+    return np.unique(r[(r >= 0) & (r < T)])
+
+
+def _timed_calls(fn, steps, stream):
+    """Time `steps` calls of fn with HIP events on `stream` (after one warm
+    call); returns (wall ms per call, event ms per call)."""
+    fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s_, e_ in evs:
+        s_.record(stream)
+        fn()
+        e_.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return wall, float(np.mean(_events_ms(evs)))
+
+
 # ------------------------------------------------------------------ prefill
 
 def bench_prefill(dsa, args, log):
@@ -95,7 +155,7 @@ def bench_prefill(dsa, args, log):
     q, k, w, qs, ks = wl["q"], wl["k"], wl["w"], wl["q_scale"], wl["k_scale"]
     out = torch.empty((T, K), dtype=torch.int32, device="cuda")
     nchunks = T // chunk
-    # one workspace for every chunk: chunks whose rows fit a full-row buffer need more than the last
+    # one workspace serves every chunk (its size does not depend on the key count)
     ws = torch.empty(max(dsa.workspace_prefill(chunk, (c + 1) * chunk, H, d, K, dsa.DSAIDX_FP8_E4M3)
                          for c in range(nchunks)), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
@@ -149,10 +209,9 @@ def cpu_prefill(wl, out, args, log):
     """The oracle on a stratified sample of query rows of the same workload;
     the sampled GPU rows are checked against it (tolerance rule)."""
     import oracle
-    from tests.parity import compare
+    from tests.parity import compare, pair_refs
     T, K = 131072, 2048
-    n = args.cpu_rows
-    rows = np.unique(np.concatenate([np.linspace(0, T - 1, n - 2).astype(np.int64), [T - 2, T - 1]]))
+    rows = _stratified(T, args.cpu_rows)
     log(f"cpu oracle on {len(rows)} sampled prefill rows")
     qh = wl["q"].cpu()
     kh, wh = wl["k"].cpu(), wl["w"].cpu()
@@ -163,17 +222,12 @@ def cpu_prefill(wl, out, args, log):
     pairs = int((rows + 1).sum())
     gi = out[torch.as_tensor(rows, device="cuda")].cpu().numpy()
 
-    def score_of(r, keys):
-        return oracle.score_pairs(qh, kh, wh, np.full(len(keys), rows[r]), keys, "fp8", "fp8", qsh, ksh)
-    parity = "ok"
-    try:
-        compare(gi, None, ri, rs, False, score_of)
-    except AssertionError as e:  # reported, not raised: the bench still prints its line
-        parity = "FAILED: " + str(e)[:300]
+    score_of, cond_of = pair_refs(qh, kh, wh, rows, "fp8", "fp8", qsh, ksh)
+    parity = _parity("prefill128k", lambda: compare(gi, None, ri, rs, False, score_of, ref_cond_of=cond_of))
     return dict(value=2 * 64 * 128 * pairs / dt / 1e12, unit="TFLOP/s", gpairs_per_s=pairs / dt / 1e9,
-                cores=oracle.max_threads(), kind="oracle", seconds=dt,
-                sample=f"{len(rows)} query rows of the 128K prefill spread over positions 0..{T - 1} "
-                       f"({pairs} scored pairs), fp64 C oracle with OpenMP over rows",
+                kind="oracle", seconds=dt, **_cpu_fields(oracle),
+                sample=f"{len(rows)} query rows of the 128K prefill: evenly spread over positions 0..{T - 1} "
+                       f"and the last 16 ({pairs} scored pairs), fp64 C oracle with OpenMP over rows",
                 parity_of_sampled_gpu_rows=parity)
 
 
@@ -222,7 +276,7 @@ def bench_decode(dsa, args, log):
                              traffic=_traffic("decode_call_decode256k")))
     if not args.no_cpu:
         import oracle
-        from tests.parity import compare
+        from tests.parity import compare, pair_refs
         rows = np.arange(0, B, max(1, B // args.cpu_decode_rows))[:args.cpu_decode_rows]
         log(f"cpu oracle on {len(rows)} decode rows")
         h = {k2: v.cpu() for k2, v in t.items()}
@@ -232,26 +286,44 @@ def bench_decode(dsa, args, log):
         kc = h["k_cache"].reshape(B * N, d)
         ksc = h["k_scale"].reshape(B * N)
 
-        def score_of(r, keys):
-            return oracle.score_pairs(h["q"], kc, h["w"], np.full(len(keys), rows[r]), rows[r] * N + keys,
-                                      "bf16", "fp8", None, ksc)
-        parity = "ok"
-        try:
-            compare(out.cpu().numpy()[rows], None, ri, rs, False, score_of)
-        except AssertionError as e:
-            parity = "FAILED: " + str(e)[:300]
+        score_of, cond_of = pair_refs(h["q"], kc, h["w"], rows, "bf16", "fp8", None, ksc,
+                                      key_of=lambda r, keys: rows[r] * N + keys)
+        parity = _parity("decode256k", lambda: compare(out.cpu().numpy()[rows], None, ri, rs, False, score_of,
+                                                       ref_cond_of=cond_of))
         per_row = alg_bytes / B
         res["cpu_baseline"] = dict(value=per_row * len(rows) / dt / 1e9, unit="GB/s",
-                                   gpairs_per_s=len(rows) * N / dt / 1e9, cores=oracle.max_threads(),
-                                   kind="oracle", seconds=dt,
+                                   gpairs_per_s=len(rows) * N / dt / 1e9, kind="oracle", seconds=dt,
+                                   **_cpu_fields(oracle),
                                    sample=f"{len(rows)} of the 32 decode rows (full 262144-key scans)",
                                    parity_of_sampled_gpu_rows=parity)
+    del t, wl
+    res["read_ceiling"] = bench_read_probe(dsa, args, log)
+    res["read_ceiling"]["decode_frac_of_ceiling"] = achieved / res["read_ceiling"]["gbs"]
     return res
+
+
+def bench_read_probe(dsa, args, log):
+    """The plain HBM read stream (indexer_read_probe: every byte of a 4 GiB
+    buffer read once with coalesced 16-byte loads), timed with HIP events: the
+    practical ceiling the memory-bound decode scan is compared with."""
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    out = torch.empty(2048, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    log("timing the plain read stream (4 GiB)")
+    _, ms = _timed_calls(lambda: dsa.read_probe(buf, 2048, out), 20, stream)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return dict(kernel="read_probe_kernel (indexer_read_probe)", bytes=nbytes, ms=ms, gbs=gbs,
+                frac_of_peak=gbs / PEAK_HBM_GBS)
 
 
 # ------------------------------------------------------------------ ADIndex
 
 def bench_adindex(dsa, args, log):
+    """The ADIndex group token bank (T=65536, G=16, P=8192, H=Hs=64, d=128,
+    bf16) against the dense bf16 indexer at the same length; the roofline is
+    the method's algorithmic flops (2*H*d per scored pair) over the event-timed
+    call, against the bf16 MFMA peak."""
     from workloads import make_workload
     T, H, d, K, G, P = args.adindex_len, 64, 128, 2048, 16, 8192
     log(f"generating ADIndex inputs T={T} bf16 on the GPU")
@@ -259,14 +331,16 @@ def bench_adindex(dsa, args, log):
     t = wl.tensors
     out = torch.empty((T, K), dtype=torch.int32, device="cuda")
     out_pool = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    bank = torch.empty((-(-T // G), P), dtype=torch.int32, device="cuda")
     ws = torch.empty(dsa.workspace_group_bank(T, T, H, H, d, G, P, K, dsa.DSAIDX_BF16, dsa.POOL_MEAN),
                      dtype=torch.uint8, device="cuda")
     dense_out = torch.empty((T, K), dtype=torch.int32, device="cuda")
     wsd = torch.empty(dsa.workspace_prefill(T, T, H, d, K, dsa.DSAIDX_BF16), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
 
     def step():
         dsa.indexer_group_bank(t["q"], t["k"], t["w"], t["qbar"], t["wbar"], 0, G, P, K, want_score=False,
-                               out_idx=out, ws=ws)
+                               out_idx=out, out_bank=bank, ws=ws)
 
     def step_pool():
         dsa.indexer_group_bank(t["q"], t["k"], t["w"], None, None, 0, G, P, K, flags=dsa.POOL_MEAN,
@@ -275,16 +349,13 @@ def bench_adindex(dsa, args, log):
     def dense():
         dsa.indexer_prefill(t["q"], t["k"], t["w"], 0, K, want_score=False, out_idx=dense_out, ws=wsd)
 
-    res = {}
+    log("timing the ADIndex bank path, its pooled variant and the dense indexer")
+    ms, ev = {}, {}
     for name, fn, steps in (("adindex", step, args.steps), ("adindex_pool", step_pool, args.steps),
-                            ("dense", dense, max(1, args.steps // 2))):
-        fn()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            fn()
-        torch.cuda.synchronize()
-        res[name] = (time.perf_counter() - t0) * 1e3 / steps
+                            ("dense", dense, max(2, args.steps // 2))):
+        ms[name], ev[name] = _timed_calls(fn, steps, stream)
+    step()  # leave the bank result (and its banks) in `out` for the parity leg
+    torch.cuda.synchronize()
     pairs = dsa.indexer_group_bank_pairs(T, 0, G, P)
     flops = 2 * H * d * pairs
     dense_pairs = _pairs_causal(0, T)
@@ -295,26 +366,88 @@ def bench_adindex(dsa, args, log):
     def recall(o):
         return float(np.mean([len(np.intersect1d(x, y)) / len(y) for x, y in zip(o[sample].cpu().numpy(), b)]))
     rec, rec_pool = recall(out), recall(out_pool)
-    return dict(workload=f"ADIndex group token bank: T={T}, G=16, P=8192, H=Hs=64, d=128, top-2048, bf16",
-                ms_per_step=res["adindex"], tflops=flops / (res["adindex"] * 1e-3) / 1e12,
-                gpairs_per_s=pairs / (res["adindex"] * 1e-3) / 1e9, pairs=pairs,
-                dense_ms=res["dense"], dense_tflops=2 * H * d * dense_pairs / (res["dense"] * 1e-3) / 1e12,
-                speedup_vs_dense=res["dense"] / res["adindex"], scoring_count_ratio=dense_pairs / pairs,
-                recall_vs_dense=rec,
-                pooled=dict(ms_per_step=res["adindex_pool"], speedup_vs_dense=res["dense"] / res["adindex_pool"],
-                            recall_vs_dense=rec_pool,
-                            note="training-free group query: mean of the group's own queries and gates"),
-                recall_note="synthetic i.i.d. queries: recall reflects the random inputs, not trained data",
-                roofline=dict(bound="mfma", achieved=flops / (res["adindex"] * 1e-3) / 1e12,
-                              peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                              frac=flops / (res["adindex"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS))
+    achieved = flops / (ev["adindex"] * 1e-3) / 1e12
+    res = dict(workload=f"ADIndex group token bank: T={T}, G=16, P=8192, H=Hs=64, d=128, top-2048, bf16",
+               ms_per_step=ms["adindex"], tflops=flops / (ms["adindex"] * 1e-3) / 1e12,
+               gpairs_per_s=pairs / (ms["adindex"] * 1e-3) / 1e9, pairs=pairs,
+               dense_ms=ms["dense"], dense_tflops=2 * H * d * dense_pairs / (ms["dense"] * 1e-3) / 1e12,
+               speedup_vs_dense=ms["dense"] / ms["adindex"], scoring_count_ratio=dense_pairs / pairs,
+               recall_vs_dense=rec,
+               pooled=dict(ms_per_step=ms["adindex_pool"], speedup_vs_dense=ms["dense"] / ms["adindex_pool"],
+                           recall_vs_dense=rec_pool,
+                           note="training-free group query: mean of the group's own queries and gates"),
+               recall_note="synthetic i.i.d. queries: recall reflects the random inputs, not trained data",
+               roofline=dict(bound="mfma", kernel="indexer_group_bank (group scan + refinement + fallback "
+                                                  "launches of dense_topk_kernel<bf16>, one call)",
+                             achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                             frac=achieved / PEAK_BF16_TFLOPS, avg_launch_ms=ev["adindex"],
+                             flops_per_launch=flops, traffic=None))
+    if T == 65536 and not args.no_cpu:
+        res["cpu_baseline"] = cpu_adindex(wl, out, bank, G, P, K, args, log)
+    res["_dense_ms"] = ms["dense"]
+    return res
+
+
+def cpu_adindex(wl, out, bank, G, P, K, args, log):
+    """The oracle's group bank on stratified query rows (the last 16 and the
+    groups around the fallback/bank boundary included); the sampled GPU rows
+    and their groups' banks are checked against it under the tolerance rule."""
+    import oracle
+    from tests.parity import compare, pair_refs, refine_over_bank
+    T = wl.params["T"]
+    rows = _stratified(T, args.cpu_adindex_rows, always=np.arange(8176, 8208))
+    log(f"cpu oracle on {len(rows)} sampled ADIndex rows")
+    h = {k: v.cpu() for k, v in wl.tensors.items()}
+    t0 = time.perf_counter()
+    ri, rs, rb, _ = oracle.group_bank(h["q"], h["k"], h["w"], h["qbar"], h["wbar"], "bf16", 0, G, P, K,
+                                      rows=rows, want_bank=True)
+    dt = time.perf_counter() - t0
+    gi = out[torch.as_tensor(rows, device="cuda")].cpu().numpy()
+    gbank = bank.cpu().numpy()
+    groups = np.unique(rows // G)
+    # scored pairs of the sample: each sampled group's anchor scan (once) and
+    # each sampled row's candidates
+    pairs = 0
+    for g in groups:
+        a = g * G
+        pairs += (a + 1) if a + 1 > P else 0
+    for r in rows:
+        a = (r // G) * G
+        pairs += (r + 1) if a + 1 <= P else min(P, a + 1) + (r - a)
+
+    def check():
+        score_of, cond_of = pair_refs(h["q"], h["k"], h["w"], rows, "bf16", "bf16")
+        for g in groups:
+            if (rb[g] == -1).all():
+                assert (gbank[g] == -1).all(), f"bank {g} should be empty"
+                continue
+            bank_score, bank_cond = pair_refs(h["qbar"], h["k"], h["wbar"], [g], "bf16", "bf16")
+            v = rb[g][rb[g] >= 0]
+            compare(gbank[g:g + 1], None, rb[g:g + 1], bank_score(0, v)[None, :], False, bank_score,
+                    label=f"bank {g}", ref_cond_of=bank_cond)
+        same = np.array([np.array_equal(rb[r // G], gbank[r // G]) for r in rows])
+        sel = np.nonzero(same)[0]
+        compare(gi[sel], None, ri[sel], rs[sel], False, lambda r, keys: score_of(sel[r], keys),
+                ref_cond_of=lambda r, keys: cond_of(sel[r], keys))
+        other = rows[~same]
+        if len(other):  # groups whose bank differs by tolerated swaps: Eq. (14) over the GPU's bank
+            oi, osc = refine_over_bank(h, gbank, other, G, K)
+            o_score, o_cond = pair_refs(h["q"], h["k"], h["w"], other, "bf16", "bf16")
+            compare(gi[~same], None, oi, osc, False, o_score, label="own bank", ref_cond_of=o_cond)
+    parity = _parity("adindex64k", check)
+    return dict(value=2 * 64 * 128 * pairs / dt / 1e12, unit="TFLOP/s", gpairs_per_s=pairs / dt / 1e9,
+                kind="oracle", seconds=dt, **_cpu_fields(oracle),
+                sample=f"{len(rows)} query rows of the 64K ADIndex call (evenly spread, the last 16, rows "
+                       f"8176..8207 around the first bank group) and the banks of their {len(groups)} groups "
+                       f"({pairs} scored pairs), fp64 C oracle with OpenMP",
+                parity_of_sampled_gpu_rows=parity)
 
 
 # ---------------------------------------------------- DSA-shaped bf16 prefill
 
 def bench_dsa16k(dsa, args, log):
     """One layer of DSA-shaped bf16 prefill: T=16384, H=64, d=128, top-2048, one
-    call (134,225,920 pairs, 2.199 TFLOP)."""
+    call (134,225,920 pairs, 2.199 TFLOP), against the bf16 MFMA peak."""
     from workloads import make_workload
     T, H, d, K = 16384, 64, 128, 2048
     log("generating DSA bf16 prefill inputs T=16384 on the GPU")
@@ -322,20 +455,111 @@ def bench_dsa16k(dsa, args, log):
     t = wl.tensors
     out = torch.empty((T, K), dtype=torch.int32, device="cuda")
     ws = torch.empty(dsa.workspace_prefill(T, T, H, d, K, dsa.DSAIDX_BF16), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
 
     def step():
         dsa.indexer_prefill(t["q"], t["k"], t["w"], 0, K, want_score=False, out_idx=out, ws=ws)
-    step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    log("timing the 16K bf16 prefill")
+    ms, ev = _timed_calls(step, args.steps * 2, stream)
     pairs = _pairs_causal(0, T)
-    tf = 2 * H * d * pairs / (ms * 1e-3) / 1e12
-    return dict(workload="DSA prefill, one layer: T=16384, H=64, d=128, top-2048, bf16", ms_per_call=ms,
-                tflops=tf, gpairs_per_s=pairs / (ms * 1e-3) / 1e9, frac_of_bf16_peak=tf / PEAK_BF16_TFLOPS)
+    flops = 2 * H * d * pairs
+    tf = flops / (ms * 1e-3) / 1e12
+    achieved = flops / (ev * 1e-3) / 1e12
+    res = dict(workload="DSA prefill, one layer: T=16384, H=64, d=128, top-2048, bf16", ms_per_call=ms,
+               tflops=tf, gpairs_per_s=pairs / (ms * 1e-3) / 1e9, frac_of_bf16_peak=tf / PEAK_BF16_TFLOPS,
+               roofline=dict(bound="mfma", kernel="dense_topk_kernel<bf16> (one call: rows of at most "
+                                                  "2K + 2048 keys keep their row, the rest stream)",
+                             achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                             frac=achieved / PEAK_BF16_TFLOPS, avg_launch_ms=ev, flops_per_launch=flops,
+                             traffic=None))
+    if not args.no_cpu:
+        import oracle
+        from tests.parity import compare, pair_refs
+        rows = _stratified(T, args.cpu_dsa16k_rows)
+        log(f"cpu oracle on {len(rows)} sampled 16K rows")
+        h = {k2: v.cpu() for k2, v in t.items()}
+        t0 = time.perf_counter()
+        ri, rs = oracle.prefill(h["q"], h["k"], h["w"], "bf16", 0, K, rows=rows)
+        dt = time.perf_counter() - t0
+        spairs = int((rows + 1).sum())
+        gi = out[torch.as_tensor(rows, device="cuda")].cpu().numpy()
+
+        score_of, cond_of = pair_refs(h["q"], h["k"], h["w"], rows, "bf16", "bf16")
+        parity = _parity("dsa16k", lambda: compare(gi, None, ri, rs, False, score_of, ref_cond_of=cond_of))
+        res["cpu_baseline"] = dict(value=2 * H * d * spairs / dt / 1e12, unit="TFLOP/s",
+                                   gpairs_per_s=spairs / dt / 1e9, kind="oracle", seconds=dt,
+                                   **_cpu_fields(oracle),
+                                   sample=f"{len(rows)} query rows of the 16K prefill (evenly spread and the "
+                                          f"last 16; {spairs} scored pairs), fp64 C oracle with OpenMP",
+                                   parity_of_sampled_gpu_rows=parity)
+    return res
+
+
+# ------------------------------------------------------ layer-wise reuse
+
+TABLE9_DEEPSEEK_MAX = (  # (G, P, layers) of Appendix C.4 Table 9 (DeepSeek-V3.2, max statistic)
+    (16, 8192, "2,3,5-8,10,12-14,18,22,37,44"),
+    (8, 8192, "0,1,9,15,23,25,34,36,41,42,47,53,54,58,60"),
+    (16, 16384, "4,11,16,19,20,24,26-32,35,38-40,48,50-52,56,57,59"),
+    (8, 16384, "17,21,33,43,45,46,49,55"),
+)
+
+
+def _layer_list(spec):
+    out = []
+    for part in spec.split(","):
+        a, _, b = part.partition("-")
+        out.extend(range(int(a), int(b or a) + 1))
+    return out
+
+
+def bench_layerwise(dsa, args, log, dense_ms=None):
+    """The 61 indexer layers of DeepSeek-V3.2 at T=65536, each with the (G, P)
+    that Table 9 assigns it, in one indexer_layers call (bf16, H=Hs=64,
+    d=128, top-2048; every layer on the same synthetic inputs).  Reported
+    against 61 dense layers (the dense 64K layer's time times 61) and against
+    Eq. (27)'s scoring-count prediction for prefill."""
+    from workloads import make_workload
+    T, H, d, K = 65536, 64, 128, 2048
+    setting = {}
+    for G, P, spec in TABLE9_DEEPSEEK_MAX:
+        for layer in _layer_list(spec):
+            setting[layer] = (G, P)
+    n = len(setting)
+    assert sorted(setting) == list(range(61)), "Table 9 covers layers 0..60 once"
+    log("generating layer-wise inputs T=65536 bf16 on the GPU")
+    wl = make_workload(5, seed=args.seed, device="cuda", T=T)
+    t = wl.tensors
+    g8w = make_workload(5, seed=args.seed + 1, device="cuda", T=T, G=8)  # a group query for groups of 8
+    g8 = dict(qbar=g8w["qbar"], wbar=g8w["wbar"])
+    del g8w
+    out = torch.empty((T, K), dtype=torch.int32, device="cuda")  # every layer writes here (timing only)
+    layers = []
+    for layer in range(n):
+        G, P = setting[layer]
+        src = t if G == 16 else g8
+        layers.append(dict(q=t["q"], k=t["k"], w=t["w"], qbar=src["qbar"], wbar=src["wbar"], G=G, P=P,
+                           out_idx=out))
+    ws = torch.empty(dsa.workspace_layers(layers, T, T, H, d, K, dsa.DSAIDX_BF16), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+    log(f"timing {n} layers with Table 9's settings")
+    ms, ev = _timed_calls(lambda: dsa.indexer_layers(layers, 0, K, ws=ws), max(1, args.layer_steps), stream)
+    Gs = [setting[i][0] for i in range(n)]
+    Ps = [setting[i][1] for i in range(n)]
+    predicted = dsa.layerwise_speedup(list(zip(Gs, Ps)), T, R=0)
+    pairs = sum(dsa.indexer_group_bank_pairs(T, 0, G, P) for G, P in zip(Gs, Ps))
+    res = dict(workload=f"layer-wise reuse: DeepSeek-V3.2's 61 indexer layers at T={T}, (G, P) per layer from "
+                        "Table 9 (max statistic: 14 x (16, 8K), 15 x (8, 8K), 24 x (16, 16K), 8 x (8, 16K)), "
+                        "bf16, H=Hs=64, d=128, top-2048, one indexer_layers call",
+               ms_per_call=ms, ms_per_layer=ms / n, pairs=pairs,
+               tflops=2 * H * d * pairs / (ms * 1e-3) / 1e12,
+               eq27_predicted_speedup=predicted)
+    if dense_ms:
+        res["dense_ms_61_layers"] = dense_ms * n
+        res["measured_speedup_vs_dense"] = dense_ms * n / ms
+        res["measured_over_predicted"] = res["measured_speedup_vs_dense"] / predicted
+    return res
 
 
 # ------------------------------------------------------------------ MTP
@@ -471,12 +695,16 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--cpu-decode-rows", type=int, default=32)
+    ap.add_argument("--cpu-dsa16k-rows", type=int, default=1024)
+    ap.add_argument("--cpu-adindex-rows", type=int, default=512)
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--adindex", action="store_true", help="also time the ADIndex group-bank workload")
+    ap.add_argument("--no-adindex", action="store_true", help="skip the ADIndex group-bank workload")
     ap.add_argument("--adindex-len", type=int, default=65536, metavar="T",
                     help="sequence length of the ADIndex workload (65536; the pages quote 262144)")
+    ap.add_argument("--no-dsa16k", action="store_true", help="skip the 16K bf16 DSA prefill layer")
+    ap.add_argument("--no-layerwise", action="store_true", help="skip the 61-layer Table 9 pass")
+    ap.add_argument("--layer-steps", type=int, default=1, help="timed 61-layer passes (about 0.7 s each)")
     ap.add_argument("--mtp", action="store_true", help="also time MTP verification windows at 256K")
-    ap.add_argument("--dsa16k", action="store_true", help="also time the 16K bf16 DSA prefill layer")
     ap.add_argument("--calib", action="store_true", help="also time the calibration statistics kernels")
     ap.add_argument("--group-query", action="store_true", help="also time the group query construction")
     ap.add_argument("--quiet", action="store_true")
@@ -532,17 +760,30 @@ def main():
     }
     if not args.no_decode:
         line["decode"] = bench_decode(dsa, args, log)
-    if args.adindex:
-        line["adindex"] = bench_adindex(dsa, args, log)
-    if args.dsa16k:
+    if not args.no_dsa16k:
         line["dsa16k"] = bench_dsa16k(dsa, args, log)
+    dense64k_ms = None
+    if not args.no_adindex:
+        line["adindex"] = bench_adindex(dsa, args, log)
+        dense64k_ms = line["adindex"].pop("_dense_ms")
+    if not args.no_layerwise:
+        line["layerwise"] = bench_layerwise(dsa, args, log,
+                                            dense64k_ms if args.adindex_len == 65536 else None)
     if args.mtp:
         line["mtp"] = bench_mtp(dsa, args, log)
     if args.calib:
         line["calib"] = bench_calib(dsa, args, log)
     if args.group_query:
         line["group_query"] = bench_group_query(dsa, args, log)
+    failed = {k: v for k, v in PARITY.items() if v != "ok"}
+    if failed:  # a wrong result makes every rate above meaningless
+        line["value"] = None
+        line["invalid"] = "parity of sampled GPU rows against the oracle failed: " + "; ".join(
+            f"{k}: {v}" for k, v in failed.items())
+    line["parity"] = dict(PARITY)
     print(json.dumps(line), flush=True)
+    if failed:
+        sys.exit(1)
 
 
 if __name__ == "__main__":

@@ -77,12 +77,13 @@ enum {
  *   k_scale  [Tk] fp32    per-key-token scale (fp8 only, else NULL)
  *   w        [Tq, H] fp32 per-query head weights
  *   out_idx  [Tq, topk] int32;  out_score [Tq, topk] fp32 or NULL
- * The whole Tq x Tk score matrix is never stored.  With Tk above 65472 each
- * query keeps a streaming candidate buffer of 2 topk + 2048 entries in `ws`;
- * with Tk at most 65472 every query's row of Tk scores fits its buffer, so
- * the row is stored in `ws` and selected once at the end (the workspace then
- * grows with Tk: 8 bytes per key per query of a launch of at most 16384
- * queries, about 2 GB for 4096 queries over 61440 keys).
+ * The Tq x Tk score matrix is never stored: each query keeps a candidate
+ * buffer of cap = 2 topk + 2048 entries (rounded up to a multiple of 64) in
+ * `ws`, 8 bytes per entry, for the queries of one launch (at most 16384), so
+ * the workspace does not depend on Tk.  A query that sees at most cap keys
+ * stores its whole (short) score row there and selects once at the end; a
+ * longer one streams: only scores above a running threshold enter the
+ * buffer, and a radix selection compacts it to the best topk when it fills.
  */
 int indexer_prefill(const void *q, const float *q_scale, const void *k, const float *k_scale,
                     const float *w, int dtype, int64_t Tq, int64_t Tk, int H, int d,
@@ -136,6 +137,42 @@ int indexer_group_bank(const void *q, const float *q_scale, const void *k, const
  * DSAIDX_POOL_MEAN changes the size: it adds the pooled queries and gates). */
 size_t indexer_group_bank_workspace_size(int64_t Tq, int64_t Tk, int H, int Hs, int d, int G,
                                          int P, int topk, int dtype, unsigned flags);
+
+/*
+ * Layer-wise reuse, Section 4.1 (Eq. (5): each layer keeps its own calibrated
+ * group size and bank budget), Section 4.3 and Appendix C.4 (Tables 9-14 list
+ * the per-layer (G, P) of two models): one call runs the indexer of nlayers
+ * layers that share the shapes (Tq, Tk, H, d, q_pos0, topk, dtype), each with
+ * its own tensors and setting.  A layer with G = 0 runs the original indexer
+ * (indexer_prefill; its qbar, qbar_scale, wbar, out_bank must be NULL and
+ * flags 0); any other layer runs indexer_group_bank with its G, P, Hs and
+ * flags.  Every layer is checked before anything is enqueued (an error names
+ * the layer and leaves every output untouched); the layers then run in
+ * order on `stream`, one after another, sharing one workspace of
+ * indexer_layers_workspace_size() bytes (the largest layer's need).
+ */
+typedef struct {
+    const void *q;          /* [Tq, H, d] dtype codes */
+    const float *q_scale;   /* [Tq] (fp8) or NULL */
+    const void *k;          /* [Tk, d] dtype codes */
+    const float *k_scale;   /* [Tk] (fp8) or NULL */
+    const float *w;         /* [Tq, H] */
+    const void *qbar;       /* G > 0: [ceil(Tq/G), Hs, d] (NULL with DSAIDX_POOL_MEAN) */
+    const float *qbar_scale;/* G > 0, fp8: [ceil(Tq/G)] */
+    const float *wbar;      /* G > 0: [ceil(Tq/G), Hs] (NULL with DSAIDX_POOL_MEAN) */
+    int Hs;                 /* G > 0: group-indexer heads */
+    int G, P;               /* G = 0: the original indexer (P ignored) */
+    unsigned flags;         /* G > 0: DSAIDX_FORCE_BANK, DSAIDX_POOL_MEAN or 0 */
+    int32_t *out_idx;       /* [Tq, topk] */
+    float *out_score;       /* [Tq, topk] or NULL */
+    int32_t *out_bank;      /* G > 0: [ceil(Tq/G), P] or NULL */
+} dsaidx_layer;
+
+int indexer_layers(const dsaidx_layer *layers, int nlayers, int dtype, int64_t Tq, int64_t Tk, int H,
+                   int d, int64_t q_pos0, int topk, void *ws, size_t ws_bytes, void *stream);
+/* Workspace bytes of indexer_layers for any q_pos0 (0 on bad arguments). */
+size_t indexer_layers_workspace_size(const dsaidx_layer *layers, int nlayers, int64_t Tq, int64_t Tk,
+                                     int H, int d, int topk, int dtype);
 
 /* Number of query-key scores indexer_group_bank evaluates for these sizes
  * (the unit of the cost model of Appendix A.1): fallback queries score t+1
@@ -244,6 +281,16 @@ int indexer_select_setting(const double *stat_by_G, double L, int R, int m, doub
  * the layers.  -1 on bad arguments. */
 double indexer_layerwise_speedup(const int *G, const int *P, int nlayers, double L, int R, int m,
                                  double a);
+
+/*
+ * Measurement aid (not an operation of the pages): read `bytes` bytes of
+ * device memory at p (16-byte aligned) once with coalesced 16-byte loads,
+ * spread over nblocks workgroups (1..65535), and write one XOR checksum word
+ * per workgroup to out [nblocks] (device).  Its rate is the plain HBM read
+ * stream that the memory-bound kernels (the decode scan above all) are
+ * compared with.
+ */
+int indexer_read_probe(const void *p, int64_t bytes, uint32_t *out, int nblocks, void *stream);
 
 /* Message describing the calling thread's last non-OK return ("" if none). */
 const char *indexer_last_error(void);

@@ -11,6 +11,8 @@ without the built library, or with host tensors, raises.
     idx, score, bank = indexer_group_bank(q, k, w, None, None, q_pos0, G, P, topk,
                                           flags=POOL_MEAN)   # training-free group query
     idx, score, bank = indexer_mtp(q, k_cache, k_scale, w, qbar, wbar, prefix_lens, G, P, topk)
+    outs = indexer_layers([dict(q=q, k=k, w=w, qbar=qb, wbar=wb, G=16, P=8192), dict(q=q, k=k, w=w, G=0)],
+                          q_pos0, topk)            # per-layer (G, P); G = 0 is the original indexer
 
 Tensors (contiguous, on the GPU): q [Tq,H,d] bf16 or uint8 E4M3 codes,
 k [Tk,d] the same dtype, w [Tq,H] fp32, per-token fp32 scales for E4M3.
@@ -20,12 +22,13 @@ from __future__ import annotations
 import torch
 
 from ._lib import (DSAIDX_BF16, DSAIDX_FORCE_BANK, DSAIDX_FP8_E4M3, DSAIDX_OK,  # noqa: F401
-                   DSAIDX_NO_BANK, DSAIDX_POOL_MEAN, LIB_PATH, last_error, lib)
+                   DSAIDX_NO_BANK, DSAIDX_POOL_MEAN, LIB_PATH, Layer, last_error, lib)
 
 __all__ = ["indexer_prefill", "indexer_decode", "indexer_group_bank", "indexer_group_bank_pairs",
+           "indexer_layers", "workspace_layers",
            "workspace_prefill", "workspace_decode", "workspace_group_bank", "indexer_mtp", "indexer_mtp_pairs",
            "workspace_mtp", "indexer_group_query", "union_sizes", "topk_overlap", "union_stat", "speedup_joint", "select_setting",
-           "layerwise_speedup", "FORCE_BANK", "POOL_MEAN", "NO_BANK", "lib",
+           "layerwise_speedup", "read_probe", "FORCE_BANK", "POOL_MEAN", "NO_BANK", "lib",
            "LIB_PATH"]
 
 FORCE_BANK = DSAIDX_FORCE_BANK
@@ -158,6 +161,67 @@ def indexer_group_bank(q, k, w, qbar, wbar, q_pos0, G, P, topk=2048, q_scale=Non
     return out_idx, out_score, out_bank
 
 
+def _layer_structs(layers):
+    arr = (Layer * len(layers))()
+    for i, L in enumerate(layers):
+        for name in ("q", "q_scale", "k", "k_scale", "w", "qbar", "qbar_scale", "wbar", "out_idx", "out_score",
+                     "out_bank"):
+            setattr(arr[i], name, _ptr(L.get(name)))
+        arr[i].Hs = L.get("Hs", 0)
+        arr[i].G = L.get("G", 0)
+        arr[i].P = L.get("P", 0)
+        arr[i].flags = L.get("flags", 0)
+    return arr
+
+
+def workspace_layers(layers, Tq, Tk, H, d, topk, dtype):
+    """Workspace bytes of indexer_layers (layers as in indexer_layers)."""
+    return lib().indexer_layers_workspace_size(_layer_structs(layers), len(layers), Tq, Tk, H, d, topk, dtype)
+
+
+def indexer_layers(layers, q_pos0=0, topk=2048, want_score=False, want_bank=False, ws=None):
+    """Layer-wise reuse (Section 4.1 Eq. (5); Appendix C.4): one call over
+    several layers of the same shapes, each with its own tensors and (G, P).
+
+    ``layers`` is a list of dicts with q, k, w (q_scale, k_scale for E4M3),
+    G and P (G = 0: the original indexer), and for G > 0 qbar, wbar (Hs from
+    qbar; qbar_scale for E4M3) or flags=POOL_MEAN, optional out_idx,
+    out_score, out_bank.  Outputs are allocated where missing (scores and
+    banks only when asked for).  Returns the list of (idx, score or None,
+    bank or None) per layer."""
+    if not layers:
+        return []
+    L0 = layers[0]
+    dev = _dev(*[L.get(n) for L in layers for n in ("q", "q_scale", "k", "k_scale", "w", "qbar", "qbar_scale",
+                                                  "wbar", "out_idx", "out_score", "out_bank")], ws)
+    Tq, H, d = L0["q"].shape
+    Tk = L0["k"].shape[0]
+    dt = _dtype(L0["q"])
+    full = []
+    for L in layers:
+        L = dict(L)
+        if L["q"].shape != L0["q"].shape or L["k"].shape != L0["k"].shape or _dtype(L["q"]) != dt:
+            raise ValueError("every layer of one call has the same q and k shapes and dtype")
+        G = L.get("G", 0)
+        if G and L.get("qbar") is not None:
+            L.setdefault("Hs", L["qbar"].shape[1])
+        elif G:
+            L.setdefault("Hs", H)
+        if L.get("out_idx") is None:
+            L["out_idx"] = torch.empty((Tq, topk), dtype=torch.int32, device=dev)
+        if want_score and L.get("out_score") is None:
+            L["out_score"] = torch.empty((Tq, topk), dtype=torch.float32, device=dev)
+        if G and want_bank and L.get("out_bank") is None:
+            L["out_bank"] = torch.empty((-(-Tq // G), L["P"]), dtype=torch.int32, device=dev)
+        full.append(L)
+    arr = _layer_structs(full)
+    ws = _ws(lib().indexer_layers_workspace_size(arr, len(full), Tq, Tk, H, d, topk, dt), dev, ws)
+    rc = lib().indexer_layers(arr, len(full), dt, Tq, Tk, H, d, q_pos0, topk, _ptr(ws),
+                              0 if ws is None else ws.numel(), _stream(dev))
+    _check(rc, "indexer_layers")
+    return [(L["out_idx"], L.get("out_score"), L.get("out_bank")) for L in full]
+
+
 def workspace_mtp(B, Nmax, m, H, Hs, d, G, P, topk, flags=0):
     return lib().indexer_mtp_workspace_size(B, Nmax, m, H, Hs, d, G, P, topk, flags)
 
@@ -260,6 +324,18 @@ def layerwise_speedup(settings, L, R=32, m=16, a=8):
     if r < 0:
         raise ValueError("indexer_layerwise_speedup: bad arguments")
     return r
+
+
+def read_probe(buf, nblocks=2048, out=None):
+    """Read every byte of the GPU tensor ``buf`` once (the plain read stream
+    the memory-bound kernels are measured against); returns the per-workgroup
+    XOR words (int32 [nblocks], GPU)."""
+    dev = _dev(buf, out)
+    if out is None:
+        out = torch.empty((nblocks,), dtype=torch.int32, device=dev)
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().indexer_read_probe(_ptr(buf), nbytes, _ptr(out), nblocks, _stream(dev)), "indexer_read_probe")
+    return out
 
 
 # ------------------------------------------------- group query (Eq. (6)-(7))

@@ -21,6 +21,15 @@ DSAIDX_NO_BANK = 8
 # exported symbol -> (restype, argtypes)
 _P, _I, _I64, _U, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint, ctypes.c_size_t
 _D = ctypes.c_double
+
+
+class Layer(ctypes.Structure):
+    """dsaidx_layer: one layer of indexer_layers (field order of the C struct)."""
+    _fields_ = [("q", _P), ("q_scale", _P), ("k", _P), ("k_scale", _P), ("w", _P), ("qbar", _P),
+                ("qbar_scale", _P), ("wbar", _P), ("Hs", _I), ("G", _I), ("P", _I), ("flags", _U),
+                ("out_idx", _P), ("out_score", _P), ("out_bank", _P)]
+
+
 SIGNATURES = {
     "indexer_prefill": (_I, [_P, _P, _P, _P, _P, _I, _I64, _I64, _I, _I, _I64, _I, _P, _P, _P, _SZ, _P]),
     "indexer_prefill_workspace_size": (_SZ, [_I64, _I64, _I, _I, _I, _I]),
@@ -30,6 +39,8 @@ SIGNATURES = {
                                 _I, _U, _P, _P, _P, _P, _SZ, _P]),
     "indexer_group_bank_workspace_size": (_SZ, [_I64, _I64, _I, _I, _I, _I, _I, _I, _I, _U]),
     "indexer_group_bank_pairs": (_I64, [_I64, _I64, _I, _I, _U]),
+    "indexer_layers": (_I, [_P, _I, _I, _I64, _I64, _I, _I, _I64, _I, _P, _SZ, _P]),
+    "indexer_layers_workspace_size": (_SZ, [_P, _I, _I64, _I64, _I, _I, _I, _I]),
     "indexer_mtp": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I64, _I, _I, _I, _I, _I, _I, _I, _U, _P, _P, _P, _P,
                          _SZ, _P]),
     "indexer_mtp_workspace_size": (_SZ, [_I, _I64, _I, _I, _I, _I, _I, _I, _I, _U]),
@@ -43,6 +54,7 @@ SIGNATURES = {
     "indexer_speedup_joint": (_D, [_D, _I, _I, _I, _I, _D]),
     "indexer_select_setting": (_I, [_P, _D, _I, _I, _D, _P, _P]),
     "indexer_layerwise_speedup": (_D, [_P, _P, _I, _D, _I, _I, _D]),
+    "indexer_read_probe": (_I, [_P, _I64, _P, _I, _P]),
     "indexer_last_error": (ctypes.c_char_p, []),
 }
 

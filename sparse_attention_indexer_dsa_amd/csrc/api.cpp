@@ -59,10 +59,13 @@ int cap_for(int K) { return (2 * K + 2048 + 63) / 64 * 64; }
 size_t cand_bytes_cap(int64_t rows, int cap) { return 2 * align_up((size_t)rows * (size_t)cap * 4u); }
 size_t cand_bytes(int64_t rows, int K) { return cand_bytes_cap(rows, cap_for(K)); }
 
-// Rows of at most this many candidates get a buffer that holds all of them:
-// the dense kernel then keeps every score and a histogram instead of
-// streaming the top K through compactions.  The bound keeps a row's count in
-// the 16-bit histogram counters (a multiple of 64 below 65536).
+// Group-bank rows whose candidates are bounded by the bank (refinement rows
+// of at most P + G - 1 candidates, fallback rows before the first bank group)
+// get a buffer that holds all of them: the dense kernel then keeps every
+// score and a histogram instead of streaming the top K through compactions.
+// The bound keeps a row's count in the 16-bit histogram counters (a multiple
+// of 64 below 65536).  Dense prefill rows never get more than cap_for(K)
+// entries, whatever their length.
 constexpr int64_t kFullRowMax = 65472;
 int full_cap(int K, int64_t ncand) {
   const int base = cap_for(K);
@@ -122,14 +125,21 @@ int check_ws(const void* ws, size_t ws_bytes, size_t need) {
   return DSAIDX_OK;
 }
 
-// Dense rows [r0, r1) of a prefill-shaped call, sliced into launches.
+// Dense rows [r0, r1) of a prefill-shaped call, sliced into launches of at
+// most kRowsPerLaunch rows.  Rows whose candidates all fit a buffer of `cap`
+// entries (position + 1 <= cap) get launches of their own, so the dense
+// kernel keeps their whole (short) rows; longer rows stream their top K
+// through the same buffers.
 hipError_t run_dense(const void* q, const float* q_scale, const void* k, const float* k_scale,
                      const float* w, int dtype, int H, int d, int64_t q_pos0, int64_t r0,
                      int64_t r1, int topk, int cap, int32_t* out_idx, float* out_score, void* ws,
                      hipStream_t stream) {
   const int rb = row_bytes(dtype, d);
-  for (int64_t s = r0; s < r1; s += kRowsPerLaunch) {
-    const int64_t n = r1 - s < kRowsPerLaunch ? r1 - s : kRowsPerLaunch;
+  int64_t split = (int64_t)cap - q_pos0;  // first row with more than cap candidates
+  split = split < r0 ? r0 : (split > r1 ? r1 : split);
+  for (int64_t s = r0; s < r1;) {
+    const int64_t end = s < split ? split : r1;
+    const int64_t n = end - s < kRowsPerLaunch ? end - s : kRowsPerLaunch;
     ScanArgs a{};
     a.q = (const uint8_t*)q + s * H * (int64_t)rb;
     a.q_scale = q_scale ? q_scale + s : nullptr;
@@ -151,6 +161,7 @@ hipError_t run_dense(const void* q, const float* q_scale, const void* k, const f
     a.out_stride = topk;
     hipError_t e = launch_scan_topk(a, dtype, stream);
     if (e != hipSuccess) return e;
+    s += n;
   }
   return hipSuccess;
 }
@@ -199,15 +210,21 @@ size_t group_ws_bytes(int64_t Tq, int H, int d, int G, int P, int topk, unsigned
 
 }  // namespace
 
+namespace dsaidx {
+// The calling thread's error message, for entry points defined in other files.
+int report_error(int code, const char* msg) { return fail(code, "%s", msg); }
+int report_hip_error(hipError_t e, const char* what) { return hip_fail(e, what); }
+}  // namespace dsaidx
+
 extern "C" {
 
 const char* indexer_last_error(void) { return g_last_error.c_str(); }
 
 size_t indexer_prefill_workspace_size(int64_t Tq, int64_t Tk, int H, int d, int topk, int dtype) {
-  (void)H; (void)d; (void)dtype;
+  (void)Tk; (void)H; (void)d; (void)dtype;
   if (Tq <= 0 || topk <= 0) return 0;
   const int64_t rows = Tq < kRowsPerLaunch ? Tq : kRowsPerLaunch;
-  return cand_bytes_cap(rows, full_cap(topk, Tk));
+  return cand_bytes(rows, topk);
 }
 
 int indexer_prefill(const void* q, const float* q_scale, const void* k, const float* k_scale,
@@ -221,7 +238,7 @@ int indexer_prefill(const void* q, const float* q_scale, const void* k, const fl
   if (rc) return rc;
   if (Tq == 0) return ok();
   hipError_t e = run_dense(q, q_scale, k, k_scale, w, dtype, H, d, q_pos0, 0, Tq, topk,
-                           full_cap(topk, Tk), out_idx, out_score, ws, (hipStream_t)stream);
+                           cap_for(topk), out_idx, out_score, ws, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "indexer_prefill launch");
   return ok();
 }
@@ -357,12 +374,16 @@ size_t indexer_group_bank_workspace_size(int64_t Tq, int64_t Tk, int H, int Hs, 
                         true);
 }
 
-int indexer_group_bank(const void* q, const float* q_scale, const void* k, const float* k_scale,
-                       const float* w, int dtype, int64_t Tq, int64_t Tk, int H, int d,
-                       int64_t q_pos0, const void* qbar, const float* qbar_scale,
-                       const float* wbar, int Hs, int G, int P, int topk, unsigned flags,
-                       int32_t* out_idx, int32_t* out_bank, float* out_score, void* ws,
-                       size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of a group-bank call (everything but the workspace).
+int check_group_bank(const void* q, const float* q_scale, const void* k, const float* k_scale,
+                     const float* w, int dtype, int64_t Tq, int64_t Tk, int H, int d,
+                     int64_t q_pos0, const void* qbar, const float* qbar_scale,
+                     const float* wbar, int Hs, int G, int P, int topk, unsigned flags,
+                     const int32_t* out_idx, const int32_t* out_bank, const float* out_score) {
   int rc = check_prefill_common(q, q_scale, k, k_scale, w, dtype, Tq, Tk, H, d, q_pos0, topk,
                                 out_idx, out_score);
   if (rc) return rc;
@@ -390,12 +411,16 @@ int indexer_group_bank(const void* q, const float* q_scale, const void* k, const
   if (!aligned16(qbar) || !aligned16(wbar) || !aligned16(out_bank))
     return fail(DSAIDX_ERR_INVALID_ARG, "qbar, wbar and out_bank must be 16-byte aligned");
   if ((uintptr_t)qbar_scale & 3u) return fail(DSAIDX_ERR_INVALID_ARG, "qbar_scale misaligned");
-  rc = check_ws(ws, ws_bytes,
-                group_ws_bytes(Tq, H, d, G, P, topk, flags, q_pos0, out_bank == nullptr));
-  if (rc) return rc;
-  if (Tq == 0) return ok();
+  return DSAIDX_OK;
+}
 
-  hipStream_t st = (hipStream_t)stream;
+// Enqueue a checked group-bank call (Tq > 0, workspace large enough).
+int run_group_bank(const void* q, const float* q_scale, const void* k, const float* k_scale,
+                   const float* w, int dtype, int64_t Tq, int H, int d, int64_t q_pos0,
+                   const void* qbar, const float* qbar_scale, const float* wbar, int Hs, int G,
+                   int P, int topk, unsigned flags, int32_t* out_idx, int32_t* out_bank,
+                   float* out_score, void* ws, hipStream_t st) {
+  const bool pool = (flags & DSAIDX_POOL_MEAN) != 0;
   const GroupPlan p = plan_groups(Tq, q_pos0, G, P, flags);
   const int64_t nelig = p.nfull - p.g0;
   const int rb = row_bytes(dtype, d);
@@ -506,6 +531,98 @@ int indexer_group_bank(const void* q, const float* q_scale, const void* k, const
     a.out_stride = topk;
     e = launch_scan_topk(a, dtype, st);
     if (e != hipSuccess) return hip_fail(e, "indexer_group_bank refine launch");
+  }
+  return DSAIDX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int indexer_group_bank(const void* q, const float* q_scale, const void* k, const float* k_scale,
+                       const float* w, int dtype, int64_t Tq, int64_t Tk, int H, int d,
+                       int64_t q_pos0, const void* qbar, const float* qbar_scale,
+                       const float* wbar, int Hs, int G, int P, int topk, unsigned flags,
+                       int32_t* out_idx, int32_t* out_bank, float* out_score, void* ws,
+                       size_t ws_bytes, void* stream) {
+  int rc = check_group_bank(q, q_scale, k, k_scale, w, dtype, Tq, Tk, H, d, q_pos0, qbar, qbar_scale,
+                            wbar, Hs, G, P, topk, flags, out_idx, out_bank, out_score);
+  if (rc) return rc;
+  rc = check_ws(ws, ws_bytes,
+                group_ws_bytes(Tq, H, d, G, P, topk, flags, q_pos0, out_bank == nullptr));
+  if (rc) return rc;
+  if (Tq == 0) return ok();
+  rc = run_group_bank(q, q_scale, k, k_scale, w, dtype, Tq, H, d, q_pos0, qbar, qbar_scale, wbar, Hs, G,
+                      P, topk, flags, out_idx, out_bank, out_score, ws, (hipStream_t)stream);
+  return rc ? rc : ok();
+}
+
+// ------------------------------------------------------ layer-wise dispatch
+
+size_t indexer_layers_workspace_size(const dsaidx_layer* layers, int nlayers, int64_t Tq, int64_t Tk,
+                                     int H, int d, int topk, int dtype) {
+  if (!layers || nlayers <= 0 || Tq <= 0 || topk <= 0 || H <= 0 || d <= 0) return 0;
+  size_t need = 0;
+  for (int i = 0; i < nlayers; ++i) {
+    const dsaidx_layer& L = layers[i];
+    size_t n;
+    if (L.G == 0) {
+      n = indexer_prefill_workspace_size(Tq, Tk, H, d, topk, dtype);
+    } else {
+      if (L.G < 0 || L.P <= 0) return 0;
+      // any q_pos0: as many banks as complete groups, kept in ws without out_bank
+      n = group_ws_bytes(Tq, H, d, L.G, L.P, topk, DSAIDX_FORCE_BANK | (L.flags & DSAIDX_POOL_MEAN), 0,
+                         L.out_bank == nullptr);
+    }
+    if (n > need) need = n;
+  }
+  return need;
+}
+
+int indexer_layers(const dsaidx_layer* layers, int nlayers, int dtype, int64_t Tq, int64_t Tk, int H,
+                   int d, int64_t q_pos0, int topk, void* ws, size_t ws_bytes, void* stream) {
+  if (nlayers < 0) return fail(DSAIDX_ERR_INVALID_ARG, "nlayers = %d is negative", nlayers);
+  if (nlayers > 0 && !layers) return fail(DSAIDX_ERR_INVALID_ARG, "null layers");
+  // every layer is checked before anything is enqueued
+  size_t need = 0;
+  for (int i = 0; i < nlayers; ++i) {
+    const dsaidx_layer& L = layers[i];
+    int rc;
+    size_t n;
+    if (L.G == 0) {
+      if (L.qbar || L.qbar_scale || L.wbar || L.out_bank || L.flags)
+        return fail(DSAIDX_ERR_INVALID_ARG, "layer %d: an original-indexer layer (G = 0) takes no group "
+                    "query, bank or flags", i);
+      rc = check_prefill_common(L.q, L.q_scale, L.k, L.k_scale, L.w, dtype, Tq, Tk, H, d, q_pos0, topk,
+                                L.out_idx, L.out_score);
+      n = indexer_prefill_workspace_size(Tq, Tk, H, d, topk, dtype);
+    } else {
+      rc = check_group_bank(L.q, L.q_scale, L.k, L.k_scale, L.w, dtype, Tq, Tk, H, d, q_pos0, L.qbar,
+                            L.qbar_scale, L.wbar, L.Hs, L.G, L.P, topk, L.flags, L.out_idx, L.out_bank,
+                            L.out_score);
+      n = rc ? 0 : group_ws_bytes(Tq, H, d, L.G, L.P, topk, L.flags, q_pos0, L.out_bank == nullptr);
+    }
+    if (rc) {
+      const std::string msg = g_last_error;
+      return fail(rc, "layer %d: %s", i, msg.c_str());
+    }
+    if (n > need) need = n;
+  }
+  int rc = check_ws(ws, ws_bytes, need);
+  if (rc) return rc;
+  if (Tq == 0) return ok();
+  hipStream_t st = (hipStream_t)stream;
+  for (int i = 0; i < nlayers; ++i) {
+    const dsaidx_layer& L = layers[i];
+    if (L.G == 0) {
+      hipError_t e = run_dense(L.q, L.q_scale, L.k, L.k_scale, L.w, dtype, H, d, q_pos0, 0, Tq, topk,
+                               cap_for(topk), L.out_idx, L.out_score, ws, st);
+      if (e != hipSuccess) return hip_fail(e, "indexer_layers launch");
+    } else {
+      rc = run_group_bank(L.q, L.q_scale, L.k, L.k_scale, L.w, dtype, Tq, H, d, q_pos0, L.qbar, L.qbar_scale,
+                          L.wbar, L.Hs, L.G, L.P, topk, L.flags, L.out_idx, L.out_bank, L.out_score, ws, st);
+      if (rc) return rc;
+    }
   }
   return ok();
 }
@@ -822,6 +939,17 @@ int indexer_topk_overlap(const int32_t* a, const int32_t* b, int64_t n, int K, i
   if (K % 4) return fail(DSAIDX_ERR_UNSUPPORTED, "K = %d is not a multiple of 4", K);
   const hipError_t e = launch_topk_overlap(a, b, n, K, out_count, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "indexer_topk_overlap launch");
+  return ok();
+}
+
+int indexer_read_probe(const void* p, int64_t bytes, uint32_t* out, int nblocks, void* stream) {
+  if (bytes < 0 || nblocks < 1 || nblocks > 65535)
+    return fail(DSAIDX_ERR_INVALID_ARG, "bad size (bytes=%lld nblocks=%d)", (long long)bytes, nblocks);
+  if (!out || (bytes > 0 && !p)) return fail(DSAIDX_ERR_INVALID_ARG, "null p or out");
+  if (!aligned16(p) || ((uintptr_t)out & 3u))
+    return fail(DSAIDX_ERR_INVALID_ARG, "p must be 16-byte aligned, out 4-byte");
+  const hipError_t e = launch_read_probe(p, bytes, out, nblocks, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "indexer_read_probe launch");
   return ok();
 }
 

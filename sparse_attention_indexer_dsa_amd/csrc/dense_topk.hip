@@ -19,11 +19,15 @@
 //   * ReLU through the identity w*ReLU(s) = (w/2)*|s| + (w/2)*s: the first
 //     term is one FMA with an |.| source modifier per (head, key), the second
 //     summed over heads is (sum_j (w_j/2) q_j) . k, a single dot product per
-//     (query, key) that the workgroup computes with bf16 16x16x32 MFMAs.  Its
-//     query vector is split into a bf16 high and low part (16 significant
-//     bits; every E4M3 and bf16 key element is exact in bf16), so it keeps
-//     integer-valued inputs exact and otherwise errs by about 2^-17 relative
-//     to the score's magnitude.
+//     (query, key) that the workgroup computes with 16x16x32 MFMAs.  Its
+//     query vector q~ is split into parts that the MFMA takes exactly:
+//     bf16 keys use three bf16 parts (24 significant bits); E4M3 keys use an
+//     fp16 high and low part (22 bits) of q~ times a power of two that puts
+//     its largest element just below 2^15, undone after the product (every
+//     E4M3 value is exact in fp16, every bf16 value in bf16).  The linear
+//     term then carries about fp32's own rounding (integer-valued inputs stay
+//     exact), which keeps scores near zero, where the two terms cancel,
+//     within the tolerance.
 //   * Streaming top-K exactly as the general kernel: scores that beat the
 //     running threshold are staged in LDS, flushed to the query's candidate
 //     buffer, and compacted by a wave radix select when it fills (two 11-bit
@@ -150,7 +154,11 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   __shared__ float s_ks[kStages][kTile];
   __shared__ __attribute__((aligned(16))) uint32_t s_hist[kWaves][kSelectHistWords];
   __shared__ float s_lin[kStages][2][kWaves][kTile];  // [tile's stage][d half][query][key]
-  __shared__ __attribute__((aligned(16))) uint16_t s_qt[kWaves][2][kD];  // bf16 hi / lo of q-tilde
+  // parts of q-tilde: bf16 hi / mid / lo (bf16 keys) or scaled fp16 hi / lo
+  // (E4M3 keys), and the factor that undoes the fp16 parts' scale
+  constexpr int kParts = DT == kBF16 ? 3 : 2;
+  __shared__ __attribute__((aligned(16))) uint16_t s_qt[kWaves][kParts][kD];
+  __shared__ float s_qinv[kWaves];
   __shared__ int s_need[2];  // s_need[i & 1] == i: a wave asked for compaction in step i
   // gathering: the bank positions of tiles t .. t+7, slot t & 7 (tile t+7's
   // are requested in step t, read by tile t+4's request and tile t's append)
@@ -255,23 +263,54 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
         }
       }
     }
-    const uint16_t h0 = bf16_rne(t0), h1 = bf16_rne(t1);
-    s_qt[wave][0][2 * l] = h0;
-    s_qt[wave][0][2 * l + 1] = h1;
-    s_qt[wave][1][2 * l] = bf16_rne(t0 - __uint_as_float((uint32_t)h0 << 16));
-    s_qt[wave][1][2 * l + 1] = bf16_rne(t1 - __uint_as_float((uint32_t)h1 << 16));
+    if constexpr (DT == kBF16) {
+      // three bf16 parts; each remainder is exact in fp32
+      float r0 = t0, r1 = t1;
+#pragma unroll
+      for (int pt = 0; pt < 3; ++pt) {
+        const uint16_t b0 = bf16_rne(r0), b1 = bf16_rne(r1);
+        s_qt[wave][pt][2 * l] = b0;
+        s_qt[wave][pt][2 * l + 1] = b1;
+        r0 -= __uint_as_float((uint32_t)b0 << 16);
+        r1 -= __uint_as_float((uint32_t)b1 << 16);
+      }
+    } else {
+      // fp16 hi + lo of q-tilde * 2^e, with the query's largest |element|
+      // scaled into [2^14, 2^15) (e = 0 for an all-zero q-tilde)
+      float mx = fmaxf(__builtin_fabsf(t0), __builtin_fabsf(t1));
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+      int e = 0;
+      if (mx > 0.0f) e = min(15 - __builtin_amdgcn_frexp_expf(mx), 120);
+      const float y0 = __builtin_ldexpf(t0, e), y1 = __builtin_ldexpf(t1, e);
+      const _Float16 a0 = (_Float16)y0, a1 = (_Float16)y1;
+      const _Float16 b0 = (_Float16)(y0 - (float)a0), b1 = (_Float16)(y1 - (float)a1);
+      s_qt[wave][0][2 * l] = __builtin_bit_cast(uint16_t, a0);
+      s_qt[wave][0][2 * l + 1] = __builtin_bit_cast(uint16_t, a1);
+      s_qt[wave][1][2 * l] = __builtin_bit_cast(uint16_t, b0);
+      s_qt[wave][1][2 * l + 1] = __builtin_bit_cast(uint16_t, b1);
+      if (l == 0) s_qinv[wave] = __builtin_ldexpf(1.0f, -e);
+    }
   }
 
   // ---- the linear-term MFMA of this wave: keys 16*nb .. +15 of a tile, the
-  // d half kh (k-steps 2kh, 2kh+1 of 32), all 8 queries x {hi, lo} on M
+  // d half kh (k-steps 2kh, 2kh+1 of 32), all 8 queries on M: row m is part
+  // m & 1 (hi, mid / lo) of query m >> 1.  bf16 adds a second MFMA into the
+  // same accumulator whose even rows hold the queries' third parts and whose
+  // odd rows are zero, so every query's parts still end in rows 2q, 2q+1.
   const int nb = wave & 3, kh = wave >> 2;
-  v8bf la[2];
   __syncthreads();
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+  // A fragment of part row m for k-step s (part 2: even rows only)
+  auto qt_frag = [&](int part, int s) __attribute__((always_inline)) -> u32x4 {
     const int m = l & 15;
-    la[s] = __builtin_bit_cast(v8bf, *(const u32x4*)&s_qt[m >> 1][m & 1][32 * (2 * kh + s) + 8 * (l >> 4)]);
-  }
+    const u32x4 v = *(const u32x4*)&s_qt[m >> 1][part == 2 ? 2 : (m & 1)][32 * (2 * kh + s) + 8 * (l >> 4)];
+    return (part == 2 && (m & 1)) ? u32x4{0u, 0u, 0u, 0u} : v;
+  };
+  u32x4 la[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) la[s] = qt_frag(0, s);
+  const float qinv = DT == kFP8 ? s_qinv[wave] : 1.0f;
 
   uint32_t* ckey = args.cand_key + (int64_t)jq * args.cap;  // raw fp32 scores
   int32_t* cidx = args.cand_idx + (int64_t)jq * args.cap;
@@ -427,19 +466,23 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int ks = 2 * kh + s;  // d elements 32ks + 8(l>>4) .. +7
-      v8bf kb;
       if constexpr (DT == kBF16) {
-        kb = __builtin_bit_cast(v8bf, *(const u32x4*)(row + 16 * ((4 * ks + (l >> 4)) ^ x)));
+        const v8bf kb = __builtin_bit_cast(v8bf, *(const u32x4*)(row + 16 * ((4 * ks + (l >> 4)) ^ x)));
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, la[s]), kb, c, 0, 0, 0);
+        // the third parts, read from LDS here rather than held in registers
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, qt_frag(2, s)), kb, c, 0, 0, 0);
       } else {
         const int d0 = 32 * ks + 8 * (l >> 4);
         const uint2 v = *(const uint2*)(row + 16 * ((d0 >> 4) ^ x) + (d0 & 15));
-        const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, false);
-        const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, true);
-        const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, false);
-        const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, true);
-        kb = v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.x, 1.0f, false);
+        const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.x, 1.0f, true);
+        const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.y, 1.0f, false);
+        const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.y, 1.0f, true);
+        const v8h kb = __builtin_bit_cast(
+            v8h, u32x4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                       __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)});
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, la[s]), kb, c, 0, 0, 0);
       }
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(la[s], kb, c, 0, 0, 0);
     }
     // rows 4(l>>4)+i = (query 2(l>>4) + i/2, part i%2)
     const int q0 = 2 * (l >> 4);
@@ -451,13 +494,16 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   // of sub-tiles 0 and 1; swapping the upper half of p0 with the lower half of
   // p1 leaves both halves of key l's sum in lane l, in the same order on both
   // lane halves (lower-half heads first).  Then the linear term and the fp8
-  // key scale: (sum over heads of (w/2)|s| + linear term) * scale.
+  // key scale: (sum over heads of (w/2)|s| + linear term) * scale.  Adding +0
+  // last turns a -0 (a negative sum times a zero scale, or a sum of -0 terms)
+  // into +0, which is how the ranking treats it.
   auto tile_score = [&](float p0, float p1, int st) __attribute__((always_inline)) -> float {
     auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
-    float sc = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) +
-               (s_lin[st][0][wave][l] + s_lin[st][1][wave][l]);
+    // E4M3: the linear term comes scaled by 2^e; qinv = 2^-e undoes it
+    float sc = fmaf(s_lin[st][0][wave][l] + s_lin[st][1][wave][l], qinv,
+                    __uint_as_float(sw[0]) + __uint_as_float(sw[1]));
     if constexpr (DT == kFP8) sc *= s_ks[st][l];
-    return sc;
+    return sc + 0.0f;
   };
   // append the step's scores that beat the threshold: lane l holds candidate
   // tbase + l, so lane order is candidate order and one ballot serves 64

@@ -21,9 +21,10 @@ constexpr int kBufferWord3 = 0x00020000;
 
 enum { kBF16 = 1, kFP8 = 2 };
 
-// fp32 -> uint32 such that a > b (as reals, -0 == +0 after canonicalisation)
-// iff key(a) > key(b).  Key 0 is below every finite score, so it serves as the
-// "accept everything" threshold.
+// fp32 -> uint32 such that a > b iff key(a) > key(b), for finite a, b other
+// than -0: key(-0) is one below key(+0), so every kernel turns a -0 score
+// into +0 (by adding +0) before it takes its key.  Key 0 is below every finite
+// score, so it serves as the "accept everything" threshold.
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);

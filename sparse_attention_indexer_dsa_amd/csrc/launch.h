@@ -160,6 +160,15 @@ hipError_t launch_union_sizes(const int32_t* idx, int64_t groups, int K, int G, 
 hipError_t launch_topk_overlap(const int32_t* a, const int32_t* b, int64_t n, int K, int32_t* out,
                                hipStream_t stream);
 
+// Read `bytes` bytes at p once (coalesced 16-byte loads); out [nblocks] gets
+// one XOR word per workgroup.
+hipError_t launch_read_probe(const void* p, int64_t bytes, uint32_t* out, int nblocks, hipStream_t stream);
+
+// Set the calling thread's last-error message (indexer_last_error) and return
+// `code`; for entry points outside api.cpp.
+int report_error(int code, const char* msg);
+int report_hip_error(hipError_t e, const char* what);
+
 // Fill n int32 values with v (a kernel, not a memset node).
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t stream);
 

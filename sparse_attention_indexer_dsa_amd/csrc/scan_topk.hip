@@ -253,14 +253,14 @@ __global__ void __launch_bounds__(WPB * 64, 2) scan_topk_kernel(const ScanArgs a
   };
   // the full score of sub-tile u's key in this lane's column; the other
   // 16*MT heads of that key live in lane l ^ 32, so after the swap both lane
-  // halves hold the sum.  The partial sums start at +0 and every ReLU term is
-  // >= +0, so no score is -0.
+  // halves hold the sum.  A negative sum times a zero key scale is -0, which
+  // the ranking treats as +0: adding +0 turns it into +0.
   auto sub_score = [&](float part, int buf, int u) __attribute__((always_inline)) -> float {
     auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false,
                                                false);
     float sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     if constexpr (DT == kFP8) sc *= s_kscale[buf][32 * u + col];
-    return sc;
+    return sc + 0.0f;
   };
   // append the step's scores that beat the threshold: lane l holds candidate
   // tbase + l (sub-tile 0 in the low lane half, sub-tile 1 in the high half),

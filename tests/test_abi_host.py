@@ -35,7 +35,7 @@ A = P(1 << 20)  # 16-byte aligned
 def test_header_symbols_exported(L):
     names = re.findall(r"^\s*(?:[\w\s\*]+?)\b(indexer_\w+)\s*\(", open(HEADER).read(), re.M)
     names = sorted(set(names))
-    assert len(names) == 19, names
+    assert len(names) == 22, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -197,3 +197,60 @@ def test_calibration_host_functions_match_oracle(L):
     sizes = rng.integers(0, 30000, size=101)
     for st in ("max", "mean", "p90"):
         assert dsa.union_stat(sizes, st) == calib.union_stat(sizes, st)
+
+
+# ------------------------------------------------------- layer-wise dispatch
+
+def _layers(**per_layer):
+    from sparse_attention_indexer_dsa_amd._lib import Layer
+    specs = per_layer.get("specs")
+    arr = (Layer * len(specs))()
+    for i, sp in enumerate(specs):
+        arr[i].q, arr[i].k, arr[i].w, arr[i].out_idx = 1 << 20, 1 << 20, 1 << 20, 1 << 20
+        for name, v in sp.items():
+            setattr(arr[i], name, v)
+    return arr
+
+
+def _call_layers(L, arr, n=None, Tq=64, Tk=64, ws_bytes=1 << 40, topk=8):
+    return L.indexer_layers(arr, len(arr) if n is None else n, BF16, Tq, Tk, 64, 128, 0, topk, A, ws_bytes, None)
+
+
+def test_layers_validate_every_layer_first(L):
+    """indexer_layers checks every layer before it enqueues anything, and an
+    error names the layer: a bad setting in the last layer fails the call."""
+    good_bank = dict(qbar=1 << 20, wbar=1 << 20, Hs=64, G=16, P=16)
+    assert _call_layers(L, _layers(specs=[dict(), good_bank]), Tq=0) == OK
+    arr = _layers(specs=[dict(), good_bank, dict(good_bank, G=5)])
+    assert _call_layers(L, arr) == UNSUPPORTED
+    assert "layer 2" in L.indexer_last_error().decode()
+    arr = _layers(specs=[dict(qbar=1 << 20)])  # an original-indexer layer takes no group query
+    assert _call_layers(L, arr) == INVALID and "layer 0" in L.indexer_last_error().decode()
+    arr = _layers(specs=[dict(), dict(good_bank, P=4)])  # P below topk
+    assert _call_layers(L, arr) == INVALID and "layer 1" in L.indexer_last_error().decode()
+    assert L.indexer_layers(None, 2, BF16, 64, 64, 64, 128, 0, 8, A, 1 << 40, None) == INVALID
+    assert _call_layers(L, _layers(specs=[dict()]), n=-1) == INVALID
+
+
+def test_layers_workspace_is_the_largest_layers(L):
+    """The layer call's workspace is the largest need of its layers: the
+    original indexer's and each (G, P)'s group-bank workspace."""
+    Tq = Tk = 20000
+    specs = [dict(), dict(qbar=1 << 20, wbar=1 << 20, Hs=64, G=16, P=8192),
+             dict(qbar=1 << 20, wbar=1 << 20, Hs=64, G=8, P=16384)]
+    arr = _layers(specs=specs)
+    need = L.indexer_layers_workspace_size(arr, 3, Tq, Tk, 64, 128, 2048, BF16)
+    want = max(L.indexer_prefill_workspace_size(Tq, Tk, 64, 128, 2048, BF16),
+               L.indexer_group_bank_workspace_size(Tq, Tk, 64, 64, 128, 16, 8192, 2048, BF16, 0),
+               L.indexer_group_bank_workspace_size(Tq, Tk, 64, 64, 128, 8, 16384, 2048, BF16, 0))
+    assert need == want > 0
+    assert _call_layers(L, arr, Tq=Tq, Tk=Tk, ws_bytes=1000, topk=2048) == WORKSPACE
+    assert "workspace" in L.indexer_last_error().decode()
+    assert L.indexer_layers_workspace_size(arr, 0, Tq, Tk, 64, 128, 2048, BF16) == 0
+
+
+def test_read_probe_rejects(L):
+    assert L.indexer_read_probe(A, 1 << 20, A, 0, None) == INVALID
+    assert L.indexer_read_probe(P((1 << 20) + 4), 64, A, 8, None) == INVALID
+    assert L.indexer_read_probe(A, -1, A, 8, None) == INVALID
+    assert L.indexer_read_probe(A, 64, None, 8, None) == INVALID

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import oracle
-from tests.parity import compare
+from tests.parity import compare, pair_refs
 from workloads import make_decode, make_group_bank, make_mtp, make_prefill
 
 pytestmark = pytest.mark.gpu
@@ -62,10 +62,9 @@ def _prefill_check(dsa, wl, rows=None, exact=None, topk=None, chunk=None):
                             wl.tensors.get("k_scale"), rows=rows)
     exact = (p["dist"] == "int") if exact is None else exact
 
-    def score_of(r, keys):
-        return oracle.score_pairs(wl["q"], wl["k"], wl["w"], np.full(len(keys), rows[r]), keys, dt, dt,
-                                  wl.tensors.get("q_scale"), wl.tensors.get("k_scale"))
-    compare(_np(gi)[rows], _np(gs)[rows], ri, rs, exact, score_of)
+    score_of, cond_of = pair_refs(wl["q"], wl["k"], wl["w"], rows, dt, dt, wl.tensors.get("q_scale"),
+                                  wl.tensors.get("k_scale"))
+    compare(_np(gi)[rows], _np(gs)[rows], ri, rs, exact, score_of, ref_cond_of=cond_of)
     return gi, gs
 
 
@@ -109,6 +108,41 @@ def test_zero_and_negative_weights(dsa):
     assert (_np(gi)[399] == np.arange(64)).all()
     wl2 = make_prefill(T=400, H=8, d=32, topk=64, dtype="bf16", dist="int", seed=6, w_lo=-3, w_hi=0)
     _prefill_check(dsa, wl2)
+
+
+@pytest.mark.parametrize("H,d", [(64, 128), (16, 64)])
+def test_zero_key_scales_signed_gates(dsa, H, d):
+    """Integer E4M3 inputs where every fifth key token has scale 0 and the
+    gates have both signs: a negative head sum times a zero scale is -0, which
+    must rank as +0 (ties then go to the lower index), in the dense kernel
+    (64 heads, d = 128) and the general one; decode sees the same cache."""
+    T, K = 700, 96
+    wl = make_prefill(T=T, H=H, d=d, topk=K, dtype="fp8", dist="int", seed=20 + H)
+    ks = wl["k_scale"].clone()
+    ks[::5] = 0.0
+    wl.tensors["k_scale"] = ks
+    _prefill_check(dsa, wl, rows=_rows(T, 40, 20 + H))
+    B, N = 3, 900
+    wd = make_decode(B, N, H, d, K, dist="int", seed=30 + H, seq_lens=[900, 333, 4])
+    kd = wd["k_scale"].clone()
+    kd[:, ::5] = 0.0
+    wd.tensors["k_scale"] = kd
+    _decode_check(dsa, wd)
+
+
+@pytest.mark.parametrize("H,d,dtype", [(64, 128, "bf16"), (64, 128, "fp8"), (24, 64, "bf16")])
+def test_all_negative_gates_random(dsa, H, d, dtype):
+    """Normal inputs with every gate negative, w = -|N(0,1)|/8: every score is
+    at most 0 and the top K are the keys whose heads are least positive.  This
+    is where the dense kernel's (w/2)|s| + (w/2)s split of the ReLU sum
+    cancels most; the tolerance rule must still hold."""
+    T, Tq, K = 3000, 400, 256
+    wl = make_prefill(T=T, H=H, d=d, topk=K, dtype=dtype, dist="normal", seed=40 + H, Tq=Tq)
+    g = torch.Generator().manual_seed(41 + H)
+    wl.tensors["w"] = -(torch.randn((Tq, H), generator=g).abs() / 8)
+    gi, gs = _prefill_check(dsa, wl, rows=_rows(Tq, 40, 40 + H))
+    v = _np(gs)[_np(gi) >= 0]
+    assert (v <= 0).all()
 
 
 def test_compaction_many_rounds(dsa):
@@ -190,8 +224,8 @@ def test_dense_kernel_compaction(dsa):
 @pytest.mark.parametrize("H,d,dtype,K", [(64, 128, "fp8", 16), (48, 128, "bf16", 40), (8, 32, "bf16", 8),
                                          (16, 64, "fp8", 24)])
 def test_compaction_buckets(dsa, H, d, dtype, K):
-    """Normal scores, small K over 70000 keys (more than a full-row buffer
-    holds, so the top K streams): most compactions stop after two radix
+    """Normal scores, small K over 70000 keys (far more than a candidate
+    buffer holds, so the top K streams): most compactions stop after two radix
     digits and keep the K-th best's whole 22-bit key bucket; the final
     selection must still be the exact top K (dense and general kernels)."""
     wl = make_prefill(T=70000, H=H, d=d, topk=K, dtype=dtype, dist="normal", seed=70 + H + K, Tq=192)
@@ -200,10 +234,11 @@ def test_compaction_buckets(dsa, H, d, dtype, K):
 
 @pytest.mark.parametrize("dtype,dist", [("fp8", "int"), ("bf16", "int"), ("fp8", "normal")])
 def test_dense_kernel_streaming_and_full_rows(dsa, dtype, dist):
-    """Both top-K modes of the dense kernel: a 70000-key call streams its rows
-    through compacting buffers of 2K + 2048 candidates; 6000- and 40000-key
-    calls keep every score of a row and select once at the end; all match
-    the oracle."""
+    """Both top-K modes of the dense kernel: rows of at most 2K + 2048 keys
+    (the first 2304 rows of the 6000-key call) keep every score of the row and
+    select once at the end; longer rows (the rest of that call, the 40000- and
+    70000-key calls) stream their top K through compacting buffers of that
+    size; all match the oracle."""
     wl = make_prefill(T=70000, H=64, d=128, topk=100, dtype=dtype, dist=dist, seed=90, Tq=192)
     _prefill_check(dsa, wl, rows=_rows(192, 24, 90))
     short = make_prefill(T=6000, H=64, d=128, topk=100, dtype=dtype, dist=dist, seed=91)
@@ -259,11 +294,9 @@ def _decode_check(dsa, wl, rows=None, exact=None):
     kc = wl["k_cache"].reshape(B * N, -1)
     ks = wl["k_scale"].reshape(B * N)
 
-    def score_of(r, keys):
-        b = rows[r]
-        return oracle.score_pairs(wl["q"], kc, wl["w"], np.full(len(keys), b), b * N + keys, "bf16", "fp8",
-                                  None, ks)
-    compare(_np(gi)[rows], _np(gs)[rows], ri, rs, exact, score_of)
+    score_of, cond_of = pair_refs(wl["q"], kc, wl["w"], rows, "bf16", "fp8", None, ks,
+                                  key_of=lambda r, keys: rows[r] * N + keys)
+    compare(_np(gi)[rows], _np(gs)[rows], ri, rs, exact, score_of, ref_cond_of=cond_of)
     return gi, gs
 
 
@@ -340,9 +373,8 @@ def _group_check(dsa, wl, flags=0, rows=None, exact=None):
         groups = np.unique(rows // G)  # the oracle computes the banks of the requested rows' groups
         assert np.array_equal(_np(gb)[groups], rb[groups])
 
-    def score_of(r, keys):
-        return oracle.score_pairs(wl["q"], wl["k"], wl["w"], np.full(len(keys), rows[r]), keys, wl.dtype,
-                                  wl.dtype, wl.tensors.get("q_scale"), wl.tensors.get("k_scale"))
+    score_of, cond_of = pair_refs(wl["q"], wl["k"], wl["w"], rows, wl.dtype, wl.dtype, wl.tensors.get("q_scale"),
+                                  wl.tensors.get("k_scale"))
     if exact:
         compare(_np(gi)[rows], _np(gs)[rows], ri, rs, True)
     else:
@@ -364,15 +396,14 @@ def _group_check(dsa, wl, flags=0, rows=None, exact=None):
                                                         wl.dtype, wl.dtype, wl.tensors.get("qbar_scale"),
                                                         wl.tensors.get("k_scale"))
 
-        def bank_score_of(n, keys):
-            return oracle.score_pairs(qbar, wl["k"], wbar, np.full(len(keys), groups[n]), keys,
-                                      wl.dtype, wl.dtype, wl.tensors.get("qbar_scale"), wl.tensors.get("k_scale"))
-        compare(gbank, None, rb[groups], bscore, False, bank_score_of, label="bank")
+        bank_score_of, bank_cond_of = pair_refs(qbar, wl["k"], wbar, groups, wl.dtype, wl.dtype,
+                                                wl.tensors.get("qbar_scale"), wl.tensors.get("k_scale"))
+        compare(gbank, None, rb[groups], bscore, False, bank_score_of, label="bank", ref_cond_of=bank_cond_of)
         same_bank = np.array([np.array_equal(_np(gb)[r // G], rb[r // G]) for r in rows])
         assert same_bank.mean() > 0.5
         sel = np.nonzero(same_bank)[0]
         compare(_np(gi)[rows][sel], _np(gs)[rows][sel], ri[sel], rs[sel], False,
-                lambda r, keys: score_of(sel[r], keys))
+                lambda r, keys: score_of(sel[r], keys), ref_cond_of=lambda r, keys: cond_of(sel[r], keys))
     return gi, gs, gb
 
 
@@ -481,20 +512,18 @@ def _mtp_check(dsa, wl, flags=0, rows=None, exact=None, lens_dev=None):
                 continue
             grp = b * NGs + g
 
-            def bank_score(r, keys, grp=grp, b=b):
-                return oracle.score_pairs(qbf, kc, wbf, np.full(len(keys), grp), b * N + keys, "bf16", "fp8",
-                                          None, ks)
+            bank_score, bank_cond = pair_refs(qbf, kc, wbf, [grp], "bf16", "fp8", None, ks,
+                                              key_of=lambda r, keys, b=b: b * N + keys)
             compare(gb[b, g][None], None, rb[b, g][None], bank_score(0, v)[None], False, bank_score,
-                    label=f"bank {b},{g}")
+                    label=f"bank {b},{g}", ref_cond_of=bank_cond)
 
-    def score_of(r, keys):
-        row = rows[r]
-        b = row // m
-        return oracle.score_pairs(qf, kc, wf, np.full(len(keys), row), b * N + keys, "bf16", "fp8", None, ks)
+    score_of, cond_of = pair_refs(qf, kc, wf, rows, "bf16", "fp8", None, ks,
+                                  key_of=lambda r, keys: (rows[r] // m) * N + keys)
     same = np.array([np.array_equal(gb[r // m, (r % m) // G], rb[r // m, (r % m) // G]) for r in rows])
     assert same.mean() > 0.5
     sel = np.nonzero(same)[0]
-    compare(gi[rows][sel], gs[rows][sel], ri[sel], rs[sel], False, lambda r, keys: score_of(sel[r], keys))
+    compare(gi[rows][sel], gs[rows][sel], ri[sel], rs[sel], False, lambda r, keys: score_of(sel[r], keys),
+            ref_cond_of=lambda r, keys: cond_of(sel[r], keys))
     return gi, gs, gb
 
 
