@@ -108,6 +108,24 @@ int indexer_decode(const void *q, const uint8_t *k_cache, const float *k_scale, 
 size_t indexer_decode_workspace_size(int B, int64_t Nmax, int H, int d, int topk);
 
 /*
+ * indexer_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops, harnesses that forbid hipMalloc): the same
+ * arguments and kernels, with the workspace taken from a fixed device array
+ * inside the library instead of `ws`.  Each GPU the library runs on holds its
+ * own array of indexer_decode_noalloc_max_bytes() bytes (96 MiB: enough for
+ * 32 sequences of 262144 keys) from the library's load until the process
+ * ends.  Sizes whose workspace would exceed it are refused on the host
+ * (DSAIDX_ERR_UNSUPPORTED).  The call allocates nothing; it clears what must
+ * start at zero on `stream` itself.  Calls that overlap on one GPU share the
+ * array and race: issue them on one stream, or wait between them.  `stream`
+ * must belong to the current device.
+ */
+int indexer_decode_noalloc(const void *q, const uint8_t *k_cache, const float *k_scale, const float *w,
+                           const int32_t *seq_lens, int B, int64_t Nmax, int H, int d, int topk,
+                           int32_t *out_idx, float *out_score, void *stream);
+size_t indexer_decode_noalloc_max_bytes(void);
+
+/*
  * ADIndex group token bank, Section 4.3 Eq. (13)-(14) with the group score of
  * Eq. (8).  Queries are as in indexer_prefill; the call's queries form
  * consecutive groups of G starting at query 0 (q_pos0 must be a multiple of

@@ -24,7 +24,7 @@ import torch
 from ._lib import (DSAIDX_BF16, DSAIDX_FORCE_BANK, DSAIDX_FP8_E4M3, DSAIDX_OK,  # noqa: F401
                    DSAIDX_NO_BANK, DSAIDX_POOL_MEAN, LIB_PATH, Layer, last_error, lib)
 
-__all__ = ["indexer_prefill", "indexer_decode", "indexer_group_bank", "indexer_group_bank_pairs",
+__all__ = ["indexer_prefill", "indexer_decode", "indexer_decode_noalloc", "indexer_group_bank", "indexer_group_bank_pairs",
            "indexer_layers", "workspace_layers",
            "workspace_prefill", "workspace_decode", "workspace_group_bank", "indexer_mtp", "indexer_mtp_pairs",
            "workspace_mtp", "indexer_group_query", "union_sizes", "topk_overlap", "union_stat", "speedup_joint", "select_setting",
@@ -130,6 +130,21 @@ def indexer_decode(q, k_cache, k_scale, w, seq_lens, topk=2048, want_score=True,
                               topk, _ptr(out_idx), _ptr(out_score), _ptr(ws), 0 if ws is None else ws.numel(),
                               _stream(dev))
     _check(rc, "indexer_decode")
+    return out_idx, out_score
+
+
+def indexer_decode_noalloc(q, k_cache, k_scale, w, seq_lens, topk, out_idx, out_score=None):
+    """indexer_decode without a workspace: the library's fixed device scratch
+    array serves instead (for callers that cannot allocate, e.g. under graph
+    capture).  The outputs are caller tensors; nothing is allocated here."""
+    dev = _dev(q, k_cache, k_scale, w, seq_lens, out_idx, out_score)
+    B, H, d = q.shape
+    Nmax = k_cache.shape[1]
+    if q.dtype != torch.bfloat16 or k_cache.dtype != torch.uint8 or seq_lens.dtype != torch.int32:
+        raise ValueError("decode takes bf16 q, uint8 E4M3 k_cache and int32 seq_lens")
+    rc = lib().indexer_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(k_scale), _ptr(w), _ptr(seq_lens), B, Nmax, H,
+                                      d, topk, _ptr(out_idx), _ptr(out_score), _stream(dev))
+    _check(rc, "indexer_decode_noalloc")
     return out_idx, out_score
 
 

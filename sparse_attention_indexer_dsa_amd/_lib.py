@@ -35,6 +35,8 @@ SIGNATURES = {
     "indexer_prefill_workspace_size": (_SZ, [_I64, _I64, _I, _I, _I, _I]),
     "indexer_decode": (_I, [_P, _P, _P, _P, _P, _I, _I64, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "indexer_decode_workspace_size": (_SZ, [_I, _I64, _I, _I, _I]),
+    "indexer_decode_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I64, _I, _I, _I, _P, _P, _P]),
+    "indexer_decode_noalloc_max_bytes": (_SZ, []),
     "indexer_group_bank": (_I, [_P, _P, _P, _P, _P, _I, _I64, _I64, _I, _I, _I64, _P, _P, _P, _I, _I, _I,
                                 _I, _U, _P, _P, _P, _P, _SZ, _P]),
     "indexer_group_bank_workspace_size": (_SZ, [_I64, _I64, _I, _I, _I, _I, _I, _I, _I, _U]),

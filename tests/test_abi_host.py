@@ -35,7 +35,7 @@ A = P(1 << 20)  # 16-byte aligned
 def test_header_symbols_exported(L):
     names = re.findall(r"^\s*(?:[\w\s\*]+?)\b(indexer_\w+)\s*\(", open(HEADER).read(), re.M)
     names = sorted(set(names))
-    assert len(names) == 22, names
+    assert len(names) == 24, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -254,3 +254,14 @@ def test_read_probe_rejects(L):
     assert L.indexer_read_probe(P((1 << 20) + 4), 64, A, 8, None) == INVALID
     assert L.indexer_read_probe(A, -1, A, 8, None) == INVALID
     assert L.indexer_read_probe(A, 64, None, 8, None) == INVALID
+
+
+def test_decode_noalloc_refuses_beyond_its_scratch(L):
+    """The allocation-free decode entry point has a fixed scratch array: sizes
+    whose workspace exceeds it are refused on the host, before any launch."""
+    cap = L.indexer_decode_noalloc_max_bytes()
+    assert cap == 96 << 20
+    assert L.indexer_decode_workspace_size(32, 262144, 64, 128, 2048) <= cap
+    assert L.indexer_decode_workspace_size(64, 262144, 64, 128, 2048) > cap
+    rc = L.indexer_decode_noalloc(A, A, A, A, A, 64, 262144, 64, 128, 2048, A, None, None)
+    assert rc == UNSUPPORTED and "scratch" in L.indexer_last_error().decode()
