@@ -4,7 +4,9 @@
 //
 // One wavefront owns one query (at position pos0 + j * pos_stride) and walks
 // its candidate keys 0..t in ascending index; the 8 waves of a workgroup own 8
-// consecutive queries and share one stream of 64-key tiles.
+// consecutive queries and share one stream of key tiles: 128 keys for E4M3
+// over contiguous keys, 64 for bf16 (twice the bytes per key) and for
+// gathering.
 //
 //   * Tiles go from HBM straight into a five-stage LDS ring with
 //     global_load_lds (no register staging): tile t is requested four steps
@@ -35,8 +37,8 @@
 //     crowded); keys arrive in ascending index, so strict ">" keeps the lower
 //     index on ties.
 //   * Full-row top-K, for launches whose rows all fit their buffer (cap at
-//     least the largest row's candidate count): each step stores its 64
-//     scores at their candidate slots with one buffer store (the buffer range
+//     least the largest row's candidate count): each 64 scores go to their
+//     candidate slots with one buffer store (the buffer range
 //     drops those past the row) and counts them in the wave's LDS histogram
 //     of the top 11 key bits.  Nothing is appended or compacted; at the end
 //     the histogram gives the first radix digit, one pass over the row keeps
@@ -57,7 +59,7 @@ namespace dsaidx {
 
 namespace {
 
-constexpr int kTile = 64;       // keys per step
+constexpr int kTile = 64;       // keys per append (one 64-lane ballot); the bf16 and gathering step
 constexpr int kStages = 5;      // LDS ring stages
 constexpr int kAhead = 4;       // a tile is requested this many steps before it is scored
 constexpr int kWaves = 8;       // queries per workgroup
@@ -72,15 +74,16 @@ struct StageC {  // a ring stage as a compile-time constant
   constexpr operator int() const { return S; }
 };
 
-template <int DT>
+template <int DT, int TK>
 struct Cfg {
   static constexpr int kRowBytes = DT == kBF16 ? 2 * kD : kD;
-  static constexpr int kTileBytes = kTile * kRowBytes;
+  static constexpr int kTileBytes = TK * kRowBytes;
   static constexpr int kChunksPerRow = kRowBytes / 16;
   static constexpr int kDma = kTileBytes / (kThreads * 16);  // 16-byte DMAs per lane per tile
   static constexpr int kSteps = DT == kBF16 ? kD / 16 : kD / 64;  // main MFMA k-steps
   // vm operations a wave issues per step: the tile chunks and the key scales
-  static constexpr int kVmPerStep = kDma + 1;
+  // (one 64-lane request per 64 keys)
+  static constexpr int kVmPerStep = kDma + TK / 64;
   // chunk c of row r sits at slot c ^ swz(r): any 16 consecutive rows then put
   // a given chunk in 16 distinct 16-byte bank groups (a 16-lane LDS pass)
   static __device__ __forceinline__ int swz(int r) { return DT == kBF16 ? (r & 15) : ((r >> 1) & 7); }
@@ -145,15 +148,25 @@ __device__ __forceinline__ void dma_b32(const v4i& rsrc, uint32_t lds, uint32_t 
 
 template <int DT, bool GATHER, bool FULL>
 __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs args) {
-  using C = Cfg<DT>;
+  // keys per step: E4M3 scores 128 keys (four 32-key sub-tiles) between
+  // barriers, so the step's fixed costs (the compaction check, the waits and
+  // the barrier) are paid once per 128 keys; bf16 tiles are twice the bytes
+  // and keep 64, as does gathering
+  constexpr int TK = (DT == kFP8 && !GATHER) ? 128 : 64;
+  constexpr int kHalves = TK / 64;  // 64-key halves of a tile (one append each)
+  using C = Cfg<DT, TK>;
   // vm operations a wave issues per step: the tile chunks, the key scales and,
   // gathering, the candidate indices of a later tile
   constexpr int kVm = C::kVmPerStep + (GATHER ? 1 : 0);
   using Frag = typename AFrag<DT>::type;
   __shared__ __attribute__((aligned(16))) uint8_t s_tile[kStages][C::kTileBytes];
-  __shared__ float s_ks[kStages][kTile];
+  __shared__ float s_ks[kStages][TK];
   __shared__ __attribute__((aligned(16))) uint32_t s_hist[kWaves][kSelectHistWords];
-  __shared__ float s_lin[kStages][2][kWaves][kTile];  // [tile's stage][d half][query][key]
+  // the linear terms of a tile: [slot][d half][query][key], slot = the tile's
+  // ring stage, or (128-key tiles) its parity: tile t+1's are written while
+  // tile t's are read
+  constexpr int kLinSlots = TK == 128 ? 2 : kStages;
+  __shared__ float s_lin[kLinSlots][2][kWaves][TK];
   // parts of q-tilde: bf16 hi / mid / lo (bf16 keys) or scaled fp16 hi / lo
   // (E4M3 keys), and the factor that undoes the fp16 parts' scale
   constexpr int kParts = DT == kBF16 ? 3 : 2;
@@ -191,7 +204,7 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   }
   const int ncand_blk = GATHER ? nbank + (t_hi - anchor) : t_hi + 1;
   const int ncand_me = !active ? 0 : GATHER ? nbank + (pos0 + j - anchor) : pos0 + j * args.pos_stride + 1;
-  const int ntiles = (ncand_blk + kTile - 1) / kTile;
+  const int ntiles = (ncand_blk + TK - 1) / TK;
 
   // ---- this wave's query: A fragments, gate weights (w/2, with the fp8 query
   // scale folded in), and q-tilde = sum_j (w_j/2) q_j split into bf16 hi + lo
@@ -384,23 +397,26 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
         const uint32_t pos = (uint32_t)position(t, t * kTile + lane_row[n]);
         off = pos <= (uint32_t)t_hi ? pos * C::kRowBytes + lane_off[n] : kNowhere;
       } else {
-        off = (uint32_t)(t * kTile + lane_row[n]) * C::kRowBytes + lane_off[n];
+        off = (uint32_t)(t * TK + lane_row[n]) * C::kRowBytes + lane_off[n];
       }
       dma_b128(kres, lds_tile + st * C::kTileBytes + n * kThreads * 16, off);
     }
-    // every wave writes the same 64 scales (fp8; bf16 loads placeholder words),
-    // so all waves issue the same number of requests per step
-    uint32_t soff = 4 * l;
-    if constexpr (DT == kFP8) {
-      const int c = t * kTile + l;
-      if constexpr (GATHER) {
-        const uint32_t pos = (uint32_t)position(t, c);
-        soff = pos <= (uint32_t)t_hi ? 4 * pos : kNowhere;
-      } else {
-        soff = 4 * c;
+    // every wave writes the same scales (fp8; bf16 loads placeholder words),
+    // 64 per request, so all waves issue the same number of requests per step
+#pragma unroll
+    for (int hh = 0; hh < kHalves; ++hh) {
+      uint32_t soff = 4 * l;
+      if constexpr (DT == kFP8) {
+        const int c = t * TK + 64 * hh + l;
+        if constexpr (GATHER) {
+          const uint32_t pos = (uint32_t)position(t, c);
+          soff = pos <= (uint32_t)t_hi ? 4 * pos : kNowhere;
+        } else {
+          soff = 4 * c;
+        }
       }
+      dma_b32(sres, lds_ks + (st * TK + 64 * hh) * 4, soff);
     }
-    dma_b32(sres, lds_ks + st * kTile * 4, soff);
   };
   // gathering: tile t's 64 bank positions into the index ring (every wave
   // writes the same words, so every wave issues the same requests)
@@ -456,11 +472,13 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
     }
     return s0 + s1;
   };
-  // the linear term of the tile in stage st for all 8 queries: this wave's
-  // 16 keys and d half, written to s_lin[st][kh]
-  auto linear = [&](int st) __attribute__((always_inline)) {
+  // the linear-term slot of tile t (in ring stage st)
+  auto lin_slot = [&](int t, int st) __attribute__((always_inline)) { return TK == 128 ? (t & 1) : st; };
+  // the linear term of 64-key half hh of tile t (in stage st) for all 8
+  // queries: this wave's 16 keys and d half, written to s_lin[slot][kh]
+  auto linear = [&](int t, int st, int hh) __attribute__((always_inline)) {
     v4f c = {0.0f, 0.0f, 0.0f, 0.0f};
-    const int r = 16 * nb + (l & 15);
+    const int r = 64 * hh + 16 * nb + (l & 15);
     const uint8_t* row = &s_tile[st][r * C::kRowBytes];
     const int x = C::swz(r);
 #pragma unroll
@@ -486,8 +504,9 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
     }
     // rows 4(l>>4)+i = (query 2(l>>4) + i/2, part i%2)
     const int q0 = 2 * (l >> 4);
-    s_lin[st][kh][q0][r] = c[0] + c[1];
-    s_lin[st][kh][q0 + 1][r] = c[2] + c[3];
+    const int sl = lin_slot(t, st);
+    s_lin[sl][kh][q0][r] = c[0] + c[1];
+    s_lin[sl][kh][q0 + 1][r] = c[2] + c[3];
   };
   // the full scores of the step's 64 keys, key l in lane l (sub-tile l / 32,
   // column l % 32).  p0 and p1 hold this lane's half-head sums for its column
@@ -497,13 +516,22 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   // key scale: (sum over heads of (w/2)|s| + linear term) * scale.  Adding +0
   // last turns a -0 (a negative sum times a zero scale, or a sum of -0 terms)
   // into +0, which is how the ranking treats it.
-  auto tile_score = [&](float p0, float p1, int st) __attribute__((always_inline)) -> float {
+  // the LDS terms of key 64*hh + l of tile t: its two half-d linear terms and
+  // its fp8 scale (read ahead of the score that needs them)
+  struct Terms { float lin0, lin1, ks; };
+  auto read_terms = [&](int t, int st, int hh) __attribute__((always_inline)) -> Terms {
+    const int sl = lin_slot(t, st), key = 64 * hh + l;
+    return Terms{s_lin[sl][0][wave][key], s_lin[sl][1][wave][key], DT == kFP8 ? s_ks[st][key] : 1.0f};
+  };
+  auto score_of = [&](float p0, float p1, const Terms& tm) __attribute__((always_inline)) -> float {
     auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
     // E4M3: the linear term comes scaled by 2^e; qinv = 2^-e undoes it
-    float sc = fmaf(s_lin[st][0][wave][l] + s_lin[st][1][wave][l], qinv,
-                    __uint_as_float(sw[0]) + __uint_as_float(sw[1]));
-    if constexpr (DT == kFP8) sc *= s_ks[st][l];
+    float sc = fmaf(tm.lin0 + tm.lin1, qinv, __uint_as_float(sw[0]) + __uint_as_float(sw[1]));
+    if constexpr (DT == kFP8) sc *= tm.ks;
     return sc + 0.0f;
+  };
+  auto tile_score = [&](float p0, float p1, int t, int st, int hh) __attribute__((always_inline)) -> float {
+    return score_of(p0, p1, read_terms(t, st, hh));
   };
   // append the step's scores that beat the threshold: lane l holds candidate
   // tbase + l, so lane order is candidate order and one ballot serves 64
@@ -535,7 +563,8 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   for (int t = 0; t < kAhead; ++t) request(t, t);
   __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): tiles 0..3 in LDS
   __syncthreads();
-  linear(0);
+#pragma unroll
+  for (int hh = 0; hh < kHalves; ++hh) linear(0, 0, hh);
   v16f acc0[2], acc1[2];
   Frag bA[C::kSteps], bB[C::kSteps];
   load_b(bA, 0, 0);
@@ -559,13 +588,13 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
       if (i > 0 && s_need[(i - 1) & 1] == i - 1 && active && cnt + nst > args.K) {
         flush();
         thr = wave_keep_topk(ckey, cidx, cnt, args.K, hist, kCompactSlack);
-      } else if (nst > kStage - 64) {
+      } else if (nst > kStage - TK) {
         flush();
       }
     }
     request(i + kAhead, st4);
     request_idx(i + kIdxAhead);
-    const int tbase = i * kTile;
+    const int tbase = i * TK;
     // the same work every step: past the last tile the MFMAs run on zeros
     // and the append masks them out
     load_b(bA, st1, 0);
@@ -577,19 +606,74 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
     constexpr int kHeld = DT == kFP8 ? C::kSteps / 2 : C::kSteps;
     mfma_steps(acc0, bA, 0, kHeld);
     const float p1 = abs_sum(acc1);
-    linear(st1);
+    linear(i + 1, st1, 0);
     if constexpr (kHeld < C::kSteps) mfma_steps(acc0, bA, kHeld, C::kSteps);
-    append(tile_score(p0, p1, st), tbase, i);
+    append(tile_score(p0, p1, i, st, 0), tbase, i);
     // tile i+2 (gathering: and the positions of tile i+5) must have landed
     // before the barrier publishes them: after their requests this wave issued
     // those of steps i-1 and i (and maybe a flush's stores, which only makes
     // the count conservative).  In full-row mode each step also ends with
     // one store, and the two after those requests are allowed to be pending.
-    __builtin_amdgcn_s_waitcnt(0x3F70 | (2 * kVm + (FULL ? 2 : 0)));
+    __builtin_amdgcn_s_waitcnt(0x3F70 | (2 * kVm + (FULL ? 2 * kHalves : 0)));
+    __syncthreads();
+  };
+  // The 128-key step (E4M3): tile i's four 32-key sub-tiles, with tile i+1's
+  // first sub-tile and its linear terms prepared at the end.  On entry acc0
+  // holds sub-tile 0's products and bB sub-tile 1's B operands; the MFMAs of
+  // each sub-tile run while the head sums of the one before are taken, and
+  // each 64-key half is scored and appended as soon as its sums are complete.
+  auto step128 = [&](const int i, auto stage) __attribute__((always_inline)) {
+    const int st = stage;
+    const int st1 = st == kStages - 1 ? 0 : st + 1;
+    const int st4 = st == 0 ? kStages - 1 : st - 1;  // (st + kAhead) % kStages
+    if constexpr (!FULL) {
+      if (i > 0 && s_need[(i - 1) & 1] == i - 1 && active && cnt + nst > args.K) {
+        flush();
+        thr = wave_keep_topk(ckey, cidx, cnt, args.K, hist, kCompactSlack);
+      } else if (nst > kStage - TK) {
+        flush();
+      }
+    }
+    request(i + kAhead, st4);
+    const int tbase = i * TK;
+    load_b(bA, st, 2);
+    mfma_sub(acc1, bB);                    // sub-tile 1
+    const float p0 = abs_sum(acc0);        // sub-tile 0
+    load_b(bB, st, 3);
+    mfma_sub(acc0, bA);                    // sub-tile 2
+    const float p1 = abs_sum(acc1);        // sub-tile 1
+    linear(i + 1, st1, 0);
+    append(tile_score(p0, p1, i, st, 0), tbase, i);
+    load_b(bA, st1, 0);
+    mfma_sub(acc1, bB);                    // sub-tile 3
+    const float p2 = abs_sum(acc0);        // sub-tile 2
+    load_b(bB, st1, 1);
+    constexpr int kHeld = C::kSteps / 2;
+    mfma_steps(acc0, bA, 0, kHeld);        // tile i+1, sub-tile 0 (half)
+    const float p3 = abs_sum(acc1);        // sub-tile 3
+    linear(i + 1, st1, 1);
+    mfma_steps(acc0, bA, kHeld, C::kSteps);
+    append(tile_score(p2, p3, i, st, 1), tbase + 64, i);
+    // tile i+2 must have landed before the barrier publishes it: after its
+    // requests this wave issued those of steps i-1 and i; in full-row mode
+    // each step also ends with two stores
+    __builtin_amdgcn_s_waitcnt(0x3F70 | (2 * kVm + (FULL ? 2 * kHalves : 0)));
     __syncthreads();
   };
   static_assert(kStages == 5 && kAhead == kStages - 1, "the loops below assume a five-stage ring");
-  if constexpr (DT == kFP8) {
+  if constexpr (TK == 128) {
+    for (int i = 0; i < ntiles; i += kStages) {
+      step128(i, StageC<0>{});
+      if (i + 1 >= ntiles) break;
+      step128(i + 1, StageC<1>{});
+      if (i + 2 >= ntiles) break;
+      step128(i + 2, StageC<2>{});
+      if (i + 3 >= ntiles) break;
+      step128(i + 3, StageC<3>{});
+      if (i + 4 >= ntiles) break;
+      step128(i + 4, StageC<4>{});
+    }
+  } else if constexpr (DT == kFP8) {
     for (int i = 0; i < ntiles; i += kStages) {
       step(i, StageC<0>{});
       if (i + 1 >= ntiles) break;
@@ -627,7 +711,7 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
 bool dense_topk_supported(const ScanArgs& a) {
   // buffer offsets are 32-bit: the key rows up to the last query's position
   // (plus the tiles requested past it) must stay below 2 GiB
-  const int64_t keys = a.pos0 + (a.nq - 1) * a.pos_stride + 1 + kAhead * kTile;
+  const int64_t keys = a.pos0 + (a.nq - 1) * a.pos_stride + 1 + kAhead * 128;
   // bank refinement: every workgroup's 8 queries must sit in one group
   const bool shape_ok = a.bank == nullptr || (a.group % kWaves == 0 && a.nq % kWaves == 0 && a.pos_stride == 1);
   return shape_ok && a.H > 32 && a.H <= 64 && a.d == kD && keys * 2 * kD < (int64_t(1) << 31);
