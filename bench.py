@@ -302,19 +302,31 @@ def bench_decode(dsa, args, log):
     return res
 
 
+# workgroup counts the read probe is timed at: the rate of a grid-stride
+# read depends on the grid (how the concurrent addresses fall on the HBM
+# channels), so the ceiling is the best of several
+READ_PROBE_GRIDS = (256, 512, 2048, 8192, 16384, 32768)
+
+
 def bench_read_probe(dsa, args, log):
     """The plain HBM read stream (indexer_read_probe: every byte of a 4 GiB
-    buffer read once with coalesced 16-byte loads), timed with HIP events: the
-    practical ceiling the memory-bound decode scan is compared with."""
+    buffer read once with coalesced 16-byte loads), timed with HIP events at
+    several grid sizes: the best is the practical ceiling the memory-bound
+    decode scan is compared with."""
     nbytes = 4 << 30
     buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
-    out = torch.empty(2048, dtype=torch.int32, device="cuda")
+    out = torch.empty(max(READ_PROBE_GRIDS), dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
-    log("timing the plain read stream (4 GiB)")
-    _, ms = _timed_calls(lambda: dsa.read_probe(buf, 2048, out), 20, stream)
-    gbs = nbytes / (ms * 1e-3) / 1e9
-    return dict(kernel="read_probe_kernel (indexer_read_probe)", bytes=nbytes, ms=ms, gbs=gbs,
-                frac_of_peak=gbs / PEAK_HBM_GBS)
+    log(f"timing the plain read stream (4 GiB) at grids {READ_PROBE_GRIDS}")
+    by_grid = {}
+    for g in READ_PROBE_GRIDS:
+        _, ms = _timed_calls(lambda: dsa.read_probe(buf, g, out), 10, stream)
+        by_grid[g] = nbytes / (ms * 1e-3) / 1e9
+    best = max(by_grid, key=by_grid.get)
+    gbs = by_grid[best]
+    return dict(kernel="read_probe_kernel (indexer_read_probe)", bytes=nbytes,
+                ms=nbytes / (gbs * 1e9) * 1e3, gbs=gbs, frac_of_peak=gbs / PEAK_HBM_GBS, best_grid=best,
+                gbs_by_grid={str(k): round(v, 1) for k, v in by_grid.items()})
 
 
 # ------------------------------------------------------------------ ADIndex

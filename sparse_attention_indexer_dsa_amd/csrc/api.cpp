@@ -272,7 +272,7 @@ static DecodeWs decode_ws(int B, int64_t Nmax, int R = 1) {
   w.ckey = w.rowsel + align_up((size_t)B * 16u);
   w.cidx = w.ckey + align_up((size_t)B * kDecCandCap * 4u);
   w.clcnt = w.cidx + align_up((size_t)B * kDecCandCap * 4u);
-  w.above = w.clcnt + align_up((size_t)B * nblk * 4u);
+  w.above = w.clcnt + align_up((size_t)B * nblk * kDecListSegs * 4u);
   w.off = w.above + align_up((size_t)B * nblk * 4u);
   w.clidx = w.off + align_up((size_t)B * nblk * 4u);
   w.clsc = w.clidx + align_up((size_t)B * nblk * kpb * 4u);

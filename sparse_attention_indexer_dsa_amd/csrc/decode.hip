@@ -11,10 +11,11 @@
 // M.  ReLU, the gate-weighted head sum and the per-key scale follow in
 // registers.  Scores stay in LDS together with a histogram of the top 12 bits
 // of their order-preserving keys; the histogram is added to the row's, and
-// only the scores in bins at or above the span's own K-th best (a lower bound
-// of the row's K-th best, to 24 bits) leave the chip, as a compact list.  HBM writes
-// cost far more than their share of the traffic, so the row of scores is never
-// written whole.
+// only the scores in bins at or above the bin of the span's own K-th best (a
+// lower bound of the row's K-th best) leave the chip, as a compact list whose
+// four segments the four waves write in one pass.  HBM writes cost far more
+// than their share of the traffic, so the row of scores is never written
+// whole.
 //
 // Selection, with the row histogram's bin b* that holds the row's K-th best:
 //   decode_classify (one workgroup per span): counts the span's list entries
@@ -275,10 +276,10 @@ __global__ void __launch_bounds__(kDecThreads, 2) decode_scan_kernel(const Decod
     }
     // The K-th best score of the span is a lower bound of the row's K-th
     // best: scores below it cannot reach the row's top K and are not kept.
-    // Its top 12 bits come from the histogram, the next 12 from a second
-    // histogram over the span's scores inside that bin; the list keeps every
-    // score whose top 24 bits reach the result.  A span of at most K keys
-    // keeps everything.
+    // The list keeps every score in the histogram bin that holds it or above
+    // (a finer cut took a second pass over the span, which cost more than
+    // the longer lists do downstream).  A span of at most K keys keeps
+    // everything.
     uint32_t keep_from = 0;  // keep scores with (order key >> 8) >= keep_from
     if (span_b > args.K) {
       constexpr int kPer = kDecHistBins / kDecThreads;
@@ -288,61 +289,24 @@ __global__ void __launch_bounds__(kDecThreads, 2) decode_scan_kernel(const Decod
       };
       block_find_digit<kDecWaves>(kPer, bins16, args.K, s_tmp, s_res);
       const uint32_t bloc = (uint32_t)s_res[0];
-      const int krem = s_res[1];
-      for (int i = tid; i < kDecHistBins / 2; i += kDecThreads) hst[i] = 0;
-      __syncthreads();
-      // eight LDS reads in flight per thread, then their updates
-      for (int e0 = tid; e0 < span_b; e0 += 8 * kDecThreads) {
-        uint32_t kk[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int e = e0 + u * kDecThreads;
-          kk[u] = e < span_b ? order_key(scr[e]) : 0u;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          if (e0 + u * kDecThreads < span_b && (kk[u] >> 20) == bloc) {
-            const uint32_t sub = (kk[u] >> 8) & 0xFFFu;
-            atomicAdd(&hst[sub >> 1], 1u << (16 * (sub & 1)));
-          }
-        }
-      }
-      __syncthreads();
-      block_find_digit<kDecWaves>(kPer, bins16, krem, s_tmp, s_res);
-      keep_from = (bloc << 12) | (uint32_t)s_res[0];
+      keep_from = bloc << 12;
     }
-    // compact list of the kept scores, in ascending key order: wave w takes
-    // the w-th quarter of the span, 64 consecutive keys per step (lane l key
-    // base + l: conflict-free LDS reads, coalesced list writes)
-    const int quarter = ((span_b + kDecWaves - 1) / kDecWaves + 63) / 64 * 64;
-    const int c0 = wave * quarter, c1 = c0 + quarter < span_b ? c0 + quarter : span_b;
-    // eight LDS reads in flight per lane, then their ballots
-    auto keys8 = [&](int base, uint32_t (&kk)[8]) __attribute__((always_inline)) {
+    // compact list of the kept scores: wave w writes segment w, the kept
+    // keys of the span's w-th quarter in ascending order, 64 consecutive keys
+    // per step (lane l key base + l: conflict-free LDS reads, coalesced list
+    // writes), eight LDS reads in flight per lane, in one pass
+    static_assert(kDecListSegs == kDecWaves, "one list segment per wave");
+    const int seg = (int)args.kpb / kDecListSegs;
+    const int c0 = wave * seg, c1 = c0 + seg < span_b ? c0 + seg : span_b;
+    const int64_t sbase = ((int64_t)b * args.nblk + blockIdx.x) * args.kpb + c0;
+    int pos = 0;  // wave-uniform
+    for (int base = c0; base < c1; base += 8 * 64) {
+      uint32_t kk[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int e = base + 64 * u + l;
         kk[u] = e < c1 ? order_key(scr[e]) : 0u;
       }
-    };
-    int mine = 0;  // wave-uniform
-    for (int base = c0; base < c1; base += 8 * 64) {
-      uint32_t kk[8];
-      keys8(base, kk);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) mine += popc(ballot(base + 64 * u + l < c1 && (kk[u] >> 8) >= keep_from));
-    }
-    if (l == 0) s_tmp[wave] = mine;
-    __syncthreads();
-    int pos = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) {
-      pos += w < wave ? s_tmp[w] : 0;
-      total += s_tmp[w];
-    }
-    const int64_t lbase = ((int64_t)b * args.nblk + blockIdx.x) * args.kpb;
-    for (int base = c0; base < c1; base += 8 * 64) {
-      uint32_t kk[8];
-      keys8(base, kk);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int e = base + 64 * u + l;
@@ -350,13 +314,13 @@ __global__ void __launch_bounds__(kDecThreads, 2) decode_scan_kernel(const Decod
         const uint64_t km = ballot(keep);
         if (keep) {
           const int p = pos + rank_below(km);
-          args.cl_idx[lbase + p] = (int32_t)(blk0 + e);
-          args.cl_sc[lbase + p] = key_to_float(kk[u]);
+          args.cl_idx[sbase + p] = (int32_t)(blk0 + e);
+          args.cl_sc[sbase + p] = key_to_float(kk[u]);
         }
         pos += popc(km);
       }
     }
-    if (tid == 0) args.cl_cnt[(int64_t)b * args.nblk + blockIdx.x] = total;
+    if (l == 0) args.cl_cnt[((int64_t)b * args.nblk + blockIdx.x) * kDecListSegs + wave] = pos;
     if (R > 1) __syncthreads();  // s_tmp, s_res and the histogram serve the next row
   }
 }
@@ -434,19 +398,21 @@ __device__ void select_lists_exact(const DecodeArgs& args, int b, int nb, uint32
   constexpr int kB = 4 * kSelThreads;  // slots per batch
   const int64_t row0 = (int64_t)b * args.nblk * args.kpb;
   const int64_t nslots = (int64_t)nb * args.kpb;
-  const int kpb = (int)args.kpb;
-  for (int j = tid; j < nb && j < kSelThreads; j += kSelThreads) s_cnt[j] = args.cl_cnt[(int64_t)b * args.nblk + j];
+  const int seg = (int)args.kpb / kDecListSegs;  // slots per list segment
+  const int nseg = nb * kDecListSegs;
+  const int64_t cbase = (int64_t)b * args.nblk * kDecListSegs;
+  for (int j = tid; j < nseg && j < kSelThreads; j += kSelThreads) s_cnt[j] = args.cl_cnt[cbase + j];
   __syncthreads();
-  // list j's entry count (spans past the LDS copy are read from memory)
+  // segment j's entry count (segments past the LDS copy are read from memory)
   auto count = [&](uint32_t j) __attribute__((always_inline)) {
-    return j < (uint32_t)kSelThreads ? s_cnt[j] : args.cl_cnt[(int64_t)b * args.nblk + j];
+    return j < (uint32_t)kSelThreads ? s_cnt[j] : args.cl_cnt[cbase + j];
   };
   auto load = [&](int64_t s0, float (&v)[kIter][4], uint32_t (&ok)[kIter]) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < kIter; ++k) {
-      const int64_t s = s0 + k * kB + 4 * tid;  // kpb is a multiple of 4: one list
+      const int64_t s = s0 + k * kB + 4 * tid;  // a segment is a multiple of 4 slots
       const uint32_t su = (uint32_t)s;              // slots of a row fit in 32 bits
-      const int lim = s < nslots ? count(su / (uint32_t)kpb) - (int)(su % (uint32_t)kpb) : 0;
+      const int lim = s < nslots ? count(su / (uint32_t)seg) - (int)(su % (uint32_t)seg) : 0;
       ok[k] = lim >= 4 ? 0xFu : (lim > 0 ? (1u << lim) - 1u : 0u);
       if (s < nslots) {
         const v4f a = *(const v4f*)(args.cl_sc + row0 + s);
@@ -606,6 +572,30 @@ __device__ __forceinline__ void row_threshold(const DecodeArgs& args, int b, int
 // workgroup size, so every load is coalesced and all of them are in flight).
 constexpr int kSpanBatch = 16;
 
+// The compact list of span j of row b read as one list, its segments in
+// order (ascending keys): entry e of the list sits at slot(e).
+struct SpanList {
+  int64_t base;  // the span's first slot
+  int seg;       // slots per segment
+  int p1, p2, p3, n;  // entries before segments 1, 2, 3; entries in all
+  __device__ __forceinline__ SpanList(const DecodeArgs& a, int b, int j) {
+    static_assert(kDecListSegs == 4, "four segments per list");
+    const int64_t sp = (int64_t)b * a.nblk + j;
+    base = sp * a.kpb;
+    seg = (int)a.kpb / kDecListSegs;
+    const int32_t* c = a.cl_cnt + sp * kDecListSegs;
+    p1 = c[0];
+    p2 = p1 + c[1];
+    p3 = p2 + c[2];
+    n = p3 + c[3];
+  }
+  __device__ __forceinline__ int64_t slot(int e) const {
+    const int w = (e >= p1) + (e >= p2) + (e >= p3);
+    const int before = w == 0 ? 0 : (w == 1 ? p1 : (w == 2 ? p2 : p3));
+    return base + (int64_t)w * seg + (e - before);
+  }
+};
+
 // One workgroup per (span, row): counts the span's list entries above b* and
 // gathers those inside b* into the row's candidate array.
 __global__ void __launch_bounds__(kSpanThreads) decode_classify_kernel(const DecodeArgs args) {
@@ -617,15 +607,15 @@ __global__ void __launch_bounds__(kSpanThreads) decode_classify_kernel(const Dec
   int64_t n = args.seq_lens[b];
   n = n < 0 ? 0 : (n > args.Nmax ? args.Nmax : n);
   if (n <= args.K || (int64_t)j * args.kpb >= n) return;
-  const int64_t lbase = ((int64_t)b * args.nblk + j) * args.kpb;
-  const int c = args.cl_cnt[(int64_t)b * args.nblk + j];
+  const SpanList L(args, b, j);
+  const int c = L.n;
   // the first batch of the list is requested before the threshold search
   uint32_t key[kSpanBatch];
   auto load_batch = [&](int base) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kSpanBatch; ++u) {
       const int e = base + u * kSpanThreads + tid;
-      key[u] = e < c ? order_key(args.cl_sc[lbase + e]) : 0u;  // key 0: below every bin b*
+      key[u] = e < c ? order_key(args.cl_sc[L.slot(e)]) : 0u;  // key 0: below every bin b*
     }
   };
   load_batch(0);
@@ -654,7 +644,7 @@ __global__ void __launch_bounds__(kSpanThreads) decode_classify_kernel(const Dec
       if ((key[u] >> kShift) == bstar && key[u] != 0u) {
         if (p < kDecCandCap) {
           ck[p] = key[u];
-          ci[p] = args.cl_idx[lbase + base + u * kSpanThreads + tid];
+          ci[p] = args.cl_idx[L.slot(base + u * kSpanThreads + tid)];
         }
         ++p;
       }
@@ -692,13 +682,13 @@ __global__ void __launch_bounds__(kSelThreads) decode_select_kernel(const Decode
     // every span kept all of its keys: the lists are keys 0 .. n-1 in order
     int off = 0;
     for (int j = 0; j < nb; ++j) {
-      const int64_t lbase = ((int64_t)b * args.nblk + j) * args.kpb;
-      const int c = args.cl_cnt[(int64_t)b * args.nblk + j];
-      for (int i = tid; i < c; i += kSelThreads) {
-        oidx[off + i] = args.cl_idx[lbase + i];
-        if (osc) osc[off + i] = args.cl_sc[lbase + i];
+      const SpanList L(args, b, j);
+      for (int i = tid; i < L.n; i += kSelThreads) {
+        const int64_t sl = L.slot(i);
+        oidx[off + i] = args.cl_idx[sl];
+        if (osc) osc[off + i] = args.cl_sc[sl];
       }
-      off += c;
+      off += L.n;
     }
     for (int p = (int)n + tid; p < K; p += kSelThreads) {
       oidx[p] = -1;
@@ -715,9 +705,10 @@ __global__ void __launch_bounds__(kSelThreads) decode_select_kernel(const Decode
     select_lists_exact(args, b, nb, bstar, need, oidx, osc, s_h, s_tmp, s_res, s_tmpn, s_cnt);
     return;
   }
-  // The candidates are the list entries in b*: a span's list may have dropped
-  // b* keys below its own K-th best (which is at most the row's), so there can
-  // be fewer than in_bin, and none of the dropped ones is selected.
+  // The candidates are the list entries in b*: every span keeps whole bins
+  // from its own K-th best's bin up, which is at most b*, so b*'s keys are all
+  // listed (the count is at most in_bin either way, and a key a list did not
+  // keep could not be selected).
   const int nc = args.cand_cnt[b];
   for (int i = tid; i < nc; i += kSelThreads) {
     s_ckey[i] = args.cand_key[(int64_t)b * kDecCandCap + i];
@@ -791,8 +782,8 @@ __global__ void __launch_bounds__(kSpanThreads) decode_emit_kernel(const DecodeA
   n = n < 0 ? 0 : (n > args.Nmax ? args.Nmax : n);
   if ((int64_t)j * args.kpb >= n || args.rowsel[4 * b] != 1) return;
   const uint32_t kth = args.rowsel[4 * b + 1], idx_cut = args.rowsel[4 * b + 2];
-  const int64_t lbase = ((int64_t)b * args.nblk + j) * args.kpb;
-  const int c = args.cl_cnt[(int64_t)b * args.nblk + j];
+  const SpanList L(args, b, j);
+  const int c = L.n;
   int32_t* oidx = args.out_idx + (int64_t)b * args.K;
   float* osc = args.out_score ? args.out_score + (int64_t)b * args.K : nullptr;
   int out = args.span_off[(int64_t)b * args.nblk + j];
@@ -802,8 +793,9 @@ __global__ void __launch_bounds__(kSpanThreads) decode_emit_kernel(const DecodeA
 #pragma unroll
     for (int u = 0; u < kSpanBatch; ++u) {
       const int e = base + u * kSpanThreads + tid;
-      v[u] = e < c ? args.cl_sc[lbase + e] : 0.0f;
-      idx[u] = e < c ? args.cl_idx[lbase + e] : -1;
+      const int64_t sl = e < c ? L.slot(e) : 0;
+      v[u] = e < c ? args.cl_sc[sl] : 0.0f;
+      idx[u] = e < c ? args.cl_idx[sl] : -1;
     }
     bool sel[kSpanBatch];
 #pragma unroll

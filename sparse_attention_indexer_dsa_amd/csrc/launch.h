@@ -47,7 +47,12 @@ constexpr int kDecHistBins = 1 << kDecHistBits;
 
 // Decode: scores of one bf16 query per sequence against its E4M3 cache, then
 // a per-row top-K.  Scan workgroups cover kpb keys of a row each and keep, in
-// a compact list, only the scores that can still reach the row's top K.
+// a compact list, only the scores that can still reach the row's top K.  The
+// list is stored as kDecListSegs segments, one per wave of the workgroup: the
+// kpb slots of span j hold segment w (the kept keys of the span's w-th
+// quarter, ascending) at slots w*kpb/kDecListSegs onwards, and cl_cnt holds
+// each segment's count; read in segment order the list is ascending.
+constexpr int kDecListSegs = 4;
 struct DecodeArgs {
   const void* q;          // [B, H, d] bf16
   const uint8_t* kc;      // [B, Nmax, d] E4M3
@@ -68,8 +73,8 @@ struct DecodeArgs {
   int64_t kpb;            // keys per scan workgroup: a multiple of 256, <= dec_max_kpb(scan_rows)
   int nblk;               // scan workgroups per row: ceil(Nmax / kpb)
   uint32_t* hist;         // [B, kDecHistBins] workspace, zeroed per call
-  int32_t* cl_cnt;        // [B, nblk] entries of each workgroup's compact list
-  int32_t* cl_idx;        // [B, nblk, kpb] key indices of the compact lists (ascending)
+  int32_t* cl_cnt;        // [B, nblk, kDecListSegs] entries of each list segment
+  int32_t* cl_idx;        // [B, nblk, kpb] key indices of the compact lists (segments)
   float* cl_sc;           // [B, nblk, kpb] their scores
   int32_t* cand_cnt;      // [B] threshold-bin candidates gathered, zeroed per call
   uint32_t* cand_key;     // [B, kDecCandCap] their order keys
@@ -90,6 +95,7 @@ constexpr bool dec_scan_rows_ok(int R, int H, int B) { return (R == 2 || R == 4)
 constexpr int kDecCandCap = 16384;    // threshold-bin candidates a row keeps in LDS
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
 
 // Mean-pooled group query: for groups g0 .. g0+ngroups-1 of G consecutive
 // queries of q [*, H, d] bf16 and w [*, H], writes qbar [ngroups, H, d] bf16

@@ -329,9 +329,9 @@ def test_decode_select_paths(dsa):
 
 def test_decode_reused_workspace(dsa):
     """Rows whose first span holds nearly every key (its own K-th best falls in
-    the row's threshold bin, so its list drops some of that bin's keys), decoded
-    with a workspace that a previous call on other inputs left full: only the
-    candidates this call gathered may be read."""
+    the row's threshold bin), decoded with a workspace that a previous call on
+    other inputs left full: only the candidates this call gathered may be
+    read."""
     lens = [257, 300, 513, 260, 511, 258, 400, 290]
     first = make_decode(B=8, N=600, H=64, d=128, topk=100, dist="int", seed=24, seq_lens=lens)
     wl = make_decode(B=8, N=600, H=64, d=128, topk=100, dist="int", seed=25, seq_lens=lens)
@@ -342,6 +342,14 @@ def test_decode_reused_workspace(dsa):
         torch.cuda.synchronize()
         ri, rs = oracle.decode(w["q"], w["k_cache"], w["k_scale"], w["w"], w["seq_lens"], 100)
         compare(_np(gi), _np(gs), ri, rs, True)
+
+
+def test_decode_many_rows(dsa):
+    """Many short ragged rows (1100 rows of 0 to 300 keys): every row is one
+    span, rows of no keys, and rows of at most K keys."""
+    lens = [(37 * b) % 301 for b in range(1100)]
+    wl = make_decode(B=1100, N=300, H=64, d=128, topk=64, dist="int", seed=15, seq_lens=lens)
+    _decode_check(dsa, wl)
 
 
 def test_decode_small_heads(dsa):
