@@ -698,6 +698,87 @@ def bench_calib(dsa, args, log):
     return res
 
 
+# ------------------------------------------------------------------ profiles
+
+def summarize_trace(path):
+    """A table of rocprofv3's kernel statistics (kernel_stats.csv), or of a
+    kernel trace (kernel_trace.csv) by kernel and grid size."""
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    if rows and "Grid_Size_X" in rows[0]:
+        groups = {}
+        for r in rows:
+            key = (r["Kernel_Name"][:70], int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])))
+            groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        print(f"{'kernel':70s} {'workgroups':>10s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}")
+        for (name, wgs), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+            print(f"{name:70s} {wgs:10d} {len(v):6d} {sum(v) / len(v):10.2f} {min(v):10.2f} {max(v):10.2f}")
+        return
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    print(f"{'kernel':70s} {'calls':>6s} {'total_us':>11s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}")
+    for r in rows:
+        name = r["Name"][:70]
+        print(f"{name:70s} {int(r['Calls']):6d} {float(r['TotalDurationNs']) / 1e3:11.1f} "
+              f"{float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
+              f"{float(r['Percentage']):6.2f}")
+
+
+# kernels of one measured launch in the traffic records, and the calls one
+# `bench.py --steps 1 --warmup 0` makes: 32 prefill chunk calls, 3 + 20 decode
+# calls
+TRAFFIC_KERNELS = {
+    "dense_topk_fp8_prefill128k": (("dense_topk_kernel<2, false, ",), 32),
+    "decode_call_decode256k": (("fill_i32_kernel", "decode_scan_kernel<2, 128, 1>", "decode_classify_kernel",
+                                "decode_select_kernel", "decode_emit_kernel"), 23),
+}
+
+
+def _counter_sums(path, counter):
+    """counter value summed per kernel name, and dispatches per kernel name."""
+    import csv
+    tot, disp = {}, {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        name = r["Kernel_Name"]
+        tot[name] = tot.get(name, 0.0) + float(r["Counter_Value"])
+        disp[name] = disp.get(name, 0) + 1
+    return tot, disp
+
+
+def summarize_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes):
+    """Write profiles/traffic.json: HBM bytes per measured launch from the
+    FETCH_SIZE and WRITE_SIZE counters (KiB per dispatch), each scaled by the
+    factor that makes the 5-copy probe read and write its known bytes."""
+    cf, _ = _counter_sums(copy_fetch_csv, "FETCH_SIZE")
+    cw, _ = _counter_sums(copy_write_csv, "WRITE_SIZE")
+    # the five copies only (the probe's source is filled by another kernel first)
+    copy_fetch_kib = sum(v for k, v in cf.items() if "copyBuffer" in k) / 5
+    copy_write_kib = sum(v for k, v in cw.items() if "copyBuffer" in k) / 5
+    ff = copy_bytes / 1024 / copy_fetch_kib
+    wf = copy_bytes / 1024 / copy_write_kib
+    fetch, fd = _counter_sums(fetch_csv, "FETCH_SIZE")
+    write, _ = _counter_sums(write_csv, "WRITE_SIZE")
+    out = {"_note": "HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each "
+                    "scaled by the factor that makes a plain device copy of copy_bytes read and write "
+                    "copy_bytes; source_sha1 hashes the device sources listed (bench.py ignores a record "
+                    "whose hash differs from the sources it runs).",
+           "calibration": {"copy_bytes": copy_bytes, "copy_fetch_kib": copy_fetch_kib,
+                           "copy_write_kib": copy_write_kib, "fetch_factor": ff, "write_factor": wf}}
+    for key, (prefixes, calls) in TRAFFIC_KERNELS.items():
+        names = [n for n in fetch if any(n.startswith(p) or ("::" + p) in n or (" " + p) in n for p in prefixes)]
+        f_kib = sum(fetch[n] for n in names) / calls
+        w_kib = sum(write.get(n, 0.0) for n in names) / calls
+        out[key] = {"kernels": sorted(names), "dispatches": [fd[n] for n in sorted(names)], "calls": calls,
+                    "fetch_kib_per_launch": f_kib, "write_kib_per_launch": w_kib,
+                    "hbm_bytes_per_launch": (f_kib * ff + w_kib * wf) * 1024,
+                    "source_sha1": _source_sha1(KERNEL_SOURCES[key]), "sources": list(KERNEL_SOURCES[key])}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -722,7 +803,21 @@ def main():
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only copy BYTES device-to-device 5 times (calibrates HBM byte counters)")
+    ap.add_argument("--summarize-trace", metavar="CSV",
+                    help="only print a table of a rocprofv3 kernel_stats.csv (no GPU)")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="only update profiles/traffic.json from four rocprofv3 counter_collection.csv files "
+                         "(FETCH_SIZE and WRITE_SIZE of `bench.py --steps 1 --warmup 0 --no-cpu --no-dsa16k "
+                         "--no-adindex --no-layerwise`, then of `bench.py --copy-probe BYTES`; no GPU)")
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30, help="the copy probe's BYTES (--summarize-traffic)")
     args = ap.parse_args()
+
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic, copy_bytes=args.copy_bytes)
+        return
 
     if args.copy_probe:
         src = torch.empty(args.copy_probe, dtype=torch.uint8, device="cuda").fill_(1)

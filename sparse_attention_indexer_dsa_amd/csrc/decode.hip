@@ -873,16 +873,24 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   return launch_dec<2, 128>(a, stream);
 }
 
+// p[0, n) = v: 16-byte stores from the first 16-byte boundary, single words
+// before it and after the last whole vector.
 __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = v;
+  const int64_t head = (int64_t)((16u - ((uintptr_t)p & 15u)) & 15u) / 4;  // words before the boundary
+  const int64_t h = head < n ? head : n;
+  const int64_t nq = (n - h) / 4;
+  const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x, stride = (int64_t)gridDim.x * blockDim.x;
+  u32x4* q = (u32x4*)(p + h);
+  const u32x4 vv = {(uint32_t)v, (uint32_t)v, (uint32_t)v, (uint32_t)v};
+  for (int64_t i = t0; i < nq; i += stride) q[i] = vv;
+  if (t0 < h) p[t0] = v;
+  if (t0 < n - h - 4 * nq) p[h + 4 * nq + t0] = v;
 }
 
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
-  int64_t blocks = (n + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
+  int64_t blocks = (n / 4 + 255) / 256 + 1;
+  if (blocks > 1024) blocks = 1024;
   hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n, v);
   return hipGetLastError();
 }
