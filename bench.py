@@ -366,6 +366,22 @@ def bench_adindex(dsa, args, log):
     for name, fn, steps in (("adindex", step, args.steps), ("adindex_pool", step_pool, args.steps),
                             ("dense", dense, max(2, args.steps // 2))):
         ms[name], ev[name] = _timed_calls(fn, steps, stream)
+    # the other (G, P) settings of Eq. (5)'s search, with the training-free
+    # pooled group query (the q-bar input above is G = 16's); G = 4 refines in
+    # the general kernel, G = 8 and 16 in the dense kernel's gather mode
+    settings = []
+    for g2, p2 in ((4, 8192), (8, 8192), (16, 8192), (8, 16384), (16, 16384)):
+        ws2 = torch.empty(dsa.workspace_group_bank(T, T, H, H, d, g2, p2, K, dsa.DSAIDX_BF16, dsa.POOL_MEAN),
+                          dtype=torch.uint8, device="cuda")
+        fn = (lambda g2=g2, p2=p2, ws2=ws2: dsa.indexer_group_bank(
+            t["q"], t["k"], t["w"], None, None, 0, g2, p2, K, flags=dsa.POOL_MEAN, want_score=False,
+            out_idx=out_pool, ws=ws2))
+        m2, _ = _timed_calls(fn, max(2, args.steps // 2), stream)
+        pr = dsa.indexer_group_bank_pairs(T, 0, g2, p2)
+        settings.append(dict(G=g2, P=p2, ms_per_call=m2, speedup_vs_dense=ms["dense"] / m2,
+                             scoring_count_ratio=_pairs_causal(0, T) / pr,
+                             tflops=2 * H * d * pr / (m2 * 1e-3) / 1e12))
+        del ws2
     step()  # leave the bank result (and its banks) in `out` for the parity leg
     torch.cuda.synchronize()
     pairs = dsa.indexer_group_bank_pairs(T, 0, G, P)
@@ -389,6 +405,7 @@ def bench_adindex(dsa, args, log):
                            recall_vs_dense=rec_pool,
                            note="training-free group query: mean of the group's own queries and gates"),
                recall_note="synthetic i.i.d. queries: recall reflects the random inputs, not trained data",
+               pooled_settings=settings,
                roofline=dict(bound="mfma", kernel="indexer_group_bank (group scan + refinement + fallback "
                                                   "launches of dense_topk_kernel<bf16>, one call)",
                              achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
