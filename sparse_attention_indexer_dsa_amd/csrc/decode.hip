@@ -293,13 +293,19 @@ __global__ void __launch_bounds__(kDecThreads, 2) decode_scan_kernel(const Decod
     }
     // compact list of the kept scores: wave w writes segment w, the kept
     // keys of the span's w-th quarter in ascending order, 64 consecutive keys
-    // per step (lane l key base + l: conflict-free LDS reads, coalesced list
-    // writes), eight LDS reads in flight per lane, in one pass
+    // per step (lane l key base + l: conflict-free LDS reads), eight LDS reads
+    // in flight per lane, in one pass.  Kept entries gather in a per-wave LDS
+    // stage (the histogram's words, free now) and leave it 64 at a time, so
+    // every list store but the last writes a whole wave's 256 bytes.
     static_assert(kDecListSegs == kDecWaves, "one list segment per wave");
+    static_assert(kDecHistBins / 2 >= kDecWaves * 256, "a 128-entry stage per wave");
     const int seg = (int)args.kpb / kDecListSegs;
     const int c0 = wave * seg, c1 = c0 + seg < span_b ? c0 + seg : span_b;
     const int64_t sbase = ((int64_t)b * args.nblk + blockIdx.x) * args.kpb + c0;
-    int pos = 0;  // wave-uniform
+    __syncthreads();  // every wave is done with the histogram's words
+    uint32_t* stg_sc = hst + wave * 256;                  // score bits [128]
+    int32_t* stg_ix = (int32_t*)(hst + wave * 256 + 128);  // key indices [128]
+    int pos = 0, nst = 0;  // wave-uniform: entries written, entries staged (< 64 between steps)
     for (int base = c0; base < c1; base += 8 * 64) {
       uint32_t kk[8];
 #pragma unroll
@@ -313,13 +319,34 @@ __global__ void __launch_bounds__(kDecThreads, 2) decode_scan_kernel(const Decod
         const bool keep = e < c1 && (kk[u] >> 8) >= keep_from;
         const uint64_t km = ballot(keep);
         if (keep) {
-          const int p = pos + rank_below(km);
-          args.cl_idx[sbase + p] = (int32_t)(blk0 + e);
-          args.cl_sc[sbase + p] = key_to_float(kk[u]);
+          const int p = nst + rank_below(km);
+          stg_sc[p] = __float_as_uint(key_to_float(kk[u]));
+          stg_ix[p] = (int32_t)(blk0 + e);
         }
-        pos += popc(km);
+        nst += popc(km);
+        if (nst >= 64) {  // a whole wave's worth: store it, keep the rest
+          wave_lds_sync();
+          args.cl_sc[sbase + pos + l] = __uint_as_float(stg_sc[l]);
+          args.cl_idx[sbase + pos + l] = stg_ix[l];
+          const uint32_t rs = stg_sc[64 + l];
+          const int32_t ri = stg_ix[64 + l];
+          wave_lds_sync();
+          if (l < nst - 64) {
+            stg_sc[l] = rs;
+            stg_ix[l] = ri;
+          }
+          pos += 64;
+          nst -= 64;
+          wave_lds_sync();
+        }
       }
     }
+    wave_lds_sync();
+    if (l < nst) {
+      args.cl_sc[sbase + pos + l] = __uint_as_float(stg_sc[l]);
+      args.cl_idx[sbase + pos + l] = stg_ix[l];
+    }
+    pos += nst;
     if (l == 0) args.cl_cnt[((int64_t)b * args.nblk + blockIdx.x) * kDecListSegs + wave] = pos;
     if (R > 1) __syncthreads();  // s_tmp, s_res and the histogram serve the next row
   }
