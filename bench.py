@@ -199,10 +199,39 @@ def bench_prefill(dsa, args, log):
                              avg_launch_ms=float(launch_ms.mean()),
                              flops_per_launch=flops / nchunks,
                              traffic=_traffic("dense_topk_fp8_prefill128k")))
+    # the sustained matrix-core stream, right after the prefill (same clocks
+    # and temperature)
+    res["mfma_ceiling"] = bench_mfma_probe(dsa, log)
+    res["mfma_ceiling"]["dense_frac_of_ceiling"] = achieved / res["mfma_ceiling"]["tflops"]
     cpu = None
     if not args.no_cpu:
         cpu = cpu_prefill(wl, out, args, log)
     return res, cpu
+
+
+def bench_mfma_probe(dsa, log):
+    """The E4M3 matrix-core stream (indexer_mfma_probe: back-to-back 32x32x64
+    MFMAs on register operands, four accumulators per wave, one workgroup per
+    CU) at 1, 2 and 4 waves per SIMD, timed with HIP events; the best rate is
+    the sustained ceiling the fp8 prefill kernel is compared with.  Each wave's
+    shader-clock and 100 MHz constant-clock counts give the clock it ran at."""
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    log(f"timing the E4M3 MFMA stream on {ncu} CUs")
+    by_wps = {}
+    for wps in (1, 2, 4):
+        iters = 24576 // wps
+        out, clocks = dsa.mfma_probe(iters, wps, ncu)
+        _, ms = _timed_calls(lambda: dsa.mfma_probe(iters, wps, ncu, out, clocks), 20, stream)
+        flops = 2.0 * 32 * 32 * 64 * 4 * iters * (ncu * 4 * wps)
+        c = clocks.cpu().numpy().astype(np.float64)
+        mhz = float(np.mean(c[:, 0] / (c[:, 1] / 100.0)))  # counts per microsecond
+        by_wps[wps] = dict(tflops=flops / (ms * 1e-3) / 1e12, ms=ms, shader_clock_mhz=mhz)
+    best = max(by_wps, key=lambda k: by_wps[k]["tflops"])
+    tf = by_wps[best]["tflops"]
+    return dict(kernel="mfma_probe_kernel (indexer_mfma_probe)", tflops=tf, frac_of_peak=tf / PEAK_FP8_TFLOPS,
+                best_waves_per_simd=best,
+                by_waves_per_simd={str(k): {kk: round(vv, 3) for kk, vv in v.items()} for k, v in by_wps.items()})
 
 
 def cpu_prefill(wl, out, args, log):
@@ -880,6 +909,7 @@ def main():
         "gpairs_per_s": pre["gpairs_per_s"],
         "pairs_per_step": pre["pairs_per_step"],
         "roofline": pre["roofline"],
+        "mfma_ceiling": pre["mfma_ceiling"],
         "cpu_baseline": cpu,
     }
     if not args.no_decode:

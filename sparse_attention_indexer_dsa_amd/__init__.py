@@ -28,7 +28,7 @@ __all__ = ["indexer_prefill", "indexer_decode", "indexer_decode_noalloc", "index
            "indexer_layers", "workspace_layers",
            "workspace_prefill", "workspace_decode", "workspace_group_bank", "indexer_mtp", "indexer_mtp_pairs",
            "workspace_mtp", "indexer_group_query", "union_sizes", "topk_overlap", "union_stat", "speedup_joint", "select_setting",
-           "layerwise_speedup", "read_probe", "FORCE_BANK", "POOL_MEAN", "NO_BANK", "lib",
+           "layerwise_speedup", "read_probe", "mfma_probe", "FORCE_BANK", "POOL_MEAN", "NO_BANK", "lib",
            "LIB_PATH"]
 
 FORCE_BANK = DSAIDX_FORCE_BANK
@@ -351,6 +351,22 @@ def read_probe(buf, nblocks=2048, out=None):
     nbytes = buf.numel() * buf.element_size()
     _check(lib().indexer_read_probe(_ptr(buf), nbytes, _ptr(out), nblocks, _stream(dev)), "indexer_read_probe")
     return out
+
+
+def mfma_probe(iters, waves_per_simd, nblocks, out=None, clocks=None, device="cuda"):
+    """Run the E4M3 matrix-core stream (nblocks workgroups of waves_per_simd
+    waves per SIMD, each wave 4 * iters 32x32x64 MFMAs); returns (out, clocks):
+    the lanes' accumulator sums (float32, GPU) and each wave's shader-clock
+    and 100 MHz constant-clock counts around its loop (int64 [waves, 2], GPU)."""
+    waves = nblocks * 4 * waves_per_simd
+    if out is None:
+        out = torch.empty((nblocks * 256 * waves_per_simd,), dtype=torch.float32, device=device)
+    if clocks is None:
+        clocks = torch.empty((waves, 2), dtype=torch.int64, device=out.device)
+    dev = _dev(out, clocks)
+    _check(lib().indexer_mfma_probe(int(iters), int(waves_per_simd), int(nblocks), _ptr(out), _ptr(clocks),
+                                    _stream(dev)), "indexer_mfma_probe")
+    return out, clocks
 
 
 # ------------------------------------------------- group query (Eq. (6)-(7))

@@ -953,6 +953,20 @@ int indexer_read_probe(const void* p, int64_t bytes, uint32_t* out, int nblocks,
   return ok();
 }
 
+int indexer_mfma_probe(int iters, int waves_per_simd, int nblocks, float* out, uint64_t* clocks,
+                       void* stream) {
+  if (iters < 1 || nblocks < 1 || nblocks > 65535)
+    return fail(DSAIDX_ERR_INVALID_ARG, "bad size (iters=%d nblocks=%d)", iters, nblocks);
+  if (waves_per_simd != 1 && waves_per_simd != 2 && waves_per_simd != 4)
+    return fail(DSAIDX_ERR_INVALID_ARG, "waves_per_simd must be 1, 2 or 4 (got %d)", waves_per_simd);
+  if (!out || !clocks) return fail(DSAIDX_ERR_INVALID_ARG, "null out or clocks");
+  if (((uintptr_t)out & 3u) || ((uintptr_t)clocks & 7u))
+    return fail(DSAIDX_ERR_INVALID_ARG, "out must be 4-byte aligned, clocks 8-byte");
+  const hipError_t e = launch_mfma_probe(iters, waves_per_simd, nblocks, out, clocks, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "indexer_mfma_probe launch");
+  return ok();
+}
+
 double indexer_union_stat(const int32_t* sizes, int64_t n, int stat) {
   if (n <= 0 || !sizes || stat < 0 || stat > 2) return -1.0;
   if (stat == 1) {

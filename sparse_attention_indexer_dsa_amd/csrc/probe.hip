@@ -1,7 +1,13 @@
-// probe.hip -- the plain read stream that the memory-bound kernels are
-// measured against: every byte of a buffer read once with coalesced 16-byte
-// loads, eight per lane in flight, and nothing else (an XOR of the words so
-// the loads cannot be dropped; one word per workgroup is written).
+// probe.hip -- the two streams the kernels are measured against:
+//   * the plain read stream (memory-bound kernels): every byte of a buffer
+//     read once with coalesced 16-byte loads, eight per lane in flight, and
+//     nothing else (an XOR of the words so the loads cannot be dropped; one
+//     word per workgroup is written);
+//   * the E4M3 matrix-core stream (the fp8 prefill kernel): back-to-back
+//     32x32x64 E4M3 MFMAs on register operands into kMfmaChains independent
+//     accumulators per wave, no memory traffic in the loop, with each wave's
+//     shader-clock and 100 MHz constant-clock counts around its loop, so a run
+//     gives the sustained rate and the clock the SIMDs ran at.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -45,7 +51,64 @@ __global__ void __launch_bounds__(kProbeThreads) read_probe_kernel(const u32x4* 
   }
 }
 
+constexpr int kMfmaChains = 4;
+constexpr int kMfmaPadWords = 24576;  // 96 KiB of LDS: one workgroup per CU
+
+template <int kWavesPerSimd>
+__global__ void __launch_bounds__(256 * kWavesPerSimd) mfma_probe_kernel(int iters, float* out,
+                                                                           uint64_t* clocks) {
+  __shared__ uint32_t s_pad[kMfmaPadWords];
+  const int tid = threadIdx.x, l = tid & 63;
+  // operands: E4M3 bytes of magnitude below 1 (exponent field < 7), varied
+  // per lane, written through LDS so the allocation stays
+  for (int i = tid; i < kMfmaPadWords; i += blockDim.x) s_pad[i] = ((uint32_t)i * 2654435761u) & 0x37373737u;
+  __syncthreads();
+  v8i a[2], b[2];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    a[0][k] = (int)s_pad[l * 8 + k];
+    a[1][k] = (int)s_pad[512 + l * 8 + k];
+    b[0][k] = (int)s_pad[1024 + l * 8 + k];
+    b[1][k] = (int)s_pad[1536 + l * 8 + k];
+  }
+  v16f acc[kMfmaChains];
+#pragma unroll
+  for (int c = 0; c < kMfmaChains; ++c) acc[c] = v16f{};
+  __syncthreads();
+  const uint64_t c0 = __builtin_amdgcn_s_memtime();
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < kMfmaChains; ++c)
+      acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[c & 1], b[(c >> 1) & 1], acc[c], 0, 0, 0, 0, 0, 0);
+  }
+  const uint64_t c1 = __builtin_amdgcn_s_memtime();
+  const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+  float sum = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kMfmaChains; ++c)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += acc[c][i];
+  out[(int64_t)blockIdx.x * blockDim.x + tid] = sum;
+  if (l == 0) {
+    const int64_t wv = (int64_t)blockIdx.x * (blockDim.x / 64) + (tid >> 6);
+    clocks[2 * wv] = c1 - c0;
+    clocks[2 * wv + 1] = r1 - r0;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_mfma_probe(int iters, int waves_per_simd, int nblocks, float* out, uint64_t* clocks,
+                             hipStream_t stream) {
+  const dim3 grid((unsigned)nblocks), block((unsigned)(256 * waves_per_simd));
+  switch (waves_per_simd) {
+    case 1: hipLaunchKernelGGL(mfma_probe_kernel<1>, grid, block, 0, stream, iters, out, clocks); break;
+    case 2: hipLaunchKernelGGL(mfma_probe_kernel<2>, grid, block, 0, stream, iters, out, clocks); break;
+    default: hipLaunchKernelGGL(mfma_probe_kernel<4>, grid, block, 0, stream, iters, out, clocks); break;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_read_probe(const void* p, int64_t bytes, uint32_t* out, int nblocks, hipStream_t stream) {
   const int64_t n16 = bytes / 16;

@@ -35,7 +35,7 @@ A = P(1 << 20)  # 16-byte aligned
 def test_header_symbols_exported(L):
     names = re.findall(r"^\s*(?:[\w\s\*]+?)\b(indexer_\w+)\s*\(", open(HEADER).read(), re.M)
     names = sorted(set(names))
-    assert len(names) == 24, names
+    assert len(names) == 25, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -254,6 +254,16 @@ def test_read_probe_rejects(L):
     assert L.indexer_read_probe(P((1 << 20) + 4), 64, A, 8, None) == INVALID
     assert L.indexer_read_probe(A, -1, A, 8, None) == INVALID
     assert L.indexer_read_probe(A, 64, None, 8, None) == INVALID
+
+
+def test_mfma_probe_rejects(L):
+    assert L.indexer_mfma_probe(0, 1, 256, A, A, None) == INVALID
+    assert L.indexer_mfma_probe(16, 3, 256, A, A, None) == INVALID
+    assert L.indexer_mfma_probe(16, 1, 0, A, A, None) == INVALID
+    assert L.indexer_mfma_probe(16, 1, 65536, A, A, None) == INVALID
+    assert L.indexer_mfma_probe(16, 1, 256, None, A, None) == INVALID
+    assert L.indexer_mfma_probe(16, 1, 256, A, P(A.value + 4), None) == INVALID
+    assert "clocks" in L.indexer_last_error().decode()
 
 
 def test_decode_noalloc_refuses_beyond_its_scratch(L):

@@ -1,0 +1,73 @@
+"""The two measurement probes through the C ABI: the read stream returns the
+XOR of every word it read, and the E4M3 matrix-core stream's accumulator sums
+equal the sums of the products of its operands (so the rate it reports is a
+rate of real 32x32x64 MFMAs)."""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_attention_indexer_dsa_amd as m
+    m.lib()
+    return m
+
+
+@pytest.mark.parametrize("nbytes,nblocks", [(1 << 20, 7), ((1 << 20) + 13, 64), (100, 3)])
+def test_read_probe_xor(dsa, nbytes, nblocks):
+    rng = np.random.default_rng(nbytes)
+    host = rng.integers(0, 256, nbytes, dtype=np.uint8)
+    buf = torch.from_numpy(host).cuda()
+    out = dsa.read_probe(buf, nblocks)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
+    n16 = nbytes // 16
+    words = host[:n16 * 16].view(np.uint32)
+    want = np.bitwise_xor.reduce(words) if words.size else np.uint32(0)
+    want ^= np.bitwise_xor.reduce(host[n16 * 16:].astype(np.uint32)) if nbytes % 16 else np.uint32(0)
+    assert int(got) == int(want)
+
+
+def _operand_bytes():
+    """The probe's operand words, word i = (i * 2654435761 mod 2^32) with each
+    byte's E4M3 exponent field cut below 7, as E4M3 values [4 operands, 64
+    lanes, 32 bytes]: a0, a1, b0, b1."""
+    i = np.arange(2048, dtype=np.uint64)
+    words = ((i * np.uint64(2654435761)) & np.uint64(0xFFFFFFFF)).astype(np.uint32) & np.uint32(0x37373737)
+    vals = torch.from_numpy(words.view(np.uint8).copy()).view(torch.float8_e4m3fn).float().numpy()
+    return vals.reshape(4, 64, 32).astype(np.float64)
+
+
+@pytest.mark.parametrize("wps", [1, 2, 4])
+def test_mfma_probe_sums(dsa, wps):
+    """A wave's 64 lane sums add up to the sum of all entries of its four
+    accumulators, iters * sum over chains of sum_k colsum(A)[k] * rowsum(B)[k]:
+    lane l holds row (A) or column (B) l % 32 and the k block l // 32."""
+    ops = _operand_bytes()
+    chains = [(0, 2), (1, 2), (0, 3), (1, 3)]  # (a, b) operand of accumulator c
+    per_iter = 0.0
+    for a, b in chains:
+        for h in range(2):
+            sa = ops[a, 32 * h:32 * h + 32].sum(axis=0)
+            sb = ops[b, 32 * h:32 * h + 32].sum(axis=0)
+            per_iter += float(sa @ sb)
+    nblocks = 5
+    for iters in (1, 3):
+        out, clocks = dsa.mfma_probe(iters, wps, nblocks)
+        torch.cuda.synchronize()
+        lanes = out.cpu().numpy().astype(np.float64).reshape(nblocks * 4 * wps, 64)
+        # the matrix core sums 64 products per entry and the kernel 64 entries
+        # per lane in fp32: agreement to 1e-4 shows the products were all taken
+        np.testing.assert_allclose(lanes.sum(axis=1), iters * per_iter, rtol=1e-4)
+        c = clocks.cpu().numpy()
+        assert c.shape == (nblocks * 4 * wps, 2) and (c > 0).all()
+
+
+def test_mfma_probe_rejects(dsa):
+    with pytest.raises(Exception):
+        dsa.mfma_probe(8, 3, 4)
