@@ -212,26 +212,39 @@ def bench_prefill(dsa, args, log):
 def bench_mfma_probe(dsa, log):
     """The E4M3 matrix-core stream (indexer_mfma_probe: back-to-back 32x32x64
     MFMAs on register operands, four accumulators per wave, one workgroup per
-    CU) at 1, 2 and 4 waves per SIMD, timed with HIP events; the best rate is
-    the sustained ceiling the fp8 prefill kernel is compared with.  Each wave's
-    shader-clock and 100 MHz constant-clock counts give the clock it ran at."""
+    CU) at 1, 2 and 4 waves per SIMD, timed with HIP events, for two operand
+    distributions: bytes spanning the whole E4M3 range with random signs (like
+    the prefill's E4M3 q and k) and small positive magnitudes.  The chip's
+    power limit makes the sustained rate depend on the data; the best rate on
+    whole-range operands is the ceiling the fp8 prefill kernel is compared
+    with.  Each wave's shader-clock and 100 MHz constant-clock counts give the
+    clock it ran at."""
     ncu = torch.cuda.get_device_properties(0).multi_processor_count
     stream = torch.cuda.current_stream()
     log(f"timing the E4M3 MFMA stream on {ncu} CUs")
-    by_wps = {}
-    for wps in (1, 2, 4):
-        iters = 24576 // wps
-        out, clocks = dsa.mfma_probe(iters, wps, ncu)
-        _, ms = _timed_calls(lambda: dsa.mfma_probe(iters, wps, ncu, out, clocks), 20, stream)
-        flops = 2.0 * 32 * 32 * 64 * 4 * iters * (ncu * 4 * wps)
-        c = clocks.cpu().numpy().astype(np.float64)
-        mhz = float(np.mean(c[:, 0] / (c[:, 1] / 100.0)))  # counts per microsecond
-        by_wps[wps] = dict(tflops=flops / (ms * 1e-3) / 1e12, ms=ms, shader_clock_mhz=mhz)
-    best = max(by_wps, key=lambda k: by_wps[k]["tflops"])
-    tf = by_wps[best]["tflops"]
-    return dict(kernel="mfma_probe_kernel (indexer_mfma_probe)", tflops=tf, frac_of_peak=tf / PEAK_FP8_TFLOPS,
-                best_waves_per_simd=best,
-                by_waves_per_simd={str(k): {kk: round(vv, 3) for kk, vv in v.items()} for k, v in by_wps.items()})
+
+    def sweep(mask):
+        by_wps = {}
+        for wps in (1, 2, 4):
+            iters = 24576 // wps
+            out, clocks = dsa.mfma_probe(iters, wps, ncu, mask)
+            _, ms = _timed_calls(lambda: dsa.mfma_probe(iters, wps, ncu, mask, out, clocks), 20, stream)
+            flops = 2.0 * 32 * 32 * 64 * 4 * iters * (ncu * 4 * wps)
+            c = clocks.cpu().numpy().astype(np.float64)
+            mhz = float(np.mean(c[:, 0] / (c[:, 1] / 100.0)))  # counts per microsecond
+            by_wps[wps] = dict(tflops=flops / (ms * 1e-3) / 1e12, ms=ms, shader_clock_mhz=mhz)
+        best = max(by_wps, key=lambda k: by_wps[k]["tflops"])
+        return by_wps[best]["tflops"], best, {str(k): {kk: round(vv, 3) for kk, vv in v.items()}
+                                              for k, v in by_wps.items()}
+
+    tf, best, by = sweep(0xFEFEFEFE)
+    tf_low, best_low, by_low = sweep(0x37373737)
+    return dict(kernel="mfma_probe_kernel (indexer_mfma_probe)", operands="whole E4M3 range, random signs "
+                "(operand_mask 0xFEFEFEFE)", tflops=tf, frac_of_peak=tf / PEAK_FP8_TFLOPS, best_waves_per_simd=best,
+                by_waves_per_simd=by,
+                small_operands=dict(operands="magnitudes below 1, positive (operand_mask 0x37373737)", tflops=tf_low,
+                                    frac_of_peak=tf_low / PEAK_FP8_TFLOPS, best_waves_per_simd=best_low,
+                                    by_waves_per_simd=by_low))
 
 
 def cpu_prefill(wl, out, args, log):

@@ -353,19 +353,20 @@ def read_probe(buf, nblocks=2048, out=None):
     return out
 
 
-def mfma_probe(iters, waves_per_simd, nblocks, out=None, clocks=None, device="cuda"):
+def mfma_probe(iters, waves_per_simd, nblocks, operand_mask=0x37373737, out=None, clocks=None, device="cuda"):
     """Run the E4M3 matrix-core stream (nblocks workgroups of waves_per_simd
-    waves per SIMD, each wave 4 * iters 32x32x64 MFMAs); returns (out, clocks):
-    the lanes' accumulator sums (float32, GPU) and each wave's shader-clock
-    and 100 MHz constant-clock counts around its loop (int64 [waves, 2], GPU)."""
+    waves per SIMD, each wave 4 * iters 32x32x64 MFMAs on operand bytes under
+    operand_mask); returns (out, clocks): the lanes' accumulator sums
+    (float32, GPU) and each wave's shader-clock and 100 MHz constant-clock
+    counts around its loop (int64 [waves, 2], GPU)."""
     waves = nblocks * 4 * waves_per_simd
     if out is None:
         out = torch.empty((nblocks * 256 * waves_per_simd,), dtype=torch.float32, device=device)
     if clocks is None:
         clocks = torch.empty((waves, 2), dtype=torch.int64, device=out.device)
     dev = _dev(out, clocks)
-    _check(lib().indexer_mfma_probe(int(iters), int(waves_per_simd), int(nblocks), _ptr(out), _ptr(clocks),
-                                    _stream(dev)), "indexer_mfma_probe")
+    _check(lib().indexer_mfma_probe(int(iters), int(waves_per_simd), int(nblocks), int(operand_mask), _ptr(out),
+                                    _ptr(clocks), _stream(dev)), "indexer_mfma_probe")
     return out, clocks
 
 

@@ -7,7 +7,9 @@
 //     32x32x64 E4M3 MFMAs on register operands into kMfmaChains independent
 //     accumulators per wave, no memory traffic in the loop, with each wave's
 //     shader-clock and 100 MHz constant-clock counts around its loop, so a run
-//     gives the sustained rate and the clock the SIMDs ran at.
+//     gives the sustained rate and the clock the SIMDs ran at.  The operand
+//     bytes' mask sets how much of the E4M3 range they span: the chip's power
+//     limit makes the sustained rate depend on the data.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -54,14 +56,23 @@ __global__ void __launch_bounds__(kProbeThreads) read_probe_kernel(const u32x4* 
 constexpr int kMfmaChains = 4;
 constexpr int kMfmaPadWords = 24576;  // 96 KiB of LDS: one workgroup per CU
 
+// Operand word i of the probe: a 32-bit mix of i, masked.
+__device__ __forceinline__ uint32_t probe_word(uint32_t i, uint32_t mask) {
+  uint32_t h = i * 0x9E3779B1u;
+  h ^= h >> 15;
+  h *= 0x85EBCA77u;
+  h ^= h >> 13;
+  return h & mask;
+}
+
 template <int kWavesPerSimd>
-__global__ void __launch_bounds__(256 * kWavesPerSimd) mfma_probe_kernel(int iters, float* out,
+__global__ void __launch_bounds__(256 * kWavesPerSimd) mfma_probe_kernel(int iters, uint32_t mask, float* out,
                                                                            uint64_t* clocks) {
   __shared__ uint32_t s_pad[kMfmaPadWords];
   const int tid = threadIdx.x, l = tid & 63;
-  // operands: E4M3 bytes of magnitude below 1 (exponent field < 7), varied
+  // operands: E4M3 bytes from a mixed index under the caller's mask, varied
   // per lane, written through LDS so the allocation stays
-  for (int i = tid; i < kMfmaPadWords; i += blockDim.x) s_pad[i] = ((uint32_t)i * 2654435761u) & 0x37373737u;
+  for (int i = tid; i < kMfmaPadWords; i += blockDim.x) s_pad[i] = probe_word((uint32_t)i, mask);
   __syncthreads();
   v8i a[2], b[2];
 #pragma unroll
@@ -99,13 +110,13 @@ __global__ void __launch_bounds__(256 * kWavesPerSimd) mfma_probe_kernel(int ite
 
 }  // namespace
 
-hipError_t launch_mfma_probe(int iters, int waves_per_simd, int nblocks, float* out, uint64_t* clocks,
-                             hipStream_t stream) {
+hipError_t launch_mfma_probe(int iters, int waves_per_simd, int nblocks, uint32_t mask, float* out,
+                             uint64_t* clocks, hipStream_t stream) {
   const dim3 grid((unsigned)nblocks), block((unsigned)(256 * waves_per_simd));
   switch (waves_per_simd) {
-    case 1: hipLaunchKernelGGL(mfma_probe_kernel<1>, grid, block, 0, stream, iters, out, clocks); break;
-    case 2: hipLaunchKernelGGL(mfma_probe_kernel<2>, grid, block, 0, stream, iters, out, clocks); break;
-    default: hipLaunchKernelGGL(mfma_probe_kernel<4>, grid, block, 0, stream, iters, out, clocks); break;
+    case 1: hipLaunchKernelGGL(mfma_probe_kernel<1>, grid, block, 0, stream, iters, mask, out, clocks); break;
+    case 2: hipLaunchKernelGGL(mfma_probe_kernel<2>, grid, block, 0, stream, iters, mask, out, clocks); break;
+    default: hipLaunchKernelGGL(mfma_probe_kernel<4>, grid, block, 0, stream, iters, mask, out, clocks); break;
   }
   return hipGetLastError();
 }

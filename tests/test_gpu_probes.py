@@ -33,22 +33,26 @@ def test_read_probe_xor(dsa, nbytes, nblocks):
     assert int(got) == int(want)
 
 
-def _operand_bytes():
-    """The probe's operand words, word i = (i * 2654435761 mod 2^32) with each
-    byte's E4M3 exponent field cut below 7, as E4M3 values [4 operands, 64
-    lanes, 32 bytes]: a0, a1, b0, b1."""
-    i = np.arange(2048, dtype=np.uint64)
-    words = ((i * np.uint64(2654435761)) & np.uint64(0xFFFFFFFF)).astype(np.uint32) & np.uint32(0x37373737)
+def _operand_bytes(mask):
+    """The probe's operand words (a 32-bit mix of the word index under mask)
+    as E4M3 values [4 operands, 64 lanes, 32 bytes]: a0, a1, b0, b1."""
+    h = np.arange(2048, dtype=np.uint32)
+    with np.errstate(over="ignore"):
+        h = h * np.uint32(0x9E3779B1)
+        h ^= h >> np.uint32(15)
+        h = h * np.uint32(0x85EBCA77)
+        h ^= h >> np.uint32(13)
+    words = h & np.uint32(mask)
     vals = torch.from_numpy(words.view(np.uint8).copy()).view(torch.float8_e4m3fn).float().numpy()
     return vals.reshape(4, 64, 32).astype(np.float64)
 
 
-@pytest.mark.parametrize("wps", [1, 2, 4])
-def test_mfma_probe_sums(dsa, wps):
+@pytest.mark.parametrize("wps,mask", [(1, 0x37373737), (2, 0x37373737), (4, 0x37373737), (2, 0x3E3E3E3E)])
+def test_mfma_probe_sums(dsa, wps, mask):
     """A wave's 64 lane sums add up to the sum of all entries of its four
     accumulators, iters * sum over chains of sum_k colsum(A)[k] * rowsum(B)[k]:
     lane l holds row (A) or column (B) l % 32 and the k block l // 32."""
-    ops = _operand_bytes()
+    ops = _operand_bytes(mask)
     chains = [(0, 2), (1, 2), (0, 3), (1, 3)]  # (a, b) operand of accumulator c
     per_iter = 0.0
     for a, b in chains:
@@ -58,7 +62,7 @@ def test_mfma_probe_sums(dsa, wps):
             per_iter += float(sa @ sb)
     nblocks = 5
     for iters in (1, 3):
-        out, clocks = dsa.mfma_probe(iters, wps, nblocks)
+        out, clocks = dsa.mfma_probe(iters, wps, nblocks, mask)
         torch.cuda.synchronize()
         lanes = out.cpu().numpy().astype(np.float64).reshape(nblocks * 4 * wps, 64)
         # the matrix core sums 64 products per entry and the kernel 64 entries
@@ -71,3 +75,5 @@ def test_mfma_probe_sums(dsa, wps):
 def test_mfma_probe_rejects(dsa):
     with pytest.raises(Exception):
         dsa.mfma_probe(8, 3, 4)
+    with pytest.raises(Exception):
+        dsa.mfma_probe(8, 1, 4, 0xFFFFFFFF)
