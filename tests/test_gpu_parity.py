@@ -352,6 +352,15 @@ def test_decode_many_rows(dsa):
     _decode_check(dsa, wl)
 
 
+def test_decode_rows_of_one_span(dsa):
+    """500 ragged rows of one scan span each (0 to 600 keys, top-200): empty
+    rows, rows of at most K keys, and rows whose only span's list is the
+    whole selection."""
+    lens = [(53 * b) % 601 for b in range(500)]
+    wl = make_decode(B=500, N=600, H=64, d=128, topk=200, dist="int", seed=16, seq_lens=lens)
+    _decode_check(dsa, wl)
+
+
 def test_decode_small_heads(dsa):
     wl = make_decode(B=3, N=777, H=7, d=64, topk=100, dist="int", seed=14, seq_lens=[777, 100, 99])
     _decode_check(dsa, wl)
