@@ -210,11 +210,13 @@ def bench_prefill(dsa, args, log):
 
 
 def bench_mfma_probe(dsa, log):
-    """The E4M3 matrix-core stream (indexer_mfma_probe: back-to-back 32x32x64
+    """The matrix-core stream (indexer_mfma_probe: back-to-back 32x32x64 E4M3
     MFMAs on register operands, four accumulators per wave, one workgroup per
     CU) at 1, 2 and 4 waves per SIMD, timed with HIP events, for two operand
     distributions: bytes spanning the whole E4M3 range with random signs (like
-    the prefill's E4M3 q and k) and small positive magnitudes.  The chip's
+    the prefill's E4M3 q and k) and small positive magnitudes; and the same
+    stream of 32x32x16 bf16 MFMAs on random signs and mantissas (the bf16
+    paths' ceiling).  The chip's
     power limit makes the sustained rate depend on the data; the best rate on
     whole-range operands is the ceiling the fp8 prefill kernel is compared
     with.  Each wave's shader-clock and 100 MHz constant-clock counts give the
@@ -223,13 +225,14 @@ def bench_mfma_probe(dsa, log):
     stream = torch.cuda.current_stream()
     log(f"timing the E4M3 MFMA stream on {ncu} CUs")
 
-    def sweep(mask):
+    def sweep(mask, dtype="fp8"):
         by_wps = {}
+        kdim = 64 if dtype == "fp8" else 16  # k of one MFMA: 32x32x64 E4M3, 32x32x16 bf16
         for wps in (1, 2, 4):
-            iters = 24576 // wps
-            out, clocks = dsa.mfma_probe(iters, wps, ncu, mask)
-            _, ms = _timed_calls(lambda: dsa.mfma_probe(iters, wps, ncu, mask, out, clocks), 20, stream)
-            flops = 2.0 * 32 * 32 * 64 * 4 * iters * (ncu * 4 * wps)
+            iters = (24576 if dtype == "fp8" else 49152) // wps
+            out, clocks = dsa.mfma_probe(iters, wps, ncu, mask, dtype=dtype)
+            _, ms = _timed_calls(lambda: dsa.mfma_probe(iters, wps, ncu, mask, out, clocks, dtype=dtype), 20, stream)
+            flops = 2.0 * 32 * 32 * kdim * 4 * iters * (ncu * 4 * wps)
             c = clocks.cpu().numpy().astype(np.float64)
             mhz = float(np.mean(c[:, 0] / (c[:, 1] / 100.0)))  # counts per microsecond
             by_wps[wps] = dict(tflops=flops / (ms * 1e-3) / 1e12, ms=ms, shader_clock_mhz=mhz)
@@ -239,12 +242,17 @@ def bench_mfma_probe(dsa, log):
 
     tf, best, by = sweep(0xFEFEFEFE)
     tf_low, best_low, by_low = sweep(0x37373737)
+    tf_bf, best_bf, by_bf = sweep(0xBFFFBFFF, "bf16")
     return dict(kernel="mfma_probe_kernel (indexer_mfma_probe)", operands="whole E4M3 range, random signs "
                 "(operand_mask 0xFEFEFEFE)", tflops=tf, frac_of_peak=tf / PEAK_FP8_TFLOPS, best_waves_per_simd=best,
                 by_waves_per_simd=by,
                 small_operands=dict(operands="magnitudes below 1, positive (operand_mask 0x37373737)", tflops=tf_low,
                                     frac_of_peak=tf_low / PEAK_FP8_TFLOPS, best_waves_per_simd=best_low,
-                                    by_waves_per_simd=by_low))
+                                    by_waves_per_simd=by_low),
+                bf16=dict(kernel="mfma_probe_kernel, 32x32x16 bf16", operands="random signs and mantissas, "
+                          "magnitudes below 2 (operand_mask 0xBFFFBFFF)", tflops=tf_bf,
+                          frac_of_peak=tf_bf / PEAK_BF16_TFLOPS, best_waves_per_simd=best_bf,
+                          by_waves_per_simd=by_bf))
 
 
 def cpu_prefill(wl, out, args, log):
@@ -929,9 +937,13 @@ def main():
         line["decode"] = bench_decode(dsa, args, log)
     if not args.no_dsa16k:
         line["dsa16k"] = bench_dsa16k(dsa, args, log)
+        line["dsa16k"]["roofline"]["frac_of_bf16_ceiling"] = (
+            line["dsa16k"]["roofline"]["achieved"] / pre["mfma_ceiling"]["bf16"]["tflops"])
     dense64k_ms = None
     if not args.no_adindex:
         line["adindex"] = bench_adindex(dsa, args, log)
+        line["adindex"]["roofline"]["frac_of_bf16_ceiling"] = (
+            line["adindex"]["roofline"]["achieved"] / pre["mfma_ceiling"]["bf16"]["tflops"])
         dense64k_ms = line["adindex"].pop("_dense_ms")
     if not args.no_layerwise:
         line["layerwise"] = bench_layerwise(dsa, args, log,

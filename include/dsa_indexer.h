@@ -311,24 +311,27 @@ double indexer_layerwise_speedup(const int *G, const int *P, int nlayers, double
 int indexer_read_probe(const void *p, int64_t bytes, uint32_t *out, int nblocks, void *stream);
 
 /*
- * Measurement aid (not an operation of the pages): the E4M3 matrix-core
- * stream.  nblocks workgroups (1..65535; one per CU when nblocks is at most
- * the CU count, as each holds 96 KiB of LDS) of waves_per_simd (1, 2 or 4)
- * waves per SIMD each run `iters` (>= 1) rounds of four independent 32x32x64
- * E4M3 MFMAs on register operands, with no memory traffic in the loop:
- * 2 * 32 * 32 * 64 * 4 * iters flops per wave.  The operand words are a
- * 32-bit mix of their index (h = i * 0x9E3779B1; h ^= h >> 15;
- * h *= 0x85EBCA77; h ^= h >> 13) ANDed with operand_mask, which must clear a
- * mantissa or an exponent bit of every byte so that no operand is NaN:
- * 0x37373737 gives magnitudes below 1, 0xFEFEFEFE spans the whole E4M3 range
- * (the sustained rate depends on the data through the chip's power limit).
- * out [nblocks * 256 * waves_per_simd] (device) receives each lane's sum of
- * its accumulators; clocks [2 * waves] (device, waves = nblocks * 4 *
- * waves_per_simd) each wave's shader-clock count (s_memtime) and 100 MHz
- * constant-clock count (s_memrealtime) around its loop.  Its rate is the
- * sustained matrix-core ceiling the fp8 prefill kernel is compared with.
+ * Measurement aid (not an operation of the pages): the matrix-core stream.
+ * nblocks workgroups (1..65535; one per CU when nblocks is at most the CU
+ * count, as each holds 96 KiB of LDS) of waves_per_simd (1, 2 or 4) waves per
+ * SIMD each run `iters` (>= 1) rounds of four independent MFMAs on register
+ * operands, with no memory traffic in the loop: 32x32x64 E4M3 MFMAs for
+ * dtype DSAIDX_FP8_E4M3 (2 * 32 * 32 * 64 * 4 * iters flops per wave) or
+ * 32x32x16 bf16 MFMAs for DSAIDX_BF16 (2 * 32 * 32 * 16 * 4 * iters).  The
+ * operand words are a 32-bit mix of their index (h = i * 0x9E3779B1;
+ * h ^= h >> 15; h *= 0x85EBCA77; h ^= h >> 13) ANDed with operand_mask,
+ * which must keep every operand a number: each byte must clear one of its
+ * low seven bits (E4M3), each 16-bit half one of its exponent bits (bf16).
+ * E4M3 0x37373737 gives magnitudes below 1, 0xFEFEFEFE the whole E4M3 range
+ * with random signs; bf16 0xBFFFBFFF random signs and mantissas below 2 in
+ * magnitude.  The sustained rate depends on the data through the chip's
+ * power limit.  out [nblocks * 256 * waves_per_simd] (device) receives each
+ * lane's sum of its accumulators; clocks [2 * waves] (device, waves =
+ * nblocks * 4 * waves_per_simd) each wave's shader-clock count (s_memtime)
+ * and 100 MHz constant-clock count (s_memrealtime) around its loop.  Its rate
+ * is the sustained matrix-core ceiling the prefill kernels are compared with.
  */
-int indexer_mfma_probe(int iters, int waves_per_simd, int nblocks, uint32_t operand_mask, float *out,
+int indexer_mfma_probe(int dtype, int iters, int waves_per_simd, int nblocks, uint32_t operand_mask, float *out,
                        uint64_t *clocks, void *stream);
 
 /* Message describing the calling thread's last non-OK return ("" if none). */

@@ -353,20 +353,23 @@ def read_probe(buf, nblocks=2048, out=None):
     return out
 
 
-def mfma_probe(iters, waves_per_simd, nblocks, operand_mask=0x37373737, out=None, clocks=None, device="cuda"):
-    """Run the E4M3 matrix-core stream (nblocks workgroups of waves_per_simd
-    waves per SIMD, each wave 4 * iters 32x32x64 MFMAs on operand bytes under
-    operand_mask); returns (out, clocks): the lanes' accumulator sums
-    (float32, GPU) and each wave's shader-clock and 100 MHz constant-clock
-    counts around its loop (int64 [waves, 2], GPU)."""
+def mfma_probe(iters, waves_per_simd, nblocks, operand_mask=0x37373737, out=None, clocks=None, device="cuda",
+               dtype="fp8"):
+    """Run the matrix-core stream (nblocks workgroups of waves_per_simd waves
+    per SIMD, each wave 4 * iters 32x32x64 E4M3 MFMAs, or 32x32x16 bf16 MFMAs
+    for dtype "bf16", on operand words under operand_mask); returns (out,
+    clocks): the lanes' accumulator sums (float32, GPU) and each wave's
+    shader-clock and 100 MHz constant-clock counts around its loop (int64
+    [waves, 2], GPU)."""
     waves = nblocks * 4 * waves_per_simd
     if out is None:
         out = torch.empty((nblocks * 256 * waves_per_simd,), dtype=torch.float32, device=device)
     if clocks is None:
         clocks = torch.empty((waves, 2), dtype=torch.int64, device=out.device)
     dev = _dev(out, clocks)
-    _check(lib().indexer_mfma_probe(int(iters), int(waves_per_simd), int(nblocks), int(operand_mask), _ptr(out),
-                                    _ptr(clocks), _stream(dev)), "indexer_mfma_probe")
+    dt = {"fp8": DSAIDX_FP8_E4M3, "bf16": DSAIDX_BF16}[dtype]
+    _check(lib().indexer_mfma_probe(dt, int(iters), int(waves_per_simd), int(nblocks), int(operand_mask),
+                                    _ptr(out), _ptr(clocks), _stream(dev)), "indexer_mfma_probe")
     return out, clocks
 
 

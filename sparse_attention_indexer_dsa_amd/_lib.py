@@ -57,7 +57,7 @@ SIGNATURES = {
     "indexer_select_setting": (_I, [_P, _D, _I, _I, _D, _P, _P]),
     "indexer_layerwise_speedup": (_D, [_P, _P, _I, _D, _I, _I, _D]),
     "indexer_read_probe": (_I, [_P, _I64, _P, _I, _P]),
-    "indexer_mfma_probe": (_I, [_I, _I, _I, ctypes.c_uint32, _P, _P, _P]),
+    "indexer_mfma_probe": (_I, [_I, _I, _I, _I, ctypes.c_uint32, _P, _P, _P]),
     "indexer_last_error": (ctypes.c_char_p, []),
 }
 

@@ -953,8 +953,10 @@ int indexer_read_probe(const void* p, int64_t bytes, uint32_t* out, int nblocks,
   return ok();
 }
 
-int indexer_mfma_probe(int iters, int waves_per_simd, int nblocks, uint32_t operand_mask, float* out,
+int indexer_mfma_probe(int dtype, int iters, int waves_per_simd, int nblocks, uint32_t operand_mask, float* out,
                        uint64_t* clocks, void* stream) {
+  if (dtype != DSAIDX_BF16 && dtype != DSAIDX_FP8_E4M3)
+    return fail(DSAIDX_ERR_INVALID_ARG, "dtype %d is not DSAIDX_BF16 or DSAIDX_FP8_E4M3", dtype);
   if (iters < 1 || nblocks < 1 || nblocks > 65535)
     return fail(DSAIDX_ERR_INVALID_ARG, "bad size (iters=%d nblocks=%d)", iters, nblocks);
   if (waves_per_simd != 1 && waves_per_simd != 2 && waves_per_simd != 4)
@@ -962,13 +964,23 @@ int indexer_mfma_probe(int iters, int waves_per_simd, int nblocks, uint32_t oper
   if (!out || !clocks) return fail(DSAIDX_ERR_INVALID_ARG, "null out or clocks");
   if (((uintptr_t)out & 3u) || ((uintptr_t)clocks & 7u))
     return fail(DSAIDX_ERR_INVALID_ARG, "out must be 4-byte aligned, clocks 8-byte");
-  // E4M3 NaN is S.1111.111: each mask byte must clear one of the low seven
-  // bits, so that every operand is a number
-  for (int k = 0; k < 4; ++k)
-    if (((operand_mask >> (8 * k)) & 0x7Fu) == 0x7Fu)
-      return fail(DSAIDX_ERR_INVALID_ARG, "operand_mask 0x%08x lets E4M3 NaN bytes through", operand_mask);
+  if (dtype == DSAIDX_FP8_E4M3) {
+    // E4M3 NaN is S.1111.111: each mask byte must clear one of the low seven
+    // bits, so that every operand is a number
+    for (int k = 0; k < 4; ++k)
+      if (((operand_mask >> (8 * k)) & 0x7Fu) == 0x7Fu)
+        return fail(DSAIDX_ERR_INVALID_ARG, "operand_mask 0x%08x lets E4M3 NaN bytes through", operand_mask);
+  } else {
+    // bf16 infinities and NaNs have every exponent bit set: each mask half
+    // must clear one of them
+    for (int k = 0; k < 2; ++k)
+      if (((operand_mask >> (16 * k)) & 0x7F80u) == 0x7F80u)
+        return fail(DSAIDX_ERR_INVALID_ARG, "operand_mask 0x%08x lets bf16 infinities and NaNs through",
+                    operand_mask);
+  }
+  // the kernels' dtype codes are the ABI's (bf16 1, E4M3 2)
   const hipError_t e =
-      launch_mfma_probe(iters, waves_per_simd, nblocks, operand_mask, out, clocks, (hipStream_t)stream);
+      launch_mfma_probe(dtype, iters, waves_per_simd, nblocks, operand_mask, out, clocks, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "indexer_mfma_probe launch");
   return ok();
 }

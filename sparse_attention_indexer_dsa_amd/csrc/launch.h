@@ -169,7 +169,7 @@ hipError_t launch_topk_overlap(const int32_t* a, const int32_t* b, int64_t n, in
 // Read `bytes` bytes at p once (coalesced 16-byte loads); out [nblocks] gets
 // one XOR word per workgroup.
 hipError_t launch_read_probe(const void* p, int64_t bytes, uint32_t* out, int nblocks, hipStream_t stream);
-hipError_t launch_mfma_probe(int iters, int waves_per_simd, int nblocks, uint32_t mask, float* out,
+hipError_t launch_mfma_probe(int dtype, int iters, int waves_per_simd, int nblocks, uint32_t mask, float* out,
                              uint64_t* clocks, hipStream_t stream);
 
 // Set the calling thread's last-error message (indexer_last_error) and return

@@ -3,17 +3,18 @@
 //     read once with coalesced 16-byte loads, eight per lane in flight, and
 //     nothing else (an XOR of the words so the loads cannot be dropped; one
 //     word per workgroup is written);
-//   * the E4M3 matrix-core stream (the fp8 prefill kernel): back-to-back
-//     32x32x64 E4M3 MFMAs on register operands into kMfmaChains independent
+//   * the matrix-core stream (the prefill kernels): back-to-back 32x32x64
+//     E4M3 or 32x32x16 bf16 MFMAs on register operands into kMfmaChains independent
 //     accumulators per wave, no memory traffic in the loop, with each wave's
 //     shader-clock and 100 MHz constant-clock counts around its loop, so a run
 //     gives the sustained rate and the clock the SIMDs ran at.  The operand
-//     bytes' mask sets how much of the E4M3 range they span: the chip's power
-//     limit makes the sustained rate depend on the data.
+//     words' mask sets how much of the number range they span: the chip's
+//     power limit makes the sustained rate depend on the data.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "device.h"
+#include "dsa_indexer.h"
 #include "launch.h"
 
 namespace dsaidx {
@@ -65,18 +66,22 @@ __device__ __forceinline__ uint32_t probe_word(uint32_t i, uint32_t mask) {
   return h & mask;
 }
 
-template <int kWavesPerSimd>
+template <int kWavesPerSimd, int DT>
 __global__ void __launch_bounds__(256 * kWavesPerSimd) mfma_probe_kernel(int iters, uint32_t mask, float* out,
                                                                            uint64_t* clocks) {
   __shared__ uint32_t s_pad[kMfmaPadWords];
   const int tid = threadIdx.x, l = tid & 63;
-  // operands: E4M3 bytes from a mixed index under the caller's mask, varied
-  // per lane, written through LDS so the allocation stays
+  // operands: E4M3 bytes or bf16 halves from a mixed index under the
+  // caller's mask, varied per lane, written through LDS so the allocation
+  // stays
   for (int i = tid; i < kMfmaPadWords; i += blockDim.x) s_pad[i] = probe_word((uint32_t)i, mask);
   __syncthreads();
-  v8i a[2], b[2];
+  // E4M3: 32x32x64 on 8-word operands; bf16: 32x32x16 on 4-word operands
+  constexpr int kW = DT == kFP8 ? 8 : 4;
+  typedef int vw __attribute__((ext_vector_type(kW)));
+  vw a[2], b[2];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
+  for (int k = 0; k < kW; ++k) {
     a[0][k] = (int)s_pad[l * 8 + k];
     a[1][k] = (int)s_pad[512 + l * 8 + k];
     b[0][k] = (int)s_pad[1024 + l * 8 + k];
@@ -90,8 +95,13 @@ __global__ void __launch_bounds__(256 * kWavesPerSimd) mfma_probe_kernel(int ite
   const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int c = 0; c < kMfmaChains; ++c)
-      acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[c & 1], b[(c >> 1) & 1], acc[c], 0, 0, 0, 0, 0, 0);
+    for (int c = 0; c < kMfmaChains; ++c) {
+      if constexpr (DT == kFP8)
+        acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[c & 1], b[(c >> 1) & 1], acc[c], 0, 0, 0, 0, 0, 0);
+      else
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a[c & 1]),
+                                                         __builtin_bit_cast(v8bf, b[(c >> 1) & 1]), acc[c], 0, 0, 0);
+    }
   }
   const uint64_t c1 = __builtin_amdgcn_s_memtime();
   const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
@@ -108,17 +118,26 @@ __global__ void __launch_bounds__(256 * kWavesPerSimd) mfma_probe_kernel(int ite
   }
 }
 
-}  // namespace
-
-hipError_t launch_mfma_probe(int iters, int waves_per_simd, int nblocks, uint32_t mask, float* out,
-                             uint64_t* clocks, hipStream_t stream) {
+template <int DT>
+hipError_t launch_mfma_probe_dt(int iters, int waves_per_simd, int nblocks, uint32_t mask, float* out,
+                                uint64_t* clocks, hipStream_t stream) {
   const dim3 grid((unsigned)nblocks), block((unsigned)(256 * waves_per_simd));
   switch (waves_per_simd) {
-    case 1: hipLaunchKernelGGL(mfma_probe_kernel<1>, grid, block, 0, stream, iters, mask, out, clocks); break;
-    case 2: hipLaunchKernelGGL(mfma_probe_kernel<2>, grid, block, 0, stream, iters, mask, out, clocks); break;
-    default: hipLaunchKernelGGL(mfma_probe_kernel<4>, grid, block, 0, stream, iters, mask, out, clocks); break;
+    case 1: hipLaunchKernelGGL((mfma_probe_kernel<1, DT>), grid, block, 0, stream, iters, mask, out, clocks); break;
+    case 2: hipLaunchKernelGGL((mfma_probe_kernel<2, DT>), grid, block, 0, stream, iters, mask, out, clocks); break;
+    default: hipLaunchKernelGGL((mfma_probe_kernel<4, DT>), grid, block, 0, stream, iters, mask, out, clocks); break;
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+static_assert(kFP8 == DSAIDX_FP8_E4M3 && kBF16 == DSAIDX_BF16, "the probe takes the ABI's dtype codes");
+
+hipError_t launch_mfma_probe(int dtype, int iters, int waves_per_simd, int nblocks, uint32_t mask, float* out,
+                             uint64_t* clocks, hipStream_t stream) {
+  return dtype == kFP8 ? launch_mfma_probe_dt<kFP8>(iters, waves_per_simd, nblocks, mask, out, clocks, stream)
+                       : launch_mfma_probe_dt<kBF16>(iters, waves_per_simd, nblocks, mask, out, clocks, stream);
 }
 
 hipError_t launch_read_probe(const void* p, int64_t bytes, uint32_t* out, int nblocks, hipStream_t stream) {

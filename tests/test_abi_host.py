@@ -258,17 +258,22 @@ def test_read_probe_rejects(L):
 
 def test_mfma_probe_rejects(L):
     M = 0x37373737
-    assert L.indexer_mfma_probe(0, 1, 256, M, A, A, None) == INVALID
-    assert L.indexer_mfma_probe(16, 3, 256, M, A, A, None) == INVALID
-    assert L.indexer_mfma_probe(16, 1, 0, M, A, A, None) == INVALID
-    assert L.indexer_mfma_probe(16, 1, 65536, M, A, A, None) == INVALID
-    assert L.indexer_mfma_probe(16, 1, 256, M, None, A, None) == INVALID
-    assert L.indexer_mfma_probe(16, 1, 256, M, A, P(A.value + 4), None) == INVALID
+    assert L.indexer_mfma_probe(FP8, 0, 1, 256, M, A, A, None) == INVALID
+    assert L.indexer_mfma_probe(FP8, 16, 3, 256, M, A, A, None) == INVALID
+    assert L.indexer_mfma_probe(FP8, 16, 1, 0, M, A, A, None) == INVALID
+    assert L.indexer_mfma_probe(FP8, 16, 1, 65536, M, A, A, None) == INVALID
+    assert L.indexer_mfma_probe(FP8, 16, 1, 256, M, None, A, None) == INVALID
+    assert L.indexer_mfma_probe(FP8, 16, 1, 256, M, A, P(A.value + 4), None) == INVALID
     assert "clocks" in L.indexer_last_error().decode()
+    assert L.indexer_mfma_probe(7, 16, 1, 256, M, A, A, None) == INVALID
     # a mask byte that keeps the low seven bits lets E4M3 NaN (S.1111.111) through
     for bad in (0xFFFFFFFF, 0x7F000000, 0x0000007F, 0xFEFE7FFE):
-        assert L.indexer_mfma_probe(16, 1, 256, bad, A, A, None) == INVALID
+        assert L.indexer_mfma_probe(FP8, 16, 1, 256, bad, A, A, None) == INVALID
         assert "NaN" in L.indexer_last_error().decode()
+    # a mask half that keeps every exponent bit lets bf16 infinities and NaNs through
+    for bad in (0xFFFFFFFF, 0x7F800000, 0x00007F80, 0xBFFF7F80):
+        assert L.indexer_mfma_probe(BF16, 16, 1, 256, bad, A, A, None) == INVALID
+        assert "bf16" in L.indexer_last_error().decode()
 
 
 def test_decode_noalloc_refuses_beyond_its_scratch(L):
