@@ -361,6 +361,18 @@ def test_decode_rows_of_one_span(dsa):
     _decode_check(dsa, wl)
 
 
+def test_decode_lengths_clamped(dsa):
+    """Lengths outside [0, Nmax] are clamped on the device: -3 acts as 0 and
+    Nmax + 100 as Nmax (the oracle takes the clamped lengths)."""
+    wl = make_decode(B=4, N=500, H=64, d=128, topk=64, dist="int", seed=17, seq_lens=[0, 500, 250, 7])
+    t = {k: v.cuda() for k, v in wl.tensors.items()}
+    lens = torch.tensor([-3, 600, 250, 7], dtype=torch.int32, device="cuda")
+    gi, gs = dsa.indexer_decode(t["q"], t["k_cache"], t["k_scale"], t["w"], lens, 64)
+    torch.cuda.synchronize()
+    ri, rs = oracle.decode(wl["q"], wl["k_cache"], wl["k_scale"], wl["w"], wl["seq_lens"], 64)
+    compare(_np(gi), _np(gs), ri, rs, True)
+
+
 def test_decode_small_heads(dsa):
     wl = make_decode(B=3, N=777, H=7, d=64, topk=100, dist="int", seed=14, seq_lens=[777, 100, 99])
     _decode_check(dsa, wl)
