@@ -5,6 +5,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -58,6 +59,9 @@ int cap_for(int K) { return (2 * K + 2048 + 63) / 64 * 64; }
 
 size_t cand_bytes_cap(int64_t rows, int cap) { return 2 * align_up((size_t)rows * (size_t)cap * 4u); }
 size_t cand_bytes(int64_t rows, int K) { return cand_bytes_cap(rows, cap_for(K)); }
+// the dense E4M3 kernel's sampled start: a start per row and a flag per
+// workgroup of 8 rows, after the candidate buffers
+size_t sample_bytes(int64_t rows) { return align_up((size_t)rows * 4u) + align_up((size_t)(rows + 7) / 8 * 4u); }
 
 // Group-bank rows whose candidates are bounded by the bank (refinement rows
 // of at most P + G - 1 candidates, fallback rows before the first bank group)
@@ -125,15 +129,25 @@ int check_ws(const void* ws, size_t ws_bytes, size_t need) {
   return DSAIDX_OK;
 }
 
+// The environment variable DSAIDX_SAMPLE_RERUN=1 makes the dense E4M3
+// kernel's sampled start fail on purpose, so that the rows it covers are
+// streamed a second time from -inf: a test of that path (results unchanged).
+static int sample_test_forced() {
+  const char* v = std::getenv("DSAIDX_SAMPLE_RERUN");
+  return v != nullptr && v[0] == '1';
+}
+
 // Dense rows [r0, r1) of a prefill-shaped call, sliced into launches of at
 // most kRowsPerLaunch rows.  Rows whose candidates all fit a buffer of `cap`
 // entries (position + 1 <= cap) get launches of their own, so the dense
 // kernel keeps their whole (short) rows; longer rows stream their top K
-// through the same buffers.
+// through the same buffers.  `sample`: the workspace also holds
+// sample_bytes(rows) after the candidate buffers of `rows` rows (rows >= every
+// launch's n), so that long E4M3 rows can stream from a sampled start.
 hipError_t run_dense(const void* q, const float* q_scale, const void* k, const float* k_scale,
                      const float* w, int dtype, int H, int d, int64_t q_pos0, int64_t r0,
                      int64_t r1, int topk, int cap, int32_t* out_idx, float* out_score, void* ws,
-                     hipStream_t stream) {
+                     hipStream_t stream, bool sample = false) {
   const int rb = row_bytes(dtype, d);
   int64_t split = (int64_t)cap - q_pos0;  // first row with more than cap candidates
   split = split < r0 ? r0 : (split > r1 ? r1 : split);
@@ -159,6 +173,13 @@ hipError_t run_dense(const void* q, const float* q_scale, const void* k, const f
     a.out_idx = out_idx + s * topk;
     a.out_score = out_score ? out_score + s * topk : nullptr;
     a.out_stride = topk;
+    if (sample) {
+      const int64_t rows = r1 - r0 < kRowsPerLaunch ? r1 - r0 : kRowsPerLaunch;
+      uint8_t* sws = (uint8_t*)ws + cand_bytes_cap(rows, cap);
+      a.start = (float*)sws;
+      a.rerun = (int32_t*)(sws + align_up((size_t)rows * 4u));
+      a.sample_test = sample_test_forced();
+    }
     hipError_t e = launch_scan_topk(a, dtype, stream);
     if (e != hipSuccess) return e;
     s += n;
@@ -224,7 +245,7 @@ size_t indexer_prefill_workspace_size(int64_t Tq, int64_t Tk, int H, int d, int 
   (void)Tk; (void)H; (void)d; (void)dtype;
   if (Tq <= 0 || topk <= 0) return 0;
   const int64_t rows = Tq < kRowsPerLaunch ? Tq : kRowsPerLaunch;
-  return cand_bytes(rows, topk);
+  return cand_bytes(rows, topk) + sample_bytes(rows);
 }
 
 int indexer_prefill(const void* q, const float* q_scale, const void* k, const float* k_scale,
@@ -238,7 +259,7 @@ int indexer_prefill(const void* q, const float* q_scale, const void* k, const fl
   if (rc) return rc;
   if (Tq == 0) return ok();
   hipError_t e = run_dense(q, q_scale, k, k_scale, w, dtype, H, d, q_pos0, 0, Tq, topk,
-                           cap_for(topk), out_idx, out_score, ws, (hipStream_t)stream);
+                           cap_for(topk), out_idx, out_score, ws, (hipStream_t)stream, true);
   if (e != hipSuccess) return hip_fail(e, "indexer_prefill launch");
   return ok();
 }
@@ -616,7 +637,7 @@ int indexer_layers(const dsaidx_layer* layers, int nlayers, int dtype, int64_t T
     const dsaidx_layer& L = layers[i];
     if (L.G == 0) {
       hipError_t e = run_dense(L.q, L.q_scale, L.k, L.k_scale, L.w, dtype, H, d, q_pos0, 0, Tq, topk,
-                               cap_for(topk), L.out_idx, L.out_score, ws, st);
+                               cap_for(topk), L.out_idx, L.out_score, ws, st, true);
       if (e != hipSuccess) return hip_fail(e, "indexer_layers launch");
     } else {
       rc = run_group_bank(L.q, L.q_scale, L.k, L.k_scale, L.w, dtype, Tq, H, d, q_pos0, L.qbar, L.qbar_scale,

@@ -52,6 +52,20 @@
 //     them and fetch the listed rows (and fp8 scales) with the same LDS DMA,
 //     and the append stores positions instead of list slots.  The list is
 //     ascending in position, so ties still keep the lower index.
+//   * Sampled start (E4M3 over contiguous keys, rows of 16K candidates and
+//     more): a pre-pass of the same kernel scores, per workgroup, one or two
+//     rounds of the ring of sample keys spread evenly over its shortest row
+//     and gives each query a start that about 3.5 K of its keys beat (the
+//     16-bit key bucket of its m-th best sample).  The stream then keeps
+//     only scores above the start, so far fewer enter the buffer and it is
+//     compacted about once instead of four times.  The top K all lie above
+//     the start whenever at least K entries did; the stream checks that at
+//     its end and flags its workgroup when a query kept fewer, and a third
+//     launch streams the flagged workgroups again from -inf (every other
+//     workgroup of it ends at once), so the result never depends on the
+//     sample.  The start leaves at least 35 samples expected above it, which
+//     makes a flag rarer than one query in 10^9 on i.i.d. scores.  The
+//     stream's own code is the same with or without a start.
 #include "device.h"
 #include "launch.h"
 
@@ -68,10 +82,21 @@ constexpr int kStage = kSelectHistWords / 2;  // LDS append stage entries per wa
 constexpr int kD = 128;
 constexpr int kIdxRing = 8;   // gathering: tiles of bank positions held in LDS
 constexpr int kIdxAhead = 7;  // a tile's positions are requested this many steps before it is scored
+// sampled start: the shortest row that samples, the fewest samples a query
+// expects above its start, and the radix digits of the start's select over
+// the samples' 16-bit keys (a 9-bit digit, then the low 9 bits)
+constexpr int kSampleMinRow = 16384;
+constexpr int kSampleMinAbove = 35;
+constexpr int kSampleBins = 512;
 
 template <int S>
 struct StageC {  // a ring stage as a compile-time constant
   constexpr operator int() const { return S; }
+};
+
+template <bool B>
+struct SampleC {  // whether a step scores sample keys, as a compile-time constant
+  static constexpr bool value = B;
 };
 
 template <int DT, int TK>
@@ -146,7 +171,9 @@ __device__ __forceinline__ void dma_b32(const v4i& rsrc, uint32_t lds, uint32_t 
                :: "v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
 }
 
-template <int DT, bool GATHER, bool FULL>
+// SAMPLE: the sampled start's pre-pass (E4M3 over contiguous keys): the
+// sample tiles only, then each query's start into args.start.
+template <int DT, bool GATHER, bool FULL, bool SAMPLE>
 __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs args) {
   // keys per step: E4M3 scores 128 keys (four 32-key sub-tiles) between
   // barriers, so the step's fixed costs (the compaction check, the waits and
@@ -173,6 +200,7 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   __shared__ __attribute__((aligned(16))) uint16_t s_qt[kWaves][kParts][kD];
   __shared__ float s_qinv[kWaves];
   __shared__ int s_need[2];  // s_need[i & 1] == i: a wave asked for compaction in step i
+  __shared__ int s_rerun;    // sampled start: some query kept fewer than K entries
   // gathering: the bank positions of tiles t .. t+7, slot t & 7 (tile t+7's
   // are requested in step t, read by tile t+4's request and tile t's append)
   __shared__ int32_t s_idx[GATHER ? kIdxRing : 1][kTile];
@@ -205,6 +233,35 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   const int ncand_blk = GATHER ? nbank + (t_hi - anchor) : t_hi + 1;
   const int ncand_me = !active ? 0 : GATHER ? nbank + (pos0 + j - anchor) : pos0 + j * args.pos_stride + 1;
   const int ntiles = (ncand_blk + TK - 1) / TK;
+  // Sampled start.  The stream (E4M3 over contiguous keys) takes its query's
+  // start from args.start when given; its re-stream launch (args.rerun_pass)
+  // runs only the workgroups that the first stream flagged, from -inf.
+  constexpr bool kCertify = TK == 128 && !GATHER && !FULL && !SAMPLE;
+  static_assert(!SAMPLE || (DT == kFP8 && !GATHER && !FULL), "the pre-pass is for E4M3 over contiguous keys");
+  if constexpr (kCertify) {
+    if (args.rerun_pass && args.rerun[blockIdx.x] == 0) return;
+  }
+  // The pre-pass: nsamp sample tiles (one or two rounds of the ring), sample
+  // s at key s * sstride + sstride / 2, all inside the workgroup's shortest
+  // row.  A query's start is its m-th best sample, m = 3.5 K S / ncand + 1 of
+  // the S samples; the round count is the least that gives every query of
+  // the workgroup m >= kSampleMinAbove.  Workgroups whose rows are short, or
+  // whose 3.5 K best keys reach back past key 0, start at -inf.
+  int nsamp = 0, sstride = 1;
+  if constexpr (SAMPLE) {
+    const int lo = pos0 + max(j_hi - (kWaves - 1), 0) * args.pos_stride + 1;
+    if (lo >= kSampleMinRow && 7 * (int64_t)args.K < 2 * (int64_t)lo) {
+      for (int r = 1; r <= 2 && nsamp == 0; ++r) {
+        const int64_t S = (int64_t)r * kStages * TK;
+        if (7 * (int64_t)args.K * S / (2 * (int64_t)ncand_blk) + 1 >= kSampleMinAbove) nsamp = r * kStages;
+      }
+    }
+    if (nsamp == 0) {
+      if (active) args.start[j] = -__builtin_inff();
+      return;
+    }
+    sstride = lo / (nsamp * TK);
+  }
 
   // ---- this wave's query: A fragments, gate weights (w/2, with the fp8 query
   // scale folded in), and q-tilde = sum_j (w_j/2) q_j split into bf16 hi + lo
@@ -349,7 +406,9 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   int32_t* stage_idx = (int32_t*)(hist + kStage);
   int cnt = 0;                                        // entries in the buffer
   int nst = 0;                                        // entries in the LDS stage
-  float thr = active ? -__builtin_inff() : __builtin_inff();  // scores must exceed it
+  // scores must exceed thr: the query's sampled start, when it has one
+  float thr = !active ? __builtin_inff()
+            : (kCertify && args.start != nullptr && !args.rerun_pass) ? args.start[jq] : -__builtin_inff();
   auto flush = [&]() __attribute__((always_inline)) {
     for (int e = l; e < nst; e += 64) {
       ckey[cnt + e] = stage_key[e];
@@ -389,6 +448,14 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   const uint32_t lds_tile = lds_addr(&s_tile[0][0]) + wave * 64 * 16;
   const uint32_t lds_ks = lds_addr(&s_ks[0][0]);
   auto request = [&](int t, int st) __attribute__((always_inline)) {
+    // contiguous keys: tile t holds keys rb + rs * (0 .. TK-1).  The pre-pass
+    // reads the sample tiles; its requests past them point past the buffer
+    // range, which fetches nothing.
+    int rb = t * TK, rs = 1;
+    if constexpr (SAMPLE) {
+      rb = t < nsamp ? t * TK * sstride + (sstride >> 1) : t_hi + 1;
+      rs = t < nsamp ? sstride : 0;
+    }
 #pragma unroll
     for (int n = 0; n < C::kDma; ++n) {
       uint32_t off;
@@ -397,7 +464,7 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
         const uint32_t pos = (uint32_t)position(t, t * kTile + lane_row[n]);
         off = pos <= (uint32_t)t_hi ? pos * C::kRowBytes + lane_off[n] : kNowhere;
       } else {
-        off = (uint32_t)(t * TK + lane_row[n]) * C::kRowBytes + lane_off[n];
+        off = (uint32_t)(rb + lane_row[n] * rs) * C::kRowBytes + lane_off[n];
       }
       dma_b128(kres, lds_tile + st * C::kTileBytes + n * kThreads * 16, off);
     }
@@ -407,12 +474,11 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
     for (int hh = 0; hh < kHalves; ++hh) {
       uint32_t soff = 4 * l;
       if constexpr (DT == kFP8) {
-        const int c = t * TK + 64 * hh + l;
         if constexpr (GATHER) {
-          const uint32_t pos = (uint32_t)position(t, c);
+          const uint32_t pos = (uint32_t)position(t, t * TK + 64 * hh + l);
           soff = pos <= (uint32_t)t_hi ? 4 * pos : kNowhere;
         } else {
-          soff = 4 * c;
+          soff = 4 * (rb + (64 * hh + l) * rs);
         }
       }
       dma_b32(sres, lds_ks + (st * TK + 64 * hh) * 4, soff);
@@ -553,6 +619,38 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
       if (cnt + nst > lim && l == 0) s_need[i & 1] = i;
     }
   };
+  // The pre-pass's sample tiles: each score's top 16 order-key bits, in this
+  // wave's LDS words past the start's histogram
+  uint16_t* const samp = (uint16_t*)(hist + kSampleBins / 2);
+  static_assert(2 * kStages * 128 <= 2 * (kSelectHistWords - kSampleBins / 2), "two rounds of samples fit");
+  // The start: the 16-bit key of the m-th best of the S samples (two radix
+  // digits), taken at the bottom of its bucket so that it errs low; -inf when
+  // m leaves too few samples above it or reaches past them.
+  auto sampled_start = [&]() __attribute__((always_inline)) -> float {
+    const int S = nsamp * TK;
+    const int64_t m = 7 * (int64_t)args.K * S / (2 * (int64_t)ncand_me) + 1;
+    if (m >= S || m < kSampleMinAbove) return -__builtin_inff();
+    uint32_t prefix = 0, pmask = 0;
+    int krem = (int)m;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int shift = pass == 0 ? 7 : 0;
+      hist_zero<kSampleBins>(hist);
+      wave_lds_sync();
+      for (int e = l; e < S; e += 64) {
+        const uint32_t k = samp[e];
+        if ((k & pmask) == prefix) hist_add<kSampleBins>(hist, k, shift);
+      }
+      wave_lds_sync();
+      radix_pick<kSampleBins>(hist, shift, prefix, pmask, krem);
+      wave_lds_sync();
+    }
+    // a test hook: a start above every score, so that every sampled query
+    // keeps nothing and its workgroup streams again
+    if (args.sample_test) return __builtin_inff();
+    return key_to_float(prefix << 16);
+  };
+
   // ---- prologue: (gathering: the positions of tiles 0..6) tiles 0..3
   // requested, tile 0's linear term, first MFMAs
   if constexpr (GATHER) {
@@ -622,11 +720,12 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   // holds sub-tile 0's products and bB sub-tile 1's B operands; the MFMAs of
   // each sub-tile run while the head sums of the one before are taken, and
   // each 64-key half is scored and appended as soon as its sums are complete.
-  auto step128 = [&](const int i, auto stage) __attribute__((always_inline)) {
+  auto step128 = [&](const int i, auto stage, auto sample) __attribute__((always_inline)) {
+    constexpr bool kSamp = decltype(sample)::value;  // tile i is a sample tile
     const int st = stage;
     const int st1 = st == kStages - 1 ? 0 : st + 1;
     const int st4 = st == 0 ? kStages - 1 : st - 1;  // (st + kAhead) % kStages
-    if constexpr (!FULL) {
+    if constexpr (!FULL && !kSamp) {
       if (i > 0 && s_need[(i - 1) & 1] == i - 1 && active && cnt + nst > args.K) {
         flush();
         thr = wave_keep_topk(ckey, cidx, cnt, args.K, hist, kCompactSlack);
@@ -636,6 +735,11 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
     }
     request(i + kAhead, st4);
     const int tbase = i * TK;
+    // a sample's top 16 key bits, or the append of a row tile's scores
+    auto take = [&](float sc, int hh) __attribute__((always_inline)) {
+      if constexpr (kSamp) samp[i * TK + 64 * hh + l] = (uint16_t)(order_key(sc) >> 16);
+      else append(sc, tbase + 64 * hh, i);
+    };
     load_b(bA, st, 2);
     mfma_sub(acc1, bB);                    // sub-tile 1
     const float p0 = abs_sum(acc0);        // sub-tile 0
@@ -643,7 +747,7 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
     mfma_sub(acc0, bA);                    // sub-tile 2
     const float p1 = abs_sum(acc1);        // sub-tile 1
     linear(i + 1, st1, 0);
-    append(tile_score(p0, p1, i, st, 0), tbase, i);
+    take(tile_score(p0, p1, i, st, 0), 0);
     load_b(bA, st1, 0);
     mfma_sub(acc1, bB);                    // sub-tile 3
     const float p2 = abs_sum(acc0);        // sub-tile 2
@@ -653,7 +757,7 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
     const float p3 = abs_sum(acc1);        // sub-tile 3
     linear(i + 1, st1, 1);
     mfma_steps(acc0, bA, kHeld, C::kSteps);
-    append(tile_score(p2, p3, i, st, 1), tbase + 64, i);
+    take(tile_score(p2, p3, i, st, 1), 1);
     // tile i+2 must have landed before the barrier publishes it: after its
     // requests this wave issued those of steps i-1 and i; in full-row mode
     // each step also ends with two stores
@@ -661,17 +765,32 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
     __syncthreads();
   };
   static_assert(kStages == 5 && kAhead == kStages - 1, "the loops below assume a five-stage ring");
-  if constexpr (TK == 128) {
+  if constexpr (SAMPLE) {
+    // nsamp is a whole number of rounds of the ring
+    for (int i = 0; i < nsamp; i += kStages) {
+      step128(i, StageC<0>{}, SampleC<true>{});
+      step128(i + 1, StageC<1>{}, SampleC<true>{});
+      step128(i + 2, StageC<2>{}, SampleC<true>{});
+      step128(i + 3, StageC<3>{}, SampleC<true>{});
+      step128(i + 4, StageC<4>{}, SampleC<true>{});
+    }
+    __builtin_amdgcn_s_waitcnt(0x3F70);  // the requests past the sample tiles
+    if (active) {
+      const float s = sampled_start();
+      if (l == 0) args.start[j] = s;
+    }
+    return;
+  } else if constexpr (TK == 128) {
     for (int i = 0; i < ntiles; i += kStages) {
-      step128(i, StageC<0>{});
+      step128(i, StageC<0>{}, SampleC<false>{});
       if (i + 1 >= ntiles) break;
-      step128(i + 1, StageC<1>{});
+      step128(i + 1, StageC<1>{}, SampleC<false>{});
       if (i + 2 >= ntiles) break;
-      step128(i + 2, StageC<2>{});
+      step128(i + 2, StageC<2>{}, SampleC<false>{});
       if (i + 3 >= ntiles) break;
-      step128(i + 3, StageC<3>{});
+      step128(i + 3, StageC<3>{}, SampleC<false>{});
       if (i + 4 >= ntiles) break;
-      step128(i + 4, StageC<4>{});
+      step128(i + 4, StageC<4>{}, SampleC<false>{});
     }
   } else if constexpr (DT == kFP8) {
     for (int i = 0; i < ntiles; i += kStages) {
@@ -692,6 +811,21 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   // the requests issued past the last tile: none may still be writing LDS
   // when the wave ends
   __builtin_amdgcn_s_waitcnt(0x3F70);
+  if constexpr (kCertify) {
+    // the check of a sampled start: a query that kept at least K entries (a
+    // compaction keeps at least K) holds its whole top K; otherwise the
+    // workgroup is flagged and its rows are streamed again, by the re-stream
+    // launch, which writes the output instead
+    if (args.start != nullptr && !args.rerun_pass) {
+      if (tid == 0) s_rerun = 0;
+      __syncthreads();
+      if (active && args.start[jq] > -__builtin_inff() && cnt + nst < args.K) s_rerun = 1;
+      __syncthreads();
+      const int flag = s_rerun;
+      if (tid == 0) args.rerun[blockIdx.x] = flag;
+      if (flag) return;
+    }
+  }
   if (!active) return;
   int32_t* const orow = args.out_idx + (int64_t)j * args.out_stride;
   float* const srow = args.out_score ? args.out_score + (int64_t)j * args.out_stride : nullptr;
@@ -720,9 +854,9 @@ bool dense_topk_supported(const ScanArgs& a) {
 template <bool GATHER, bool FULL>
 static void launch_dt(const ScanArgs& a, int dtype, dim3 grid, hipStream_t stream) {
   if (dtype == kBF16)
-    hipLaunchKernelGGL((dense_topk_kernel<kBF16, GATHER, FULL>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((dense_topk_kernel<kBF16, GATHER, FULL, false>), grid, dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((dense_topk_kernel<kFP8, GATHER, FULL>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((dense_topk_kernel<kFP8, GATHER, FULL, false>), grid, dim3(kThreads), 0, stream, a);
 }
 
 hipError_t launch_dense_topk(const ScanArgs& a, int dtype, hipStream_t stream) {
@@ -737,9 +871,20 @@ hipError_t launch_dense_topk(const ScanArgs& a, int dtype, hipStream_t stream) {
   if (a.bank) {
     if (full) launch_dt<true, true>(a, dtype, grid, stream);
     else launch_dt<true, false>(a, dtype, grid, stream);
+  } else if (full) {
+    launch_dt<false, true>(a, dtype, grid, stream);
+  } else if (dtype == kFP8 && a.start != nullptr && ncand_max >= kSampleMinRow) {
+    // sampled start: the pre-pass, the stream, the re-stream of flagged
+    // workgroups
+    hipLaunchKernelGGL((dense_topk_kernel<kFP8, false, false, true>), grid, dim3(kThreads), 0, stream, a);
+    launch_dt<false, false>(a, dtype, grid, stream);
+    ScanArgs r = a;
+    r.rerun_pass = 1;
+    launch_dt<false, false>(r, dtype, grid, stream);
   } else {
-    if (full) launch_dt<false, true>(a, dtype, grid, stream);
-    else launch_dt<false, false>(a, dtype, grid, stream);
+    ScanArgs r = a;
+    r.start = nullptr;  // no start: nothing to check
+    launch_dt<false, false>(r, dtype, grid, stream);
   }
   return hipGetLastError();
 }

@@ -30,6 +30,15 @@ struct ScanArgs {
   int32_t* out_idx;        // [nq, out_stride]
   float* out_score;        // [nq, out_stride] or nullptr
   int out_stride;
+  // Sampled start of the dense E4M3 kernel over contiguous keys (nullptr:
+  // none): start [nq] floats, rerun [ceil(nq / 8)] flags, both workspace.
+  // rerun_pass is set inside the launch; sample_test != 0 puts every start
+  // above all scores, so that each sampled workgroup is streamed a second
+  // time (a test of that path; the results are the same).
+  float* start;
+  int32_t* rerun;
+  int rerun_pass;
+  int sample_test;
 };
 
 hipError_t launch_scan_topk(const ScanArgs& a, int dtype, hipStream_t stream);

@@ -247,6 +247,47 @@ def test_dense_kernel_streaming_and_full_rows(dsa, dtype, dist):
     _prefill_check(dsa, mid, rows=_rows(192, 24, 92))
 
 
+def _run_prefill(dsa, wl, K):
+    t = {k: v.cuda() for k, v in wl.tensors.items()}
+    gi, gs = dsa.indexer_prefill(t["q"], t["k"], t["w"], wl.params["q_pos0"], K, t.get("q_scale"), t.get("k_scale"))
+    torch.cuda.synchronize()
+    return gi, gs
+
+
+# E4M3 rows of 16K keys and more stream from a sampled start: one round of the
+# ring of samples (T = 24K, K = 2048), two rounds (T = 40K, K = 512), and a
+# call whose rows straddle 16K, so that workgroups with and without a start
+# share the launch.
+_SAMPLED = [(24576, 2048, 1024, None), (40000, 512, 512, None), (17000, 2048, 1024, 16384 - 520)]
+
+
+@pytest.mark.parametrize("T,K,Tq,q_pos0", _SAMPLED)
+@pytest.mark.parametrize("dist", ["normal", "int"])
+def test_dense_kernel_sampled_start(dsa, T, K, Tq, q_pos0, dist):
+    """Rows that stream from a sampled start match the oracle (integer inputs
+    bit for bit), including the first and last rows of the call."""
+    wl = make_prefill(T=T, H=64, d=128, topk=K, dtype="fp8", dist=dist, seed=T % 997 + K, Tq=Tq, q_pos0=q_pos0)
+    rows = np.unique(np.concatenate([_rows(Tq, 24, T % 101), [0, 7, 8, Tq - 9, Tq - 1]]))
+    _prefill_check(dsa, wl, rows=rows)
+
+
+@pytest.mark.parametrize("T,K,Tq,q_pos0", _SAMPLED)
+def test_dense_kernel_sampled_start_restream(dsa, monkeypatch, T, K, Tq, q_pos0):
+    """A start that no score beats fails every sampled query's check, so every
+    sampled workgroup is streamed again from -inf by the re-stream launch: the
+    output is identical to the normal run's, bit for bit, and matches the
+    oracle."""
+    wl = make_prefill(T=T, H=64, d=128, topk=K, dtype="fp8", dist="normal", seed=T % 991 + K, Tq=Tq,
+                      q_pos0=q_pos0)
+    a = _run_prefill(dsa, wl, K)
+    monkeypatch.setenv("DSAIDX_SAMPLE_RERUN", "1")
+    b = _run_prefill(dsa, wl, K)
+    monkeypatch.delenv("DSAIDX_SAMPLE_RERUN")
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    monkeypatch.setenv("DSAIDX_SAMPLE_RERUN", "1")
+    _prefill_check(dsa, wl, rows=_rows(Tq, 12, T % 89))
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 def test_dense_kernel_full_row_edges(dsa, dtype):
     """Full-row top-K at its edges: rows of K - 1, K and K + 1 candidates
