@@ -59,7 +59,7 @@ int cap_for(int K) { return (2 * K + 2048 + 63) / 64 * 64; }
 
 size_t cand_bytes_cap(int64_t rows, int cap) { return 2 * align_up((size_t)rows * (size_t)cap * 4u); }
 size_t cand_bytes(int64_t rows, int K) { return cand_bytes_cap(rows, cap_for(K)); }
-// the dense E4M3 kernel's sampled start: a start per row and a flag per
+// the dense kernel's sampled start: a start per row and a flag per
 // workgroup of 8 rows, after the candidate buffers
 size_t sample_bytes(int64_t rows) { return align_up((size_t)rows * 4u) + align_up((size_t)(rows + 7) / 8 * 4u); }
 
@@ -129,8 +129,8 @@ int check_ws(const void* ws, size_t ws_bytes, size_t need) {
   return DSAIDX_OK;
 }
 
-// The environment variable DSAIDX_SAMPLE_RERUN=1 makes the dense E4M3
-// kernel's sampled start fail on purpose, so that the rows it covers are
+// The environment variable DSAIDX_SAMPLE_RERUN=1 makes the dense kernel's
+// sampled start fail on purpose, so that the rows it covers are
 // streamed a second time from -inf: a test of that path (results unchanged).
 static int sample_test_forced() {
   const char* v = std::getenv("DSAIDX_SAMPLE_RERUN");
@@ -143,7 +143,7 @@ static int sample_test_forced() {
 // kernel keeps their whole (short) rows; longer rows stream their top K
 // through the same buffers.  `sample`: the workspace also holds
 // sample_bytes(rows) after the candidate buffers of `rows` rows (rows >= every
-// launch's n), so that long E4M3 rows can stream from a sampled start.
+// launch's n), so that long rows can stream from a sampled start.
 hipError_t run_dense(const void* q, const float* q_scale, const void* k, const float* k_scale,
                      const float* w, int dtype, int H, int d, int64_t q_pos0, int64_t r0,
                      int64_t r1, int topk, int cap, int32_t* out_idx, float* out_score, void* ws,

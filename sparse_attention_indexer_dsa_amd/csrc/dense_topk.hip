@@ -52,20 +52,22 @@
 //     them and fetch the listed rows (and fp8 scales) with the same LDS DMA,
 //     and the append stores positions instead of list slots.  The list is
 //     ascending in position, so ties still keep the lower index.
-//   * Sampled start (E4M3 over contiguous keys, rows of 16K candidates and
-//     more): a pre-pass of the same kernel scores, per workgroup, one or two
-//     rounds of the ring of sample keys spread evenly over its shortest row
-//     and gives each query a start that about 3.5 K of its keys beat (the
-//     16-bit key bucket of its m-th best sample).  The stream then keeps
-//     only scores above the start, so far fewer enter the buffer and it is
-//     compacted about once instead of four times.  The top K all lie above
-//     the start whenever at least K entries did; the stream checks that at
-//     its end and flags its workgroup when a query kept fewer, and a third
-//     launch streams the flagged workgroups again from -inf (every other
-//     workgroup of it ends at once), so the result never depends on the
-//     sample.  The start leaves at least 35 samples expected above it, which
-//     makes a flag rarer than one query in 10^9 on i.i.d. scores.  The
-//     stream's own code is the same with or without a start.
+//   * Sampled start (contiguous keys; E4M3 rows of 16K candidates and more,
+//     bf16 rows of 12K and more): a pre-pass of the same kernel scores, per
+//     workgroup, one or two rounds of the ring of sample keys spread evenly
+//     over its shortest row and gives each query a start that about 3.5 K of
+//     its keys beat (the 16-bit key bucket of its m-th best sample).  The
+//     stream then keeps only scores above the start, so far fewer enter the
+//     buffer and it is compacted about once instead of four times.  The top
+//     K all lie above the start whenever at least K entries did; the stream
+//     checks that at its end, and a query that kept fewer writes nothing and
+//     flags its workgroup (the pre-pass cleared the flag); a third launch
+//     streams the flagged workgroups again from -inf (every other workgroup
+//     of it ends at once), so the result never depends on the sample.  The
+//     start leaves at least 35 samples expected above it, which makes a flag
+//     rarer than one query in 10^9 on i.i.d. scores.  The stream's own code
+//     is the same with or without a start.  Shorter bf16 rows gain nothing:
+//     the pre-pass repeats the prologue (each query's 16 KB of fragments).
 #include "device.h"
 #include "launch.h"
 
@@ -82,10 +84,13 @@ constexpr int kStage = kSelectHistWords / 2;  // LDS append stage entries per wa
 constexpr int kD = 128;
 constexpr int kIdxRing = 8;   // gathering: tiles of bank positions held in LDS
 constexpr int kIdxAhead = 7;  // a tile's positions are requested this many steps before it is scored
-// sampled start: the shortest row that samples, the fewest samples a query
-// expects above its start, and the radix digits of the start's select over
-// the samples' 16-bit keys (a 9-bit digit, then the low 9 bits)
-constexpr int kSampleMinRow = 16384;
+// sampled start: the shortest row that samples (E4M3, bf16), the fewest
+// samples a query expects above its start, and the radix digits of the
+// start's select over the samples' 16-bit keys (a 9-bit digit, then the low
+// 9 bits)
+constexpr int kSampleMinRowFp8 = 16384;
+constexpr int kSampleMinRowBf16 = 12288;
+constexpr int sample_min_row(int dt) { return dt == kFP8 ? kSampleMinRowFp8 : kSampleMinRowBf16; }
 constexpr int kSampleMinAbove = 35;
 constexpr int kSampleBins = 512;
 
@@ -200,7 +205,6 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   __shared__ __attribute__((aligned(16))) uint16_t s_qt[kWaves][kParts][kD];
   __shared__ float s_qinv[kWaves];
   __shared__ int s_need[2];  // s_need[i & 1] == i: a wave asked for compaction in step i
-  __shared__ int s_rerun;    // sampled start: some query kept fewer than K entries
   // gathering: the bank positions of tiles t .. t+7, slot t & 7 (tile t+7's
   // are requested in step t, read by tile t+4's request and tile t's append)
   __shared__ int32_t s_idx[GATHER ? kIdxRing : 1][kTile];
@@ -236,8 +240,8 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   // Sampled start.  The stream (E4M3 over contiguous keys) takes its query's
   // start from args.start when given; its re-stream launch (args.rerun_pass)
   // runs only the workgroups that the first stream flagged, from -inf.
-  constexpr bool kCertify = TK == 128 && !GATHER && !FULL && !SAMPLE;
-  static_assert(!SAMPLE || (DT == kFP8 && !GATHER && !FULL), "the pre-pass is for E4M3 over contiguous keys");
+  constexpr bool kCertify = !GATHER && !FULL && !SAMPLE;
+  static_assert(!SAMPLE || (!GATHER && !FULL), "the pre-pass is for streaming rows over contiguous keys");
   if constexpr (kCertify) {
     if (args.rerun_pass && args.rerun[blockIdx.x] == 0) return;
   }
@@ -249,8 +253,9 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   // whose 3.5 K best keys reach back past key 0, start at -inf.
   int nsamp = 0, sstride = 1;
   if constexpr (SAMPLE) {
+    if (tid == 0) args.rerun[blockIdx.x] = 0;  // the stream sets it when a query fails its check
     const int lo = pos0 + max(j_hi - (kWaves - 1), 0) * args.pos_stride + 1;
-    if (lo >= kSampleMinRow && 7 * (int64_t)args.K < 2 * (int64_t)lo) {
+    if (lo >= sample_min_row(DT) && 7 * (int64_t)args.K < 2 * (int64_t)lo) {
       for (int r = 1; r <= 2 && nsamp == 0; ++r) {
         const int64_t S = (int64_t)r * kStages * TK;
         if (7 * (int64_t)args.K * S / (2 * (int64_t)ncand_blk) + 1 >= kSampleMinAbove) nsamp = r * kStages;
@@ -677,12 +682,13 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   // the loop is unrolled over the ring so that every stage is a constant (LDS
   // addresses fold into the instructions' offsets); bf16, whose operands take
   // twice the registers, keeps one copy of the step with run-time stages.
-  auto step = [&](const int i, auto stage) __attribute__((always_inline)) {
+  auto step = [&](const int i, auto stage, auto sample) __attribute__((always_inline)) {
+    constexpr bool kSamp = decltype(sample)::value;  // tile i is a sample tile
     const int st = stage;
     const int st1 = st == kStages - 1 ? 0 : st + 1;
     const int st4 = st == 0 ? kStages - 1 : st - 1;  // (st + kAhead) % kStages
     // compaction requests raised during step i-1 (seen after its barrier)
-    if constexpr (!FULL) {
+    if constexpr (!FULL && !kSamp) {
       if (i > 0 && s_need[(i - 1) & 1] == i - 1 && active && cnt + nst > args.K) {
         flush();
         thr = wave_keep_topk(ckey, cidx, cnt, args.K, hist, kCompactSlack);
@@ -706,7 +712,9 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
     const float p1 = abs_sum(acc1);
     linear(i + 1, st1, 0);
     if constexpr (kHeld < C::kSteps) mfma_steps(acc0, bA, kHeld, C::kSteps);
-    append(tile_score(p0, p1, i, st, 0), tbase, i);
+    const float sc = tile_score(p0, p1, i, st, 0);
+    if constexpr (kSamp) samp[i * TK + l] = (uint16_t)(order_key(sc) >> 16);
+    else append(sc, tbase, i);
     // tile i+2 (gathering: and the positions of tile i+5) must have landed
     // before the barrier publishes them: after their requests this wave issued
     // those of steps i-1 and i (and maybe a flush's stores, which only makes
@@ -766,13 +774,18 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   };
   static_assert(kStages == 5 && kAhead == kStages - 1, "the loops below assume a five-stage ring");
   if constexpr (SAMPLE) {
-    // nsamp is a whole number of rounds of the ring
-    for (int i = 0; i < nsamp; i += kStages) {
-      step128(i, StageC<0>{}, SampleC<true>{});
-      step128(i + 1, StageC<1>{}, SampleC<true>{});
-      step128(i + 2, StageC<2>{}, SampleC<true>{});
-      step128(i + 3, StageC<3>{}, SampleC<true>{});
-      step128(i + 4, StageC<4>{}, SampleC<true>{});
+    // nsamp is a whole number of rounds of the ring (bf16, whose fragments
+    // take twice the registers, keeps one copy of the step)
+    if constexpr (TK == 128) {
+      for (int i = 0; i < nsamp; i += kStages) {
+        step128(i, StageC<0>{}, SampleC<true>{});
+        step128(i + 1, StageC<1>{}, SampleC<true>{});
+        step128(i + 2, StageC<2>{}, SampleC<true>{});
+        step128(i + 3, StageC<3>{}, SampleC<true>{});
+        step128(i + 4, StageC<4>{}, SampleC<true>{});
+      }
+    } else {
+      for (int i = 0, st = 0; i < nsamp; ++i, st = st == kStages - 1 ? 0 : st + 1) step(i, st, SampleC<true>{});
     }
     __builtin_amdgcn_s_waitcnt(0x3F70);  // the requests past the sample tiles
     if (active) {
@@ -794,18 +807,18 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
     }
   } else if constexpr (DT == kFP8) {
     for (int i = 0; i < ntiles; i += kStages) {
-      step(i, StageC<0>{});
+      step(i, StageC<0>{}, SampleC<false>{});
       if (i + 1 >= ntiles) break;
-      step(i + 1, StageC<1>{});
+      step(i + 1, StageC<1>{}, SampleC<false>{});
       if (i + 2 >= ntiles) break;
-      step(i + 2, StageC<2>{});
+      step(i + 2, StageC<2>{}, SampleC<false>{});
       if (i + 3 >= ntiles) break;
-      step(i + 3, StageC<3>{});
+      step(i + 3, StageC<3>{}, SampleC<false>{});
       if (i + 4 >= ntiles) break;
-      step(i + 4, StageC<4>{});
+      step(i + 4, StageC<4>{}, SampleC<false>{});
     }
   } else {
-    for (int i = 0, st = 0; i < ntiles; ++i, st = st == kStages - 1 ? 0 : st + 1) step(i, st);
+    for (int i = 0, st = 0; i < ntiles; ++i, st = st == kStages - 1 ? 0 : st + 1) step(i, st, SampleC<false>{});
   }
 
   // the requests issued past the last tile: none may still be writing LDS
@@ -815,15 +828,15 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
     // the check of a sampled start: a query that kept at least K entries (a
     // compaction keeps at least K) holds its whole top K; otherwise the
     // workgroup is flagged and its rows are streamed again, by the re-stream
-    // launch, which writes the output instead
-    if (args.start != nullptr && !args.rerun_pass) {
-      if (tid == 0) s_rerun = 0;
-      __syncthreads();
-      if (active && args.start[jq] > -__builtin_inff() && cnt + nst < args.K) s_rerun = 1;
-      __syncthreads();
-      const int flag = s_rerun;
-      if (tid == 0) args.rerun[blockIdx.x] = flag;
-      if (flag) return;
+    // launch, which writes the output instead.  A finite threshold means a
+    // sampled start or a compaction, and after a compaction at least K are
+    // kept, so the test needs no second read of the start.
+    // The pre-pass cleared the workgroup's flag; a query that fails sets it
+    // and writes nothing, the others write their rows (the re-stream writes
+    // the same ones again).
+    if (args.start != nullptr && !args.rerun_pass && active && thr > -__builtin_inff() && cnt + nst < args.K) {
+      if (l == 0) args.rerun[blockIdx.x] = 1;
+      return;
     }
   }
   if (!active) return;
@@ -873,10 +886,13 @@ hipError_t launch_dense_topk(const ScanArgs& a, int dtype, hipStream_t stream) {
     else launch_dt<true, false>(a, dtype, grid, stream);
   } else if (full) {
     launch_dt<false, true>(a, dtype, grid, stream);
-  } else if (dtype == kFP8 && a.start != nullptr && ncand_max >= kSampleMinRow) {
+  } else if (a.start != nullptr && ncand_max >= sample_min_row(dtype)) {
     // sampled start: the pre-pass, the stream, the re-stream of flagged
     // workgroups
-    hipLaunchKernelGGL((dense_topk_kernel<kFP8, false, false, true>), grid, dim3(kThreads), 0, stream, a);
+    if (dtype == kBF16)
+      hipLaunchKernelGGL((dense_topk_kernel<kBF16, false, false, true>), grid, dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((dense_topk_kernel<kFP8, false, false, true>), grid, dim3(kThreads), 0, stream, a);
     launch_dt<false, false>(a, dtype, grid, stream);
     ScanArgs r = a;
     r.rerun_pass = 1;

@@ -254,30 +254,34 @@ def _run_prefill(dsa, wl, K):
     return gi, gs
 
 
-# E4M3 rows of 16K keys and more stream from a sampled start: one round of the
-# ring of samples (T = 24K, K = 2048), two rounds (T = 40K, K = 512), and a
-# call whose rows straddle 16K, so that workgroups with and without a start
-# share the launch.
-_SAMPLED = [(24576, 2048, 1024, None), (40000, 512, 512, None), (17000, 2048, 1024, 16384 - 520)]
+# Rows of 16K keys and more (E4M3) or 12K and more (bf16) stream from a
+# sampled start: one round of the ring of samples (E4M3 T = 24K, bf16 T = 16K,
+# K = 2048), two rounds (E4M3 T = 40K, bf16 T = 20K, K = 512), and a call
+# whose rows straddle the shortest sampled row, so that workgroups with and
+# without a start share the launch.
+_SAMPLED = [("fp8", 24576, 2048, 1024, None), ("fp8", 40000, 512, 512, None),
+            ("fp8", 17000, 2048, 1024, 16384 - 520),
+            ("bf16", 16384, 2048, 1024, None), ("bf16", 20000, 512, 512, None),
+            ("bf16", 13000, 2048, 1024, 12288 - 520)]
 
 
-@pytest.mark.parametrize("T,K,Tq,q_pos0", _SAMPLED)
+@pytest.mark.parametrize("dtype,T,K,Tq,q_pos0", _SAMPLED)
 @pytest.mark.parametrize("dist", ["normal", "int"])
-def test_dense_kernel_sampled_start(dsa, T, K, Tq, q_pos0, dist):
+def test_dense_kernel_sampled_start(dsa, dtype, T, K, Tq, q_pos0, dist):
     """Rows that stream from a sampled start match the oracle (integer inputs
     bit for bit), including the first and last rows of the call."""
-    wl = make_prefill(T=T, H=64, d=128, topk=K, dtype="fp8", dist=dist, seed=T % 997 + K, Tq=Tq, q_pos0=q_pos0)
+    wl = make_prefill(T=T, H=64, d=128, topk=K, dtype=dtype, dist=dist, seed=T % 997 + K, Tq=Tq, q_pos0=q_pos0)
     rows = np.unique(np.concatenate([_rows(Tq, 24, T % 101), [0, 7, 8, Tq - 9, Tq - 1]]))
     _prefill_check(dsa, wl, rows=rows)
 
 
-@pytest.mark.parametrize("T,K,Tq,q_pos0", _SAMPLED)
-def test_dense_kernel_sampled_start_restream(dsa, monkeypatch, T, K, Tq, q_pos0):
+@pytest.mark.parametrize("dtype,T,K,Tq,q_pos0", _SAMPLED)
+def test_dense_kernel_sampled_start_restream(dsa, monkeypatch, dtype, T, K, Tq, q_pos0):
     """A start that no score beats fails every sampled query's check, so every
     sampled workgroup is streamed again from -inf by the re-stream launch: the
     output is identical to the normal run's, bit for bit, and matches the
     oracle."""
-    wl = make_prefill(T=T, H=64, d=128, topk=K, dtype="fp8", dist="normal", seed=T % 991 + K, Tq=Tq,
+    wl = make_prefill(T=T, H=64, d=128, topk=K, dtype=dtype, dist="normal", seed=T % 991 + K, Tq=Tq,
                       q_pos0=q_pos0)
     a = _run_prefill(dsa, wl, K)
     monkeypatch.setenv("DSAIDX_SAMPLE_RERUN", "1")
