@@ -224,7 +224,8 @@ size_t group_ws_bytes(int64_t Tq, int H, int d, int G, int P, int topk, unsigned
   if (flags & DSAIDX_POOL_MEAN) bank += pool_q_bytes(nelig, H, d) + pool_w_bytes(nelig, H);
   const int64_t anchors = nelig < kAnchorsPerLaunch ? nelig : kAnchorsPerLaunch;
   const int64_t rows = Tq < kRowsPerLaunch ? Tq : kRowsPerLaunch;
-  size_t scan = anchors > 0 ? cand_bytes(anchors, P) : 0;
+  // the group scan's candidate buffers and its sampled starts
+  size_t scan = anchors > 0 ? cand_bytes(anchors, P) + sample_bytes(anchors) : 0;
   size_t refine = rows > 0 ? cand_bytes_cap(rows, full_cap(topk, (int64_t)P + G - 1)) : 0;
   return bank + (scan > refine ? scan : refine);
 }
@@ -517,6 +518,12 @@ int run_group_bank(const void* q, const float* q_scale, const void* k, const flo
     a.out_idx = bank + s * (int64_t)P;
     a.out_score = nullptr;
     a.out_stride = P;
+    // long anchor rows stream from a sampled start (the dense kernel only)
+    const int64_t anchors = nelig < kAnchorsPerLaunch ? nelig : kAnchorsPerLaunch;
+    uint8_t* sws = (uint8_t*)cand_ws + cand_bytes(anchors, P);
+    a.start = (float*)sws;
+    a.rerun = (int32_t*)(sws + align_up((size_t)anchors * 4u));
+    a.sample_test = sample_test_forced();
     e = launch_scan_topk(a, dtype, st);
     if (e != hipSuccess) return hip_fail(e, "indexer_group_bank group scan launch");
   }

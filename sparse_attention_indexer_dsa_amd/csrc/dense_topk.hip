@@ -94,6 +94,18 @@ constexpr int sample_min_row(int dt) { return dt == kFP8 ? kSampleMinRowFp8 : kS
 constexpr int kSampleMinAbove = 35;
 constexpr int kSampleBins = 512;
 
+// The rank m of a query's sampled start among its S samples.  If the samples
+// fell like independent draws, mu = K S / n of them would beat the row's K-th
+// best score, and the start fails (fewer than K keys beat it) only when at
+// least m of them do: m = min(3.5 mu, mu + 6 sqrt(mu) + 10) + 1 puts that
+// binomial tail below 5e-10 wherever m >= 35 (the least that sampling takes),
+// while the share of the row kept above the start falls from 3.5 K to under
+// 2 K once mu reaches about 80.
+__device__ __forceinline__ int64_t start_rank(int K, int64_t S, int64_t n) {
+  const float mu = (float)K * (float)S / (float)n;
+  return (int64_t)fminf(3.5f * mu, mu + 6.0f * __builtin_sqrtf(mu) + 10.0f) + 1;
+}
+
 template <int S>
 struct StageC {  // a ring stage as a compile-time constant
   constexpr operator int() const { return S; }
@@ -247,9 +259,10 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   }
   // The pre-pass: nsamp sample tiles (one or two rounds of the ring), sample
   // s at key s * sstride + sstride / 2, all inside the workgroup's shortest
-  // row.  A query's start is its m-th best sample, m = 3.5 K S / ncand + 1 of
-  // the S samples; the round count is the least that gives every query of
-  // the workgroup m >= kSampleMinAbove.  Workgroups whose rows are short, or
+  // row.  A query's start is its m-th best sample (start_rank: m is about
+  // 3.5 K S / ncand + 1 of the S samples for short or few samples, less
+  // above); the round count is the least that gives every query of the
+  // workgroup m >= kSampleMinAbove.  Workgroups whose rows are short, or
   // whose 3.5 K best keys reach back past key 0, start at -inf.
   int nsamp = 0, sstride = 1;
   if constexpr (SAMPLE) {
@@ -258,7 +271,7 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
     if (lo >= sample_min_row(DT) && 7 * (int64_t)args.K < 2 * (int64_t)lo) {
       for (int r = 1; r <= 2 && nsamp == 0; ++r) {
         const int64_t S = (int64_t)r * kStages * TK;
-        if (7 * (int64_t)args.K * S / (2 * (int64_t)ncand_blk) + 1 >= kSampleMinAbove) nsamp = r * kStages;
+        if (start_rank(args.K, S, ncand_blk) >= kSampleMinAbove) nsamp = r * kStages;
       }
     }
     if (nsamp == 0) {
@@ -633,7 +646,7 @@ __global__ void __launch_bounds__(kThreads, 2) dense_topk_kernel(const ScanArgs 
   // m leaves too few samples above it or reaches past them.
   auto sampled_start = [&]() __attribute__((always_inline)) -> float {
     const int S = nsamp * TK;
-    const int64_t m = 7 * (int64_t)args.K * S / (2 * (int64_t)ncand_me) + 1;
+    const int64_t m = start_rank(args.K, S, ncand_me);
     if (m >= S || m < kSampleMinAbove) return -__builtin_inff();
     uint32_t prefix = 0, pmask = 0;
     int krem = (int)m;

@@ -531,6 +531,23 @@ def test_group_bank_pooled_small_heads(dsa, flags):
     _group_check(dsa, wl, flags)
 
 
+# The group scan's anchor rows (K = P) stream from a sampled start too: rows
+# of 12K keys and more (bf16) or 16K and more (E4M3) whose 3.5 P best keys
+# lie inside the row.
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("restream", [False, True])
+def test_group_scan_sampled_start(dsa, monkeypatch, dtype, restream):
+    """Banks of anchors past the shortest sampled row, and the rows refined
+    in them, match the oracle bit for bit on integer inputs; also when every
+    sampled start is made to fail, so that the re-stream launch builds the
+    banks."""
+    if restream:
+        monkeypatch.setenv("DSAIDX_SAMPLE_RERUN", "1")
+    wl = make_group_bank(T=20000, H=64, Hs=48, d=128, topk=256, G=16, P=1024, dtype=dtype, dist="int", seed=70)
+    rows = np.unique(np.r_[_rows(20000, 40, 70), 12287, 12288, 16383, 16384, 19999])
+    _group_check(dsa, wl, rows=rows)
+
+
 def test_group_bank_pooled_random(dsa):
     wl = make_group_bank(T=2000, H=64, Hs=64, d=128, topk=256, G=16, P=1024, dtype="bf16", dist="normal",
                          seed=45)
