@@ -767,6 +767,22 @@ def bench_calib(dsa, args, log):
 
 # ------------------------------------------------------------------ profiles
 
+def _short_kernel_name(name):
+    """A kernel's name without its return type, namespaces and parameter list
+    (the template arguments stay)."""
+    for p in ("void ", "dsaidx::", "(anonymous namespace)::"):
+        name = name.replace(p, "")
+    depth = 0
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return name[:i][:70]
+    return name[:70]
+
+
 def summarize_trace(path):
     """A table of rocprofv3's kernel statistics (kernel_stats.csv), or of a
     kernel trace (kernel_trace.csv) by kernel and grid size."""
@@ -775,7 +791,7 @@ def summarize_trace(path):
     if rows and "Grid_Size_X" in rows[0]:
         groups = {}
         for r in rows:
-            key = (r["Kernel_Name"][:70], int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])))
+            key = (_short_kernel_name(r["Kernel_Name"]), int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])))
             groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
         print(f"{'kernel':70s} {'workgroups':>10s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}")
         for (name, wgs), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
@@ -784,7 +800,7 @@ def summarize_trace(path):
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
     print(f"{'kernel':70s} {'calls':>6s} {'total_us':>11s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}")
     for r in rows:
-        name = r["Name"][:70]
+        name = _short_kernel_name(r["Name"])
         print(f"{name:70s} {int(r['Calls']):6d} {float(r['TotalDurationNs']) / 1e3:11.1f} "
               f"{float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
               f"{float(r['Percentage']):6.2f}")
