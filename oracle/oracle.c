@@ -34,7 +34,7 @@
  * whole prefix when it is built for a prefix not longer than P (forced mode);
  * query i = t sees only the bank (the literal candidate set of Eq. (14));
  * the mean pooling averages the final indexer queries and gates head by head
- * (fp32 sums in member order, times 1/G, the query rounded to bf16); query r
+ * (the fp64 mean, rounded once: the query to bf16, the gates to fp32); query r
  * of an MTP window whose first query sees N keys sits at position N - 1 + r.
  *
  * Precision: inputs are widened to double (bf16 and E4M3 widen exactly; an
@@ -563,26 +563,39 @@ int oracle_mtp(const void *q, const uint8_t *k_cache, const float *k_scale, cons
  * pooling of Appendix B.3 (Table 8) and B.4: the frozen DSA indexer builds the
  * bank with a group query that is the mean of the group's own indexer
  * queries, head by head, and head weights that are the mean of theirs.
- * The pooled query is a bf16 value that then decides the bank (an integer
- * result), so it is formed in the precision the library forms it in: an fp32
- * sum over the group's queries in query order, times 1/G (exact: G is a
- * power of two), rounded to the nearest bf16 (ties to even); the weights the
- * same way, kept in fp32.  Complete groups only; the rows of an incomplete
- * last group (which never builds a bank) are zero.  bf16 queries only. */
-static uint16_t f32_to_bf16_rne(float x)
-{
-    uint32_t u;
-    memcpy(&u, &x, 4);
-    const uint32_t lsb = (u >> 16) & 1u;
-    return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
-}
-
-static float bf16_bits_to_f32(uint16_t b)
+ * The pooled query is stored in bf16 and the weights in fp32, so each is the
+ * mean rounded once to the nearest value of its format (ties to even).  The
+ * mean is taken in fp64: the sum of G <= 16 bf16 values (8 significant bits
+ * each) is exact in fp64 unless their magnitudes span more than 2^40, and the
+ * sum of G fp32 gates unless theirs span more than 2^25; 1/G is a power of
+ * two.  Complete groups only; the rows of an incomplete last group (which
+ * never builds a bank) are zero.  bf16 queries only. */
+static double bf16_bits_to_f64(uint16_t b)
 {
     const uint32_t u = (uint32_t)b << 16;
     float x;
     memcpy(&x, &u, 4);
-    return x;
+    return (double)x;
+}
+
+/* x rounded to the nearest bf16 value, ties to the even significand: bf16
+ * values with exponent e (2^e <= |v| < 2^(e+1), e >= -126) are the multiples
+ * of 2^(e-7); below 2^-126 (subnormal) the multiples of 2^-133.  The scaled
+ * value is rounded to an integer with nearbyint (round to nearest even in the
+ * default mode); scaling by a power of two is exact.  |x| stays below the
+ * largest bf16 here (a mean of bf16 values). */
+static uint16_t f64_to_bf16_nearest(double x)
+{
+    if (x == 0.0) return signbit(x) ? 0x8000u : 0u;
+    int e;
+    frexp(x, &e);           /* |x| = f * 2^e, f in [0.5, 1): exponent e - 1 */
+    int ex = e - 1;
+    if (ex < -126) ex = -126;
+    const double v = ldexp(nearbyint(ldexp(x, 7 - ex)), ex - 7);
+    const float f = (float)v; /* exact: v has at most 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return (uint16_t)(u >> 16);
 }
 
 int oracle_pool_mean_bf16(const uint16_t *q, const float *w, int64_t Tq, int H, int d, int G,
@@ -590,19 +603,18 @@ int oracle_pool_mean_bf16(const uint16_t *q, const float *w, int64_t Tq, int H, 
 {
     if (Tq < 0 || H <= 0 || d <= 0 || (G != 4 && G != 8 && G != 16)) return -1;
     const int64_t NG = (Tq + G - 1) / G, nfull = Tq / G;
-    const float inv = 1.0f / (float)G;
     for (int64_t g = 0; g < NG; ++g) {
         for (int64_t e = 0; e < (int64_t)H * d; ++e) {
-            float s = 0.0f;
+            double s = 0.0;
             if (g < nfull)
-                for (int i = 0; i < G; ++i) s += bf16_bits_to_f32(q[(g * G + i) * (int64_t)H * d + e]);
-            qbar[g * (int64_t)H * d + e] = f32_to_bf16_rne(s * inv);
+                for (int i = 0; i < G; ++i) s += bf16_bits_to_f64(q[(g * G + i) * (int64_t)H * d + e]);
+            qbar[g * (int64_t)H * d + e] = f64_to_bf16_nearest(s / G);
         }
         for (int j = 0; j < H; ++j) {
-            float s = 0.0f;
+            double s = 0.0;
             if (g < nfull)
-                for (int i = 0; i < G; ++i) s += w[(g * G + i) * (int64_t)H + j];
-            wbar[g * (int64_t)H + j] = s * inv;
+                for (int i = 0; i < G; ++i) s += (double)w[(g * G + i) * (int64_t)H + j];
+            wbar[g * (int64_t)H + j] = (float)(s / G);
         }
     }
     return 0;

@@ -70,6 +70,10 @@ def _stream(dev):
     return torch.cuda.current_stream(dev).cuda_stream
 
 
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def _ws(nbytes, dev, ws):
     if nbytes == 0:
         return None
@@ -108,7 +112,7 @@ def indexer_prefill(q, k, w, q_pos0=0, topk=2048, q_scale=None, k_scale=None, wa
     ws = _ws(workspace_prefill(Tq, Tk, H, d, topk, dt), dev, ws)
     rc = lib().indexer_prefill(_ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(w), dt, Tq, Tk, H, d,
                                q_pos0, topk, _ptr(out_idx), _ptr(out_score), _ptr(ws),
-                               0 if ws is None else ws.numel(), _stream(dev))
+                               _nbytes(ws), _stream(dev))
     _check(rc, "indexer_prefill")
     return out_idx, out_score
 
@@ -127,7 +131,7 @@ def indexer_decode(q, k_cache, k_scale, w, seq_lens, topk=2048, want_score=True,
         out_score = torch.empty((B, topk), dtype=torch.float32, device=dev)
     ws = _ws(workspace_decode(B, Nmax, H, d, topk), dev, ws)
     rc = lib().indexer_decode(_ptr(q), _ptr(k_cache), _ptr(k_scale), _ptr(w), _ptr(seq_lens), B, Nmax, H, d,
-                              topk, _ptr(out_idx), _ptr(out_score), _ptr(ws), 0 if ws is None else ws.numel(),
+                              topk, _ptr(out_idx), _ptr(out_score), _ptr(ws), _nbytes(ws),
                               _stream(dev))
     _check(rc, "indexer_decode")
     return out_idx, out_score
@@ -171,7 +175,7 @@ def indexer_group_bank(q, k, w, qbar, wbar, q_pos0, G, P, topk=2048, q_scale=Non
     rc = lib().indexer_group_bank(_ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(w), dt, Tq, Tk, H, d,
                                   q_pos0, _ptr(qbar), _ptr(qbar_scale), _ptr(wbar), Hs, G, P, topk, flags,
                                   _ptr(out_idx), _ptr(out_bank), _ptr(out_score), _ptr(ws),
-                                  0 if ws is None else ws.numel(), _stream(dev))
+                                  _nbytes(ws), _stream(dev))
     _check(rc, "indexer_group_bank")
     return out_idx, out_score, out_bank
 
@@ -232,7 +236,7 @@ def indexer_layers(layers, q_pos0=0, topk=2048, want_score=False, want_bank=Fals
     arr = _layer_structs(full)
     ws = _ws(lib().indexer_layers_workspace_size(arr, len(full), Tq, Tk, H, d, topk, dt), dev, ws)
     rc = lib().indexer_layers(arr, len(full), dt, Tq, Tk, H, d, q_pos0, topk, _ptr(ws),
-                              0 if ws is None else ws.numel(), _stream(dev))
+                              _nbytes(ws), _stream(dev))
     _check(rc, "indexer_layers")
     return [(L["out_idx"], L.get("out_score"), L.get("out_bank")) for L in full]
 
@@ -272,7 +276,7 @@ def indexer_mtp(q, k_cache, k_scale, w, qbar, wbar, prefix_lens, G, P, topk=2048
     ws = _ws(workspace_mtp(B, Nmax, m, H, Hs, d, G, P, topk, flags), dev, ws)
     rc = lib().indexer_mtp(_ptr(q), _ptr(k_cache), _ptr(k_scale), _ptr(w), _ptr(qbar), _ptr(wbar), _ptr(prefix_lens),
                            B, Nmax, m, H, Hs, d, G, P, topk, flags, _ptr(out_idx), _ptr(out_bank), _ptr(out_score),
-                           _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
+                           _ptr(ws), _nbytes(ws), _stream(dev))
     _check(rc, "indexer_mtp")
     return out_idx, out_score, out_bank
 
@@ -394,6 +398,6 @@ def indexer_group_query(c, h, w_pool, w_q, w_g, G, Hs, d, q_pos0=0, rope_dim=64,
     ws = _ws(lib().indexer_group_query_workspace_size(Tq, dc, dh, Hs, d, G), dev, ws)
     rc = lib().indexer_group_query(_ptr(c), _ptr(h), _ptr(w_pool), _ptr(w_q), _ptr(w_g), Tq, dc, dh, Hs, d, G, q_pos0,
                                    rope_dim, float(rope_base), _ptr(qbar), _ptr(wbar), _ptr(ws),
-                                   0 if ws is None else ws.numel(), _stream(dev))
+                                   _nbytes(ws), _stream(dev))
     _check(rc, "indexer_group_query")
     return qbar, wbar

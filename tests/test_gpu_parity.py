@@ -554,6 +554,39 @@ def test_group_bank_pooled_random(dsa):
     _group_check(dsa, wl, flags=dsa.POOL_MEAN, rows=_rows(2000, 48, 45))
 
 
+@pytest.mark.parametrize("G", [4, 8, 16])
+def test_pool_mean_kernel_bits(dsa, G):
+    """The training-free group query itself, bit for bit: with out_bank given,
+    the call keeps the pooled q-bar [groups, H, d] bf16 and w-bar [groups, H]
+    fp32 at the start of its workspace (each region 256-byte aligned).  Normal
+    inputs, with group 0's first element built so that its mean lies just
+    above a bf16 midpoint: members 2, 1 x (G - 3), 1 + G/256 and 2^-27 have the
+    mean 1 + 2^-8 + 2^-27/G, which an fp32 sum would put on the midpoint
+    1 + 2^-8 (then rounded to even, 1.0); the correctly rounded mean is
+    1 + 2^-7.  Every element must equal the oracle's correctly rounded mean."""
+    T, H, d, P, K = G * 40 + 5, 64, 128, 64, 16
+    wl = make_group_bank(T=T, H=H, Hs=H, d=d, topk=K, G=G, P=P, dtype="bf16", dist="normal", seed=80 + G)
+    q, w = wl["q"].clone(), wl["w"].clone()
+    members = [2.0] + [1.0] * (G - 3) + [1.0 + G / 256, 2.0 ** -27]
+    q[0:G, 0, 0] = torch.tensor(members, dtype=torch.float32).to(torch.bfloat16)
+    nfull = T // G
+    qb_bytes = -(-nfull * H * d * 2 // 256) * 256
+    ws = torch.zeros(dsa.workspace_group_bank(T, T, H, H, d, G, P, K, dsa.DSAIDX_BF16,
+                                              dsa.POOL_MEAN | dsa.FORCE_BANK) // 4 + 1,
+                     dtype=torch.int32, device="cuda")
+    dev = {"q": q.cuda(), "k": wl["k"].cuda(), "w": w.cuda()}
+    dsa.indexer_group_bank(dev["q"], dev["k"], dev["w"], None, None, 0, G, P, K,
+                           flags=dsa.POOL_MEAN | dsa.FORCE_BANK, want_bank=True, ws=ws)
+    torch.cuda.synchronize()
+    raw = ws.cpu().numpy().view(np.uint8)
+    gq = raw[:nfull * H * d * 2].view(np.uint16).reshape(nfull, H, d)
+    gw = raw[qb_bytes:qb_bytes + nfull * H * 4].view(np.float32).reshape(nfull, H)
+    rq, rw = oracle.pool_mean_bf16(q, w, G)
+    assert np.array_equal(gq, rq[:nfull])
+    assert np.array_equal(gw.view(np.uint32), rw[:nfull].view(np.uint32))
+    assert gq[0, 0, 0] == 0x3F81
+
+
 def test_group_bank_random(dsa):
     wl = make_group_bank(T=2000, H=64, Hs=64, d=128, topk=256, G=16, P=1024, dtype="bf16", dist="normal",
                          seed=19)

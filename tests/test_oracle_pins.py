@@ -581,27 +581,64 @@ def test_pool_mean_exact_on_integers(oracle_lib, G):
     assert np.abs(ref_q).max() > 0.2  # the case is not trivially zero
 
 
-def test_pool_mean_within_one_ulp_of_exact(oracle_lib):
-    """Normal inputs: the pooled bf16 value is within one bf16 ulp of the fp64
-    mean rounded to bf16 (the fp32 sum of 16 terms adds far less than one)."""
-    G = 16
-    wl = _gb(T=G * 12, G=G, P=16, K=8, seed=25, dist="normal", H=4, d=32)
-    q, w = wl["q"], wl["w"]
-    qbar, wbar = oracle.pool_mean_bf16(q, w, G)
-    ref_q = _f64(q).reshape(-1, G, *q.shape[1:]).mean(1)
-    ref_b = _bits(to_bf16(torch.from_numpy(ref_q).float())).astype(np.int32)
-    mine = qbar.astype(np.int32)
-    # same sign, at most one step apart in the ordered bf16 code space
-    sign = (mine >> 15) == (ref_b >> 15)
-    near = np.abs((mine & 0x7FFF) - (ref_b & 0x7FFF)) <= 1
-    zero = (ref_b & 0x7FFF) <= 1
-    assert (near & (sign | zero)).all()
-    assert (mine == ref_b).mean() > 0.95
-    # fp32 sum of G signed gates: error below G * 2^-24 of the largest term
-    wg = _f64(w).reshape(-1, G, w.shape[1])
-    bound = G * 2.0 ** -24 * np.abs(wg).max(1) + 1e-30
-    assert (np.abs(wbar - wg.mean(1)) <= bound).all()
+def _bf16_value(code):
+    """The exact value of a bf16 bit pattern, as a Fraction."""
+    from fractions import Fraction
+    return Fraction(float(np.array([int(code) << 16], dtype=np.uint32).view(np.float32)[0]))
 
+
+def _nearest_bf16(x):
+    """The bf16 code nearest to the Fraction x, ties to the even code, found by
+    comparing x exactly with the bf16 values around its float image."""
+    f = np.float32(float(x))
+    c = int(np.array([f], dtype=np.float32).view(np.uint32)[0] >> 16)
+    best = None
+    for cand in (c - 1, c, c + 1, c + 2, c ^ 0x8000):
+        cand &= 0xFFFF
+        if (cand & 0x7F80) == 0x7F80:  # inf / nan
+            continue
+        err = abs(_bf16_value(cand) - x)
+        key = (err, cand & 1)
+        if best is None or key < best[0]:
+            best = (key, cand)
+    return best[1]
+
+
+def test_pool_mean_is_the_correctly_rounded_mean(oracle_lib):
+    """Normal inputs: every pooled query element is the group's exact mean
+    (rational arithmetic) rounded to the nearest bf16 with ties to even, and
+    every pooled gate the exact mean rounded to the nearest fp32.  Group 0 is
+    built so that its mean lies just above a bf16 midpoint by less than an
+    fp32 sum of its members can resolve (members 2, 1 x 5, 1 + 2^-5, 2^-27 give
+    1 + 2^-8 + 2^-30): a sum in fp32 would land on the midpoint and round to
+    even (down); the correctly rounded mean rounds up.  Group 1 is an exact
+    midpoint (1 + 2^-8), which rounds to even."""
+    from fractions import Fraction
+    G = 8
+    wl = _gb(T=G * 12, G=G, P=16, K=8, seed=25, dist="normal", H=4, d=32)
+    q, w = wl["q"].clone(), wl["w"].clone()
+    q[0:G, 0, 0] = torch.tensor([2, 1, 1, 1, 1, 1, 1 + 2 ** -5, 2 ** -27], dtype=torch.float32).to(torch.bfloat16)
+    q[G:2 * G, 0, 0] = torch.tensor([1, 1, 1, 1, 1, 1, 1, 1 + 2 ** -5], dtype=torch.float32).to(torch.bfloat16)
+    qbar, wbar = oracle.pool_mean_bf16(q, w, G)
+    assert qbar[0, 0, 0] == 0x3F81  # 1 + 2^-7: above the midpoint rounds up
+    assert qbar[1, 0, 0] == 0x3F80  # 1 + 2^-8 exactly: the even neighbour, 1.0
+    qb = _bits(q).reshape(-1, G, *q.shape[1:])
+    qv = qb.astype(np.uint32) << 16
+    qf = qv.view(np.float32)
+    for g in range(qb.shape[0]):
+        for e in np.ndindex(*qb.shape[2:]):
+            x = sum(Fraction(float(qf[g, i][e])) for i in range(G)) / G
+            assert qbar[g][e] == _nearest_bf16(x), (g, e)
+    wg = w.numpy().reshape(-1, G, w.shape[1])
+    for g in range(wg.shape[0]):
+        for j in range(wg.shape[2]):
+            x = sum(Fraction(float(v)) for v in wg[g, :, j]) / G
+            lo = np.float32(float(x))  # the float nearest to x's float64 image
+            cands = [np.nextafter(lo, np.float32(-np.inf)), lo, np.nextafter(lo, np.float32(np.inf))]
+            errs = [abs(Fraction(float(c)) - x) for c in cands]
+            m = min(errs)
+            ok = [c for c, e in zip(cands, errs) if e == m]
+            assert wbar[g, j] in ok, (g, j)
 
 def test_pooled_bank_is_the_bank_of_the_mean(oracle_lib):
     """The pooling flag uses the pooled query as the group query with all H heads:
