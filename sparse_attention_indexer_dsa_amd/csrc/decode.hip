@@ -631,18 +631,25 @@ __global__ void __launch_bounds__(kSpanThreads) decode_classify_kernel(const Dec
   __shared__ int s_base;
   const int b = blockIdx.y, j = blockIdx.x;
   const int tid = threadIdx.x;
+  // the span's list counts are read together with the row's length (they lie
+  // inside the workspace for every span of the grid; unused past the row)
+  const SpanList L(args, b, j);
   int64_t n = args.seq_lens[b];
   n = n < 0 ? 0 : (n > args.Nmax ? args.Nmax : n);
   if (n <= args.K || (int64_t)j * args.kpb >= n) return;
-  const SpanList L(args, b, j);
   const int c = L.n;
-  // the first batch of the list is requested before the threshold search
+  // the first batch of the list (scores and key indices together, so a
+  // candidate's index needs no second round trip) is requested before the
+  // threshold search
   uint32_t key[kSpanBatch];
+  int32_t kid[kSpanBatch];
   auto load_batch = [&](int base) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kSpanBatch; ++u) {
       const int e = base + u * kSpanThreads + tid;
-      key[u] = e < c ? order_key(args.cl_sc[L.slot(e)]) : 0u;  // key 0: below every bin b*
+      const int64_t sl = e < c ? L.slot(e) : 0;
+      key[u] = e < c ? order_key(args.cl_sc[sl]) : 0u;  // key 0: below every bin b*
+      kid[u] = e < c ? args.cl_idx[sl] : 0;
     }
   };
   load_batch(0);
@@ -671,7 +678,7 @@ __global__ void __launch_bounds__(kSpanThreads) decode_classify_kernel(const Dec
       if ((key[u] >> kShift) == bstar && key[u] != 0u) {
         if (p < kDecCandCap) {
           ck[p] = key[u];
-          ci[p] = args.cl_idx[L.slot(base + u * kSpanThreads + tid)];
+          ci[p] = kid[u];
         }
         ++p;
       }
@@ -686,6 +693,7 @@ __global__ void __launch_bounds__(kSpanThreads) decode_classify_kernel(const Dec
 // One workgroup per row: the exact K-th key among the candidates of b*, the
 // tie cut, and every span's output offset.  Rows of at most K keys, and rows
 // whose b* bin or span count is too large, are written here completely.
+static_assert(kSelThreads <= kDecCandCap, "each thread's first candidate slot is inside the row's array");
 __global__ void __launch_bounds__(kSelThreads) decode_select_kernel(const DecodeArgs args) {
   __shared__ uint32_t s_ckey[kDecCandCap];
   __shared__ int32_t s_cidx[kDecCandCap];
@@ -697,6 +705,13 @@ __global__ void __launch_bounds__(kSelThreads) decode_select_kernel(const Decode
   __shared__ int s_cnt[kSelThreads];  // list entries per span (exact path)
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
+  // reads that depend on nothing, issued together before the first wait: the
+  // row's candidate count, each thread's first candidate and its span's
+  // count above b* (all inside the workspace, whatever the row needs)
+  const int nc = args.cand_cnt[b];
+  const uint32_t ck0 = args.cand_key[(int64_t)b * kDecCandCap + tid];
+  const int32_t ci0 = args.cand_idx[(int64_t)b * kDecCandCap + tid];
+  const int above0 = tid < args.nblk ? args.span_above[(int64_t)b * args.nblk + tid] : 0;
   int64_t n = args.seq_lens[b];
   if (args.skip_negative && n < 0) return;  // a row this launch does not own
   n = n < 0 ? 0 : (n > args.Nmax ? args.Nmax : n);
@@ -736,8 +751,11 @@ __global__ void __launch_bounds__(kSelThreads) decode_select_kernel(const Decode
   // from its own K-th best's bin up, which is at most b*, so b*'s keys are all
   // listed (the count is at most in_bin either way, and a key a list did not
   // keep could not be selected).
-  const int nc = args.cand_cnt[b];
-  for (int i = tid; i < nc; i += kSelThreads) {
+  if (tid < nc) {
+    s_ckey[tid] = ck0;
+    s_cidx[tid] = ci0;
+  }
+  for (int i = tid + kSelThreads; i < nc; i += kSelThreads) {
     s_ckey[i] = args.cand_key[(int64_t)b * kDecCandCap + i];
     s_cidx[i] = args.cand_idx[(int64_t)b * kDecCandCap + i];
   }
@@ -785,7 +803,7 @@ __global__ void __launch_bounds__(kSelThreads) decode_select_kernel(const Decode
     if (key > kth || (key == kth && ~e >= idx_cut)) atomicAdd(&s_chosen[e / (uint32_t)args.kpb], 1);
   }
   __syncthreads();
-  const int mine = tid < nb ? s_chosen[tid] + args.span_above[(int64_t)b * args.nblk + tid] : 0;
+  const int mine = tid < nb ? s_chosen[tid] + above0 : 0;  // nb <= nblk
   int total;
   const int off = block_excl_scan(mine, s_tmp, total);
   if (tid < nb) args.span_off[(int64_t)b * args.nblk + tid] = off;
@@ -805,15 +823,19 @@ __global__ void __launch_bounds__(kSpanThreads) decode_emit_kernel(const DecodeA
   __shared__ int s_wc[kSpanBatch * kSpanWaves];
   const int b = blockIdx.y, j = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  // the row's length and selection, and the span's list counts and output
+  // offset, are independent reads: all are issued before the first test
+  const SpanList L(args, b, j);
+  const int sel_mode = args.rowsel[4 * b];
+  const uint32_t kth = args.rowsel[4 * b + 1], idx_cut = args.rowsel[4 * b + 2];
+  const int off0 = args.span_off[(int64_t)b * args.nblk + j];
   int64_t n = args.seq_lens[b];
   n = n < 0 ? 0 : (n > args.Nmax ? args.Nmax : n);
-  if ((int64_t)j * args.kpb >= n || args.rowsel[4 * b] != 1) return;
-  const uint32_t kth = args.rowsel[4 * b + 1], idx_cut = args.rowsel[4 * b + 2];
-  const SpanList L(args, b, j);
+  if ((int64_t)j * args.kpb >= n || sel_mode != 1) return;
   const int c = L.n;
   int32_t* oidx = args.out_idx + (int64_t)b * args.K;
   float* osc = args.out_score ? args.out_score + (int64_t)b * args.K : nullptr;
-  int out = args.span_off[(int64_t)b * args.nblk + j];
+  int out = off0;
   for (int base = 0; base < c; base += kSpanBatch * kSpanThreads) {
     float v[kSpanBatch];
     int32_t idx[kSpanBatch];
