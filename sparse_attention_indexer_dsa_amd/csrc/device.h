@@ -346,10 +346,18 @@ __device__ __forceinline__ void wave_emit_topk(const uint32_t* keys, const int32
     uint32_t prefix = 0, pmask = 0;
     int krem = K;
     radix_step<2048, B>(keys, n, hist, 21, prefix, pmask, krem);
-    radix_step<2048, B>(keys, n, hist, 10, prefix, pmask, krem);
-    radix_step<1024, B>(keys, n, hist, 0, prefix, pmask, krem);
-    kth = prefix;
-    keep_eq = krem;
+    radix_count<2048, B>(keys, n, hist, 10, prefix, pmask);
+    const int in_bucket = radix_pick<2048>(hist, 10, prefix, pmask, krem);
+    if (in_bucket == krem && prefix != 0u) {
+      // the K-th best's 22-bit key bucket is taken whole: the top K are the
+      // entries at or above its lowest key, and the last digit needs no pass
+      kth = prefix - 1u;
+      keep_eq = 0;
+    } else {
+      radix_step<1024, B>(keys, n, hist, 0, prefix, pmask, krem);
+      kth = prefix;
+      keep_eq = krem;
+    }
   }
   emit_kept<B / 2>(keys, n, K, select, kth, keep_eq, oidx, osc, [&](int e) { return idx[e]; },
                    [](int32_t i) { return i; });
@@ -411,7 +419,13 @@ __device__ __forceinline__ void wave_emit_row(uint32_t* keys, int32_t* ids, int 
   }
   wave_mem_fence();
   wave_lds_sync();
-  radix_pick<2048>(hist, 10, prefix, pmask, krem);
+  const int in_bucket = radix_pick<2048>(hist, 10, prefix, pmask, krem);
+  if (in_bucket == krem && prefix != 0u) {
+    // the K-th best's 22-bit bucket is taken whole (no last-digit pass)
+    emit_kept<B>(keys, m, K, true, prefix - 1u, 0, oidx, osc, [&](int e) { return ids[e]; },
+                 [](int32_t i) { return i; });
+    return;
+  }
   radix_step<1024, B>(keys, m, hist, 0, prefix, pmask, krem);
   emit_kept<B>(keys, m, K, true, prefix, krem, oidx, osc, [&](int e) { return ids[e]; },
                [](int32_t i) { return i; });
